@@ -1,0 +1,262 @@
+"""Benchmark of the batch-invariant GEMM library on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+Prints ONE JSON line.  The headline workload is the square fp16 product
+M = N = K = 8192 with fp32 output through gemm_run (one step = one product
+over one batch of seeded synthetic input already resident in HBM); `value`
+is its throughput in TFLOP/s.  The same run also measures, as secondary
+results under "extra": the fp8 e5m2 8192^3 product (bf16 out), the decode
+products N=4096 K=14336 at M in {1, 8, 32, 128} through the split-K path
+(GB/s, inputs rotated through enough copies to defeat the 256 MB last-level
+cache), the huge-K product 256 x 256 x 131072 at split_k in {1, 8, 32, 128},
+and torch.matmul (hipBLASLt) on the headline shape as a run-only comparator.
+
+"roofline" reports the dominant kernel (the main-loop GEMM kernel) against
+the MI355X dense fp16 matrix peak: achieved = 2*M*N*K flop per launch divided
+by the kernel's average duration, timed with HIP events on the launch
+stream.  "cpu_baseline" times the CPU oracle (test infrastructure, fp64
+triple loop) on a bounded sample of rows of the same product.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = {"f16": 2516.6, "bf16": 2516.6, "e4m3": 5033.2, "e5m2": 5033.2}
+PEAK_HBM_GBS = 8000.0
+MALL_BYTES = 256 * 2 ** 20
+KERNEL_SOURCES = [os.path.join(ROOT, "invariant_matmul_amd", "csrc", f)
+                  for f in ("gemm_kernels.hip", "imm_internal.h", "api.cpp")]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_square_f16_8192.json")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def time_launches(fn, n, warmup, torch):
+    """Per-call durations (ms) from HIP events recorded on the current stream."""
+    for _ in range(warmup):
+        fn(0)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for i in range(n):
+        ev[i][0].record()
+        fn(i)
+        ev[i][1].record()
+    t1.record()
+    torch.cuda.synchronize()
+    per = [a.elapsed_time(b) for a, b in ev]
+    return per, t0.elapsed_time(t1)
+
+
+def summary(per):
+    s = sorted(per)
+    return {"median_ms": statistics.median(s), "min_ms": s[0],
+            "p90_ms": s[min(len(s) - 1, int(0.9 * len(s)))], "n": len(s)}
+
+
+def cpu_baseline(w, A, B, target_s=12.0):
+    """Time the oracle on the first rows of the product (~target_s seconds)."""
+    import oracle
+    import workloads as wl
+    a_bits, b_bits = wl.bits(A), wl.bits(B)
+    threads = oracle.max_threads()
+    rows = 4
+    t = time.perf_counter()
+    oracle.gemm(a_bits, b_bits, w.dtype, rows=list(range(rows)))
+    dt = time.perf_counter() - t
+    # the first call also decodes B; scale the row count to the target time
+    more = max(rows, min(w.M, int(rows * target_s / max(dt, 1e-3))))
+    t = time.perf_counter()
+    oracle.gemm(a_bits, b_bits, w.dtype, rows=list(range(more)))
+    dt = time.perf_counter() - t
+    flops = 2.0 * more * w.N * w.K
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"rows 0..{more - 1} of the {w.M}x{w.N}x{w.K} {w.dtype} product "
+                      f"(includes decoding B once), {dt:.1f} s"}
+
+
+def bench_square(name, steps, warmup, torch, imm, wl):
+    w = wl.WORKLOADS[name]
+    A, B = w.make()
+    Ad, Bd = A.cuda(), B.cuda()
+    plan = imm.gemm_plan(w.M, w.N, w.K, w.dtype)
+    out_t = torch.float32 if w.out == "f32" else torch.bfloat16
+    C = torch.empty((w.M, w.N), dtype=out_t, device="cuda")
+    per, total = time_launches(lambda i: imm.gemm_run(plan, Ad, Bd, C), steps, warmup, torch)
+    return w, plan, per, total, (A, B, Ad, Bd)
+
+
+def bench_splitk(name, split, torch, imm, wl, n=30, warmup=5, M=None):
+    """Split-K path with inputs rotated through enough copies to defeat the MALL."""
+    w = wl.WORKLOADS[name]
+    A, B = w.make()
+    Ad, Bd = A.cuda(), B.cuda()
+    Mrows = w.M if M is None else M
+    Ad = Ad[:Mrows].contiguous()
+    bytes_in = Ad.numel() * Ad.element_size() + Bd.numel() * Bd.element_size()
+    copies = max(1, -(-2 * MALL_BYTES // bytes_in)) + 1
+    As = [Ad] + [Ad.clone() for _ in range(copies - 1)]
+    Bs = [Bd] + [Bd.clone() for _ in range(copies - 1)]
+    plan = imm.gemm_plan_ex(Mrows, w.N, w.K, w.dtype, w.out, split_k=split)
+    C = torch.empty((Mrows, w.N), dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(1, imm.gemm_workspace_size(plan) // 4), dtype=torch.float32,
+                     device="cuda")
+    per, _ = time_launches(
+        lambda i: imm.gemm_splitk_run(plan, As[i % copies], Bs[i % copies], C, ws),
+        n, warmup, torch)
+    algo = bytes_in + Mrows * w.N * 4
+    med = statistics.median(per)
+    return {"M": Mrows, "N": w.N, "K": w.K, "split_k": plan.info["split_k"],
+            "tile": f"{plan.info['block_m']}x{plan.info['block_n']}",
+            "copies_rotated": copies, **summary(per),
+            "algorithmic_bytes": algo, "GBps": algo / (med * 1e-3) / 1e9,
+            "pct_hbm_peak": 100.0 * algo / (med * 1e-3) / 1e9 / PEAK_HBM_GBS,
+            "TFLOPs": 2.0 * Mrows * w.N * w.K / (med * 1e-3) / 1e12,
+            "workspace_traffic_bytes": 2 * plan.info["workspace_bytes"]}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-extra", action="store_true", help="headline workload only")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    ap.add_argument("--profile-pass", action="store_true",
+                    help="a few launches of the headline kernel plus a plain copy of known "
+                         "size, for hardware-counter runs; prints nothing else")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (this build has no multi-GPU path); "
+              f"--gpus {args.gpus} is not supported", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import invariant_matmul_amd as imm
+    import workloads as wl
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    imm.lib()
+
+    if args.profile_pass:
+        w = wl.WORKLOADS["square_f16_8192"]
+        A, B = w.make()
+        Ad, Bd = A.cuda(), B.cuda()
+        plan = imm.gemm_plan(w.M, w.N, w.K, w.dtype)
+        C = torch.empty((w.M, w.N), dtype=torch.float32, device="cuda")
+        src = torch.empty(256 * 2 ** 20 // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)   # plain copy: 256 MiB read + 256 MiB written
+        for _ in range(3):
+            imm.gemm_run(plan, Ad, Bd, C)
+        torch.cuda.synchronize()
+        print("profile pass done", flush=True)
+        return
+
+    log("headline: square fp16 8192^3, gemm_run")
+    w, plan, per, total, host = bench_square("square_f16_8192", args.steps, args.warmup,
+                                             torch, imm, wl)
+    ms_per_step = total / args.steps
+    value = w.flops / (ms_per_step * 1e-3) / 1e12
+    kavg = statistics.mean(per)
+    achieved = w.flops / (kavg * 1e-3) / 1e12
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+        if t.get("kernel_source_hash") == kernel_source_hash():
+            traffic = t.get("bytes_per_launch")
+    roofline = {"bound": "mfma", "achieved": achieved, "peak": PEAK_TFLOPS["f16"],
+                "unit": "TFLOP/s", "frac": achieved / PEAK_TFLOPS["f16"], "traffic": traffic,
+                "kernel": "gemm_tile_kernel<f16,f32,256x256>",
+                "algorithmic_flop_per_launch": w.flops, "avg_launch_ms": kavg}
+
+    extra = {"headline_kernel": summary(per),
+             "plan": {k: plan.info[k] for k in ("block_m", "block_n", "block_k", "waves",
+                                                  "group_m", "split_k", "mfma_k")}}
+    if not args.no_extra:
+        A, B, Ad, Bd = host
+        try:
+            ref = torch.empty((w.M, w.N), dtype=torch.float16, device="cuda")
+            tper, _ = time_launches(lambda i: torch.matmul(Ad, Bd, out=ref), 20, 5, torch)
+            extra["torch_matmul_f16_8192_TFLOPs"] = w.flops / (statistics.median(tper) * 1e-3) / 1e12
+        except Exception as e:  # comparator only
+            extra["torch_matmul_error"] = str(e)
+        del Ad, Bd
+        torch.cuda.empty_cache()
+        log("fp8 e5m2 8192^3")
+        w8, plan8, per8, _, _ = bench_square("square_e5m2_8192", 30, 5, torch, imm, wl)
+        med8 = statistics.median(per8)
+        extra["square_e5m2_8192"] = {**summary(per8),
+                                     "TFLOPs": w8.flops / (med8 * 1e-3) / 1e12,
+                                     "pct_mfma_peak": 100 * w8.flops / (med8 * 1e-3) / 1e12 /
+                                     PEAK_TFLOPS["e5m2"]}
+        torch.cuda.empty_cache()
+        for n in ("square_f16_4096", "square_f16_1024"):
+            wn, _, pn, _, _ = bench_square(n, 50, 10, torch, imm, wl)
+            medn = statistics.median(pn)
+            extra[n] = {**summary(pn), "TFLOPs": wn.flops / (medn * 1e-3) / 1e12}
+            torch.cuda.empty_cache()
+        log("decode bf16 N=4096 K=14336, split-K path")
+        extra["decode_bf16"] = [bench_splitk("decode_bf16_m128", 0, torch, imm, wl, M=m)
+                                for m in (1, 8, 32, 128)]
+        torch.cuda.empty_cache()
+        log("huge-K fp16 256x256x131072, split-K path")
+        extra["hugek_f16"] = [bench_splitk("hugek_f16", s, torch, imm, wl) for s in (1, 8, 32, 128)]
+        torch.cuda.empty_cache()
+        A, B = host[0], host[1]
+    else:
+        A, B = host[0], host[1]
+
+    cpu = None
+    if not args.no_cpu:
+        log("cpu baseline (oracle)")
+        cpu = cpu_baseline(w, A, B)
+
+    line = {
+        "metric": "GEMM TFLOPS & % MFMA peak (8192^3 fp16, fp8); GB/s at M<=32; batch-invariance",
+        "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+        "data": "synthetic (seeded uniform[-1,1) fp16, resident in HBM)",
+        "config": {"workload": "square fp16 GEMM M=N=K=8192, fp32 accumulate, fp32 output, "
+                               "gemm_run (no split-K)",
+                   "M": w.M, "N": w.N, "K": w.K, "pct_mfma_peak": 100 * value / PEAK_TFLOPS["f16"]},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,169 @@
+/*
+ * invariant_matmul.h -- C ABI of a batch-invariant GEMM library for AMD
+ * MI355X (gfx950).
+ *
+ * It computes C = scale_a * scale_b * (A x B) with A [M,K], B [K,N] and
+ * C [M,N], all row-major and contiguous (leading dimensions K, N and N), from
+ * fp16, bf16 or OCP fp8 (e4m3fn / e5m2) inputs with fp32 accumulation.  The
+ * problem statement, the matrix shapes and the element formula follow the
+ * Tencent engineer article on deterministic LLM inference ("AI インフラの深化：
+ * 大規模モデルに確定的な出力を実現する方法"), section "Batch Invariance の由来"
+ * (C = A x B with A [M,K], B [K,N]; C_ij is the dot product of row i of A and
+ * column j of B over k).
+ *
+ * Batch invariance.  The same article (same section) shows that the
+ * spatial tile sizes and the workgroup order do not change any bit, while the
+ * reduction step and the split of K do.  This library therefore fixes the
+ * matrix-core instruction per input dtype and fixes the K order, the K-step
+ * and the split of K from (N, K, dtypes, explicit options) alone -- never
+ * from M.  For one plan key the bits of row i of C are a function of row i of
+ * A and of B only: they do not depend on M, on other rows, on concurrently
+ * running work, on the stream or on how often the call has run.
+ *
+ * Calls, their passages:
+ *   gemm_run          one workgroup per output tile running the K loop
+ *                     (article, section "Tiling - 分塊行列乗算": accumulator
+ *                     init, load/compute/accumulate per K step, one write-back);
+ *                     tiles visited in GROUP_M order (section "GROUP_M -
+ *                     Swizzle L2 Cache").
+ *   gemm_splitk_run   split-K through a [split_k, M, N] fp32 workspace and a
+ *                     separate reduction kernel on the same stream, no atomics
+ *                     (section "Split-K", the workspace variant).
+ *
+ * Conventions for every call:
+ *   - All matrices and the workspace are DEVICE memory owned by the caller; the
+ *     library never allocates device memory.  A plan is host memory owned by
+ *     the caller (free it with gemm_plan_destroy).  Plans are immutable and
+ *     may be used from several host threads / streams at once (each concurrent
+ *     split-K call needs its own workspace).
+ *   - `stream` is a hipStream_t passed as void* (NULL means the null stream).
+ *     Run calls only enqueue work on it: they never synchronise the host.
+ *   - Inputs are read-only.  C is fully overwritten (there is no beta).  The
+ *     workspace holds no meaningful data after the call.
+ *   - Every argument is validated before any HIP call; on error nothing is
+ *     enqueued and C is untouched.  A status other than GEMM_OK is returned:
+ *       GEMM_ERR_INVALID_VALUE  negative size, NULL pointer for a non-empty
+ *                               operand, pointer not 16-byte aligned, NULL
+ *                               plan or output handle;
+ *       GEMM_ERR_UNSUPPORTED    unsupported dtype pair, N or K not a multiple of
+ *                               16 bytes' worth of elements (8 for 16-bit
+ *                               inputs, 16 for fp8), bad option value;
+ *       GEMM_ERR_WORKSPACE      workspace NULL or smaller than
+ *                               gemm_workspace_size();
+ *       GEMM_ERR_HIP            no usable GPU, or a launch failed (the HIP
+ *                               error is then available from hipGetLastError
+ *                               semantics inside the library: call
+ *                               gemm_last_hip_error() for its code).
+ *   - Empty products: M == 0 or N == 0 enqueue nothing and return GEMM_OK;
+ *     K == 0 writes C = 0.
+ */
+#ifndef INVARIANT_MATMUL_H
+#define INVARIANT_MATMUL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GEMM_OK = 0,
+  GEMM_ERR_INVALID_VALUE = 1,
+  GEMM_ERR_UNSUPPORTED = 2,
+  GEMM_ERR_WORKSPACE = 3,
+  GEMM_ERR_HIP = 4
+} gemm_status;
+
+/* Element types.  Inputs: F16, BF16, F8_E4M3 (OCP e4m3fn), F8_E5M2 (OCP e5m2).
+ * Outputs: F32 or BF16 (round to nearest, ties to even). */
+typedef enum {
+  GEMM_F16 = 0,
+  GEMM_BF16 = 1,
+  GEMM_F8_E4M3 = 2,
+  GEMM_F8_E5M2 = 3,
+  GEMM_F32 = 4
+} gemm_dtype;
+
+/* Output-tile shapes (rows x columns of C per workgroup).  All tiles of one
+ * input dtype use the same matrix-core instruction and the same K order, so
+ * for a fixed split of K they produce identical bits; the choice only moves
+ * work in space. */
+typedef enum {
+  GEMM_TILE_DEFAULT = 0,  /* chosen from (N, K, dtype) */
+  GEMM_TILE_256x256 = 1,
+  GEMM_TILE_128x128 = 2,
+  GEMM_TILE_32x128 = 3
+} gemm_tile;
+
+typedef struct gemm_plan_s* gemm_plan_t;
+
+typedef struct {
+  int64_t M, N, K;
+  int32_t in_dtype, out_dtype;  /* gemm_dtype values */
+  int32_t tile;                 /* gemm_tile value actually used */
+  int32_t block_m, block_n;     /* output tile */
+  int32_t block_k;              /* K elements staged per main-loop step */
+  int32_t mfma_m, mfma_n, mfma_k; /* matrix-core instruction shape */
+  int32_t waves;                /* 64-lane wavefronts per workgroup */
+  int32_t group_m;              /* GROUP_M of the tile raster */
+  int32_t split_k;              /* K slices used by gemm_splitk_run */
+  int64_t k_per_split;          /* K elements per slice (multiple of block_k) */
+  int64_t tiles_m, tiles_n;     /* output tiles along M and N */
+  int64_t grid_run;             /* workgroups launched by gemm_run */
+  int64_t grid_splitk;          /* workgroups of the split-K partial kernel */
+  uint64_t workspace_bytes;     /* split_k * M * N * 4 */
+  float scale_a, scale_b;
+} gemm_plan_info_t;
+
+/* Plan C[M,N] = A[M,K] x B[K,N] with default options: fp32 output for fp16 /
+ * bf16 inputs and bf16 output for fp8 inputs, split and tile chosen from
+ * (N, K, dtype), GROUP_M = 8, scales 1.0.  M only sizes the grid and the
+ * workspace.  On success *out receives a new plan. */
+gemm_status gemm_plan(int64_t M, int64_t N, int64_t K, gemm_dtype in, gemm_plan_t* out);
+
+/* As gemm_plan with explicit options.  out_dtype: GEMM_F32 or GEMM_BF16.
+ * split_k: 0 = default, else 1..4096 (the slice length is rounded up to a
+ * multiple of block_k; the split actually used is reported by
+ * gemm_plan_info).  group_m: 0 = default (8), else >= 1.  tile: a gemm_tile
+ * value.  scale_a, scale_b: per-tensor scales multiplied into the result
+ * (their fp32 product is applied to the fp32 sum before the output
+ * conversion); must be finite. */
+gemm_status gemm_plan_ex(int64_t M, int64_t N, int64_t K, gemm_dtype in, gemm_dtype out,
+                         int split_k, int group_m, int tile, float scale_a, float scale_b,
+                         gemm_plan_t* plan);
+
+gemm_status gemm_plan_info(gemm_plan_t plan, gemm_plan_info_t* info);
+
+/* Bytes of workspace gemm_splitk_run needs: split_k * M * N * sizeof(float). */
+size_t gemm_workspace_size(gemm_plan_t plan);
+
+/* Tile raster: the (k_slice, pid_m, pid_n) that workgroup `workgroup` of the
+ * split-K partial kernel computes (k_slice is 0 for gemm_run's grid).  Pure
+ * host function, exposed so the raster can be checked to be a bijection. */
+gemm_status gemm_plan_tile_of(gemm_plan_t plan, int64_t workgroup, int64_t* k_slice,
+                              int64_t* pid_m, int64_t* pid_n);
+
+/* C = A x B in one pass: one workgroup per output tile, full K in order. */
+gemm_status gemm_run(gemm_plan_t plan, const void* A, const void* B, void* C, void* stream);
+
+/* C = A x B through the split-K workspace: the partial kernel writes slice s
+ * of K to workspace[s, :, :] (fp32, no atomics), then a reduction kernel sums
+ * the slices in ascending s and writes C.  With split_k == 1 the result is
+ * bitwise identical to gemm_run. */
+gemm_status gemm_splitk_run(gemm_plan_t plan, const void* A, const void* B, void* C,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+void gemm_plan_destroy(gemm_plan_t plan);
+
+const char* gemm_status_string(gemm_status status);
+
+/* HIP error code (hipError_t as int) of the most recent GEMM_ERR_HIP return on
+ * this host thread, 0 if none. */
+int gemm_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* INVARIANT_MATMUL_H */

@@ -1,0 +1,260 @@
+"""Python binding of the batch-invariant GEMM library (libinvariant_matmul.so).
+
+Argument marshalling only: every step of the product runs in the library's
+HIP kernels.  PyTorch supplies device memory and streams.  The calls mirror
+the C ABI in include/invariant_matmul.h:
+
+    plan = gemm_plan(M, N, K, "f16")                  # pure host call
+    gemm_run(plan, A, B, C)                           # C = A @ B
+    gemm_splitk_run(plan, A, B, C, workspace)         # split-K path
+
+A, B, C, workspace are CUDA(HIP) tensors (or raw device addresses as ints);
+``stream`` defaults to torch's current stream on the operands' device.  There
+is no fallback: if the shared library is missing, importing it raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "GemmError", "Plan", "PlanInfo", "gemm_plan", "gemm_plan_ex", "gemm_plan_info",
+    "gemm_workspace_size", "gemm_plan_tile_of", "gemm_run", "gemm_splitk_run",
+    "gemm_plan_destroy", "gemm_status_string", "gemm_last_hip_error", "mm", "lib", "LIB_PATH",
+    "DTYPE", "TILE", "STATUS", "EXPORTED_SYMBOLS",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libinvariant_matmul.so")
+
+STATUS = {0: "GEMM_OK", 1: "GEMM_ERR_INVALID_VALUE", 2: "GEMM_ERR_UNSUPPORTED",
+          3: "GEMM_ERR_WORKSPACE", 4: "GEMM_ERR_HIP"}
+DTYPE = {"f16": 0, "bf16": 1, "e4m3": 2, "e5m2": 3, "f32": 4}
+TILE = {"default": 0, "256x256": 1, "128x128": 2, "32x128": 3}
+EXPORTED_SYMBOLS = (
+    "gemm_plan", "gemm_plan_ex", "gemm_plan_info", "gemm_workspace_size", "gemm_plan_tile_of",
+    "gemm_run", "gemm_splitk_run", "gemm_plan_destroy", "gemm_status_string",
+    "gemm_last_hip_error",
+)
+
+
+class GemmError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        name = STATUS.get(status, f"status {status}")
+        msg = f"{where}: {name}"
+        if status == 4:
+            msg += f" (hip error {lib().gemm_last_hip_error()})"
+        super().__init__(msg)
+
+
+class PlanInfo(ctypes.Structure):
+    _fields_ = [
+        ("M", ctypes.c_int64), ("N", ctypes.c_int64), ("K", ctypes.c_int64),
+        ("in_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32), ("tile", ctypes.c_int32),
+        ("block_m", ctypes.c_int32), ("block_n", ctypes.c_int32), ("block_k", ctypes.c_int32),
+        ("mfma_m", ctypes.c_int32), ("mfma_n", ctypes.c_int32), ("mfma_k", ctypes.c_int32),
+        ("waves", ctypes.c_int32), ("group_m", ctypes.c_int32), ("split_k", ctypes.c_int32),
+        ("k_per_split", ctypes.c_int64), ("tiles_m", ctypes.c_int64), ("tiles_n", ctypes.c_int64),
+        ("grid_run", ctypes.c_int64), ("grid_splitk", ctypes.c_int64),
+        ("workspace_bytes", ctypes.c_uint64), ("scale_a", ctypes.c_float),
+        ("scale_b", ctypes.c_float),
+    ]
+
+    def as_dict(self):
+        return {name: getattr(self, name) for name, _ in self._fields_}
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded shared library (loaded on first use; raises if it is not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is not built; run `python -m invariant_matmul_amd.build` "
+                "(there is no fallback implementation)")
+        L = ctypes.CDLL(LIB_PATH)
+        i64, i32, vp, f32 = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_float
+        pp = ctypes.POINTER(ctypes.c_void_p)
+        L.gemm_plan.argtypes = [i64, i64, i64, i32, pp]
+        L.gemm_plan_ex.argtypes = [i64, i64, i64, i32, i32, i32, i32, i32, f32, f32, pp]
+        L.gemm_plan_info.argtypes = [vp, ctypes.POINTER(PlanInfo)]
+        L.gemm_workspace_size.argtypes = [vp]
+        L.gemm_workspace_size.restype = ctypes.c_size_t
+        p64 = ctypes.POINTER(ctypes.c_int64)
+        L.gemm_plan_tile_of.argtypes = [vp, i64, p64, p64, p64]
+        L.gemm_run.argtypes = [vp, vp, vp, vp, vp]
+        L.gemm_splitk_run.argtypes = [vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+        L.gemm_plan_destroy.argtypes = [vp]
+        L.gemm_plan_destroy.restype = None
+        L.gemm_status_string.argtypes = [i32]
+        L.gemm_status_string.restype = ctypes.c_char_p
+        L.gemm_last_hip_error.argtypes = []
+        for f in ("gemm_plan", "gemm_plan_ex", "gemm_plan_info", "gemm_plan_tile_of",
+                  "gemm_run", "gemm_splitk_run", "gemm_last_hip_error"):
+            getattr(L, f).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _dtype_code(dt) -> int:
+    if isinstance(dt, int):
+        return dt
+    if isinstance(dt, str):
+        return DTYPE[dt]
+    import torch
+    m = {torch.float16: 0, torch.bfloat16: 1, torch.float8_e4m3fn: 2, torch.float8_e5m2: 3,
+         torch.float32: 4}
+    return m[dt]
+
+
+class Plan:
+    """Owns a gemm_plan_t; destroyed with the object."""
+
+    def __init__(self, handle: int):
+        self.handle = handle
+        self._lib = lib()
+
+    def __del__(self):
+        h, self.handle = getattr(self, "handle", None), None
+        if h:
+            self._lib.gemm_plan_destroy(h)
+
+    @property
+    def info(self) -> dict:
+        return gemm_plan_info(self)
+
+    @property
+    def workspace_bytes(self) -> int:
+        return gemm_workspace_size(self)
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise GemmError(status, where)
+
+
+def gemm_plan(M: int, N: int, K: int, dtype) -> Plan:
+    h = ctypes.c_void_p()
+    _check(lib().gemm_plan(M, N, K, _dtype_code(dtype), ctypes.byref(h)), "gemm_plan")
+    return Plan(h.value)
+
+
+def gemm_plan_ex(M: int, N: int, K: int, dtype, out_dtype="f32", split_k: int = 0,
+                 group_m: int = 0, tile="default", scale_a: float = 1.0,
+                 scale_b: float = 1.0) -> Plan:
+    h = ctypes.c_void_p()
+    t = TILE[tile] if isinstance(tile, str) else int(tile)
+    _check(lib().gemm_plan_ex(M, N, K, _dtype_code(dtype), _dtype_code(out_dtype), split_k,
+                              group_m, t, scale_a, scale_b, ctypes.byref(h)), "gemm_plan_ex")
+    return Plan(h.value)
+
+
+def gemm_plan_info(plan: Plan) -> dict:
+    info = PlanInfo()
+    _check(lib().gemm_plan_info(plan.handle, ctypes.byref(info)), "gemm_plan_info")
+    return info.as_dict()
+
+
+def gemm_workspace_size(plan: Plan) -> int:
+    return int(lib().gemm_workspace_size(plan.handle))
+
+
+def gemm_plan_tile_of(plan: Plan, workgroup: int):
+    s, m, n = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+    _check(lib().gemm_plan_tile_of(plan.handle, workgroup, ctypes.byref(s), ctypes.byref(m),
+                                   ctypes.byref(n)), "gemm_plan_tile_of")
+    return s.value, m.value, n.value
+
+
+def _addr(x) -> int:
+    if x is None:
+        return 0
+    if isinstance(x, int):
+        return x
+    return int(x.data_ptr())
+
+
+def _stream(stream, *tensors):
+    if stream is not None:
+        return stream if isinstance(stream, int) else int(stream.cuda_stream)
+    for t in tensors:
+        if t is not None and not isinstance(t, int) and t.is_cuda:
+            import torch
+            return int(torch.cuda.current_stream(t.device).cuda_stream)
+    return 0
+
+
+def _check_tensor(t, name, dtype_code, numel):
+    if t is None or isinstance(t, int):
+        return
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if _dtype_code(t.dtype) != dtype_code:
+        raise ValueError(f"{name} has dtype {t.dtype}, plan expects code {dtype_code}")
+    if t.numel() != numel:
+        raise ValueError(f"{name} has {t.numel()} elements, plan expects {numel}")
+
+
+def _check_operands(plan: Plan, A, B, C):
+    i = gemm_plan_info(plan)
+    _check_tensor(A, "A", i["in_dtype"], i["M"] * i["K"])
+    _check_tensor(B, "B", i["in_dtype"], i["K"] * i["N"])
+    _check_tensor(C, "C", i["out_dtype"], i["M"] * i["N"])
+
+
+def gemm_run(plan: Plan, A, B, C, stream=None) -> None:
+    _check_operands(plan, A, B, C)
+    _check(lib().gemm_run(plan.handle, _addr(A), _addr(B), _addr(C), _stream(stream, A, B, C)),
+           "gemm_run")
+
+
+def gemm_splitk_run(plan: Plan, A, B, C, workspace, stream=None, workspace_bytes=None) -> None:
+    _check_operands(plan, A, B, C)
+    if workspace_bytes is None:
+        workspace_bytes = 0 if workspace is None or isinstance(workspace, int) else (
+            workspace.numel() * workspace.element_size())
+    _check(lib().gemm_splitk_run(plan.handle, _addr(A), _addr(B), _addr(C), _addr(workspace),
+                                 int(workspace_bytes), _stream(stream, A, B, C)),
+           "gemm_splitk_run")
+
+
+def gemm_plan_destroy(plan: Plan) -> None:
+    h, plan.handle = plan.handle, None
+    if h:
+        lib().gemm_plan_destroy(h)
+
+
+def gemm_status_string(status: int) -> str:
+    return lib().gemm_status_string(status).decode()
+
+
+def gemm_last_hip_error() -> int:
+    return int(lib().gemm_last_hip_error())
+
+
+def mm(A, B, out_dtype=None, split_k=None, plan: Plan | None = None, stream=None):
+    """C = A @ B through the library, allocating C (and a workspace) with torch.
+
+    split_k=None uses gemm_run; an int (0 = the plan's default) uses the split-K
+    path.  The plan is made from (N, K, dtype) options only, never from M.
+    """
+    import torch
+    M, K = A.shape
+    N = B.shape[1]
+    if plan is None:
+        od = out_dtype if out_dtype is not None else (
+            "bf16" if A.dtype in (torch.float8_e4m3fn, torch.float8_e5m2) else "f32")
+        plan = gemm_plan_ex(M, N, K, A.dtype, od, split_k=split_k or 0)
+    info = gemm_plan_info(plan)
+    out_t = torch.float32 if info["out_dtype"] == DTYPE["f32"] else torch.bfloat16
+    C = torch.empty((M, N), dtype=out_t, device=A.device)
+    if split_k is None:
+        gemm_run(plan, A, B, C, stream)
+    else:
+        ws = torch.empty(max(1, gemm_workspace_size(plan) // 4), dtype=torch.float32,
+                         device=A.device)
+        gemm_splitk_run(plan, A, B, C, ws, stream)
+    return C

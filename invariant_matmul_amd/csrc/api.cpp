@@ -1,0 +1,265 @@
+// Host side of the C ABI: planning, argument validation, launches.
+//
+// Citations: [TDI] = Tencent engineer article on deterministic LLM inference
+// ("AI インフラの深化：大規模モデルに確定的な出力を実現する方法").
+//
+// The plan is a pure function of (N, K, input dtype, output dtype, explicit
+// options).  M is stored only to size the grid and the workspace.  [TDI]
+// "Batch Invariance の由来" concludes that a configuration which changes the
+// K step or the split of K with the batch size is what breaks batch
+// invariance, and [TDI] "演算子チューニング" describes exactly such M-driven
+// tile and split heuristics; this planner never reads M for any decision.
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cmath>
+#include <cstring>
+#include <new>
+
+#include "imm_internal.h"
+
+using namespace imm;
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+// Number of workgroups the split heuristic aims for per output-tile row: two
+// per compute unit of a 256-CU MI355X.  A constant, not a device query, so a
+// plan (and therefore the bits) never depends on the machine it was made on.
+constexpr int64_t kTargetWorkgroups = 512;
+constexpr int kMaxSplit = 4096;
+
+bool valid_in(int dt) {
+  return dt == GEMM_F16 || dt == GEMM_BF16 || dt == GEMM_F8_E4M3 || dt == GEMM_F8_E5M2;
+}
+bool valid_out(int dt) { return dt == GEMM_F32 || dt == GEMM_BF16; }
+
+void tile_shape(int tile, int* bm, int* bn, int* wm, int* wn) {
+  switch (tile) {
+    case GEMM_TILE_256x256: *bm = 256; *bn = 256; *wm = 2; *wn = 4; break;
+    case GEMM_TILE_128x128: *bm = 128; *bn = 128; *wm = 2; *wn = 2; break;
+    default: *bm = 32; *bn = 128; *wm = 1; *wn = 4; break;  // GEMM_TILE_32x128
+  }
+}
+
+// Reduction-dominated shapes (K at least twice N): the regime where the
+// output has few tiles and split-K is the tool ([TDI] "Split-K": tiny M x N,
+// huge K; the parameter table restricts SPLIT_K to such shapes).  These get
+// the narrow 32-row tile; the rest get the large tile.
+bool reduction_dominated(int64_t N, int64_t K) { return K >= 2 * N; }
+
+int default_tile(int64_t N, int64_t K) {
+  return reduction_dominated(N, K) ? GEMM_TILE_32x128 : GEMM_TILE_256x256;
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Default split: only for reduction-dominated shapes; the largest power of two
+// that brings one tile-row of the grid to about kTargetWorkgroups while every
+// slice keeps at least 4 main-loop steps.
+int default_split(int64_t N, int64_t K, int bn, int bk) {
+  if (!reduction_dominated(N, K)) return 1;
+  const int64_t tiles_n = ceil_div(N, bn);
+  const int64_t steps = ceil_div(K, bk);
+  int s = 1;
+  while (s * 2 <= kMaxSplit && tiles_n * s * 2 <= kTargetWorkgroups && steps / (s * 2) >= 4) s *= 2;
+  return s;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+gemm_status hip_fail(hipError_t e) {
+  g_last_hip_error = (int)e;
+  return GEMM_ERR_HIP;
+}
+
+// 0 if a HIP device is usable from this thread, else the HIP error.
+hipError_t device_ready() {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  int n = 0;
+  e = hipGetDeviceCount(&n);
+  if (e != hipSuccess) return e;
+  return n > 0 ? hipSuccess : hipErrorNoDevice;
+}
+
+gemm_status check_operands(const gemm_plan_s* p, const void* A, const void* B, const void* C) {
+  if (!p) return GEMM_ERR_INVALID_VALUE;
+  if (p->M == 0 || p->N == 0) return GEMM_OK;
+  if (!C || !aligned16(C)) return GEMM_ERR_INVALID_VALUE;
+  if (p->K > 0) {
+    if (!A || !B || !aligned16(A) || !aligned16(B)) return GEMM_ERR_INVALID_VALUE;
+  }
+  return GEMM_OK;
+}
+
+GemmArgs make_args(const gemm_plan_s* p, const void* A, const void* B, void* out, bool split) {
+  GemmArgs a;
+  a.A = A;
+  a.B = B;
+  a.C = out;
+  a.M = p->M;
+  a.N = p->N;
+  a.K = p->K;
+  a.k_per_split = split ? p->k_per_split : (p->K > 0 ? p->K : p->bk);
+  a.tiles_m = p->tiles_m;
+  a.tiles_n = p->tiles_n;
+  a.grid = p->tiles_m * p->tiles_n * (split ? p->split_k : 1);
+  a.group_m = p->group_m;
+  a.scale = p->scale;
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+gemm_status gemm_plan_ex(int64_t M, int64_t N, int64_t K, gemm_dtype in, gemm_dtype out,
+                         int split_k, int group_m, int tile, float scale_a, float scale_b,
+                         gemm_plan_t* plan) {
+  if (!plan) return GEMM_ERR_INVALID_VALUE;
+  *plan = nullptr;
+  if (M < 0 || N < 0 || K < 0) return GEMM_ERR_INVALID_VALUE;
+  if (M > INT_MAX || N > INT_MAX || K > INT_MAX) return GEMM_ERR_UNSUPPORTED;
+  if (!valid_in(in) || !valid_out(out)) return GEMM_ERR_UNSUPPORTED;
+  if (split_k < 0 || split_k > kMaxSplit || group_m < 0) return GEMM_ERR_UNSUPPORTED;
+  if (tile < GEMM_TILE_DEFAULT || tile > GEMM_TILE_32x128) return GEMM_ERR_UNSUPPORTED;
+  if (!std::isfinite(scale_a) || !std::isfinite(scale_b)) return GEMM_ERR_UNSUPPORTED;
+  // 16-byte vector access of every row of A and B needs K and N to be
+  // multiples of 16 bytes' worth of elements.
+  const int eb = elem_bytes(in);
+  const int vec = 16 / eb;
+  if (K % vec != 0 || N % vec != 0) return GEMM_ERR_UNSUPPORTED;
+
+  gemm_plan_s* p = new (std::nothrow) gemm_plan_s();
+  if (!p) return GEMM_ERR_INVALID_VALUE;
+  p->M = M;
+  p->N = N;
+  p->K = K;
+  p->in = in;
+  p->out = out;
+  p->tile = tile == GEMM_TILE_DEFAULT ? default_tile(N, K) : tile;
+  tile_shape(p->tile, &p->bm, &p->bn, &p->waves_m, &p->waves_n);
+  p->bk = block_k_elems(in);
+  p->group_m = group_m == 0 ? 8 : group_m;
+  const int64_t steps = ceil_div(K, p->bk);
+  int s = split_k == 0 ? default_split(N, K, p->bn, p->bk) : split_k;
+  // Slices are contiguous, equal multiples of bk ([TDI] "Split-K" leaves the
+  // segment boundaries open; this is the plain reading).  Drop trailing empty
+  // slices so every slice has work.
+  int64_t steps_per = steps > 0 ? ceil_div(steps, s) : 1;
+  if (steps > 0) s = (int)ceil_div(steps, steps_per);
+  p->split_k = s;
+  p->k_per_split = steps_per * p->bk;
+  p->tiles_m = ceil_div(M, p->bm);
+  p->tiles_n = ceil_div(N, p->bn);
+  p->scale_a = scale_a;
+  p->scale_b = scale_b;
+  p->scale = (float)((double)scale_a * (double)scale_b);
+  const int64_t threads = (int64_t)p->waves_m * p->waves_n * 64;
+  if (p->tiles_m * p->tiles_n * p->split_k * threads >= ((int64_t)1 << 32)) {
+    delete p;
+    return GEMM_ERR_UNSUPPORTED;
+  }
+  *plan = p;
+  return GEMM_OK;
+}
+
+gemm_status gemm_plan(int64_t M, int64_t N, int64_t K, gemm_dtype in, gemm_plan_t* out) {
+  const gemm_dtype od = (in == GEMM_F8_E4M3 || in == GEMM_F8_E5M2) ? GEMM_BF16 : GEMM_F32;
+  return gemm_plan_ex(M, N, K, in, od, 0, 0, GEMM_TILE_DEFAULT, 1.0f, 1.0f, out);
+}
+
+gemm_status gemm_plan_info(gemm_plan_t p, gemm_plan_info_t* info) {
+  if (!p || !info) return GEMM_ERR_INVALID_VALUE;
+  std::memset(info, 0, sizeof(*info));
+  info->M = p->M;
+  info->N = p->N;
+  info->K = p->K;
+  info->in_dtype = p->in;
+  info->out_dtype = p->out;
+  info->tile = p->tile;
+  info->block_m = p->bm;
+  info->block_n = p->bn;
+  info->block_k = p->bk;
+  info->mfma_m = 32;
+  info->mfma_n = 32;
+  info->mfma_k = mfma_k(p->in);
+  info->waves = p->waves_m * p->waves_n;
+  info->group_m = p->group_m;
+  info->split_k = p->split_k;
+  info->k_per_split = p->k_per_split;
+  info->tiles_m = p->tiles_m;
+  info->tiles_n = p->tiles_n;
+  info->grid_run = p->tiles_m * p->tiles_n;
+  info->grid_splitk = p->tiles_m * p->tiles_n * p->split_k;
+  info->workspace_bytes = gemm_workspace_size(p);
+  info->scale_a = p->scale_a;
+  info->scale_b = p->scale_b;
+  return GEMM_OK;
+}
+
+size_t gemm_workspace_size(gemm_plan_t p) {
+  if (!p) return 0;
+  return (size_t)p->split_k * (size_t)p->M * (size_t)p->N * sizeof(float);
+}
+
+gemm_status gemm_plan_tile_of(gemm_plan_t p, int64_t w, int64_t* k_slice, int64_t* pid_m,
+                              int64_t* pid_n) {
+  if (!p || !k_slice || !pid_m || !pid_n) return GEMM_ERR_INVALID_VALUE;
+  const int64_t G = p->tiles_m * p->tiles_n * p->split_k;
+  if (w < 0 || w >= G) return GEMM_ERR_INVALID_VALUE;
+  raster_tile(w, G, p->tiles_m, p->tiles_n, p->group_m, k_slice, pid_m, pid_n);
+  return GEMM_OK;
+}
+
+gemm_status gemm_run(gemm_plan_t p, const void* A, const void* B, void* C, void* stream) {
+  gemm_status st = check_operands(p, A, B, C);
+  if (st != GEMM_OK || p->M == 0 || p->N == 0) return st;
+  hipError_t e = device_ready();
+  if (e != hipSuccess) return hip_fail(e);
+  e = launch_gemm(*p, make_args(p, A, B, C, false), false, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e);
+  return GEMM_OK;
+}
+
+gemm_status gemm_splitk_run(gemm_plan_t p, const void* A, const void* B, void* C,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  gemm_status st = check_operands(p, A, B, C);
+  if (st != GEMM_OK || p->M == 0 || p->N == 0) return st;
+  if (!workspace || workspace_bytes < gemm_workspace_size(p)) return GEMM_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return GEMM_ERR_INVALID_VALUE;
+  hipError_t e = device_ready();
+  if (e != hipSuccess) return hip_fail(e);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  e = launch_gemm(*p, make_args(p, A, B, workspace, true), true, s);
+  if (e != hipSuccess) return hip_fail(e);
+  ReduceArgs r;
+  r.ws = static_cast<const float*>(workspace);
+  r.C = C;
+  r.MN = p->M * p->N;
+  r.split_k = p->split_k;
+  r.scale = p->scale;
+  e = launch_reduce(*p, r, s);
+  if (e != hipSuccess) return hip_fail(e);
+  return GEMM_OK;
+}
+
+void gemm_plan_destroy(gemm_plan_t p) { delete p; }
+
+const char* gemm_status_string(gemm_status s) {
+  switch (s) {
+    case GEMM_OK: return "GEMM_OK";
+    case GEMM_ERR_INVALID_VALUE: return "GEMM_ERR_INVALID_VALUE";
+    case GEMM_ERR_UNSUPPORTED: return "GEMM_ERR_UNSUPPORTED";
+    case GEMM_ERR_WORKSPACE: return "GEMM_ERR_WORKSPACE";
+    case GEMM_ERR_HIP: return "GEMM_ERR_HIP";
+    default: return "GEMM_ERR_UNKNOWN";
+  }
+}
+
+int gemm_last_hip_error(void) { return g_last_hip_error; }
+
+}  // extern "C"

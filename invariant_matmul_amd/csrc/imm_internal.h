@@ -1,0 +1,107 @@
+// Internal declarations shared by the host library (api.cpp) and the kernels.
+//
+// Citations: [TDI] = Tencent engineer article on deterministic LLM inference
+// ("AI インフラの深化：大規模モデルに確定的な出力を実現する方法").
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "invariant_matmul.h"
+
+namespace imm {
+
+// Static description of one tile configuration.  Every configuration of an
+// input dtype uses the same matrix-core instruction (32x32 output block; K of
+// 16 for 16-bit inputs, 64 for fp8) and walks K in ascending order in steps of
+// that instruction, so configurations differ only in how output elements are
+// spread over workgroups and waves -- which [TDI] "Batch Invariance の由来"
+// (BLOCK_M / BLOCK_N, num_warps paragraphs) shows has no effect on bits.
+struct TileCfg {
+  int tile;     // gemm_tile
+  int bm, bn;   // output tile
+  int waves_m, waves_n;
+};
+
+// Bytes of K staged per main-loop step: 64 fp16/bf16 elements or 128 fp8.
+constexpr int kTileKBytes = 128;
+
+inline int elem_bytes(int dt) { return (dt == GEMM_F8_E4M3 || dt == GEMM_F8_E5M2) ? 1 : 2; }
+inline int block_k_elems(int dt) { return kTileKBytes / elem_bytes(dt); }
+inline int mfma_k(int dt) { return elem_bytes(dt) == 1 ? 64 : 16; }
+
+}  // namespace imm
+
+struct gemm_plan_s {
+  int64_t M, N, K;
+  int in, out;
+  int tile;             // gemm_tile actually used
+  int bm, bn, bk;       // bk in elements
+  int waves_m, waves_n;
+  int group_m;
+  int split_k;          // slices actually used (after rounding)
+  int64_t k_per_split;  // elements, multiple of bk
+  int64_t tiles_m, tiles_n;
+  float scale_a, scale_b;
+  float scale;          // fp32 product applied in the epilogue
+};
+
+namespace imm {
+
+// Workgroup -> (k_slice, pid_m, pid_n).
+//
+// Step 1 (XCD remap): the dispatcher hands workgroup w to XCD w % 8, and each
+// XCD has its own L2.  Renumber so that every XCD works on one contiguous run
+// of logical ids, so tiles that share A rows / B columns share one L2.
+// Step 2: the K slice is the slowest-moving coordinate.
+// Step 3 (GROUP_M, [TDI] "GROUP_M - Swizzle L2 Cache"): within a slice, tiles
+// are taken group_m rows of tiles at a time, column by column, so that
+// consecutive workgroups reuse the same A rows and B columns from L2.
+// Every step is a bijection of [0, G); none of them affects any bit of C.
+__host__ __device__ inline void raster_tile(int64_t w, int64_t G, int64_t tiles_m,
+                                            int64_t tiles_n, int64_t group_m,
+                                            int64_t* k_slice, int64_t* pid_m,
+                                            int64_t* pid_n) {
+  const int64_t per = G / 8, rem = G % 8;
+  const int64_t x = w % 8, loc = w / 8;
+  const int64_t logical = (x < rem) ? x * (per + 1) + loc : rem * (per + 1) + (x - rem) * per + loc;
+  const int64_t tiles = tiles_m * tiles_n;
+  *k_slice = logical / tiles;
+  const int64_t t = logical % tiles;
+  const int64_t width = group_m * tiles_n;
+  const int64_t first_m = (t / width) * group_m;
+  const int64_t rows_left = tiles_m - first_m;
+  const int64_t gm = rows_left < group_m ? rows_left : group_m;
+  const int64_t in_group = t % width;
+  *pid_m = first_m + in_group % gm;
+  *pid_n = in_group / gm;
+}
+
+// Kernel arguments (passed by value).
+struct GemmArgs {
+  const void* A;
+  const void* B;
+  void* C;              // output (store-C mode) or workspace (slice mode)
+  int64_t M, N, K;
+  int64_t k_per_split;  // elements per K slice (K itself when not split)
+  int64_t tiles_m, tiles_n;
+  int64_t grid;         // total workgroups
+  int64_t group_m;
+  float scale;
+};
+
+struct ReduceArgs {
+  const float* ws;
+  void* C;
+  int64_t MN;           // M * N
+  int split_k;
+  float scale;
+};
+
+// Launchers (gemm_kernels.hip).  They only enqueue; they return the launch
+// status.  `slice_mode` selects the split-K partial kernel (fp32 workspace
+// output, raw sums, no scale) instead of the final store.
+hipError_t launch_gemm(const gemm_plan_s& p, const GemmArgs& a, bool slice_mode, hipStream_t s);
+hipError_t launch_reduce(const gemm_plan_s& p, const ReduceArgs& a, hipStream_t s);
+
+}  // namespace imm

@@ -1,0 +1,88 @@
+"""Shared helpers for the GPU tests: run the library, fetch bits, check bounds.
+
+The error bound for fp32 output is the one the deterministic-GEMM target
+fixes: |C - C_ref| <= K * 2^-24 * (|A||B|)_ij, with C_ref the exact (fp64)
+product.  For bf16 output it adds the final rounding to bf16 (unit roundoff
+2^-8): K u (|A||B|)(1 + 2^-8) + 2^-8 |C_ref|.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import invariant_matmul_amd as imm
+import oracle
+import workloads as wl
+
+U32 = 2.0 ** -24
+U_BF16 = 2.0 ** -8
+
+
+def log(msg: str) -> None:
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def dev():
+    return torch.device("cuda:0")
+
+
+def out_torch_dtype(code: int):
+    return torch.float32 if code == imm.DTYPE["f32"] else torch.bfloat16
+
+
+def run(plan, A, B, split: bool, stream=None):
+    """Run the plan on device tensors A, B; returns the device output."""
+    info = plan.info
+    C = torch.empty((info["M"], info["N"]), dtype=out_torch_dtype(info["out_dtype"]),
+                    device=A.device)
+    if split:
+        ws = torch.empty(max(1, imm.gemm_workspace_size(plan) // 4), dtype=torch.float32,
+                         device=A.device)
+        imm.gemm_splitk_run(plan, A, B, C, ws, stream)
+    else:
+        imm.gemm_run(plan, A, B, C, stream)
+    return C
+
+
+def bits_of(C: torch.Tensor) -> np.ndarray:
+    """Raw output bits on the host (uint32 for fp32, uint16 for bf16)."""
+    torch.cuda.synchronize()
+    return wl.bits(C.cpu())
+
+
+def values_of(C: torch.Tensor) -> np.ndarray:
+    torch.cuda.synchronize()
+    return C.cpu().to(torch.float64).numpy()
+
+
+def expected_bits(C64: np.ndarray, out: str) -> np.ndarray:
+    return oracle.round_rne(out, C64)
+
+
+def bound(K: int, C64: np.ndarray, Cabs: np.ndarray, out: str) -> np.ndarray:
+    b = K * U32 * Cabs
+    if out == "bf16":
+        b = b * (1.0 + U_BF16) + U_BF16 * np.abs(C64)
+    return b
+
+
+def check_bound(C: np.ndarray, C64: np.ndarray, Cabs: np.ndarray, K: int, out: str) -> float:
+    """Assert every element is within the bound; returns max |err| / bound."""
+    err = np.abs(C - C64)
+    b = bound(K, C64, Cabs, out)
+    bad = err > b
+    if bad.any():
+        idx = np.argwhere(bad)[:5]
+        raise AssertionError(
+            f"{int(bad.sum())} elements outside the bound; first {idx.tolist()}: "
+            f"got {C[bad][:5]}, want {C64[bad][:5]}, bound {b[bad][:5]}")
+    with np.errstate(divide="ignore", invalid="ignore"):
+        r = np.where(b > 0, err / b, 0.0)
+    return float(r.max()) if r.size else 0.0
+
+
+def dtype_name(code: int) -> str:
+    return {v: k for k, v in imm.DTYPE.items()}[code]

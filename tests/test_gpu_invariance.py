@@ -1,0 +1,180 @@
+"""GPU batch invariance and run-to-run determinism, bit for bit.
+
+The Tencent deterministic-inference article (sections "背景" and "Batch
+Invariance の由来") separates run-to-run determinism (the same request alone,
+repeated) from batch invariance (the same request while other rows share the
+batch), and shows which GEMM parameters may change bits: BLOCK_M/BLOCK_N,
+GROUP_M, num_warps and pipelining may not; the K step and the split of K do.
+These tests pin each of those statements on the hardware:
+
+- rows are identical across M (row prefixes), under row permutations, and
+  when other rows hold different data;
+- repeats, other streams and concurrently running work change nothing;
+- GROUP_M and the tile shape change nothing (same instruction, same K order);
+- gemm_splitk_run with one slice equals gemm_run;
+- a different split of K may change bits on random inputs, never on exact ones.
+"""
+import numpy as np
+import pytest
+import torch
+
+import invariant_matmul_amd as imm
+import workloads as wl
+from tests.helpers import bits_of, dev, log, run
+
+pytestmark = pytest.mark.gpu
+
+TILES = ["256x256", "128x128", "32x128"]
+
+
+def _to_dev(*ts):
+    return [t.to(dev()) for t in ts]
+
+
+def _rand(M, N, K, dt, seed):
+    g = wl.gen(seed)
+    if dt in ("e4m3", "e5m2"):
+        return wl.normal((M, K), dt, g), wl.normal((K, N), dt, g)
+    return wl.uniform((M, K), dt, g), wl.uniform((K, N), dt, g)
+
+
+def test_decode_rows_identical_across_M():
+    w = wl.WORKLOADS["decode_bf16_m128"]
+    A, B = w.make()
+    Ad, Bd = _to_dev(A, B)
+    full = None
+    for m in (128, 32, 8, 1):
+        plan = imm.gemm_plan(m, w.N, w.K, "bf16")
+        C = bits_of(run(plan, Ad[:m].contiguous(), Bd, True))
+        if full is None:
+            full = C
+        log(f"decode M={m}: split {plan.info['split_k']}")
+        assert np.array_equal(C, full[:m]), m
+
+
+def test_exact256_slices():
+    w = wl.WORKLOADS["exact256"]
+    A, B = w.make()
+    Ad, Bd = _to_dev(A, B)
+    full = bits_of(run(imm.gemm_plan(256, 256, 256, "f16"), Ad, Bd, False))
+    for m in w.m_slices:
+        C = bits_of(run(imm.gemm_plan(m, 256, 256, "f16"), Ad[:m].contiguous(), Bd, False))
+        assert np.array_equal(C, full[:m]), m
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16", "e4m3", "e5m2"])
+@pytest.mark.parametrize("split", [None, 4])
+def test_random_rows_identical_across_M(dt, split):
+    N, K = 512, 2048
+    A, B = _rand(1000, N, K, dt, 8000)
+    Ad, Bd = _to_dev(A, B)
+    plan = lambda m: imm.gemm_plan_ex(m, N, K, dt, "f32", split_k=split or 0)
+    full = bits_of(run(plan(1000), Ad, Bd, split is not None))
+    for m in (1, 2, 31, 33, 255, 257, 999):
+        C = bits_of(run(plan(m), Ad[:m].contiguous(), Bd, split is not None))
+        assert np.array_equal(C, full[:m]), (dt, split, m)
+
+
+def test_row_depends_only_on_its_own_row():
+    # Permute rows and replace every other row with fresh data: the surviving
+    # rows must come out with the same bits wherever they land.
+    N, K, M = 384, 1024, 700
+    A, B = _rand(M, N, K, "bf16", 8100)
+    Ad, Bd = _to_dev(A, B)
+    for tile in TILES:
+        plan = imm.gemm_plan_ex(M, N, K, "bf16", "f32", tile=tile, split_k=2)
+        for split in (False, True):
+            base = bits_of(run(plan, Ad, Bd, split))
+            perm = torch.randperm(M, generator=wl.gen(8101))
+            noise = wl.uniform((M, K), "bf16", wl.gen(8102))
+            keep = torch.arange(M) % 2 == 0
+            A2 = torch.where(keep[:, None], A[perm], noise)
+            C2 = bits_of(run(plan, A2.to(dev()), Bd, split))
+            pk = perm.numpy()[keep.numpy()]
+            assert np.array_equal(C2[keep.numpy()], base[pk]), (tile, split)
+
+
+def test_repeated_runs_identical():
+    w = wl.WORKLOADS["square_f16_1024"]
+    A, B = w.make()
+    Ad, Bd = _to_dev(A, B)
+    plan = imm.gemm_plan(1024, 1024, 1024, "f16")
+    ref = run(plan, Ad, Bd, False)
+    outs = [run(plan, Ad, Bd, False) for _ in range(100)]
+    torch.cuda.synchronize()
+    for C in outs:
+        assert torch.equal(C.view(torch.int32), ref.view(torch.int32))
+    hp = imm.gemm_plan(256, 256, 131072, "f16")
+    Ah, Bh = _to_dev(*wl.WORKLOADS["hugek_f16"].make())
+    refh = run(hp, Ah, Bh, True)
+    for _ in range(50):
+        assert torch.equal(run(hp, Ah, Bh, True).view(torch.int32), refh.view(torch.int32))
+
+
+def test_group_m_and_tile_shape_do_not_change_bits():
+    N, K, M = 768, 1536, 640
+    for dt in ("f16", "e5m2"):
+        A, B = _rand(M, N, K, dt, 8200)
+        Ad, Bd = _to_dev(A, B)
+        for split in (False, True):
+            ref = None
+            for tile in TILES:
+                for gm in (1, 3, 8):
+                    p = imm.gemm_plan_ex(M, N, K, dt, "f32", split_k=3, group_m=gm, tile=tile)
+                    C = bits_of(run(p, Ad, Bd, split))
+                    if ref is None:
+                        ref = C
+                    assert np.array_equal(C, ref), (dt, split, tile, gm)
+            log(f"{dt} split={split}: 3 tiles x 3 GROUP_M identical")
+
+
+def test_splitk_one_slice_equals_run():
+    for name in ("square_f16_1024", "decode_bf16_m32", "hugek_f16"):
+        w = wl.WORKLOADS[name]
+        A, B = w.make()
+        Ad, Bd = _to_dev(A, B)
+        p = imm.gemm_plan_ex(w.M, w.N, w.K, w.dtype, w.out, split_k=1)
+        assert np.array_equal(bits_of(run(p, Ad, Bd, False)), bits_of(run(p, Ad, Bd, True))), name
+
+
+def test_other_stream_and_corunning_work():
+    w = wl.WORKLOADS["decode_bf16_m32"]
+    A, B = w.make()
+    Ad, Bd = _to_dev(A, B)
+    plan = imm.gemm_plan(w.M, w.N, w.K, "bf16")
+    ref = bits_of(run(plan, Ad, Bd, True))
+    s1 = torch.cuda.Stream()
+    s2 = torch.cuda.Stream()
+    X = torch.randn((4096, 4096), device=dev(), dtype=torch.float32)
+    outs = []
+    for _ in range(10):
+        with torch.cuda.stream(s2):
+            for _ in range(3):
+                X = torch.tanh(X @ X * 1e-3)  # busy work on another stream
+        with torch.cuda.stream(s1):
+            outs.append(run(plan, Ad, Bd, True, stream=s1))
+    torch.cuda.synchronize()
+    for C in outs:
+        assert np.array_equal(bits_of(C), ref)
+
+
+def test_split_changes_bits_only_where_rounding_happens():
+    # A different split of K is a different summation tree: on random data some
+    # bits differ (non-associativity), on integer data nothing may differ.
+    w = wl.WORKLOADS["hugek_f16"]
+    A, B = w.make()
+    Ad, Bd = _to_dev(A, B)
+    outs = {}
+    for s in (1, 8, 32, 128):
+        outs[s] = bits_of(run(imm.gemm_plan_ex(256, 256, w.K, "f16", "f32", split_k=s), Ad, Bd, True))
+    diff = sum(int((outs[s] != outs[1]).sum()) for s in (8, 32, 128))
+    log(f"hugek random: elements differing from split 1: {diff}")
+    assert diff > 0
+    g = wl.gen(8300)
+    Ai = wl.integers((256, 16384), "f16", g)
+    Bi = wl.integers((16384, 256), "f16", g)
+    Aid, Bid = _to_dev(Ai, Bi)
+    ref = bits_of(run(imm.gemm_plan_ex(256, 256, 16384, "f16", "f32", split_k=1), Aid, Bid, True))
+    for s in (8, 32, 128):
+        p = imm.gemm_plan_ex(256, 256, 16384, "f16", "f32", split_k=s)
+        assert np.array_equal(bits_of(run(p, Aid, Bid, True)), ref), s

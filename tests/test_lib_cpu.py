@@ -1,0 +1,226 @@
+"""Host-side tests of the C ABI (no GPU needed).
+
+- the shared library loads and exports every function include/invariant_matmul.h declares;
+- plans are a pure function of (N, K, dtypes, options): nothing but the grid
+  and the workspace size changes with M (the Tencent deterministic-inference
+  article, section "Batch Invariance の由来", names M-driven choices of the K
+  step and of split-K as the cause of batch variance);
+- the tile raster (XCD remap + GROUP_M) is a bijection onto the tiles x slices;
+- every invalid argument is rejected with its status before any HIP call, and
+  a valid call on a machine without a GPU returns GEMM_ERR_HIP.
+"""
+import ctypes
+import itertools
+import os
+import re
+
+import pytest
+
+import invariant_matmul_amd as imm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "invariant_matmul.h")
+
+M_INDEPENDENT = ("N", "K", "in_dtype", "out_dtype", "tile", "block_m", "block_n", "block_k",
+                 "mfma_m", "mfma_n", "mfma_k", "waves", "group_m", "split_k", "k_per_split",
+                 "tiles_n", "scale_a", "scale_b")
+
+SHAPES = [  # (N, K, dtype) of every workload family, plus a few others
+    (256, 256, "f16"), (1024, 1024, "f16"), (4096, 4096, "f16"), (8192, 8192, "f16"),
+    (4096, 14336, "bf16"), (256, 131072, "f16"), (4096, 4096, "e5m2"), (8192, 8192, "e5m2"),
+    (16384, 16384, "e5m2"), (6144, 4096, "bf16"), (4096, 4096, "e4m3"), (136, 200, "f16"),
+]
+
+
+def _declared_functions():
+    text = open(HEADER, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gemm_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared_functions()
+    assert set(names) == set(imm.EXPORTED_SYMBOLS), names
+    L = imm.lib()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings():
+    for code, name in imm.STATUS.items():
+        assert imm.gemm_status_string(code) == name
+
+
+@pytest.mark.parametrize("N,K,dt", SHAPES)
+def test_plan_is_independent_of_M(N, K, dt):
+    ref = None
+    for M in (1, 2, 7, 8, 31, 32, 33, 64, 127, 128, 1000, 4096, 8192):
+        info = imm.gemm_plan(M, N, K, dt).info
+        key = {k: info[k] for k in M_INDEPENDENT}
+        if ref is None:
+            ref = key
+        assert key == ref, (M, key, ref)
+        assert info["workspace_bytes"] == info["split_k"] * M * N * 4
+        assert info["tiles_m"] == -(-M // info["block_m"])
+        assert info["grid_splitk"] == info["grid_run"] * info["split_k"]
+
+
+@pytest.mark.parametrize("N,K,dt", SHAPES)
+def test_plan_ex_options_are_independent_of_M(N, K, dt):
+    for split, gm, tile in [(1, 1, "128x128"), (8, 4, "32x128"), (3, 0, "256x256")]:
+        infos = [imm.gemm_plan_ex(M, N, K, dt, "f32", split, gm, tile).info for M in (1, 77, 4096)]
+        keys = [{k: i[k] for k in M_INDEPENDENT} for i in infos]
+        assert keys[0] == keys[1] == keys[2]
+
+
+@pytest.mark.parametrize("N,K,dt", SHAPES)
+def test_split_covers_K_in_block_multiples(N, K, dt):
+    for split in (0, 1, 2, 7, 8, 32, 128, 4096):
+        i = imm.gemm_plan_ex(64, N, K, dt, "f32", split_k=split).info
+        assert i["k_per_split"] % i["block_k"] == 0
+        assert i["k_per_split"] * i["split_k"] >= K
+        assert i["k_per_split"] * (i["split_k"] - 1) < K  # no empty slice
+        if split:
+            assert i["split_k"] <= split
+
+
+def test_default_plans_of_the_workloads():
+    sq = imm.gemm_plan(8192, 8192, 8192, "f16").info
+    assert (sq["block_m"], sq["block_n"], sq["split_k"]) == (256, 256, 1)
+    assert sq["mfma_k"] == 16
+    fp8 = imm.gemm_plan(8192, 8192, 8192, "e5m2").info
+    assert fp8["mfma_k"] == 64 and fp8["out_dtype"] == imm.DTYPE["bf16"]
+    dec = imm.gemm_plan(1, 4096, 14336, "bf16").info
+    assert dec["split_k"] > 1 and dec["block_m"] == 32
+
+
+@pytest.mark.parametrize("M,N,K,dt,split,gm", [
+    (8192, 8192, 8192, "f16", 1, 8), (1000, 1000, 512, "f16", 1, 8), (256, 256, 131072, "f16", 128, 8),
+    (128, 4096, 14336, "bf16", 0, 8), (300, 136, 200, "bf16", 3, 3), (77, 272, 64, "e5m2", 1, 1),
+    (4096, 4096, 4096, "e5m2", 2, 5),
+])
+def test_raster_is_a_bijection(M, N, K, dt, split, gm):
+    p = imm.gemm_plan_ex(M, N, K, dt, "f32", split_k=split, group_m=gm)
+    i = p.info
+    G = i["grid_splitk"]
+    seen = set()
+    for w in range(G):
+        s, pm, pn = imm.gemm_plan_tile_of(p, w)
+        assert 0 <= s < i["split_k"] and 0 <= pm < i["tiles_m"] and 0 <= pn < i["tiles_n"]
+        seen.add((s, pm, pn))
+    assert len(seen) == G == i["split_k"] * i["tiles_m"] * i["tiles_n"]
+    with pytest.raises(imm.GemmError):
+        imm.gemm_plan_tile_of(p, G)
+
+
+def test_raster_groups_rows_within_an_xcd():
+    # Consecutive workgroups on one XCD (w, w+8, w+16, ...) sweep GROUP_M rows of
+    # tiles before moving to the next column.
+    p = imm.gemm_plan_ex(8192, 8192, 8192, "f16", "f32", group_m=8)
+    coords = [imm.gemm_plan_tile_of(p, w) for w in range(0, 8 * 16, 8)]
+    assert [c[1] for c in coords[:8]] == list(range(8))
+    assert all(c[2] == 0 for c in coords[:8]) and all(c[2] == 1 for c in coords[8:16])
+
+
+# ------------------------------------------------------------ error statuses
+
+
+def _plan_status(*args):
+    h = ctypes.c_void_p()
+    return imm.lib().gemm_plan_ex(*args, ctypes.byref(h))
+
+
+@pytest.mark.parametrize("args,status", [
+    ((-1, 8, 8, 0, 4, 0, 0, 0, 1.0, 1.0), 1),
+    ((8, -8, 8, 0, 4, 0, 0, 0, 1.0, 1.0), 1),
+    ((8, 8, -8, 0, 4, 0, 0, 0, 1.0, 1.0), 1),
+    ((8, 8, 8, 4, 4, 0, 0, 0, 1.0, 1.0), 2),      # fp32 input unsupported
+    ((8, 8, 8, 0, 0, 0, 0, 0, 1.0, 1.0), 2),      # fp16 output unsupported
+    ((8, 8, 8, 7, 4, 0, 0, 0, 1.0, 1.0), 2),      # unknown dtype
+    ((8, 12, 8, 0, 4, 0, 0, 0, 1.0, 1.0), 2),     # N not a multiple of 8
+    ((8, 8, 12, 0, 4, 0, 0, 0, 1.0, 1.0), 2),     # K not a multiple of 8
+    ((8, 16, 8, 3, 4, 0, 0, 0, 1.0, 1.0), 2),     # fp8 needs K % 16 == 0
+    ((8, 8, 8, 0, 4, -1, 0, 0, 1.0, 1.0), 2),     # split_k < 0
+    ((8, 8, 8, 0, 4, 4097, 0, 0, 1.0, 1.0), 2),   # split_k too large
+    ((8, 8, 8, 0, 4, 0, -1, 0, 1.0, 1.0), 2),     # group_m < 0
+    ((8, 8, 8, 0, 4, 0, 0, 9, 1.0, 1.0), 2),      # unknown tile
+    ((8, 8, 8, 0, 4, 0, 0, 0, float("inf"), 1.0), 2),
+    ((8, 8, 8, 0, 4, 0, 0, 0, 1.0, float("nan")), 2),
+    ((2 ** 31, 8, 8, 0, 4, 0, 0, 0, 1.0, 1.0), 2),
+    ((8, 8, 8, 0, 4, 0, 0, 0, 1.0, 1.0), 0),
+    ((0, 8, 8, 0, 4, 0, 0, 0, 1.0, 1.0), 0),
+    ((8, 8, 0, 0, 4, 0, 0, 0, 1.0, 1.0), 0),
+])
+def test_plan_validation(args, status):
+    assert _plan_status(*args) == status
+
+
+def test_null_plan_handles():
+    L = imm.lib()
+    assert L.gemm_plan(8, 8, 8, 0, None) == 1
+    assert L.gemm_plan_info(None, None) == 1
+    assert L.gemm_workspace_size(None) == 0
+    assert L.gemm_run(None, 16, 16, 16, None) == 1
+    assert L.gemm_splitk_run(None, 16, 16, 16, 16, 1 << 20, None) == 1
+    L.gemm_plan_destroy(None)
+
+
+FAKE = 1 << 40  # a 16-byte aligned address; never dereferenced by these tests
+
+
+def test_run_validation_before_any_hip_call():
+    L = imm.lib()
+    p = imm.gemm_plan(64, 64, 64, "f16")
+    h = p.handle
+    assert L.gemm_run(h, 0, FAKE, FAKE, None) == 1          # NULL A
+    assert L.gemm_run(h, FAKE, 0, FAKE, None) == 1          # NULL B
+    assert L.gemm_run(h, FAKE, FAKE, 0, None) == 1          # NULL C
+    assert L.gemm_run(h, FAKE + 2, FAKE, FAKE, None) == 1   # misaligned A
+    assert L.gemm_run(h, FAKE, FAKE + 8, FAKE, None) == 1   # misaligned B
+    assert L.gemm_run(h, FAKE, FAKE, FAKE + 4, None) == 1   # misaligned C
+    ws = imm.gemm_workspace_size(p)
+    assert L.gemm_splitk_run(h, FAKE, FAKE, FAKE, 0, ws, None) == 3        # NULL workspace
+    assert L.gemm_splitk_run(h, FAKE, FAKE, FAKE, FAKE, ws - 4, None) == 3  # too small
+    assert L.gemm_splitk_run(h, FAKE, FAKE, FAKE, FAKE + 4, ws, None) == 1  # misaligned ws
+
+
+def test_empty_products_are_noops_without_a_gpu():
+    L = imm.lib()
+    for M, N in ((0, 64), (64, 0)):
+        p = imm.gemm_plan(M, N, 64, "f16")
+        assert L.gemm_run(p.handle, 0, 0, 0, None) == 0
+        assert L.gemm_splitk_run(p.handle, 0, 0, 0, 0, 0, None) == 0
+
+
+def _have_gpu():
+    import torch
+    return torch.cuda.is_available()
+
+
+@pytest.mark.skipif(_have_gpu(), reason="checks the no-GPU error path")
+def test_valid_call_without_gpu_returns_hip_error():
+    L = imm.lib()
+    p = imm.gemm_plan(64, 64, 64, "f16")
+    assert L.gemm_run(p.handle, FAKE, FAKE, FAKE, None) == 4
+    assert imm.gemm_last_hip_error() != 0
+    ws = imm.gemm_workspace_size(p)
+    assert L.gemm_splitk_run(p.handle, FAKE, FAKE, FAKE, FAKE, ws, None) == 4
+    with pytest.raises(imm.GemmError) as e:
+        imm.gemm_run(p, FAKE, FAKE, FAKE)
+    assert e.value.status == 4
+
+
+def test_binding_checks_tensor_shapes_and_dtypes():
+    import torch
+    p = imm.gemm_plan(4, 8, 16, "f16")
+    A = torch.zeros((4, 16), dtype=torch.float16)
+    B = torch.zeros((16, 8), dtype=torch.float16)
+    C = torch.zeros((4, 8), dtype=torch.float32)
+    with pytest.raises(ValueError):
+        imm.gemm_run(p, A.to(torch.bfloat16), B, C)
+    with pytest.raises(ValueError):
+        imm.gemm_run(p, A, B[:8], C)
+    with pytest.raises(ValueError):
+        imm.gemm_run(p, A, B, C.to(torch.bfloat16))
+    with pytest.raises(ValueError):
+        imm.gemm_run(p, A.t(), B, C)
