@@ -77,25 +77,29 @@ def summary(per):
             "p90_ms": s[min(len(s) - 1, int(0.9 * len(s)))], "n": len(s)}
 
 
-def cpu_baseline(w, A, B, target_s=12.0):
-    """Time the oracle on the first rows of the product (~target_s seconds)."""
+def cpu_baseline(w, A, B, target_s=15.0):
+    """Time the oracle on the first rows of the product (about target_s seconds)."""
     import oracle
     import workloads as wl
     a_bits, b_bits = wl.bits(A), wl.bits(B)
     threads = oracle.max_threads()
-    rows = 4
-    t = time.perf_counter()
-    oracle.gemm(a_bits, b_bits, w.dtype, rows=list(range(rows)))
-    dt = time.perf_counter() - t
-    # the first call also decodes B; scale the row count to the target time
-    more = max(rows, min(w.M, int(rows * target_s / max(dt, 1e-3))))
-    t = time.perf_counter()
-    oracle.gemm(a_bits, b_bits, w.dtype, rows=list(range(more)))
-    dt = time.perf_counter() - t
-    flops = 2.0 * more * w.N * w.K
+
+    def timed(rows):
+        t = time.perf_counter()
+        oracle.gemm(a_bits, b_bits, w.dtype, rows=list(range(rows)))
+        return time.perf_counter() - t
+
+    r1, r2 = threads, 4 * threads
+    t1, t2 = timed(r1), timed(r2)
+    per_row = max((t2 - t1) / (r2 - r1), 1e-6)
+    fixed = max(t1 - r1 * per_row, 0.0)  # decoding B, once per call
+    rows = int(min(w.M, max(r2, (target_s - fixed) / per_row)))
+    rows -= rows % threads if rows > threads else 0
+    dt = timed(rows)
+    flops = 2.0 * rows * w.N * w.K
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"rows 0..{more - 1} of the {w.M}x{w.N}x{w.K} {w.dtype} product "
-                      f"(includes decoding B once), {dt:.1f} s"}
+            "sample": f"rows 0..{rows - 1} of the {w.M}x{w.N}x{w.K} {w.dtype} product, one "
+                      f"call including the decode of B, {dt:.1f} s wall"}
 
 
 def bench_square(name, steps, warmup, torch, imm, wl):

@@ -90,10 +90,11 @@ typedef enum {
  * for a fixed split of K they produce identical bits; the choice only moves
  * work in space. */
 typedef enum {
-  GEMM_TILE_DEFAULT = 0,  /* chosen from (N, K, dtype) */
-  GEMM_TILE_256x256 = 1,
-  GEMM_TILE_128x128 = 2,
-  GEMM_TILE_32x128 = 3
+  GEMM_TILE_DEFAULT = 0,    /* chosen from (N, K, dtype) */
+  GEMM_TILE_256x256 = 1,    /* 4 waves, LDS ring filled by buffer->LDS DMA */
+  GEMM_TILE_128x128 = 2,    /* 4 waves, register-staged LDS tiles */
+  GEMM_TILE_32x128 = 3,     /* 4 waves, register-staged LDS tiles */
+  GEMM_TILE_256x256_RS = 4  /* 8 waves, register-staged LDS tiles */
 } gemm_tile;
 
 typedef struct gemm_plan_s* gemm_plan_t;

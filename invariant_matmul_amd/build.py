@@ -18,7 +18,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libinvariant_matmul.so")
 BUILD_DIR = os.path.join(HERE, "_build")
 
-SOURCES = ["api.cpp", "gemm_kernels.hip"]
+SOURCES = ["api.cpp", "gemm_kernels.hip", "gemm_dma.hip"]
 ARCH = "gfx950"
 
 # Packed fp32 VALU instructions are kept out of all device code.
@@ -59,8 +59,20 @@ def build(verbose: bool = False) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
+    _check_loads(tmp)
     os.replace(tmp, LIB)
     return LIB
+
+
+def _check_loads(path: str) -> None:
+    """dlopen the fresh library with immediate binding: a kernel whose host
+    stub the compiler dropped shows up here as an undefined symbol."""
+    import ctypes
+    try:
+        ctypes.CDLL(path, mode=os.RTLD_NOW | os.RTLD_LOCAL)
+    except OSError as e:
+        os.unlink(path)
+        raise RuntimeError(f"built library does not load: {e}") from None
 
 
 if __name__ == "__main__":

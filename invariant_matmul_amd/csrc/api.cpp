@@ -37,7 +37,8 @@ bool valid_out(int dt) { return dt == GEMM_F32 || dt == GEMM_BF16; }
 
 void tile_shape(int tile, int* bm, int* bn, int* wm, int* wn) {
   switch (tile) {
-    case GEMM_TILE_256x256: *bm = 256; *bn = 256; *wm = 2; *wn = 4; break;
+    case GEMM_TILE_256x256: *bm = 256; *bn = 256; *wm = 2; *wn = 2; break;
+    case GEMM_TILE_256x256_RS: *bm = 256; *bn = 256; *wm = 2; *wn = 4; break;
     case GEMM_TILE_128x128: *bm = 128; *bn = 128; *wm = 2; *wn = 2; break;
     default: *bm = 32; *bn = 128; *wm = 1; *wn = 4; break;  // GEMM_TILE_32x128
   }
@@ -125,7 +126,7 @@ gemm_status gemm_plan_ex(int64_t M, int64_t N, int64_t K, gemm_dtype in, gemm_dt
   if (M > INT_MAX || N > INT_MAX || K > INT_MAX) return GEMM_ERR_UNSUPPORTED;
   if (!valid_in(in) || !valid_out(out)) return GEMM_ERR_UNSUPPORTED;
   if (split_k < 0 || split_k > kMaxSplit || group_m < 0) return GEMM_ERR_UNSUPPORTED;
-  if (tile < GEMM_TILE_DEFAULT || tile > GEMM_TILE_32x128) return GEMM_ERR_UNSUPPORTED;
+  if (tile < GEMM_TILE_DEFAULT || tile > GEMM_TILE_256x256_RS) return GEMM_ERR_UNSUPPORTED;
   if (!std::isfinite(scale_a) || !std::isfinite(scale_b)) return GEMM_ERR_UNSUPPORTED;
   // 16-byte vector access of every row of A and B needs K and N to be
   // multiples of 16 bytes' worth of elements.
@@ -141,6 +142,12 @@ gemm_status gemm_plan_ex(int64_t M, int64_t N, int64_t K, gemm_dtype in, gemm_dt
   p->in = in;
   p->out = out;
   p->tile = tile == GEMM_TILE_DEFAULT ? default_tile(N, K) : tile;
+  // The DMA kernel addresses one 256-row A tile and one 64-byte-deep B stage
+  // with 32-bit offsets; beyond that the register-staged kernel (same bits)
+  // takes over.
+  if (p->tile == GEMM_TILE_256x256 &&
+      (256 * K * eb >= ((int64_t)1 << 31) - 64 || 64 * N * eb >= ((int64_t)1 << 31) - 64))
+    p->tile = GEMM_TILE_256x256_RS;
   tile_shape(p->tile, &p->bm, &p->bn, &p->waves_m, &p->waves_n);
   p->bk = block_k_elems(in);
   p->group_m = group_m == 0 ? 8 : group_m;

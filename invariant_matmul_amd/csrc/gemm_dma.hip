@@ -1,0 +1,362 @@
+// Large-tile GEMM main loop for gfx950 fed by buffer->LDS DMA.
+//
+// Citations: [TDI] = Tencent engineer article on deterministic LLM inference
+// ("AI インフラの深化：大規模モデルに確定的な出力を実現する方法").
+//
+// One workgroup of 4 waves (one per SIMD) owns a 256 x 256 tile of C (or of
+// one K slice of it); each wave owns a 128 x 128 quarter held in 256 fp32
+// accumulators per lane (the AGPR file).  K is walked in ascending stages of
+// 64 bytes of K per row ([TDI] "Tiling - 分塊行列乗算": load, compute,
+// accumulate per K step, one write-back at the end).
+//
+// Memory pipeline ([TDI] "演算子チューニング": latency is hidden by
+// multi-buffering rather than by occupancy).  A ring of 4 LDS stages (32 KB
+// each) is filled by buffer_load ... lds: every lane moves 16 bytes straight
+// from HBM/L2 into LDS, no registers, no LDS-store instructions, and an
+// out-of-range offset writes zeros (used for rows past M, columns past N and
+// K past the end of the slice).  Stage t+4 is requested while stage t+1 is
+// computed, so three stages of loads are in flight behind the math.
+//
+// LDS layouts.  A is stored K-contiguous (64 bytes per row, 4 slots of 16
+// bytes, slot c of row r at c ^ ((r >> 2) & 3)), read with ds_read_b128.
+// B is stored as it lies in memory, N-contiguous (512 bytes per K row for
+// 16-bit, 256 for fp8), and read with the gfx950 transposing LDS reads
+// (ds_read_b64_tr_b16 / _b8), which hand each lane the K-contiguous column
+// piece the matrix core needs.  16-byte slot c of B row k lives at
+// c ^ ((k & 3) << 2) (16-bit) or c ^ ((k & 7) << 1) (fp8) so that the rows one
+// transposing read touches fall on different banks.  The swizzles are applied
+// on the global side: each DMA lane fetches the chunk that belongs in its
+// fixed LDS slot.
+//
+// Synchronisation.  Each wave waits (vmcnt) for its own DMA of the next stage,
+// then one s_barrier makes every wave's data visible and certifies that every
+// wave has finished reading the stage about to be refilled.  The barrier sits
+// half-way through the stage's last MFMA step, so the fragment reads of the
+// next stage overlap the remaining MFMAs.
+//
+// Bits: the per-element chain is the same as in every other kernel of the
+// library (same instruction, MFMA K steps in ascending k from +0), so this
+// kernel's output is bitwise identical to theirs.
+#include "kernel_common.h"
+
+namespace imm {
+namespace {
+using namespace dev;
+
+constexpr int NS = 4;             // LDS stages
+constexpr int SKB = 64;           // bytes of K per row per stage
+constexpr int TBM = 256, TBN = 256;
+constexpr int A_STAGE = TBM * SKB;  // 16 KB
+constexpr int B_STAGE = 16384;      // (64 / eb) K rows x 256 columns x eb
+constexpr int STAGE = A_STAGE + B_STAGE;
+constexpr unsigned OOB = 0x80000000u;
+constexpr int NREC = 0x7fffffff;
+constexpr int RSRC_FLAGS = 0x00020000;
+
+template <int IN>
+struct Frag {
+  typename FragOf<IN>::type a[4];
+  typename FragOf<IN>::type b[4];
+};
+
+template <int IN, int OUT, bool SLICE>
+__global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmArgs g) {
+  using T = InT<IN>;
+  constexpr int EB = T::EB;
+  constexpr int BKE = SKB / EB;              // K elements per stage
+  constexpr int KS = SKB / T::KSTEP_B;       // MFMA k-steps per stage (2 or 1)
+  constexpr int BROW = TBN * EB;             // bytes per B row in LDS
+  constexpr int BSLOTS = BROW / 16;
+  constexpr int BROWS_PER_DMA = 1024 / BROW; // B rows written by one DMA instruction
+
+  __shared__ __attribute__((aligned(1024))) char lds[NS * STAGE];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (uniform)
+  const int wm = w >> 1, wn = w & 1;
+  const int h = lane >> 5, l32 = lane & 31;
+
+  int64_t ksl, pm, pn;
+  raster_tile(blockIdx.x, g.grid, g.tiles_m, g.tiles_n, g.group_m, &ksl, &pm, &pn);
+  const int64_t m0 = pm * TBM, n0 = pn * TBN;
+  const int64_t kbeg = ksl * g.k_per_split;
+  const int64_t kend = (g.K < kbeg + g.k_per_split) ? g.K : kbeg + g.k_per_split;
+  const int nt = kend > kbeg ? (int)((kend - kbeg + BKE - 1) / BKE) : 0;
+  const char* A = static_cast<const char*>(g.A);
+  const char* B = static_cast<const char*>(g.B);
+
+  // ---- DMA geometry of this lane (the same for every stage).  Offsets of
+  // rows past M / columns past N are replaced by an out-of-range offset once;
+  // the K check is only needed in a partial last stage.
+  unsigned a_off[4], b_off[4];
+  int a_kel[4], b_k[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = 16 * (4 * w + i) + (lane >> 2);
+    const int c = (lane & 3) ^ ((row >> 2) & 3);
+    a_off[i] = (m0 + row < g.M) ? (unsigned)(row * g.K * EB + c * 16) : OOB;
+    a_kel[i] = c * (16 / EB);
+    const int k = BROWS_PER_DMA * (4 * w + i) + lane / BSLOTS;
+    const int s = lane % BSLOTS;
+    const int cb = EB == 2 ? (s ^ ((k & 3) << 2)) : (s ^ ((k & 7) << 1));
+    b_off[i] = (n0 + cb * (16 / EB) < g.N) ? (unsigned)(k * g.N * EB + cb * 16) : OOB;
+    b_k[i] = k;
+  }
+
+  // Buffer descriptors of stage t and whether it is a full stage.
+  struct StageSrc {
+    const char* pa;  // first byte of the stage's A block (row m0)
+    const char* pb;  // first byte of the stage's B block (column n0)
+    int rem;         // K elements of this stage inside the slice (BKE for a full stage)
+  };
+  auto stage_src = [&](int t) {
+    StageSrc q;
+    const int64_t kst = kbeg + (int64_t)t * BKE;
+    q.pa = A + (m0 * g.K + kst) * EB;
+    q.pb = B + (kst * g.N + n0) * EB;
+    q.rem = kend - kst < BKE ? (int)(kend - kst) : BKE;
+    return q;
+  };
+  // DMA instruction x (0..3: A rows, 4..7: B rows) of stage t into LDS slot t % NS.
+  auto dma_one = [&](const StageSrc& q, int t, int x) {
+    char* sb = lds + (t % NS) * STAGE;
+    if (x < 4) {
+      const unsigned off = a_kel[x] < q.rem ? a_off[x] : OOB;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          __builtin_amdgcn_make_buffer_rsrc((void*)q.pa, 0, NREC, RSRC_FLAGS),
+          IMM_LDS(sb + (4 * w + x) * 1024), 16, off, 0, 0, 0);
+    } else {
+      const int i = x - 4;
+      const unsigned off = b_k[i] < q.rem ? b_off[i] : OOB;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          __builtin_amdgcn_make_buffer_rsrc((void*)q.pb, 0, NREC, RSRC_FLAGS),
+          IMM_LDS(sb + A_STAGE + (4 * w + i) * 1024), 16, off, 0, 0, 0);
+    }
+  };
+  auto dma = [&](int t) {
+    const StageSrc q = stage_src(t);
+#pragma unroll
+    for (int x = 0; x < 8; ++x) dma_one(q, t, x);
+  };
+
+  // ---- fragment read offsets within a stage.
+  const int asw = (l32 >> 2) & 3;
+  int a_rd[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) a_rd[i] = (wm * 128 + i * 32 + l32) * SKB;
+  const int grp = lane >> 4, gi = lane & 15;
+  int b_rd[4];  // per column block j: byte offset of the first transposing read
+  if constexpr (EB == 2) {
+    const int t_ = gi >> 2, q = gi & 3;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = wn * 128 + j * 32 + 16 * (grp & 1) + 4 * q;
+      const int k = 8 * (grp >> 1) + t_;
+      b_rd[j] = A_STAGE + k * BROW + (((n >> 3) ^ (t_ << 2)) << 4) + (q & 1) * 8;
+    }
+  } else {
+    const int t_ = gi >> 1, q = gi & 1;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = wn * 128 + j * 32 + 16 * (grp & 1) + 8 * q;
+      const int k = 32 * (grp >> 1) + t_;
+      b_rd[j] = A_STAGE + k * BROW + (((n >> 4) ^ (t_ << 1)) << 4) + q * 8;
+    }
+  }
+
+  // LDS byte address of the ring (for the transposing reads).
+  const unsigned lds_addr = (unsigned)(uintptr_t)((__attribute__((address_space(3))) char*)lds);
+
+  // Fragment read x of k-step ks of LDS slot `slot` into F.
+  //   16-bit: x = 0..3 -> A block i = x (one ds_read_b128);
+  //           x = 4..11 -> B block j = (x-4)/2, half r = (x-4)%2 (K elements 4r..4r+3).
+  //   fp8:    x = 0..7 -> A block i = x/2, half x%2 (16 bytes of K each);
+  //           x = 8..23 -> B block j = (x-8)/4, piece r = (x-8)%4 (8 K values).
+  constexpr int NREAD = EB == 2 ? 12 : 24;
+  auto read_one = [&](Frag<IN>& F, int slot, int ks, int x) {
+    const char* sb = lds + slot;
+    if constexpr (EB == 2) {
+      if (x < 4) {
+        const int c = ks * 2 + h;
+        F.a[x] = *reinterpret_cast<const i32x4*>(sb + a_rd[x] + ((c ^ asw) << 4));
+      } else {
+        const int j = (x - 4) >> 1, r = (x - 4) & 1;
+        const unsigned p0 = lds_addr + slot + b_rd[j];
+        i32x2 v;
+        if (ks == 0)
+          v = r == 0 ? ds_read_tr16_b64<0>(p0) : ds_read_tr16_b64<4 * BROW>(p0);
+        else
+          v = r == 0 ? ds_read_tr16_b64<16 * BROW>(p0) : ds_read_tr16_b64<20 * BROW>(p0);
+        F.b[j][2 * r] = v[0];
+        F.b[j][2 * r + 1] = v[1];
+      }
+    } else {
+      if (x < 8) {
+        const int i = x >> 1, f = x & 1;
+        const i32x4 v =
+            *reinterpret_cast<const i32x4*>(sb + a_rd[i] + (((2 * h + f) ^ asw) << 4));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) F.a[i][4 * f + e] = v[e];
+      } else {
+        const int j = (x - 8) >> 2, r = (x - 8) & 3;
+        const unsigned p0 = lds_addr + slot + b_rd[j];
+        i32x2 v;
+        if (r == 0) v = ds_read_tr8_b64<0>(p0);
+        else if (r == 1) v = ds_read_tr8_b64<8 * BROW>(p0);
+        else if (r == 2) v = ds_read_tr8_b64<16 * BROW>(p0);
+        else v = ds_read_tr8_b64<24 * BROW>(p0);
+        F.b[j][2 * r] = v[0];
+        F.b[j][2 * r + 1] = v[1];
+      }
+    }
+  };
+
+  // The B fragments come from inline-assembly reads the compiler does not
+  // track, so MFMAs that use freshly read fragments are preceded by an
+  // explicit lgkmcnt(0) wait, fenced with sched_barrier.
+  auto fence = [&]() { __builtin_amdgcn_sched_barrier(0); };
+  auto lds_wait = [&]() {
+    fence();
+    __builtin_amdgcn_s_waitcnt(lgkmcnt_imm(0));
+    fence();
+  };
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+
+  auto mfma_x = [&](const Frag<IN>& F, int x) {
+    acc[x >> 2][x & 3] = mfma_v<IN>(F.a[x >> 2], F.b[x & 3], acc[x >> 2][x & 3]);
+  };
+
+  Frag<IN> F0, F1;
+  if (nt > 0) {
+    const int pre = nt < NS ? nt : NS;
+    for (int p = 0; p < pre; ++p) dma(p);
+    // stage 0 landed: pre - 1 stages were requested after it
+    if (pre >= 4)
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(24));
+    else if (pre == 3)
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(16));
+    else if (pre == 2)
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(8));
+    else
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    __builtin_amdgcn_s_barrier();
+    fence();
+#pragma unroll
+    for (int x = 0; x < NREAD; ++x) read_one(F0, 0, 0, x);
+  }
+
+  // Second half of the last k-step of stage t, with the stage change folded
+  // in: wait for this wave's DMA of stage t+1, barrier (every wave's data of
+  // t+1 has landed and every wave holds stage t in registers), then issue the
+  // DMA of stage t+NS into slot t % NS and the fragment reads of stage t+1,
+  // one or more between consecutive MFMAs.
+  auto boundary_half = [&](int t, const Frag<IN>& Fc, Frag<IN>& Fn) {
+    const bool next = t + 1 < nt;
+    if (next) {
+      const int last_req = (nt - 1 < t + NS - 1) ? nt - 1 : t + NS - 1;
+      const int ahead = last_req - (t + 1);
+      fence();
+      if (ahead >= 2)
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(16));
+      else if (ahead == 1)
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(8));
+      else
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+      __builtin_amdgcn_s_waitcnt(lgkmcnt_imm(0));
+      __builtin_amdgcn_s_barrier();
+      fence();
+    }
+    const bool refill = t + NS < nt;
+    const StageSrc q = stage_src(t + NS);
+    const int nslot = ((t + 1) % NS) * STAGE;
+#pragma unroll
+    for (int x = 0; x < 8; ++x) {
+      mfma_x(Fc, 8 + x);
+      if (refill) dma_one(q, t + NS, x);
+      if (next) {
+#pragma unroll
+        for (int y = x * NREAD / 8; y < (x + 1) * NREAD / 8; ++y) read_one(Fn, nslot, 0, y);
+      }
+      fence();
+    }
+  };
+
+  if constexpr (KS == 2) {
+    for (int t = 0; t < nt; ++t) {
+      const int slot = (t % NS) * STAGE;
+      lds_wait();  // F0 (stage t, k-step 0) has landed
+#pragma unroll
+      for (int x = 0; x < 16; ++x) {
+        mfma_x(F0, x);
+        if (x < NREAD) read_one(F1, slot, 1, x);
+        fence();
+      }
+      lds_wait();  // F1 (stage t, k-step 1) has landed
+#pragma unroll
+      for (int x = 0; x < 8; ++x) mfma_x(F1, x);
+      boundary_half(t, F1, F0);
+    }
+  } else {
+    for (int t = 0; t < nt; ++t) {
+      lds_wait();  // F0 (stage t) has landed
+#pragma unroll
+      for (int x = 0; x < 8; ++x) mfma_x(F0, x);
+      boundary_half(t, F0, F1);
+      lds_wait();  // F1 (stage t+1) has landed before it is copied
+      F0 = F1;
+    }
+  }
+
+  // Write-back.  32x32 accumulator layout: lane l, register r holds
+  // row 8*(r/4) + 4*(l/32) + r%4, column l%32 of the block.
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t col = n0 + wn * 128 + j * 32 + l32;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t row = m0 + wm * 128 + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+        if (row < g.M && col < g.N) {
+          const float v = acc[i][j][r];
+          if constexpr (SLICE) {
+            static_cast<float*>(g.C)[(ksl * g.M + row) * g.N + col] = v;
+          } else {
+            store_out<OUT>(g.C, row * g.N + col, v * g.scale);
+          }
+        }
+      }
+    }
+  }
+}
+
+template <int IN>
+hipError_t launch_in(const gemm_plan_s& p, const GemmArgs& a, bool slice, hipStream_t s) {
+  const dim3 grid((unsigned)a.grid), block(256);
+  if (slice)
+    hipLaunchKernelGGL((gemm_dma_kernel<IN, GEMM_F32, true>), grid, block, 0, s, a);
+  else if (p.out == GEMM_F32)
+    hipLaunchKernelGGL((gemm_dma_kernel<IN, GEMM_F32, false>), grid, block, 0, s, a);
+  else
+    hipLaunchKernelGGL((gemm_dma_kernel<IN, GEMM_BF16, false>), grid, block, 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemm_dma(const gemm_plan_s& p, const GemmArgs& a, bool slice_mode,
+                           hipStream_t s) {
+  switch (p.in) {
+    case GEMM_F16: return launch_in<GEMM_F16>(p, a, slice_mode, s);
+    case GEMM_BF16: return launch_in<GEMM_BF16>(p, a, slice_mode, s);
+    case GEMM_F8_E4M3: return launch_in<GEMM_F8_E4M3>(p, a, slice_mode, s);
+    case GEMM_F8_E5M2: return launch_in<GEMM_F8_E5M2>(p, a, slice_mode, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace imm

@@ -32,70 +32,24 @@
 // data per lane, so each thread loads a 4 x 16-byte block of B (4 K rows)
 // and transposes it in registers before writing it to LDS ([GKM] discusses
 // the non-coalesced column access of B that this avoids).
-#include "imm_internal.h"
+#include "kernel_common.h"
 
 namespace imm {
 namespace {
-
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef int i32x8 __attribute__((ext_vector_type(8)));
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-typedef int i32x2 __attribute__((ext_vector_type(2)));
+using namespace dev;
 
 constexpr int ROWB = kTileKBytes;  // bytes of K per LDS row per stage
 constexpr int CHUNKS = ROWB / 16;  // 16-byte chunks per LDS row
 
 template <int IN>
-struct InT {
-  static constexpr int EB = (IN == GEMM_F8_E4M3 || IN == GEMM_F8_E5M2) ? 1 : 2;
-  static constexpr int BKE = ROWB / EB;          // K elements per stage
-  static constexpr int KSTEP_B = EB == 2 ? 32 : 64;  // bytes of K per MFMA
-  static constexpr int NKK = ROWB / KSTEP_B;     // MFMAs per stage per block
-  static constexpr int FRAG = KSTEP_B / 32;      // 16-byte chunks per lane
+struct TileT {
+  static constexpr int EB = InT<IN>::EB;
+  static constexpr int BKE = ROWB / EB;                  // K elements per stage
+  static constexpr int NKK = ROWB / InT<IN>::KSTEP_B;    // MFMA steps per stage
+  static constexpr int FRAG = InT<IN>::FRAG;             // 16-byte chunks per lane
 };
 
-// One 32x32 MFMA step.  Lane l supplies row (l % 32) of A / column (l % 32) of
-// B; its 16 (32) bytes are the K elements [h*half, (h+1)*half) of the step,
-// h = l / 32, in increasing k.  A and B use the same K placement, so the
-// instruction computes the plain dot product over its K step.
-template <int IN>
-__device__ __forceinline__ f32x16 mfma(const i32x4* a, const i32x4* b, f32x16 c) {
-  if constexpr (IN == GEMM_F16) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a[0]),
-                                                  __builtin_bit_cast(f16x8, b[0]), c, 0, 0, 0);
-  } else if constexpr (IN == GEMM_BF16) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[0]),
-                                                   __builtin_bit_cast(bf16x8, b[0]), c, 0, 0, 0);
-  } else {
-    // cbsz / blgp select the operand formats: 0 = fp8 e4m3, 1 = bf8 e5m2.
-    constexpr int fmt = IN == GEMM_F8_E4M3 ? 0 : 1;
-    const i32x8 av = __builtin_shufflevector(a[0], a[1], 0, 1, 2, 3, 4, 5, 6, 7);
-    const i32x8 bv = __builtin_shufflevector(b[0], b[1], 0, 1, 2, 3, 4, 5, 6, 7);
-    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, c, fmt, fmt, 0, 0, 0, 0);
-  }
-}
-
 __device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
-
-// fp32 -> bf16, round to nearest, ties to even (quiet NaN stays NaN).
-__device__ __forceinline__ unsigned short f32_to_bf16(float f) {
-  unsigned u = __builtin_bit_cast(unsigned, f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (unsigned short)((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (unsigned short)(u >> 16);
-}
-
-template <int OUT>
-__device__ __forceinline__ void store_out(void* C, int64_t idx, float v) {
-  if constexpr (OUT == GEMM_F32) {
-    static_cast<float*>(C)[idx] = v;
-  } else {
-    static_cast<unsigned short*>(C)[idx] = f32_to_bf16(v);
-  }
-}
 
 // Transpose a 4 (K) x 16-byte (N) block of B held as rows q[0..3] into
 // K-major pieces: for 16-bit elements, 8 columns x 4 K values (8 bytes each);
@@ -131,7 +85,7 @@ __device__ __forceinline__ void transpose_b(const i32x4 (&q)[4], i32x2 (&o16)[8]
 
 template <int IN, int OUT, int BM, int BN, int WAVES_M, int WAVES_N, bool SLICE>
 __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_tile_kernel(GemmArgs g) {
-  using T = InT<IN>;
+  using T = TileT<IN>;
   constexpr int THREADS = WAVES_M * WAVES_N * 64;
   constexpr int EB = T::EB;
   constexpr int BKE = T::BKE;
@@ -326,7 +280,7 @@ hipError_t launch_cfg(const GemmArgs& a, bool slice, hipStream_t s) {
 template <int IN, int OUT>
 hipError_t launch_tile(int tile, const GemmArgs& a, bool slice, hipStream_t s) {
   switch (tile) {
-    case GEMM_TILE_256x256: return launch_cfg<IN, OUT, 256, 256, 2, 4>(a, slice, s);
+    case GEMM_TILE_256x256_RS: return launch_cfg<IN, OUT, 256, 256, 2, 4>(a, slice, s);
     case GEMM_TILE_128x128: return launch_cfg<IN, OUT, 128, 128, 2, 2>(a, slice, s);
     case GEMM_TILE_32x128: return launch_cfg<IN, OUT, 32, 128, 1, 4>(a, slice, s);
     default: return hipErrorInvalidValue;
@@ -342,6 +296,7 @@ hipError_t launch_in(const gemm_plan_s& p, const GemmArgs& a, bool slice, hipStr
 }  // namespace
 
 hipError_t launch_gemm(const gemm_plan_s& p, const GemmArgs& a, bool slice_mode, hipStream_t s) {
+  if (p.tile == GEMM_TILE_256x256) return launch_gemm_dma(p, a, slice_mode, s);
   switch (p.in) {
     case GEMM_F16: return launch_in<GEMM_F16>(p, a, slice_mode, s);
     case GEMM_BF16: return launch_in<GEMM_BF16>(p, a, slice_mode, s);

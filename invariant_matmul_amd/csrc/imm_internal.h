@@ -103,5 +103,7 @@ struct ReduceArgs {
 // output, raw sums, no scale) instead of the final store.
 hipError_t launch_gemm(const gemm_plan_s& p, const GemmArgs& a, bool slice_mode, hipStream_t s);
 hipError_t launch_reduce(const gemm_plan_s& p, const ReduceArgs& a, hipStream_t s);
+// The DMA-fed 256x256 kernel (gemm_dma.hip); launch_gemm forwards to it.
+hipError_t launch_gemm_dma(const gemm_plan_s& p, const GemmArgs& a, bool slice_mode, hipStream_t s);
 
 }  // namespace imm

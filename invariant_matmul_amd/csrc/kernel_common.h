@@ -1,0 +1,122 @@
+// Device helpers shared by the GEMM kernels (gfx950).
+//
+// Citations: [TDI] = Tencent engineer article on deterministic LLM inference
+// ("AI インフラの深化：大規模モデルに確定的な出力を実現する方法").
+#pragma once
+
+#include <type_traits>
+
+#include "imm_internal.h"
+
+namespace imm {
+namespace dev {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+#define IMM_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+
+template <int IN>
+struct InT {
+  static constexpr int EB = (IN == GEMM_F8_E4M3 || IN == GEMM_F8_E5M2) ? 1 : 2;
+  static constexpr int KSTEP_B = EB == 2 ? 32 : 64;  // bytes of K per MFMA (per row)
+  static constexpr int FRAG = KSTEP_B / 32;          // 16-byte pieces per lane per operand
+};
+
+// The one matrix-core step every kernel uses for an input dtype (the bits of
+// the product depend on this choice, [TDI] "Batch Invariance の由来", BLOCK_K
+// paragraph): a 32x32 output block, K = 16 (fp16/bf16) or 64 (fp8).  Lane l
+// supplies row (l % 32) of A and column (l % 32) of B; its data are the K
+// elements [h*half, (h+1)*half) of the step, h = l / 32, in increasing k.
+template <int IN>
+__device__ __forceinline__ f32x16 mfma(const i32x4* a, const i32x4* b, f32x16 c) {
+  if constexpr (IN == GEMM_F16) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a[0]),
+                                                  __builtin_bit_cast(f16x8, b[0]), c, 0, 0, 0);
+  } else if constexpr (IN == GEMM_BF16) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[0]),
+                                                   __builtin_bit_cast(bf16x8, b[0]), c, 0, 0, 0);
+  } else {
+    // cbsz / blgp select the operand formats: 0 = fp8 e4m3, 1 = bf8 e5m2.
+    constexpr int fmt = IN == GEMM_F8_E4M3 ? 0 : 1;
+    const i32x8 av = __builtin_shufflevector(a[0], a[1], 0, 1, 2, 3, 4, 5, 6, 7);
+    const i32x8 bv = __builtin_shufflevector(b[0], b[1], 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, c, fmt, fmt, 0, 0, 0, 0);
+  }
+}
+
+// The same step on whole-operand registers: 4 dwords (16-bit inputs) or 8
+// dwords (fp8) per lane, allocated as one register tuple.
+template <int IN>
+struct FragOf {
+  using type = typename std::conditional<InT<IN>::EB == 2, i32x4, i32x8>::type;
+};
+
+template <int IN>
+__device__ __forceinline__ f32x16 mfma_v(const typename FragOf<IN>::type& a,
+                                         const typename FragOf<IN>::type& b, f32x16 c) {
+  if constexpr (IN == GEMM_F16) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  } else if constexpr (IN == GEMM_BF16) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  } else {
+    constexpr int fmt = IN == GEMM_F8_E4M3 ? 0 : 1;
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, fmt, fmt, 0, 0, 0, 0);
+  }
+}
+
+// fp32 -> bf16, round to nearest, ties to even (quiet NaN stays NaN).
+__device__ __forceinline__ unsigned short f32_to_bf16(float f) {
+  unsigned u = __builtin_bit_cast(unsigned, f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (unsigned short)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (unsigned short)(u >> 16);
+}
+
+template <int OUT>
+__device__ __forceinline__ void store_out(void* C, int64_t idx, float v) {
+  if constexpr (OUT == GEMM_F32) {
+    static_cast<float*>(C)[idx] = v;
+  } else {
+    static_cast<unsigned short*>(C)[idx] = f32_to_bf16(v);
+  }
+}
+
+// Transposing LDS reads (gfx950).  Issued as inline assembly: the compiler
+// otherwise waits for every outstanding buffer->LDS transfer before each such
+// read (it cannot tell which LDS bytes the transfer writes), which would drain
+// the prefetch pipeline every stage.  The caller must wait for lgkmcnt before
+// using the result.  In each group of 16 lanes, lanes 4t..4t+3 (16-bit) or
+// 2t..2t+1 (8-bit) supply row t from their own addresses and lane j receives
+// column j of those rows.
+template <int OFF>
+__device__ __forceinline__ i32x2 ds_read_tr16_b64(unsigned addr) {
+  i32x2 v;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "n"(OFF));
+  return v;
+}
+template <int OFF>
+__device__ __forceinline__ i32x2 ds_read_tr8_b64(unsigned addr) {
+  i32x2 v;
+  asm volatile("ds_read_b64_tr_b8 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "n"(OFF));
+  return v;
+}
+
+// s_waitcnt immediate that waits until at most `n` vector-memory operations
+// of this wave are outstanding (LDS/scalar and export counters unconstrained).
+__host__ __device__ constexpr int vmcnt_imm(int n) {
+  return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8);
+}
+// ... and until at most `n` LDS operations are outstanding.
+__host__ __device__ constexpr int lgkmcnt_imm(int n) { return 15 | (3 << 14) | (7 << 4) | (n << 8); }
+
+}  // namespace dev
+}  // namespace imm
