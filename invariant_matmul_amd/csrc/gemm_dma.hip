@@ -37,6 +37,8 @@
 // Bits: the per-element chain is the same as in every other kernel of the
 // library (same instruction, MFMA K steps in ascending k from +0), so this
 // kernel's output is bitwise identical to theirs.
+#include <type_traits>
+
 #include "kernel_common.h"
 
 namespace imm {
@@ -53,14 +55,19 @@ constexpr unsigned OOB = 0x80000000u;
 constexpr int NREC = 0x7fffffff;
 constexpr int RSRC_FLAGS = 0x00020000;
 
-template <int IN>
+// Fragments of one MFMA k-step of one wave: FM blocks of A (rows), FN of B.
+template <int IN, int FN>
 struct Frag {
   typename FragOf<IN>::type a[4];
-  typename FragOf<IN>::type b[4];
+  typename FragOf<IN>::type b[FN];
 };
 
-template <int IN, int OUT, bool SLICE>
-__global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmArgs g) {
+// WN waves along N, 2 along M.  WN = 2: 4 waves of 128 x 128 (one per SIMD);
+// WN = 4: 8 waves of 128 x 64 (two per SIMD, so that one wave's LDS and DMA
+// instructions issue while the other wave's MFMAs run -- a single wave per
+// SIMD serialises its memory instructions with its own MFMAs).
+template <int IN, int OUT, bool SLICE, int WN>
+__global__ __launch_bounds__(128 * WN, WN / 2) void gemm_dma_kernel(GemmArgs g) {
   using T = InT<IN>;
   constexpr int EB = T::EB;
   constexpr int BKE = SKB / EB;              // K elements per stage
@@ -68,12 +75,22 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmArgs g) {
   constexpr int BROW = TBN * EB;             // bytes per B row in LDS
   constexpr int BSLOTS = BROW / 16;
   constexpr int BROWS_PER_DMA = 1024 / BROW; // B rows written by one DMA instruction
+  constexpr int WAVES = 2 * WN;
+  constexpr int WTN = TBN / WN;              // wave tile columns (128 or 64)
+  constexpr int FN = WTN / 32;               // MFMA column blocks per wave
+  constexpr int NM = 4 * FN;                 // MFMAs per k-step per wave
+  constexpr int DPW = 32 / WAVES;            // DMA instructions per wave per stage
+  constexpr int DA = DPW / 2;                // ... of which for A (the rest for B)
+  // fragment reads per k-step: A blocks, then B pieces
+  constexpr int NRA = EB == 2 ? 4 : 8;
+  constexpr int NRB = EB == 2 ? 2 * FN : 4 * FN;
+  constexpr int NREAD = NRA + NRB;
 
   __shared__ __attribute__((aligned(1024))) char lds[NS * STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (uniform)
-  const int wm = w >> 1, wn = w & 1;
+  const int wm = w / WN, wn = w % WN;
   const int h = lane >> 5, l32 = lane & 31;
 
   int64_t ksl, pm, pn;
@@ -85,25 +102,26 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmArgs g) {
   const char* A = static_cast<const char*>(g.A);
   const char* B = static_cast<const char*>(g.B);
 
-  // ---- DMA geometry of this lane (the same for every stage).  Offsets of
-  // rows past M / columns past N are replaced by an out-of-range offset once;
-  // the K check is only needed in a partial last stage.
-  unsigned a_off[4], b_off[4];
-  int a_kel[4], b_k[4];
+  // ---- DMA geometry of this lane (the same for every stage).  The 32
+  // one-kilobyte DMA instructions of a stage (16 for A, 16 for B) are spread
+  // over the waves.  Offsets of rows past M / columns past N are replaced by
+  // an out-of-range offset once; the K check only matters in a partial stage.
+  unsigned a_off[DA], b_off[DA];
+  int a_kel[DA], b_k[DA];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = 16 * (4 * w + i) + (lane >> 2);
+  for (int i = 0; i < DA; ++i) {
+    const int idx = w * DA + i;
+    const int row = 16 * idx + (lane >> 2);
     const int c = (lane & 3) ^ ((row >> 2) & 3);
     a_off[i] = (m0 + row < g.M) ? (unsigned)(row * g.K * EB + c * 16) : OOB;
     a_kel[i] = c * (16 / EB);
-    const int k = BROWS_PER_DMA * (4 * w + i) + lane / BSLOTS;
+    const int k = BROWS_PER_DMA * idx + lane / BSLOTS;
     const int s = lane % BSLOTS;
     const int cb = EB == 2 ? (s ^ ((k & 3) << 2)) : (s ^ ((k & 7) << 1));
     b_off[i] = (n0 + cb * (16 / EB) < g.N) ? (unsigned)(k * g.N * EB + cb * 16) : OOB;
     b_k[i] = k;
   }
 
-  // Buffer descriptors of stage t and whether it is a full stage.
   struct StageSrc {
     const char* pa;  // first byte of the stage's A block (row m0)
     const char* pb;  // first byte of the stage's B block (column n0)
@@ -117,26 +135,26 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmArgs g) {
     q.rem = kend - kst < BKE ? (int)(kend - kst) : BKE;
     return q;
   };
-  // DMA instruction x (0..3: A rows, 4..7: B rows) of stage t into LDS slot t % NS.
+  // DMA instruction x of this wave (x < DA: A rows, else B rows) of stage t.
   auto dma_one = [&](const StageSrc& q, int t, int x) {
     char* sb = lds + (t % NS) * STAGE;
-    if (x < 4) {
+    if (x < DA) {
       const unsigned off = a_kel[x] < q.rem ? a_off[x] : OOB;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           __builtin_amdgcn_make_buffer_rsrc((void*)q.pa, 0, NREC, RSRC_FLAGS),
-          IMM_LDS(sb + (4 * w + x) * 1024), 16, off, 0, 0, 0);
+          IMM_LDS(sb + (w * DA + x) * 1024), 16, off, 0, 0, 0);
     } else {
-      const int i = x - 4;
+      const int i = x - DA;
       const unsigned off = b_k[i] < q.rem ? b_off[i] : OOB;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           __builtin_amdgcn_make_buffer_rsrc((void*)q.pb, 0, NREC, RSRC_FLAGS),
-          IMM_LDS(sb + A_STAGE + (4 * w + i) * 1024), 16, off, 0, 0, 0);
+          IMM_LDS(sb + A_STAGE + (w * DA + i) * 1024), 16, off, 0, 0, 0);
     }
   };
   auto dma = [&](int t) {
     const StageSrc q = stage_src(t);
 #pragma unroll
-    for (int x = 0; x < 8; ++x) dma_one(q, t, x);
+    for (int x = 0; x < DPW; ++x) dma_one(q, t, x);
   };
 
   // ---- fragment read offsets within a stage.
@@ -145,20 +163,20 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmArgs g) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) a_rd[i] = (wm * 128 + i * 32 + l32) * SKB;
   const int grp = lane >> 4, gi = lane & 15;
-  int b_rd[4];  // per column block j: byte offset of the first transposing read
+  int b_rd[FN];  // per column block j: byte offset of the first transposing read
   if constexpr (EB == 2) {
     const int t_ = gi >> 2, q = gi & 3;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int n = wn * 128 + j * 32 + 16 * (grp & 1) + 4 * q;
+    for (int j = 0; j < FN; ++j) {
+      const int n = wn * WTN + j * 32 + 16 * (grp & 1) + 4 * q;
       const int k = 8 * (grp >> 1) + t_;
       b_rd[j] = A_STAGE + k * BROW + (((n >> 3) ^ (t_ << 2)) << 4) + (q & 1) * 8;
     }
   } else {
     const int t_ = gi >> 1, q = gi & 1;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int n = wn * 128 + j * 32 + 16 * (grp & 1) + 8 * q;
+    for (int j = 0; j < FN; ++j) {
+      const int n = wn * WTN + j * 32 + 16 * (grp & 1) + 8 * q;
       const int k = 32 * (grp >> 1) + t_;
       b_rd[j] = A_STAGE + k * BROW + (((n >> 4) ^ (t_ << 1)) << 4) + q * 8;
     }
@@ -168,19 +186,18 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmArgs g) {
   const unsigned lds_addr = (unsigned)(uintptr_t)((__attribute__((address_space(3))) char*)lds);
 
   // Fragment read x of k-step ks of LDS slot `slot` into F.
-  //   16-bit: x = 0..3 -> A block i = x (one ds_read_b128);
-  //           x = 4..11 -> B block j = (x-4)/2, half r = (x-4)%2 (K elements 4r..4r+3).
-  //   fp8:    x = 0..7 -> A block i = x/2, half x%2 (16 bytes of K each);
-  //           x = 8..23 -> B block j = (x-8)/4, piece r = (x-8)%4 (8 K values).
-  constexpr int NREAD = EB == 2 ? 12 : 24;
-  auto read_one = [&](Frag<IN>& F, int slot, int ks, int x) {
+  //   16-bit: x < 4 -> A block i = x (one ds_read_b128);
+  //           else B block j = (x-4)/2, half r = (x-4)%2 (K elements 4r..4r+3).
+  //   fp8:    x < 8 -> A block i = x/2, half x%2 (16 bytes of K each);
+  //           else B block j = (x-8)/4, piece r = (x-8)%4 (8 K values).
+  auto read_one = [&](Frag<IN, FN>& F, int slot, int ks, int x) {
     const char* sb = lds + slot;
     if constexpr (EB == 2) {
-      if (x < 4) {
+      if (x < NRA) {
         const int c = ks * 2 + h;
         F.a[x] = *reinterpret_cast<const i32x4*>(sb + a_rd[x] + ((c ^ asw) << 4));
       } else {
-        const int j = (x - 4) >> 1, r = (x - 4) & 1;
+        const int j = (x - NRA) >> 1, r = (x - NRA) & 1;
         const unsigned p0 = lds_addr + slot + b_rd[j];
         i32x2 v;
         if (ks == 0)
@@ -191,14 +208,14 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmArgs g) {
         F.b[j][2 * r + 1] = v[1];
       }
     } else {
-      if (x < 8) {
+      if (x < NRA) {
         const int i = x >> 1, f = x & 1;
         const i32x4 v =
             *reinterpret_cast<const i32x4*>(sb + a_rd[i] + (((2 * h + f) ^ asw) << 4));
 #pragma unroll
         for (int e = 0; e < 4; ++e) F.a[i][4 * f + e] = v[e];
       } else {
-        const int j = (x - 8) >> 2, r = (x - 8) & 3;
+        const int j = (x - NRA) >> 2, r = (x - NRA) & 3;
         const unsigned p0 = lds_addr + slot + b_rd[j];
         i32x2 v;
         if (r == 0) v = ds_read_tr8_b64<0>(p0);
@@ -220,104 +237,96 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmArgs g) {
     __builtin_amdgcn_s_waitcnt(lgkmcnt_imm(0));
     fence();
   };
-  f32x16 acc[4][4];
+
+  f32x16 acc[4][FN];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
-
-  auto mfma_x = [&](const Frag<IN>& F, int x) {
-    acc[x >> 2][x & 3] = mfma_v<IN>(F.a[x >> 2], F.b[x & 3], acc[x >> 2][x & 3]);
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{};
+  auto mfma_x = [&](const Frag<IN, FN>& F, int x) {
+    acc[x / FN][x % FN] = mfma_v<IN>(F.a[x / FN], F.b[x % FN], acc[x / FN][x % FN]);
   };
 
-  Frag<IN> F0, F1;
+  Frag<IN, FN> F0, F1;
   if (nt > 0) {
-    const int pre = nt < NS ? nt : NS;
-    for (int p = 0; p < pre; ++p) dma(p);
-    // stage 0 landed: pre - 1 stages were requested after it
-    if (pre >= 4)
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(24));
-    else if (pre == 3)
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(16));
-    else if (pre == 2)
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(8));
-    else
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    for (int p = 0; p < NS; ++p) dma(p);
+    // stage 0 landed: NS - 1 stages were requested after it
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 1) * DPW));
     __builtin_amdgcn_s_barrier();
     fence();
 #pragma unroll
     for (int x = 0; x < NREAD; ++x) read_one(F0, 0, 0, x);
   }
 
-  // Second half of the last k-step of stage t, with the stage change folded
-  // in: wait for this wave's DMA of stage t+1, barrier (every wave's data of
-  // t+1 has landed and every wave holds stage t in registers), then issue the
-  // DMA of stage t+NS into slot t % NS and the fragment reads of stage t+1,
-  // one or more between consecutive MFMAs.
-  auto boundary_half = [&](int t, const Frag<IN>& Fc, Frag<IN>& Fn) {
-    const bool next = t + 1 < nt;
-    if (next) {
-      const int last_req = (nt - 1 < t + NS - 1) ? nt - 1 : t + NS - 1;
-      const int ahead = last_req - (t + 1);
-      fence();
-      if (ahead >= 2)
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(16));
-      else if (ahead == 1)
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(8));
-      else
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-      __builtin_amdgcn_s_waitcnt(lgkmcnt_imm(0));
-      __builtin_amdgcn_s_barrier();
-      fence();
-    }
-    const bool refill = t + NS < nt;
-    const StageSrc q = stage_src(t + NS);
-    const int nslot = ((t + 1) % NS) * STAGE;
+  // The stage change sits at the start of the last k-step of stage t: once a
+  // wave's fragment reads of that k-step have landed it has read all of stage
+  // t, so after it waits for its own DMA of stage t+1 a single barrier
+  // certifies that (a) stage t+1 is in LDS for every wave and (b) no wave
+  // reads slot t % NS any more.  The whole last k-step then overlaps the DMA
+  // of stage t+NS into that slot and the fragment reads of stage t+1.
+  auto stage_change = [&]() {
+    fence();
+    // DMA is issued for every stage index in order (past the end of the
+    // slice it only writes zeros), so after stage t+1 exactly the stages t+2
+    // and t+3 can still be in flight.
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 2) * DPW));
+    __builtin_amdgcn_s_barrier();
+    fence();
+  };
+  // MFMAs of one k-step on Fc, with the DMA of stage td (if dma_on) and the
+  // fragment reads of k-step ks of stage tr into Fn spread between them.
+  // Every stage runs the same instructions: a refill past the end of the
+  // slice has only out-of-range offsets (zero fill, no memory traffic) and
+  // the reads past the last stage land in registers that are never used.
+  auto kstep = [&](bool dma_on, const Frag<IN, FN>& Fc, int td, Frag<IN, FN>& Fn, int tr,
+                   int ks) {
+    const StageSrc q = stage_src(td);
+    const int slot = (tr % NS) * STAGE;
 #pragma unroll
-    for (int x = 0; x < 8; ++x) {
-      mfma_x(Fc, 8 + x);
-      if (refill) dma_one(q, t + NS, x);
-      if (next) {
+    for (int x = 0; x < NM; ++x) {
+      mfma_x(Fc, x);
+      if (dma_on) {
 #pragma unroll
-        for (int y = x * NREAD / 8; y < (x + 1) * NREAD / 8; ++y) read_one(Fn, nslot, 0, y);
+        for (int y = x * DPW / NM; y < (x + 1) * DPW / NM; ++y) dma_one(q, td, y);
       }
+#pragma unroll
+      for (int y = x * NREAD / NM; y < (x + 1) * NREAD / NM; ++y) read_one(Fn, slot, ks, y);
       fence();
     }
   };
 
   if constexpr (KS == 2) {
     for (int t = 0; t < nt; ++t) {
-      const int slot = (t % NS) * STAGE;
       lds_wait();  // F0 (stage t, k-step 0) has landed
-#pragma unroll
-      for (int x = 0; x < 16; ++x) {
-        mfma_x(F0, x);
-        if (x < NREAD) read_one(F1, slot, 1, x);
-        fence();
-      }
-      lds_wait();  // F1 (stage t, k-step 1) has landed
-#pragma unroll
-      for (int x = 0; x < 8; ++x) mfma_x(F1, x);
-      boundary_half(t, F1, F0);
+      kstep(false, F0, t, F1, t, 1);
+      lds_wait();  // F1 has landed: this wave has read all of stage t
+      stage_change();
+      kstep(true, F1, t + NS, F0, t + 1, 0);
     }
   } else {
-    for (int t = 0; t < nt; ++t) {
-      lds_wait();  // F0 (stage t) has landed
-#pragma unroll
-      for (int x = 0; x < 8; ++x) mfma_x(F0, x);
-      boundary_half(t, F0, F1);
-      lds_wait();  // F1 (stage t+1) has landed before it is copied
-      F0 = F1;
+    // one k-step per stage; fragments alternate between F0 and F1
+    for (int t = 0; t < nt; t += 2) {
+      lds_wait();  // F0 (stage t) has landed: this wave has read all of stage t
+      stage_change();
+      kstep(true, F0, t + NS, F1, t + 1, 0);
+      if (t + 1 < nt) {
+        lds_wait();
+        stage_change();
+        kstep(true, F1, t + 1 + NS, F0, t + 2, 0);
+      }
     }
   }
+  // No LDS transfer or read may still be in flight when the workgroup ends.
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  __builtin_amdgcn_s_waitcnt(lgkmcnt_imm(0));
 
   // Write-back.  32x32 accumulator layout: lane l, register r holds
   // row 8*(r/4) + 4*(l/32) + r%4, column l%32 of the block.
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t col = n0 + wn * 128 + j * 32 + l32;
+    for (int j = 0; j < FN; ++j) {
+      const int64_t col = n0 + wn * WTN + j * 32 + l32;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int64_t row = m0 + wm * 128 + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
@@ -334,29 +343,38 @@ __global__ __launch_bounds__(256, 1) void gemm_dma_kernel(GemmArgs g) {
   }
 }
 
-template <int IN>
+template <int IN, int WN>
 hipError_t launch_in(const gemm_plan_s& p, const GemmArgs& a, bool slice, hipStream_t s) {
-  const dim3 grid((unsigned)a.grid), block(256);
+  const dim3 grid((unsigned)a.grid), block(128 * WN);
   if (slice)
-    hipLaunchKernelGGL((gemm_dma_kernel<IN, GEMM_F32, true>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((gemm_dma_kernel<IN, GEMM_F32, true, WN>), grid, block, 0, s, a);
   else if (p.out == GEMM_F32)
-    hipLaunchKernelGGL((gemm_dma_kernel<IN, GEMM_F32, false>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((gemm_dma_kernel<IN, GEMM_F32, false, WN>), grid, block, 0, s, a);
   else
-    hipLaunchKernelGGL((gemm_dma_kernel<IN, GEMM_BF16, false>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((gemm_dma_kernel<IN, GEMM_BF16, false, WN>), grid, block, 0, s, a);
   return hipGetLastError();
+}
+
+template <int WN>
+hipError_t launch_wn(const gemm_plan_s& p, const GemmArgs& a, bool slice, hipStream_t s) {
+  switch (p.in) {
+    case GEMM_F16: return launch_in<GEMM_F16, WN>(p, a, slice, s);
+    case GEMM_BF16: return launch_in<GEMM_BF16, WN>(p, a, slice, s);
+    case GEMM_F8_E4M3: return launch_in<GEMM_F8_E4M3, WN>(p, a, slice, s);
+    case GEMM_F8_E5M2: return launch_in<GEMM_F8_E5M2, WN>(p, a, slice, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace
 
 hipError_t launch_gemm_dma(const gemm_plan_s& p, const GemmArgs& a, bool slice_mode,
                            hipStream_t s) {
-  switch (p.in) {
-    case GEMM_F16: return launch_in<GEMM_F16>(p, a, slice_mode, s);
-    case GEMM_BF16: return launch_in<GEMM_BF16>(p, a, slice_mode, s);
-    case GEMM_F8_E4M3: return launch_in<GEMM_F8_E4M3>(p, a, slice_mode, s);
-    case GEMM_F8_E5M2: return launch_in<GEMM_F8_E5M2>(p, a, slice_mode, s);
-    default: return hipErrorInvalidValue;
-  }
+#ifdef IMM_DMA_WN
+  return launch_wn<IMM_DMA_WN>(p, a, slice_mode, s);
+#else
+  return launch_wn<4>(p, a, slice_mode, s);
+#endif
 }
 
 }  // namespace imm
