@@ -3,22 +3,26 @@
 // Citations: [TDI] = Tencent engineer article on deterministic LLM inference
 // ("AI インフラの深化：大規模モデルに確定的な出力を実現する方法").
 //
-// One workgroup of 4 waves (one per SIMD) owns a 256 x 256 tile of C (or of
-// one K slice of it); each wave owns a 128 x 128 quarter held in 256 fp32
-// accumulators per lane (the AGPR file).  K is walked in ascending stages of
-// 64 bytes of K per row ([TDI] "Tiling - 分塊行列乗算": load, compute,
-// accumulate per K step, one write-back at the end).
+// One workgroup of 8 waves (two per SIMD) owns a 256 x 256 tile of C (or of
+// one K slice of it); each wave owns a 128 x 64 block held in 128 fp32
+// accumulators per lane.  K is walked in ascending stages ([TDI] "Tiling -
+// 分塊行列乗算": load, compute, accumulate per K step, one write-back at the
+// end).  Two waves per SIMD, because a single wave serialises its own LDS and
+// DMA instructions with its MFMAs while a second wave's memory instructions
+// overlap the first wave's MFMAs (both measured).
 //
 // Memory pipeline ([TDI] "演算子チューニング": latency is hidden by
-// multi-buffering rather than by occupancy).  A ring of 4 LDS stages (32 KB
-// each) is filled by buffer_load ... lds: every lane moves 16 bytes straight
-// from HBM/L2 into LDS, no registers, no LDS-store instructions, and an
-// out-of-range offset writes zeros (used for rows past M, columns past N and
-// K past the end of the slice).  Stage t+4 is requested while stage t+1 is
-// computed, so three stages of loads are in flight behind the math.
+// multi-buffering rather than by occupancy).  A ring of 2 LDS stages of 128
+// bytes of K per row (64 KB each: 32 KB of A, 32 KB of B) is filled by
+// buffer_load ... lds: every lane moves 16 bytes straight from L2/HBM into
+// LDS, no registers, no LDS-store instructions, and an out-of-range offset
+// writes zeros (used for rows past M, columns past N and K past the end of
+// the slice).  128-byte rows make every A request one whole cache line
+// (64-byte rows, which would allow a 4-deep ring, measured slower, as did a
+// 3-slot A ring beside a 2-slot B ring and L2 prefetching of later stages).
 //
-// LDS layouts.  A is stored K-contiguous (64 bytes per row, 4 slots of 16
-// bytes, slot c of row r at c ^ ((r >> 2) & 3)), read with ds_read_b128.
+// LDS layouts.  A is stored K-contiguous (128 bytes per row in 16-byte
+// slots, slot c of row r at c ^ ((r >> 1) & 7)), read with ds_read_b128.
 // B is stored as it lies in memory, N-contiguous (512 bytes per K row for
 // 16-bit, 256 for fp8), and read with the gfx950 transposing LDS reads
 // (ds_read_b64_tr_b16 / _b8), which hand each lane the K-contiguous column
@@ -45,46 +49,73 @@ namespace imm {
 namespace {
 using namespace dev;
 
-constexpr int NS = 4;             // LDS stages
-constexpr int SKB = 64;           // bytes of K per row per stage
 constexpr int TBM = 256, TBN = 256;
-constexpr int A_STAGE = TBM * SKB;  // 16 KB
-constexpr int B_STAGE = 16384;      // (64 / eb) K rows x 256 columns x eb
-constexpr int STAGE = A_STAGE + B_STAGE;
+constexpr int SKB = 128;  // bytes of K per row per stage
+constexpr int NS = 2;     // stages in the LDS ring
 constexpr unsigned OOB = 0x80000000u;
 constexpr int NREC = 0x7fffffff;
 constexpr int RSRC_FLAGS = 0x00020000;
 
-// Fragments of one MFMA k-step of one wave: FM blocks of A (rows), FN of B.
+// Fragments of one MFMA k-step of one wave: 4 blocks of A (rows), FN of B.
 template <int IN, int FN>
 struct Frag {
   typename FragOf<IN>::type a[4];
   typename FragOf<IN>::type b[FN];
 };
 
-// WN waves along N, 2 along M.  WN = 2: 4 waves of 128 x 128 (one per SIMD);
-// WN = 4: 8 waves of 128 x 64 (two per SIMD, so that one wave's LDS and DMA
-// instructions issue while the other wave's MFMAs run -- a single wave per
-// SIMD serialises its memory instructions with its own MFMAs).
-template <int IN, int OUT, bool SLICE, int WN>
-__global__ __launch_bounds__(128 * WN, WN / 2) void gemm_dma_kernel(GemmArgs g) {
+// Transposing reads at a compile-time row offset (immediate field); `rows`
+// is constant after unrolling, the switch folds away.
+template <int BROW>
+__device__ __forceinline__ i32x2 tr16_rows(unsigned p0, int rows) {
+  switch (rows) {
+    case 0: return ds_read_tr16_b64<0>(p0);
+    case 4: return ds_read_tr16_b64<4 * BROW>(p0);
+    case 16: return ds_read_tr16_b64<16 * BROW>(p0);
+    case 20: return ds_read_tr16_b64<20 * BROW>(p0);
+    case 32: return ds_read_tr16_b64<32 * BROW>(p0);
+    case 36: return ds_read_tr16_b64<36 * BROW>(p0);
+    case 48: return ds_read_tr16_b64<48 * BROW>(p0);
+    default: return ds_read_tr16_b64<52 * BROW>(p0);
+  }
+}
+template <int BROW>
+__device__ __forceinline__ i32x2 tr8_rows(unsigned p0, int rows) {
+  switch (rows) {
+    case 0: return ds_read_tr8_b64<0>(p0);
+    case 8: return ds_read_tr8_b64<8 * BROW>(p0);
+    case 16: return ds_read_tr8_b64<16 * BROW>(p0);
+    case 24: return ds_read_tr8_b64<24 * BROW>(p0);
+    case 64: return ds_read_tr8_b64<64 * BROW>(p0);
+    case 72: return ds_read_tr8_b64<72 * BROW>(p0);
+    case 80: return ds_read_tr8_b64<80 * BROW>(p0);
+    default: return ds_read_tr8_b64<88 * BROW>(p0);
+  }
+}
+
+template <int IN, int OUT, bool SLICE>
+__global__ __launch_bounds__(512, 2) void gemm_dma_kernel(GemmArgs g) {
   using T = InT<IN>;
   constexpr int EB = T::EB;
-  constexpr int BKE = SKB / EB;              // K elements per stage
-  constexpr int KS = SKB / T::KSTEP_B;       // MFMA k-steps per stage (2 or 1)
+  constexpr int WAVES = 8, WN = 4;           // 2 x 4 waves
+  constexpr int WTN = TBN / WN;              // wave tile columns (64)
+  constexpr int FN = WTN / 32;               // MFMA column blocks per wave (2)
+  constexpr int NM = 4 * FN;                 // MFMAs per k-step per wave (8)
+  constexpr int A_STAGE = TBM * SKB;         // bytes of A per stage
+  constexpr int STAGE = 2 * A_STAGE;         // A + B (B has as many bytes as A)
+  constexpr int BKE = SKB / EB;              // K elements (= B rows) per stage
+  constexpr int KS = SKB / T::KSTEP_B;       // MFMA k-steps per stage
+  constexpr int ACH = SKB / 16;              // 16-byte slots per A row
+  constexpr int AROWS_PER_DMA = 1024 / SKB;  // A rows written by one DMA instruction
   constexpr int BROW = TBN * EB;             // bytes per B row in LDS
   constexpr int BSLOTS = BROW / 16;
   constexpr int BROWS_PER_DMA = 1024 / BROW; // B rows written by one DMA instruction
-  constexpr int WAVES = 2 * WN;
-  constexpr int WTN = TBN / WN;              // wave tile columns (128 or 64)
-  constexpr int FN = WTN / 32;               // MFMA column blocks per wave
-  constexpr int NM = 4 * FN;                 // MFMAs per k-step per wave
-  constexpr int DPW = 32 / WAVES;            // DMA instructions per wave per stage
+  constexpr int DPW = (2 * A_STAGE / 1024) / WAVES;  // DMA instructions per wave per stage
   constexpr int DA = DPW / 2;                // ... of which for A (the rest for B)
-  // fragment reads per k-step: A blocks, then B pieces
-  constexpr int NRA = EB == 2 ? 4 : 8;
-  constexpr int NRB = EB == 2 ? 2 * FN : 4 * FN;
+  constexpr int NRA = EB == 2 ? 4 : 8;       // fragment reads per k-step: A ...
+  constexpr int NRB = EB == 2 ? 2 * FN : 4 * FN;  // ... and B
   constexpr int NREAD = NRA + NRB;
+  static_assert(NS * STAGE <= 160 * 1024, "LDS ring too large");
+  static_assert(KS % 2 == 0, "k-steps per stage");
 
   __shared__ __attribute__((aligned(1024))) char lds[NS * STAGE];
 
@@ -102,17 +133,19 @@ __global__ __launch_bounds__(128 * WN, WN / 2) void gemm_dma_kernel(GemmArgs g) 
   const char* A = static_cast<const char*>(g.A);
   const char* B = static_cast<const char*>(g.B);
 
-  // ---- DMA geometry of this lane (the same for every stage).  The 32
-  // one-kilobyte DMA instructions of a stage (16 for A, 16 for B) are spread
-  // over the waves.  Offsets of rows past M / columns past N are replaced by
-  // an out-of-range offset once; the K check only matters in a partial stage.
+  // A row r keeps its 16-byte slot c at c ^ aswz(r).
+  auto aswz = [](int r) { return (r >> 1) & 7; };
+
+  // ---- DMA geometry of this lane (the same for every stage).  Offsets of
+  // rows past M / columns past N are replaced by an out-of-range offset once;
+  // the K check only matters in a partial stage.
   unsigned a_off[DA], b_off[DA];
   int a_kel[DA], b_k[DA];
 #pragma unroll
   for (int i = 0; i < DA; ++i) {
     const int idx = w * DA + i;
-    const int row = 16 * idx + (lane >> 2);
-    const int c = (lane & 3) ^ ((row >> 2) & 3);
+    const int row = AROWS_PER_DMA * idx + lane / ACH;
+    const int c = (lane % ACH) ^ aswz(row);
     a_off[i] = (m0 + row < g.M) ? (unsigned)(row * g.K * EB + c * 16) : OOB;
     a_kel[i] = c * (16 / EB);
     const int k = BROWS_PER_DMA * idx + lane / BSLOTS;
@@ -158,7 +191,7 @@ __global__ __launch_bounds__(128 * WN, WN / 2) void gemm_dma_kernel(GemmArgs g) 
   };
 
   // ---- fragment read offsets within a stage.
-  const int asw = (l32 >> 2) & 3;
+  const int asw = aswz(l32);  // rows of a fragment differ from l32 by multiples of 32
   int a_rd[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) a_rd[i] = (wm * 128 + i * 32 + l32) * SKB;
@@ -198,30 +231,20 @@ __global__ __launch_bounds__(128 * WN, WN / 2) void gemm_dma_kernel(GemmArgs g) 
         F.a[x] = *reinterpret_cast<const i32x4*>(sb + a_rd[x] + ((c ^ asw) << 4));
       } else {
         const int j = (x - NRA) >> 1, r = (x - NRA) & 1;
-        const unsigned p0 = lds_addr + slot + b_rd[j];
-        i32x2 v;
-        if (ks == 0)
-          v = r == 0 ? ds_read_tr16_b64<0>(p0) : ds_read_tr16_b64<4 * BROW>(p0);
-        else
-          v = r == 0 ? ds_read_tr16_b64<16 * BROW>(p0) : ds_read_tr16_b64<20 * BROW>(p0);
+        const i32x2 v = tr16_rows<BROW>(lds_addr + slot + b_rd[j], ks * 16 + 4 * r);
         F.b[j][2 * r] = v[0];
         F.b[j][2 * r + 1] = v[1];
       }
     } else {
       if (x < NRA) {
         const int i = x >> 1, f = x & 1;
-        const i32x4 v =
-            *reinterpret_cast<const i32x4*>(sb + a_rd[i] + (((2 * h + f) ^ asw) << 4));
+        const int c = ks * 4 + 2 * h + f;
+        const i32x4 v = *reinterpret_cast<const i32x4*>(sb + a_rd[i] + ((c ^ asw) << 4));
 #pragma unroll
         for (int e = 0; e < 4; ++e) F.a[i][4 * f + e] = v[e];
       } else {
         const int j = (x - NRA) >> 2, r = (x - NRA) & 3;
-        const unsigned p0 = lds_addr + slot + b_rd[j];
-        i32x2 v;
-        if (r == 0) v = ds_read_tr8_b64<0>(p0);
-        else if (r == 1) v = ds_read_tr8_b64<8 * BROW>(p0);
-        else if (r == 2) v = ds_read_tr8_b64<16 * BROW>(p0);
-        else v = ds_read_tr8_b64<24 * BROW>(p0);
+        const i32x2 v = tr8_rows<BROW>(lds_addr + slot + b_rd[j], ks * 64 + 8 * r);
         F.b[j][2 * r] = v[0];
         F.b[j][2 * r + 1] = v[1];
       }
@@ -267,8 +290,8 @@ __global__ __launch_bounds__(128 * WN, WN / 2) void gemm_dma_kernel(GemmArgs g) 
   auto stage_change = [&]() {
     fence();
     // DMA is issued for every stage index in order (past the end of the
-    // slice it only writes zeros), so after stage t+1 exactly the stages t+2
-    // and t+3 can still be in flight.
+    // slice it only writes zeros), so after stage t+1 exactly NS-2 later
+    // stages can still be in flight.
     __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 2) * DPW));
     __builtin_amdgcn_s_barrier();
     fence();
@@ -295,26 +318,19 @@ __global__ __launch_bounds__(128 * WN, WN / 2) void gemm_dma_kernel(GemmArgs g) 
     }
   };
 
-  if constexpr (KS == 2) {
-    for (int t = 0; t < nt; ++t) {
-      lds_wait();  // F0 (stage t, k-step 0) has landed
-      kstep(false, F0, t, F1, t, 1);
-      lds_wait();  // F1 has landed: this wave has read all of stage t
-      stage_change();
-      kstep(true, F1, t + NS, F0, t + 1, 0);
+  // k-steps alternate between F0 and F1; KS is even, so every stage starts on F0
+  for (int t = 0; t < nt; ++t) {
+#pragma unroll
+    for (int ks = 0; ks + 1 < KS; ++ks) {
+      lds_wait();  // fragments of k-step ks have landed
+      if (ks % 2 == 0)
+        kstep(false, F0, t, F1, t, ks + 1);
+      else
+        kstep(false, F1, t, F0, t, ks + 1);
     }
-  } else {
-    // one k-step per stage; fragments alternate between F0 and F1
-    for (int t = 0; t < nt; t += 2) {
-      lds_wait();  // F0 (stage t) has landed: this wave has read all of stage t
-      stage_change();
-      kstep(true, F0, t + NS, F1, t + 1, 0);
-      if (t + 1 < nt) {
-        lds_wait();
-        stage_change();
-        kstep(true, F1, t + 1 + NS, F0, t + 2, 0);
-      }
-    }
+    lds_wait();  // last k-step's fragments landed: this wave has read all of stage t
+    stage_change();
+    kstep(true, F1, t + NS, F0, t + 1, 0);
   }
   // No LDS transfer or read may still be in flight when the workgroup ends.
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
@@ -343,38 +359,29 @@ __global__ __launch_bounds__(128 * WN, WN / 2) void gemm_dma_kernel(GemmArgs g) 
   }
 }
 
-template <int IN, int WN>
+template <int IN>
 hipError_t launch_in(const gemm_plan_s& p, const GemmArgs& a, bool slice, hipStream_t s) {
-  const dim3 grid((unsigned)a.grid), block(128 * WN);
+  const dim3 grid((unsigned)a.grid), block(512);
   if (slice)
-    hipLaunchKernelGGL((gemm_dma_kernel<IN, GEMM_F32, true, WN>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((gemm_dma_kernel<IN, GEMM_F32, true>), grid, block, 0, s, a);
   else if (p.out == GEMM_F32)
-    hipLaunchKernelGGL((gemm_dma_kernel<IN, GEMM_F32, false, WN>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((gemm_dma_kernel<IN, GEMM_F32, false>), grid, block, 0, s, a);
   else
-    hipLaunchKernelGGL((gemm_dma_kernel<IN, GEMM_BF16, false, WN>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((gemm_dma_kernel<IN, GEMM_BF16, false>), grid, block, 0, s, a);
   return hipGetLastError();
-}
-
-template <int WN>
-hipError_t launch_wn(const gemm_plan_s& p, const GemmArgs& a, bool slice, hipStream_t s) {
-  switch (p.in) {
-    case GEMM_F16: return launch_in<GEMM_F16, WN>(p, a, slice, s);
-    case GEMM_BF16: return launch_in<GEMM_BF16, WN>(p, a, slice, s);
-    case GEMM_F8_E4M3: return launch_in<GEMM_F8_E4M3, WN>(p, a, slice, s);
-    case GEMM_F8_E5M2: return launch_in<GEMM_F8_E5M2, WN>(p, a, slice, s);
-    default: return hipErrorInvalidValue;
-  }
 }
 
 }  // namespace
 
 hipError_t launch_gemm_dma(const gemm_plan_s& p, const GemmArgs& a, bool slice_mode,
                            hipStream_t s) {
-#ifdef IMM_DMA_WN
-  return launch_wn<IMM_DMA_WN>(p, a, slice_mode, s);
-#else
-  return launch_wn<4>(p, a, slice_mode, s);
-#endif
+  switch (p.in) {
+    case GEMM_F16: return launch_in<GEMM_F16>(p, a, slice_mode, s);
+    case GEMM_BF16: return launch_in<GEMM_BF16>(p, a, slice_mode, s);
+    case GEMM_F8_E4M3: return launch_in<GEMM_F8_E4M3>(p, a, slice_mode, s);
+    case GEMM_F8_E5M2: return launch_in<GEMM_F8_E5M2>(p, a, slice_mode, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace imm
