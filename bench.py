@@ -12,7 +12,7 @@ products N=4096 K=14336 at M in {1, 8, 32, 128} through the split-K path
 cache), the huge-K product 256 x 256 x 131072 at split_k in {1, 8, 32, 128},
 and torch.matmul (hipBLASLt) on the headline shape as a run-only comparator.
 
-"roofline" reports the dominant kernel (the main-loop GEMM kernel) against
+"roofline" reports the dominant kernel (the DMA-fed 256x256 GEMM kernel) against
 the MI355X dense fp16 matrix peak: achieved = 2*M*N*K flop per launch divided
 by the kernel's average duration, timed with HIP events on the launch
 stream.  "cpu_baseline" times the CPU oracle (test infrastructure, fp64
@@ -35,7 +35,7 @@ PEAK_TFLOPS = {"f16": 2516.6, "bf16": 2516.6, "e4m3": 5033.2, "e5m2": 5033.2}
 PEAK_HBM_GBS = 8000.0
 MALL_BYTES = 256 * 2 ** 20
 KERNEL_SOURCES = [os.path.join(ROOT, "invariant_matmul_amd", "csrc", f)
-                  for f in ("gemm_kernels.hip", "imm_internal.h", "api.cpp")]
+                  for f in ("gemm_dma.hip", "kernel_common.h", "imm_internal.h", "api.cpp")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_square_f16_8192.json")
 
 
@@ -45,6 +45,49 @@ def kernel_source_hash() -> str:
         with open(p, "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
+
+
+COPY_BYTES = 256 * 2 ** 20  # the plain copy of the profile pass: this many bytes read and written
+
+
+def write_traffic(fetch_csv, write_csv):
+    """Turn two rocprofv3 --pmc runs of `bench.py --profile-pass` (FETCH_SIZE, then
+    WRITE_SIZE, KiB per dispatch) into the per-launch HBM traffic of the headline
+    kernel.  Each counter is scaled by what it reads for the plain copy of known
+    size in the same pass (FETCH_SIZE counts half the bytes a copy reads on this
+    part; WRITE_SIZE counts them all)."""
+    import csv
+
+    def per_kernel(path, counter):
+        copy, gemm = [], []
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] != counter:
+                    continue
+                v = float(r["Counter_Value"])
+                if "copyBuffer" in r["Kernel_Name"]:
+                    copy.append(v)
+                elif "gemm_dma_kernel<0, 4, false, 256" in r["Kernel_Name"]:
+                    gemm.append(v)
+        if not copy or not gemm:
+            raise SystemExit(f"{path}: no copy or headline-kernel dispatches with {counter}")
+        return statistics.mean(copy), statistics.mean(gemm), len(gemm)
+
+    cf, gf, n = per_kernel(fetch_csv, "FETCH_SIZE")
+    cw, gw, _ = per_kernel(write_csv, "WRITE_SIZE")
+    ff, wf = COPY_BYTES / 1024 / cf, COPY_BYTES / 1024 / cw
+    out = {"kernel": "gemm_dma_kernel<f16, f32 out, 256x256 tile>, M=N=K=8192",
+           "kernel_source_hash": kernel_source_hash(),
+           "fetch_kib_per_launch": gf, "write_kib_per_launch": gw, "launches": n,
+           "copy_fetch_kib": cf, "copy_write_kib": cw,
+           "fetch_scale": ff, "write_scale": wf,
+           "read_bytes_per_launch": gf * ff * 1024, "write_bytes_per_launch": gw * wf * 1024,
+           "bytes_per_launch": (gf * ff + gw * wf) * 1024}
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out))
 
 
 def log(msg):
@@ -152,7 +195,13 @@ def main():
     ap.add_argument("--profile-pass", action="store_true",
                     help="a few launches of the headline kernel plus a plain copy of known "
                          "size, for hardware-counter runs; prints nothing else")
+    ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="host only: write the headline kernel's HBM traffic from two "
+                         "counter runs of --profile-pass, then exit")
     args = ap.parse_args()
+    if args.write_traffic:
+        write_traffic(*args.write_traffic)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (this build has no multi-GPU path); "
               f"--gpus {args.gpus} is not supported", file=sys.stderr)
@@ -201,7 +250,7 @@ def main():
             traffic = t.get("bytes_per_launch")
     roofline = {"bound": "mfma", "achieved": achieved, "peak": PEAK_TFLOPS["f16"],
                 "unit": "TFLOP/s", "frac": achieved / PEAK_TFLOPS["f16"], "traffic": traffic,
-                "kernel": "gemm_tile_kernel<f16,f32,256x256>",
+                "kernel": "gemm_dma_kernel<f16, f32 out, 256x256 tile>",
                 "algorithmic_flop_per_launch": w.flops, "avg_launch_ms": kavg}
 
     extra = {"headline_kernel": summary(per),

@@ -91,10 +91,13 @@ typedef enum {
  * work in space. */
 typedef enum {
   GEMM_TILE_DEFAULT = 0,    /* chosen from (N, K, dtype) */
-  GEMM_TILE_256x256 = 1,    /* 4 waves, LDS ring filled by buffer->LDS DMA */
+  GEMM_TILE_256x256 = 1,    /* 8 waves, LDS ring filled by buffer->LDS DMA */
   GEMM_TILE_128x128 = 2,    /* 4 waves, register-staged LDS tiles */
   GEMM_TILE_32x128 = 3,     /* 4 waves, register-staged LDS tiles */
-  GEMM_TILE_256x256_RS = 4  /* 8 waves, register-staged LDS tiles */
+  GEMM_TILE_256x256_RS = 4, /* 8 waves, register-staged LDS tiles */
+  GEMM_TILE_32x256 = 5,     /* 4 waves, DMA ring; narrow tile for skinny or
+                               reduction-dominated shapes */
+  GEMM_TILE_64x256 = 6      /* 4 waves, DMA ring */
 } gemm_tile;
 
 typedef struct gemm_plan_s* gemm_plan_t;

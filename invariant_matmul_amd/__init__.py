@@ -29,7 +29,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libinvarian
 STATUS = {0: "GEMM_OK", 1: "GEMM_ERR_INVALID_VALUE", 2: "GEMM_ERR_UNSUPPORTED",
           3: "GEMM_ERR_WORKSPACE", 4: "GEMM_ERR_HIP"}
 DTYPE = {"f16": 0, "bf16": 1, "e4m3": 2, "e5m2": 3, "f32": 4}
-TILE = {"default": 0, "256x256": 1, "128x128": 2, "32x128": 3, "256x256_rs": 4}
+TILE = {"default": 0, "256x256": 1, "128x128": 2, "32x128": 3, "256x256_rs": 4, "32x256": 5,
+        "64x256": 6}
 EXPORTED_SYMBOLS = (
     "gemm_plan", "gemm_plan_ex", "gemm_plan_info", "gemm_workspace_size", "gemm_plan_tile_of",
     "gemm_run", "gemm_splitk_run", "gemm_plan_destroy", "gemm_status_string",

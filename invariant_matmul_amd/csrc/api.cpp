@@ -24,10 +24,6 @@ namespace {
 
 thread_local int g_last_hip_error = 0;
 
-// Number of workgroups the split heuristic aims for per output-tile row: two
-// per compute unit of a 256-CU MI355X.  A constant, not a device query, so a
-// plan (and therefore the bits) never depends on the machine it was made on.
-constexpr int64_t kTargetWorkgroups = 512;
 constexpr int kMaxSplit = 4096;
 
 bool valid_in(int dt) {
@@ -37,34 +33,54 @@ bool valid_out(int dt) { return dt == GEMM_F32 || dt == GEMM_BF16; }
 
 void tile_shape(int tile, int* bm, int* bn, int* wm, int* wn) {
   switch (tile) {
-    case GEMM_TILE_256x256: *bm = 256; *bn = 256; *wm = 2; *wn = 2; break;
+    case GEMM_TILE_256x256: *bm = 256; *bn = 256; *wm = 2; *wn = 4; break;
     case GEMM_TILE_256x256_RS: *bm = 256; *bn = 256; *wm = 2; *wn = 4; break;
     case GEMM_TILE_128x128: *bm = 128; *bn = 128; *wm = 2; *wn = 2; break;
+    case GEMM_TILE_32x256: *bm = 32; *bn = 256; *wm = 1; *wn = 4; break;
+    case GEMM_TILE_64x256: *bm = 64; *bn = 256; *wm = 1; *wn = 4; break;
     default: *bm = 32; *bn = 128; *wm = 1; *wn = 4; break;  // GEMM_TILE_32x128
   }
 }
 
 // Reduction-dominated shapes (K at least twice N): the regime where the
 // output has few tiles and split-K is the tool ([TDI] "Split-K": tiny M x N,
-// huge K; the parameter table restricts SPLIT_K to such shapes).  These get
-// the narrow 32-row tile; the rest get the large tile.
+// huge K; the parameter table restricts SPLIT_K to such shapes).  Wide ones
+// (decode-like, N > 512) get the narrow 32 x 128 tile, whose time is the
+// stream of B; narrow ones (N <= 512) get the 64 x 256 DMA tile, which reads
+// each slice of B once per 64 rows instead of once per 32.  The rest get the
+// large tile.
 bool reduction_dominated(int64_t N, int64_t K) { return K >= 2 * N; }
 
 int default_tile(int64_t N, int64_t K) {
-  return reduction_dominated(N, K) ? GEMM_TILE_32x128 : GEMM_TILE_256x256;
+  if (!reduction_dominated(N, K)) return GEMM_TILE_256x256;
+  return N <= 512 ? GEMM_TILE_64x256 : GEMM_TILE_32x128;
 }
+
+// Workgroups the default split aims for per row of output tiles.  Wide
+// shapes: two per compute unit of a 256-CU MI355X (512).  Narrow shapes
+// (N <= 512): 64, because there the row tiles multiply it -- at M = 256 the
+// 64 x 256 tile gives 4 x 64 = 256 workgroups, one per CU, and more slices
+// only add workspace traffic (measured: 64 slices beat 32 and 128 at
+// 256 x 256 x 131072).  Constants, not device queries, so a plan (and
+// therefore the bits) never depends on the machine it was made on.
+int64_t target_workgroups(int64_t N) { return N <= 512 ? 64 : 512; }
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+bool is_dma_tile(int tile) {
+  return tile == GEMM_TILE_256x256 || tile == GEMM_TILE_32x256 || tile == GEMM_TILE_64x256;
+}
+
 // Default split: only for reduction-dominated shapes; the largest power of two
-// that brings one tile-row of the grid to about kTargetWorkgroups while every
-// slice keeps at least 4 main-loop steps.
+// that brings one tile-row of the grid to about target_workgroups(N) while
+// every slice keeps at least 4 main-loop steps.
 int default_split(int64_t N, int64_t K, int bn, int bk) {
   if (!reduction_dominated(N, K)) return 1;
   const int64_t tiles_n = ceil_div(N, bn);
   const int64_t steps = ceil_div(K, bk);
+  const int64_t target = target_workgroups(N);
   int s = 1;
-  while (s * 2 <= kMaxSplit && tiles_n * s * 2 <= kTargetWorkgroups && steps / (s * 2) >= 4) s *= 2;
+  while (s * 2 <= kMaxSplit && tiles_n * s * 2 <= target && steps / (s * 2) >= 4) s *= 2;
   return s;
 }
 
@@ -126,7 +142,7 @@ gemm_status gemm_plan_ex(int64_t M, int64_t N, int64_t K, gemm_dtype in, gemm_dt
   if (M > INT_MAX || N > INT_MAX || K > INT_MAX) return GEMM_ERR_UNSUPPORTED;
   if (!valid_in(in) || !valid_out(out)) return GEMM_ERR_UNSUPPORTED;
   if (split_k < 0 || split_k > kMaxSplit || group_m < 0) return GEMM_ERR_UNSUPPORTED;
-  if (tile < GEMM_TILE_DEFAULT || tile > GEMM_TILE_256x256_RS) return GEMM_ERR_UNSUPPORTED;
+  if (tile < GEMM_TILE_DEFAULT || tile > GEMM_TILE_64x256) return GEMM_ERR_UNSUPPORTED;
   if (!std::isfinite(scale_a) || !std::isfinite(scale_b)) return GEMM_ERR_UNSUPPORTED;
   // 16-byte vector access of every row of A and B needs K and N to be
   // multiples of 16 bytes' worth of elements.
@@ -142,12 +158,16 @@ gemm_status gemm_plan_ex(int64_t M, int64_t N, int64_t K, gemm_dtype in, gemm_dt
   p->in = in;
   p->out = out;
   p->tile = tile == GEMM_TILE_DEFAULT ? default_tile(N, K) : tile;
-  // The DMA kernel addresses one 256-row A tile and one 64-byte-deep B stage
-  // with 32-bit offsets; beyond that the register-staged kernel (same bits)
-  // takes over.
-  if (p->tile == GEMM_TILE_256x256 &&
-      (256 * K * eb >= ((int64_t)1 << 31) - 64 || 64 * N * eb >= ((int64_t)1 << 31) - 64))
-    p->tile = GEMM_TILE_256x256_RS;
+  // The DMA kernels address one A tile (bm rows) and one B stage (128 bytes
+  // of K: 128 / eb rows of N elements) with 32-bit offsets; beyond that the
+  // register-staged kernels (same bits) take over.
+  if (is_dma_tile(p->tile)) {
+    int bm, bn, wm, wn;
+    tile_shape(p->tile, &bm, &bn, &wm, &wn);
+    const int64_t lim = ((int64_t)1 << 31) - 256;
+    if (bm * K * eb >= lim || 128 * N >= lim)
+      p->tile = p->tile == GEMM_TILE_256x256 ? GEMM_TILE_256x256_RS : GEMM_TILE_32x128;
+  }
   tile_shape(p->tile, &p->bm, &p->bn, &p->waves_m, &p->waves_n);
   p->bk = block_k_elems(in);
   p->group_m = group_m == 0 ? 8 : group_m;

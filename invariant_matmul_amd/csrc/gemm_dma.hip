@@ -49,17 +49,16 @@ namespace imm {
 namespace {
 using namespace dev;
 
-constexpr int TBM = 256, TBN = 256;
+constexpr int TBN = 256;  // tile columns (every configuration)
 constexpr int SKB = 128;  // bytes of K per row per stage
-constexpr int NS = 2;     // stages in the LDS ring
 constexpr unsigned OOB = 0x80000000u;
 constexpr int NREC = 0x7fffffff;
 constexpr int RSRC_FLAGS = 0x00020000;
 
-// Fragments of one MFMA k-step of one wave: 4 blocks of A (rows), FN of B.
-template <int IN, int FN>
+// Fragments of one MFMA k-step of one wave: FM blocks of A (rows), FN of B.
+template <int IN, int FM, int FN>
 struct Frag {
-  typename FragOf<IN>::type a[4];
+  typename FragOf<IN>::type a[FM];
   typename FragOf<IN>::type b[FN];
 };
 
@@ -92,16 +91,31 @@ __device__ __forceinline__ i32x2 tr8_rows(unsigned p0, int rows) {
   }
 }
 
-template <int IN, int OUT, bool SLICE>
-__global__ __launch_bounds__(512, 2) void gemm_dma_kernel(GemmArgs g) {
+// TBM x 256 tile of C per workgroup of WM x 4 waves; NS stages in the ring.
+//   TBM = 256, WM = 2, NS = 2: the large tile (wave tile 128 x 64);
+//   TBM = 64 / 32, WM = 1, NS = 4: narrow tiles for reduction-dominated
+//   shapes (wave tile 64 x 64 / 32 x 64), where the time is the stream of B.
+// Two workgroups share a CU when their rings fit in half the LDS; the
+// register budget then has to allow two waves per SIMD.
+template <int TBM, int NS>
+constexpr int waves_per_simd() {
+  return NS * (TBM + TBN) * SKB <= 80 * 1024 || TBM == 256 ? 2 : 1;
+}
+
+template <int IN, int OUT, bool SLICE, int TBM, int WM, int NS>
+__global__ __launch_bounds__(256 * WM, (waves_per_simd<TBM, NS>())) void gemm_dma_kernel(GemmArgs g) {
   using T = InT<IN>;
   constexpr int EB = T::EB;
-  constexpr int WAVES = 8, WN = 4;           // 2 x 4 waves
+  constexpr int WN = 4;
+  constexpr int WAVES = WM * WN;
+  constexpr int WTM = TBM / WM;              // wave tile rows
   constexpr int WTN = TBN / WN;              // wave tile columns (64)
+  constexpr int FM = WTM / 32;               // MFMA row blocks per wave
   constexpr int FN = WTN / 32;               // MFMA column blocks per wave (2)
-  constexpr int NM = 4 * FN;                 // MFMAs per k-step per wave (8)
+  constexpr int NM = FM * FN;                // MFMAs per k-step per wave
   constexpr int A_STAGE = TBM * SKB;         // bytes of A per stage
-  constexpr int STAGE = 2 * A_STAGE;         // A + B (B has as many bytes as A)
+  constexpr int B_STAGE = TBN * SKB;         // bytes of B per stage (32 KB)
+  constexpr int STAGE = A_STAGE + B_STAGE;
   constexpr int BKE = SKB / EB;              // K elements (= B rows) per stage
   constexpr int KS = SKB / T::KSTEP_B;       // MFMA k-steps per stage
   constexpr int ACH = SKB / 16;              // 16-byte slots per A row
@@ -109,9 +123,12 @@ __global__ __launch_bounds__(512, 2) void gemm_dma_kernel(GemmArgs g) {
   constexpr int BROW = TBN * EB;             // bytes per B row in LDS
   constexpr int BSLOTS = BROW / 16;
   constexpr int BROWS_PER_DMA = 1024 / BROW; // B rows written by one DMA instruction
-  constexpr int DPW = (2 * A_STAGE / 1024) / WAVES;  // DMA instructions per wave per stage
-  constexpr int DA = DPW / 2;                // ... of which for A (the rest for B)
-  constexpr int NRA = EB == 2 ? 4 : 8;       // fragment reads per k-step: A ...
+  constexpr int DA = A_STAGE / 1024 / WAVES; // DMA instructions per wave per stage: A ...
+  constexpr int DB = B_STAGE / 1024 / WAVES; // ... and B
+  constexpr int DPW = DA + DB;
+  static_assert(DA * WAVES * 1024 == A_STAGE && DB * WAVES * 1024 == B_STAGE, "DMA split");
+  static_assert(FM * 32 * WM == TBM, "tile rows");
+  constexpr int NRA = EB == 2 ? FM : 2 * FM; // fragment reads per k-step: A ...
   constexpr int NRB = EB == 2 ? 2 * FN : 4 * FN;  // ... and B
   constexpr int NREAD = NRA + NRB;
   static_assert(NS * STAGE <= 160 * 1024, "LDS ring too large");
@@ -139,8 +156,8 @@ __global__ __launch_bounds__(512, 2) void gemm_dma_kernel(GemmArgs g) {
   // ---- DMA geometry of this lane (the same for every stage).  Offsets of
   // rows past M / columns past N are replaced by an out-of-range offset once;
   // the K check only matters in a partial stage.
-  unsigned a_off[DA], b_off[DA];
-  int a_kel[DA], b_k[DA];
+  unsigned a_off[DA], b_off[DB];
+  int a_kel[DA], b_k[DB];
 #pragma unroll
   for (int i = 0; i < DA; ++i) {
     const int idx = w * DA + i;
@@ -148,6 +165,10 @@ __global__ __launch_bounds__(512, 2) void gemm_dma_kernel(GemmArgs g) {
     const int c = (lane % ACH) ^ aswz(row);
     a_off[i] = (m0 + row < g.M) ? (unsigned)(row * g.K * EB + c * 16) : OOB;
     a_kel[i] = c * (16 / EB);
+  }
+#pragma unroll
+  for (int i = 0; i < DB; ++i) {
+    const int idx = w * DB + i;
     const int k = BROWS_PER_DMA * idx + lane / BSLOTS;
     const int s = lane % BSLOTS;
     const int cb = EB == 2 ? (s ^ ((k & 3) << 2)) : (s ^ ((k & 7) << 1));
@@ -181,7 +202,7 @@ __global__ __launch_bounds__(512, 2) void gemm_dma_kernel(GemmArgs g) {
       const unsigned off = b_k[i] < q.rem ? b_off[i] : OOB;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           __builtin_amdgcn_make_buffer_rsrc((void*)q.pb, 0, NREC, RSRC_FLAGS),
-          IMM_LDS(sb + A_STAGE + (w * DA + i) * 1024), 16, off, 0, 0, 0);
+          IMM_LDS(sb + A_STAGE + (w * DB + i) * 1024), 16, off, 0, 0, 0);
     }
   };
   auto dma = [&](int t) {
@@ -192,9 +213,9 @@ __global__ __launch_bounds__(512, 2) void gemm_dma_kernel(GemmArgs g) {
 
   // ---- fragment read offsets within a stage.
   const int asw = aswz(l32);  // rows of a fragment differ from l32 by multiples of 32
-  int a_rd[4];
+  int a_rd[FM];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) a_rd[i] = (wm * 128 + i * 32 + l32) * SKB;
+  for (int i = 0; i < FM; ++i) a_rd[i] = (wm * WTM + i * 32 + l32) * SKB;
   const int grp = lane >> 4, gi = lane & 15;
   int b_rd[FN];  // per column block j: byte offset of the first transposing read
   if constexpr (EB == 2) {
@@ -219,11 +240,11 @@ __global__ __launch_bounds__(512, 2) void gemm_dma_kernel(GemmArgs g) {
   const unsigned lds_addr = (unsigned)(uintptr_t)((__attribute__((address_space(3))) char*)lds);
 
   // Fragment read x of k-step ks of LDS slot `slot` into F.
-  //   16-bit: x < 4 -> A block i = x (one ds_read_b128);
-  //           else B block j = (x-4)/2, half r = (x-4)%2 (K elements 4r..4r+3).
-  //   fp8:    x < 8 -> A block i = x/2, half x%2 (16 bytes of K each);
-  //           else B block j = (x-8)/4, piece r = (x-8)%4 (8 K values).
-  auto read_one = [&](Frag<IN, FN>& F, int slot, int ks, int x) {
+  //   16-bit: x < FM -> A block i = x (one ds_read_b128);
+  //           else B block j = (x-FM)/2, half r = (x-FM)%2 (K elements 4r..4r+3).
+  //   fp8:    x < 2FM -> A block i = x/2, half x%2 (16 bytes of K each);
+  //           else B block j = (x-2FM)/4, piece r = (x-2FM)%4 (8 K values).
+  auto read_one = [&](Frag<IN, FM, FN>& F, int slot, int ks, int x) {
     const char* sb = lds + slot;
     if constexpr (EB == 2) {
       if (x < NRA) {
@@ -261,16 +282,16 @@ __global__ __launch_bounds__(512, 2) void gemm_dma_kernel(GemmArgs g) {
     fence();
   };
 
-  f32x16 acc[4][FN];
+  f32x16 acc[FM][FN];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < FM; ++i)
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{};
-  auto mfma_x = [&](const Frag<IN, FN>& F, int x) {
+  auto mfma_x = [&](const Frag<IN, FM, FN>& F, int x) {
     acc[x / FN][x % FN] = mfma_v<IN>(F.a[x / FN], F.b[x % FN], acc[x / FN][x % FN]);
   };
 
-  Frag<IN, FN> F0, F1;
+  Frag<IN, FM, FN> F0, F1;
   if (nt > 0) {
     for (int p = 0; p < NS; ++p) dma(p);
     // stage 0 landed: NS - 1 stages were requested after it
@@ -301,7 +322,7 @@ __global__ __launch_bounds__(512, 2) void gemm_dma_kernel(GemmArgs g) {
   // Every stage runs the same instructions: a refill past the end of the
   // slice has only out-of-range offsets (zero fill, no memory traffic) and
   // the reads past the last stage land in registers that are never used.
-  auto kstep = [&](bool dma_on, const Frag<IN, FN>& Fc, int td, Frag<IN, FN>& Fn, int tr,
+  auto kstep = [&](bool dma_on, const Frag<IN, FM, FN>& Fc, int td, Frag<IN, FM, FN>& Fn, int tr,
                    int ks) {
     const StageSrc q = stage_src(td);
     const int slot = (tr % NS) * STAGE;
@@ -339,13 +360,13 @@ __global__ __launch_bounds__(512, 2) void gemm_dma_kernel(GemmArgs g) {
   // Write-back.  32x32 accumulator layout: lane l, register r holds
   // row 8*(r/4) + 4*(l/32) + r%4, column l%32 of the block.
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < FM; ++i) {
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
       const int64_t col = n0 + wn * WTN + j * 32 + l32;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int64_t row = m0 + wm * 128 + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+        const int64_t row = m0 + wm * WTM + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
         if (row < g.M && col < g.N) {
           const float v = acc[i][j][r];
           if constexpr (SLICE) {
@@ -359,16 +380,30 @@ __global__ __launch_bounds__(512, 2) void gemm_dma_kernel(GemmArgs g) {
   }
 }
 
+template <int IN, int TBM, int WM, int NS>
+hipError_t launch_cfg(const gemm_plan_s& p, const GemmArgs& a, bool slice, hipStream_t s) {
+  const dim3 grid((unsigned)a.grid), block(256 * WM);
+  if (slice)
+    hipLaunchKernelGGL((gemm_dma_kernel<IN, GEMM_F32, true, TBM, WM, NS>), grid, block, 0, s, a);
+  else if (p.out == GEMM_F32)
+    hipLaunchKernelGGL((gemm_dma_kernel<IN, GEMM_F32, false, TBM, WM, NS>), grid, block, 0, s, a);
+  else
+    hipLaunchKernelGGL((gemm_dma_kernel<IN, GEMM_BF16, false, TBM, WM, NS>), grid, block, 0, s, a);
+  return hipGetLastError();
+}
+
+#ifndef IMM_NARROW_NS
+#define IMM_NARROW_NS 4
+#endif
+
 template <int IN>
 hipError_t launch_in(const gemm_plan_s& p, const GemmArgs& a, bool slice, hipStream_t s) {
-  const dim3 grid((unsigned)a.grid), block(512);
-  if (slice)
-    hipLaunchKernelGGL((gemm_dma_kernel<IN, GEMM_F32, true>), grid, block, 0, s, a);
-  else if (p.out == GEMM_F32)
-    hipLaunchKernelGGL((gemm_dma_kernel<IN, GEMM_F32, false>), grid, block, 0, s, a);
-  else
-    hipLaunchKernelGGL((gemm_dma_kernel<IN, GEMM_BF16, false>), grid, block, 0, s, a);
-  return hipGetLastError();
+  switch (p.tile) {
+    case GEMM_TILE_256x256: return launch_cfg<IN, 256, 2, 2>(p, a, slice, s);
+    case GEMM_TILE_64x256: return launch_cfg<IN, 64, 1, IMM_NARROW_NS>(p, a, slice, s);
+    case GEMM_TILE_32x256: return launch_cfg<IN, 32, 1, IMM_NARROW_NS>(p, a, slice, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace

@@ -248,19 +248,32 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_tile_kernel(GemmAr
 // C = convert(scale * (((ws[0] + ws[1]) + ws[2]) + ... + ws[S-1])), fp32 adds in
 // ascending slice order for every element ([TDI] "Split-K": the separate
 // reduction kernel that sums the workspace over split_k).  Four consecutive
-// elements per thread, grid-stride.
+// elements per thread, grid-stride.  The slices are loaded in groups of RG
+// before they are added (in order), so a thread waits for one memory latency
+// per group instead of one per slice.
 template <int OUT>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(ReduceArgs r) {
+  constexpr int RG = 8;
   const int64_t n4 = r.MN / 4;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  const f32x4* ws = reinterpret_cast<const f32x4*>(r.ws);
+  const int64_t slice4 = r.MN / 4;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) {
-    f32x4 v = reinterpret_cast<const f32x4*>(r.ws)[i];
-    for (int s = 1; s < r.split_k; ++s) {
-      const f32x4 w = reinterpret_cast<const f32x4*>(r.ws + (int64_t)s * r.MN)[i];
-      v[0] = v[0] + w[0];
-      v[1] = v[1] + w[1];
-      v[2] = v[2] + w[2];
-      v[3] = v[3] + w[3];
+    f32x4 v = ws[i];
+    for (int s0 = 1; s0 < r.split_k; s0 += RG) {
+      f32x4 w[RG];
+#pragma unroll
+      for (int j = 0; j < RG; ++j)
+        if (s0 + j < r.split_k) w[j] = ws[(int64_t)(s0 + j) * slice4 + i];
+#pragma unroll
+      for (int j = 0; j < RG; ++j) {
+        if (s0 + j < r.split_k) {
+          v[0] = v[0] + w[j][0];
+          v[1] = v[1] + w[j][1];
+          v[2] = v[2] + w[j][2];
+          v[3] = v[3] + w[j][3];
+        }
+      }
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) store_out<OUT>(r.C, i * 4 + e, v[e] * r.scale);
@@ -296,7 +309,8 @@ hipError_t launch_in(const gemm_plan_s& p, const GemmArgs& a, bool slice, hipStr
 }  // namespace
 
 hipError_t launch_gemm(const gemm_plan_s& p, const GemmArgs& a, bool slice_mode, hipStream_t s) {
-  if (p.tile == GEMM_TILE_256x256) return launch_gemm_dma(p, a, slice_mode, s);
+  if (p.tile == GEMM_TILE_256x256 || p.tile == GEMM_TILE_32x256 || p.tile == GEMM_TILE_64x256)
+    return launch_gemm_dma(p, a, slice_mode, s);
   switch (p.in) {
     case GEMM_F16: return launch_in<GEMM_F16>(p, a, slice_mode, s);
     case GEMM_BF16: return launch_in<GEMM_BF16>(p, a, slice_mode, s);

@@ -24,7 +24,7 @@ from tests.helpers import bits_of, dev, log, run
 
 pytestmark = pytest.mark.gpu
 
-TILES = ["256x256", "128x128", "32x128", "256x256_rs"]
+TILES = ["256x256", "128x128", "32x128", "256x256_rs", "32x256", "64x256"]
 
 
 def _to_dev(*ts):
