@@ -284,7 +284,8 @@ def main():
                                 for m in (1, 8, 32, 128)]
         torch.cuda.empty_cache()
         log("huge-K fp16 256x256x131072, split-K path")
-        extra["hugek_f16"] = [bench_splitk("hugek_f16", s, torch, imm, wl) for s in (1, 8, 32, 128)]
+        # split 0 = the plan's default for this shape
+        extra["hugek_f16"] = [bench_splitk("hugek_f16", s, torch, imm, wl) for s in (1, 8, 32, 128, 0)]
         torch.cuda.empty_cache()
         A, B = host[0], host[1]
     else:
