@@ -254,7 +254,7 @@ def main():
                 "algorithmic_flop_per_launch": w.flops, "avg_launch_ms": kavg}
 
     extra = {"headline_kernel": summary(per),
-             "plan": {k: plan.info[k] for k in ("block_m", "block_n", "block_k", "waves",
+             "plan": {k: plan.info[k] for k in ("run_block_m", "run_block_n", "block_k", "run_waves",
                                                   "group_m", "split_k", "mfma_k")}}
     if not args.no_extra:
         A, B, Ad, Bd = host

@@ -102,22 +102,30 @@ typedef enum {
 
 typedef struct gemm_plan_s* gemm_plan_t;
 
+/* A plan holds one tile for each entry point: tile / block_m / block_n /
+ * waves / tiles_m / tiles_n describe gemm_splitk_run's partial kernel, the
+ * run_* fields gemm_run's single pass.  Both are chosen from (N, K, dtype,
+ * options) alone, and the bits of C depend on neither. */
 typedef struct {
   int64_t M, N, K;
   int32_t in_dtype, out_dtype;  /* gemm_dtype values */
-  int32_t tile;                 /* gemm_tile value actually used */
-  int32_t block_m, block_n;     /* output tile */
+  int32_t tile;                 /* gemm_tile value of the split-K path */
+  int32_t block_m, block_n;     /* its output tile */
   int32_t block_k;              /* K elements staged per main-loop step */
   int32_t mfma_m, mfma_n, mfma_k; /* matrix-core instruction shape */
-  int32_t waves;                /* 64-lane wavefronts per workgroup */
+  int32_t waves;                /* 64-lane wavefronts per workgroup (split-K path) */
   int32_t group_m;              /* GROUP_M of the tile raster */
   int32_t split_k;              /* K slices used by gemm_splitk_run */
   int64_t k_per_split;          /* K elements per slice (multiple of block_k) */
-  int64_t tiles_m, tiles_n;     /* output tiles along M and N */
+  int64_t tiles_m, tiles_n;     /* output tiles along M and N (split-K path) */
   int64_t grid_run;             /* workgroups launched by gemm_run */
   int64_t grid_splitk;          /* workgroups of the split-K partial kernel */
   uint64_t workspace_bytes;     /* split_k * M * N * 4 */
   float scale_a, scale_b;
+  int32_t run_tile;             /* gemm_tile value of gemm_run */
+  int32_t run_block_m, run_block_n;
+  int32_t run_waves;
+  int64_t run_tiles_m, run_tiles_n;
 } gemm_plan_info_t;
 
 /* Plan C[M,N] = A[M,K] x B[K,N] with default options: fp32 output for fp16 /

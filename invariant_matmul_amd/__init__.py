@@ -58,7 +58,10 @@ class PlanInfo(ctypes.Structure):
         ("k_per_split", ctypes.c_int64), ("tiles_m", ctypes.c_int64), ("tiles_n", ctypes.c_int64),
         ("grid_run", ctypes.c_int64), ("grid_splitk", ctypes.c_int64),
         ("workspace_bytes", ctypes.c_uint64), ("scale_a", ctypes.c_float),
-        ("scale_b", ctypes.c_float),
+        ("scale_b", ctypes.c_float), ("run_tile", ctypes.c_int32),
+        ("run_block_m", ctypes.c_int32), ("run_block_n", ctypes.c_int32),
+        ("run_waves", ctypes.c_int32), ("run_tiles_m", ctypes.c_int64),
+        ("run_tiles_n", ctypes.c_int64),
     ]
 
     def as_dict(self):

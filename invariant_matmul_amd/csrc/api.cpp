@@ -51,9 +51,45 @@ void tile_shape(int tile, int* bm, int* bn, int* wm, int* wn) {
 // large tile.
 bool reduction_dominated(int64_t N, int64_t K) { return K >= 2 * N; }
 
-int default_tile(int64_t N, int64_t K) {
-  if (!reduction_dominated(N, K)) return GEMM_TILE_256x256;
+// Small B (at most 4 MB, the L2 of one XCD): the product is too small to
+// fill the machine with 256 x 256 tiles (1024^3 has 16 of them), while
+// re-reading B from L2 for every 32 rows of A is cheap.  Measured at 1024^3:
+// 14.5 us with 32 x 256 against 29.4 us with 256 x 256.
+bool small_b(int64_t N, int64_t K, int eb) { return N * K * eb <= ((int64_t)4 << 20); }
+
+// Tile of the split-K path.
+int default_tile(int64_t N, int64_t K, int eb) {
+  if (!reduction_dominated(N, K)) return small_b(N, K, eb) ? GEMM_TILE_32x256 : GEMM_TILE_256x256;
   return N <= 512 ? GEMM_TILE_64x256 : GEMM_TILE_32x128;
+}
+
+// Tile of the single pass.  Without a split, a 32-row tile only pays off
+// when M is small, and the plan does not look at M: a reduction-dominated
+// shape with a large M (4096 x 4096 x 8192) ran at 440 TFLOP/s with the
+// 32 x 128 tile and at over 1100 with 256 x 256.  So the single pass keeps
+// the large tile except for small B (as above) and narrow N (N <= 512, where
+// 256 columns already cover all of N).
+int default_run_tile(int64_t N, int64_t K, int eb) {
+  if (small_b(N, K, eb)) return GEMM_TILE_32x256;
+  if (reduction_dominated(N, K) && N <= 512) return GEMM_TILE_64x256;
+  return GEMM_TILE_256x256;
+}
+
+bool is_dma_tile(int tile) {
+  return tile == GEMM_TILE_256x256 || tile == GEMM_TILE_32x256 || tile == GEMM_TILE_64x256;
+}
+
+// A DMA tile whose 32-bit buffer offsets would overflow falls back to a
+// register-staged tile of the same bits.  The DMA kernels address one A tile
+// (bm rows) and one B stage (128 bytes of K: 128 / eb rows of N elements).
+int checked_tile(int tile, int64_t N, int64_t K, int eb) {
+  if (!is_dma_tile(tile)) return tile;
+  int bm, bn, wm, wn;
+  tile_shape(tile, &bm, &bn, &wm, &wn);
+  const int64_t lim = ((int64_t)1 << 31) - 256;
+  if (bm * K * eb >= lim || 128 * N >= lim)
+    return tile == GEMM_TILE_256x256 ? GEMM_TILE_256x256_RS : GEMM_TILE_32x128;
+  return tile;
 }
 
 // Workgroups the default split aims for per row of output tiles.  Wide
@@ -67,9 +103,6 @@ int64_t target_workgroups(int64_t N) { return N <= 512 ? 64 : 512; }
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-bool is_dma_tile(int tile) {
-  return tile == GEMM_TILE_256x256 || tile == GEMM_TILE_32x256 || tile == GEMM_TILE_64x256;
-}
 
 // Default split: only for reduction-dominated shapes; the largest power of two
 // that brings one tile-row of the grid to about target_workgroups(N) while
@@ -121,9 +154,9 @@ GemmArgs make_args(const gemm_plan_s* p, const void* A, const void* B, void* out
   a.N = p->N;
   a.K = p->K;
   a.k_per_split = split ? p->k_per_split : (p->K > 0 ? p->K : p->bk);
-  a.tiles_m = p->tiles_m;
-  a.tiles_n = p->tiles_n;
-  a.grid = p->tiles_m * p->tiles_n * (split ? p->split_k : 1);
+  a.tiles_m = split ? p->tiles_m : p->run_tiles_m;
+  a.tiles_n = split ? p->tiles_n : p->run_tiles_n;
+  a.grid = a.tiles_m * a.tiles_n * (split ? p->split_k : 1);
   a.group_m = p->group_m;
   a.scale = p->scale;
   return a;
@@ -157,18 +190,11 @@ gemm_status gemm_plan_ex(int64_t M, int64_t N, int64_t K, gemm_dtype in, gemm_dt
   p->K = K;
   p->in = in;
   p->out = out;
-  p->tile = tile == GEMM_TILE_DEFAULT ? default_tile(N, K) : tile;
-  // The DMA kernels address one A tile (bm rows) and one B stage (128 bytes
-  // of K: 128 / eb rows of N elements) with 32-bit offsets; beyond that the
-  // register-staged kernels (same bits) take over.
-  if (is_dma_tile(p->tile)) {
-    int bm, bn, wm, wn;
-    tile_shape(p->tile, &bm, &bn, &wm, &wn);
-    const int64_t lim = ((int64_t)1 << 31) - 256;
-    if (bm * K * eb >= lim || 128 * N >= lim)
-      p->tile = p->tile == GEMM_TILE_256x256 ? GEMM_TILE_256x256_RS : GEMM_TILE_32x128;
-  }
+  p->tile = checked_tile(tile == GEMM_TILE_DEFAULT ? default_tile(N, K, eb) : tile, N, K, eb);
+  p->run_tile =
+      checked_tile(tile == GEMM_TILE_DEFAULT ? default_run_tile(N, K, eb) : tile, N, K, eb);
   tile_shape(p->tile, &p->bm, &p->bn, &p->waves_m, &p->waves_n);
+  tile_shape(p->run_tile, &p->run_bm, &p->run_bn, &p->run_waves_m, &p->run_waves_n);
   p->bk = block_k_elems(in);
   p->group_m = group_m == 0 ? 8 : group_m;
   const int64_t steps = ceil_div(K, p->bk);
@@ -182,11 +208,15 @@ gemm_status gemm_plan_ex(int64_t M, int64_t N, int64_t K, gemm_dtype in, gemm_dt
   p->k_per_split = steps_per * p->bk;
   p->tiles_m = ceil_div(M, p->bm);
   p->tiles_n = ceil_div(N, p->bn);
+  p->run_tiles_m = ceil_div(M, p->run_bm);
+  p->run_tiles_n = ceil_div(N, p->run_bn);
   p->scale_a = scale_a;
   p->scale_b = scale_b;
   p->scale = (float)((double)scale_a * (double)scale_b);
   const int64_t threads = (int64_t)p->waves_m * p->waves_n * 64;
-  if (p->tiles_m * p->tiles_n * p->split_k * threads >= ((int64_t)1 << 32)) {
+  const int64_t run_threads = (int64_t)p->run_waves_m * p->run_waves_n * 64;
+  if (p->tiles_m * p->tiles_n * p->split_k * threads >= ((int64_t)1 << 32) ||
+      p->run_tiles_m * p->run_tiles_n * run_threads >= ((int64_t)1 << 32)) {
     delete p;
     return GEMM_ERR_UNSUPPORTED;
   }
@@ -220,8 +250,14 @@ gemm_status gemm_plan_info(gemm_plan_t p, gemm_plan_info_t* info) {
   info->k_per_split = p->k_per_split;
   info->tiles_m = p->tiles_m;
   info->tiles_n = p->tiles_n;
-  info->grid_run = p->tiles_m * p->tiles_n;
+  info->grid_run = p->run_tiles_m * p->run_tiles_n;
   info->grid_splitk = p->tiles_m * p->tiles_n * p->split_k;
+  info->run_tile = p->run_tile;
+  info->run_block_m = p->run_bm;
+  info->run_block_n = p->run_bn;
+  info->run_waves = p->run_waves_m * p->run_waves_n;
+  info->run_tiles_m = p->run_tiles_m;
+  info->run_tiles_n = p->run_tiles_n;
   info->workspace_bytes = gemm_workspace_size(p);
   info->scale_a = p->scale_a;
   info->scale_b = p->scale_b;
@@ -247,7 +283,8 @@ gemm_status gemm_run(gemm_plan_t p, const void* A, const void* B, void* C, void*
   if (st != GEMM_OK || p->M == 0 || p->N == 0) return st;
   hipError_t e = device_ready();
   if (e != hipSuccess) return hip_fail(e);
-  e = launch_gemm(*p, make_args(p, A, B, C, false), false, static_cast<hipStream_t>(stream));
+  e = launch_gemm(*p, p->run_tile, make_args(p, A, B, C, false), false,
+                  static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e);
   return GEMM_OK;
 }
@@ -261,7 +298,7 @@ gemm_status gemm_splitk_run(gemm_plan_t p, const void* A, const void* B, void* C
   hipError_t e = device_ready();
   if (e != hipSuccess) return hip_fail(e);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  e = launch_gemm(*p, make_args(p, A, B, workspace, true), true, s);
+  e = launch_gemm(*p, p->tile, make_args(p, A, B, workspace, true), true, s);
   if (e != hipSuccess) return hip_fail(e);
   ReduceArgs r;
   r.ws = static_cast<const float*>(workspace);

@@ -102,7 +102,10 @@ constexpr int waves_per_simd() {
   return NS * (TBM + TBN) * SKB <= 80 * 1024 || TBM == 256 ? 2 : 1;
 }
 
-template <int IN, int OUT, bool SLICE, int TBM, int WM, int NS>
+// NBR: 0 = A and B blocks of a stage share one ring of NS slots; otherwise B
+// has a ring of its own with NBR slots (A keeps NS), so B is requested
+// NBR - 1 stages ahead while A is requested NS - 1 stages ahead.
+template <int IN, int OUT, bool SLICE, int TBM, int WM, int NS, int NBR>
 __global__ __launch_bounds__(256 * WM, (waves_per_simd<TBM, NS>())) void gemm_dma_kernel(GemmArgs g) {
   using T = InT<IN>;
   constexpr int EB = T::EB;
@@ -131,10 +134,19 @@ __global__ __launch_bounds__(256 * WM, (waves_per_simd<TBM, NS>())) void gemm_dm
   constexpr int NRA = EB == 2 ? FM : 2 * FM; // fragment reads per k-step: A ...
   constexpr int NRB = EB == 2 ? 2 * FN : 4 * FN;  // ... and B
   constexpr int NREAD = NRA + NRB;
-  static_assert(NS * STAGE <= 160 * 1024, "LDS ring too large");
+  constexpr bool SPLIT = NBR > 0;
+  constexpr int NBS = SPLIT ? NBR : NS;      // B slots
+  constexpr int LDS_BYTES = SPLIT ? NS * A_STAGE + NBR * B_STAGE : NS * STAGE;
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS ring too large");
   static_assert(KS % 2 == 0, "k-steps per stage");
+  static_assert(!SPLIT || (NS == 2 && NBR >= NS), "split rings: A has 2 slots, B at least 2");
 
-  __shared__ __attribute__((aligned(1024))) char lds[NS * STAGE];
+  __shared__ __attribute__((aligned(1024))) char lds[LDS_BYTES];
+  // LDS offsets of the A and B blocks of stage t.
+  auto a_slot = [](int t) { return SPLIT ? (t % NS) * A_STAGE : (t % NS) * STAGE; };
+  auto b_slot = [](int t) {
+    return SPLIT ? NS * A_STAGE + (t % NBS) * B_STAGE : (t % NS) * STAGE + A_STAGE;
+  };
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (uniform)
@@ -189,26 +201,21 @@ __global__ __launch_bounds__(256 * WM, (waves_per_simd<TBM, NS>())) void gemm_dm
     q.rem = kend - kst < BKE ? (int)(kend - kst) : BKE;
     return q;
   };
-  // DMA instruction x of this wave (x < DA: A rows, else B rows) of stage t.
-  auto dma_one = [&](const StageSrc& q, int t, int x) {
-    char* sb = lds + (t % NS) * STAGE;
+  // DMA instruction x of this wave: x < DA: A rows of stage ta (source qa),
+  // else B rows of stage tb (source qb).
+  auto dma_one = [&](const StageSrc& qa, int ta, const StageSrc& qb, int tb, int x) {
     if (x < DA) {
-      const unsigned off = a_kel[x] < q.rem ? a_off[x] : OOB;
+      const unsigned off = a_kel[x] < qa.rem ? a_off[x] : OOB;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          __builtin_amdgcn_make_buffer_rsrc((void*)q.pa, 0, NREC, RSRC_FLAGS),
-          IMM_LDS(sb + (w * DA + x) * 1024), 16, off, 0, 0, 0);
+          __builtin_amdgcn_make_buffer_rsrc((void*)qa.pa, 0, NREC, RSRC_FLAGS),
+          IMM_LDS(lds + a_slot(ta) + (w * DA + x) * 1024), 16, off, 0, 0, 0);
     } else {
       const int i = x - DA;
-      const unsigned off = b_k[i] < q.rem ? b_off[i] : OOB;
+      const unsigned off = b_k[i] < qb.rem ? b_off[i] : OOB;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          __builtin_amdgcn_make_buffer_rsrc((void*)q.pb, 0, NREC, RSRC_FLAGS),
-          IMM_LDS(sb + A_STAGE + (w * DB + i) * 1024), 16, off, 0, 0, 0);
+          __builtin_amdgcn_make_buffer_rsrc((void*)qb.pb, 0, NREC, RSRC_FLAGS),
+          IMM_LDS(lds + b_slot(tb) + (w * DB + i) * 1024), 16, off, 0, 0, 0);
     }
-  };
-  auto dma = [&](int t) {
-    const StageSrc q = stage_src(t);
-#pragma unroll
-    for (int x = 0; x < DPW; ++x) dma_one(q, t, x);
   };
 
   // ---- fragment read offsets within a stage.
@@ -224,7 +231,7 @@ __global__ __launch_bounds__(256 * WM, (waves_per_simd<TBM, NS>())) void gemm_dm
     for (int j = 0; j < FN; ++j) {
       const int n = wn * WTN + j * 32 + 16 * (grp & 1) + 4 * q;
       const int k = 8 * (grp >> 1) + t_;
-      b_rd[j] = A_STAGE + k * BROW + (((n >> 3) ^ (t_ << 2)) << 4) + (q & 1) * 8;
+      b_rd[j] = k * BROW + (((n >> 3) ^ (t_ << 2)) << 4) + (q & 1) * 8;
     }
   } else {
     const int t_ = gi >> 1, q = gi & 1;
@@ -232,27 +239,28 @@ __global__ __launch_bounds__(256 * WM, (waves_per_simd<TBM, NS>())) void gemm_dm
     for (int j = 0; j < FN; ++j) {
       const int n = wn * WTN + j * 32 + 16 * (grp & 1) + 8 * q;
       const int k = 32 * (grp >> 1) + t_;
-      b_rd[j] = A_STAGE + k * BROW + (((n >> 4) ^ (t_ << 1)) << 4) + q * 8;
+      b_rd[j] = k * BROW + (((n >> 4) ^ (t_ << 1)) << 4) + q * 8;
     }
   }
 
   // LDS byte address of the ring (for the transposing reads).
   const unsigned lds_addr = (unsigned)(uintptr_t)((__attribute__((address_space(3))) char*)lds);
 
-  // Fragment read x of k-step ks of LDS slot `slot` into F.
+  // Fragment read x of k-step ks of the stage whose A and B blocks sit at LDS
+  // offsets as and bs, into F.
   //   16-bit: x < FM -> A block i = x (one ds_read_b128);
   //           else B block j = (x-FM)/2, half r = (x-FM)%2 (K elements 4r..4r+3).
   //   fp8:    x < 2FM -> A block i = x/2, half x%2 (16 bytes of K each);
   //           else B block j = (x-2FM)/4, piece r = (x-2FM)%4 (8 K values).
-  auto read_one = [&](Frag<IN, FM, FN>& F, int slot, int ks, int x) {
-    const char* sb = lds + slot;
+  auto read_one = [&](Frag<IN, FM, FN>& F, int as, int bs, int ks, int x) {
+    const char* sb = lds + as;
     if constexpr (EB == 2) {
       if (x < NRA) {
         const int c = ks * 2 + h;
         F.a[x] = *reinterpret_cast<const i32x4*>(sb + a_rd[x] + ((c ^ asw) << 4));
       } else {
         const int j = (x - NRA) >> 1, r = (x - NRA) & 1;
-        const i32x2 v = tr16_rows<BROW>(lds_addr + slot + b_rd[j], ks * 16 + 4 * r);
+        const i32x2 v = tr16_rows<BROW>(lds_addr + bs + b_rd[j], ks * 16 + 4 * r);
         F.b[j][2 * r] = v[0];
         F.b[j][2 * r + 1] = v[1];
       }
@@ -265,7 +273,7 @@ __global__ __launch_bounds__(256 * WM, (waves_per_simd<TBM, NS>())) void gemm_dm
         for (int e = 0; e < 4; ++e) F.a[i][4 * f + e] = v[e];
       } else {
         const int j = (x - NRA) >> 2, r = (x - NRA) & 3;
-        const i32x2 v = tr8_rows<BROW>(lds_addr + slot + b_rd[j], ks * 64 + 8 * r);
+        const i32x2 v = tr8_rows<BROW>(lds_addr + bs + b_rd[j], ks * 64 + 8 * r);
         F.b[j][2 * r] = v[0];
         F.b[j][2 * r + 1] = v[1];
       }
@@ -291,50 +299,70 @@ __global__ __launch_bounds__(256 * WM, (waves_per_simd<TBM, NS>())) void gemm_dm
     acc[x / FN][x % FN] = mfma_v<IN>(F.a[x / FN], F.b[x % FN], acc[x / FN][x % FN]);
   };
 
+  // Issue order.  The prologue requests A(p) then B(p) for p = 0, 1, ...
+  // (A only for p < NS, B only for p < NBS); every refill requests A(t+NS)
+  // then B(t+NBS).  Before stage t+1 is used, the requests still allowed in
+  // flight are those after the later of A(t+1) and B(t+1): the B blocks of
+  // the NBS - NS stages that B runs ahead of A (split rings), or the NS - 2
+  // whole stages after t+1 (shared ring).  DMA is issued for every stage
+  // index in order (past the end of the slice it only writes zeros), so
+  // these counts never change.
+  constexpr int WAIT_FIRST = (NS - 1) * DA + (NBS - 1) * DB;
+  constexpr int WAIT_NEXT = SPLIT ? (NBS - NS) * DB : (NS - 2) * DPW;
   Frag<IN, FM, FN> F0, F1;
   if (nt > 0) {
-    for (int p = 0; p < NS; ++p) dma(p);
-    // stage 0 landed: NS - 1 stages were requested after it
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 1) * DPW));
+    const int np = NS > NBS ? NS : NBS;
+    for (int p = 0; p < np; ++p) {
+      const StageSrc q = stage_src(p);
+      if (p < NS) {
+#pragma unroll
+        for (int x = 0; x < DA; ++x) dma_one(q, p, q, p, x);
+      }
+      if (p < NBS) {
+#pragma unroll
+        for (int x = DA; x < DPW; ++x) dma_one(q, p, q, p, x);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(WAIT_FIRST));
     __builtin_amdgcn_s_barrier();
     fence();
 #pragma unroll
-    for (int x = 0; x < NREAD; ++x) read_one(F0, 0, 0, x);
+    for (int x = 0; x < NREAD; ++x) read_one(F0, a_slot(0), b_slot(0), 0, x);
   }
 
   // The stage change sits at the start of the last k-step of stage t: once a
   // wave's fragment reads of that k-step have landed it has read all of stage
   // t, so after it waits for its own DMA of stage t+1 a single barrier
   // certifies that (a) stage t+1 is in LDS for every wave and (b) no wave
-  // reads slot t % NS any more.  The whole last k-step then overlaps the DMA
-  // of stage t+NS into that slot and the fragment reads of stage t+1.
+  // reads the slots of stage t any more.  The whole last k-step then
+  // overlaps the refill of those slots (A with stage t+NS, B with stage
+  // t+NBS) and the fragment reads of stage t+1.
   auto stage_change = [&]() {
     fence();
-    // DMA is issued for every stage index in order (past the end of the
-    // slice it only writes zeros), so after stage t+1 exactly NS-2 later
-    // stages can still be in flight.
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 2) * DPW));
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(WAIT_NEXT));
     __builtin_amdgcn_s_barrier();
     fence();
   };
-  // MFMAs of one k-step on Fc, with the DMA of stage td (if dma_on) and the
-  // fragment reads of k-step ks of stage tr into Fn spread between them.
-  // Every stage runs the same instructions: a refill past the end of the
-  // slice has only out-of-range offsets (zero fill, no memory traffic) and
-  // the reads past the last stage land in registers that are never used.
-  auto kstep = [&](bool dma_on, const Frag<IN, FM, FN>& Fc, int td, Frag<IN, FM, FN>& Fn, int tr,
+  // MFMAs of one k-step on Fc, with (if refill) the DMA of A(t+NS) and
+  // B(t+NBS), and the fragment reads of k-step ks of stage tr into Fn spread
+  // between them.  Every stage runs the same instructions: a refill past the
+  // end of the slice has only out-of-range offsets (zero fill, no memory
+  // traffic) and the reads past the last stage land in registers that are
+  // never used.
+  auto kstep = [&](bool refill, const Frag<IN, FM, FN>& Fc, int t, Frag<IN, FM, FN>& Fn, int tr,
                    int ks) {
-    const StageSrc q = stage_src(td);
-    const int slot = (tr % NS) * STAGE;
+    const StageSrc qa = stage_src(t + NS);
+    const StageSrc qb = stage_src(t + NBS);
+    const int as = a_slot(tr), bs = b_slot(tr);
 #pragma unroll
     for (int x = 0; x < NM; ++x) {
       mfma_x(Fc, x);
-      if (dma_on) {
+      if (refill) {
 #pragma unroll
-        for (int y = x * DPW / NM; y < (x + 1) * DPW / NM; ++y) dma_one(q, td, y);
+        for (int y = x * DPW / NM; y < (x + 1) * DPW / NM; ++y) dma_one(qa, t + NS, qb, t + NBS, y);
       }
 #pragma unroll
-      for (int y = x * NREAD / NM; y < (x + 1) * NREAD / NM; ++y) read_one(Fn, slot, ks, y);
+      for (int y = x * NREAD / NM; y < (x + 1) * NREAD / NM; ++y) read_one(Fn, as, bs, ks, y);
       fence();
     }
   };
@@ -351,7 +379,7 @@ __global__ __launch_bounds__(256 * WM, (waves_per_simd<TBM, NS>())) void gemm_dm
     }
     lds_wait();  // last k-step's fragments landed: this wave has read all of stage t
     stage_change();
-    kstep(true, F1, t + NS, F0, t + 1, 0);
+    kstep(true, F1, t, F0, t + 1, 0);
   }
   // No LDS transfer or read may still be in flight when the workgroup ends.
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
@@ -380,41 +408,44 @@ __global__ __launch_bounds__(256 * WM, (waves_per_simd<TBM, NS>())) void gemm_dm
   }
 }
 
-template <int IN, int TBM, int WM, int NS>
+template <int IN, int TBM, int WM, int NS, int NBR>
 hipError_t launch_cfg(const gemm_plan_s& p, const GemmArgs& a, bool slice, hipStream_t s) {
   const dim3 grid((unsigned)a.grid), block(256 * WM);
   if (slice)
-    hipLaunchKernelGGL((gemm_dma_kernel<IN, GEMM_F32, true, TBM, WM, NS>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((gemm_dma_kernel<IN, GEMM_F32, true, TBM, WM, NS, NBR>), grid, block, 0, s, a);
   else if (p.out == GEMM_F32)
-    hipLaunchKernelGGL((gemm_dma_kernel<IN, GEMM_F32, false, TBM, WM, NS>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((gemm_dma_kernel<IN, GEMM_F32, false, TBM, WM, NS, NBR>), grid, block, 0, s, a);
   else
-    hipLaunchKernelGGL((gemm_dma_kernel<IN, GEMM_BF16, false, TBM, WM, NS>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((gemm_dma_kernel<IN, GEMM_BF16, false, TBM, WM, NS, NBR>), grid, block, 0, s, a);
   return hipGetLastError();
 }
 
 #ifndef IMM_NARROW_NS
 #define IMM_NARROW_NS 4
 #endif
+#ifndef IMM_BIG_NBR
+#define IMM_BIG_NBR 0
+#endif
 
 template <int IN>
-hipError_t launch_in(const gemm_plan_s& p, const GemmArgs& a, bool slice, hipStream_t s) {
-  switch (p.tile) {
-    case GEMM_TILE_256x256: return launch_cfg<IN, 256, 2, 2>(p, a, slice, s);
-    case GEMM_TILE_64x256: return launch_cfg<IN, 64, 1, IMM_NARROW_NS>(p, a, slice, s);
-    case GEMM_TILE_32x256: return launch_cfg<IN, 32, 1, IMM_NARROW_NS>(p, a, slice, s);
+hipError_t launch_in(const gemm_plan_s& p, int tile, const GemmArgs& a, bool slice, hipStream_t s) {
+  switch (tile) {
+    case GEMM_TILE_256x256: return launch_cfg<IN, 256, 2, 2, IMM_BIG_NBR>(p, a, slice, s);
+    case GEMM_TILE_64x256: return launch_cfg<IN, 64, 1, IMM_NARROW_NS, 0>(p, a, slice, s);
+    case GEMM_TILE_32x256: return launch_cfg<IN, 32, 1, IMM_NARROW_NS, 0>(p, a, slice, s);
     default: return hipErrorInvalidValue;
   }
 }
 
 }  // namespace
 
-hipError_t launch_gemm_dma(const gemm_plan_s& p, const GemmArgs& a, bool slice_mode,
+hipError_t launch_gemm_dma(const gemm_plan_s& p, int tile, const GemmArgs& a, bool slice_mode,
                            hipStream_t s) {
   switch (p.in) {
-    case GEMM_F16: return launch_in<GEMM_F16>(p, a, slice_mode, s);
-    case GEMM_BF16: return launch_in<GEMM_BF16>(p, a, slice_mode, s);
-    case GEMM_F8_E4M3: return launch_in<GEMM_F8_E4M3>(p, a, slice_mode, s);
-    case GEMM_F8_E5M2: return launch_in<GEMM_F8_E5M2>(p, a, slice_mode, s);
+    case GEMM_F16: return launch_in<GEMM_F16>(p, tile, a, slice_mode, s);
+    case GEMM_BF16: return launch_in<GEMM_BF16>(p, tile, a, slice_mode, s);
+    case GEMM_F8_E4M3: return launch_in<GEMM_F8_E4M3>(p, tile, a, slice_mode, s);
+    case GEMM_F8_E5M2: return launch_in<GEMM_F8_E5M2>(p, tile, a, slice_mode, s);
     default: return hipErrorInvalidValue;
   }
 }

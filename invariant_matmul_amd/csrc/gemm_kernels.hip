@@ -301,21 +301,22 @@ hipError_t launch_tile(int tile, const GemmArgs& a, bool slice, hipStream_t s) {
 }
 
 template <int IN>
-hipError_t launch_in(const gemm_plan_s& p, const GemmArgs& a, bool slice, hipStream_t s) {
-  if (p.out == GEMM_F32) return launch_tile<IN, GEMM_F32>(p.tile, a, slice, s);
-  return launch_tile<IN, GEMM_BF16>(p.tile, a, slice, s);
+hipError_t launch_in(const gemm_plan_s& p, int tile, const GemmArgs& a, bool slice, hipStream_t s) {
+  if (p.out == GEMM_F32) return launch_tile<IN, GEMM_F32>(tile, a, slice, s);
+  return launch_tile<IN, GEMM_BF16>(tile, a, slice, s);
 }
 
 }  // namespace
 
-hipError_t launch_gemm(const gemm_plan_s& p, const GemmArgs& a, bool slice_mode, hipStream_t s) {
-  if (p.tile == GEMM_TILE_256x256 || p.tile == GEMM_TILE_32x256 || p.tile == GEMM_TILE_64x256)
-    return launch_gemm_dma(p, a, slice_mode, s);
+hipError_t launch_gemm(const gemm_plan_s& p, int tile, const GemmArgs& a, bool slice_mode,
+                       hipStream_t s) {
+  if (tile == GEMM_TILE_256x256 || tile == GEMM_TILE_32x256 || tile == GEMM_TILE_64x256)
+    return launch_gemm_dma(p, tile, a, slice_mode, s);
   switch (p.in) {
-    case GEMM_F16: return launch_in<GEMM_F16>(p, a, slice_mode, s);
-    case GEMM_BF16: return launch_in<GEMM_BF16>(p, a, slice_mode, s);
-    case GEMM_F8_E4M3: return launch_in<GEMM_F8_E4M3>(p, a, slice_mode, s);
-    case GEMM_F8_E5M2: return launch_in<GEMM_F8_E5M2>(p, a, slice_mode, s);
+    case GEMM_F16: return launch_in<GEMM_F16>(p, tile, a, slice_mode, s);
+    case GEMM_BF16: return launch_in<GEMM_BF16>(p, tile, a, slice_mode, s);
+    case GEMM_F8_E4M3: return launch_in<GEMM_F8_E4M3>(p, tile, a, slice_mode, s);
+    case GEMM_F8_E5M2: return launch_in<GEMM_F8_E5M2>(p, tile, a, slice_mode, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -35,13 +35,20 @@ inline int mfma_k(int dt) { return elem_bytes(dt) == 1 ? 64 : 16; }
 struct gemm_plan_s {
   int64_t M, N, K;
   int in, out;
+  // Tile of the split-K path (gemm_splitk_run) ...
   int tile;             // gemm_tile actually used
   int bm, bn, bk;       // bk in elements
   int waves_m, waves_n;
+  int64_t tiles_m, tiles_n;
+  // ... and of the single pass (gemm_run).  Both are chosen from (N, K,
+  // dtype, options); the bits do not depend on either.
+  int run_tile;
+  int run_bm, run_bn;
+  int run_waves_m, run_waves_n;
+  int64_t run_tiles_m, run_tiles_n;
   int group_m;
   int split_k;          // slices actually used (after rounding)
   int64_t k_per_split;  // elements, multiple of bk
-  int64_t tiles_m, tiles_n;
   float scale_a, scale_b;
   float scale;          // fp32 product applied in the epilogue
 };
@@ -101,9 +108,11 @@ struct ReduceArgs {
 // Launchers (gemm_kernels.hip).  They only enqueue; they return the launch
 // status.  `slice_mode` selects the split-K partial kernel (fp32 workspace
 // output, raw sums, no scale) instead of the final store.
-hipError_t launch_gemm(const gemm_plan_s& p, const GemmArgs& a, bool slice_mode, hipStream_t s);
+hipError_t launch_gemm(const gemm_plan_s& p, int tile, const GemmArgs& a, bool slice_mode,
+                       hipStream_t s);
 hipError_t launch_reduce(const gemm_plan_s& p, const ReduceArgs& a, hipStream_t s);
-// The DMA-fed 256x256 kernel (gemm_dma.hip); launch_gemm forwards to it.
-hipError_t launch_gemm_dma(const gemm_plan_s& p, const GemmArgs& a, bool slice_mode, hipStream_t s);
+// The DMA-fed kernels (gemm_dma.hip); launch_gemm forwards the DMA tiles to it.
+hipError_t launch_gemm_dma(const gemm_plan_s& p, int tile, const GemmArgs& a, bool slice_mode,
+                           hipStream_t s);
 
 }  // namespace imm

@@ -23,7 +23,8 @@ HEADER = os.path.join(ROOT, "include", "invariant_matmul.h")
 
 M_INDEPENDENT = ("N", "K", "in_dtype", "out_dtype", "tile", "block_m", "block_n", "block_k",
                  "mfma_m", "mfma_n", "mfma_k", "waves", "group_m", "split_k", "k_per_split",
-                 "tiles_n", "scale_a", "scale_b")
+                 "tiles_n", "scale_a", "scale_b", "run_tile", "run_block_m", "run_block_n",
+                 "run_waves", "run_tiles_n")
 
 SHAPES = [  # (N, K, dtype) of every workload family, plus a few others
     (256, 256, "f16"), (1024, 1024, "f16"), (4096, 4096, "f16"), (8192, 8192, "f16"),
@@ -62,7 +63,9 @@ def test_plan_is_independent_of_M(N, K, dt):
         assert key == ref, (M, key, ref)
         assert info["workspace_bytes"] == info["split_k"] * M * N * 4
         assert info["tiles_m"] == -(-M // info["block_m"])
-        assert info["grid_splitk"] == info["grid_run"] * info["split_k"]
+        assert info["run_tiles_m"] == -(-M // info["run_block_m"])
+        assert info["grid_splitk"] == info["tiles_m"] * info["tiles_n"] * info["split_k"]
+        assert info["grid_run"] == info["run_tiles_m"] * info["run_tiles_n"]
 
 
 @pytest.mark.parametrize("N,K,dt", SHAPES)
@@ -92,6 +95,13 @@ def test_default_plans_of_the_workloads():
     assert fp8["mfma_k"] == 64 and fp8["out_dtype"] == imm.DTYPE["bf16"]
     dec = imm.gemm_plan(1, 4096, 14336, "bf16").info
     assert dec["split_k"] > 1 and dec["block_m"] == 32
+    # without a split the single pass keeps the large tile (the plan cannot
+    # know that M is small)
+    assert (dec["run_block_m"], dec["run_block_n"]) == (256, 256)
+    hk = imm.gemm_plan(256, 256, 131072, "f16").info
+    assert (hk["block_m"], hk["block_n"], hk["split_k"]) == (64, 256, 64)
+    small = imm.gemm_plan(1024, 1024, 1024, "f16").info
+    assert (small["run_block_m"], small["run_block_n"]) == (32, 256)
 
 
 @pytest.mark.parametrize("M,N,K,dt,split,gm", [
