@@ -76,7 +76,8 @@ typedef enum {
 } gemm_status;
 
 /* Element types.  Inputs: F16, BF16, F8_E4M3 (OCP e4m3fn), F8_E5M2 (OCP e5m2).
- * Outputs: F32 or BF16 (round to nearest, ties to even). */
+ * Outputs: F32, BF16 or F16 (round to nearest, ties to even; fp16 keeps
+ * subnormals and overflows to infinity). */
 typedef enum {
   GEMM_F16 = 0,
   GEMM_BF16 = 1,
@@ -99,6 +100,16 @@ typedef enum {
                                reduction-dominated shapes */
   GEMM_TILE_64x256 = 6      /* 4 waves, DMA ring */
 } gemm_tile;
+
+/* Plan flags (gemm_plan_ex2). */
+typedef enum {
+  /* B is given transposed: a [N, K] row-major matrix W with B = W^T (the
+   * weight layout of a linear layer, y = x W^T + b, as in the vLLM
+   * batch-invariant operators the Tencent article lists in its closing
+   * section).  Only the DMA tiles (256x256, 64x256, 32x256) read this layout;
+   * the bits of C are those of the [K, N] layout holding the same values. */
+  GEMM_PLAN_B_TRANSPOSED = 1
+} gemm_plan_flags;
 
 typedef struct gemm_plan_s* gemm_plan_t;
 
@@ -134,7 +145,8 @@ typedef struct {
  * workspace.  On success *out receives a new plan. */
 gemm_status gemm_plan(int64_t M, int64_t N, int64_t K, gemm_dtype in, gemm_plan_t* out);
 
-/* As gemm_plan with explicit options.  out_dtype: GEMM_F32 or GEMM_BF16.
+/* As gemm_plan with explicit options.  out_dtype: GEMM_F32, GEMM_BF16 or
+ * GEMM_F16.
  * split_k: 0 = default, else 1..4096 (the slice length is rounded up to a
  * multiple of block_k; the split actually used is reported by
  * gemm_plan_info).  group_m: 0 = default (8), else >= 1.  tile: a gemm_tile
@@ -144,6 +156,14 @@ gemm_status gemm_plan(int64_t M, int64_t N, int64_t K, gemm_dtype in, gemm_plan_
 gemm_status gemm_plan_ex(int64_t M, int64_t N, int64_t K, gemm_dtype in, gemm_dtype out,
                          int split_k, int group_m, int tile, float scale_a, float scale_b,
                          gemm_plan_t* plan);
+
+/* As gemm_plan_ex with plan flags (a bitwise OR of gemm_plan_flags; unknown
+ * bits give GEMM_ERR_UNSUPPORTED).  With GEMM_PLAN_B_TRANSPOSED, B is read as
+ * [N, K] row-major; an explicit register-staged tile, or a K so large that the
+ * DMA tiles' 32-bit offsets overflow, gives GEMM_ERR_UNSUPPORTED. */
+gemm_status gemm_plan_ex2(int64_t M, int64_t N, int64_t K, gemm_dtype in, gemm_dtype out,
+                          int split_k, int group_m, int tile, float scale_a, float scale_b,
+                          unsigned flags, gemm_plan_t* plan);
 
 gemm_status gemm_plan_info(gemm_plan_t plan, gemm_plan_info_t* info);
 
@@ -159,12 +179,25 @@ gemm_status gemm_plan_tile_of(gemm_plan_t plan, int64_t workgroup, int64_t* k_sl
 /* C = A x B in one pass: one workgroup per output tile, full K in order. */
 gemm_status gemm_run(gemm_plan_t plan, const void* A, const void* B, void* C, void* stream);
 
+/* As gemm_run plus a bias: C[i, j] = convert(scale * sum_ij + bias[j]), one
+ * fp32 add after the scale.  bias: device fp32 [N], 4-byte aligned, or NULL
+ * (then exactly gemm_run).  The bias term of a linear layer (the vLLM
+ * batch-invariant linear operator in the Tencent article's closing section). */
+gemm_status gemm_run_bias(gemm_plan_t plan, const void* A, const void* B, const float* bias,
+                          void* C, void* stream);
+
 /* C = A x B through the split-K workspace: the partial kernel writes slice s
  * of K to workspace[s, :, :] (fp32, no atomics), then a reduction kernel sums
  * the slices in ascending s and writes C.  With split_k == 1 the result is
  * bitwise identical to gemm_run. */
 gemm_status gemm_splitk_run(gemm_plan_t plan, const void* A, const void* B, void* C,
                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* As gemm_splitk_run plus a bias, added by the reduction kernel after the
+ * ascending-slice sum and the scale (same rule as gemm_run_bias). */
+gemm_status gemm_splitk_run_bias(gemm_plan_t plan, const void* A, const void* B,
+                                 const float* bias, void* C, void* workspace,
+                                 size_t workspace_bytes, void* stream);
 
 void gemm_plan_destroy(gemm_plan_t plan);
 

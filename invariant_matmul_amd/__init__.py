@@ -7,6 +7,8 @@ the C ABI in include/invariant_matmul.h:
     plan = gemm_plan(M, N, K, "f16")                  # pure host call
     gemm_run(plan, A, B, C)                           # C = A @ B
     gemm_splitk_run(plan, A, B, C, workspace)         # split-K path
+    plan = gemm_plan_ex2(M, N, K, "f16", "f16", flags=PLAN_B_TRANSPOSED)
+    gemm_run(plan, A, W, C, bias=b)                   # C = A @ W.T + b
 
 A, B, C, workspace are CUDA(HIP) tensors (or raw device addresses as ints);
 ``stream`` defaults to torch's current stream on the operands' device.  There
@@ -18,10 +20,10 @@ import ctypes
 import os
 
 __all__ = [
-    "GemmError", "Plan", "PlanInfo", "gemm_plan", "gemm_plan_ex", "gemm_plan_info",
-    "gemm_workspace_size", "gemm_plan_tile_of", "gemm_run", "gemm_splitk_run",
+    "GemmError", "Plan", "PlanInfo", "gemm_plan", "gemm_plan_ex", "gemm_plan_ex2",
+    "gemm_plan_info", "gemm_workspace_size", "gemm_plan_tile_of", "gemm_run", "gemm_splitk_run",
     "gemm_plan_destroy", "gemm_status_string", "gemm_last_hip_error", "mm", "lib", "LIB_PATH",
-    "DTYPE", "TILE", "STATUS", "EXPORTED_SYMBOLS",
+    "DTYPE", "TILE", "STATUS", "EXPORTED_SYMBOLS", "PLAN_B_TRANSPOSED",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libinvariant_matmul.so")
@@ -31,10 +33,11 @@ STATUS = {0: "GEMM_OK", 1: "GEMM_ERR_INVALID_VALUE", 2: "GEMM_ERR_UNSUPPORTED",
 DTYPE = {"f16": 0, "bf16": 1, "e4m3": 2, "e5m2": 3, "f32": 4}
 TILE = {"default": 0, "256x256": 1, "128x128": 2, "32x128": 3, "256x256_rs": 4, "32x256": 5,
         "64x256": 6}
+PLAN_B_TRANSPOSED = 1
 EXPORTED_SYMBOLS = (
-    "gemm_plan", "gemm_plan_ex", "gemm_plan_info", "gemm_workspace_size", "gemm_plan_tile_of",
-    "gemm_run", "gemm_splitk_run", "gemm_plan_destroy", "gemm_status_string",
-    "gemm_last_hip_error",
+    "gemm_plan", "gemm_plan_ex", "gemm_plan_ex2", "gemm_plan_info", "gemm_workspace_size",
+    "gemm_plan_tile_of", "gemm_run", "gemm_run_bias", "gemm_splitk_run", "gemm_splitk_run_bias",
+    "gemm_plan_destroy", "gemm_status_string", "gemm_last_hip_error",
 )
 
 
@@ -84,20 +87,25 @@ def lib() -> ctypes.CDLL:
         pp = ctypes.POINTER(ctypes.c_void_p)
         L.gemm_plan.argtypes = [i64, i64, i64, i32, pp]
         L.gemm_plan_ex.argtypes = [i64, i64, i64, i32, i32, i32, i32, i32, f32, f32, pp]
+        L.gemm_plan_ex2.argtypes = [i64, i64, i64, i32, i32, i32, i32, i32, f32, f32,
+                                    ctypes.c_uint, pp]
         L.gemm_plan_info.argtypes = [vp, ctypes.POINTER(PlanInfo)]
         L.gemm_workspace_size.argtypes = [vp]
         L.gemm_workspace_size.restype = ctypes.c_size_t
         p64 = ctypes.POINTER(ctypes.c_int64)
         L.gemm_plan_tile_of.argtypes = [vp, i64, p64, p64, p64]
         L.gemm_run.argtypes = [vp, vp, vp, vp, vp]
+        L.gemm_run_bias.argtypes = [vp, vp, vp, vp, vp, vp]
         L.gemm_splitk_run.argtypes = [vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+        L.gemm_splitk_run_bias.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
         L.gemm_plan_destroy.argtypes = [vp]
         L.gemm_plan_destroy.restype = None
         L.gemm_status_string.argtypes = [i32]
         L.gemm_status_string.restype = ctypes.c_char_p
         L.gemm_last_hip_error.argtypes = []
-        for f in ("gemm_plan", "gemm_plan_ex", "gemm_plan_info", "gemm_plan_tile_of",
-                  "gemm_run", "gemm_splitk_run", "gemm_last_hip_error"):
+        for f in ("gemm_plan", "gemm_plan_ex", "gemm_plan_ex2", "gemm_plan_info",
+                  "gemm_plan_tile_of", "gemm_run", "gemm_run_bias", "gemm_splitk_run",
+                  "gemm_splitk_run_bias", "gemm_last_hip_error"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -156,6 +164,17 @@ def gemm_plan_ex(M: int, N: int, K: int, dtype, out_dtype="f32", split_k: int = 
     return Plan(h.value)
 
 
+def gemm_plan_ex2(M: int, N: int, K: int, dtype, out_dtype="f32", split_k: int = 0,
+                  group_m: int = 0, tile="default", scale_a: float = 1.0, scale_b: float = 1.0,
+                  flags: int = 0) -> Plan:
+    h = ctypes.c_void_p()
+    t = TILE[tile] if isinstance(tile, str) else int(tile)
+    _check(lib().gemm_plan_ex2(M, N, K, _dtype_code(dtype), _dtype_code(out_dtype), split_k,
+                               group_m, t, scale_a, scale_b, int(flags), ctypes.byref(h)),
+           "gemm_plan_ex2")
+    return Plan(h.value)
+
+
 def gemm_plan_info(plan: Plan) -> dict:
     info = PlanInfo()
     _check(lib().gemm_plan_info(plan.handle, ctypes.byref(info)), "gemm_plan_info")
@@ -202,27 +221,31 @@ def _check_tensor(t, name, dtype_code, numel):
         raise ValueError(f"{name} has {t.numel()} elements, plan expects {numel}")
 
 
-def _check_operands(plan: Plan, A, B, C):
+def _check_operands(plan: Plan, A, B, C, bias=None):
     i = gemm_plan_info(plan)
     _check_tensor(A, "A", i["in_dtype"], i["M"] * i["K"])
     _check_tensor(B, "B", i["in_dtype"], i["K"] * i["N"])
     _check_tensor(C, "C", i["out_dtype"], i["M"] * i["N"])
+    _check_tensor(bias, "bias", DTYPE["f32"], i["N"])
 
 
-def gemm_run(plan: Plan, A, B, C, stream=None) -> None:
-    _check_operands(plan, A, B, C)
-    _check(lib().gemm_run(plan.handle, _addr(A), _addr(B), _addr(C), _stream(stream, A, B, C)),
-           "gemm_run")
+def gemm_run(plan: Plan, A, B, C, stream=None, bias=None) -> None:
+    """C = A @ B (+ bias, an fp32 vector of N) in one pass."""
+    _check_operands(plan, A, B, C, bias)
+    _check(lib().gemm_run_bias(plan.handle, _addr(A), _addr(B), _addr(bias), _addr(C),
+                               _stream(stream, A, B, C)), "gemm_run")
 
 
-def gemm_splitk_run(plan: Plan, A, B, C, workspace, stream=None, workspace_bytes=None) -> None:
-    _check_operands(plan, A, B, C)
+def gemm_splitk_run(plan: Plan, A, B, C, workspace, stream=None, workspace_bytes=None,
+                    bias=None) -> None:
+    """C = A @ B (+ bias) through the split-K workspace and the reduction kernel."""
+    _check_operands(plan, A, B, C, bias)
     if workspace_bytes is None:
         workspace_bytes = 0 if workspace is None or isinstance(workspace, int) else (
             workspace.numel() * workspace.element_size())
-    _check(lib().gemm_splitk_run(plan.handle, _addr(A), _addr(B), _addr(C), _addr(workspace),
-                                 int(workspace_bytes), _stream(stream, A, B, C)),
-           "gemm_splitk_run")
+    _check(lib().gemm_splitk_run_bias(plan.handle, _addr(A), _addr(B), _addr(bias), _addr(C),
+                                      _addr(workspace), int(workspace_bytes),
+                                      _stream(stream, A, B, C)), "gemm_splitk_run")
 
 
 def gemm_plan_destroy(plan: Plan) -> None:

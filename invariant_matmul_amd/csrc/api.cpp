@@ -29,7 +29,7 @@ constexpr int kMaxSplit = 4096;
 bool valid_in(int dt) {
   return dt == GEMM_F16 || dt == GEMM_BF16 || dt == GEMM_F8_E4M3 || dt == GEMM_F8_E5M2;
 }
-bool valid_out(int dt) { return dt == GEMM_F32 || dt == GEMM_BF16; }
+bool valid_out(int dt) { return dt == GEMM_F32 || dt == GEMM_BF16 || dt == GEMM_F16; }
 
 void tile_shape(int tile, int* bm, int* bn, int* wm, int* wn) {
   switch (tile) {
@@ -79,17 +79,23 @@ bool is_dma_tile(int tile) {
   return tile == GEMM_TILE_256x256 || tile == GEMM_TILE_32x256 || tile == GEMM_TILE_64x256;
 }
 
-// A DMA tile whose 32-bit buffer offsets would overflow falls back to a
-// register-staged tile of the same bits.  The DMA kernels address one A tile
-// (bm rows) and one B stage (128 bytes of K: 128 / eb rows of N elements).
-int checked_tile(int tile, int64_t N, int64_t K, int eb) {
-  if (!is_dma_tile(tile)) return tile;
+// The DMA kernels address one A tile (bm rows of K) and one B stage (128
+// bytes of K: 128 / eb rows of N elements, or with B transposed bn rows of
+// K) with 32-bit offsets.
+bool dma_offsets_fit(int tile, int64_t N, int64_t K, int eb, bool b_trans) {
   int bm, bn, wm, wn;
   tile_shape(tile, &bm, &bn, &wm, &wn);
   const int64_t lim = ((int64_t)1 << 31) - 256;
-  if (bm * K * eb >= lim || 128 * N >= lim)
-    return tile == GEMM_TILE_256x256 ? GEMM_TILE_256x256_RS : GEMM_TILE_32x128;
-  return tile;
+  return bm * K * eb < lim && (b_trans ? bn * K * eb < lim : 128 * N < lim);
+}
+
+// A DMA tile whose offsets would overflow falls back to a register-staged
+// tile of the same bits (none exists for transposed B: -1).
+int checked_tile(int tile, int64_t N, int64_t K, int eb, bool b_trans) {
+  if (!is_dma_tile(tile)) return b_trans ? -1 : tile;
+  if (dma_offsets_fit(tile, N, K, eb, b_trans)) return tile;
+  if (b_trans) return -1;
+  return tile == GEMM_TILE_256x256 ? GEMM_TILE_256x256_RS : GEMM_TILE_32x128;
 }
 
 // Workgroups the default split aims for per row of output tiles.  Wide
@@ -118,6 +124,7 @@ int default_split(int64_t N, int64_t K, int bn, int bk) {
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
 gemm_status hip_fail(hipError_t e) {
   g_last_hip_error = (int)e;
@@ -150,6 +157,7 @@ GemmArgs make_args(const gemm_plan_s* p, const void* A, const void* B, void* out
   a.A = A;
   a.B = B;
   a.C = out;
+  a.bias = nullptr;
   a.M = p->M;
   a.N = p->N;
   a.K = p->K;
@@ -169,6 +177,12 @@ extern "C" {
 gemm_status gemm_plan_ex(int64_t M, int64_t N, int64_t K, gemm_dtype in, gemm_dtype out,
                          int split_k, int group_m, int tile, float scale_a, float scale_b,
                          gemm_plan_t* plan) {
+  return gemm_plan_ex2(M, N, K, in, out, split_k, group_m, tile, scale_a, scale_b, 0, plan);
+}
+
+gemm_status gemm_plan_ex2(int64_t M, int64_t N, int64_t K, gemm_dtype in, gemm_dtype out,
+                          int split_k, int group_m, int tile, float scale_a, float scale_b,
+                          unsigned flags, gemm_plan_t* plan) {
   if (!plan) return GEMM_ERR_INVALID_VALUE;
   *plan = nullptr;
   if (M < 0 || N < 0 || K < 0) return GEMM_ERR_INVALID_VALUE;
@@ -177,6 +191,8 @@ gemm_status gemm_plan_ex(int64_t M, int64_t N, int64_t K, gemm_dtype in, gemm_dt
   if (split_k < 0 || split_k > kMaxSplit || group_m < 0) return GEMM_ERR_UNSUPPORTED;
   if (tile < GEMM_TILE_DEFAULT || tile > GEMM_TILE_64x256) return GEMM_ERR_UNSUPPORTED;
   if (!std::isfinite(scale_a) || !std::isfinite(scale_b)) return GEMM_ERR_UNSUPPORTED;
+  if (flags & ~(unsigned)GEMM_PLAN_B_TRANSPOSED) return GEMM_ERR_UNSUPPORTED;
+  const bool bt = (flags & GEMM_PLAN_B_TRANSPOSED) != 0;
   // 16-byte vector access of every row of A and B needs K and N to be
   // multiples of 16 bytes' worth of elements.
   const int eb = elem_bytes(in);
@@ -190,15 +206,30 @@ gemm_status gemm_plan_ex(int64_t M, int64_t N, int64_t K, gemm_dtype in, gemm_dt
   p->K = K;
   p->in = in;
   p->out = out;
-  p->tile = checked_tile(tile == GEMM_TILE_DEFAULT ? default_tile(N, K, eb) : tile, N, K, eb);
+  p->b_trans = bt;
+  int split_tile = tile == GEMM_TILE_DEFAULT ? default_tile(N, K, eb) : tile;
+  // Transposed B runs on the DMA tiles only; its decode-like default is the
+  // 32-row DMA tile.
+  if (bt && tile == GEMM_TILE_DEFAULT && split_tile == GEMM_TILE_32x128) split_tile = GEMM_TILE_32x256;
+  p->tile = checked_tile(split_tile, N, K, eb, bt);
   p->run_tile =
-      checked_tile(tile == GEMM_TILE_DEFAULT ? default_run_tile(N, K, eb) : tile, N, K, eb);
+      checked_tile(tile == GEMM_TILE_DEFAULT ? default_run_tile(N, K, eb) : tile, N, K, eb, bt);
+  if (p->tile < 0 || p->run_tile < 0) {
+    delete p;
+    return GEMM_ERR_UNSUPPORTED;
+  }
   tile_shape(p->tile, &p->bm, &p->bn, &p->waves_m, &p->waves_n);
   tile_shape(p->run_tile, &p->run_bm, &p->run_bn, &p->run_waves_m, &p->run_waves_n);
   p->bk = block_k_elems(in);
   p->group_m = group_m == 0 ? 8 : group_m;
   const int64_t steps = ceil_div(K, p->bk);
-  int s = split_k == 0 ? default_split(N, K, p->bn, p->bk) : split_k;
+  // The default split (which decides bits) comes from (N, K, dtype) alone:
+  // it is computed for the default split-path tile of the [K, N] layout,
+  // whatever tile or B layout this plan runs, so an explicit tile or a
+  // transposed B never changes the bits.
+  int def_bm, def_bn, def_wm, def_wn;
+  tile_shape(default_tile(N, K, eb), &def_bm, &def_bn, &def_wm, &def_wn);
+  int s = split_k == 0 ? default_split(N, K, def_bn, p->bk) : split_k;
   // Slices are contiguous, equal multiples of bk ([TDI] "Split-K" leaves the
   // segment boundaries open; this is the plain reading).  Drop trailing empty
   // slices so every slice has work.
@@ -278,21 +309,34 @@ gemm_status gemm_plan_tile_of(gemm_plan_t p, int64_t w, int64_t* k_slice, int64_
   return GEMM_OK;
 }
 
-gemm_status gemm_run(gemm_plan_t p, const void* A, const void* B, void* C, void* stream) {
+gemm_status gemm_run_bias(gemm_plan_t p, const void* A, const void* B, const float* bias,
+                          void* C, void* stream) {
   gemm_status st = check_operands(p, A, B, C);
   if (st != GEMM_OK || p->M == 0 || p->N == 0) return st;
+  if (bias && !aligned4(bias)) return GEMM_ERR_INVALID_VALUE;
   hipError_t e = device_ready();
   if (e != hipSuccess) return hip_fail(e);
-  e = launch_gemm(*p, p->run_tile, make_args(p, A, B, C, false), false,
-                  static_cast<hipStream_t>(stream));
+  GemmArgs a = make_args(p, A, B, C, false);
+  a.bias = bias;
+  e = launch_gemm(*p, p->run_tile, a, false, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e);
   return GEMM_OK;
 }
 
+gemm_status gemm_run(gemm_plan_t p, const void* A, const void* B, void* C, void* stream) {
+  return gemm_run_bias(p, A, B, nullptr, C, stream);
+}
+
 gemm_status gemm_splitk_run(gemm_plan_t p, const void* A, const void* B, void* C,
                             void* workspace, size_t workspace_bytes, void* stream) {
+  return gemm_splitk_run_bias(p, A, B, nullptr, C, workspace, workspace_bytes, stream);
+}
+
+gemm_status gemm_splitk_run_bias(gemm_plan_t p, const void* A, const void* B, const float* bias,
+                                 void* C, void* workspace, size_t workspace_bytes, void* stream) {
   gemm_status st = check_operands(p, A, B, C);
   if (st != GEMM_OK || p->M == 0 || p->N == 0) return st;
+  if (bias && !aligned4(bias)) return GEMM_ERR_INVALID_VALUE;
   if (!workspace || workspace_bytes < gemm_workspace_size(p)) return GEMM_ERR_WORKSPACE;
   if (!aligned16(workspace)) return GEMM_ERR_INVALID_VALUE;
   hipError_t e = device_ready();
@@ -303,7 +347,9 @@ gemm_status gemm_splitk_run(gemm_plan_t p, const void* A, const void* B, void* C
   ReduceArgs r;
   r.ws = static_cast<const float*>(workspace);
   r.C = C;
+  r.bias = bias;
   r.MN = p->M * p->N;
+  r.N = p->N;
   r.split_k = p->split_k;
   r.scale = p->scale;
   e = launch_reduce(*p, r, s);

@@ -105,7 +105,12 @@ constexpr int waves_per_simd() {
 // NBR: 0 = A and B blocks of a stage share one ring of NS slots; otherwise B
 // has a ring of its own with NBR slots (A keeps NS), so B is requested
 // NBR - 1 stages ahead while A is requested NS - 1 stages ahead.
-template <int IN, int OUT, bool SLICE, int TBM, int WM, int NS, int NBR>
+// BT: B is given transposed, as [N, K] row-major (the weight layout of a
+// linear layer).  Its rows are then K-contiguous like those of A, so B is
+// staged and read exactly like A (128-byte rows, ds_read_b128); the matrix
+// core sees the same values in the same K order, so the bits are those of
+// the [K, N] layout.
+template <int IN, int OUT, bool SLICE, int TBM, int WM, int NS, int NBR, bool BT>
 __global__ __launch_bounds__(256 * WM, (waves_per_simd<TBM, NS>())) void gemm_dma_kernel(GemmArgs g) {
   using T = InT<IN>;
   constexpr int EB = T::EB;
@@ -132,7 +137,7 @@ __global__ __launch_bounds__(256 * WM, (waves_per_simd<TBM, NS>())) void gemm_dm
   static_assert(DA * WAVES * 1024 == A_STAGE && DB * WAVES * 1024 == B_STAGE, "DMA split");
   static_assert(FM * 32 * WM == TBM, "tile rows");
   constexpr int NRA = EB == 2 ? FM : 2 * FM; // fragment reads per k-step: A ...
-  constexpr int NRB = EB == 2 ? 2 * FN : 4 * FN;  // ... and B
+  constexpr int NRB = BT ? (EB == 2 ? FN : 2 * FN) : (EB == 2 ? 2 * FN : 4 * FN);  // ... and B
   constexpr int NREAD = NRA + NRB;
   constexpr bool SPLIT = NBR > 0;
   constexpr int NBS = SPLIT ? NBR : NS;      // B slots
@@ -181,11 +186,19 @@ __global__ __launch_bounds__(256 * WM, (waves_per_simd<TBM, NS>())) void gemm_dm
 #pragma unroll
   for (int i = 0; i < DB; ++i) {
     const int idx = w * DB + i;
-    const int k = BROWS_PER_DMA * idx + lane / BSLOTS;
-    const int s = lane % BSLOTS;
-    const int cb = EB == 2 ? (s ^ ((k & 3) << 2)) : (s ^ ((k & 7) << 1));
-    b_off[i] = (n0 + cb * (16 / EB) < g.N) ? (unsigned)(k * g.N * EB + cb * 16) : OOB;
-    b_k[i] = k;
+    if constexpr (BT) {
+      // row n of B^T (column n of B), laid out like a row of A
+      const int row = AROWS_PER_DMA * idx + lane / ACH;
+      const int c = (lane % ACH) ^ aswz(row);
+      b_off[i] = (n0 + row < g.N) ? (unsigned)(row * g.K * EB + c * 16) : OOB;
+      b_k[i] = c * (16 / EB);  // first K element of the chunk
+    } else {
+      const int k = BROWS_PER_DMA * idx + lane / BSLOTS;
+      const int s = lane % BSLOTS;
+      const int cb = EB == 2 ? (s ^ ((k & 3) << 2)) : (s ^ ((k & 7) << 1));
+      b_off[i] = (n0 + cb * (16 / EB) < g.N) ? (unsigned)(k * g.N * EB + cb * 16) : OOB;
+      b_k[i] = k;  // K row of the chunk
+    }
   }
 
   struct StageSrc {
@@ -197,7 +210,7 @@ __global__ __launch_bounds__(256 * WM, (waves_per_simd<TBM, NS>())) void gemm_dm
     StageSrc q;
     const int64_t kst = kbeg + (int64_t)t * BKE;
     q.pa = A + (m0 * g.K + kst) * EB;
-    q.pb = B + (kst * g.N + n0) * EB;
+    q.pb = BT ? B + (n0 * g.K + kst) * EB : B + (kst * g.N + n0) * EB;
     q.rem = kend - kst < BKE ? (int)(kend - kst) : BKE;
     return q;
   };
@@ -224,8 +237,11 @@ __global__ __launch_bounds__(256 * WM, (waves_per_simd<TBM, NS>())) void gemm_dm
 #pragma unroll
   for (int i = 0; i < FM; ++i) a_rd[i] = (wm * WTM + i * 32 + l32) * SKB;
   const int grp = lane >> 4, gi = lane & 15;
-  int b_rd[FN];  // per column block j: byte offset of the first transposing read
-  if constexpr (EB == 2) {
+  int b_rd[FN];  // per column block j: byte offset of its first read
+  if constexpr (BT) {
+#pragma unroll
+    for (int j = 0; j < FN; ++j) b_rd[j] = (wn * WTN + j * 32 + l32) * SKB;
+  } else if constexpr (EB == 2) {
     const int t_ = gi >> 2, q = gi & 3;
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
@@ -252,8 +268,26 @@ __global__ __launch_bounds__(256 * WM, (waves_per_simd<TBM, NS>())) void gemm_dm
   //           else B block j = (x-FM)/2, half r = (x-FM)%2 (K elements 4r..4r+3).
   //   fp8:    x < 2FM -> A block i = x/2, half x%2 (16 bytes of K each);
   //           else B block j = (x-2FM)/4, piece r = (x-2FM)%4 (8 K values).
+  //   B given transposed: B block j is read like an A block (x-NRA = j for
+  //   16-bit, 2j + half for fp8).
   auto read_one = [&](Frag<IN, FM, FN>& F, int as, int bs, int ks, int x) {
     const char* sb = lds + as;
+    if constexpr (BT) {
+      if (x >= NRA) {
+        const char* sbb = lds + bs;
+        if constexpr (EB == 2) {
+          const int j = x - NRA, c = ks * 2 + h;
+          F.b[j] = *reinterpret_cast<const i32x4*>(sbb + b_rd[j] + ((c ^ asw) << 4));
+        } else {
+          const int j = (x - NRA) >> 1, f = (x - NRA) & 1;
+          const int c = ks * 4 + 2 * h + f;
+          const i32x4 v = *reinterpret_cast<const i32x4*>(sbb + b_rd[j] + ((c ^ asw) << 4));
+#pragma unroll
+          for (int e = 0; e < 4; ++e) F.b[j][4 * f + e] = v[e];
+        }
+        return;
+      }
+    }
     if constexpr (EB == 2) {
       if (x < NRA) {
         const int c = ks * 2 + h;
@@ -400,7 +434,7 @@ __global__ __launch_bounds__(256 * WM, (waves_per_simd<TBM, NS>())) void gemm_dm
           if constexpr (SLICE) {
             static_cast<float*>(g.C)[(ksl * g.M + row) * g.N + col] = v;
           } else {
-            store_out<OUT>(g.C, row * g.N + col, v * g.scale);
+            store_final<OUT>(g.C, row * g.N + col, v, g.scale, g.bias, col);
           }
         }
       }
@@ -408,33 +442,34 @@ __global__ __launch_bounds__(256 * WM, (waves_per_simd<TBM, NS>())) void gemm_dm
   }
 }
 
-template <int IN, int TBM, int WM, int NS, int NBR>
+template <int IN, int TBM, int WM, int NS, bool BT>
 hipError_t launch_cfg(const gemm_plan_s& p, const GemmArgs& a, bool slice, hipStream_t s) {
   const dim3 grid((unsigned)a.grid), block(256 * WM);
   if (slice)
-    hipLaunchKernelGGL((gemm_dma_kernel<IN, GEMM_F32, true, TBM, WM, NS, NBR>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((gemm_dma_kernel<IN, GEMM_F32, true, TBM, WM, NS, 0, BT>), grid, block, 0, s, a);
   else if (p.out == GEMM_F32)
-    hipLaunchKernelGGL((gemm_dma_kernel<IN, GEMM_F32, false, TBM, WM, NS, NBR>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((gemm_dma_kernel<IN, GEMM_F32, false, TBM, WM, NS, 0, BT>), grid, block, 0, s, a);
+  else if (p.out == GEMM_F16)
+    hipLaunchKernelGGL((gemm_dma_kernel<IN, GEMM_F16, false, TBM, WM, NS, 0, BT>), grid, block, 0, s, a);
   else
-    hipLaunchKernelGGL((gemm_dma_kernel<IN, GEMM_BF16, false, TBM, WM, NS, NBR>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((gemm_dma_kernel<IN, GEMM_BF16, false, TBM, WM, NS, 0, BT>), grid, block, 0, s, a);
   return hipGetLastError();
 }
 
-#ifndef IMM_NARROW_NS
-#define IMM_NARROW_NS 4
-#endif
-#ifndef IMM_BIG_NBR
-#define IMM_BIG_NBR 0
-#endif
+template <int IN, bool BT>
+hipError_t launch_tiles(const gemm_plan_s& p, int tile, const GemmArgs& a, bool slice, hipStream_t s) {
+  switch (tile) {
+    case GEMM_TILE_256x256: return launch_cfg<IN, 256, 2, 2, BT>(p, a, slice, s);
+    case GEMM_TILE_64x256: return launch_cfg<IN, 64, 1, 4, BT>(p, a, slice, s);
+    case GEMM_TILE_32x256: return launch_cfg<IN, 32, 1, 4, BT>(p, a, slice, s);
+    default: return hipErrorInvalidValue;
+  }
+}
 
 template <int IN>
 hipError_t launch_in(const gemm_plan_s& p, int tile, const GemmArgs& a, bool slice, hipStream_t s) {
-  switch (tile) {
-    case GEMM_TILE_256x256: return launch_cfg<IN, 256, 2, 2, IMM_BIG_NBR>(p, a, slice, s);
-    case GEMM_TILE_64x256: return launch_cfg<IN, 64, 1, IMM_NARROW_NS, 0>(p, a, slice, s);
-    case GEMM_TILE_32x256: return launch_cfg<IN, 32, 1, IMM_NARROW_NS, 0>(p, a, slice, s);
-    default: return hipErrorInvalidValue;
-  }
+  return p.b_trans ? launch_tiles<IN, true>(p, tile, a, slice, s)
+                   : launch_tiles<IN, false>(p, tile, a, slice, s);
 }
 
 }  // namespace

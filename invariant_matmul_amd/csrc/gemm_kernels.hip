@@ -237,7 +237,7 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_tile_kernel(GemmAr
           if constexpr (SLICE) {
             static_cast<float*>(g.C)[(ks * g.M + row) * g.N + col] = v;
           } else {
-            store_out<OUT>(g.C, row * g.N + col, v * g.scale);
+            store_final<OUT>(g.C, row * g.N + col, v, g.scale, g.bias, col);
           }
         }
       }
@@ -245,8 +245,8 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_tile_kernel(GemmAr
   }
 }
 
-// C = convert(scale * (((ws[0] + ws[1]) + ws[2]) + ... + ws[S-1])), fp32 adds in
-// ascending slice order for every element ([TDI] "Split-K": the separate
+// C = convert(scale * (((ws[0] + ws[1]) + ws[2]) + ... + ws[S-1]) [+ bias]),
+// fp32 adds in ascending slice order for every element ([TDI] "Split-K": the separate
 // reduction kernel that sums the workspace over split_k).  Four consecutive
 // elements per thread, grid-stride.  The slices are loaded in groups of RG
 // before they are added (in order), so a thread waits for one memory latency
@@ -276,7 +276,10 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(ReduceArgs r) {
       }
     }
 #pragma unroll
-    for (int e = 0; e < 4; ++e) store_out<OUT>(r.C, i * 4 + e, v[e] * r.scale);
+    for (int e = 0; e < 4; ++e) {
+      const int64_t idx = i * 4 + e;
+      store_final<OUT>(r.C, idx, v[e], r.scale, r.bias, idx % r.N);
+    }
   }
 }
 
@@ -303,6 +306,7 @@ hipError_t launch_tile(int tile, const GemmArgs& a, bool slice, hipStream_t s) {
 template <int IN>
 hipError_t launch_in(const gemm_plan_s& p, int tile, const GemmArgs& a, bool slice, hipStream_t s) {
   if (p.out == GEMM_F32) return launch_tile<IN, GEMM_F32>(tile, a, slice, s);
+  if (p.out == GEMM_F16) return launch_tile<IN, GEMM_F16>(tile, a, slice, s);
   return launch_tile<IN, GEMM_BF16>(tile, a, slice, s);
 }
 
@@ -328,6 +332,8 @@ hipError_t launch_reduce(const gemm_plan_s& p, const ReduceArgs& a, hipStream_t 
   if (blocks < 1) blocks = 1;
   if (p.out == GEMM_F32)
     hipLaunchKernelGGL(splitk_reduce_kernel<GEMM_F32>, dim3((unsigned)blocks), dim3(256), 0, s, a);
+  else if (p.out == GEMM_F16)
+    hipLaunchKernelGGL(splitk_reduce_kernel<GEMM_F16>, dim3((unsigned)blocks), dim3(256), 0, s, a);
   else
     hipLaunchKernelGGL(splitk_reduce_kernel<GEMM_BF16>, dim3((unsigned)blocks), dim3(256), 0, s, a);
   return hipGetLastError();

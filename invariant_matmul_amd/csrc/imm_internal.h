@@ -46,6 +46,7 @@ struct gemm_plan_s {
   int run_bm, run_bn;
   int run_waves_m, run_waves_n;
   int64_t run_tiles_m, run_tiles_n;
+  bool b_trans;         // B is given as [N, K] row-major (DMA tiles only)
   int group_m;
   int split_k;          // slices actually used (after rounding)
   int64_t k_per_split;  // elements, multiple of bk
@@ -89,6 +90,7 @@ struct GemmArgs {
   const void* A;
   const void* B;
   void* C;              // output (store-C mode) or workspace (slice mode)
+  const float* bias;    // fp32 [N] added in the epilogue, or null (store-C mode only)
   int64_t M, N, K;
   int64_t k_per_split;  // elements per K slice (K itself when not split)
   int64_t tiles_m, tiles_n;
@@ -100,7 +102,9 @@ struct GemmArgs {
 struct ReduceArgs {
   const float* ws;
   void* C;
+  const float* bias;    // fp32 [N] or null
   int64_t MN;           // M * N
+  int64_t N;
   int split_k;
   float scale;
 };

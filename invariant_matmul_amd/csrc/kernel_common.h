@@ -85,9 +85,23 @@ template <int OUT>
 __device__ __forceinline__ void store_out(void* C, int64_t idx, float v) {
   if constexpr (OUT == GEMM_F32) {
     static_cast<float*>(C)[idx] = v;
+  } else if constexpr (OUT == GEMM_F16) {
+    // v_cvt_f16_f32: round to nearest even, fp16 subnormals kept, overflow to inf
+    static_cast<_Float16*>(C)[idx] = static_cast<_Float16>(v);
   } else {
     static_cast<unsigned short*>(C)[idx] = f32_to_bf16(v);
   }
+}
+
+// The epilogue of one output element: the fp32 sum times the fp32 product
+// of the scales, plus the fp32 bias of its column when there is one (one
+// fp32 add), converted to the output format.
+template <int OUT>
+__device__ __forceinline__ void store_final(void* C, int64_t idx, float sum, float scale,
+                                            const float* bias, int64_t col) {
+  float v = sum * scale;
+  if (bias) v = v + bias[col];
+  store_out<OUT>(C, idx, v);
 }
 
 // Transposing LDS reads (gfx950).  Issued as inline assembly: the compiler

@@ -137,6 +137,32 @@ def gemm(A_bits, B_bits, fmt: str, scale: float = 1.0, rows=None, nthreads: int 
     return C, Ca
 
 
+def linear(x_bits, w_bits, fmt: str, bias=None, scale: float = 1.0, rows=None,
+           nthreads: int = 0):
+    """(Y64, Yabs) for the linear layer Y = scale * x @ W^T + bias.
+
+    The layer a batch-invariant inference stack puts on top of the matrix
+    product (the vLLM batch-invariant ``linear`` operator listed in the
+    closing section of the Tencent deterministic-inference article): x is
+    [M, K], the weight W is [N, K] (one row per output feature), bias is an
+    fp64-decodable vector of N values or None.  ``Y64`` is the exact product
+    from ``gemm`` (with B = W^T) plus the bias, added in fp64; ``Yabs`` is
+    ``|scale| |x| |W^T| + |bias|`` for the error bound.
+    """
+    W = _bits(fmt, w_bits)
+    if W.ndim != 2:
+        raise ValueError(f"weight must be 2-D, got {W.shape}")
+    C, Ca = gemm(x_bits, np.ascontiguousarray(W.T), fmt, scale=scale, rows=rows,
+                 nthreads=nthreads)
+    if bias is not None:
+        b = np.asarray(bias, dtype=np.float64)
+        if b.shape != (C.shape[1],):
+            raise ValueError(f"bias must have {C.shape[1]} values, got {b.shape}")
+        C = C + b[None, :]
+        Ca = Ca + np.abs(b)[None, :]
+    return C, Ca
+
+
 def gemm_elems(A_bits, B_bits, fmt: str, ii, jj, scale: float = 1.0, nthreads: int = 0):
     """(c64, cabs) at the listed output positions (ii[t], jj[t])."""
     A = _bits(fmt, A_bits)

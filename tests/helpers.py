@@ -3,7 +3,10 @@
 The error bound for fp32 output is the one the deterministic-GEMM target
 fixes: |C - C_ref| <= K * 2^-24 * (|A||B|)_ij, with C_ref the exact (fp64)
 product.  For bf16 output it adds the final rounding to bf16 (unit roundoff
-2^-8): K u (|A||B|)(1 + 2^-8) + 2^-8 |C_ref|.
+2^-8): K u (|A||B|)(1 + 2^-8) + 2^-8 |C_ref|; fp16 output likewise with
+2^-11 plus half the smallest fp16 subnormal (2^-25).  A bias adds one fp32
+rounding of the sum: the accumulated bound times (1 + 2^-24) plus
+2^-24 |C_ref|, with |A||B| + |bias| in place of |A||B|.
 """
 from __future__ import annotations
 
@@ -18,6 +21,7 @@ import workloads as wl
 
 U32 = 2.0 ** -24
 U_BF16 = 2.0 ** -8
+U_F16 = 2.0 ** -11
 
 
 def log(msg: str) -> None:
@@ -30,7 +34,8 @@ def dev():
 
 
 def out_torch_dtype(code: int):
-    return torch.float32 if code == imm.DTYPE["f32"] else torch.bfloat16
+    return {imm.DTYPE["f32"]: torch.float32, imm.DTYPE["bf16"]: torch.bfloat16,
+            imm.DTYPE["f16"]: torch.float16}[code]
 
 
 def run(plan, A, B, split: bool, stream=None):
@@ -62,17 +67,22 @@ def expected_bits(C64: np.ndarray, out: str) -> np.ndarray:
     return oracle.round_rne(out, C64)
 
 
-def bound(K: int, C64: np.ndarray, Cabs: np.ndarray, out: str) -> np.ndarray:
+def bound(K: int, C64: np.ndarray, Cabs: np.ndarray, out: str, bias: bool = False) -> np.ndarray:
     b = K * U32 * Cabs
+    if bias:
+        b = b * (1.0 + U32) + U32 * np.abs(C64)
     if out == "bf16":
         b = b * (1.0 + U_BF16) + U_BF16 * np.abs(C64)
+    elif out == "f16":
+        b = b * (1.0 + U_F16) + U_F16 * np.abs(C64) + 2.0 ** -25
     return b
 
 
-def check_bound(C: np.ndarray, C64: np.ndarray, Cabs: np.ndarray, K: int, out: str) -> float:
+def check_bound(C: np.ndarray, C64: np.ndarray, Cabs: np.ndarray, K: int, out: str,
+                bias: bool = False) -> float:
     """Assert every element is within the bound; returns max |err| / bound."""
     err = np.abs(C - C64)
-    b = bound(K, C64, Cabs, out)
+    b = bound(K, C64, Cabs, out, bias)
     bad = err > b
     if bad.any():
         idx = np.argwhere(bad)[:5]

@@ -145,7 +145,8 @@ def _plan_status(*args):
     ((8, -8, 8, 0, 4, 0, 0, 0, 1.0, 1.0), 1),
     ((8, 8, -8, 0, 4, 0, 0, 0, 1.0, 1.0), 1),
     ((8, 8, 8, 4, 4, 0, 0, 0, 1.0, 1.0), 2),      # fp32 input unsupported
-    ((8, 8, 8, 0, 0, 0, 0, 0, 1.0, 1.0), 2),      # fp16 output unsupported
+    ((8, 8, 8, 0, 3, 0, 0, 0, 1.0, 1.0), 2),      # fp8 output unsupported
+    ((8, 8, 8, 0, 0, 0, 0, 0, 1.0, 1.0), 0),      # fp16 output
     ((8, 8, 8, 7, 4, 0, 0, 0, 1.0, 1.0), 2),      # unknown dtype
     ((8, 12, 8, 0, 4, 0, 0, 0, 1.0, 1.0), 2),     # N not a multiple of 8
     ((8, 8, 12, 0, 4, 0, 0, 0, 1.0, 1.0), 2),     # K not a multiple of 8
@@ -163,6 +164,34 @@ def _plan_status(*args):
 ])
 def test_plan_validation(args, status):
     assert _plan_status(*args) == status
+
+
+def _plan2_status(*args):
+    h = ctypes.c_void_p()
+    return imm.lib().gemm_plan_ex2(*args, ctypes.byref(h))
+
+
+@pytest.mark.parametrize("args,status", [
+    ((8, 8, 8, 0, 4, 0, 0, 0, 1.0, 1.0, 0), 0),
+    ((8, 8, 8, 0, 4, 0, 0, 0, 1.0, 1.0, 1), 0),            # B given as [N, K]
+    ((8, 8, 8, 0, 4, 0, 0, 0, 1.0, 1.0, 2), 2),            # unknown flag bit
+    ((8, 8, 8, 0, 4, 0, 0, 3, 1.0, 1.0, 1), 2),            # transposed B needs a DMA tile
+    ((8, 8, 8, 0, 4, 0, 0, 5, 1.0, 1.0, 1), 0),
+    ((8, 8, 2 ** 24, 0, 4, 0, 0, 0, 1.0, 1.0, 1), 2),      # DMA offsets would overflow
+    ((8, 8, 2 ** 24, 0, 4, 0, 0, 0, 1.0, 1.0, 0), 0),      # register-staged fallback
+])
+def test_plan_flags_validation(args, status):
+    assert _plan2_status(*args) == status
+
+
+def test_transposed_b_plans_use_dma_tiles_and_the_same_split():
+    dma = {imm.TILE[t] for t in ("256x256", "32x256", "64x256")}
+    for N, K, dt in SHAPES:
+        a = imm.gemm_plan_ex2(64, N, K, dt, "f32").info
+        b = imm.gemm_plan_ex2(64, N, K, dt, "f32", flags=imm.PLAN_B_TRANSPOSED).info
+        assert b["tile"] in dma and b["run_tile"] in dma, (N, K, dt)
+        # the split (which decides the bits) does not depend on the layout
+        assert (a["split_k"], a["k_per_split"]) == (b["split_k"], b["k_per_split"]), (N, K, dt)
 
 
 def test_null_plan_handles():
