@@ -1,0 +1,171 @@
+"""Batch-invariant torch operators on top of the library.
+
+The Tencent deterministic-inference article closes with vLLM's
+batch-invariant mode, which replaces ``mm``, ``addmm``, ``matmul`` and
+``linear`` with a GEMM whose configuration never depends on the batch size.
+This module gives the same four operators on this library, and a context
+manager that routes torch's own entry points through them:
+
+    from invariant_matmul_amd import torch_ops
+    y = torch_ops.linear(x, weight, bias)          # x [..., K], weight [N, K]
+    with torch_ops.batch_invariant_mode():
+        y = model(x)                               # nn.Linear, torch.mm, @ ...
+
+Every product is planned from (N, K, dtype) alone (the library's rule), so
+row i of a result depends only on row i of the input, on the weight and on
+K: never on how many rows share the call.  A weight given as a transposed
+view (``W.t()`` of a contiguous [N, K] tensor, which is how ``linear`` hands
+it over) is read in place through the library's transposed-B plans.  Inputs
+are fp16 or bf16 CUDA tensors; the result has the input dtype (fp32 sums,
+one rounding at the end); a bias is added in fp32 before that rounding.
+
+The direct functions raise for anything else.  The context manager only
+reroutes what the library computes (2-D weights, fp16 / bf16, N and K
+multiples of 8, alpha = beta = 1) and leaves other calls (fp32 tensors, CPU
+tensors, batched weights) to torch's own implementation.
+"""
+from __future__ import annotations
+
+import contextlib
+import functools
+
+import torch
+
+from . import PLAN_B_TRANSPOSED, gemm_plan_ex2, gemm_run, gemm_splitk_run, gemm_workspace_size
+
+__all__ = ["mm", "addmm", "linear", "matmul", "batch_invariant_mode", "supported"]
+
+_DT = {torch.float16: "f16", torch.bfloat16: "bf16"}
+
+
+@functools.lru_cache(maxsize=512)
+def _plan(M: int, N: int, K: int, dt: str, flags: int):
+    return gemm_plan_ex2(M, N, K, dt, dt, flags=flags)
+
+
+def supported(a: torch.Tensor, b: torch.Tensor) -> bool:
+    """True if a @ b (a [..., K], b [K, N]) is a product this module computes."""
+    return (a.is_cuda and b.is_cuda and a.dtype in _DT and b.dtype == a.dtype
+            and b.dim() == 2 and a.dim() >= 1 and a.shape[-1] == b.shape[0]
+            and b.shape[0] % 8 == 0 and b.shape[1] % 8 == 0)
+
+
+def _product(a2: torch.Tensor, b: torch.Tensor, bias) -> torch.Tensor:
+    """a2 [M, K] @ b [K, N] (+ bias [N]) in the dtype of a2."""
+    M, K = a2.shape
+    N = b.shape[1]
+    dt = _DT[a2.dtype]
+    a2 = a2.contiguous()
+    flags = 0
+    if b.is_contiguous():
+        bm = b
+    elif b.t().is_contiguous():
+        bm, flags = b.t(), PLAN_B_TRANSPOSED  # the [N, K] weight itself
+    else:
+        bm = b.contiguous()
+    out = torch.empty((M, N), dtype=a2.dtype, device=a2.device)
+    if M == 0 or N == 0:
+        return out
+    bias32 = None
+    if bias is not None:
+        bias32 = bias.reshape(N).to(device=a2.device, dtype=torch.float32).contiguous()
+    plan = _plan(M, N, K, dt, flags)
+    if plan.info["split_k"] > 1:
+        ws = torch.empty(max(1, gemm_workspace_size(plan) // 4), dtype=torch.float32,
+                         device=a2.device)
+        gemm_splitk_run(plan, a2, bm, out, ws, bias=bias32)
+    else:
+        gemm_run(plan, a2, bm, out, bias=bias32)
+    return out
+
+
+def _require(a, b):
+    if not supported(a, b):
+        raise ValueError(
+            "invariant_matmul_amd.torch_ops: needs fp16/bf16 CUDA tensors, a [..., K] and a 2-D "
+            f"[K, N] second operand with K, N multiples of 8; got {tuple(a.shape)} {a.dtype} @ "
+            f"{tuple(b.shape)} {b.dtype}")
+
+
+def mm(a: torch.Tensor, b: torch.Tensor) -> torch.Tensor:
+    """a [M, K] @ b [K, N]."""
+    if a.dim() != 2:
+        raise ValueError("mm: a must be 2-D")
+    _require(a, b)
+    return _product(a, b, None)
+
+
+def addmm(bias: torch.Tensor, a: torch.Tensor, b: torch.Tensor, *, beta=1, alpha=1) -> torch.Tensor:
+    """bias + a @ b with a bias of N values (broadcast over rows); beta = alpha = 1."""
+    if beta != 1 or alpha != 1:
+        raise ValueError("addmm: only beta = alpha = 1")
+    if a.dim() != 2:
+        raise ValueError("addmm: a must be 2-D")
+    _require(a, b)
+    if bias.numel() != b.shape[1]:
+        raise ValueError("addmm: the bias must hold N values")
+    return _product(a, b, bias)
+
+
+def linear(x: torch.Tensor, weight: torch.Tensor, bias=None) -> torch.Tensor:
+    """x [..., K] @ weight[N, K]^T + bias."""
+    wt = weight.t()
+    _require(x, wt)
+    lead = x.shape[:-1]
+    y = _product(x.reshape(-1, x.shape[-1]), wt, bias)
+    return y.reshape(*lead, weight.shape[0])
+
+
+def matmul(a: torch.Tensor, b: torch.Tensor) -> torch.Tensor:
+    """a [..., K] @ b [K, N] (leading dimensions of a are rows)."""
+    _require(a, b)
+    if a.dim() == 1:
+        return _product(a.reshape(1, -1), b, None).reshape(b.shape[1])
+    lead = a.shape[:-1]
+    return _product(a.reshape(-1, a.shape[-1]), b, None).reshape(*lead, b.shape[1])
+
+
+@contextlib.contextmanager
+def batch_invariant_mode():
+    """Route torch.nn.functional.linear, torch.mm, torch.addmm, torch.matmul and
+    the ``@`` operator through this module while the context is active."""
+    import torch.nn.functional as F
+
+    saved = {"linear": F.linear, "mm": torch.mm, "addmm": torch.addmm,
+             "matmul": torch.matmul, "tmatmul": torch.Tensor.__matmul__}
+
+    def _linear(x, weight, bias=None):
+        if weight.dim() == 2 and supported(x, weight.t()) and (
+                bias is None or bias.numel() == weight.shape[0]):
+            return linear(x, weight, bias)
+        return saved["linear"](x, weight, bias)
+
+    def _mm(a, b, **kw):
+        if not kw and a.dim() == 2 and supported(a, b):
+            return mm(a, b)
+        return saved["mm"](a, b, **kw)
+
+    def _addmm(bias, a, b, *, beta=1, alpha=1, **kw):
+        if (not kw and beta == 1 and alpha == 1 and a.dim() == 2 and supported(a, b)
+                and bias.numel() == b.shape[1]):
+            return addmm(bias, a, b)
+        return saved["addmm"](bias, a, b, beta=beta, alpha=alpha, **kw)
+
+    def _matmul(a, b, **kw):
+        if not kw and isinstance(a, torch.Tensor) and isinstance(b, torch.Tensor) and supported(a, b):
+            return matmul(a, b)
+        return saved["matmul"](a, b, **kw)
+
+    def _tmatmul(a, b):
+        if isinstance(b, torch.Tensor) and supported(a, b):
+            return matmul(a, b)
+        return saved["tmatmul"](a, b)
+
+    F.linear, torch.mm, torch.addmm, torch.matmul = _linear, _mm, _addmm, _matmul
+    torch.Tensor.__matmul__ = _tmatmul
+    try:
+        yield
+    finally:
+        F.linear, torch.mm, torch.addmm = saved["linear"], saved["mm"], saved["addmm"]
+        torch.matmul, torch.Tensor.__matmul__ = saved["matmul"], saved["tmatmul"]
+
