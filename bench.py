@@ -185,6 +185,30 @@ def bench_splitk(name, split, torch, imm, wl, n=30, warmup=5, M=None):
             "workspace_traffic_bytes": 2 * plan.info["workspace_bytes"]}
 
 
+def bench_m_sweep(torch, imm, wl, N=6144, K=4096, ms=(1, 16, 64, 256, 1024, 4096, 8192)):
+    """The price of one M-independent plan: gemm_run on the fused-QKV projection
+    shape at growing M, next to torch.matmul (hipBLASLt, which picks its kernel
+    per shape and is not batch-invariant).  Rows are prefixes of one A."""
+    g = wl.gen(6000)
+    A = wl.uniform((max(ms), K), "f16", g).cuda()
+    B = wl.uniform((K, N), "f16", g).cuda()
+    out = []
+    for m in ms:
+        a = A[:m].contiguous()
+        plan = imm.gemm_plan(m, N, K, "f16")
+        C = torch.empty((m, N), dtype=torch.float32, device="cuda")
+        per, _ = time_launches(lambda i: imm.gemm_run(plan, a, B, C), 20, 5, torch)
+        ref = torch.empty((m, N), dtype=torch.float16, device="cuda")
+        tper, _ = time_launches(lambda i: torch.matmul(a, B, out=ref), 20, 5, torch)
+        med, tmed = statistics.median(per), statistics.median(tper)
+        out.append({"M": m, "N": N, "K": K,
+                    "tile": f"{plan.info['run_block_m']}x{plan.info['run_block_n']}",
+                    "median_us": med * 1e3, "TFLOPs": 2.0 * m * N * K / (med * 1e-3) / 1e12,
+                    "torch_matmul_median_us": tmed * 1e3,
+                    "torch_matmul_TFLOPs": 2.0 * m * N * K / (tmed * 1e-3) / 1e12})
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -282,6 +306,9 @@ def main():
         log("decode bf16 N=4096 K=14336, split-K path")
         extra["decode_bf16"] = [bench_splitk("decode_bf16_m128", 0, torch, imm, wl, M=m)
                                 for m in (1, 8, 32, 128)]
+        torch.cuda.empty_cache()
+        log("M sweep on the fused-QKV projection shape N=6144 K=4096, gemm_run")
+        extra["qkv_m_sweep_f16"] = bench_m_sweep(torch, imm, wl)
         torch.cuda.empty_cache()
         log("huge-K fp16 256x256x131072, split-K path")
         # split 0 = the plan's default for this shape
