@@ -102,15 +102,12 @@ constexpr int waves_per_simd() {
   return NS * (TBM + TBN) * SKB <= 80 * 1024 || TBM == 256 ? 2 : 1;
 }
 
-// NBR: 0 = A and B blocks of a stage share one ring of NS slots; otherwise B
-// has a ring of its own with NBR slots (A keeps NS), so B is requested
-// NBR - 1 stages ahead while A is requested NS - 1 stages ahead.
 // BT: B is given transposed, as [N, K] row-major (the weight layout of a
 // linear layer).  Its rows are then K-contiguous like those of A, so B is
 // staged and read exactly like A (128-byte rows, ds_read_b128); the matrix
 // core sees the same values in the same K order, so the bits are those of
 // the [K, N] layout.
-template <int IN, int OUT, bool SLICE, int TBM, int WM, int NS, int NBR, bool BT>
+template <int IN, int OUT, bool SLICE, int TBM, int WM, int NS, bool BT>
 __global__ __launch_bounds__(256 * WM, (waves_per_simd<TBM, NS>())) void gemm_dma_kernel(GemmArgs g) {
   using T = InT<IN>;
   constexpr int EB = T::EB;
@@ -139,19 +136,14 @@ __global__ __launch_bounds__(256 * WM, (waves_per_simd<TBM, NS>())) void gemm_dm
   constexpr int NRA = EB == 2 ? FM : 2 * FM; // fragment reads per k-step: A ...
   constexpr int NRB = BT ? (EB == 2 ? FN : 2 * FN) : (EB == 2 ? 2 * FN : 4 * FN);  // ... and B
   constexpr int NREAD = NRA + NRB;
-  constexpr bool SPLIT = NBR > 0;
-  constexpr int NBS = SPLIT ? NBR : NS;      // B slots
-  constexpr int LDS_BYTES = SPLIT ? NS * A_STAGE + NBR * B_STAGE : NS * STAGE;
+  constexpr int LDS_BYTES = NS * STAGE;
   static_assert(LDS_BYTES <= 160 * 1024, "LDS ring too large");
   static_assert(KS % 2 == 0, "k-steps per stage");
-  static_assert(!SPLIT || (NS == 2 && NBR >= NS), "split rings: A has 2 slots, B at least 2");
 
   __shared__ __attribute__((aligned(1024))) char lds[LDS_BYTES];
   // LDS offsets of the A and B blocks of stage t.
-  auto a_slot = [](int t) { return SPLIT ? (t % NS) * A_STAGE : (t % NS) * STAGE; };
-  auto b_slot = [](int t) {
-    return SPLIT ? NS * A_STAGE + (t % NBS) * B_STAGE : (t % NS) * STAGE + A_STAGE;
-  };
+  auto a_slot = [](int t) { return (t % NS) * STAGE; };
+  auto b_slot = [](int t) { return (t % NS) * STAGE + A_STAGE; };
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (uniform)
@@ -214,20 +206,20 @@ __global__ __launch_bounds__(256 * WM, (waves_per_simd<TBM, NS>())) void gemm_dm
     q.rem = kend - kst < BKE ? (int)(kend - kst) : BKE;
     return q;
   };
-  // DMA instruction x of this wave: x < DA: A rows of stage ta (source qa),
-  // else B rows of stage tb (source qb).
-  auto dma_one = [&](const StageSrc& qa, int ta, const StageSrc& qb, int tb, int x) {
+  // DMA instruction x of this wave for stage t (source q): x < DA: A rows,
+  // else B rows.
+  auto dma_one = [&](const StageSrc& q, int t, int x) {
     if (x < DA) {
-      const unsigned off = a_kel[x] < qa.rem ? a_off[x] : OOB;
+      const unsigned off = a_kel[x] < q.rem ? a_off[x] : OOB;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          __builtin_amdgcn_make_buffer_rsrc((void*)qa.pa, 0, NREC, RSRC_FLAGS),
-          IMM_LDS(lds + a_slot(ta) + (w * DA + x) * 1024), 16, off, 0, 0, 0);
+          __builtin_amdgcn_make_buffer_rsrc((void*)q.pa, 0, NREC, RSRC_FLAGS),
+          IMM_LDS(lds + a_slot(t) + (w * DA + x) * 1024), 16, off, 0, 0, 0);
     } else {
       const int i = x - DA;
-      const unsigned off = b_k[i] < qb.rem ? b_off[i] : OOB;
+      const unsigned off = b_k[i] < q.rem ? b_off[i] : OOB;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          __builtin_amdgcn_make_buffer_rsrc((void*)qb.pb, 0, NREC, RSRC_FLAGS),
-          IMM_LDS(lds + b_slot(tb) + (w * DB + i) * 1024), 16, off, 0, 0, 0);
+          __builtin_amdgcn_make_buffer_rsrc((void*)q.pb, 0, NREC, RSRC_FLAGS),
+          IMM_LDS(lds + b_slot(t) + (w * DB + i) * 1024), 16, off, 0, 0, 0);
     }
   };
 
@@ -333,29 +325,19 @@ __global__ __launch_bounds__(256 * WM, (waves_per_simd<TBM, NS>())) void gemm_dm
     acc[x / FN][x % FN] = mfma_v<IN>(F.a[x / FN], F.b[x % FN], acc[x / FN][x % FN]);
   };
 
-  // Issue order.  The prologue requests A(p) then B(p) for p = 0, 1, ...
-  // (A only for p < NS, B only for p < NBS); every refill requests A(t+NS)
-  // then B(t+NBS).  Before stage t+1 is used, the requests still allowed in
-  // flight are those after the later of A(t+1) and B(t+1): the B blocks of
-  // the NBS - NS stages that B runs ahead of A (split rings), or the NS - 2
-  // whole stages after t+1 (shared ring).  DMA is issued for every stage
-  // index in order (past the end of the slice it only writes zeros), so
-  // these counts never change.
-  constexpr int WAIT_FIRST = (NS - 1) * DA + (NBS - 1) * DB;
-  constexpr int WAIT_NEXT = SPLIT ? (NBS - NS) * DB : (NS - 2) * DPW;
+  // Issue order.  Stages are requested whole (A rows, then B rows) in
+  // ascending stage index: the prologue requests stages 0 .. NS-1, every
+  // refill stage t+NS.  Before stage t+1 is used, the NS - 2 stages after it
+  // may still be in flight.  DMA is issued for every stage index (past the
+  // end of the slice it only writes zeros), so these counts never change.
+  constexpr int WAIT_FIRST = (NS - 1) * DPW;
+  constexpr int WAIT_NEXT = (NS - 2) * DPW;
   Frag<IN, FM, FN> F0, F1;
   if (nt > 0) {
-    const int np = NS > NBS ? NS : NBS;
-    for (int p = 0; p < np; ++p) {
+    for (int p = 0; p < NS; ++p) {
       const StageSrc q = stage_src(p);
-      if (p < NS) {
 #pragma unroll
-        for (int x = 0; x < DA; ++x) dma_one(q, p, q, p, x);
-      }
-      if (p < NBS) {
-#pragma unroll
-        for (int x = DA; x < DPW; ++x) dma_one(q, p, q, p, x);
-      }
+      for (int x = 0; x < DPW; ++x) dma_one(q, p, x);
     }
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(WAIT_FIRST));
     __builtin_amdgcn_s_barrier();
@@ -368,32 +350,30 @@ __global__ __launch_bounds__(256 * WM, (waves_per_simd<TBM, NS>())) void gemm_dm
   // wave's fragment reads of that k-step have landed it has read all of stage
   // t, so after it waits for its own DMA of stage t+1 a single barrier
   // certifies that (a) stage t+1 is in LDS for every wave and (b) no wave
-  // reads the slots of stage t any more.  The whole last k-step then
-  // overlaps the refill of those slots (A with stage t+NS, B with stage
-  // t+NBS) and the fragment reads of stage t+1.
+  // reads the slot of stage t any more.  The whole last k-step then
+  // overlaps the refill of that slot with stage t+NS and the fragment reads
+  // of stage t+1.
   auto stage_change = [&]() {
     fence();
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(WAIT_NEXT));
     __builtin_amdgcn_s_barrier();
     fence();
   };
-  // MFMAs of one k-step on Fc, with (if refill) the DMA of A(t+NS) and
-  // B(t+NBS), and the fragment reads of k-step ks of stage tr into Fn spread
-  // between them.  Every stage runs the same instructions: a refill past the
+  // MFMAs of one k-step on Fc, with (if refill) the DMA of stage t+NS and the
+  // fragment reads of k-step ks of stage tr into Fn spread between them.  Every stage runs the same instructions: a refill past the
   // end of the slice has only out-of-range offsets (zero fill, no memory
   // traffic) and the reads past the last stage land in registers that are
   // never used.
   auto kstep = [&](bool refill, const Frag<IN, FM, FN>& Fc, int t, Frag<IN, FM, FN>& Fn, int tr,
                    int ks) {
-    const StageSrc qa = stage_src(t + NS);
-    const StageSrc qb = stage_src(t + NBS);
+    const StageSrc q = stage_src(t + NS);
     const int as = a_slot(tr), bs = b_slot(tr);
 #pragma unroll
     for (int x = 0; x < NM; ++x) {
       mfma_x(Fc, x);
       if (refill) {
 #pragma unroll
-        for (int y = x * DPW / NM; y < (x + 1) * DPW / NM; ++y) dma_one(qa, t + NS, qb, t + NBS, y);
+        for (int y = x * DPW / NM; y < (x + 1) * DPW / NM; ++y) dma_one(q, t + NS, y);
       }
 #pragma unroll
       for (int y = x * NREAD / NM; y < (x + 1) * NREAD / NM; ++y) read_one(Fn, as, bs, ks, y);
@@ -446,13 +426,13 @@ template <int IN, int TBM, int WM, int NS, bool BT>
 hipError_t launch_cfg(const gemm_plan_s& p, const GemmArgs& a, bool slice, hipStream_t s) {
   const dim3 grid((unsigned)a.grid), block(256 * WM);
   if (slice)
-    hipLaunchKernelGGL((gemm_dma_kernel<IN, GEMM_F32, true, TBM, WM, NS, 0, BT>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((gemm_dma_kernel<IN, GEMM_F32, true, TBM, WM, NS, BT>), grid, block, 0, s, a);
   else if (p.out == GEMM_F32)
-    hipLaunchKernelGGL((gemm_dma_kernel<IN, GEMM_F32, false, TBM, WM, NS, 0, BT>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((gemm_dma_kernel<IN, GEMM_F32, false, TBM, WM, NS, BT>), grid, block, 0, s, a);
   else if (p.out == GEMM_F16)
-    hipLaunchKernelGGL((gemm_dma_kernel<IN, GEMM_F16, false, TBM, WM, NS, 0, BT>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((gemm_dma_kernel<IN, GEMM_F16, false, TBM, WM, NS, BT>), grid, block, 0, s, a);
   else
-    hipLaunchKernelGGL((gemm_dma_kernel<IN, GEMM_BF16, false, TBM, WM, NS, 0, BT>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((gemm_dma_kernel<IN, GEMM_BF16, false, TBM, WM, NS, BT>), grid, block, 0, s, a);
   return hipGetLastError();
 }
 

@@ -14,7 +14,8 @@ import torch
 import invariant_matmul_amd as imm
 import oracle
 import workloads as wl
-from tests.helpers import (bits_of, check_bound, dev, expected_bits, log, run, values_of)
+from tests.helpers import (FP8, bits_of, check_bound, dev, expected_bits, fp8_step_window, log,
+                           run, values_of)
 
 pytestmark = pytest.mark.gpu
 
@@ -106,13 +107,16 @@ def test_random_inputs_within_bound_ragged(dt):
     A = wl.uniform((M, K), dt, g) if dt in ("f16", "bf16") else wl.normal((M, K), dt, g)
     B = wl.uniform((K, N), dt, g) if dt in ("f16", "bf16") else wl.normal((K, N), dt, g)
     C64, Ca = oracle.gemm(wl.bits(A), wl.bits(B), dt)
+    win = None
+    if dt in FP8:
+        win = fp8_step_window(oracle.decode(dt, wl.bits(A)), oracle.decode(dt, wl.bits(B)))
     Ad, Bd = _to_dev(A, B)
     for out in ("f32", "bf16"):
         for tile in TILES:
             for split in (1, 5):
                 p = imm.gemm_plan_ex(M, N, K, dt, out, split_k=split, tile=tile)
-                r1 = check_bound(values_of(run(p, Ad, Bd, False)), C64, Ca, K, out)
-                r2 = check_bound(values_of(run(p, Ad, Bd, True)), C64, Ca, K, out)
+                r1 = check_bound(values_of(run(p, Ad, Bd, False)), C64, Ca, K, out, window=win)
+                r2 = check_bound(values_of(run(p, Ad, Bd, True)), C64, Ca, K, out, window=win)
                 log(f"random {dt}->{out} tile {tile} split {split}: max err/bound {r1:.3g} {r2:.3g}")
 
 
@@ -184,15 +188,22 @@ def _check_sampled(w, plan, split, n=2048):
     got = C[torch.from_numpy(ii).to(dev()), torch.from_numpy(jj).to(dev())]
     got = got.cpu().to(torch.float64).numpy()
     c64, ca = oracle.gemm_elems(wl.bits(A), wl.bits(B), w.dtype, ii, jj)
-    r = check_bound(got, c64, ca, w.K, w.out)
+    fp8 = w.dtype in FP8
+    if fp8:
+        Av, Bv = oracle.decode(w.dtype, wl.bits(A)), oracle.decode(w.dtype, wl.bits(B))
+    win = (lambda i, j: fp8_step_window(Av, Bv, i, j)) if fp8 else (lambda i, j: None)
+    r = check_bound(got, c64, ca, w.K, w.out, window=win(ii, jj))
     # a full row and a full column as well
     row = w.M // 2
     cr, car = oracle.gemm(wl.bits(A), wl.bits(B), w.dtype, rows=[row])
-    r = max(r, check_bound(C[row].cpu().to(torch.float64).numpy(), cr[0], car[0], w.K, w.out))
+    jr = np.arange(w.N)
+    r = max(r, check_bound(C[row].cpu().to(torch.float64).numpy(), cr[0], car[0], w.K, w.out,
+                           window=win(np.full(w.N, row), jr)))
     col = w.N // 3
     ic = np.arange(w.M)
     cc, cac = oracle.gemm_elems(wl.bits(A), wl.bits(B), w.dtype, ic, np.full(w.M, col))
-    r = max(r, check_bound(C[:, col].cpu().to(torch.float64).numpy(), cc, cac, w.K, w.out))
+    r = max(r, check_bound(C[:, col].cpu().to(torch.float64).numpy(), cc, cac, w.K, w.out,
+                           window=win(ic, np.full(w.M, col))))
     log(f"{w.name}: max err/bound {r:.3g}")
     return C
 
