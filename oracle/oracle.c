@@ -104,18 +104,27 @@ int orc_decode(int code, const void* bits, int64_t n, double* out) {
 /* ---- rounding (fp64 -> narrower binary format, RNE) ------------------- */
 
 /* Round x to the nearest value of format f with ties to even and return its
- * bit pattern.  NaN maps to a quiet NaN, overflow to infinity (formats with
- * infinities only; the e4m3fn code is never a rounding target here). */
+ * bit pattern.  NaN maps to a quiet NaN; overflow goes to infinity, or to
+ * NaN in OCP e4m3fn, which has no infinity (OCP FP8 conversion without
+ * saturation). */
 static uint32_t round_bits(const orc_fmt* f, double x) {
   const int sign_shift = f->exp_bits + f->man_bits;
   const uint32_t emask = (1u << f->exp_bits) - 1u;
   uint32_t sign = signbit(x) ? (1u << sign_shift) : 0u;
-  if (isnan(x)) return sign | (emask << f->man_bits) | (1u << (f->man_bits - 1));
+  if (isnan(x)) {
+    return f->ieee_special ? (sign | (emask << f->man_bits) | (1u << (f->man_bits - 1)))
+                           : (sign | (emask << f->man_bits) | ((1u << f->man_bits) - 1u));
+  }
   double a = fabs(x);
-  if (isinf(a)) return sign | (emask << f->man_bits);
+  if (isinf(a)) {
+    return f->ieee_special ? (sign | (emask << f->man_bits))
+                           : (sign | (emask << f->man_bits) | ((1u << f->man_bits) - 1u));
+  }
   if (a == 0.0) return sign;
   const int emin = 1 - f->bias;           /* smallest normal exponent */
-  const int emax = (int)emask - 1 - f->bias; /* largest finite exponent */
+  /* largest finite exponent: the all-ones field is reserved in IEEE-like
+   * formats; e4m3fn uses it for finite values (only S.1111.111 is NaN) */
+  const int emax = (int)emask - (f->ieee_special ? 1 : 0) - f->bias;
   int ex;
   (void)frexp(a, &ex);                    /* a = fr * 2^ex, fr in [0.5, 1) */
   int E = ex - 1;                         /* a in [2^E, 2^(E+1)) */
@@ -127,8 +136,15 @@ static uint32_t round_bits(const orc_fmt* f, double x) {
   const double frac = n - r;              /* exact */
   if (frac > 0.5 || (frac == 0.5 && fmod(r, 2.0) != 0.0)) r += 1.0;
   const double v = r * q;                 /* exact */
-  const double maxfin = ldexp((double)((2u << f->man_bits) - 1u), emax - f->man_bits);
-  if (v > maxfin) return sign | (emask << f->man_bits); /* overflow -> inf */
+  /* largest finite significand: all ones, or all ones but the last bit for
+   * e4m3fn (1.110b * 2^8 = 448) */
+  const double maxfin = ldexp((double)((2u << f->man_bits) - (f->ieee_special ? 1u : 2u)),
+                              emax - f->man_bits);
+  if (v > maxfin) {
+    /* overflow: infinity, or NaN in e4m3fn, which has no infinity */
+    return f->ieee_special ? (sign | (emask << f->man_bits))
+                           : (sign | (emask << f->man_bits) | ((1u << f->man_bits) - 1u));
+  }
   if (v < ldexp(1.0, emin)) {
     /* subnormal: biased exponent 0, significand = v / 2^(emin - man_bits) */
     return sign | (uint32_t)(v / ldexp(1.0, emin - f->man_bits));
@@ -144,7 +160,6 @@ static uint32_t round_bits(const orc_fmt* f, double x) {
 int orc_round(int code, const double* x, int64_t n, void* out) {
   orc_fmt f;
   if (orc_format(code, &f)) return -1;
-  if (code == ORC_E4M3) return -1; /* no output in this format */
   for (int64_t i = 0; i < n; ++i) {
     uint32_t b = round_bits(&f, x[i]);
     if (f.bytes == 1) ((uint8_t*)out)[i] = (uint8_t)b;

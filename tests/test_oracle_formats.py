@@ -188,3 +188,22 @@ def test_round_ties_to_even_f16():
     # 2053 lies halfway between 2052 (even) and 2054: goes down.
     d = oracle.decode("f16", oracle.round_rne("f16", [2051.0, 2053.0, -2051.0]))
     assert list(d) == [2052.0, 2052.0, -2052.0]
+
+
+def test_round_e4m3_vs_torch():
+    # OCP e4m3fn: every finite value and every midpoint between neighbours
+    # (ties to even), plus random values in range, against torch's cast of
+    # fp32 inputs (all of them exact in fp32).
+    allv = oracle.decode("e4m3", np.arange(256, dtype=np.uint8))
+    fin = np.unique(allv[np.isfinite(allv)])
+    mids = (fin[:-1] + fin[1:]) / 2.0
+    rng = np.random.default_rng(14)
+    xs = rng.uniform(-448.0, 448.0, 200_000).astype(np.float32).astype(np.float64)
+    tiny = rng.uniform(-2.0 ** -6, 2.0 ** -6, 50_000).astype(np.float32).astype(np.float64)
+    x = np.concatenate([fin, mids, xs, tiny, np.array([0.0, -0.0])])
+    got = oracle.round_rne("e4m3", x)
+    want = torch.from_numpy(x.astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8)
+    assert np.array_equal(got, want.numpy()), np.flatnonzero(got != want.numpy())[:10]
+    # 448 is the largest finite value; beyond it e4m3fn has only NaN
+    assert oracle.round_rne("e4m3", [448.0, 464.0 - 1e-9, 1e6]).tolist()[:2] == [0x7E, 0x7E]
+    assert oracle.round_rne("e4m3", [1e6])[0] & 0x7F == 0x7F
