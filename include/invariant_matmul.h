@@ -201,6 +201,90 @@ gemm_status gemm_splitk_run_bias(gemm_plan_t plan, const void* A, const void* B,
 
 void gemm_plan_destroy(gemm_plan_t plan);
 
+/* ---------------------------------------------------------------------------
+ * fp64 matrix product by the Ozaki scheme: C = A x B with A [M,K], B [K,N]
+ * and C [M,N] in fp64 (row-major, contiguous), computed on the fp32-
+ * accumulating matrix cores from low-precision slices.  Insight Edge blog on
+ * cuTile Python, section "倍精度行列積エミュレーション":
+ *   split ("分解(Split)", equations (1)-(5)): every row of A and every column
+ *     of B is cut into `slices` Type2 slices (bf16 or fp8 e4m3) with
+ *     c0 = ceil(log2 max|x|) of that row / column, c_p = c0 - p*delta,
+ *     sigma = 0.75*2^(rho+c_p), v = (x+sigma)-sigma, x -= v,
+ *     slice_p = Type2(v*2^-c_p);
+ *   product ("行列積の計算", equations (10), (11)): for each slice pair (p,q),
+ *     p ascending then q ascending, without the pairs with p+q >= d ("Fast
+ *     Mode（GEMMの削減）"), the fp32 product of the two slices, scaled by
+ *     2^(c_p(row) + c_q(column)), is added to an fp64 sum starting at +0.
+ * Precision parameter ("分解(Split)"): rho = max(gamma, xi),
+ * gamma = ceil(53 - (24 - log2 K)/2), xi = 53 - m_Type2 (m = 8 for bf16, 4 for
+ * e4m3), with K the inner dimension.  A slice carries b = 53 - rho bits, so
+ * every fp32 slice product is exact and the result does not depend on any
+ * summation order inside the matrix cores: it is a bitwise function of row i
+ * of A, of B, of K and of (type2, slices, d).  delta = b + 1.
+ * Defaults: slices = min(ceil(53 / b), 20) (7 for bf16 and K <= 256, 14 for
+ * e4m3 and K <= 65536; 20 is the most the page's split routine makes),
+ * d = slices + 2 (39 products for 7 bf16 slices, 130 for 14 e4m3 slices, the
+ * page's "最適化後の結果" tables).
+ * Domain: finite inputs whose nonzero row / column maxima lie in
+ * [2^-300, 2^300].  There every slice value, scaled term and partial sum is
+ * a normal fp64 number, so the kernel may apply 2^(c0(row) + c0(column)) once
+ * at the end instead of to every term without changing a bit.  Outside it
+ * the result is unspecified (no error is reported).
+ *
+ * Workspace (device memory, caller-owned, 16-byte aligned, at least
+ * ozaki_workspace_size bytes), with the offsets that ozaki_plan_info reports:
+ *   a_slices  [slices, M, k_pad] Type2, row-major (k_pad = K rounded up to 16)
+ *   b_slices  [slices, k_pad, n_pad] Type2 (n_pad = N rounded up to 16)
+ *   a_exp     [M] int32 c0 of each row of A
+ *   b_exp     [n_pad] int32 c0 of each column of B
+ *   scratch   column maxima of B
+ * Padding entries of the slices are zero.  The contents stay valid after a
+ * call until the workspace is used again.
+ * ------------------------------------------------------------------------- */
+typedef struct ozaki_plan_s* ozaki_plan_t;
+
+typedef struct {
+  int64_t M, N, K;
+  int32_t type2;              /* GEMM_BF16 or GEMM_F8_E4M3 */
+  int32_t rho, bits, delta;   /* precision parameter, bits per slice, exponent step */
+  int32_t slices, d, pairs;   /* slices per operand, Fast Mode threshold, products */
+  int32_t tile_m, tile_n;     /* output tile of the product kernel */
+  int64_t k_pad, n_pad;
+  int64_t grid;               /* workgroups of the product kernel */
+  uint64_t workspace_bytes;
+  uint64_t a_slices_offset, b_slices_offset, a_exp_offset, b_exp_offset, scratch_offset;
+} ozaki_plan_info_t;
+
+/* Plan an Ozaki-scheme product.  type2: GEMM_BF16 or GEMM_F8_E4M3.
+ * slices: 0 = default, else 1..20; d: 0 = default, else >= 1.  M, N, K >= 0;
+ * K at most 2^22 (one bit per slice left); N below 2^23.  Errors:
+ * GEMM_ERR_INVALID_VALUE (negative size, NULL handle), GEMM_ERR_UNSUPPORTED
+ * (other type2, slices or d out of range, sizes too large). */
+gemm_status ozaki_plan(int64_t M, int64_t N, int64_t K, gemm_dtype type2, int slices, int d,
+                       ozaki_plan_t* plan);
+
+gemm_status ozaki_plan_info(ozaki_plan_t plan, ozaki_plan_info_t* info);
+
+size_t ozaki_workspace_size(ozaki_plan_t plan);
+
+/* The split of one operand into the workspace: operand 0 = A (x is [M, K]),
+ * 1 = B (x is [K, N]); x is device fp64, 8-byte aligned.  Enqueues the
+ * exponent and split kernels on `stream`. */
+gemm_status ozaki_split(ozaki_plan_t plan, int operand, const double* x, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
+/* The slice-pair product from a workspace holding both operands' slices and
+ * exponents (after ozaki_split of A and of B): writes C (device fp64 [M, N],
+ * 8-byte aligned). */
+gemm_status ozaki_multiply(ozaki_plan_t plan, const void* workspace, size_t workspace_bytes,
+                           double* C, void* stream);
+
+/* ozaki_split(A), ozaki_split(B), ozaki_multiply on one stream. */
+gemm_status ozaki_run(ozaki_plan_t plan, const double* A, const double* B, double* C,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+void ozaki_plan_destroy(ozaki_plan_t plan);
+
 const char* gemm_status_string(gemm_status status);
 
 /* HIP error code (hipError_t as int) of the most recent GEMM_ERR_HIP return on

@@ -24,6 +24,8 @@ __all__ = [
     "gemm_plan_info", "gemm_workspace_size", "gemm_plan_tile_of", "gemm_run", "gemm_splitk_run",
     "gemm_plan_destroy", "gemm_status_string", "gemm_last_hip_error", "mm", "lib", "LIB_PATH",
     "DTYPE", "TILE", "STATUS", "EXPORTED_SYMBOLS", "PLAN_B_TRANSPOSED",
+    "OzakiPlan", "ozaki_plan", "ozaki_plan_info", "ozaki_workspace_size", "ozaki_split",
+    "ozaki_multiply", "ozaki_run", "ozaki_mm",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libinvariant_matmul.so")
@@ -38,6 +40,8 @@ EXPORTED_SYMBOLS = (
     "gemm_plan", "gemm_plan_ex", "gemm_plan_ex2", "gemm_plan_info", "gemm_workspace_size",
     "gemm_plan_tile_of", "gemm_run", "gemm_run_bias", "gemm_splitk_run", "gemm_splitk_run_bias",
     "gemm_plan_destroy", "gemm_status_string", "gemm_last_hip_error",
+    "ozaki_plan", "ozaki_plan_info", "ozaki_workspace_size", "ozaki_split", "ozaki_multiply",
+    "ozaki_run", "ozaki_plan_destroy",
 )
 
 
@@ -65,6 +69,22 @@ class PlanInfo(ctypes.Structure):
         ("run_block_m", ctypes.c_int32), ("run_block_n", ctypes.c_int32),
         ("run_waves", ctypes.c_int32), ("run_tiles_m", ctypes.c_int64),
         ("run_tiles_n", ctypes.c_int64),
+    ]
+
+    def as_dict(self):
+        return {name: getattr(self, name) for name, _ in self._fields_}
+
+
+class OzakiPlanInfo(ctypes.Structure):
+    _fields_ = [
+        ("M", ctypes.c_int64), ("N", ctypes.c_int64), ("K", ctypes.c_int64),
+        ("type2", ctypes.c_int32), ("rho", ctypes.c_int32), ("bits", ctypes.c_int32),
+        ("delta", ctypes.c_int32), ("slices", ctypes.c_int32), ("d", ctypes.c_int32),
+        ("pairs", ctypes.c_int32), ("tile_m", ctypes.c_int32), ("tile_n", ctypes.c_int32),
+        ("k_pad", ctypes.c_int64), ("n_pad", ctypes.c_int64), ("grid", ctypes.c_int64),
+        ("workspace_bytes", ctypes.c_uint64), ("a_slices_offset", ctypes.c_uint64),
+        ("b_slices_offset", ctypes.c_uint64), ("a_exp_offset", ctypes.c_uint64),
+        ("b_exp_offset", ctypes.c_uint64), ("scratch_offset", ctypes.c_uint64),
     ]
 
     def as_dict(self):
@@ -103,9 +123,20 @@ def lib() -> ctypes.CDLL:
         L.gemm_status_string.argtypes = [i32]
         L.gemm_status_string.restype = ctypes.c_char_p
         L.gemm_last_hip_error.argtypes = []
+        sz = ctypes.c_size_t
+        L.ozaki_plan.argtypes = [i64, i64, i64, i32, i32, i32, pp]
+        L.ozaki_plan_info.argtypes = [vp, ctypes.POINTER(OzakiPlanInfo)]
+        L.ozaki_workspace_size.argtypes = [vp]
+        L.ozaki_workspace_size.restype = sz
+        L.ozaki_split.argtypes = [vp, i32, vp, vp, sz, vp]
+        L.ozaki_multiply.argtypes = [vp, vp, sz, vp, vp]
+        L.ozaki_run.argtypes = [vp, vp, vp, vp, vp, sz, vp]
+        L.ozaki_plan_destroy.argtypes = [vp]
+        L.ozaki_plan_destroy.restype = None
         for f in ("gemm_plan", "gemm_plan_ex", "gemm_plan_ex2", "gemm_plan_info",
                   "gemm_plan_tile_of", "gemm_run", "gemm_run_bias", "gemm_splitk_run",
-                  "gemm_splitk_run_bias", "gemm_last_hip_error"):
+                  "gemm_splitk_run_bias", "gemm_last_hip_error", "ozaki_plan", "ozaki_plan_info",
+                  "ozaki_split", "ozaki_multiply", "ozaki_run"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -284,4 +315,99 @@ def mm(A, B, out_dtype=None, split_k=None, plan: Plan | None = None, stream=None
         ws = torch.empty(max(1, gemm_workspace_size(plan) // 4), dtype=torch.float32,
                          device=A.device)
         gemm_splitk_run(plan, A, B, C, ws, stream)
+    return C
+
+
+# ---- Ozaki-scheme fp64 product ------------------------------------------------
+
+class OzakiPlan:
+    """Owns an ozaki_plan_t; destroyed with the object."""
+
+    def __init__(self, handle: int):
+        self.handle = handle
+        self._lib = lib()
+
+    def __del__(self):
+        h, self.handle = getattr(self, "handle", None), None
+        if h:
+            self._lib.ozaki_plan_destroy(h)
+
+    @property
+    def info(self) -> dict:
+        return ozaki_plan_info(self)
+
+
+def ozaki_plan(M: int, N: int, K: int, type2="bf16", slices: int = 0, d: int = 0) -> OzakiPlan:
+    """Plan C = A @ B in fp64 by the Ozaki scheme with Type2 slices ("bf16" or
+    "e4m3"); slices / d = 0 take the library's defaults."""
+    h = ctypes.c_void_p()
+    _check(lib().ozaki_plan(M, N, K, _dtype_code(type2), int(slices), int(d), ctypes.byref(h)),
+           "ozaki_plan")
+    return OzakiPlan(h.value)
+
+
+def ozaki_plan_info(plan: OzakiPlan) -> dict:
+    info = OzakiPlanInfo()
+    _check(lib().ozaki_plan_info(plan.handle, ctypes.byref(info)), "ozaki_plan_info")
+    return info.as_dict()
+
+
+def ozaki_workspace_size(plan: OzakiPlan) -> int:
+    return int(lib().ozaki_workspace_size(plan.handle))
+
+
+def _ws_bytes(workspace, workspace_bytes):
+    if workspace_bytes is not None:
+        return int(workspace_bytes)
+    if workspace is None or isinstance(workspace, int):
+        return 0
+    return workspace.numel() * workspace.element_size()
+
+
+def _check_f64(t, name, numel):
+    if t is None or isinstance(t, int):
+        return
+    import torch
+    if t.dtype != torch.float64 or not t.is_contiguous() or t.numel() != numel:
+        raise ValueError(f"{name} must be a contiguous float64 tensor of {numel} elements")
+
+
+def ozaki_split(plan: OzakiPlan, operand: int, x, workspace, stream=None,
+                workspace_bytes=None) -> None:
+    """Slices and exponents of A (operand 0, [M, K]) or B (1, [K, N]) into the workspace."""
+    i = ozaki_plan_info(plan)
+    _check_f64(x, "x", i["M"] * i["K"] if operand == 0 else i["K"] * i["N"])
+    _check(lib().ozaki_split(plan.handle, int(operand), _addr(x), _addr(workspace),
+                             _ws_bytes(workspace, workspace_bytes), _stream(stream, x, workspace)),
+           "ozaki_split")
+
+
+def ozaki_multiply(plan: OzakiPlan, workspace, C, stream=None, workspace_bytes=None) -> None:
+    """The slice-pair product from a workspace filled by ozaki_split of A and B."""
+    i = ozaki_plan_info(plan)
+    _check_f64(C, "C", i["M"] * i["N"])
+    _check(lib().ozaki_multiply(plan.handle, _addr(workspace), _ws_bytes(workspace, workspace_bytes),
+                                _addr(C), _stream(stream, C, workspace)), "ozaki_multiply")
+
+
+def ozaki_run(plan: OzakiPlan, A, B, C, workspace, stream=None, workspace_bytes=None) -> None:
+    """C = A @ B (fp64) by the Ozaki scheme: split A, split B, multiply."""
+    i = ozaki_plan_info(plan)
+    _check_f64(A, "A", i["M"] * i["K"])
+    _check_f64(B, "B", i["K"] * i["N"])
+    _check_f64(C, "C", i["M"] * i["N"])
+    _check(lib().ozaki_run(plan.handle, _addr(A), _addr(B), _addr(C), _addr(workspace),
+                           _ws_bytes(workspace, workspace_bytes), _stream(stream, A, B, C)),
+           "ozaki_run")
+
+
+def ozaki_mm(A, B, type2="bf16", slices: int = 0, d: int = 0, stream=None):
+    """C = A @ B for fp64 CUDA tensors, allocating C and the workspace with torch."""
+    import torch
+    M, K = A.shape
+    N = B.shape[1]
+    plan = ozaki_plan(M, N, K, type2, slices, d)
+    ws = torch.empty(max(1, ozaki_workspace_size(plan)), dtype=torch.uint8, device=A.device)
+    C = torch.empty((M, N), dtype=torch.float64, device=A.device)
+    ozaki_run(plan, A.contiguous(), B.contiguous(), C, ws, stream)
     return C

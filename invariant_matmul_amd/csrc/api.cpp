@@ -170,7 +170,35 @@ GemmArgs make_args(const gemm_plan_s* p, const void* A, const void* B, void* out
   return a;
 }
 
+// ---- Ozaki scheme ----------------------------------------------------------
+
+constexpr int kOzMaxSlices = 20;  // as many as the page's split routine makes at most
+constexpr int64_t kOzColChunk = 256;  // rows per partial column maximum of B
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+bool aligned8(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 7u) == 0; }
+
+// Largest b with K * 4^b <= 2^24: the bits per slice for which a K-term fp32
+// sum of slice products is exact (gamma = 53 - b_max of the Insight Edge
+// blog's "分解(Split)" formula gamma = ceil(53 - (24 - log2 k) / 2)).
+int oz_exact_bits(int64_t K) {
+  const int64_t k = K > 0 ? K : 1;
+  int b = 0;
+  while (b < 12 && k * ((int64_t)1 << (2 * (b + 1))) <= ((int64_t)1 << 24)) ++b;
+  return b;
+}
+
 }  // namespace
+
+struct ozaki_plan_s {
+  int64_t M, N, K;
+  int type2, eb;
+  int rho, b, delta, slices, d, npairs;
+  int64_t kp, np;
+  int64_t tiles_m, tiles_n, grid;
+  int64_t col_chunks;
+  size_t off_sa, off_sb, off_ea, off_eb, off_part, ws_bytes;
+};
 
 extern "C" {
 
@@ -358,6 +386,189 @@ gemm_status gemm_splitk_run_bias(gemm_plan_t p, const void* A, const void* B, co
 }
 
 void gemm_plan_destroy(gemm_plan_t p) { delete p; }
+
+gemm_status ozaki_plan(int64_t M, int64_t N, int64_t K, gemm_dtype type2, int slices, int d,
+                       ozaki_plan_t* plan) {
+  if (!plan) return GEMM_ERR_INVALID_VALUE;
+  *plan = nullptr;
+  if (M < 0 || N < 0 || K < 0) return GEMM_ERR_INVALID_VALUE;
+  if (type2 != GEMM_BF16 && type2 != GEMM_F8_E4M3) return GEMM_ERR_UNSUPPORTED;
+  if (slices < 0 || slices > kOzMaxSlices || d < 0) return GEMM_ERR_UNSUPPORTED;
+  if (M > INT_MAX || K > ((int64_t)1 << 22) || N >= ((int64_t)1 << 23)) return GEMM_ERR_UNSUPPORTED;
+  // rho = max(gamma, xi): b = min(exact bits for K, significand bits of Type2)
+  const int m_type2 = type2 == GEMM_BF16 ? 8 : 4;
+  const int bx = oz_exact_bits(K);
+  const int b = bx < m_type2 ? bx : m_type2;
+  if (b < 1) return GEMM_ERR_UNSUPPORTED;
+  ozaki_plan_s* p = new (std::nothrow) ozaki_plan_s();
+  if (!p) return GEMM_ERR_INVALID_VALUE;
+  p->M = M;
+  p->N = N;
+  p->K = K;
+  p->type2 = type2;
+  p->eb = type2 == GEMM_BF16 ? 2 : 1;
+  p->b = b;
+  p->rho = 53 - b;
+  p->delta = b + 1;
+  p->slices = slices ? slices : (53 + b - 1) / b;
+  if (p->slices > kOzMaxSlices) p->slices = kOzMaxSlices;
+  p->d = d ? d : p->slices + 2;
+  int n = 0;
+  for (int i = 0; i < p->slices; ++i) {
+    const int c = p->d - i < p->slices ? p->d - i : p->slices;
+    if (c > 0) n += c;
+  }
+  p->npairs = n;
+  // slices padded so every row starts on 16 bytes (and fp8 rows on 16 elements)
+  p->kp = (K + 15) / 16 * 16;
+  p->np = (N + 15) / 16 * 16;
+  p->tiles_m = ceil_div(M, oz_tile_m(type2));
+  p->tiles_n = ceil_div(p->np, kOzTileN);
+  p->grid = p->tiles_m * p->tiles_n;
+  p->col_chunks = ceil_div(K, kOzColChunk);
+  const size_t sa = (size_t)p->slices * M * p->kp * p->eb;
+  const size_t sb = (size_t)p->slices * p->kp * p->np * p->eb;
+  p->off_sa = 0;
+  p->off_sb = align256(sa);
+  p->off_ea = p->off_sb + align256(sb);
+  p->off_eb = p->off_ea + align256((size_t)M * 4);
+  p->off_part = p->off_eb + align256((size_t)p->np * 4);
+  p->ws_bytes = p->off_part + align256((size_t)p->col_chunks * N * 8);
+  // DMA offsets of one 128-row A tile and one stage of B stay below 2^31
+  if (oz_tile_m(type2) * p->kp * p->eb >= ((int64_t)1 << 31) - 256 ||
+      p->grid * 512 >= ((int64_t)1 << 32)) {
+    delete p;
+    return GEMM_ERR_UNSUPPORTED;
+  }
+  *plan = p;
+  return GEMM_OK;
+}
+
+gemm_status ozaki_plan_info(ozaki_plan_t p, ozaki_plan_info_t* info) {
+  if (!p || !info) return GEMM_ERR_INVALID_VALUE;
+  std::memset(info, 0, sizeof(*info));
+  info->M = p->M;
+  info->N = p->N;
+  info->K = p->K;
+  info->type2 = p->type2;
+  info->rho = p->rho;
+  info->bits = p->b;
+  info->delta = p->delta;
+  info->slices = p->slices;
+  info->d = p->d;
+  info->pairs = p->npairs;
+  info->tile_m = oz_tile_m(p->type2);
+  info->tile_n = kOzTileN;
+  info->k_pad = p->kp;
+  info->n_pad = p->np;
+  info->grid = p->grid;
+  info->workspace_bytes = p->ws_bytes;
+  info->a_slices_offset = p->off_sa;
+  info->b_slices_offset = p->off_sb;
+  info->a_exp_offset = p->off_ea;
+  info->b_exp_offset = p->off_eb;
+  info->scratch_offset = p->off_part;
+  return GEMM_OK;
+}
+
+size_t ozaki_workspace_size(ozaki_plan_t p) { return p ? p->ws_bytes : 0; }
+
+namespace {
+
+gemm_status oz_check_ws(ozaki_plan_t p, const void* ws, size_t bytes) {
+  if (!ws || bytes < p->ws_bytes) return GEMM_ERR_WORKSPACE;
+  if (!aligned16(ws)) return GEMM_ERR_INVALID_VALUE;
+  return GEMM_OK;
+}
+
+gemm_status oz_split(ozaki_plan_t p, int operand, const double* x, void* ws, hipStream_t s) {
+  char* w = static_cast<char*>(ws);
+  hipError_t e;
+  if (operand == 0) {
+    int32_t* ea = reinterpret_cast<int32_t*>(w + p->off_ea);
+    e = launch_oz_row_exp(x, p->M, p->K, ea, s);
+    if (e == hipSuccess)
+      e = launch_oz_split(p->type2, true, x, p->M, p->K, p->M, p->kp, ea, p->slices, p->rho,
+                          p->delta, w + p->off_sa, s);
+  } else {
+    int32_t* eb = reinterpret_cast<int32_t*>(w + p->off_eb);
+    e = launch_oz_col_exp(x, p->K, p->N, kOzColChunk, reinterpret_cast<double*>(w + p->off_part),
+                          eb, s);
+    if (e == hipSuccess)
+      e = launch_oz_split(p->type2, false, x, p->K, p->N, p->kp, p->np, eb, p->slices, p->rho,
+                          p->delta, w + p->off_sb, s);
+  }
+  return e == hipSuccess ? GEMM_OK : hip_fail(e);
+}
+
+}  // namespace
+
+gemm_status ozaki_split(ozaki_plan_t p, int operand, const double* x, void* ws, size_t bytes,
+                        void* stream) {
+  if (!p || (operand != 0 && operand != 1)) return GEMM_ERR_INVALID_VALUE;
+  const int64_t n = operand == 0 ? p->M * p->K : p->K * p->N;
+  if (n > 0 && (!x || !aligned8(x))) return GEMM_ERR_INVALID_VALUE;
+  gemm_status st = oz_check_ws(p, ws, bytes);
+  if (st != GEMM_OK) return st;
+  hipError_t e = device_ready();
+  if (e != hipSuccess) return hip_fail(e);
+  return oz_split(p, operand, x, ws, static_cast<hipStream_t>(stream));
+}
+
+gemm_status ozaki_multiply(ozaki_plan_t p, const void* ws, size_t bytes, double* C, void* stream) {
+  if (!p) return GEMM_ERR_INVALID_VALUE;
+  if (p->M == 0 || p->N == 0) return GEMM_OK;
+  if (!C || !aligned8(C)) return GEMM_ERR_INVALID_VALUE;
+  gemm_status st = oz_check_ws(p, ws, bytes);
+  if (st != GEMM_OK) return st;
+  hipError_t e = device_ready();
+  if (e != hipSuccess) return hip_fail(e);
+  const char* w = static_cast<const char*>(ws);
+  OzGemmArgs a;
+  a.A = w + p->off_sa;
+  a.B = w + p->off_sb;
+  a.C = C;
+  a.bias = nullptr;
+  a.M = p->M;
+  a.N = p->np;
+  a.K = p->kp;
+  a.k_per_split = p->kp;
+  a.tiles_m = p->tiles_m;
+  a.tiles_n = p->tiles_n;
+  a.grid = p->grid;
+  a.group_m = 8;
+  a.scale = 1.0f;
+  a.slice_a = p->M * p->kp * p->eb;
+  a.slice_b = p->kp * p->np * p->eb;
+  a.n_out = p->N;
+  a.ldc = p->N;
+  a.ea = reinterpret_cast<const int32_t*>(w + p->off_ea);
+  a.eb = reinterpret_cast<const int32_t*>(w + p->off_eb);
+  a.slices = p->slices;
+  a.d = p->d;
+  a.npairs = p->npairs;
+  a.delta = p->delta;
+  e = launch_ozaki_gemm(p->type2, a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? GEMM_OK : hip_fail(e);
+}
+
+gemm_status ozaki_run(ozaki_plan_t p, const double* A, const double* B, double* C, void* ws,
+                      size_t bytes, void* stream) {
+  if (!p) return GEMM_ERR_INVALID_VALUE;
+  if (p->M == 0 || p->N == 0) return GEMM_OK;
+  if (!C || !aligned8(C)) return GEMM_ERR_INVALID_VALUE;
+  if (p->K > 0 && (!A || !B || !aligned8(A) || !aligned8(B))) return GEMM_ERR_INVALID_VALUE;
+  gemm_status st = oz_check_ws(p, ws, bytes);
+  if (st != GEMM_OK) return st;
+  hipError_t e = device_ready();
+  if (e != hipSuccess) return hip_fail(e);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if ((st = oz_split(p, 0, A, ws, s)) != GEMM_OK) return st;
+  if ((st = oz_split(p, 1, B, ws, s)) != GEMM_OK) return st;
+  return ozaki_multiply(p, ws, bytes, C, stream);
+}
+
+void ozaki_plan_destroy(ozaki_plan_t p) { delete p; }
 
 const char* gemm_status_string(gemm_status s) {
   switch (s) {

@@ -50,6 +50,32 @@ namespace {
 using namespace dev;
 
 constexpr int TBN = 256;  // tile columns (every configuration)
+
+// What a workgroup does with its tile.
+//   MODE_STORE: the product, scaled, converted, stored to C.
+//   MODE_SLICE: the raw fp32 sum of one K slice, stored to the workspace.
+//   MODE_OZAKI: the Ozaki-scheme product (Insight Edge cuTile blog, "行列積の
+//     計算" and its fused kernel listing): for every slice pair (p, q) of the
+//     pair list, the full K loop over slice p of A and slice q of B into the
+//     fp32 accumulators, which are then scaled by 2^-(p+q)*delta and added
+//     to an fp64 accumulator; at the end the row and column exponents are
+//     applied and fp64 C is stored.  The LDS ring runs on across pair
+//     boundaries (the stage sequence is pair-major).
+enum { MODE_STORE = 0, MODE_SLICE = 1, MODE_OZAKI = 2 };
+
+// Slice pair P of the Ozaki pair list -> (p, q): p ascending, then q
+// ascending, with q < min(s, d - p) (Fast Mode skips p + q >= d).
+__device__ __forceinline__ void oz_pair(int P, int s, int d, int* p, int* q) {
+  int pp = 0;
+  for (; pp < s; ++pp) {
+    const int n = max(0, min(s, d - pp));
+    if (P < n) break;
+    P -= n;
+  }
+  *p = pp;
+  *q = P;
+}
+
 constexpr int SKB = 128;  // bytes of K per row per stage
 constexpr unsigned OOB = 0x80000000u;
 constexpr int NREC = 0x7fffffff;
@@ -97,9 +123,9 @@ __device__ __forceinline__ i32x2 tr8_rows(unsigned p0, int rows) {
 //   shapes (wave tile 64 x 64 / 32 x 64), where the time is the stream of B.
 // Two workgroups share a CU when their rings fit in half the LDS; the
 // register budget then has to allow two waves per SIMD.
-template <int TBM, int NS>
+template <int TBM, int WM, int NS>
 constexpr int waves_per_simd() {
-  return NS * (TBM + TBN) * SKB <= 80 * 1024 || TBM == 256 ? 2 : 1;
+  return NS * (TBM + TBN) * SKB <= 80 * 1024 || WM == 2 ? 2 : 1;
 }
 
 // BT: B is given transposed, as [N, K] row-major (the weight layout of a
@@ -107,8 +133,8 @@ constexpr int waves_per_simd() {
 // staged and read exactly like A (128-byte rows, ds_read_b128); the matrix
 // core sees the same values in the same K order, so the bits are those of
 // the [K, N] layout.
-template <int IN, int OUT, bool SLICE, int TBM, int WM, int NS, bool BT>
-__global__ __launch_bounds__(256 * WM, (waves_per_simd<TBM, NS>())) void gemm_dma_kernel(GemmArgs g) {
+template <int IN, int OUT, int MODE, int TBM, int WM, int NS, bool BT, class ARGS>
+__global__ __launch_bounds__(256 * WM, (waves_per_simd<TBM, WM, NS>())) void gemm_dma_kernel(ARGS g) {
   using T = InT<IN>;
   constexpr int EB = T::EB;
   constexpr int WN = 4;
@@ -155,7 +181,10 @@ __global__ __launch_bounds__(256 * WM, (waves_per_simd<TBM, NS>())) void gemm_dm
   const int64_t m0 = pm * TBM, n0 = pn * TBN;
   const int64_t kbeg = ksl * g.k_per_split;
   const int64_t kend = (g.K < kbeg + g.k_per_split) ? g.K : kbeg + g.k_per_split;
-  const int nt = kend > kbeg ? (int)((kend - kbeg + BKE - 1) / BKE) : 0;
+  // stages of one K pass; the Ozaki mode makes one pass per slice pair
+  const int ntp = kend > kbeg ? (int)((kend - kbeg + BKE - 1) / BKE) : 0;
+  int nt = ntp;
+  if constexpr (MODE == MODE_OZAKI) nt = ntp * g.npairs;
   const char* A = static_cast<const char*>(g.A);
   const char* B = static_cast<const char*>(g.B);
 
@@ -200,10 +229,26 @@ __global__ __launch_bounds__(256 * WM, (waves_per_simd<TBM, NS>())) void gemm_dm
   };
   auto stage_src = [&](int t) {
     StageSrc q;
-    const int64_t kst = kbeg + (int64_t)t * BKE;
-    q.pa = A + (m0 * g.K + kst) * EB;
-    q.pb = BT ? B + (n0 * g.K + kst) * EB : B + (kst * g.N + n0) * EB;
-    q.rem = kend - kst < BKE ? (int)(kend - kst) : BKE;
+    if constexpr (MODE == MODE_OZAKI) {
+      // stage t is stage kt of slice pair P; past the last pair: zero fill
+      const int P = t / ntp, kt = t - P * ntp;
+      q.pa = A;
+      q.pb = B;
+      q.rem = 0;
+      if (P < g.npairs) {
+        int sp, sq;
+        oz_pair(P, g.slices, g.d, &sp, &sq);
+        const int64_t kst = (int64_t)kt * BKE;
+        q.pa = A + sp * g.slice_a + (m0 * g.K + kst) * EB;
+        q.pb = B + sq * g.slice_b + (kst * g.N + n0) * EB;
+        q.rem = g.K - kst < BKE ? (int)(g.K - kst) : BKE;
+      }
+    } else {
+      const int64_t kst = kbeg + (int64_t)t * BKE;
+      q.pa = A + (m0 * g.K + kst) * EB;
+      q.pb = BT ? B + (n0 * g.K + kst) * EB : B + (kst * g.N + n0) * EB;
+      q.rem = kend - kst < BKE ? (int)(kend - kst) : BKE;
+    }
     return q;
   };
   // DMA instruction x of this wave for stage t (source q): x < DA: A rows,
@@ -324,6 +369,33 @@ __global__ __launch_bounds__(256 * WM, (waves_per_simd<TBM, NS>())) void gemm_dm
   auto mfma_x = [&](const Frag<IN, FM, FN>& F, int x) {
     acc[x / FN][x % FN] = mfma_v<IN>(F.a[x / FN], F.b[x % FN], acc[x / FN][x % FN]);
   };
+  // Ozaki mode: fp64 sum over the slice pairs (dead code otherwise).
+  double acc64[FM][FN][16];
+  if constexpr (MODE == MODE_OZAKI) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc64[i][j][r] = 0.0;
+  }
+  // End of slice pair P: its exact fp32 sums, scaled by 2^-(p+q)*delta, join
+  // the fp64 sum in pair order; the fp32 accumulators restart from +0.
+  auto oz_flush = [&](int P) {
+    if constexpr (MODE == MODE_OZAKI) {
+      int sp, sq;
+      oz_pair(P, g.slices, g.d, &sp, &sq);
+      const int sh = -(sp + sq) * g.delta;
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc64[i][j][r] += ldexp((double)acc[i][j][r], sh);
+          acc[i][j] = f32x16{};
+        }
+    }
+  };
 
   // Issue order.  Stages are requested whole (A rows, then B rows) in
   // ascending stage index: the prologue requests stages 0 .. NS-1, every
@@ -394,6 +466,9 @@ __global__ __launch_bounds__(256 * WM, (waves_per_simd<TBM, NS>())) void gemm_dm
     lds_wait();  // last k-step's fragments landed: this wave has read all of stage t
     stage_change();
     kstep(true, F1, t, F0, t + 1, 0);
+    if constexpr (MODE == MODE_OZAKI) {
+      if ((t + 1) % ntp == 0) oz_flush(t / ntp);
+    }
   }
   // No LDS transfer or read may still be in flight when the workgroup ends.
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
@@ -409,9 +484,16 @@ __global__ __launch_bounds__(256 * WM, (waves_per_simd<TBM, NS>())) void gemm_dm
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int64_t row = m0 + wm * WTM + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-        if (row < g.M && col < g.N) {
+        if constexpr (MODE == MODE_OZAKI) {
+          // C = 2^(ea[row] + eb[col]) * sum: the same bits as scaling every
+          // pair's term by its full exponent while no value leaves fp64's
+          // normal range
+          if (row < g.M && col < g.n_out)
+            static_cast<double*>(g.C)[row * g.ldc + col] =
+                ldexp(acc64[i][j][r], g.ea[row] + g.eb[col]);
+        } else if (row < g.M && col < g.N) {
           const float v = acc[i][j][r];
-          if constexpr (SLICE) {
+          if constexpr (MODE == MODE_SLICE) {
             static_cast<float*>(g.C)[(ksl * g.M + row) * g.N + col] = v;
           } else {
             store_final<OUT>(g.C, row * g.N + col, v, g.scale, g.bias, col);
@@ -426,13 +508,17 @@ template <int IN, int TBM, int WM, int NS, bool BT>
 hipError_t launch_cfg(const gemm_plan_s& p, const GemmArgs& a, bool slice, hipStream_t s) {
   const dim3 grid((unsigned)a.grid), block(256 * WM);
   if (slice)
-    hipLaunchKernelGGL((gemm_dma_kernel<IN, GEMM_F32, true, TBM, WM, NS, BT>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((gemm_dma_kernel<IN, GEMM_F32, MODE_SLICE, TBM, WM, NS, BT, GemmArgs>), grid,
+                       block, 0, s, a);
   else if (p.out == GEMM_F32)
-    hipLaunchKernelGGL((gemm_dma_kernel<IN, GEMM_F32, false, TBM, WM, NS, BT>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((gemm_dma_kernel<IN, GEMM_F32, MODE_STORE, TBM, WM, NS, BT, GemmArgs>), grid,
+                       block, 0, s, a);
   else if (p.out == GEMM_F16)
-    hipLaunchKernelGGL((gemm_dma_kernel<IN, GEMM_F16, false, TBM, WM, NS, BT>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((gemm_dma_kernel<IN, GEMM_F16, MODE_STORE, TBM, WM, NS, BT, GemmArgs>), grid,
+                       block, 0, s, a);
   else
-    hipLaunchKernelGGL((gemm_dma_kernel<IN, GEMM_BF16, false, TBM, WM, NS, BT>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((gemm_dma_kernel<IN, GEMM_BF16, MODE_STORE, TBM, WM, NS, BT, GemmArgs>), grid,
+                       block, 0, s, a);
   return hipGetLastError();
 }
 
@@ -453,6 +539,25 @@ hipError_t launch_in(const gemm_plan_s& p, int tile, const GemmArgs& a, bool sli
 }
 
 }  // namespace
+
+hipError_t launch_ozaki_gemm(int type2, const OzGemmArgs& a, hipStream_t s) {
+  static_assert(kOzTileN == TBN, "Ozaki tile");
+  // The fp64 sums (two registers per element) must sit in architectural
+  // VGPRs, at most 256 per wave.  bf16: a 128 x 256 tile of 8 waves (two per
+  // SIMD) of 64 x 64, 253 VGPRs.  fp8 fragments are twice as wide and spill
+  // there, so e4m3 runs a 64 x 256 tile of 4 waves (one per SIMD) of 64 x 64,
+  // with its fp32 accumulators in AGPRs and a 3-stage ring.
+  const dim3 grid((unsigned)a.grid);
+  if (type2 == GEMM_BF16)
+    hipLaunchKernelGGL((gemm_dma_kernel<GEMM_BF16, GEMM_F32, MODE_OZAKI, 128, 2, 2, false,
+                                        OzGemmArgs>), grid, dim3(512), 0, s, a);
+  else if (type2 == GEMM_F8_E4M3)
+    hipLaunchKernelGGL((gemm_dma_kernel<GEMM_F8_E4M3, GEMM_F32, MODE_OZAKI, 64, 1, 3, false,
+                                        OzGemmArgs>), grid, dim3(256), 0, s, a);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
 
 hipError_t launch_gemm_dma(const gemm_plan_s& p, int tile, const GemmArgs& a, bool slice_mode,
                            hipStream_t s) {

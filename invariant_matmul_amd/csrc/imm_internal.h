@@ -99,6 +99,19 @@ struct GemmArgs {
   float scale;
 };
 
+// Arguments of the Ozaki-scheme slice-pair product (the DMA kernel in its
+// slice-pair mode).  A and B point at the first slice of each operand; slice
+// p of A starts slice_a bytes after slice p-1 (likewise B).  K and N are the
+// slices' padded sizes (their leading dimensions); n_out and ldc describe the
+// fp64 output.
+struct OzGemmArgs : GemmArgs {
+  int64_t slice_a, slice_b;
+  int64_t n_out, ldc;
+  const int32_t* ea;    // exponent of each row of A (M values)
+  const int32_t* eb;    // exponent of each column of B (n_out values)
+  int32_t slices, d, npairs, delta;
+};
+
 struct ReduceArgs {
   const float* ws;
   void* C;
@@ -118,5 +131,21 @@ hipError_t launch_reduce(const gemm_plan_s& p, const ReduceArgs& a, hipStream_t 
 // The DMA-fed kernels (gemm_dma.hip); launch_gemm forwards the DMA tiles to it.
 hipError_t launch_gemm_dma(const gemm_plan_s& p, int tile, const GemmArgs& a, bool slice_mode,
                            hipStream_t s);
+// The Ozaki slice-pair product on the DMA kernel (gemm_dma.hip); type2 is
+// GEMM_BF16 or GEMM_F8_E4M3.  Output tile oz_tile_m(type2) x 256.
+constexpr int kOzTileN = 256;
+inline int oz_tile_m(int type2) { return type2 == GEMM_BF16 ? 128 : 64; }
+hipError_t launch_ozaki_gemm(int type2, const OzGemmArgs& a, hipStream_t s);
+// The Ozaki split (ozaki.hip): exponents of the rows of x [R, C] ...
+hipError_t launch_oz_row_exp(const double* x, int64_t R, int64_t C, int32_t* e, hipStream_t s);
+// ... of its columns (maxima over chunks of rc rows into part [ceil(R/rc), C],
+// then combined) ...
+hipError_t launch_oz_col_exp(const double* x, int64_t R, int64_t C, int64_t rc, double* part,
+                             int32_t* e, hipStream_t s);
+// ... and the slices [slices, Ro, Co] of x with one exponent per row
+// (per_row) or per column.
+hipError_t launch_oz_split(int type2, bool per_row, const double* x, int64_t R, int64_t C,
+                           int64_t Ro, int64_t Co, const int32_t* e, int slices, int rho, int delta,
+                           void* out, hipStream_t s);
 
 }  // namespace imm

@@ -45,7 +45,8 @@ Readings where the page is open (each listed in the design notes):
     One exponent per row of A makes row i of C depend on row i of A only,
     the batch-invariance the rest of this library is built on.
   * default slice count s = ceil(53 / b), the page's "ceil(m_Type1 / m_Type2)"
-    with m_Type2 replaced by the bits a slice actually carries; default
+    with m_Type2 replaced by the bits a slice actually carries, at most 20
+    (the limit of the page's split routine); default
     d = s + 2, which reproduces the page's tables (7 bf16 slices with d = 9
     giving 39 products; 14 e4m3 slices with d = 16 giving 130).
 
@@ -65,6 +66,7 @@ from . import decode, round_rne
 TYPE2_BITS = {"bf16": 8, "e4m3": 4}   # significand bits, hidden bit included
 M_TYPE1 = 53
 M_TYPE3 = 24
+MAX_SLICES = 20   # the page's split routine stops after at most 20 slices
 
 
 @dataclass(frozen=True)
@@ -102,7 +104,7 @@ def params(K: int, type2: str = "bf16", s: int = 0, d: int = 0) -> OzakiParams:
     b = M_TYPE1 - rho
     if b < 1:
         raise ValueError(f"K = {K} leaves no bits per slice")
-    s = s or -(-M_TYPE1 // b)
+    s = s or min(-(-M_TYPE1 // b), MAX_SLICES)
     d = d or s + 2
     return OzakiParams(type2, int(K), rho, b, b + 1, int(s), int(d))
 

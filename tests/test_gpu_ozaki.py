@@ -1,0 +1,179 @@
+"""GPU parity of the Ozaki-scheme fp64 product against the CPU oracle.
+
+Source: Insight Edge blog on cuTile Python, section "倍精度行列積エミュレーション"
+(split equations (1)-(5), product equations (10)-(11), Fast Mode, the fused
+split kernel).  Every slice product is exact (rho from the inner dimension),
+so the library and oracle/ozaki.py must agree BIT FOR BIT: the slices, the
+exponents and the fp64 result.  Shapes span several output tiles with ragged
+edges in M, N and K; the bench-size cases compare sampled elements, which
+the oracle computes one by one from their own row and column.
+"""
+import numpy as np
+import pytest
+import torch
+
+import invariant_matmul_amd as imm
+import workloads as wl
+from oracle import ozaki as OZ
+from tests.helpers import dev, log
+
+pytestmark = pytest.mark.gpu
+
+T2_VIEW = {"bf16": (torch.int16, np.uint16), "e4m3": (torch.uint8, np.uint8)}
+
+
+def _inputs(M, N, K, kind, seed):
+    g = wl.gen(seed)
+    if kind == "uniform":
+        return wl.uniform64((M, K), g), wl.uniform64((K, N), g)
+    if kind == "wide":
+        return wl.wide64((M, K), g), wl.wide64((K, N), g)
+    if kind == "int":
+        A = torch.randint(-2 ** 20, 2 ** 20, (M, K), generator=g, dtype=torch.int64)
+        B = torch.randint(-2 ** 20, 2 ** 20, (K, N), generator=g, dtype=torch.int64)
+        return A.to(torch.float64), B.to(torch.float64)
+    raise ValueError(kind)
+
+
+def _run(plan, A, B):
+    i = plan.info
+    ws = torch.empty(max(1, imm.ozaki_workspace_size(plan)), dtype=torch.uint8, device=dev())
+    C = torch.empty((i["M"], i["N"]), dtype=torch.float64, device=dev())
+    imm.ozaki_run(plan, A, B, C, ws)
+    torch.cuda.synchronize()
+    return C, ws
+
+
+def _bits64(x) -> np.ndarray:
+    a = x.cpu().numpy() if isinstance(x, torch.Tensor) else np.asarray(x)
+    return np.ascontiguousarray(a, dtype=np.float64).view(np.uint64)
+
+
+def _slices(ws, off, shape, t2):
+    eb = 2 if t2 == "bf16" else 1
+    n = int(np.prod(shape))
+    raw = ws[off:off + n * eb].cpu().numpy()
+    return raw.view(T2_VIEW[t2][1]).reshape(shape)
+
+
+@pytest.mark.parametrize("t2", ["bf16", "e4m3"])
+def test_split_matches_oracle(t2):
+    M, N, K = 70, 90, 150          # ragged: K and N padded to 16
+    A, B = _inputs(M, N, K, "wide", 7100)
+    plan = imm.ozaki_plan(M, N, K, t2)
+    i = plan.info
+    P = OZ.params(K, t2)
+    C, ws = _run(plan, A.to(dev()), B.to(dev()))
+    sa, ca = OZ.split(A.numpy(), 1, P)
+    sb, cb = OZ.split(B.numpy(), 0, P)
+    kp, np_ = i["k_pad"], i["n_pad"]
+    ga = _slices(ws, i["a_slices_offset"], (P.s, M, kp), t2)
+    gb = _slices(ws, i["b_slices_offset"], (P.s, kp, np_), t2)
+    assert np.array_equal(ga[:, :, :K], sa) and not ga[:, :, K:].any()
+    assert np.array_equal(gb[:, :K, :N], sb) and not gb[:, K:, :].any() and not gb[:, :, N:].any()
+    ea = ws[i["a_exp_offset"]:i["a_exp_offset"] + 4 * M].cpu().numpy().view(np.int32)
+    eb = ws[i["b_exp_offset"]:i["b_exp_offset"] + 4 * N].cpu().numpy().view(np.int32)
+    assert np.array_equal(ea, ca) and np.array_equal(eb, cb)
+
+
+CASES = [
+    # (type2, M, N, K, kind, slices, d)
+    ("bf16", 300, 600, 1000, "uniform", 0, 0),
+    ("e4m3", 300, 600, 1000, "uniform", 0, 0),
+    ("bf16", 129, 257, 200, "wide", 0, 0),
+    ("e4m3", 65, 520, 333, "wide", 0, 0),
+    ("bf16", 200, 300, 256, "int", 0, 0),
+    ("e4m3", 100, 100, 64, "int", 0, 0),
+    ("bf16", 130, 270, 500, "uniform", 4, 3),
+    ("e4m3", 70, 300, 260, "uniform", 5, 99),
+    ("bf16", 1, 16, 4096, "uniform", 0, 0),
+    ("e4m3", 2, 1, 1, "wide", 0, 0),
+]
+
+
+@pytest.mark.parametrize("t2,M,N,K,kind,s,d", CASES,
+                         ids=[f"{c[0]}-{c[1]}x{c[2]}x{c[3]}-{c[4]}-s{c[5]}d{c[6]}" for c in CASES])
+def test_product_bit_exact(t2, M, N, K, kind, s, d):
+    A, B = _inputs(M, N, K, kind, 7200 + M + N + K)
+    plan = imm.ozaki_plan(M, N, K, t2, s, d)
+    log(f"ozaki {t2} {M}x{N}x{K} {kind}: {plan.info['slices']} slices, {plan.info['pairs']} pairs")
+    C, _ = _run(plan, A.to(dev()), B.to(dev()))
+    want = OZ.gemm(A.numpy(), B.numpy(), t2, s, d)
+    got = _bits64(C)
+    bad = got != _bits64(want)
+    assert not bad.any(), (f"{int(bad.sum())} of {bad.size} differ; first {np.argwhere(bad)[:3]}")
+    if kind == "int":
+        assert np.array_equal(C.cpu().numpy(), (A @ B).numpy())
+
+
+@pytest.mark.parametrize("t2", ["bf16", "e4m3"])
+def test_rows_invariant_and_repeatable(t2):
+    M, N, K = 257, 300, 700
+    A, B = _inputs(M, N, K, "wide", 7300)
+    Ad, Bd = A.to(dev()), B.to(dev())
+    full, _ = _run(imm.ozaki_plan(M, N, K, t2), Ad, Bd)
+    full = _bits64(full)
+    for m in (1, 7, 64, 129):
+        part, _ = _run(imm.ozaki_plan(m, N, K, t2), Ad[:m].contiguous(), Bd)
+        assert np.array_equal(_bits64(part), full[:m]), m
+    perm = torch.randperm(M, generator=wl.gen(7301))
+    pc, _ = _run(imm.ozaki_plan(M, N, K, t2), Ad[perm.to(dev())].contiguous(), Bd)
+    assert np.array_equal(_bits64(pc), full[perm.numpy()])
+    again, _ = _run(imm.ozaki_plan(M, N, K, t2), Ad, Bd)
+    assert np.array_equal(_bits64(again), full)
+
+
+def test_split_then_multiply_equals_run():
+    M, N, K = 90, 130, 300
+    A, B = _inputs(M, N, K, "uniform", 7400)
+    Ad, Bd = A.to(dev()), B.to(dev())
+    plan = imm.ozaki_plan(M, N, K, "bf16")
+    C1, _ = _run(plan, Ad, Bd)
+    ws = torch.zeros(imm.ozaki_workspace_size(plan), dtype=torch.uint8, device=dev())
+    imm.ozaki_split(plan, 1, Bd, ws)
+    imm.ozaki_split(plan, 0, Ad, ws)
+    C2 = torch.empty_like(C1)
+    imm.ozaki_multiply(plan, ws, C2)
+    torch.cuda.synchronize()
+    assert np.array_equal(_bits64(C1), _bits64(C2))
+
+
+def test_edge_cases():
+    # K = 0 gives +0; zero rows give +0; empty M or N enqueue nothing
+    plan = imm.ozaki_plan(5, 7, 0, "bf16")
+    C, _ = _run(plan, torch.empty((5, 0), dtype=torch.float64, device=dev()),
+                torch.empty((0, 7), dtype=torch.float64, device=dev()))
+    assert np.array_equal(_bits64(C), np.zeros((5, 7), np.uint64))
+    A, B = _inputs(4, 33, 40, "uniform", 7500)
+    A[1] = 0.0
+    A[3] = -0.0
+    C, _ = _run(imm.ozaki_plan(4, 33, 40, "e4m3"), A.to(dev()), B.to(dev()))
+    assert np.array_equal(_bits64(C[[1, 3]]), np.zeros((2, 33), np.uint64))
+    assert np.array_equal(_bits64(C), _bits64(OZ.gemm(A.numpy(), B.numpy(), "e4m3")))
+    for M, N in ((0, 5), (5, 0)):
+        plan = imm.ozaki_plan(M, N, 8, "bf16")
+        ws = torch.empty(max(1, imm.ozaki_workspace_size(plan)), dtype=torch.uint8, device=dev())
+        imm.ozaki_run(plan, torch.zeros((M, 8), dtype=torch.float64, device=dev()),
+                      torch.zeros((8, N), dtype=torch.float64, device=dev()),
+                      torch.zeros((M, N), dtype=torch.float64, device=dev()), ws)
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("name", ["ozaki_bf16_8192", "ozaki_e4m3_8192"])
+def test_bench_size_sampled(name):
+    """The configuration the benchmark times, checked on sampled elements."""
+    w = wl.OZAKI_WORKLOADS[name]
+    A, B = w.make()
+    plan = imm.ozaki_plan(w.n, w.n, w.n, w.type2)
+    C, _ = _run(plan, A.to(dev()), B.to(dev()))
+    r = np.random.default_rng(7600)
+    ii = np.concatenate([r.integers(0, w.n, 40), [0, w.n - 1, w.n - 1]])
+    jj = np.concatenate([r.integers(0, w.n, 40), [w.n - 1, 0, w.n - 1]])
+    want = OZ.gemm_elems(A.numpy(), B.numpy(), ii, jj, w.type2)
+    got = C.cpu().numpy()[ii, jj]
+    assert np.array_equal(_bits64(got), _bits64(want))
+    # and it is an fp64-accurate product: within the page's Fast Mode target
+    ab = np.abs(A.numpy()[ii]) * np.abs(B.numpy()[:, jj]).T
+    exact = np.array([np.sum(A.numpy()[i] * B.numpy()[:, j]) for i, j in zip(ii, jj)])
+    assert np.all(np.abs(got - exact) <= 2 * np.sqrt(w.n) * 2.0 ** -53 * ab.sum(axis=1)
+                  + w.n * 2.0 ** -53 * ab.sum(axis=1))

@@ -36,7 +36,7 @@ SHAPES = [  # (N, K, dtype) of every workload family, plus a few others
 def _declared_functions():
     text = open(HEADER, encoding="utf-8").read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(gemm_[a-z_0-9]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b((?:gemm|ozaki)_[a-z_0-9]+)\s*\(", text)))
 
 
 def test_library_exports_every_declared_symbol():
@@ -263,3 +263,95 @@ def test_binding_checks_tensor_shapes_and_dtypes():
         imm.gemm_run(p, A, B, C.to(torch.bfloat16))
     with pytest.raises(ValueError):
         imm.gemm_run(p, A.t(), B, C)
+
+
+# ---- Ozaki-scheme fp64 product: host logic ----------------------------------
+
+def _oz_status(*args):
+    h = ctypes.c_void_p()
+    st = imm.lib().ozaki_plan(*args, ctypes.byref(h))
+    if h.value:
+        imm.lib().ozaki_plan_destroy(h)
+    return st
+
+
+@pytest.mark.parametrize("args,status", [
+    ((8, 8, 8, 1, 0, 0), 0),                 # bf16 slices
+    ((8, 8, 8, 2, 0, 0), 0),                 # e4m3 slices
+    ((8, 8, 8, 0, 0, 0), 2),                 # fp16 is not a slice format here
+    ((8, 8, 8, 3, 0, 0), 2),
+    ((-1, 8, 8, 1, 0, 0), 1),
+    ((8, 8, 8, 1, 20, 0), 0),
+    ((8, 8, 8, 1, 21, 0), 2),                # at most 20 slices
+    ((8, 8, 8, 1, -1, 0), 2),
+    ((8, 8, 8, 1, 0, -2), 2),
+    ((8, 8, 2 ** 22, 1, 0, 0), 0),           # one bit per slice left
+    ((8, 8, 2 ** 22 + 1, 1, 0, 0), 2),
+    ((8, 2 ** 23, 8, 1, 0, 0), 2),
+    ((0, 0, 0, 1, 0, 0), 0),
+])
+def test_ozaki_plan_validation(args, status):
+    assert _oz_status(*args) == status
+
+
+@pytest.mark.parametrize("K", [1, 15, 256, 257, 1000, 4096, 16384, 131072, 2 ** 22])
+@pytest.mark.parametrize("t2", ["bf16", "e4m3"])
+def test_ozaki_plan_matches_oracle_parameters_for_any_M(K, t2):
+    from oracle import ozaki as OZ
+    P = OZ.params(K, t2)
+    ref = None
+    for M in (1, 100, 4097):
+        i = imm.ozaki_plan(M, 200, K, t2).info
+        got = (i["rho"], i["bits"], i["delta"], i["slices"], i["d"], i["pairs"], i["k_pad"],
+               i["n_pad"], i["tile_m"], i["tile_n"])
+        assert got[:6] == (P.rho, P.b, P.delta, P.s, P.d, len(P.pairs))
+        assert got[6] % 16 == 0 and K <= got[6] < K + 16 and got[7] == 208
+        ref = ref or got
+        assert got == ref                    # nothing but the grid depends on M
+
+
+def test_ozaki_explicit_slices_and_d():
+    from oracle import ozaki as OZ
+    for s, d in ((4, 3), (7, 5), (20, 40), (1, 1)):
+        i = imm.ozaki_plan(10, 10, 500, "bf16", s, d).info
+        assert (i["slices"], i["d"], i["pairs"]) == (s, d, len(OZ.pair_list(s, d)))
+
+
+def test_ozaki_workspace_layout():
+    i = imm.ozaki_plan(100, 300, 1000, "bf16").info
+    s, kp, np_ = i["slices"], i["k_pad"], i["n_pad"]
+    assert i["a_slices_offset"] == 0
+    assert i["b_slices_offset"] >= s * 100 * kp * 2
+    assert i["a_exp_offset"] >= i["b_slices_offset"] + s * kp * np_ * 2
+    assert i["b_exp_offset"] >= i["a_exp_offset"] + 100 * 4
+    assert i["scratch_offset"] >= i["b_exp_offset"] + np_ * 4
+    assert i["workspace_bytes"] >= i["scratch_offset"] + 4 * 300 * 8
+    for k in ("b_slices_offset", "a_exp_offset", "b_exp_offset", "scratch_offset"):
+        assert i[k] % 256 == 0
+
+
+def test_ozaki_validation_before_any_hip_call():
+    L = imm.lib()
+    p = imm.ozaki_plan(64, 64, 64, "bf16")
+    h, ws = p.handle, imm.ozaki_workspace_size(p)
+    assert L.ozaki_run(None, FAKE, FAKE, FAKE, FAKE, ws, None) == 1
+    assert L.ozaki_run(h, 0, FAKE, FAKE, FAKE, ws, None) == 1        # NULL A
+    assert L.ozaki_run(h, FAKE, FAKE + 4, FAKE, FAKE, ws, None) == 1  # misaligned B
+    assert L.ozaki_run(h, FAKE, FAKE, 0, FAKE, ws, None) == 1        # NULL C
+    assert L.ozaki_run(h, FAKE, FAKE, FAKE, 0, ws, None) == 3        # NULL workspace
+    assert L.ozaki_run(h, FAKE, FAKE, FAKE, FAKE, ws - 1, None) == 3
+    assert L.ozaki_run(h, FAKE, FAKE, FAKE, FAKE + 8, ws, None) == 1  # misaligned workspace
+    assert L.ozaki_split(h, 2, FAKE, FAKE, ws, None) == 1             # no such operand
+    assert L.ozaki_multiply(h, FAKE, ws, FAKE + 1, None) == 1
+    e = imm.ozaki_plan(0, 64, 64, "bf16")
+    assert L.ozaki_run(e.handle, 0, 0, 0, 0, 0, None) == 0            # empty: nothing to do
+
+
+@pytest.mark.skipif(_have_gpu(), reason="checks the no-GPU error path")
+def test_ozaki_without_gpu_returns_hip_error():
+    L = imm.lib()
+    p = imm.ozaki_plan(64, 64, 64, "e4m3")
+    ws = imm.ozaki_workspace_size(p)
+    assert L.ozaki_run(p.handle, FAKE, FAKE, FAKE, FAKE, ws, None) == 4
+    assert L.ozaki_split(p.handle, 0, FAKE, FAKE, ws, None) == 4
+    assert L.ozaki_multiply(p.handle, FAKE, ws, FAKE, None) == 4

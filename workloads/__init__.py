@@ -73,6 +73,19 @@ def grid(shape, dtype, g, mag=255, exp=-6) -> torch.Tensor:
     return x.to(DTYPES[dtype] if isinstance(dtype, str) else dtype)
 
 
+def uniform64(shape, g, lo=-1.0, hi=1.0) -> torch.Tensor:
+    """i.i.d. uniform[lo, hi) in fp64 (53 random significand bits)."""
+    return torch.rand(shape, generator=g, dtype=torch.float64) * (hi - lo) + lo
+
+
+def wide64(shape, g, spread=20) -> torch.Tensor:
+    """fp64 N(0,1) values times 2^e, e uniform integers in [-spread, spread]:
+    full significands over a wide exponent range."""
+    x = torch.randn(shape, generator=g, dtype=torch.float64)
+    e = torch.randint(-spread, spread + 1, shape, generator=g, dtype=torch.int32)
+    return torch.ldexp(x, e.to(torch.float64))
+
+
 @dataclasses.dataclass(frozen=True)
 class Workload:
     name: str
@@ -145,3 +158,34 @@ def _registry():
 
 
 WORKLOADS = _registry()
+
+
+@dataclasses.dataclass(frozen=True)
+class OzakiWorkload:
+    """Square fp64 product by the Ozaki scheme (the Insight Edge blog's FP64
+    emulation tables run square sizes 1024 .. 16384)."""
+    name: str
+    n: int
+    type2: str
+    seed: int
+
+    def make(self):
+        """(A, B) fp64 CPU tensors, uniform[-1, 1)."""
+        g = gen(self.seed)
+        return uniform64((self.n, self.n), g), uniform64((self.n, self.n), g)
+
+    @property
+    def flops(self) -> int:
+        """fp64 flops of the product it emulates (2 n^3)."""
+        return 2 * self.n ** 3
+
+
+def _ozaki_registry():
+    w = {}
+    for t, t2 in enumerate(("bf16", "e4m3")):
+        for i, n in enumerate((1024, 4096, 8192, 16384)):
+            w[f"ozaki_{t2}_{n}"] = OzakiWorkload(f"ozaki_{t2}_{n}", n, t2, 6000 + 10 * t + i)
+    return w
+
+
+OZAKI_WORKLOADS = _ozaki_registry()
