@@ -16,10 +16,15 @@ What is computed, in the page's order:
 
 1. Parameters.  rho = max(gamma, xi) with gamma = ceil(53 - (24 - log2 k)/2)
    and xi = 53 - m_Type2 ("分解(Split)", the precision parameter).  k is the
-   inner dimension K of the product.  A slice then carries b = 53 - rho bits:
-   its entries are integer multiples of 2^-b in [-1, 1], so a product of two
+   number of products one fp32 accumulation chain sums: min(K, kc), with K
+   cut into chunks of kc.  A slice then carries b = 53 - rho bits: its
+   entries are integer multiples of 2^-b in [-1, 1], so a product of two
    slice entries is a multiple of 2^-2b of magnitude <= 1 and any fp32 sum of
-   K of them is exact (K 2^2b <= 2^24): equation (11) holds exactly.
+   k of them is exact (k 2^2b <= 2^24): equation (11) holds exactly for every
+   chunk.  The page argues exactly this way for one K tile (a bf16 product
+   has 16 bits, and 128 of them sum exactly in fp32's 24).  The default kc
+   is the longest chain that keeps all of Type2's bits: 2^(24 - 2 m_Type2),
+   256 for bf16 and 65536 for e4m3.
 2. Split (equations (1)-(5)) of each row of A and each column of B (the
    vectors x and y of the inner product x^T y in equation (10)):
    c0 = ceil(log2 max_i |x_i|) (equation (1); 0 for a zero vector), then for
@@ -35,22 +40,28 @@ What is computed, in the page's order:
    |x - v| <= 2^(c_p - b - 1) and c_{p+1} = c_p - delta with delta = b + 1
    keeps |x| <= 2^c for every slice.
 3. Products (equations (10), (11)): for every slice pair (p, q) in ascending
-   p, then ascending q, skipping p + q >= d (Fast Mode), the exact slice
-   product S_pq = slice_p(A) @ slice_q(B) is scaled by 2^(c_p(A row) +
-   c_q(B column)) and added to an fp64 accumulator that starts at +0.0.
+   p, then ascending q, skipping p + q >= d (Fast Mode), and for every K
+   chunk in ascending order, the exact chunk product
+   S = slice_p(A)[:, chunk] @ slice_q(B)[chunk, :] is scaled by
+   2^(c_p(A row) + c_q(B column)) and added to an fp64 accumulator that
+   starts at +0.0.
 
 Readings where the page is open (each listed in the design notes):
   * per-row / per-column exponents: the page's listing takes one maximum per
     matrix; the equations are written for the vectors of an inner product.
     One exponent per row of A makes row i of C depend on row i of A only,
     the batch-invariance the rest of this library is built on.
+  * k in gamma is the length of one exact fp32 chain (a K chunk), whose
+    exact sums join the fp64 accumulator one by one; with the default chunks
+    every size keeps the page's 7 bf16 / 14 e4m3 slices, as its tables show
+    for all sizes up to 16384.
   * default slice count s = ceil(53 / b), the page's "ceil(m_Type1 / m_Type2)"
     with m_Type2 replaced by the bits a slice actually carries, at most 20
     (the limit of the page's split routine); default
     d = s + 2, which reproduces the page's tables (7 bf16 slices with d = 9
     giving 39 products; 14 e4m3 slices with d = 16 giving 130).
 
-The slice products are evaluated with numpy's fp64 matmul on the integer
+The chunk products are evaluated with numpy's fp64 matmul on the integer
 slice values n = slice * 2^b: every product and every partial sum is an
 integer below 2^53, so any summation order gives the exact result.
 """
@@ -78,6 +89,7 @@ class OzakiParams:
     delta: int    # exponent step between consecutive slices
     s: int        # slices per operand
     d: int        # Fast Mode: pairs with p + q >= d are skipped
+    kc: int       # K chunk: products per exact fp32 chain
 
     @property
     def pairs(self):
@@ -95,18 +107,25 @@ def gamma_of(K: int) -> int:
     return g
 
 
-def params(K: int, type2: str = "bf16", s: int = 0, d: int = 0) -> OzakiParams:
-    """Precision parameter and slice layout for an inner dimension K."""
+def default_chunk(type2: str) -> int:
+    """Longest exact fp32 chain at full Type2 precision: 2^(24 - 2 m_Type2)."""
+    return 2 ** (M_TYPE3 - 2 * TYPE2_BITS[type2])
+
+
+def params(K: int, type2: str = "bf16", s: int = 0, d: int = 0, kc: int = 0) -> OzakiParams:
+    """Precision parameter and slice layout for an inner dimension K cut into
+    exact chains of kc products (0: the default chunk)."""
     if type2 not in TYPE2_BITS:
         raise ValueError(f"unsupported Type2 {type2!r}")
+    kc = kc or default_chunk(type2)
     xi = M_TYPE1 - TYPE2_BITS[type2]
-    rho = max(gamma_of(K), xi)
+    rho = max(gamma_of(max(1, min(K, kc))), xi)
     b = M_TYPE1 - rho
     if b < 1:
         raise ValueError(f"K = {K} leaves no bits per slice")
     s = s or min(-(-M_TYPE1 // b), MAX_SLICES)
     d = d or s + 2
-    return OzakiParams(type2, int(K), rho, b, b + 1, int(s), int(d))
+    return OzakiParams(type2, int(K), rho, b, b + 1, int(s), int(d), int(kc))
 
 
 def pair_list(s: int, d: int):
@@ -150,33 +169,36 @@ def slice_ints(slices_bits: np.ndarray, P: OzakiParams) -> np.ndarray:
     return np.ldexp(decode(P.type2, slices_bits), P.b)
 
 
-def gemm(A: np.ndarray, B: np.ndarray, type2: str = "bf16", s: int = 0, d: int = 0):
+def gemm(A: np.ndarray, B: np.ndarray, type2: str = "bf16", s: int = 0, d: int = 0,
+         kc: int = 0):
     """C = A @ B by the Ozaki scheme (fp64 in, fp64 out)."""
     A = np.asarray(A, dtype=np.float64)
     B = np.asarray(B, dtype=np.float64)
     if A.ndim != 2 or B.ndim != 2 or A.shape[1] != B.shape[0]:
         raise ValueError(f"shape mismatch {A.shape} @ {B.shape}")
-    P = params(A.shape[1], type2, s, d)
+    K = A.shape[1]
+    P = params(K, type2, s, d, kc)
     sa, ca = split(A, 1, P)
     sb, cb = split(B, 0, P)
     na, nb = slice_ints(sa, P), slice_ints(sb, P)
     C = np.zeros((A.shape[0], B.shape[1]), dtype=np.float64)
     for p, q in P.pairs:
-        S = np.ldexp(na[p] @ nb[q], -2 * P.b)          # (11), exact
         scale = (ca - p * P.delta)[:, None] + (cb - q * P.delta)[None, :]
-        C = C + np.ldexp(S, scale)                      # (10)
+        for k0 in range(0, K, P.kc):
+            S = np.ldexp(na[p][:, k0:k0 + P.kc] @ nb[q][k0:k0 + P.kc, :], -2 * P.b)  # (11)
+            C = C + np.ldexp(S, scale)                                             # (10)
     return C
 
 
 def gemm_elems(A: np.ndarray, B: np.ndarray, ii, jj, type2: str = "bf16", s: int = 0,
-               d: int = 0) -> np.ndarray:
+               d: int = 0, kc: int = 0) -> np.ndarray:
     """C[ii[t], jj[t]] of ``gemm`` for listed positions: each needs only row
     ii[t] of A and column jj[t] of B (their exponents are their own)."""
     ii = np.asarray(ii, dtype=np.int64)
     jj = np.asarray(jj, dtype=np.int64)
     out = np.empty(ii.size, dtype=np.float64)
     for t in range(ii.size):
-        out[t] = gemm(A[ii[t]:ii[t] + 1, :], B[:, jj[t]:jj[t] + 1], type2, s, d)[0, 0]
+        out[t] = gemm(A[ii[t]:ii[t] + 1, :], B[:, jj[t]:jj[t] + 1], type2, s, d, kc)[0, 0]
     return out
 
 

@@ -59,6 +59,10 @@ def pin_pair_counts(oz=OZ):
     for K in (64, 4096, 65536):
         P = oz.params(K, "e4m3")
         assert (P.s, len(P.pairs)) == (14, 130)
+    # ... at every size of the page's tables (1024 .. 16384: 7 x 7 bf16 slices)
+    for K in (1024, 2048, 4096, 8192, 16384):
+        P = oz.params(K, "bf16")
+        assert (P.s, P.d, len(P.pairs)) == (7, 9, 39)
 
 
 def pin_gamma_formula(oz=OZ):
@@ -69,7 +73,9 @@ def pin_gamma_formula(oz=OZ):
         assert oz.gamma_of(K) == want, K
     # rho = max(gamma, xi), xi = 53 - m_Type2
     assert oz.params(256, "bf16").rho == 45 and oz.params(256, "e4m3").rho == 49
-    assert oz.params(16384, "bf16").rho == 48
+    # k is the length of one exact chain: the whole K when it is one chunk
+    assert oz.params(16384, "bf16", kc=16384).rho == 48
+    assert oz.params(16384, "bf16").rho == 45 and oz.params(1000, "bf16", kc=4096).rho == 46
 
 
 def pin_slices_are_type2_on_grid(oz=OZ):
@@ -129,11 +135,11 @@ def pin_integer_inputs_exact(oz=OZ):
     A = r.integers(-2 ** 20, 2 ** 20, (7, 64))
     B = r.integers(-2 ** 20, 2 ** 20, (64, 5))
     want = A.astype(object) @ B.astype(object)
-    for t2 in ("bf16", "e4m3"):
-        C = oz.gemm(A.astype(np.float64), B.astype(np.float64), t2)
+    for t2, kc in (("bf16", 0), ("e4m3", 0), ("bf16", 16), ("e4m3", 24), ("bf16", 64)):
+        C = oz.gemm(A.astype(np.float64), B.astype(np.float64), t2, kc=kc)
         assert C.shape == (7, 5)
         assert all(int(C[i, j]) == want[i, j] and C[i, j] == float(want[i, j])
-                   for i in range(7) for j in range(5))
+                   for i in range(7) for j in range(5)), (t2, kc)
 
 
 def pin_identity(oz=OZ):
@@ -165,7 +171,7 @@ def pin_rows_independent(oz=OZ):
     assert np.array_equal(oz.gemm(A, B[:, 2:5], "e4m3"), C[:, 2:5])
 
 
-def _rigorous_bound(oz, A, B, P):
+def _rigorous_bound(oz, A, B, P, chunks=1):
     """Truncation of both operands, the skipped pairs and the fp64 sums, from
     the residual bound of the split (|x^(p)| <= 2^c_p) -- not from the
     oracle's code."""
@@ -181,33 +187,36 @@ def _rigorous_bound(oz, A, B, P):
     # every slice term is at most 2^c_p in magnitude
     sa = (np.abs(A) + np.exp2(ca - P.delta + 1)[:, None])
     sb = (np.abs(B) + np.exp2(cb - P.delta + 1)[None, :])
-    rounding = len(P.pairs) * 2.0 ** -53 * (sa @ sb)
+    rounding = len(P.pairs) * chunks * 2.0 ** -53 * (sa @ sb)
     return trunc + dropped + rounding
 
 
 def pin_random_vs_exact(oz=OZ):
     r = _rng(9)
-    for t2, (M, K, N) in (("bf16", (4, 96, 3)), ("e4m3", (3, 70, 4))):
+    for t2, (M, K, N), kc in (("bf16", (4, 96, 3), 0), ("e4m3", (3, 70, 4), 0),
+                              ("bf16", (3, 100, 3), 32)):
         A = r.uniform(-1.0, 1.0, (M, K))
         B = r.uniform(-1.0, 1.0, (K, N))
-        C = oz.gemm(A, B, t2)
+        C = oz.gemm(A, B, t2, kc=kc)
         ex = _exact_product(A, B)
         err = np.array([[abs(Fraction(float(C[i, j])) - ex[i][j]) for j in range(N)]
                         for i in range(M)], dtype=float)
         # the page's Fast Mode accuracy target ...
         assert np.all(err <= OZ.fast_mode_error_target(A, B)), t2
-        # ... and the result is the exact product rounded up to a few ulps
-        assert np.all(err <= 4 * 2.0 ** -53 * np.abs(C)), t2
+        # ... and with one chunk the result is the exact product to a few ulps
+        # (several chunks round against partial sums, which may exceed |C|)
+        if not kc:
+            assert np.all(err <= 4 * 2.0 ** -53 * np.abs(C)), t2
     # wide dynamic range, fewer slices and pairs: the derived bound
     A = r.standard_normal((3, 64)) * np.ldexp(1.0, r.integers(-20, 20, (3, 64)))
     B = r.standard_normal((64, 3)) * np.ldexp(1.0, r.integers(-20, 20, (64, 3)))
-    for s, d in ((5, 5), (4, 3), (9, 0)):
-        P = oz.params(64, "bf16", s, d)
-        C = oz.gemm(A, B, "bf16", s, d)
+    for s, d, kc in ((5, 5, 0), (4, 3, 0), (9, 0, 0), (6, 6, 16)):
+        P = oz.params(64, "bf16", s, d, kc)
+        C = oz.gemm(A, B, "bf16", s, d, kc)
         ex = _exact_product(A, B)
         err = np.array([[abs(Fraction(float(C[i, j])) - ex[i][j]) for j in range(3)]
                         for i in range(3)], dtype=float)
-        assert np.all(err <= _rigorous_bound(oz, A, B, P)), (s, d)
+        assert np.all(err <= _rigorous_bound(oz, A, B, P, -(-64 // P.kc))), (s, d, kc)
 
 
 def pin_vs_numpy(oz=OZ):
@@ -228,6 +237,23 @@ def pin_elems_match_full(oz=OZ):
     assert np.array_equal(oz.gemm_elems(A, B, ii, jj, "e4m3"), C[ii, jj])
 
 
+def pin_chunking_only_moves_roundings(oz=OZ):
+    """Chunks change which fp64 additions round, never the exact value: on
+    inputs where every partial sum is exact, any chunk length gives the same
+    bits; on random inputs the results agree to a few ulps."""
+    r = _rng(13)
+    A = r.integers(-1000, 1000, (5, 200)).astype(np.float64) / 64
+    B = r.integers(-1000, 1000, (200, 4)).astype(np.float64) / 128
+    base = oz.gemm(A, B, "bf16", kc=200)
+    for kc in (16, 48, 64, 128):
+        assert np.array_equal(oz.gemm(A, B, "bf16", kc=kc), base), kc
+    A = r.standard_normal((5, 300))
+    B = r.standard_normal((300, 4))
+    ab = np.abs(A) @ np.abs(B)
+    c1, c2 = oz.gemm(A, B, "bf16", kc=256), oz.gemm(A, B, "bf16", kc=32)
+    assert np.all(np.abs(c1 - c2) <= 64 * 2.0 ** -53 * ab)
+
+
 def pin_zero_rows(oz=OZ):
     A = np.zeros((3, 32))
     A[1] = np.arange(32) - 7.5
@@ -239,7 +265,8 @@ def pin_zero_rows(oz=OZ):
 PINS = [pin_pair_counts, pin_gamma_formula, pin_slices_are_type2_on_grid,
         pin_split_reconstructs, pin_split_residual_bound, pin_integer_inputs_exact,
         pin_identity, pin_powers_of_two_and_sign, pin_rows_independent,
-        pin_random_vs_exact, pin_vs_numpy, pin_elems_match_full, pin_zero_rows]
+        pin_random_vs_exact, pin_vs_numpy, pin_elems_match_full, pin_chunking_only_moves_roundings,
+        pin_zero_rows]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -255,15 +282,18 @@ MUTANTS = [
     ("residual_not_updated", "r = r - v  ", "r = r  "),
     ("scale_sign", "scale = (ca - p * P.delta)[:, None] + (cb - q * P.delta)[None, :]",
      "scale = (ca + p * P.delta)[:, None] + (cb - q * P.delta)[None, :]"),
-    ("transposed_B", "S = np.ldexp(na[p] @ nb[q], -2 * P.b)",
-     "S = np.ldexp(na[p] @ (nb[q].T if nb[q].shape[0] == nb[q].shape[1] else nb[q][::-1]), -2 * P.b)"),
+    ("B_rows_reversed", "@ nb[q][k0:k0 + P.kc, :], -2 * P.b)",
+     "@ nb[q][k0:k0 + P.kc, :][::-1], -2 * P.b)"),
+    ("chunk_scale_missing", "C = C + np.ldexp(S, scale)", "C = C + S"),
     ("one_max_per_matrix", "c0 = ceil_log2(np.max(np.abs(x), axis=axis))",
      "c0 = ceil_log2(np.max(np.abs(x)) + 0 * np.max(np.abs(x), axis=axis))"),
-    ("delta_too_small", "return OzakiParams(type2, int(K), rho, b, b + 1, int(s), int(d))",
-     "return OzakiParams(type2, int(K), rho, b, b - 1, int(s), int(d))"),
+    ("delta_too_small", "return OzakiParams(type2, int(K), rho, b, b + 1, int(s), int(d), int(kc))",
+     "return OzakiParams(type2, int(K), rho, b, b - 1, int(s), int(d), int(kc))"),
     ("gamma_without_log", "while K * 4 ** (M_TYPE1 - g) > 2 ** M_TYPE3:",
      "while 4 ** (M_TYPE1 - g) > 2 ** M_TYPE3:"),
     ("ceil_log2_floor", "c = np.where(mant == 0.5, e - 1, e)", "c = e - 1"),
+    ("first_chunk_dropped", "for k0 in range(0, K, P.kc):", "for k0 in range(P.kc, K, P.kc):"),
+    ("chunk_rho_from_K", "rho = max(gamma_of(max(1, min(K, kc))), xi)", "rho = max(gamma_of(max(1, kc)), xi)"),
     ("first_slice_dropped", "for p in range(P.s):\n        cp =",
      "for p in range(P.s):\n        if p == 0: r = r - ((r + np.ldexp(0.75, P.rho + c0.reshape(shape))) - np.ldexp(0.75, P.rho + c0.reshape(shape)))\n        cp ="),
 ]
