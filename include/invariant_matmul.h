@@ -215,14 +215,19 @@ void gemm_plan_destroy(gemm_plan_t plan);
  *     p ascending then q ascending, without the pairs with p+q >= d ("Fast
  *     Mode（GEMMの削減）"), the fp32 product of the two slices, scaled by
  *     2^(c_p(row) + c_q(column)), is added to an fp64 sum starting at +0.
+ * K is cut into chunks of `chunk` products; for each pair the exact fp32
+ * product of every chunk is added to the fp64 sum in ascending chunk order
+ * (the page's exactness argument in "最適化後の結果" is per K tile).
  * Precision parameter ("分解(Split)"): rho = max(gamma, xi),
- * gamma = ceil(53 - (24 - log2 K)/2), xi = 53 - m_Type2 (m = 8 for bf16, 4 for
- * e4m3), with K the inner dimension.  A slice carries b = 53 - rho bits, so
- * every fp32 slice product is exact and the result does not depend on any
- * summation order inside the matrix cores: it is a bitwise function of row i
- * of A, of B, of K and of (type2, slices, d).  delta = b + 1.
- * Defaults: slices = min(ceil(53 / b), 20) (7 for bf16 and K <= 256, 14 for
- * e4m3 and K <= 65536; 20 is the most the page's split routine makes),
+ * gamma = ceil(53 - (24 - log2 k)/2), xi = 53 - m_Type2 (m = 8 for bf16, 4 for
+ * e4m3), with k = min(K, chunk) the length of one fp32 chain.  A slice
+ * carries b = 53 - rho bits, so every fp32 chunk product is exact and the
+ * result does not depend on any summation order inside the matrix cores: it
+ * is a bitwise function of row i of A, of B, of K and of (type2, slices, d,
+ * chunk).  delta = b + 1.
+ * Defaults: chunk = 2^(24 - 2 m_Type2), the longest exact chain with all of
+ * Type2's bits (256 for bf16, 65536 for e4m3); slices = min(ceil(53 / b), 20)
+ * (7 for bf16, 14 for e4m3; 20 is the most the page's split routine makes),
  * d = slices + 2 (39 products for 7 bf16 slices, 130 for 14 e4m3 slices, the
  * page's "最適化後の結果" tables).
  * Domain: finite inputs whose nonzero row / column maxima lie in
@@ -248,6 +253,7 @@ typedef struct {
   int32_t type2;              /* GEMM_BF16 or GEMM_F8_E4M3 */
   int32_t rho, bits, delta;   /* precision parameter, bits per slice, exponent step */
   int32_t slices, d, pairs;   /* slices per operand, Fast Mode threshold, products */
+  int64_t chunk;              /* products per exact fp32 chain */
   int32_t tile_m, tile_n;     /* output tile of the product kernel */
   int64_t k_pad, n_pad;
   int64_t grid;               /* workgroups of the product kernel */
@@ -256,12 +262,14 @@ typedef struct {
 } ozaki_plan_info_t;
 
 /* Plan an Ozaki-scheme product.  type2: GEMM_BF16 or GEMM_F8_E4M3.
- * slices: 0 = default, else 1..20; d: 0 = default, else >= 1.  M, N, K >= 0;
- * K at most 2^22 (one bit per slice left); N below 2^23.  Errors:
- * GEMM_ERR_INVALID_VALUE (negative size, NULL handle), GEMM_ERR_UNSUPPORTED
- * (other type2, slices or d out of range, sizes too large). */
+ * slices: 0 = default, else 1..20; d: 0 = default, else >= 1; chunk: 0 =
+ * default, else a multiple of 128 (at most 2^22).  M, N, K >= 0; K below 2^23
+ * (bf16) or 2^25 (e4m3), N below 2^23 (32-bit offsets inside one tile).
+ * Errors: GEMM_ERR_INVALID_VALUE (negative size, NULL
+ * handle), GEMM_ERR_UNSUPPORTED (other type2, slices, d or chunk out of range,
+ * sizes too large). */
 gemm_status ozaki_plan(int64_t M, int64_t N, int64_t K, gemm_dtype type2, int slices, int d,
-                       ozaki_plan_t* plan);
+                       int64_t chunk, ozaki_plan_t* plan);
 
 gemm_status ozaki_plan_info(ozaki_plan_t plan, ozaki_plan_info_t* info);
 

@@ -80,7 +80,8 @@ class OzakiPlanInfo(ctypes.Structure):
         ("M", ctypes.c_int64), ("N", ctypes.c_int64), ("K", ctypes.c_int64),
         ("type2", ctypes.c_int32), ("rho", ctypes.c_int32), ("bits", ctypes.c_int32),
         ("delta", ctypes.c_int32), ("slices", ctypes.c_int32), ("d", ctypes.c_int32),
-        ("pairs", ctypes.c_int32), ("tile_m", ctypes.c_int32), ("tile_n", ctypes.c_int32),
+        ("pairs", ctypes.c_int32), ("chunk", ctypes.c_int64), ("tile_m", ctypes.c_int32),
+        ("tile_n", ctypes.c_int32),
         ("k_pad", ctypes.c_int64), ("n_pad", ctypes.c_int64), ("grid", ctypes.c_int64),
         ("workspace_bytes", ctypes.c_uint64), ("a_slices_offset", ctypes.c_uint64),
         ("b_slices_offset", ctypes.c_uint64), ("a_exp_offset", ctypes.c_uint64),
@@ -124,7 +125,7 @@ def lib() -> ctypes.CDLL:
         L.gemm_status_string.restype = ctypes.c_char_p
         L.gemm_last_hip_error.argtypes = []
         sz = ctypes.c_size_t
-        L.ozaki_plan.argtypes = [i64, i64, i64, i32, i32, i32, pp]
+        L.ozaki_plan.argtypes = [i64, i64, i64, i32, i32, i32, i64, pp]
         L.ozaki_plan_info.argtypes = [vp, ctypes.POINTER(OzakiPlanInfo)]
         L.ozaki_workspace_size.argtypes = [vp]
         L.ozaki_workspace_size.restype = sz
@@ -337,12 +338,13 @@ class OzakiPlan:
         return ozaki_plan_info(self)
 
 
-def ozaki_plan(M: int, N: int, K: int, type2="bf16", slices: int = 0, d: int = 0) -> OzakiPlan:
+def ozaki_plan(M: int, N: int, K: int, type2="bf16", slices: int = 0, d: int = 0,
+               chunk: int = 0) -> OzakiPlan:
     """Plan C = A @ B in fp64 by the Ozaki scheme with Type2 slices ("bf16" or
-    "e4m3"); slices / d = 0 take the library's defaults."""
+    "e4m3"); slices / d / chunk = 0 take the library's defaults."""
     h = ctypes.c_void_p()
-    _check(lib().ozaki_plan(M, N, K, _dtype_code(type2), int(slices), int(d), ctypes.byref(h)),
-           "ozaki_plan")
+    _check(lib().ozaki_plan(M, N, K, _dtype_code(type2), int(slices), int(d), int(chunk),
+                            ctypes.byref(h)), "ozaki_plan")
     return OzakiPlan(h.value)
 
 
@@ -401,12 +403,12 @@ def ozaki_run(plan: OzakiPlan, A, B, C, workspace, stream=None, workspace_bytes=
            "ozaki_run")
 
 
-def ozaki_mm(A, B, type2="bf16", slices: int = 0, d: int = 0, stream=None):
+def ozaki_mm(A, B, type2="bf16", slices: int = 0, d: int = 0, chunk: int = 0, stream=None):
     """C = A @ B for fp64 CUDA tensors, allocating C and the workspace with torch."""
     import torch
     M, K = A.shape
     N = B.shape[1]
-    plan = ozaki_plan(M, N, K, type2, slices, d)
+    plan = ozaki_plan(M, N, K, type2, slices, d, chunk)
     ws = torch.empty(max(1, ozaki_workspace_size(plan)), dtype=torch.uint8, device=A.device)
     C = torch.empty((M, N), dtype=torch.float64, device=A.device)
     ozaki_run(plan, A.contiguous(), B.contiguous(), C, ws, stream)

@@ -178,11 +178,11 @@ constexpr int64_t kOzColChunk = 256;  // rows per partial column maximum of B
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 bool aligned8(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 7u) == 0; }
 
-// Largest b with K * 4^b <= 2^24: the bits per slice for which a K-term fp32
+// Largest b with k * 4^b <= 2^24: the bits per slice for which a k-term fp32
 // sum of slice products is exact (gamma = 53 - b_max of the Insight Edge
 // blog's "分解(Split)" formula gamma = ceil(53 - (24 - log2 k) / 2)).
-int oz_exact_bits(int64_t K) {
-  const int64_t k = K > 0 ? K : 1;
+int oz_exact_bits(int64_t k) {
+  if (k < 1) k = 1;
   int b = 0;
   while (b < 12 && k * ((int64_t)1 << (2 * (b + 1))) <= ((int64_t)1 << 24)) ++b;
   return b;
@@ -194,6 +194,7 @@ struct ozaki_plan_s {
   int64_t M, N, K;
   int type2, eb;
   int rho, b, delta, slices, d, npairs;
+  int64_t chunk;
   int64_t kp, np;
   int64_t tiles_m, tiles_n, grid;
   int64_t col_chunks;
@@ -388,16 +389,20 @@ gemm_status gemm_splitk_run_bias(gemm_plan_t p, const void* A, const void* B, co
 void gemm_plan_destroy(gemm_plan_t p) { delete p; }
 
 gemm_status ozaki_plan(int64_t M, int64_t N, int64_t K, gemm_dtype type2, int slices, int d,
-                       ozaki_plan_t* plan) {
+                       int64_t chunk, ozaki_plan_t* plan) {
   if (!plan) return GEMM_ERR_INVALID_VALUE;
   *plan = nullptr;
   if (M < 0 || N < 0 || K < 0) return GEMM_ERR_INVALID_VALUE;
   if (type2 != GEMM_BF16 && type2 != GEMM_F8_E4M3) return GEMM_ERR_UNSUPPORTED;
   if (slices < 0 || slices > kOzMaxSlices || d < 0) return GEMM_ERR_UNSUPPORTED;
-  if (M > INT_MAX || K > ((int64_t)1 << 22) || N >= ((int64_t)1 << 23)) return GEMM_ERR_UNSUPPORTED;
-  // rho = max(gamma, xi): b = min(exact bits for K, significand bits of Type2)
+  if (chunk < 0 || chunk % 128 != 0 || chunk > ((int64_t)1 << 22)) return GEMM_ERR_UNSUPPORTED;
+  if (M > INT_MAX || K > INT_MAX || N >= ((int64_t)1 << 23)) return GEMM_ERR_UNSUPPORTED;
+  // rho = max(gamma, xi): b = min(exact bits of one chain, significand bits
+  // of Type2); the default chain is the longest that keeps all of Type2's
+  // bits, 2^(24 - 2 m_Type2)
   const int m_type2 = type2 == GEMM_BF16 ? 8 : 4;
-  const int bx = oz_exact_bits(K);
+  const int64_t kc = chunk ? chunk : ((int64_t)1 << (24 - 2 * m_type2));
+  const int bx = oz_exact_bits(K < kc ? K : kc);
   const int b = bx < m_type2 ? bx : m_type2;
   if (b < 1) return GEMM_ERR_UNSUPPORTED;
   ozaki_plan_s* p = new (std::nothrow) ozaki_plan_s();
@@ -408,6 +413,7 @@ gemm_status ozaki_plan(int64_t M, int64_t N, int64_t K, gemm_dtype type2, int sl
   p->type2 = type2;
   p->eb = type2 == GEMM_BF16 ? 2 : 1;
   p->b = b;
+  p->chunk = kc;
   p->rho = 53 - b;
   p->delta = b + 1;
   p->slices = slices ? slices : (53 + b - 1) / b;
@@ -434,9 +440,11 @@ gemm_status ozaki_plan(int64_t M, int64_t N, int64_t K, gemm_dtype type2, int sl
   p->off_eb = p->off_ea + align256((size_t)M * 4);
   p->off_part = p->off_eb + align256((size_t)p->np * 4);
   p->ws_bytes = p->off_part + align256((size_t)p->col_chunks * N * 8);
-  // DMA offsets of one 128-row A tile and one stage of B stay below 2^31
+  // DMA offsets of one A tile and one stage of B stay below 2^31, and so does
+  // the kernel's stage count (stages per pair times pairs)
+  const int64_t stages = ceil_div(p->kp, 128 / p->eb) * p->npairs;
   if (oz_tile_m(type2) * p->kp * p->eb >= ((int64_t)1 << 31) - 256 ||
-      p->grid * 512 >= ((int64_t)1 << 32)) {
+      p->grid * 512 >= ((int64_t)1 << 32) || stages >= ((int64_t)1 << 31)) {
     delete p;
     return GEMM_ERR_UNSUPPORTED;
   }
@@ -457,6 +465,7 @@ gemm_status ozaki_plan_info(ozaki_plan_t p, ozaki_plan_info_t* info) {
   info->slices = p->slices;
   info->d = p->d;
   info->pairs = p->npairs;
+  info->chunk = p->chunk;
   info->tile_m = oz_tile_m(p->type2);
   info->tile_n = kOzTileN;
   info->k_pad = p->kp;
@@ -548,6 +557,7 @@ gemm_status ozaki_multiply(ozaki_plan_t p, const void* ws, size_t bytes, double*
   a.d = p->d;
   a.npairs = p->npairs;
   a.delta = p->delta;
+  a.chunk_stages = (int32_t)(p->chunk / (128 / p->eb));  // 128-byte K stages
   e = launch_ozaki_gemm(p->type2, a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? GEMM_OK : hip_fail(e);
 }

@@ -57,24 +57,32 @@ constexpr int TBN = 256;  // tile columns (every configuration)
 //   MODE_OZAKI: the Ozaki-scheme product (Insight Edge cuTile blog, "行列積の
 //     計算" and its fused kernel listing): for every slice pair (p, q) of the
 //     pair list, the full K loop over slice p of A and slice q of B into the
-//     fp32 accumulators, which are then scaled by 2^-(p+q)*delta and added
-//     to an fp64 accumulator; at the end the row and column exponents are
-//     applied and fp64 C is stored.  The LDS ring runs on across pair
-//     boundaries (the stage sequence is pair-major).
+//     fp32 accumulators; after every chunk of K (chunk_stages stages, the
+//     length of an exact fp32 chain) and at the end of the pair they are
+//     scaled by 2^-(p+q)*delta, added to an fp64 accumulator and cleared.  At
+//     the end the row and column exponents are applied and fp64 C is stored.
+//     The LDS ring runs on across pair boundaries (the stage sequence is
+//     pair-major).
 enum { MODE_STORE = 0, MODE_SLICE = 1, MODE_OZAKI = 2 };
 
-// Slice pair P of the Ozaki pair list -> (p, q): p ascending, then q
-// ascending, with q < min(s, d - p) (Fast Mode skips p + q >= d).
-__device__ __forceinline__ void oz_pair(int P, int s, int d, int* p, int* q) {
-  int pp = 0;
-  for (; pp < s; ++pp) {
-    const int n = max(0, min(s, d - pp));
-    if (P < n) break;
-    P -= n;
+// Position in the Ozaki stage sequence: slice pair (p, q) -- p ascending,
+// then q ascending with q < min(s, d - p) (Fast Mode skips p + q >= d) --
+// and stage kt of its K pass.  Advanced one stage at a time, no divisions.
+struct OzCursor {
+  int p = 0, q = 0, kt = 0;
+  __device__ __forceinline__ bool live(int s) const { return p < s; }
+  // returns true when the step ends the pair
+  __device__ __forceinline__ bool step(int ntp, int s, int d) {
+    if (++kt < ntp) return false;
+    kt = 0;
+    if (++q >= min(s, d - p)) {
+      ++p;
+      q = 0;
+      if (d - p <= 0) p = s;  // no pair left with p + q < d
+    }
+    return true;
   }
-  *p = pp;
-  *q = P;
-}
+};
 
 constexpr int SKB = 128;  // bytes of K per row per stage
 constexpr unsigned OOB = 0x80000000u;
@@ -229,25 +237,29 @@ __global__ __launch_bounds__(256 * WM, (waves_per_simd<TBM, WM, NS>())) void gem
   };
   auto stage_src = [&](int t) {
     StageSrc q;
+    const int64_t kst = kbeg + (int64_t)t * BKE;
+    q.pa = A + (m0 * g.K + kst) * EB;
+    q.pb = BT ? B + (n0 * g.K + kst) * EB : B + (kst * g.N + n0) * EB;
+    q.rem = kend - kst < BKE ? (int)(kend - kst) : BKE;
+    return q;
+  };
+  // Ozaki mode: the stages are requested strictly in sequence (prologue, then
+  // one refill per stage), so the source of the next one comes from a cursor;
+  // past the last pair it is a zero fill.
+  OzCursor pf;
+  auto next_src = [&]() {
+    StageSrc q;
+    q.pa = A;
+    q.pb = B;
+    q.rem = 0;
     if constexpr (MODE == MODE_OZAKI) {
-      // stage t is stage kt of slice pair P; past the last pair: zero fill
-      const int P = t / ntp, kt = t - P * ntp;
-      q.pa = A;
-      q.pb = B;
-      q.rem = 0;
-      if (P < g.npairs) {
-        int sp, sq;
-        oz_pair(P, g.slices, g.d, &sp, &sq);
-        const int64_t kst = (int64_t)kt * BKE;
-        q.pa = A + sp * g.slice_a + (m0 * g.K + kst) * EB;
-        q.pb = B + sq * g.slice_b + (kst * g.N + n0) * EB;
+      if (pf.live(g.slices)) {
+        const int64_t kst = (int64_t)pf.kt * BKE;
+        q.pa = A + pf.p * g.slice_a + (m0 * g.K + kst) * EB;
+        q.pb = B + pf.q * g.slice_b + (kst * g.N + n0) * EB;
         q.rem = g.K - kst < BKE ? (int)(g.K - kst) : BKE;
+        pf.step(ntp, g.slices, g.d);
       }
-    } else {
-      const int64_t kst = kbeg + (int64_t)t * BKE;
-      q.pa = A + (m0 * g.K + kst) * EB;
-      q.pb = BT ? B + (n0 * g.K + kst) * EB : B + (kst * g.N + n0) * EB;
-      q.rem = kend - kst < BKE ? (int)(kend - kst) : BKE;
     }
     return q;
   };
@@ -379,13 +391,12 @@ __global__ __launch_bounds__(256 * WM, (waves_per_simd<TBM, WM, NS>())) void gem
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc64[i][j][r] = 0.0;
   }
-  // End of slice pair P: its exact fp32 sums, scaled by 2^-(p+q)*delta, join
-  // the fp64 sum in pair order; the fp32 accumulators restart from +0.
-  auto oz_flush = [&](int P) {
+  // End of a chunk of the slice pair at level p + q: its exact fp32 sums,
+  // scaled by 2^-(p+q)*delta, join the fp64 sum in (pair, chunk) order; the
+  // fp32 accumulators restart from +0.
+  auto oz_flush = [&](int level) {
     if constexpr (MODE == MODE_OZAKI) {
-      int sp, sq;
-      oz_pair(P, g.slices, g.d, &sp, &sq);
-      const int sh = -(sp + sq) * g.delta;
+      const int sh = -level * g.delta;
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -407,7 +418,7 @@ __global__ __launch_bounds__(256 * WM, (waves_per_simd<TBM, WM, NS>())) void gem
   Frag<IN, FM, FN> F0, F1;
   if (nt > 0) {
     for (int p = 0; p < NS; ++p) {
-      const StageSrc q = stage_src(p);
+      const StageSrc q = MODE == MODE_OZAKI ? next_src() : stage_src(p);
 #pragma unroll
       for (int x = 0; x < DPW; ++x) dma_one(q, p, x);
     }
@@ -438,7 +449,12 @@ __global__ __launch_bounds__(256 * WM, (waves_per_simd<TBM, WM, NS>())) void gem
   // never used.
   auto kstep = [&](bool refill, const Frag<IN, FM, FN>& Fc, int t, Frag<IN, FM, FN>& Fn, int tr,
                    int ks) {
-    const StageSrc q = stage_src(t + NS);
+    StageSrc q;
+    if constexpr (MODE == MODE_OZAKI) {
+      if (refill) q = next_src();
+    } else {
+      q = stage_src(t + NS);
+    }
     const int as = a_slot(tr), bs = b_slot(tr);
 #pragma unroll
     for (int x = 0; x < NM; ++x) {
@@ -454,6 +470,9 @@ __global__ __launch_bounds__(256 * WM, (waves_per_simd<TBM, WM, NS>())) void gem
   };
 
   // k-steps alternate between F0 and F1; KS is even, so every stage starts on F0
+  OzCursor cur;      // Ozaki mode: the pair and stage being computed
+  int chunk_left = 0;
+  if constexpr (MODE == MODE_OZAKI) chunk_left = g.chunk_stages;
   for (int t = 0; t < nt; ++t) {
 #pragma unroll
     for (int ks = 0; ks + 1 < KS; ++ks) {
@@ -467,7 +486,12 @@ __global__ __launch_bounds__(256 * WM, (waves_per_simd<TBM, WM, NS>())) void gem
     stage_change();
     kstep(true, F1, t, F0, t + 1, 0);
     if constexpr (MODE == MODE_OZAKI) {
-      if ((t + 1) % ntp == 0) oz_flush(t / ntp);
+      const int level = cur.p + cur.q;
+      const bool pair_end = cur.step(ntp, g.slices, g.d);
+      if (pair_end || --chunk_left == 0) {
+        oz_flush(level);
+        chunk_left = g.chunk_stages;
+      }
     }
   }
   // No LDS transfer or read may still be in flight when the workgroup ends.

@@ -110,6 +110,7 @@ struct OzGemmArgs : GemmArgs {
   const int32_t* ea;    // exponent of each row of A (M values)
   const int32_t* eb;    // exponent of each column of B (n_out values)
   int32_t slices, d, npairs, delta;
+  int32_t chunk_stages;  // K stages per exact fp32 chain
 };
 
 struct ReduceArgs {

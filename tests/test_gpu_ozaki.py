@@ -77,8 +77,11 @@ def test_split_matches_oracle(t2):
 
 
 CASES = [
-    # (type2, M, N, K, kind, slices, d)
+    # (type2, M, N, K, kind, slices, d[, chunk])
     ("bf16", 300, 600, 1000, "uniform", 0, 0),
+    ("bf16", 200, 300, 1000, "uniform", 0, 0, 1024),
+    ("bf16", 130, 260, 1300, "wide", 0, 0, 384),
+    ("e4m3", 70, 260, 700, "uniform", 0, 0, 256),
     ("e4m3", 300, 600, 1000, "uniform", 0, 0),
     ("bf16", 129, 257, 200, "wide", 0, 0),
     ("e4m3", 65, 520, 333, "wide", 0, 0),
@@ -91,14 +94,18 @@ CASES = [
 ]
 
 
-@pytest.mark.parametrize("t2,M,N,K,kind,s,d", CASES,
-                         ids=[f"{c[0]}-{c[1]}x{c[2]}x{c[3]}-{c[4]}-s{c[5]}d{c[6]}" for c in CASES])
-def test_product_bit_exact(t2, M, N, K, kind, s, d):
+@pytest.mark.parametrize("case", CASES,
+                         ids=[f"{c[0]}-{c[1]}x{c[2]}x{c[3]}-{c[4]}-s{c[5]}d{c[6]}"
+                              + (f"c{c[7]}" if len(c) > 7 else "") for c in CASES])
+def test_product_bit_exact(case):
+    t2, M, N, K, kind, s, d = case[:7]
+    kc = case[7] if len(case) > 7 else 0
     A, B = _inputs(M, N, K, kind, 7200 + M + N + K)
-    plan = imm.ozaki_plan(M, N, K, t2, s, d)
-    log(f"ozaki {t2} {M}x{N}x{K} {kind}: {plan.info['slices']} slices, {plan.info['pairs']} pairs")
+    plan = imm.ozaki_plan(M, N, K, t2, s, d, kc)
+    log(f"ozaki {t2} {M}x{N}x{K} {kind}: {plan.info['slices']} slices, {plan.info['pairs']} "
+        f"pairs, chunk {plan.info['chunk']}")
     C, _ = _run(plan, A.to(dev()), B.to(dev()))
-    want = OZ.gemm(A.numpy(), B.numpy(), t2, s, d)
+    want = OZ.gemm(A.numpy(), B.numpy(), t2, s, d, kc)
     got = _bits64(C)
     bad = got != _bits64(want)
     assert not bad.any(), (f"{int(bad.sum())} of {bad.size} differ; first {np.argwhere(bad)[:3]}")

@@ -276,36 +276,43 @@ def _oz_status(*args):
 
 
 @pytest.mark.parametrize("args,status", [
-    ((8, 8, 8, 1, 0, 0), 0),                 # bf16 slices
-    ((8, 8, 8, 2, 0, 0), 0),                 # e4m3 slices
-    ((8, 8, 8, 0, 0, 0), 2),                 # fp16 is not a slice format here
-    ((8, 8, 8, 3, 0, 0), 2),
-    ((-1, 8, 8, 1, 0, 0), 1),
-    ((8, 8, 8, 1, 20, 0), 0),
-    ((8, 8, 8, 1, 21, 0), 2),                # at most 20 slices
-    ((8, 8, 8, 1, -1, 0), 2),
-    ((8, 8, 8, 1, 0, -2), 2),
-    ((8, 8, 2 ** 22, 1, 0, 0), 0),           # one bit per slice left
-    ((8, 8, 2 ** 22 + 1, 1, 0, 0), 2),
-    ((8, 2 ** 23, 8, 1, 0, 0), 2),
-    ((0, 0, 0, 1, 0, 0), 0),
+    ((8, 8, 8, 1, 0, 0, 0), 0),              # bf16 slices
+    ((8, 8, 8, 2, 0, 0, 0), 0),              # e4m3 slices
+    ((8, 8, 8, 0, 0, 0, 0), 2),              # fp16 is not a slice format here
+    ((8, 8, 8, 3, 0, 0, 0), 2),
+    ((-1, 8, 8, 1, 0, 0, 0), 1),
+    ((8, 8, 8, 1, 20, 0, 0), 0),
+    ((8, 8, 8, 1, 21, 0, 0), 2),             # at most 20 slices
+    ((8, 8, 8, 1, -1, 0, 0), 2),
+    ((8, 8, 8, 1, 0, -2, 0), 2),
+    ((8, 8, 8, 1, 0, 0, 128), 0),
+    ((8, 8, 8, 1, 0, 0, 100), 2),            # chunks are multiples of 128
+    ((8, 8, 8, 1, 0, 0, -128), 2),
+    ((8, 8, 8, 1, 0, 0, 2 ** 22), 0),        # one bit per slice left
+    ((8, 8, 8, 1, 0, 0, 2 ** 22 + 128), 2),
+    ((8, 8, 2 ** 22 - 16, 1, 0, 0, 0), 0),   # chunks keep the chain short for any K ...
+    ((8, 8, 2 ** 24 - 16, 2, 0, 0, 0), 0),
+    ((8, 8, 2 ** 23, 1, 0, 0, 0), 2),        # ... up to the tile's 32-bit offsets
+    ((8, 2 ** 23, 8, 1, 0, 0, 0), 2),
+    ((0, 0, 0, 1, 0, 0, 0), 0),
 ])
 def test_ozaki_plan_validation(args, status):
     assert _oz_status(*args) == status
 
 
 @pytest.mark.parametrize("K", [1, 15, 256, 257, 1000, 4096, 16384, 131072, 2 ** 22])
-@pytest.mark.parametrize("t2", ["bf16", "e4m3"])
-def test_ozaki_plan_matches_oracle_parameters_for_any_M(K, t2):
+@pytest.mark.parametrize("t2,kc", [("bf16", 0), ("e4m3", 0), ("bf16", 1024), ("bf16", K_ALL := 2 ** 22),
+                                   ("e4m3", 128)])
+def test_ozaki_plan_matches_oracle_parameters_for_any_M(K, t2, kc):
     from oracle import ozaki as OZ
-    P = OZ.params(K, t2)
+    P = OZ.params(K, t2, kc=kc)
     ref = None
     for M in (1, 100, 4097):
-        i = imm.ozaki_plan(M, 200, K, t2).info
-        got = (i["rho"], i["bits"], i["delta"], i["slices"], i["d"], i["pairs"], i["k_pad"],
-               i["n_pad"], i["tile_m"], i["tile_n"])
-        assert got[:6] == (P.rho, P.b, P.delta, P.s, P.d, len(P.pairs))
-        assert got[6] % 16 == 0 and K <= got[6] < K + 16 and got[7] == 208
+        i = imm.ozaki_plan(M, 200, K, t2, chunk=kc).info
+        got = (i["rho"], i["bits"], i["delta"], i["slices"], i["d"], i["pairs"], i["chunk"],
+               i["k_pad"], i["n_pad"], i["tile_m"], i["tile_n"])
+        assert got[:7] == (P.rho, P.b, P.delta, P.s, P.d, len(P.pairs), P.kc)
+        assert got[7] % 16 == 0 and K <= got[7] < K + 16 and got[8] == 208
         ref = ref or got
         assert got == ref                    # nothing but the grid depends on M
 
