@@ -108,7 +108,14 @@ typedef enum {
    * batch-invariant operators the Tencent article lists in its closing
    * section).  Only the DMA tiles (256x256, 64x256, 32x256) read this layout;
    * the bits of C are those of the [K, N] layout holding the same values. */
-  GEMM_PLAN_B_TRANSPOSED = 1
+  GEMM_PLAN_B_TRANSPOSED = 1,
+  /* gemm_run / gemm_run_bias with the 256x256 tile launch at most one
+   * workgroup per compute unit, each walking the tiles of the one-tile-per-
+   * workgroup grid in the same raster order, with its LDS pipeline running
+   * on from one tile into the next (the persistent batch-invariant matmul of
+   * the Tencent article's closing section).  The bits of C are those of the
+   * plan without the flag; other tiles and the split-K path ignore it. */
+  GEMM_PLAN_PERSISTENT = 2
 } gemm_plan_flags;
 
 typedef struct gemm_plan_s* gemm_plan_t;

@@ -23,7 +23,7 @@ __all__ = [
     "GemmError", "Plan", "PlanInfo", "gemm_plan", "gemm_plan_ex", "gemm_plan_ex2",
     "gemm_plan_info", "gemm_workspace_size", "gemm_plan_tile_of", "gemm_run", "gemm_splitk_run",
     "gemm_plan_destroy", "gemm_status_string", "gemm_last_hip_error", "mm", "lib", "LIB_PATH",
-    "DTYPE", "TILE", "STATUS", "EXPORTED_SYMBOLS", "PLAN_B_TRANSPOSED",
+    "DTYPE", "TILE", "STATUS", "EXPORTED_SYMBOLS", "PLAN_B_TRANSPOSED", "PLAN_PERSISTENT",
     "OzakiPlan", "ozaki_plan", "ozaki_plan_info", "ozaki_workspace_size", "ozaki_split",
     "ozaki_multiply", "ozaki_run", "ozaki_mm",
 ]
@@ -36,6 +36,7 @@ DTYPE = {"f16": 0, "bf16": 1, "e4m3": 2, "e5m2": 3, "f32": 4}
 TILE = {"default": 0, "256x256": 1, "128x128": 2, "32x128": 3, "256x256_rs": 4, "32x256": 5,
         "64x256": 6}
 PLAN_B_TRANSPOSED = 1
+PLAN_PERSISTENT = 2
 EXPORTED_SYMBOLS = (
     "gemm_plan", "gemm_plan_ex", "gemm_plan_ex2", "gemm_plan_info", "gemm_workspace_size",
     "gemm_plan_tile_of", "gemm_run", "gemm_run_bias", "gemm_splitk_run", "gemm_splitk_run_bias",

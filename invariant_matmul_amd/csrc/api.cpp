@@ -220,7 +220,7 @@ gemm_status gemm_plan_ex2(int64_t M, int64_t N, int64_t K, gemm_dtype in, gemm_d
   if (split_k < 0 || split_k > kMaxSplit || group_m < 0) return GEMM_ERR_UNSUPPORTED;
   if (tile < GEMM_TILE_DEFAULT || tile > GEMM_TILE_64x256) return GEMM_ERR_UNSUPPORTED;
   if (!std::isfinite(scale_a) || !std::isfinite(scale_b)) return GEMM_ERR_UNSUPPORTED;
-  if (flags & ~(unsigned)GEMM_PLAN_B_TRANSPOSED) return GEMM_ERR_UNSUPPORTED;
+  if (flags & ~(unsigned)(GEMM_PLAN_B_TRANSPOSED | GEMM_PLAN_PERSISTENT)) return GEMM_ERR_UNSUPPORTED;
   const bool bt = (flags & GEMM_PLAN_B_TRANSPOSED) != 0;
   // 16-byte vector access of every row of A and B needs K and N to be
   // multiples of 16 bytes' worth of elements.
@@ -236,6 +236,7 @@ gemm_status gemm_plan_ex2(int64_t M, int64_t N, int64_t K, gemm_dtype in, gemm_d
   p->in = in;
   p->out = out;
   p->b_trans = bt;
+  p->persistent = (flags & GEMM_PLAN_PERSISTENT) != 0;
   int split_tile = tile == GEMM_TILE_DEFAULT ? default_tile(N, K, eb) : tile;
   // Transposed B runs on the DMA tiles only; its decode-like default is the
   // 32-row DMA tile.
@@ -347,7 +348,24 @@ gemm_status gemm_run_bias(gemm_plan_t p, const void* A, const void* B, const flo
   if (e != hipSuccess) return hip_fail(e);
   GemmArgs a = make_args(p, A, B, C, false);
   a.bias = bias;
-  e = launch_gemm(*p, p->run_tile, a, false, static_cast<hipStream_t>(stream));
+  // The persistent kernel evaluates the raster in 32-bit arithmetic.
+  const bool raster32 = a.grid < INT_MAX && a.group_m * a.tiles_n < INT_MAX;
+  if (p->persistent && p->run_tile == GEMM_TILE_256x256 && p->K > 0 && raster32) {
+    // One workgroup per compute unit (a multiple of 8, the XCD count, so
+    // that every virtual workgroup stays on the XCD the raster assigns it);
+    // the device query only places work, it never changes a bit.
+    int dev = 0, cus = 0;
+    e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return hip_fail(e);
+    PersistArgs pa;
+    static_cast<GemmArgs&>(pa) = a;
+    const int64_t slots = cus >= 8 ? cus / 8 * 8 : 8;
+    pa.wgs = a.grid < slots ? a.grid : slots;
+    e = launch_gemm_persist(*p, pa, static_cast<hipStream_t>(stream));
+  } else {
+    e = launch_gemm(*p, p->run_tile, a, false, static_cast<hipStream_t>(stream));
+  }
   if (e != hipSuccess) return hip_fail(e);
   return GEMM_OK;
 }

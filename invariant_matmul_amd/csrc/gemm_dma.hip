@@ -63,7 +63,15 @@ constexpr int TBN = 256;  // tile columns (every configuration)
 //     the end the row and column exponents are applied and fp64 C is stored.
 //     The LDS ring runs on across pair boundaries (the stage sequence is
 //     pair-major).
-enum { MODE_STORE = 0, MODE_SLICE = 1, MODE_OZAKI = 2 };
+//   MODE_PERSIST: MODE_STORE with a grid of at most one workgroup per compute
+//     unit: workgroup b computes the tiles of virtual workgroups b, b + wgs,
+//     b + 2 wgs, ... of the one-tile-per-workgroup raster (the persistent
+//     batch-invariant kernel of the Tencent article's closing section).  The
+//     LDS ring runs on across tiles, so the next tile's first stages load
+//     while the current one finishes and stores.  Each output element still
+//     gets the same instruction chain from +0 in the same K order, so the
+//     bits are those of MODE_STORE.
+enum { MODE_STORE = 0, MODE_SLICE = 1, MODE_OZAKI = 2, MODE_PERSIST = 3 };
 
 // Position in the Ozaki stage sequence: slice pair (p, q) -- p ascending,
 // then q ascending with q < min(s, d - p) (Fast Mode skips p + q >= d) --
@@ -186,13 +194,29 @@ __global__ __launch_bounds__(256 * WM, (waves_per_simd<TBM, WM, NS>())) void gem
 
   int64_t ksl, pm, pn;
   raster_tile(blockIdx.x, g.grid, g.tiles_m, g.tiles_n, g.group_m, &ksl, &pm, &pn);
-  const int64_t m0 = pm * TBM, n0 = pn * TBN;
+  const int64_t m0 = pm * TBM, n0 = pn * TBN;  // first (MODE_PERSIST) or only tile
   const int64_t kbeg = ksl * g.k_per_split;
   const int64_t kend = (g.K < kbeg + g.k_per_split) ? g.K : kbeg + g.k_per_split;
   // stages of one K pass; the Ozaki mode makes one pass per slice pair
   const int ntp = kend > kbeg ? (int)((kend - kbeg + BKE - 1) / BKE) : 0;
   int nt = ntp;
   if constexpr (MODE == MODE_OZAKI) nt = ntp * g.npairs;
+  // tiles of this workgroup (MODE_PERSIST): virtual ids blockIdx.x + j * wgs
+  int ntiles = 1;
+  if constexpr (MODE == MODE_PERSIST) {
+    ntiles = (int)((g.grid - blockIdx.x + g.wgs - 1) / g.wgs);
+    nt = ntp * ntiles;
+  }
+  // origin of tile j of this workgroup
+  auto tile_origin = [&](int j, int64_t* tm0, int64_t* tn0) {
+    if constexpr (MODE == MODE_PERSIST) {
+      uint32_t pm_, pn_;
+      raster_tile32(blockIdx.x + (uint32_t)j * (uint32_t)g.wgs, (uint32_t)g.grid,
+                    (uint32_t)g.tiles_m, (uint32_t)g.tiles_n, (uint32_t)g.group_m, &pm_, &pn_);
+      *tm0 = (int64_t)pm_ * TBM;
+      *tn0 = (int64_t)pn_ * TBN;
+    }
+  };
   const char* A = static_cast<const char*>(g.A);
   const char* B = static_cast<const char*>(g.B);
 
@@ -201,7 +225,10 @@ __global__ __launch_bounds__(256 * WM, (waves_per_simd<TBM, WM, NS>())) void gem
 
   // ---- DMA geometry of this lane (the same for every stage).  Offsets of
   // rows past M / columns past N are replaced by an out-of-range offset once;
-  // the K check only matters in a partial stage.
+  // the K check only matters in a partial stage.  MODE_PERSIST changes tiles,
+  // so there the row / column checks are made per transfer, against bit
+  // masks of the stage's tile (tile_masks).
+  constexpr bool PER_TILE = MODE == MODE_PERSIST;
   unsigned a_off[DA], b_off[DB];
   int a_kel[DA], b_k[DB];
 #pragma unroll
@@ -209,7 +236,7 @@ __global__ __launch_bounds__(256 * WM, (waves_per_simd<TBM, WM, NS>())) void gem
     const int idx = w * DA + i;
     const int row = AROWS_PER_DMA * idx + lane / ACH;
     const int c = (lane % ACH) ^ aswz(row);
-    a_off[i] = (m0 + row < g.M) ? (unsigned)(row * g.K * EB + c * 16) : OOB;
+    a_off[i] = (PER_TILE || m0 + row < g.M) ? (unsigned)(row * g.K * EB + c * 16) : OOB;
     a_kel[i] = c * (16 / EB);
   }
 #pragma unroll
@@ -219,21 +246,46 @@ __global__ __launch_bounds__(256 * WM, (waves_per_simd<TBM, WM, NS>())) void gem
       // row n of B^T (column n of B), laid out like a row of A
       const int row = AROWS_PER_DMA * idx + lane / ACH;
       const int c = (lane % ACH) ^ aswz(row);
-      b_off[i] = (n0 + row < g.N) ? (unsigned)(row * g.K * EB + c * 16) : OOB;
+      b_off[i] = (PER_TILE || n0 + row < g.N) ? (unsigned)(row * g.K * EB + c * 16) : OOB;
       b_k[i] = c * (16 / EB);  // first K element of the chunk
     } else {
       const int k = BROWS_PER_DMA * idx + lane / BSLOTS;
       const int s = lane % BSLOTS;
       const int cb = EB == 2 ? (s ^ ((k & 3) << 2)) : (s ^ ((k & 7) << 1));
-      b_off[i] = (n0 + cb * (16 / EB) < g.N) ? (unsigned)(k * g.N * EB + cb * 16) : OOB;
+      b_off[i] = (PER_TILE || n0 + cb * (16 / EB) < g.N) ? (unsigned)(k * g.N * EB + cb * 16) : OOB;
       b_k[i] = k;  // K row of the chunk
     }
   }
+  // MODE_PERSIST: bit i set if this lane's A (B) transfer i of a stage of the
+  // tile at (tm0, tn0) lies inside M (N); recomputed from the lane index once
+  // per tile, so no per-transfer row or column is kept in registers.
+  auto tile_masks = [&](int64_t tm0, int64_t tn0, unsigned* am, unsigned* bm) {
+    *am = 0;
+    *bm = 0;
+#pragma unroll
+    for (int i = 0; i < DA; ++i) {
+      const int row = AROWS_PER_DMA * (w * DA + i) + lane / ACH;
+      *am |= (unsigned)(tm0 + row < g.M) << i;
+    }
+#pragma unroll
+    for (int i = 0; i < DB; ++i) {
+      int col;
+      if constexpr (BT) {
+        col = AROWS_PER_DMA * (w * DB + i) + lane / ACH;
+      } else {
+        const int k = BROWS_PER_DMA * (w * DB + i) + lane / BSLOTS;
+        const int sl = lane % BSLOTS;
+        col = (EB == 2 ? (sl ^ ((k & 3) << 2)) : (sl ^ ((k & 7) << 1))) * (16 / EB);
+      }
+      *bm |= (unsigned)(tn0 + col < g.N) << i;
+    }
+  };
 
   struct StageSrc {
     const char* pa;  // first byte of the stage's A block (row m0)
     const char* pb;  // first byte of the stage's B block (column n0)
     int rem;         // K elements of this stage inside the slice (BKE for a full stage)
+    unsigned amask, bmask;  // MODE_PERSIST: transfers inside M / N (tile_masks)
   };
   auto stage_src = [&](int t) {
     StageSrc q;
@@ -243,15 +295,38 @@ __global__ __launch_bounds__(256 * WM, (waves_per_simd<TBM, WM, NS>())) void gem
     q.rem = kend - kst < BKE ? (int)(kend - kst) : BKE;
     return q;
   };
-  // Ozaki mode: the stages are requested strictly in sequence (prologue, then
-  // one refill per stage), so the source of the next one comes from a cursor;
-  // past the last pair it is a zero fill.
+  // Ozaki and persistent modes: the stages are requested strictly in
+  // sequence (prologue, then one refill per stage), so the source of the next
+  // one comes from a cursor; past the last pair / tile it is a zero fill.
   OzCursor pf;
+  int pf_tile = 0, pf_kt = 0;
+  int64_t pf_m0 = m0, pf_n0 = n0;
+  unsigned pf_am = 0, pf_bm = 0;
+  if constexpr (PER_TILE) tile_masks(m0, n0, &pf_am, &pf_bm);
   auto next_src = [&]() {
     StageSrc q;
     q.pa = A;
     q.pb = B;
     q.rem = 0;
+    q.amask = 0;
+    q.bmask = 0;
+    if constexpr (MODE == MODE_PERSIST) {
+      if (pf_tile < ntiles) {
+        const int64_t kst = (int64_t)pf_kt * BKE;
+        q.pa = A + (pf_m0 * g.K + kst) * EB;
+        q.pb = BT ? B + (pf_n0 * g.K + kst) * EB : B + (kst * g.N + pf_n0) * EB;
+        q.rem = g.K - kst < BKE ? (int)(g.K - kst) : BKE;
+        q.amask = pf_am;
+        q.bmask = pf_bm;
+        if (++pf_kt == ntp) {
+          pf_kt = 0;
+          if (++pf_tile < ntiles) {
+            tile_origin(pf_tile, &pf_m0, &pf_n0);
+            tile_masks(pf_m0, pf_n0, &pf_am, &pf_bm);
+          }
+        }
+      }
+    }
     if constexpr (MODE == MODE_OZAKI) {
       if (pf.live(g.slices)) {
         const int64_t kst = (int64_t)pf.kt * BKE;
@@ -267,13 +342,17 @@ __global__ __launch_bounds__(256 * WM, (waves_per_simd<TBM, WM, NS>())) void gem
   // else B rows.
   auto dma_one = [&](const StageSrc& q, int t, int x) {
     if (x < DA) {
-      const unsigned off = a_kel[x] < q.rem ? a_off[x] : OOB;
+      bool ok = a_kel[x] < q.rem;
+      if constexpr (PER_TILE) ok = ok && ((q.amask >> x) & 1u);
+      const unsigned off = ok ? a_off[x] : OOB;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           __builtin_amdgcn_make_buffer_rsrc((void*)q.pa, 0, NREC, RSRC_FLAGS),
           IMM_LDS(lds + a_slot(t) + (w * DA + x) * 1024), 16, off, 0, 0, 0);
     } else {
       const int i = x - DA;
-      const unsigned off = b_k[i] < q.rem ? b_off[i] : OOB;
+      bool ok = b_k[i] < q.rem;
+      if constexpr (PER_TILE) ok = ok && ((q.bmask >> i) & 1u);
+      const unsigned off = ok ? b_off[i] : OOB;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           __builtin_amdgcn_make_buffer_rsrc((void*)q.pb, 0, NREC, RSRC_FLAGS),
           IMM_LDS(lds + b_slot(t) + (w * DB + i) * 1024), 16, off, 0, 0, 0);
@@ -408,6 +487,42 @@ __global__ __launch_bounds__(256 * WM, (waves_per_simd<TBM, WM, NS>())) void gem
     }
   };
 
+  // Write-back of the tile at (tm0, tn0).  32x32 accumulator layout: lane l,
+  // register r holds row 8*(r/4) + 4*(l/32) + r%4, column l%32 of the block.
+  auto store_tile = [&](int64_t tm0, int64_t tn0) {
+    // Inside the stage loop (MODE_PERSIST) the per-element offsets below are
+    // loop-invariant; opaque lane bases keep the compiler from hoisting them
+    // out of the loop (where they would sit in registers or scratch).
+    int lrow = wm * WTM + 4 * h, lcol = wn * WTN + l32;
+    if constexpr (PER_TILE) asm volatile("" : "+v"(lrow), "+v"(lcol));
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int64_t col = tn0 + lcol + j * 32;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int64_t row = tm0 + lrow + i * 32 + 8 * (r >> 2) + (r & 3);
+          if constexpr (MODE == MODE_OZAKI) {
+            // C = 2^(ea[row] + eb[col]) * sum: the same bits as scaling every
+            // pair's term by its full exponent while no value leaves fp64's
+            // normal range
+            if (row < g.M && col < g.n_out)
+              static_cast<double*>(g.C)[row * g.ldc + col] =
+                  ldexp(acc64[i][j][r], g.ea[row] + g.eb[col]);
+          } else if (row < g.M && col < g.N) {
+            const float v = acc[i][j][r];
+            if constexpr (MODE == MODE_SLICE) {
+              static_cast<float*>(g.C)[(ksl * g.M + row) * g.N + col] = v;
+            } else {
+              store_final<OUT>(g.C, row * g.N + col, v, g.scale, g.bias, col);
+            }
+          }
+        }
+      }
+    }
+  };
+
   // Issue order.  Stages are requested whole (A rows, then B rows) in
   // ascending stage index: the prologue requests stages 0 .. NS-1, every
   // refill stage t+NS.  Before stage t+1 is used, the NS - 2 stages after it
@@ -418,7 +533,7 @@ __global__ __launch_bounds__(256 * WM, (waves_per_simd<TBM, WM, NS>())) void gem
   Frag<IN, FM, FN> F0, F1;
   if (nt > 0) {
     for (int p = 0; p < NS; ++p) {
-      const StageSrc q = MODE == MODE_OZAKI ? next_src() : stage_src(p);
+      const StageSrc q = (MODE == MODE_OZAKI || PER_TILE) ? next_src() : stage_src(p);
 #pragma unroll
       for (int x = 0; x < DPW; ++x) dma_one(q, p, x);
     }
@@ -450,7 +565,7 @@ __global__ __launch_bounds__(256 * WM, (waves_per_simd<TBM, WM, NS>())) void gem
   auto kstep = [&](bool refill, const Frag<IN, FM, FN>& Fc, int t, Frag<IN, FM, FN>& Fn, int tr,
                    int ks) {
     StageSrc q;
-    if constexpr (MODE == MODE_OZAKI) {
+    if constexpr (MODE == MODE_OZAKI || PER_TILE) {
       if (refill) q = next_src();
     } else {
       q = stage_src(t + NS);
@@ -473,6 +588,8 @@ __global__ __launch_bounds__(256 * WM, (waves_per_simd<TBM, WM, NS>())) void gem
   OzCursor cur;      // Ozaki mode: the pair and stage being computed
   int chunk_left = 0;
   if constexpr (MODE == MODE_OZAKI) chunk_left = g.chunk_stages;
+  int cur_tile = 0, cur_kt = 0;  // MODE_PERSIST: the tile and stage being computed
+  int64_t cur_m0 = m0, cur_n0 = n0;
   for (int t = 0; t < nt; ++t) {
 #pragma unroll
     for (int ks = 0; ks + 1 < KS; ++ks) {
@@ -493,39 +610,24 @@ __global__ __launch_bounds__(256 * WM, (waves_per_simd<TBM, WM, NS>())) void gem
         chunk_left = g.chunk_stages;
       }
     }
+    if constexpr (PER_TILE) {
+      // End of a tile: store it while the next tile's first stages load, and
+      // start the next one from +0.
+      if (++cur_kt == ntp) {
+        cur_kt = 0;
+        store_tile(cur_m0, cur_n0);
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{};
+        if (++cur_tile < ntiles) tile_origin(cur_tile, &cur_m0, &cur_n0);
+      }
+    }
   }
   // No LDS transfer or read may still be in flight when the workgroup ends.
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   __builtin_amdgcn_s_waitcnt(lgkmcnt_imm(0));
-
-  // Write-back.  32x32 accumulator layout: lane l, register r holds
-  // row 8*(r/4) + 4*(l/32) + r%4, column l%32 of the block.
-#pragma unroll
-  for (int i = 0; i < FM; ++i) {
-#pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int64_t col = n0 + wn * WTN + j * 32 + l32;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t row = m0 + wm * WTM + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-        if constexpr (MODE == MODE_OZAKI) {
-          // C = 2^(ea[row] + eb[col]) * sum: the same bits as scaling every
-          // pair's term by its full exponent while no value leaves fp64's
-          // normal range
-          if (row < g.M && col < g.n_out)
-            static_cast<double*>(g.C)[row * g.ldc + col] =
-                ldexp(acc64[i][j][r], g.ea[row] + g.eb[col]);
-        } else if (row < g.M && col < g.N) {
-          const float v = acc[i][j][r];
-          if constexpr (MODE == MODE_SLICE) {
-            static_cast<float*>(g.C)[(ksl * g.M + row) * g.N + col] = v;
-          } else {
-            store_final<OUT>(g.C, row * g.N + col, v, g.scale, g.bias, col);
-          }
-        }
-      }
-    }
-  }
+  if constexpr (!PER_TILE) store_tile(m0, n0);
 }
 
 template <int IN, int TBM, int WM, int NS, bool BT>
@@ -544,6 +646,27 @@ hipError_t launch_cfg(const gemm_plan_s& p, const GemmArgs& a, bool slice, hipSt
     hipLaunchKernelGGL((gemm_dma_kernel<IN, GEMM_BF16, MODE_STORE, TBM, WM, NS, BT, GemmArgs>), grid,
                        block, 0, s, a);
   return hipGetLastError();
+}
+
+// Persistent single pass on the 256 x 256 tile.
+template <int IN, bool BT>
+hipError_t launch_persist_in(const gemm_plan_s& p, const PersistArgs& a, hipStream_t s) {
+  const dim3 grid((unsigned)a.wgs), block(512);
+  if (p.out == GEMM_F32)
+    hipLaunchKernelGGL((gemm_dma_kernel<IN, GEMM_F32, MODE_PERSIST, 256, 2, 2, BT, PersistArgs>),
+                       grid, block, 0, s, a);
+  else if (p.out == GEMM_F16)
+    hipLaunchKernelGGL((gemm_dma_kernel<IN, GEMM_F16, MODE_PERSIST, 256, 2, 2, BT, PersistArgs>),
+                       grid, block, 0, s, a);
+  else
+    hipLaunchKernelGGL((gemm_dma_kernel<IN, GEMM_BF16, MODE_PERSIST, 256, 2, 2, BT, PersistArgs>),
+                       grid, block, 0, s, a);
+  return hipGetLastError();
+}
+
+template <int IN>
+hipError_t launch_persist_bt(const gemm_plan_s& p, const PersistArgs& a, hipStream_t s) {
+  return p.b_trans ? launch_persist_in<IN, true>(p, a, s) : launch_persist_in<IN, false>(p, a, s);
 }
 
 template <int IN, bool BT>
@@ -581,6 +704,16 @@ hipError_t launch_ozaki_gemm(int type2, const OzGemmArgs& a, hipStream_t s) {
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
+}
+
+hipError_t launch_gemm_persist(const gemm_plan_s& p, const PersistArgs& a, hipStream_t s) {
+  switch (p.in) {
+    case GEMM_F16: return launch_persist_bt<GEMM_F16>(p, a, s);
+    case GEMM_BF16: return launch_persist_bt<GEMM_BF16>(p, a, s);
+    case GEMM_F8_E4M3: return launch_persist_bt<GEMM_F8_E4M3>(p, a, s);
+    case GEMM_F8_E5M2: return launch_persist_bt<GEMM_F8_E5M2>(p, a, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_gemm_dma(const gemm_plan_s& p, int tile, const GemmArgs& a, bool slice_mode,

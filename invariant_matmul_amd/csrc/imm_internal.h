@@ -47,6 +47,7 @@ struct gemm_plan_s {
   int run_waves_m, run_waves_n;
   int64_t run_tiles_m, run_tiles_n;
   bool b_trans;         // B is given as [N, K] row-major (DMA tiles only)
+  bool persistent;      // gemm_run: at most one workgroup per compute unit
   int group_m;
   int split_k;          // slices actually used (after rounding)
   int64_t k_per_split;  // elements, multiple of bk
@@ -85,6 +86,27 @@ __host__ __device__ inline void raster_tile(int64_t w, int64_t G, int64_t tiles_
   *pid_n = in_group / gm;
 }
 
+// The same mapping in 32-bit arithmetic for grids without a K split
+// (k_slice = 0) and fewer than 2^31 workgroups: cheap enough to evaluate once
+// per tile inside a kernel's main loop (64-bit divisions expand into long
+// vector-ALU sequences there).
+__host__ __device__ inline void raster_tile32(uint32_t w, uint32_t G, uint32_t tiles_m,
+                                              uint32_t tiles_n, uint32_t group_m, uint32_t* pid_m,
+                                              uint32_t* pid_n) {
+  const uint32_t per = G / 8, rem = G % 8;
+  const uint32_t x = w % 8, loc = w / 8;
+  const uint32_t t = (x < rem) ? x * (per + 1) + loc : rem * (per + 1) + (x - rem) * per + loc;
+  const uint32_t width = group_m * tiles_n;
+  const uint32_t grp = t / width;
+  const uint32_t first_m = grp * group_m;
+  const uint32_t rows_left = tiles_m - first_m;
+  const uint32_t gm = rows_left < group_m ? rows_left : group_m;
+  const uint32_t in_group = t - grp * width;
+  const uint32_t q = in_group / gm;
+  *pid_m = first_m + (in_group - q * gm);
+  *pid_n = q;
+}
+
 // Kernel arguments (passed by value).
 struct GemmArgs {
   const void* A;
@@ -113,6 +135,12 @@ struct OzGemmArgs : GemmArgs {
   int32_t chunk_stages;  // K stages per exact fp32 chain
 };
 
+// Arguments of the persistent single pass: `grid` (and tiles_m, tiles_n)
+// describe the one-tile-per-workgroup raster, `wgs` the workgroups launched.
+struct PersistArgs : GemmArgs {
+  int64_t wgs;
+};
+
 struct ReduceArgs {
   const float* ws;
   void* C;
@@ -132,6 +160,8 @@ hipError_t launch_reduce(const gemm_plan_s& p, const ReduceArgs& a, hipStream_t 
 // The DMA-fed kernels (gemm_dma.hip); launch_gemm forwards the DMA tiles to it.
 hipError_t launch_gemm_dma(const gemm_plan_s& p, int tile, const GemmArgs& a, bool slice_mode,
                            hipStream_t s);
+// The persistent single pass on the 256 x 256 DMA tile (gemm_dma.hip).
+hipError_t launch_gemm_persist(const gemm_plan_s& p, const PersistArgs& a, hipStream_t s);
 // The Ozaki slice-pair product on the DMA kernel (gemm_dma.hip); type2 is
 // GEMM_BF16 or GEMM_F8_E4M3.  Output tile oz_tile_m(type2) x 256.
 constexpr int kOzTileN = 256;

@@ -174,7 +174,9 @@ def _plan2_status(*args):
 @pytest.mark.parametrize("args,status", [
     ((8, 8, 8, 0, 4, 0, 0, 0, 1.0, 1.0, 0), 0),
     ((8, 8, 8, 0, 4, 0, 0, 0, 1.0, 1.0, 1), 0),            # B given as [N, K]
-    ((8, 8, 8, 0, 4, 0, 0, 0, 1.0, 1.0, 2), 2),            # unknown flag bit
+    ((8, 8, 8, 0, 4, 0, 0, 0, 1.0, 1.0, 2), 0),            # persistent single pass
+    ((8, 8, 8, 0, 4, 0, 0, 0, 1.0, 1.0, 3), 0),
+    ((8, 8, 8, 0, 4, 0, 0, 0, 1.0, 1.0, 4), 2),            # unknown flag bit
     ((8, 8, 8, 0, 4, 0, 0, 3, 1.0, 1.0, 1), 2),            # transposed B needs a DMA tile
     ((8, 8, 8, 0, 4, 0, 0, 5, 1.0, 1.0, 1), 0),
     ((8, 8, 2 ** 24, 0, 4, 0, 0, 0, 1.0, 1.0, 1), 2),      # DMA offsets would overflow
