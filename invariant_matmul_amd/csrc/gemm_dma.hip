@@ -691,15 +691,17 @@ hipError_t launch_ozaki_gemm(int type2, const OzGemmArgs& a, hipStream_t s) {
   static_assert(kOzTileN == TBN, "Ozaki tile");
   // The fp64 sums (two registers per element) must sit in architectural
   // VGPRs, at most 256 per wave.  bf16: a 128 x 256 tile of 8 waves (two per
-  // SIMD) of 64 x 64, 253 VGPRs.  fp8 fragments are twice as wide and spill
-  // there, so e4m3 runs a 64 x 256 tile of 4 waves (one per SIMD) of 64 x 64,
-  // with its fp32 accumulators in AGPRs and a 3-stage ring.
+  // SIMD) of 64 x 64, 253 VGPRs, 3-stage ring (144 KB).  fp8 fragments are
+  // twice as wide and spill there, so e4m3 runs a 64 x 256 tile of 4 waves
+  // (one per SIMD) of 64 x 64, with its fp32 accumulators in AGPRs and a
+  // 4-stage ring (160 KB).  The small tiles are fill-bound: the deeper rings
+  // measured 7-10 % faster than 2 and 3 stages.
   const dim3 grid((unsigned)a.grid);
   if (type2 == GEMM_BF16)
-    hipLaunchKernelGGL((gemm_dma_kernel<GEMM_BF16, GEMM_F32, MODE_OZAKI, 128, 2, 2, false,
+    hipLaunchKernelGGL((gemm_dma_kernel<GEMM_BF16, GEMM_F32, MODE_OZAKI, 128, 2, 3, false,
                                         OzGemmArgs>), grid, dim3(512), 0, s, a);
   else if (type2 == GEMM_F8_E4M3)
-    hipLaunchKernelGGL((gemm_dma_kernel<GEMM_F8_E4M3, GEMM_F32, MODE_OZAKI, 64, 1, 3, false,
+    hipLaunchKernelGGL((gemm_dma_kernel<GEMM_F8_E4M3, GEMM_F32, MODE_OZAKI, 64, 1, 4, false,
                                         OzGemmArgs>), grid, dim3(256), 0, s, a);
   else
     return hipErrorInvalidValue;
