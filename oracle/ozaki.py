@@ -10,7 +10,9 @@ Source: Insight Edge blog on cuTile Python, sections "å€ç²¾åº¦è¡Œåˆ—ç©ã‚¨ãƒŸãƒ
 "Fused Split Kernelï¼ˆåˆ†å‰²ã®èåˆï¼‰").  Notation follows the page: Type1 is the
 fp64 input (53 significand bits), Type2 the narrow slice format (bf16: 8,
 fp8 e4m3: 4 significand bits, hidden bit included), Type3 the fp32 accumulator
-of the matrix unit (24 bits).
+of the matrix unit (24 bits).  A third Type2, int8, is the matrix unit's
+integer format: its Type3 is the int32 accumulator (31 bits), and a slice
+entry n * 2^-b with |n| <= 2^b fits int8 for b <= 6, so m_Type2 = 6.
 
 What is computed, in the page's order:
 
@@ -74,7 +76,8 @@ import numpy as np
 
 from . import decode, round_rne
 
-TYPE2_BITS = {"bf16": 8, "e4m3": 4}   # significand bits, hidden bit included
+TYPE2_BITS = {"bf16": 8, "e4m3": 4, "i8": 6}   # bits of a slice entry's magnitude
+TYPE3_BITS = {"bf16": 24, "e4m3": 24, "i8": 31}  # fp32 / int32 accumulator
 M_TYPE1 = 53
 M_TYPE3 = 24
 MAX_SLICES = 20   # the page's split routine stops after at most 20 slices
@@ -96,20 +99,20 @@ class OzakiParams:
         return pair_list(self.s, self.d)
 
 
-def gamma_of(K: int) -> int:
-    """gamma = ceil(53 - (24 - log2 K) / 2), evaluated exactly: the smallest
-    integer g with K * 4^(53 - g) <= 2^24."""
+def gamma_of(K: int, m3: int = M_TYPE3) -> int:
+    """gamma = ceil(53 - (m3 - log2 K) / 2), evaluated exactly: the smallest
+    integer g with K * 4^(53 - g) <= 2^m3 (m3 = 24 for fp32 accumulation)."""
     if K < 1:
         raise ValueError("K must be positive")
     g = 0
-    while K * 4 ** (M_TYPE1 - g) > 2 ** M_TYPE3:
+    while K * 4 ** (M_TYPE1 - g) > 2 ** m3:
         g += 1
     return g
 
 
 def default_chunk(type2: str) -> int:
-    """Longest exact fp32 chain at full Type2 precision: 2^(24 - 2 m_Type2)."""
-    return 2 ** (M_TYPE3 - 2 * TYPE2_BITS[type2])
+    """Longest exact chain at full Type2 precision: 2^(m_Type3 - 2 m_Type2)."""
+    return 2 ** (TYPE3_BITS[type2] - 2 * TYPE2_BITS[type2])
 
 
 def params(K: int, type2: str = "bf16", s: int = 0, d: int = 0, kc: int = 0) -> OzakiParams:
@@ -119,7 +122,7 @@ def params(K: int, type2: str = "bf16", s: int = 0, d: int = 0, kc: int = 0) -> 
         raise ValueError(f"unsupported Type2 {type2!r}")
     kc = kc or default_chunk(type2)
     xi = M_TYPE1 - TYPE2_BITS[type2]
-    rho = max(gamma_of(max(1, min(K, kc))), xi)
+    rho = max(gamma_of(max(1, min(K, kc)), TYPE3_BITS[type2]), xi)
     b = M_TYPE1 - rho
     if b < 1:
         raise ValueError(f"K = {K} leaves no bits per slice")
@@ -160,12 +163,20 @@ def split(x: np.ndarray, axis: int, P: OzakiParams):
         sigma = np.ldexp(0.75, P.rho + cp)             # (2)
         v = (r + sigma) - sigma                         # (3)
         r = r - v                                       # (4)
-        out.append(round_rne(P.type2, np.ldexp(v, -cp)))  # (5)
+        if P.type2 == "i8":                             # (5), as the integer n
+            n = np.ldexp(v, P.b - cp)
+            if not (np.all(n == np.round(n)) and np.all(np.abs(n) <= 2 ** P.b)):
+                raise ValueError("an int8 slice entry is not an integer in [-2^b, 2^b]")
+            out.append(n.astype(np.int8))
+        else:
+            out.append(round_rne(P.type2, np.ldexp(v, -cp)))  # (5)
     return np.stack(out), c0
 
 
 def slice_ints(slices_bits: np.ndarray, P: OzakiParams) -> np.ndarray:
-    """Integer values n = slice * 2^b of decoded slices (as fp64)."""
+    """Integer values n = slice * 2^b of the slices (as fp64)."""
+    if P.type2 == "i8":
+        return slices_bits.astype(np.float64)
     return np.ldexp(decode(P.type2, slices_bits), P.b)
 
 

@@ -63,6 +63,9 @@ def pin_pair_counts(oz=OZ):
     for K in (1024, 2048, 4096, 8192, 16384):
         P = oz.params(K, "bf16")
         assert (P.s, P.d, len(P.pairs)) == (7, 9, 39)
+    # int8 slices: 6 bits each, exact in int32 up to chains of 2^19 products
+    P = oz.params(16384, "i8")
+    assert (P.b, P.kc, P.s, P.d, len(P.pairs)) == (6, 2 ** 19, 9, 11, 60)
 
 
 def pin_gamma_formula(oz=OZ):
@@ -76,13 +79,19 @@ def pin_gamma_formula(oz=OZ):
     # k is the length of one exact chain: the whole K when it is one chunk
     assert oz.params(16384, "bf16", kc=16384).rho == 48
     assert oz.params(16384, "bf16").rho == 45 and oz.params(1000, "bf16", kc=4096).rho == 46
+    # int32 accumulation: gamma = ceil(53 - (31 - log2 k) / 2)
+    for K in (1, 1000, 2 ** 19, 2 ** 21):
+        assert oz.gamma_of(K, 31) == math.ceil(53 - (31 - math.log2(K)) / 2)
 
 
 def pin_slices_are_type2_on_grid(oz=OZ):
     x = _rng(1).standard_normal((9, 70)) * np.ldexp(1.0, _rng(2).integers(-30, 30, (9, 1)))
-    for t2 in ("bf16", "e4m3"):
+    for t2 in ("bf16", "e4m3", "i8"):
         P = oz.params(70, t2)
         sl, c0 = oz.split(x, 1, P)
+        if t2 == "i8":
+            assert sl.dtype == np.int8 and np.all(np.abs(sl.astype(int)) <= 2 ** P.b)
+            continue
         vals = oracle.decode(t2, sl)
         n = np.ldexp(vals, P.b)
         assert np.all(n == np.round(n)) and np.all(np.abs(n) <= 2 ** P.b)
@@ -100,10 +109,10 @@ def pin_split_reconstructs(oz=OZ):
     r = _rng(3)
     x = r.uniform(0.25, 1.0, (6, 40)) * r.choice([-1.0, 1.0], (6, 40))
     x *= np.ldexp(1.0, r.integers(-40, 40, (6, 1)))
-    for t2 in ("bf16", "e4m3"):
+    for t2 in ("bf16", "e4m3", "i8"):
         P = oz.params(40, t2)
         sl, c0 = oz.split(x, 1, P)
-        vals = oracle.decode(t2, sl)
+        vals = np.ldexp(oz.slice_ints(sl, P), -P.b)
         for i in range(x.shape[0]):
             for k in range(x.shape[1]):
                 terms = [math.ldexp(vals[p, i, k], int(c0[i]) - p * P.delta) for p in range(P.s)]
@@ -135,7 +144,8 @@ def pin_integer_inputs_exact(oz=OZ):
     A = r.integers(-2 ** 20, 2 ** 20, (7, 64))
     B = r.integers(-2 ** 20, 2 ** 20, (64, 5))
     want = A.astype(object) @ B.astype(object)
-    for t2, kc in (("bf16", 0), ("e4m3", 0), ("bf16", 16), ("e4m3", 24), ("bf16", 64)):
+    for t2, kc in (("bf16", 0), ("e4m3", 0), ("i8", 0), ("bf16", 16), ("e4m3", 24), ("bf16", 64),
+                   ("i8", 40)):
         C = oz.gemm(A.astype(np.float64), B.astype(np.float64), t2, kc=kc)
         assert C.shape == (7, 5)
         assert all(int(C[i, j]) == want[i, j] and C[i, j] == float(want[i, j])
@@ -146,7 +156,7 @@ def pin_identity(oz=OZ):
     r = _rng(6)
     A = r.uniform(0.5, 1.0, (5, 48)) * r.choice([-1.0, 1.0], (5, 48)) * 4.0
     eye = np.eye(48)
-    for t2 in ("bf16", "e4m3"):
+    for t2 in ("bf16", "e4m3", "i8"):
         assert np.array_equal(oz.gemm(A, eye, t2).view(np.uint64), A.view(np.uint64))
         assert np.array_equal(oz.gemm(eye, A.T.copy(), t2), A.T)
 
@@ -167,6 +177,8 @@ def pin_rows_independent(oz=OZ):
     B = r.standard_normal((40, 6))
     C = oz.gemm(A, B, "e4m3")
     assert np.array_equal(oz.gemm(A[3:5], B, "e4m3"), C[3:5])
+    Ci = oz.gemm(A, B, "i8")
+    assert np.array_equal(oz.gemm(A[[8, 2]], B, "i8"), Ci[[8, 2]])
     assert np.array_equal(oz.gemm(A[[7, 0]], B, "e4m3"), C[[7, 0]])
     assert np.array_equal(oz.gemm(A, B[:, 2:5], "e4m3"), C[:, 2:5])
 
@@ -194,7 +206,7 @@ def _rigorous_bound(oz, A, B, P, chunks=1):
 def pin_random_vs_exact(oz=OZ):
     r = _rng(9)
     for t2, (M, K, N), kc in (("bf16", (4, 96, 3), 0), ("e4m3", (3, 70, 4), 0),
-                              ("bf16", (3, 100, 3), 32)):
+                              ("bf16", (3, 100, 3), 32), ("i8", (3, 90, 3), 0)):
         A = r.uniform(-1.0, 1.0, (M, K))
         B = r.uniform(-1.0, 1.0, (K, N))
         C = oz.gemm(A, B, t2, kc=kc)
@@ -289,11 +301,14 @@ MUTANTS = [
      "c0 = ceil_log2(np.max(np.abs(x)) + 0 * np.max(np.abs(x), axis=axis))"),
     ("delta_too_small", "return OzakiParams(type2, int(K), rho, b, b + 1, int(s), int(d), int(kc))",
      "return OzakiParams(type2, int(K), rho, b, b - 1, int(s), int(d), int(kc))"),
-    ("gamma_without_log", "while K * 4 ** (M_TYPE1 - g) > 2 ** M_TYPE3:",
-     "while 4 ** (M_TYPE1 - g) > 2 ** M_TYPE3:"),
+    ("gamma_without_log", "while K * 4 ** (M_TYPE1 - g) > 2 ** m3:",
+     "while 4 ** (M_TYPE1 - g) > 2 ** m3:"),
+    ("int8_accumulates_in_fp32", "rho = max(gamma_of(max(1, min(K, kc)), TYPE3_BITS[type2]), xi)",
+     "rho = max(gamma_of(max(1, min(K, kc))), xi)"),
     ("ceil_log2_floor", "c = np.where(mant == 0.5, e - 1, e)", "c = e - 1"),
     ("first_chunk_dropped", "for k0 in range(0, K, P.kc):", "for k0 in range(P.kc, K, P.kc):"),
-    ("chunk_rho_from_K", "rho = max(gamma_of(max(1, min(K, kc))), xi)", "rho = max(gamma_of(max(1, kc)), xi)"),
+    ("chunk_rho_from_K", "rho = max(gamma_of(max(1, min(K, kc)), TYPE3_BITS[type2]), xi)",
+     "rho = max(gamma_of(max(1, kc), TYPE3_BITS[type2]), xi)"),
     ("first_slice_dropped", "for p in range(P.s):\n        cp =",
      "for p in range(P.s):\n        if p == 0: r = r - ((r + np.ldexp(0.75, P.rho + c0.reshape(shape))) - np.ldexp(0.75, P.rho + c0.reshape(shape)))\n        cp ="),
 ]
