@@ -34,7 +34,7 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-PEAK_TFLOPS = {"f16": 2516.6, "bf16": 2516.6, "e4m3": 5033.2, "e5m2": 5033.2}
+PEAK_TFLOPS = {"f16": 2516.6, "bf16": 2516.6, "e4m3": 5033.2, "e5m2": 5033.2, "i8": 5033.2}
 PEAK_HBM_GBS = 8000.0
 MALL_BYTES = 256 * 2 ** 20
 KERNEL_SOURCES = [os.path.join(ROOT, "invariant_matmul_amd", "csrc", f)
@@ -354,9 +354,9 @@ def main():
         # split 0 = the plan's default for this shape
         extra["hugek_f16"] = [bench_splitk("hugek_f16", s, torch, imm, wl) for s in (1, 8, 32, 128, 0)]
         torch.cuda.empty_cache()
-        log("fp64 by the Ozaki scheme (bf16 and e4m3 slices)")
+        log("fp64 by the Ozaki scheme (bf16, e4m3 and int8 slices)")
         extra["ozaki_f64"] = [bench_ozaki(f"ozaki_{t2}_{n}", torch, imm, wl)
-                              for t2 in ("bf16", "e4m3") for n in (4096, 8192, 16384)]
+                              for t2 in ("bf16", "e4m3", "i8") for n in (4096, 8192, 16384)]
         A, B = host[0], host[1]
     else:
         A, B = host[0], host[1]

@@ -83,7 +83,8 @@ typedef enum {
   GEMM_BF16 = 1,
   GEMM_F8_E4M3 = 2,
   GEMM_F8_E5M2 = 3,
-  GEMM_F32 = 4
+  GEMM_F32 = 4,
+  GEMM_I8 = 5   /* int8, as Ozaki-scheme slices only (ozaki_plan) */
 } gemm_dtype;
 
 /* Output-tile shapes (rows x columns of C per workgroup).  All tiles of one
@@ -210,11 +211,12 @@ void gemm_plan_destroy(gemm_plan_t plan);
 
 /* ---------------------------------------------------------------------------
  * fp64 matrix product by the Ozaki scheme: C = A x B with A [M,K], B [K,N]
- * and C [M,N] in fp64 (row-major, contiguous), computed on the fp32-
- * accumulating matrix cores from low-precision slices.  Insight Edge blog on
+ * and C [M,N] in fp64 (row-major, contiguous), computed on the matrix cores
+ * from low-precision slices: bf16 or fp8 e4m3 with fp32 accumulation, or
+ * int8 with int32 accumulation.  Insight Edge blog on
  * cuTile Python, section "倍精度行列積エミュレーション":
  *   split ("分解(Split)", equations (1)-(5)): every row of A and every column
- *     of B is cut into `slices` Type2 slices (bf16 or fp8 e4m3) with
+ *     of B is cut into `slices` Type2 slices (bf16, fp8 e4m3 or int8) with
  *     c0 = ceil(log2 max|x|) of that row / column, c_p = c0 - p*delta,
  *     sigma = 0.75*2^(rho+c_p), v = (x+sigma)-sigma, x -= v,
  *     slice_p = Type2(v*2^-c_p);
@@ -226,17 +228,20 @@ void gemm_plan_destroy(gemm_plan_t plan);
  * product of every chunk is added to the fp64 sum in ascending chunk order
  * (the page's exactness argument in "最適化後の結果" is per K tile).
  * Precision parameter ("分解(Split)"): rho = max(gamma, xi),
- * gamma = ceil(53 - (24 - log2 k)/2), xi = 53 - m_Type2 (m = 8 for bf16, 4 for
- * e4m3), with k = min(K, chunk) the length of one fp32 chain.  A slice
+ * gamma = ceil(53 - (m_Type3 - log2 k)/2), xi = 53 - m_Type2 (m_Type2 = 8 for
+ * bf16, 4 for e4m3, 6 for int8 -- an int8 entry n * 2^-b needs |n| <= 2^b <=
+ * 127; m_Type3 = 24 for fp32, 31 for int32 accumulation), with k = min(K,
+ * chunk) the length of one accumulation chain.  A slice
  * carries b = 53 - rho bits, so every fp32 chunk product is exact and the
  * result does not depend on any summation order inside the matrix cores: it
  * is a bitwise function of row i of A, of B, of K and of (type2, slices, d,
  * chunk).  delta = b + 1.
- * Defaults: chunk = 2^(24 - 2 m_Type2), the longest exact chain with all of
- * Type2's bits (256 for bf16, 65536 for e4m3); slices = min(ceil(53 / b), 20)
- * (7 for bf16, 14 for e4m3; 20 is the most the page's split routine makes),
+ * Defaults: chunk = 2^(m_Type3 - 2 m_Type2), the longest exact chain with
+ * all of Type2's bits (256 for bf16, 65536 for e4m3, 2^19 for int8);
+ * slices = min(ceil(53 / b), 20) (7 for bf16, 14 for e4m3, 9 for int8; 20 is
+ * the most the page's split routine makes),
  * d = slices + 2 (39 products for 7 bf16 slices, 130 for 14 e4m3 slices, the
- * page's "最適化後の結果" tables).
+ * page's "最適化後の結果" tables; 60 for 9 int8 slices).
  * Domain: finite inputs whose nonzero row / column maxima lie in
  * [2^-300, 2^300].  There every slice value, scaled term and partial sum is
  * a normal fp64 number, so the kernel may apply 2^(c0(row) + c0(column)) once
@@ -257,7 +262,7 @@ typedef struct ozaki_plan_s* ozaki_plan_t;
 
 typedef struct {
   int64_t M, N, K;
-  int32_t type2;              /* GEMM_BF16 or GEMM_F8_E4M3 */
+  int32_t type2;              /* GEMM_BF16, GEMM_F8_E4M3 or GEMM_I8 */
   int32_t rho, bits, delta;   /* precision parameter, bits per slice, exponent step */
   int32_t slices, d, pairs;   /* slices per operand, Fast Mode threshold, products */
   int64_t chunk;              /* products per exact fp32 chain */
@@ -268,10 +273,11 @@ typedef struct {
   uint64_t a_slices_offset, b_slices_offset, a_exp_offset, b_exp_offset, scratch_offset;
 } ozaki_plan_info_t;
 
-/* Plan an Ozaki-scheme product.  type2: GEMM_BF16 or GEMM_F8_E4M3.
+/* Plan an Ozaki-scheme product.  type2: GEMM_BF16, GEMM_F8_E4M3 or GEMM_I8.
  * slices: 0 = default, else 1..20; d: 0 = default, else >= 1; chunk: 0 =
  * default, else a multiple of 128 (at most 2^22).  M, N, K >= 0; K below 2^23
- * (bf16) or 2^25 (e4m3), N below 2^23 (32-bit offsets inside one tile).
+ * (bf16), 2^25 (e4m3) or 2^24 (int8), N below 2^23 (32-bit offsets inside one
+ * tile).
  * Errors: GEMM_ERR_INVALID_VALUE (negative size, NULL
  * handle), GEMM_ERR_UNSUPPORTED (other type2, slices, d or chunk out of range,
  * sizes too large). */

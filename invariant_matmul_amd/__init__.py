@@ -32,7 +32,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libinvarian
 
 STATUS = {0: "GEMM_OK", 1: "GEMM_ERR_INVALID_VALUE", 2: "GEMM_ERR_UNSUPPORTED",
           3: "GEMM_ERR_WORKSPACE", 4: "GEMM_ERR_HIP"}
-DTYPE = {"f16": 0, "bf16": 1, "e4m3": 2, "e5m2": 3, "f32": 4}
+DTYPE = {"f16": 0, "bf16": 1, "e4m3": 2, "e5m2": 3, "f32": 4, "i8": 5}
 TILE = {"default": 0, "256x256": 1, "128x128": 2, "32x128": 3, "256x256_rs": 4, "32x256": 5,
         "64x256": 6}
 PLAN_B_TRANSPOSED = 1
@@ -341,8 +341,8 @@ class OzakiPlan:
 
 def ozaki_plan(M: int, N: int, K: int, type2="bf16", slices: int = 0, d: int = 0,
                chunk: int = 0) -> OzakiPlan:
-    """Plan C = A @ B in fp64 by the Ozaki scheme with Type2 slices ("bf16" or
-    "e4m3"); slices / d / chunk = 0 take the library's defaults."""
+    """Plan C = A @ B in fp64 by the Ozaki scheme with Type2 slices ("bf16",
+    "e4m3" or "i8"); slices / d / chunk = 0 take the library's defaults."""
     h = ctypes.c_void_p()
     _check(lib().ozaki_plan(M, N, K, _dtype_code(type2), int(slices), int(d), int(chunk),
                             ctypes.byref(h)), "ozaki_plan")

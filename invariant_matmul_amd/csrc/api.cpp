@@ -178,13 +178,14 @@ constexpr int64_t kOzColChunk = 256;  // rows per partial column maximum of B
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 bool aligned8(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 7u) == 0; }
 
-// Largest b with k * 4^b <= 2^24: the bits per slice for which a k-term fp32
-// sum of slice products is exact (gamma = 53 - b_max of the Insight Edge
-// blog's "分解(Split)" formula gamma = ceil(53 - (24 - log2 k) / 2)).
-int oz_exact_bits(int64_t k) {
+// Largest b with k * 4^b <= 2^m3: the bits per slice for which a k-term sum
+// of slice products is exact in an accumulator of m3 bits (24: fp32, 31:
+// int32); gamma = 53 - b_max of the Insight Edge blog's "分解(Split)" formula
+// gamma = ceil(53 - (m3 - log2 k) / 2).
+int oz_exact_bits(int64_t k, int m3) {
   if (k < 1) k = 1;
   int b = 0;
-  while (b < 12 && k * ((int64_t)1 << (2 * (b + 1))) <= ((int64_t)1 << 24)) ++b;
+  while (b < 16 && k * ((int64_t)1 << (2 * (b + 1))) <= ((int64_t)1 << m3)) ++b;
   return b;
 }
 
@@ -411,16 +412,18 @@ gemm_status ozaki_plan(int64_t M, int64_t N, int64_t K, gemm_dtype type2, int sl
   if (!plan) return GEMM_ERR_INVALID_VALUE;
   *plan = nullptr;
   if (M < 0 || N < 0 || K < 0) return GEMM_ERR_INVALID_VALUE;
-  if (type2 != GEMM_BF16 && type2 != GEMM_F8_E4M3) return GEMM_ERR_UNSUPPORTED;
+  if (type2 != GEMM_BF16 && type2 != GEMM_F8_E4M3 && type2 != GEMM_I8) return GEMM_ERR_UNSUPPORTED;
   if (slices < 0 || slices > kOzMaxSlices || d < 0) return GEMM_ERR_UNSUPPORTED;
   if (chunk < 0 || chunk % 128 != 0 || chunk > ((int64_t)1 << 22)) return GEMM_ERR_UNSUPPORTED;
   if (M > INT_MAX || K > INT_MAX || N >= ((int64_t)1 << 23)) return GEMM_ERR_UNSUPPORTED;
-  // rho = max(gamma, xi): b = min(exact bits of one chain, significand bits
-  // of Type2); the default chain is the longest that keeps all of Type2's
-  // bits, 2^(24 - 2 m_Type2)
-  const int m_type2 = type2 == GEMM_BF16 ? 8 : 4;
-  const int64_t kc = chunk ? chunk : ((int64_t)1 << (24 - 2 * m_type2));
-  const int bx = oz_exact_bits(K < kc ? K : kc);
+  // rho = max(gamma, xi): b = min(exact bits of one chain, bits of a Type2
+  // slice entry); the default chain is the longest that keeps all of
+  // Type2's bits, 2^(m_Type3 - 2 m_Type2).  int8 entries n with |n| <= 2^b
+  // need b <= 6; int8 products accumulate in int32 (31 bits).
+  const int m_type2 = type2 == GEMM_BF16 ? 8 : type2 == GEMM_I8 ? 6 : 4;
+  const int m_type3 = type2 == GEMM_I8 ? 31 : 24;
+  const int64_t kc = chunk ? chunk : ((int64_t)1 << (m_type3 - 2 * m_type2));
+  const int bx = oz_exact_bits(K < kc ? K : kc, m_type3);
   const int b = bx < m_type2 ? bx : m_type2;
   if (b < 1) return GEMM_ERR_UNSUPPORTED;
   ozaki_plan_s* p = new (std::nothrow) ozaki_plan_s();

@@ -119,6 +119,20 @@ __device__ __forceinline__ i32x2 tr16_rows(unsigned p0, int rows) {
     default: return ds_read_tr16_b64<52 * BROW>(p0);
   }
 }
+// int8 steps are 32 K rows: two reads of 8 rows per half-step
+template <int BROW>
+__device__ __forceinline__ i32x2 tr8_rows_k32(unsigned p0, int rows) {
+  switch (rows) {
+    case 0: return ds_read_tr8_b64<0>(p0);
+    case 8: return ds_read_tr8_b64<8 * BROW>(p0);
+    case 32: return ds_read_tr8_b64<32 * BROW>(p0);
+    case 40: return ds_read_tr8_b64<40 * BROW>(p0);
+    case 64: return ds_read_tr8_b64<64 * BROW>(p0);
+    case 72: return ds_read_tr8_b64<72 * BROW>(p0);
+    case 96: return ds_read_tr8_b64<96 * BROW>(p0);
+    default: return ds_read_tr8_b64<104 * BROW>(p0);
+  }
+}
 template <int BROW>
 __device__ __forceinline__ i32x2 tr8_rows(unsigned p0, int rows) {
   switch (rows) {
@@ -175,8 +189,9 @@ __global__ __launch_bounds__(256 * WM, (waves_per_simd<TBM, WM, NS>())) void gem
   constexpr int DPW = DA + DB;
   static_assert(DA * WAVES * 1024 == A_STAGE && DB * WAVES * 1024 == B_STAGE, "DMA split");
   static_assert(FM * 32 * WM == TBM, "tile rows");
-  constexpr int NRA = EB == 2 ? FM : 2 * FM; // fragment reads per k-step: A ...
-  constexpr int NRB = BT ? (EB == 2 ? FN : 2 * FN) : (EB == 2 ? 2 * FN : 4 * FN);  // ... and B
+  constexpr bool I8 = T::I8;                 // int8: 16-bit-like A reads, 8-bit B reads
+  constexpr int NRA = T::FRAG == 1 ? FM : 2 * FM;  // fragment reads per k-step: A ...
+  constexpr int NRB = BT ? (T::FRAG == 1 ? FN : 2 * FN) : (EB == 2 || I8 ? 2 * FN : 4 * FN);  // ... B
   constexpr int NREAD = NRA + NRB;
   constexpr int LDS_BYTES = NS * STAGE;
   static_assert(LDS_BYTES <= 160 * 1024, "LDS ring too large");
@@ -382,7 +397,7 @@ __global__ __launch_bounds__(256 * WM, (waves_per_simd<TBM, WM, NS>())) void gem
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
       const int n = wn * WTN + j * 32 + 16 * (grp & 1) + 8 * q;
-      const int k = 32 * (grp >> 1) + t_;
+      const int k = (I8 ? 16 : 32) * (grp >> 1) + t_;  // this lane half's K rows
       b_rd[j] = k * BROW + (((n >> 4) ^ (t_ << 1)) << 4) + q * 8;
     }
   }
@@ -400,6 +415,20 @@ __global__ __launch_bounds__(256 * WM, (waves_per_simd<TBM, WM, NS>())) void gem
   //   16-bit, 2j + half for fp8).
   auto read_one = [&](Frag<IN, FM, FN>& F, int as, int bs, int ks, int x) {
     const char* sb = lds + as;
+    if constexpr (I8 && !BT) {
+      // int8: A as for 16-bit inputs (one 16-byte slot per k-step half), B by
+      // two 8-bit transposing reads of 8 K rows each.
+      if (x < NRA) {
+        const int c = ks * 2 + h;
+        F.a[x] = *reinterpret_cast<const i32x4*>(sb + a_rd[x] + ((c ^ asw) << 4));
+      } else {
+        const int j = (x - NRA) >> 1, r = (x - NRA) & 1;
+        const i32x2 v = tr8_rows_k32<BROW>(lds_addr + bs + b_rd[j], ks * 32 + 8 * r);
+        F.b[j][2 * r] = v[0];
+        F.b[j][2 * r + 1] = v[1];
+      }
+      return;
+    }
     if constexpr (BT) {
       if (x >= NRA) {
         const char* sbb = lds + bs;
@@ -475,13 +504,22 @@ __global__ __launch_bounds__(256 * WM, (waves_per_simd<TBM, WM, NS>())) void gem
   // fp32 accumulators restart from +0.
   auto oz_flush = [&](int level) {
     if constexpr (MODE == MODE_OZAKI) {
-      const int sh = -level * g.delta;
+      // int8 slices hold the integers n of the entries n * 2^-b, so their
+      // int32 sums carry a further 2^-2b (b = delta - 1)
+      const int sh = -level * g.delta - (I8 ? 2 * (g.delta - 1) : 0);
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) acc64[i][j][r] += ldexp((double)acc[i][j][r], sh);
+          for (int r = 0; r < 16; ++r) {
+            // int8 slices accumulate in int32, held in the registers' bits (the
+            // element is copied out first: a bit cast of a vector element
+            // expression reads the vector's first element)
+            const float f = acc[i][j][r];
+            const double v = I8 ? (double)__float_as_int(f) : (double)f;
+            acc64[i][j][r] += ldexp(v, sh);
+          }
           acc[i][j] = f32x16{};
         }
     }
@@ -703,6 +741,9 @@ hipError_t launch_ozaki_gemm(int type2, const OzGemmArgs& a, hipStream_t s) {
   else if (type2 == GEMM_F8_E4M3)
     hipLaunchKernelGGL((gemm_dma_kernel<GEMM_F8_E4M3, GEMM_F32, MODE_OZAKI, 64, 1, 4, false,
                                         OzGemmArgs>), grid, dim3(256), 0, s, a);
+  else if (type2 == GEMM_I8)
+    hipLaunchKernelGGL((gemm_dma_kernel<GEMM_I8, GEMM_F32, MODE_OZAKI, 128, 2, 3, false,
+                                        OzGemmArgs>), grid, dim3(512), 0, s, a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

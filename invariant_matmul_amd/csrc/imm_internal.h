@@ -163,9 +163,9 @@ hipError_t launch_gemm_dma(const gemm_plan_s& p, int tile, const GemmArgs& a, bo
 // The persistent single pass on the 256 x 256 DMA tile (gemm_dma.hip).
 hipError_t launch_gemm_persist(const gemm_plan_s& p, const PersistArgs& a, hipStream_t s);
 // The Ozaki slice-pair product on the DMA kernel (gemm_dma.hip); type2 is
-// GEMM_BF16 or GEMM_F8_E4M3.  Output tile oz_tile_m(type2) x 256.
+// GEMM_BF16, GEMM_F8_E4M3 or GEMM_I8.  Output tile oz_tile_m(type2) x 256.
 constexpr int kOzTileN = 256;
-inline int oz_tile_m(int type2) { return type2 == GEMM_BF16 ? 128 : 64; }
+inline int oz_tile_m(int type2) { return type2 == GEMM_F8_E4M3 ? 64 : 128; }
 hipError_t launch_ozaki_gemm(int type2, const OzGemmArgs& a, hipStream_t s);
 // The Ozaki split (ozaki.hip): exponents of the rows of x [R, C] ...
 hipError_t launch_oz_row_exp(const double* x, int64_t R, int64_t C, int32_t* e, hipStream_t s);

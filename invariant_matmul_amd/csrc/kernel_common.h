@@ -16,6 +16,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x16 __attribute__((ext_vector_type(16)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -24,14 +25,16 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 template <int IN>
 struct InT {
-  static constexpr int EB = (IN == GEMM_F8_E4M3 || IN == GEMM_F8_E5M2) ? 1 : 2;
-  static constexpr int KSTEP_B = EB == 2 ? 32 : 64;  // bytes of K per MFMA (per row)
-  static constexpr int FRAG = KSTEP_B / 32;          // 16-byte pieces per lane per operand
+  static constexpr bool I8 = IN == GEMM_I8;  // int8 (Ozaki slices), int32 accumulators
+  static constexpr int EB = (IN == GEMM_F8_E4M3 || IN == GEMM_F8_E5M2 || I8) ? 1 : 2;
+  static constexpr int KSTEP_B = (EB == 2 || I8) ? 32 : 64;  // bytes of K per MFMA (per row)
+  static constexpr int FRAG = KSTEP_B / 32;                  // 16-byte pieces per lane per operand
 };
 
 // The one matrix-core step every kernel uses for an input dtype (the bits of
 // the product depend on this choice, [TDI] "Batch Invariance の由来", BLOCK_K
-// paragraph): a 32x32 output block, K = 16 (fp16/bf16) or 64 (fp8).  Lane l
+// paragraph): a 32x32 output block, K = 16 (fp16/bf16), 64 (fp8) or 32
+// (int8, int32 accumulators carried in the fp32 registers' bits).  Lane l
 // supplies row (l % 32) of A and column (l % 32) of B; its data are the K
 // elements [h*half, (h+1)*half) of the step, h = l / 32, in increasing k.
 template <int IN>
@@ -55,7 +58,7 @@ __device__ __forceinline__ f32x16 mfma(const i32x4* a, const i32x4* b, f32x16 c)
 // dwords (fp8) per lane, allocated as one register tuple.
 template <int IN>
 struct FragOf {
-  using type = typename std::conditional<InT<IN>::EB == 2, i32x4, i32x8>::type;
+  using type = typename std::conditional<InT<IN>::FRAG == 1, i32x4, i32x8>::type;
 };
 
 template <int IN>
@@ -67,6 +70,9 @@ __device__ __forceinline__ f32x16 mfma_v(const typename FragOf<IN>::type& a,
   } else if constexpr (IN == GEMM_BF16) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  } else if constexpr (IN == GEMM_I8) {
+    return __builtin_bit_cast(
+        f32x16, __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, __builtin_bit_cast(i32x16, c), 0, 0, 0));
   } else {
     constexpr int fmt = IN == GEMM_F8_E4M3 ? 0 : 1;
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, fmt, fmt, 0, 0, 0, 0);

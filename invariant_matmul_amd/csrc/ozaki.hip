@@ -17,7 +17,8 @@
 // delta = b + 1 the next slice again has |x| <= 2^c.  v * 2^-c_p is a
 // multiple of 2^-b in [-1, 1], exactly representable in the Type2 format
 // (b <= 8 for bf16, b <= 4 for e4m3), so the conversions below are exact bit
-// extractions.  All fp64 arithmetic is IEEE add/sub/ldexp, no contraction.
+// extractions; int8 slices store the integer n = v * 2^(b - c_p), |n| <= 2^b
+// with b <= 6.  All fp64 arithmetic is IEEE add/sub/ldexp, no contraction.
 //
 // Layouts: x is fp64 row-major [R, C]; the slices are [s, Ro, Co] row-major
 // with Ro >= R, Co >= C, Co a multiple of 8 (padding entries are zero).
@@ -110,8 +111,12 @@ __global__ __launch_bounds__(256) void oz_split_kernel(const double* x, int64_t 
       const double sigma = ldexp(0.75, rho + cp);  // (2)
       const double v = (xr[u] + sigma) - sigma;   // (3)
       xr[u] = xr[u] - v;                          // (4)
-      const float y = (float)ldexp(v, -cp);       // (5), exact
-      enc[u] = T2 == GEMM_BF16 ? enc_bf16(y) : enc_e4m3(y);
+      if constexpr (T2 == GEMM_I8) {
+        enc[u] = (unsigned)(int)ldexp(v, 53 - rho - cp) & 0xffu;  // (5) as the integer n
+      } else {
+        const float y = (float)ldexp(v, -cp);       // (5), exact
+        enc[u] = T2 == GEMM_BF16 ? enc_bf16(y) : enc_e4m3(y);
+      }
     }
     const int64_t idx = p * plane + r * Co + c0;
     if constexpr (T2 == GEMM_BF16) {
@@ -175,6 +180,13 @@ hipError_t launch_oz_split(int type2, bool per_row, const double* x, int64_t R, 
     else
       hipLaunchKernelGGL((oz_split_kernel<GEMM_F8_E4M3, false>), grid, block, 0, s, x, R, C, Ro, Co,
                          e, slices, rho, delta, out);
+  } else if (type2 == GEMM_I8) {
+    if (per_row)
+      hipLaunchKernelGGL((oz_split_kernel<GEMM_I8, true>), grid, block, 0, s, x, R, C, Ro, Co, e,
+                         slices, rho, delta, out);
+    else
+      hipLaunchKernelGGL((oz_split_kernel<GEMM_I8, false>), grid, block, 0, s, x, R, C, Ro, Co, e,
+                         slices, rho, delta, out);
   } else {
     return hipErrorInvalidValue;
   }

@@ -19,7 +19,8 @@ from tests.helpers import dev, log
 
 pytestmark = pytest.mark.gpu
 
-T2_VIEW = {"bf16": (torch.int16, np.uint16), "e4m3": (torch.uint8, np.uint8)}
+T2_VIEW = {"bf16": (torch.int16, np.uint16), "e4m3": (torch.uint8, np.uint8),
+           "i8": (torch.int8, np.int8)}
 
 
 def _inputs(M, N, K, kind, seed):
@@ -56,7 +57,7 @@ def _slices(ws, off, shape, t2):
     return raw.view(T2_VIEW[t2][1]).reshape(shape)
 
 
-@pytest.mark.parametrize("t2", ["bf16", "e4m3"])
+@pytest.mark.parametrize("t2", ["bf16", "e4m3", "i8"])
 def test_split_matches_oracle(t2):
     M, N, K = 70, 90, 150          # ragged: K and N padded to 16
     A, B = _inputs(M, N, K, "wide", 7100)
@@ -91,6 +92,11 @@ CASES = [
     ("e4m3", 70, 300, 260, "uniform", 5, 99),
     ("bf16", 1, 16, 4096, "uniform", 0, 0),
     ("e4m3", 2, 1, 1, "wide", 0, 0),
+    ("i8", 300, 600, 1000, "uniform", 0, 0),
+    ("i8", 129, 257, 200, "wide", 0, 0),
+    ("i8", 200, 300, 256, "int", 0, 0),
+    ("i8", 130, 270, 700, "uniform", 5, 4, 256),
+    ("i8", 1, 16, 4096, "wide", 0, 0),
 ]
 
 
@@ -113,7 +119,7 @@ def test_product_bit_exact(case):
         assert np.array_equal(C.cpu().numpy(), (A @ B).numpy())
 
 
-@pytest.mark.parametrize("t2", ["bf16", "e4m3"])
+@pytest.mark.parametrize("t2", ["bf16", "e4m3", "i8"])
 def test_rows_invariant_and_repeatable(t2):
     M, N, K = 257, 300, 700
     A, B = _inputs(M, N, K, "wide", 7300)
@@ -166,7 +172,7 @@ def test_edge_cases():
     torch.cuda.synchronize()
 
 
-@pytest.mark.parametrize("name", ["ozaki_bf16_8192", "ozaki_e4m3_8192"])
+@pytest.mark.parametrize("name", ["ozaki_bf16_8192", "ozaki_e4m3_8192", "ozaki_i8_8192"])
 def test_bench_size_sampled(name):
     """The configuration the benchmark times, checked on sampled elements."""
     w = wl.OZAKI_WORKLOADS[name]

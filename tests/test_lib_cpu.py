@@ -280,6 +280,7 @@ def _oz_status(*args):
 @pytest.mark.parametrize("args,status", [
     ((8, 8, 8, 1, 0, 0, 0), 0),              # bf16 slices
     ((8, 8, 8, 2, 0, 0, 0), 0),              # e4m3 slices
+    ((8, 8, 8, 5, 0, 0, 0), 0),              # int8 slices
     ((8, 8, 8, 0, 0, 0, 0), 2),              # fp16 is not a slice format here
     ((8, 8, 8, 3, 0, 0, 0), 2),
     ((-1, 8, 8, 1, 0, 0, 0), 1),
@@ -304,7 +305,7 @@ def test_ozaki_plan_validation(args, status):
 
 @pytest.mark.parametrize("K", [1, 15, 256, 257, 1000, 4096, 16384, 131072, 2 ** 22])
 @pytest.mark.parametrize("t2,kc", [("bf16", 0), ("e4m3", 0), ("bf16", 1024), ("bf16", K_ALL := 2 ** 22),
-                                   ("e4m3", 128)])
+                                   ("e4m3", 128), ("i8", 0), ("i8", 4096)])
 def test_ozaki_plan_matches_oracle_parameters_for_any_M(K, t2, kc):
     from oracle import ozaki as OZ
     P = OZ.params(K, t2, kc=kc)

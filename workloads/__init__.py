@@ -182,7 +182,7 @@ class OzakiWorkload:
 
 def _ozaki_registry():
     w = {}
-    for t, t2 in enumerate(("bf16", "e4m3")):
+    for t, t2 in enumerate(("bf16", "e4m3", "i8")):
         for i, n in enumerate((1024, 4096, 8192, 16384)):
             w[f"ozaki_{t2}_{n}"] = OzakiWorkload(f"ozaki_{t2}_{n}", n, t2, 6000 + 10 * t + i)
     return w
