@@ -235,16 +235,46 @@ def bench_ozaki(name, torch, imm, wl, n_iter=5, warmup=2):
            "multiply_matrix_TFLOPs": mfma_flops / (tm * 1e-3) / 1e12,
            "multiply_pct_mfma_peak": 100.0 * mfma_flops / (tm * 1e-3) / 1e12 /
            PEAK_TFLOPS[w.type2]}
-    del ws, C
     torch.cuda.empty_cache()
     try:
         ref = torch.empty((w.n, w.n), dtype=torch.float64, device="cuda")
         tper, _ = time_launches(lambda k: torch.matmul(Ad, Bd, out=ref), n_iter, warmup, torch)
         out["torch_matmul_f64_TFLOPs"] = w.flops / (statistics.median(tper) * 1e-3) / 1e12
+        # the page's accuracy figure: relative (Frobenius) error against the
+        # fp64 product (itself rounded, so ~1e-15 is the floor)
+        out["rel_error_vs_torch_f64"] = float(torch.linalg.norm(C - ref) / torch.linalg.norm(ref))
         del ref
     except Exception as e:  # comparator only
         out["torch_matmul_f64_error"] = str(e)
-    del Ad, Bd
+    del ws, C, Ad, Bd
+    torch.cuda.empty_cache()
+    return out
+
+
+def bench_ozaki_d_sweep(torch, imm, wl, n=8192, ds=(11, 9, 8, 7, 6, 5), type2s=("bf16", "i8")):
+    """Fast Mode trade-off: skipping the pairs with p + q >= d for smaller d,
+    time and relative error against torch's fp64 product (the page's
+    "dによる精度/速度トレードオフ" table runs d = 9 .. 5 at n = 16384)."""
+    w = wl.OZAKI_WORKLOADS[f"ozaki_bf16_{n}"]
+    A, B = w.make()
+    Ad, Bd = A.cuda(), B.cuda()
+    del A, B
+    ref = torch.matmul(Ad, Bd)
+    C = torch.empty_like(ref)
+    out = []
+    for t2 in type2s:
+        for d in ds:
+            plan = imm.ozaki_plan(n, n, n, t2, 0, d)
+            ws = torch.empty(imm.ozaki_workspace_size(plan), dtype=torch.uint8, device="cuda")
+            per, _ = time_launches(lambda k: imm.ozaki_run(plan, Ad, Bd, C, ws), 3, 1, torch)
+            med = statistics.median(per)
+            out.append({"type2": t2, "n": n, "d": plan.info["d"], "pairs": plan.info["pairs"],
+                        "total_ms": med, "fp64_TFLOPs": w.flops / (med * 1e-3) / 1e12,
+                        "rel_error_vs_torch_f64":
+                            float(torch.linalg.norm(C - ref) / torch.linalg.norm(ref))})
+            del ws
+            torch.cuda.empty_cache()
+    del Ad, Bd, ref, C
     torch.cuda.empty_cache()
     return out
 
@@ -357,6 +387,8 @@ def main():
         log("fp64 by the Ozaki scheme (bf16, e4m3 and int8 slices)")
         extra["ozaki_f64"] = [bench_ozaki(f"ozaki_{t2}_{n}", torch, imm, wl)
                               for t2 in ("bf16", "e4m3", "i8") for n in (4096, 8192, 16384)]
+        log("Ozaki Fast Mode d sweep at 8192")
+        extra["ozaki_d_sweep"] = bench_ozaki_d_sweep(torch, imm, wl)
         A, B = host[0], host[1]
     else:
         A, B = host[0], host[1]
