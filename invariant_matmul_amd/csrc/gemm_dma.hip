@@ -609,6 +609,10 @@ __global__ __launch_bounds__(256 * WM, (waves_per_simd<TBM, WM, NS>())) void gem
       q = stage_src(t + NS);
     }
     const int as = a_slot(tr), bs = b_slot(tr);
+    // A wave issuing its refill runs at raised priority, so its DMA goes out
+    // ahead of the other wave's MFMAs on the SIMD (measured about 1 % faster
+    // on the large tile; bits unchanged).
+    if (refill) __builtin_amdgcn_s_setprio(3);
 #pragma unroll
     for (int x = 0; x < NM; ++x) {
       mfma_x(Fc, x);
@@ -620,6 +624,7 @@ __global__ __launch_bounds__(256 * WM, (waves_per_simd<TBM, WM, NS>())) void gem
       for (int y = x * NREAD / NM; y < (x + 1) * NREAD / NM; ++y) read_one(Fn, as, bs, ks, y);
       fence();
     }
+    if (refill) __builtin_amdgcn_s_setprio(0);
   };
 
   // k-steps alternate between F0 and F1; KS is even, so every stage starts on F0
