@@ -190,3 +190,32 @@ def test_bench_size_sampled(name):
     exact = np.array([np.sum(A.numpy()[i] * B.numpy()[:, j]) for i, j in zip(ii, jj)])
     assert np.all(np.abs(got - exact) <= 2 * np.sqrt(w.n) * 2.0 ** -53 * ab.sum(axis=1)
                   + w.n * 2.0 ** -53 * ab.sum(axis=1))
+
+
+def _fuzz_cases(n=16, seed=7700):
+    r = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        t2 = ["bf16", "e4m3", "i8"][i % 3]
+        M, N, K = int(r.integers(1, 300)), int(r.integers(1, 600)), int(r.integers(1, 1500))
+        s = int(r.integers(1, 13)) if r.random() < 0.5 else 0
+        d = int(r.integers(1, 2 * max(s, 7))) if r.random() < 0.5 else 0
+        kc = 128 * int(r.integers(1, 9)) if r.random() < 0.4 else 0
+        kind = ["uniform", "wide", "int"][int(r.integers(0, 3))]
+        out.append((t2, M, N, K, kind, s, d, kc, 7800 + i))
+    return out
+
+
+@pytest.mark.parametrize("case", _fuzz_cases(), ids=lambda c: f"{c[0]}-{c[1]}x{c[2]}x{c[3]}-{c[4]}-s{c[5]}d{c[6]}c{c[7]}")
+def test_seeded_sweep_bit_exact(case):
+    """Random shapes, slice formats, slice counts, Fast Mode thresholds and
+    chunk lengths: every one bit-exact against the oracle."""
+    t2, M, N, K, kind, s, d, kc, seed = case
+    A, B = _inputs(M, N, K, kind, seed)
+    plan = imm.ozaki_plan(M, N, K, t2, s, d, kc)
+    log(f"sweep {case}: {plan.info['slices']} slices, {plan.info['pairs']} pairs, "
+        f"chunk {plan.info['chunk']}")
+    C, _ = _run(plan, A.to(dev()), B.to(dev()))
+    want = OZ.gemm(A.numpy(), B.numpy(), t2, s, d, kc)
+    bad = _bits64(C) != _bits64(want)
+    assert not bad.any(), f"{int(bad.sum())} of {bad.size} differ; first {np.argwhere(bad)[:3]}"
