@@ -173,7 +173,10 @@ GemmArgs make_args(const gemm_plan_s* p, const void* A, const void* B, void* out
 // ---- Ozaki scheme ----------------------------------------------------------
 
 constexpr int kOzMaxSlices = 20;  // as many as the page's split routine makes at most
-constexpr int64_t kOzColChunk = 256;  // rows per partial column maximum of B
+// Rows per partial column maximum of B: 256, more when K is so large that
+// the chunk count (the second grid dimension) would pass kOzMaxColChunks.
+constexpr int64_t kOzColChunk = 256;
+constexpr int64_t kOzMaxColChunks = 16384;
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 bool aligned8(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 7u) == 0; }
@@ -198,7 +201,7 @@ struct ozaki_plan_s {
   int64_t chunk;
   int64_t kp, np;
   int64_t tiles_m, tiles_n, grid;
-  int64_t col_chunks;
+  int64_t col_rows, col_chunks;
   size_t off_sa, off_sb, off_ea, off_eb, off_part, ws_bytes;
 };
 
@@ -452,7 +455,9 @@ gemm_status ozaki_plan(int64_t M, int64_t N, int64_t K, gemm_dtype type2, int sl
   p->tiles_m = ceil_div(M, oz_tile_m(type2));
   p->tiles_n = ceil_div(p->np, kOzTileN);
   p->grid = p->tiles_m * p->tiles_n;
-  p->col_chunks = ceil_div(K, kOzColChunk);
+  p->col_rows = kOzColChunk;
+  if (ceil_div(K, p->col_rows) > kOzMaxColChunks) p->col_rows = ceil_div(K, kOzMaxColChunks);
+  p->col_chunks = ceil_div(K, p->col_rows);
   const size_t sa = (size_t)p->slices * M * p->kp * p->eb;
   const size_t sb = (size_t)p->slices * p->kp * p->np * p->eb;
   p->off_sa = 0;
@@ -464,8 +469,12 @@ gemm_status ozaki_plan(int64_t M, int64_t N, int64_t K, gemm_dtype type2, int sl
   // DMA offsets of one A tile and one stage of B stay below 2^31, and so does
   // the kernel's stage count (stages per pair times pairs)
   const int64_t stages = ceil_div(p->kp, 128 / p->eb) * p->npairs;
+  // the split kernels run one thread per 8 slice entries of one operand
+  const int64_t split_a = ceil_div(M * p->kp, 8 * 256), split_b = ceil_div(p->kp * p->np, 8 * 256);
+  const int64_t split_blocks = split_a > split_b ? split_a : split_b;
   if (oz_tile_m(type2) * p->kp * p->eb >= ((int64_t)1 << 31) - 256 ||
-      p->grid * 512 >= ((int64_t)1 << 32) || stages >= ((int64_t)1 << 31)) {
+      p->grid * 512 >= ((int64_t)1 << 32) || stages >= ((int64_t)1 << 31) ||
+      split_blocks >= ((int64_t)1 << 31)) {
     delete p;
     return GEMM_ERR_UNSUPPORTED;
   }
@@ -522,7 +531,7 @@ gemm_status oz_split(ozaki_plan_t p, int operand, const double* x, void* ws, hip
                           p->delta, w + p->off_sa, s);
   } else {
     int32_t* eb = reinterpret_cast<int32_t*>(w + p->off_eb);
-    e = launch_oz_col_exp(x, p->K, p->N, kOzColChunk, reinterpret_cast<double*>(w + p->off_part),
+    e = launch_oz_col_exp(x, p->K, p->N, p->col_rows, reinterpret_cast<double*>(w + p->off_part),
                           eb, s);
     if (e == hipSuccess)
       e = launch_oz_split(p->type2, false, x, p->K, p->N, p->kp, p->np, eb, p->slices, p->rho,

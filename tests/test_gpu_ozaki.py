@@ -219,3 +219,13 @@ def test_seeded_sweep_bit_exact(case):
     want = OZ.gemm(A.numpy(), B.numpy(), t2, s, d, kc)
     bad = _bits64(C) != _bits64(want)
     assert not bad.any(), f"{int(bad.sum())} of {bad.size} differ; first {np.argwhere(bad)[:3]}"
+
+
+def test_long_K_wider_column_chunks():
+    """K beyond 16384 x 256: the column maxima of B use wider chunks."""
+    M, N, K = 1, 2, 16384 * 256 + 1000
+    A, B = _inputs(M, N, K, "wide", 7900)
+    plan = imm.ozaki_plan(M, N, K, "i8")
+    C, _ = _run(plan, A.to(dev()), B.to(dev()))
+    want = OZ.gemm(A.numpy(), B.numpy(), "i8")
+    assert np.array_equal(_bits64(C), _bits64(want))

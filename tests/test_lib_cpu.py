@@ -365,3 +365,15 @@ def test_ozaki_without_gpu_returns_hip_error():
     assert L.ozaki_run(p.handle, FAKE, FAKE, FAKE, FAKE, ws, None) == 4
     assert L.ozaki_split(p.handle, 0, FAKE, FAKE, ws, None) == 4
     assert L.ozaki_multiply(p.handle, FAKE, ws, FAKE, None) == 4
+
+
+def test_ozaki_column_maxima_chunks_are_capped():
+    # the column maxima of B run over at most 16384 chunks of K (the second
+    # grid dimension), wider chunks beyond that
+    for K, N in ((1000, 300), (2 ** 22, 64), (2 ** 24 + 16, 8)):
+        i = imm.ozaki_plan(8, N, K, "e4m3").info
+        scratch = i["workspace_bytes"] - i["scratch_offset"]
+        rows = 256 if -(-K // 256) <= 16384 else -(-K // 16384)
+        chunks = -(-K // rows)
+        assert chunks <= 16384
+        assert chunks * N * 8 <= scratch <= -(-(16384 * N * 8) // 256) * 256
