@@ -201,12 +201,17 @@ def bench_m_sweep(torch, imm, wl, N=6144, K=4096, ms=(1, 16, 64, 256, 1024, 4096
         plan = imm.gemm_plan(m, N, K, "f16")
         C = torch.empty((m, N), dtype=torch.float32, device="cuda")
         per, _ = time_launches(lambda i: imm.gemm_run(plan, a, B, C), 20, 5, torch)
+        # the same bits with the tile taken from M (GEMM_PLAN_TILE_BY_M)
+        mplan = imm.gemm_plan_ex2(m, N, K, "f16", "f32", flags=imm.PLAN_TILE_BY_M)
+        mper, _ = time_launches(lambda i: imm.gemm_run(mplan, a, B, C), 20, 5, torch)
         ref = torch.empty((m, N), dtype=torch.float16, device="cuda")
         tper, _ = time_launches(lambda i: torch.matmul(a, B, out=ref), 20, 5, torch)
-        med, tmed = statistics.median(per), statistics.median(tper)
+        med, mmed, tmed = statistics.median(per), statistics.median(mper), statistics.median(tper)
         out.append({"M": m, "N": N, "K": K,
                     "tile": f"{plan.info['run_block_m']}x{plan.info['run_block_n']}",
                     "median_us": med * 1e3, "TFLOPs": 2.0 * m * N * K / (med * 1e-3) / 1e12,
+                    "tile_by_m": f"{mplan.info['run_block_m']}x{mplan.info['run_block_n']}",
+                    "tile_by_m_median_us": mmed * 1e3,
                     "torch_matmul_median_us": tmed * 1e3,
                     "torch_matmul_TFLOPs": 2.0 * m * N * K / (tmed * 1e-3) / 1e12})
     return out
@@ -369,9 +374,14 @@ def main():
                                      PEAK_TFLOPS["e5m2"]}
         torch.cuda.empty_cache()
         for n in ("square_f16_4096", "square_f16_1024"):
-            wn, _, pn, _, _ = bench_square(n, 50, 10, torch, imm, wl)
+            wn, _, pn, _, hn = bench_square(n, 50, 10, torch, imm, wl)
             medn = statistics.median(pn)
             extra[n] = {**summary(pn), "TFLOPs": wn.flops / (medn * 1e-3) / 1e12}
+            mp = imm.gemm_plan_ex2(wn.M, wn.N, wn.K, wn.dtype, wn.out, flags=imm.PLAN_TILE_BY_M)
+            Cn = torch.empty((wn.M, wn.N), dtype=torch.float32, device="cuda")
+            pm, _ = time_launches(lambda i: imm.gemm_run(mp, hn[2], hn[3], Cn), 50, 10, torch)
+            extra[n]["tile_by_m_TFLOPs"] = wn.flops / (statistics.median(pm) * 1e-3) / 1e12
+            del hn, Cn
             torch.cuda.empty_cache()
         log("decode bf16 N=4096 K=14336, split-K path")
         extra["decode_bf16"] = [bench_splitk("decode_bf16_m128", 0, torch, imm, wl, M=m)

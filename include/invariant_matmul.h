@@ -116,7 +116,15 @@ typedef enum {
    * on from one tile into the next (the persistent batch-invariant matmul of
    * the Tencent article's closing section).  The bits of C are those of the
    * plan without the flag; other tiles and the split-K path ignore it. */
-  GEMM_PLAN_PERSISTENT = 2
+  GEMM_PLAN_PERSISTENT = 2,
+  /* gemm_run / gemm_run_bias take their tile from the workgroups each DMA
+   * tile would give at this M (256x256 if at least 192, else 64x256 if at
+   * least 192, else 32x256) instead of from (N, K, dtype).  Every tile uses
+   * the same matrix-core instruction and K order, so C is bitwise that of the
+   * plan without the flag for every M (tile sizes do not change bits: the
+   * Tencent article, "Batch Invariance の由来"); only the time changes.  An
+   * explicit tile or the split-K path ignore it. */
+  GEMM_PLAN_TILE_BY_M = 4
 } gemm_plan_flags;
 
 typedef struct gemm_plan_s* gemm_plan_t;

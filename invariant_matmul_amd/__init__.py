@@ -24,6 +24,7 @@ __all__ = [
     "gemm_plan_info", "gemm_workspace_size", "gemm_plan_tile_of", "gemm_run", "gemm_splitk_run",
     "gemm_plan_destroy", "gemm_status_string", "gemm_last_hip_error", "mm", "lib", "LIB_PATH",
     "DTYPE", "TILE", "STATUS", "EXPORTED_SYMBOLS", "PLAN_B_TRANSPOSED", "PLAN_PERSISTENT",
+    "PLAN_TILE_BY_M",
     "OzakiPlan", "ozaki_plan", "ozaki_plan_info", "ozaki_workspace_size", "ozaki_split",
     "ozaki_multiply", "ozaki_run", "ozaki_mm",
 ]
@@ -37,6 +38,7 @@ TILE = {"default": 0, "256x256": 1, "128x128": 2, "32x128": 3, "256x256_rs": 4, 
         "64x256": 6}
 PLAN_B_TRANSPOSED = 1
 PLAN_PERSISTENT = 2
+PLAN_TILE_BY_M = 4
 EXPORTED_SYMBOLS = (
     "gemm_plan", "gemm_plan_ex", "gemm_plan_ex2", "gemm_plan_info", "gemm_workspace_size",
     "gemm_plan_tile_of", "gemm_run", "gemm_run_bias", "gemm_splitk_run", "gemm_splitk_run_bias",

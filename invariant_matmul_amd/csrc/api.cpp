@@ -8,7 +8,11 @@
 // "Batch Invariance の由来" concludes that a configuration which changes the
 // K step or the split of K with the batch size is what breaks batch
 // invariance, and [TDI] "演算子チューニング" describes exactly such M-driven
-// tile and split heuristics; this planner never reads M for any decision.
+// tile and split heuristics; by default this planner never reads M for any
+// decision.  The one exception is opt-in and bits-neutral: with
+// GEMM_PLAN_TILE_BY_M the single pass takes its output tile from M, which
+// [TDI] "Batch Invariance の由来" shows does not change bits (and every tile
+// here uses the same instruction and K order).
 #include <hip/hip_runtime.h>
 
 #include <climits>
@@ -73,6 +77,18 @@ int default_run_tile(int64_t N, int64_t K, int eb) {
   if (small_b(N, K, eb)) return GEMM_TILE_32x256;
   if (reduction_dominated(N, K) && N <= 512) return GEMM_TILE_64x256;
   return GEMM_TILE_256x256;
+}
+
+// GEMM_PLAN_TILE_BY_M: the largest DMA tile whose grid still gives at least
+// 192 workgroups (three quarters of a 256-CU MI355X), else the 32-row tile.
+// Measured on the fused-QKV shape N = 6144, K = 4096 and on squares from 1024
+// to 8192, this picks the fastest DMA tile at every M tried.  Bits do not
+// depend on it.
+int tile_by_m(int64_t M, int64_t N) {
+  const int64_t tn = (N + 255) / 256;
+  if (((M + 255) / 256) * tn >= 192) return GEMM_TILE_256x256;
+  if (((M + 63) / 64) * tn >= 192) return GEMM_TILE_64x256;
+  return GEMM_TILE_32x256;
 }
 
 bool is_dma_tile(int tile) {
@@ -224,7 +240,8 @@ gemm_status gemm_plan_ex2(int64_t M, int64_t N, int64_t K, gemm_dtype in, gemm_d
   if (split_k < 0 || split_k > kMaxSplit || group_m < 0) return GEMM_ERR_UNSUPPORTED;
   if (tile < GEMM_TILE_DEFAULT || tile > GEMM_TILE_64x256) return GEMM_ERR_UNSUPPORTED;
   if (!std::isfinite(scale_a) || !std::isfinite(scale_b)) return GEMM_ERR_UNSUPPORTED;
-  if (flags & ~(unsigned)(GEMM_PLAN_B_TRANSPOSED | GEMM_PLAN_PERSISTENT)) return GEMM_ERR_UNSUPPORTED;
+  if (flags & ~(unsigned)(GEMM_PLAN_B_TRANSPOSED | GEMM_PLAN_PERSISTENT | GEMM_PLAN_TILE_BY_M))
+    return GEMM_ERR_UNSUPPORTED;
   const bool bt = (flags & GEMM_PLAN_B_TRANSPOSED) != 0;
   // 16-byte vector access of every row of A and B needs K and N to be
   // multiples of 16 bytes' worth of elements.
@@ -246,8 +263,10 @@ gemm_status gemm_plan_ex2(int64_t M, int64_t N, int64_t K, gemm_dtype in, gemm_d
   // 32-row DMA tile.
   if (bt && tile == GEMM_TILE_DEFAULT && split_tile == GEMM_TILE_32x128) split_tile = GEMM_TILE_32x256;
   p->tile = checked_tile(split_tile, N, K, eb, bt);
-  p->run_tile =
-      checked_tile(tile == GEMM_TILE_DEFAULT ? default_run_tile(N, K, eb) : tile, N, K, eb, bt);
+  int run_tile = tile;
+  if (tile == GEMM_TILE_DEFAULT)
+    run_tile = (flags & GEMM_PLAN_TILE_BY_M) ? tile_by_m(M, N) : default_run_tile(N, K, eb);
+  p->run_tile = checked_tile(run_tile, N, K, eb, bt);
   if (p->tile < 0 || p->run_tile < 0) {
     delete p;
     return GEMM_ERR_UNSUPPORTED;

@@ -178,3 +178,24 @@ def test_split_changes_bits_only_where_rounding_happens():
     for s in (8, 32, 128):
         p = imm.gemm_plan_ex(256, 256, 16384, "f16", "f32", split_k=s)
         assert np.array_equal(bits_of(run(p, Aid, Bid, True)), ref), s
+
+
+@pytest.mark.parametrize("dt,bt", [("f16", False), ("bf16", True)])
+def test_tile_by_m_rows_identical_across_M(dt, bt):
+    """GEMM_PLAN_TILE_BY_M switches the single pass between the 32x256, 64x256
+    and 256x256 tiles as M grows; every row must keep its bits."""
+    N, K = 6144, 4096
+    g = wl.gen(8400)
+    A = wl.uniform((2048, K), dt, g).to(dev())
+    B = wl.uniform((K, N), dt, g)
+    Bd = (B.float().t().contiguous().to(B.dtype) if bt else B).to(dev())
+    fl = imm.PLAN_B_TRANSPOSED if bt else 0
+    full = imm.gemm_plan_ex2(2048, N, K, dt, "f32", flags=fl)
+    ref = bits_of(run(full, A, Bd, False))
+    seen = set()
+    for m in (1, 100, 256, 512, 1024, 2048):
+        plan = imm.gemm_plan_ex2(m, N, K, dt, "f32", flags=fl | imm.PLAN_TILE_BY_M)
+        seen.add(plan.info["run_tile"])
+        got = bits_of(run(plan, A[:m].contiguous(), Bd, False))
+        assert np.array_equal(got, ref[:m]), m
+    assert len(seen) == 3, seen

@@ -176,7 +176,9 @@ def _plan2_status(*args):
     ((8, 8, 8, 0, 4, 0, 0, 0, 1.0, 1.0, 1), 0),            # B given as [N, K]
     ((8, 8, 8, 0, 4, 0, 0, 0, 1.0, 1.0, 2), 0),            # persistent single pass
     ((8, 8, 8, 0, 4, 0, 0, 0, 1.0, 1.0, 3), 0),
-    ((8, 8, 8, 0, 4, 0, 0, 0, 1.0, 1.0, 4), 2),            # unknown flag bit
+    ((8, 8, 8, 0, 4, 0, 0, 0, 1.0, 1.0, 4), 0),            # tile from M (single pass)
+    ((8, 8, 8, 0, 4, 0, 0, 0, 1.0, 1.0, 7), 0),
+    ((8, 8, 8, 0, 4, 0, 0, 0, 1.0, 1.0, 8), 2),            # unknown flag bit
     ((8, 8, 8, 0, 4, 0, 0, 3, 1.0, 1.0, 1), 2),            # transposed B needs a DMA tile
     ((8, 8, 8, 0, 4, 0, 0, 5, 1.0, 1.0, 1), 0),
     ((8, 8, 2 ** 24, 0, 4, 0, 0, 0, 1.0, 1.0, 1), 2),      # DMA offsets would overflow
@@ -377,3 +379,19 @@ def test_ozaki_column_maxima_chunks_are_capped():
         chunks = -(-K // rows)
         assert chunks <= 16384
         assert chunks * N * 8 <= scratch <= -(-(16384 * N * 8) // 256) * 256
+
+
+@pytest.mark.parametrize("M,N,K,tile", [
+    (1, 6144, 4096, "32x256"), (256, 6144, 4096, "32x256"), (512, 6144, 4096, "64x256"),
+    (1024, 6144, 4096, "64x256"), (2048, 6144, 4096, "256x256"), (1024, 1024, 1024, "32x256"),
+    (2048, 2048, 2048, "64x256"), (4096, 4096, 4096, "256x256"), (8192, 8192, 8192, "256x256"),
+])
+def test_tile_by_m_rule(M, N, K, tile):
+    """GEMM_PLAN_TILE_BY_M: the largest DMA tile with at least 192 workgroups
+    (the measured fastest at each of these shapes); split-K path and the
+    default plan unchanged."""
+    flagged = imm.gemm_plan_ex2(M, N, K, "f16", "f32", flags=imm.PLAN_TILE_BY_M).info
+    plain = imm.gemm_plan_ex2(M, N, K, "f16", "f32").info
+    assert flagged["run_tile"] == imm.TILE[tile]
+    for k in ("tile", "split_k", "k_per_split", "block_m", "block_n"):
+        assert flagged[k] == plain[k]
