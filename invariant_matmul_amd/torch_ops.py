@@ -11,9 +11,11 @@ manager that routes torch's own entry points through them:
     with torch_ops.batch_invariant_mode():
         y = model(x)                               # nn.Linear, torch.mm, @ ...
 
-Every product is planned from (N, K, dtype) alone (the library's rule), so
-row i of a result depends only on row i of the input, on the weight and on
-K: never on how many rows share the call.  A weight given as a transposed
+The split of K is planned from (N, K, dtype) alone (the library's rule) and
+the single pass takes its output tile from M (GEMM_PLAN_TILE_BY_M), which
+moves work between workgroups but never changes a bit, so row i of a result
+depends only on row i of the input, on the weight and on K: never on how many
+rows share the call.  A weight given as a transposed
 view (``W.t()`` of a contiguous [N, K] tensor, which is how ``linear`` hands
 it over) is read in place through the library's transposed-B plans.  Inputs
 are fp16 or bf16 CUDA tensors; the result has the input dtype (fp32 sums,
@@ -31,7 +33,8 @@ import functools
 
 import torch
 
-from . import PLAN_B_TRANSPOSED, gemm_plan_ex2, gemm_run, gemm_splitk_run, gemm_workspace_size
+from . import (PLAN_B_TRANSPOSED, PLAN_TILE_BY_M, gemm_plan_ex2, gemm_run, gemm_splitk_run,
+               gemm_workspace_size)
 
 __all__ = ["mm", "addmm", "linear", "matmul", "batch_invariant_mode", "supported"]
 
@@ -56,11 +59,11 @@ def _product(a2: torch.Tensor, b: torch.Tensor, bias) -> torch.Tensor:
     N = b.shape[1]
     dt = _DT[a2.dtype]
     a2 = a2.contiguous()
-    flags = 0
+    flags = PLAN_TILE_BY_M
     if b.is_contiguous():
         bm = b
     elif b.t().is_contiguous():
-        bm, flags = b.t(), PLAN_B_TRANSPOSED  # the [N, K] weight itself
+        bm, flags = b.t(), flags | PLAN_B_TRANSPOSED  # the [N, K] weight itself
     else:
         bm = b.contiguous()
     out = torch.empty((M, N), dtype=a2.dtype, device=a2.device)
