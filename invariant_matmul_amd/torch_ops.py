@@ -21,10 +21,15 @@ it over) is read in place through the library's transposed-B plans.  Inputs
 are fp16 or bf16 CUDA tensors; the result has the input dtype (fp32 sums,
 one rounding at the end); a bias is added in fp32 before that rounding.
 
+fp64 CUDA tensors go through the library's Ozaki-scheme product (int8
+slices, default slice count and Fast Mode threshold: the Insight Edge cuTile
+blog's FP64 emulation, here with one exponent per row, so it is batch-
+invariant too); a bias is then added with one fp64 addition.  Any N and K.
+
 The direct functions raise for anything else.  The context manager only
-reroutes what the library computes (2-D weights, fp16 / bf16, N and K
-multiples of 8, alpha = beta = 1) and leaves other calls (fp32 tensors, CPU
-tensors, batched weights) to torch's own implementation.
+reroutes what the library computes (2-D weights; fp16 / bf16 with N and K
+multiples of 8, or fp64; alpha = beta = 1) and leaves other calls (fp32
+tensors, CPU tensors, batched weights) to torch's own implementation.
 """
 from __future__ import annotations
 
@@ -34,7 +39,7 @@ import functools
 import torch
 
 from . import (PLAN_B_TRANSPOSED, PLAN_TILE_BY_M, gemm_plan_ex2, gemm_run, gemm_splitk_run,
-               gemm_workspace_size)
+               gemm_workspace_size, ozaki_plan, ozaki_run, ozaki_workspace_size)
 
 __all__ = ["mm", "addmm", "linear", "matmul", "batch_invariant_mode", "supported"]
 
@@ -48,13 +53,38 @@ def _plan(M: int, N: int, K: int, dt: str, flags: int):
 
 def supported(a: torch.Tensor, b: torch.Tensor) -> bool:
     """True if a @ b (a [..., K], b [K, N]) is a product this module computes."""
-    return (a.is_cuda and b.is_cuda and a.dtype in _DT and b.dtype == a.dtype
-            and b.dim() == 2 and a.dim() >= 1 and a.shape[-1] == b.shape[0]
-            and b.shape[0] % 8 == 0 and b.shape[1] % 8 == 0)
+    if not (a.is_cuda and b.is_cuda and b.dtype == a.dtype and b.dim() == 2 and a.dim() >= 1
+            and a.shape[-1] == b.shape[0]):
+        return False
+    if a.dtype == torch.float64:
+        return True
+    return a.dtype in _DT and b.shape[0] % 8 == 0 and b.shape[1] % 8 == 0
+
+
+@functools.lru_cache(maxsize=512)
+def _ozaki_plan(M: int, N: int, K: int):
+    return ozaki_plan(M, N, K, "i8")
+
+
+def _product64(a2: torch.Tensor, b: torch.Tensor, bias) -> torch.Tensor:
+    """a2 [M, K] @ b [K, N] (+ bias [N]) in fp64 by the Ozaki scheme."""
+    M, K = a2.shape
+    N = b.shape[1]
+    out = torch.empty((M, N), dtype=torch.float64, device=a2.device)
+    if M == 0 or N == 0:
+        return out
+    plan = _ozaki_plan(M, N, K)
+    ws = torch.empty(max(1, ozaki_workspace_size(plan)), dtype=torch.uint8, device=a2.device)
+    ozaki_run(plan, a2.contiguous(), b.contiguous(), out, ws)
+    if bias is not None:
+        out += bias.reshape(1, N).to(device=a2.device, dtype=torch.float64)
+    return out
 
 
 def _product(a2: torch.Tensor, b: torch.Tensor, bias) -> torch.Tensor:
     """a2 [M, K] @ b [K, N] (+ bias [N]) in the dtype of a2."""
+    if a2.dtype == torch.float64:
+        return _product64(a2, b, bias)
     M, K = a2.shape
     N = b.shape[1]
     dt = _DT[a2.dtype]
@@ -85,8 +115,9 @@ def _product(a2: torch.Tensor, b: torch.Tensor, bias) -> torch.Tensor:
 def _require(a, b):
     if not supported(a, b):
         raise ValueError(
-            "invariant_matmul_amd.torch_ops: needs fp16/bf16 CUDA tensors, a [..., K] and a 2-D "
-            f"[K, N] second operand with K, N multiples of 8; got {tuple(a.shape)} {a.dtype} @ "
+            "invariant_matmul_amd.torch_ops: needs fp16/bf16 (K, N multiples of 8) or fp64 CUDA "
+            "tensors, a [..., K] and a 2-D [K, N] second operand; got "
+            f"{tuple(a.shape)} {a.dtype} @ "
             f"{tuple(b.shape)} {b.dtype}")
 
 

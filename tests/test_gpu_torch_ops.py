@@ -94,3 +94,24 @@ def test_nn_linear_stack_is_batch_invariant_under_the_mode(dt):
         plain = layers(x)
     # outside the mode torch computes the same layers its own way: close, not bitwise
     assert torch.allclose(plain.float(), y_full.float(), rtol=5e-2, atol=5e-2)
+
+
+def test_fp64_products_go_through_the_ozaki_scheme():
+    """fp64 operators: the library's Ozaki product with int8 slices, bit for
+    bit against the oracle, any N and K, with a bias added in fp64."""
+    from oracle import ozaki
+    M, N, K = 45, 123, 301
+    g = wl.gen(8500)
+    a, b = wl.wide64((M, K), g), wl.wide64((K, N), g)
+    bias = wl.uniform64((N,), g)
+    want = ozaki.gemm(a.numpy(), b.numpy(), "i8")
+    ad, bd = a.to(dev()), b.to(dev())
+    got = torch_ops.mm(ad, bd).cpu().numpy()
+    assert np.array_equal(got.view(np.uint64), want.view(np.uint64))
+    assert np.array_equal(torch_ops.matmul(ad, bd).cpu().numpy(), got)
+    lin = torch_ops.linear(ad, bd.t(), bias.to(dev())).cpu().numpy()
+    assert np.array_equal(lin, want + bias.numpy()[None, :])
+    # rows do not depend on the rest of the batch, under the mode too
+    with torch_ops.batch_invariant_mode():
+        part = (ad[:7] @ bd).cpu().numpy()
+    assert np.array_equal(part, got[:7])
