@@ -5,7 +5,8 @@
 //
 // One workgroup of 8 waves (two per SIMD) owns a 256 x 256 tile of C (or of
 // one K slice of it); each wave owns a 128 x 64 block held in 128 fp32
-// accumulators per lane.  K is walked in ascending stages ([TDI] "Tiling -
+// accumulators per lane, as 8 x 4 blocks of 16 x 16 (16-bit inputs, the
+// 16x16x32 matrix-core step) or 4 x 2 blocks of 32 x 32 (fp8).  K is walked in ascending stages ([TDI] "Tiling -
 // 分塊行列乗算": load, compute, accumulate per K step, one write-back at the
 // end).  Two waves per SIMD, because a single wave serialises its own LDS and
 // DMA instructions with its MFMAs while a second wave's memory instructions
@@ -27,8 +28,9 @@
 // 16-bit, 256 for fp8), and read with the gfx950 transposing LDS reads
 // (ds_read_b64_tr_b16 / _b8), which hand each lane the K-contiguous column
 // piece the matrix core needs.  16-byte slot c of B row k lives at
-// c ^ ((k & 3) << 2) (16-bit) or c ^ ((k & 7) << 1) (fp8) so that the rows one
-// transposing read touches fall on different banks.  The swizzles are applied
+// c ^ ((k & 3) << 2) ^ (((k >> 3) & 1) << 1) (16-bit) or c ^ ((k & 7) << 1)
+// (fp8) so that the rows and columns the 32 lanes of one half-wave read fall
+// on different banks.  The swizzles are applied
 // on the global side: each DMA lane fetches the chunk that belongs in its
 // fixed LDS slot.
 //
@@ -39,8 +41,8 @@
 // next stage overlap the remaining MFMAs.
 //
 // Bits: the per-element chain is the same as in every other kernel of the
-// library (same instruction, MFMA K steps in ascending k from +0), so this
-// kernel's output is bitwise identical to theirs.
+// library (same instruction per input dtype, MFMA K steps in ascending k from
+// +0), so this kernel's output is bitwise identical to theirs.
 #include <type_traits>
 
 #include "kernel_common.h"
@@ -171,14 +173,21 @@ __global__ __launch_bounds__(256 * WM, (waves_per_simd<TBM, WM, NS>())) void gem
   constexpr int WAVES = WM * WN;
   constexpr int WTM = TBM / WM;              // wave tile rows
   constexpr int WTN = TBN / WN;              // wave tile columns (64)
-  constexpr int FM = WTM / 32;               // MFMA row blocks per wave
-  constexpr int FN = WTN / 32;               // MFMA column blocks per wave (2)
+  // 16-bit inputs: the 16x16x32 step; fp8, int8 and the exact Ozaki chains
+  // (whose bits no instruction changes): the 32x32 step
+  constexpr bool M16 = EB == 2 && MODE != MODE_OZAKI;
+  constexpr int BLK = M16 ? 16 : 32;         // MFMA output block edge
+  constexpr int NACC = BLK * BLK / 64;       // accumulators per lane per block
+  using AccT = typename std::conditional<M16, f32x4, f32x16>::type;
+  constexpr int KSTEP = M16 ? 64 : T::KSTEP_B;  // bytes of K per MFMA step
+  constexpr int FM = WTM / BLK;              // MFMA row blocks per wave
+  constexpr int FN = WTN / BLK;              // MFMA column blocks per wave
   constexpr int NM = FM * FN;                // MFMAs per k-step per wave
   constexpr int A_STAGE = TBM * SKB;         // bytes of A per stage
   constexpr int B_STAGE = TBN * SKB;         // bytes of B per stage (32 KB)
   constexpr int STAGE = A_STAGE + B_STAGE;
   constexpr int BKE = SKB / EB;              // K elements (= B rows) per stage
-  constexpr int KS = SKB / T::KSTEP_B;       // MFMA k-steps per stage
+  constexpr int KS = SKB / KSTEP;           // MFMA k-steps per stage
   constexpr int ACH = SKB / 16;              // 16-byte slots per A row
   constexpr int AROWS_PER_DMA = 1024 / SKB;  // A rows written by one DMA instruction
   constexpr int BROW = TBN * EB;             // bytes per B row in LDS
@@ -188,7 +197,7 @@ __global__ __launch_bounds__(256 * WM, (waves_per_simd<TBM, WM, NS>())) void gem
   constexpr int DB = B_STAGE / 1024 / WAVES; // ... and B
   constexpr int DPW = DA + DB;
   static_assert(DA * WAVES * 1024 == A_STAGE && DB * WAVES * 1024 == B_STAGE, "DMA split");
-  static_assert(FM * 32 * WM == TBM, "tile rows");
+  static_assert(FM * BLK * WM == TBM, "tile rows");
   constexpr bool I8 = T::I8;                 // int8: 16-bit-like A reads, 8-bit B reads
   constexpr int NRA = T::FRAG == 1 ? FM : 2 * FM;  // fragment reads per k-step: A ...
   constexpr int NRB = BT ? (T::FRAG == 1 ? FN : 2 * FN) : (EB == 2 || I8 ? 2 * FN : 4 * FN);  // ... B
@@ -205,7 +214,7 @@ __global__ __launch_bounds__(256 * WM, (waves_per_simd<TBM, WM, NS>())) void gem
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (uniform)
   const int wm = w / WN, wn = w % WN;
-  const int h = lane >> 5, l32 = lane & 31;
+  const int lb = lane % BLK, hq = lane / BLK;  // row / column in the MFMA block, K piece
 
   int64_t ksl, pm, pn;
   raster_tile(blockIdx.x, g.grid, g.tiles_m, g.tiles_n, g.group_m, &ksl, &pm, &pn);
@@ -237,6 +246,8 @@ __global__ __launch_bounds__(256 * WM, (waves_per_simd<TBM, WM, NS>())) void gem
 
   // A row r keeps its 16-byte slot c at c ^ aswz(r).
   auto aswz = [](int r) { return (r >> 1) & 7; };
+  // 16-bit B row k keeps its 16-byte slot c at c ^ bswz16(k).
+  auto bswz16 = [](int k) { return ((k & 3) << 2) ^ (((k >> 3) & 1) << 1); };
 
   // ---- DMA geometry of this lane (the same for every stage).  Offsets of
   // rows past M / columns past N are replaced by an out-of-range offset once;
@@ -266,7 +277,7 @@ __global__ __launch_bounds__(256 * WM, (waves_per_simd<TBM, WM, NS>())) void gem
     } else {
       const int k = BROWS_PER_DMA * idx + lane / BSLOTS;
       const int s = lane % BSLOTS;
-      const int cb = EB == 2 ? (s ^ ((k & 3) << 2)) : (s ^ ((k & 7) << 1));
+      const int cb = EB == 2 ? (s ^ bswz16(k)) : (s ^ ((k & 7) << 1));
       b_off[i] = (PER_TILE || n0 + cb * (16 / EB) < g.N) ? (unsigned)(k * g.N * EB + cb * 16) : OOB;
       b_k[i] = k;  // K row of the chunk
     }
@@ -290,7 +301,7 @@ __global__ __launch_bounds__(256 * WM, (waves_per_simd<TBM, WM, NS>())) void gem
       } else {
         const int k = BROWS_PER_DMA * (w * DB + i) + lane / BSLOTS;
         const int sl = lane % BSLOTS;
-        col = (EB == 2 ? (sl ^ ((k & 3) << 2)) : (sl ^ ((k & 7) << 1))) * (16 / EB);
+        col = (EB == 2 ? (sl ^ bswz16(k)) : (sl ^ ((k & 7) << 1))) * (16 / EB);
       }
       *bm |= (unsigned)(tn0 + col < g.N) << i;
     }
@@ -375,22 +386,25 @@ __global__ __launch_bounds__(256 * WM, (waves_per_simd<TBM, WM, NS>())) void gem
   };
 
   // ---- fragment read offsets within a stage.
-  const int asw = aswz(l32);  // rows of a fragment differ from l32 by multiples of 32
+  const int asw = aswz(lb);  // rows of a fragment differ from lb by multiples of 16
   int a_rd[FM];
 #pragma unroll
-  for (int i = 0; i < FM; ++i) a_rd[i] = (wm * WTM + i * 32 + l32) * SKB;
+  for (int i = 0; i < FM; ++i) a_rd[i] = (wm * WTM + i * BLK + lb) * SKB;
   const int grp = lane >> 4, gi = lane & 15;
   int b_rd[FN];  // per column block j: byte offset of its first read
   if constexpr (BT) {
 #pragma unroll
-    for (int j = 0; j < FN; ++j) b_rd[j] = (wn * WTN + j * 32 + l32) * SKB;
+    for (int j = 0; j < FN; ++j) b_rd[j] = (wn * WTN + j * BLK + lb) * SKB;
   } else if constexpr (EB == 2) {
+    // each group of 16 lanes reads 4 K rows x 16 columns per transposing read:
+    // 16x16 blocks, the column block and K rows 8 grp ..; 32x32 blocks, column
+    // half grp & 1 and K rows 8 (grp >> 1) ..
     const int t_ = gi >> 2, q = gi & 3;
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
-      const int n = wn * WTN + j * 32 + 16 * (grp & 1) + 4 * q;
-      const int k = 8 * (grp >> 1) + t_;
-      b_rd[j] = k * BROW + (((n >> 3) ^ (t_ << 2)) << 4) + (q & 1) * 8;
+      const int n = M16 ? wn * WTN + j * 16 + 4 * q : wn * WTN + j * 32 + 16 * (grp & 1) + 4 * q;
+      const int k = (M16 ? 8 * grp : 8 * (grp >> 1)) + t_;
+      b_rd[j] = k * BROW + (((n >> 3) ^ bswz16(k)) << 4) + (q & 1) * 8;
     }
   } else {
     const int t_ = gi >> 1, q = gi & 1;
@@ -419,7 +433,7 @@ __global__ __launch_bounds__(256 * WM, (waves_per_simd<TBM, WM, NS>())) void gem
       // int8: A as for 16-bit inputs (one 16-byte slot per k-step half), B by
       // two 8-bit transposing reads of 8 K rows each.
       if (x < NRA) {
-        const int c = ks * 2 + h;
+        const int c = ks * 2 + hq;
         F.a[x] = *reinterpret_cast<const i32x4*>(sb + a_rd[x] + ((c ^ asw) << 4));
       } else {
         const int j = (x - NRA) >> 1, r = (x - NRA) & 1;
@@ -433,11 +447,11 @@ __global__ __launch_bounds__(256 * WM, (waves_per_simd<TBM, WM, NS>())) void gem
       if (x >= NRA) {
         const char* sbb = lds + bs;
         if constexpr (EB == 2) {
-          const int j = x - NRA, c = ks * 2 + h;
+          const int j = x - NRA, c = ks * (KSTEP / 16) + hq;
           F.b[j] = *reinterpret_cast<const i32x4*>(sbb + b_rd[j] + ((c ^ asw) << 4));
         } else {
           const int j = (x - NRA) >> 1, f = (x - NRA) & 1;
-          const int c = ks * 4 + 2 * h + f;
+          const int c = ks * 4 + 2 * hq + f;
           const i32x4 v = *reinterpret_cast<const i32x4*>(sbb + b_rd[j] + ((c ^ asw) << 4));
 #pragma unroll
           for (int e = 0; e < 4; ++e) F.b[j][4 * f + e] = v[e];
@@ -447,18 +461,18 @@ __global__ __launch_bounds__(256 * WM, (waves_per_simd<TBM, WM, NS>())) void gem
     }
     if constexpr (EB == 2) {
       if (x < NRA) {
-        const int c = ks * 2 + h;
+        const int c = ks * (KSTEP / 16) + hq;
         F.a[x] = *reinterpret_cast<const i32x4*>(sb + a_rd[x] + ((c ^ asw) << 4));
       } else {
         const int j = (x - NRA) >> 1, r = (x - NRA) & 1;
-        const i32x2 v = tr16_rows<BROW>(lds_addr + bs + b_rd[j], ks * 16 + 4 * r);
+        const i32x2 v = tr16_rows<BROW>(lds_addr + bs + b_rd[j], ks * (KSTEP / 2) + 4 * r);
         F.b[j][2 * r] = v[0];
         F.b[j][2 * r + 1] = v[1];
       }
     } else {
       if (x < NRA) {
         const int i = x >> 1, f = x & 1;
-        const int c = ks * 4 + 2 * h + f;
+        const int c = ks * 4 + 2 * hq + f;
         const i32x4 v = *reinterpret_cast<const i32x4*>(sb + a_rd[i] + ((c ^ asw) << 4));
 #pragma unroll
         for (int e = 0; e < 4; ++e) F.a[i][4 * f + e] = v[e];
@@ -481,13 +495,16 @@ __global__ __launch_bounds__(256 * WM, (waves_per_simd<TBM, WM, NS>())) void gem
     fence();
   };
 
-  f32x16 acc[FM][FN];
+  AccT acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{};
+    for (int j = 0; j < FN; ++j) acc[i][j] = AccT{};
   auto mfma_x = [&](const Frag<IN, FM, FN>& F, int x) {
-    acc[x / FN][x % FN] = mfma_v<IN>(F.a[x / FN], F.b[x % FN], acc[x / FN][x % FN]);
+    if constexpr (M16)
+      acc[x / FN][x % FN] = mfma16_v<IN>(F.a[x / FN], F.b[x % FN], acc[x / FN][x % FN]);
+    else
+      acc[x / FN][x % FN] = mfma_v<IN>(F.a[x / FN], F.b[x % FN], acc[x / FN][x % FN]);
   };
   // Ozaki mode: fp64 sum over the slice pairs (dead code otherwise).
   double acc64[FM][FN][16];
@@ -520,27 +537,28 @@ __global__ __launch_bounds__(256 * WM, (waves_per_simd<TBM, WM, NS>())) void gem
             const double v = I8 ? (double)__float_as_int(f) : (double)f;
             acc64[i][j][r] += ldexp(v, sh);
           }
-          acc[i][j] = f32x16{};
+          acc[i][j] = AccT{};
         }
     }
   };
 
-  // Write-back of the tile at (tm0, tn0).  32x32 accumulator layout: lane l,
-  // register r holds row 8*(r/4) + 4*(l/32) + r%4, column l%32 of the block.
+  // Write-back of the tile at (tm0, tn0).  Accumulator layouts: 16x16 blocks,
+  // lane l, register r holds row 4*(l/16) + r, column l%16 of the block; 32x32
+  // blocks, row 8*(r/4) + 4*(l/32) + r%4, column l%32.
   auto store_tile = [&](int64_t tm0, int64_t tn0) {
     // Inside the stage loop (MODE_PERSIST) the per-element offsets below are
     // loop-invariant; opaque lane bases keep the compiler from hoisting them
     // out of the loop (where they would sit in registers or scratch).
-    int lrow = wm * WTM + 4 * h, lcol = wn * WTN + l32;
+    int lrow = wm * WTM + 4 * hq, lcol = wn * WTN + lb;
     if constexpr (PER_TILE) asm volatile("" : "+v"(lrow), "+v"(lcol));
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
-        const int64_t col = tn0 + lcol + j * 32;
+        const int64_t col = tn0 + lcol + j * BLK;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int64_t row = tm0 + lrow + i * 32 + 8 * (r >> 2) + (r & 3);
+        for (int r = 0; r < NACC; ++r) {
+          const int64_t row = tm0 + lrow + i * BLK + (M16 ? r : 8 * (r >> 2) + (r & 3));
           if constexpr (MODE == MODE_OZAKI) {
             // C = 2^(ea[row] + eb[col]) * sum: the same bits as scaling every
             // pair's term by its full exponent while no value leaves fp64's
@@ -662,7 +680,7 @@ __global__ __launch_bounds__(256 * WM, (waves_per_simd<TBM, WM, NS>())) void gem
 #pragma unroll
         for (int i = 0; i < FM; ++i)
 #pragma unroll
-          for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{};
+          for (int j = 0; j < FN; ++j) acc[i][j] = AccT{};
         if (++cur_tile < ntiles) tile_origin(cur_tile, &cur_m0, &cur_n0);
       }
     }

@@ -14,9 +14,9 @@
 // written to a double-buffered LDS tile, and fed to the matrix cores from
 // LDS.  The accumulators never leave registers until the single write-back.
 //
-// Bits.  Each output element is one accumulation chain: its 32x32 MFMA block
-// is updated once per instruction-K step (16 elements for fp16/bf16, 64 for
-// fp8) in ascending k, starting from +0.  The instruction is fixed per input
+// Bits.  Each output element is one accumulation chain: its MFMA block
+// (16x16 for fp16/bf16, 32x32 for fp8) is updated once per instruction-K step
+// (32 elements for fp16/bf16, 64 for fp8) in ascending k, starting from +0.  The instruction is fixed per input
 // dtype and the chain does not depend on BM, BN, the wave layout or the tile
 // order ([TDI] "Batch Invariance の由来": BLOCK_M/BLOCK_N and GROUP_M change
 // no bits, the K step does).  Rows past M load as zero and are never stored,
@@ -44,9 +44,14 @@ constexpr int CHUNKS = ROWB / 16;  // 16-byte chunks per LDS row
 template <int IN>
 struct TileT {
   static constexpr int EB = InT<IN>::EB;
+  static constexpr bool M16 = EB == 2;                   // 16x16x32 step (16-bit inputs)
+  static constexpr int BLK = M16 ? 16 : 32;              // MFMA output block edge
+  static constexpr int NACC = BLK * BLK / 64;            // accumulators per lane per block
+  static constexpr int KSTEP = M16 ? 64 : InT<IN>::KSTEP_B;  // bytes of K per MFMA step
   static constexpr int BKE = ROWB / EB;                  // K elements per stage
-  static constexpr int NKK = ROWB / InT<IN>::KSTEP_B;    // MFMA steps per stage
-  static constexpr int FRAG = InT<IN>::FRAG;             // 16-byte chunks per lane
+  static constexpr int NKK = ROWB / KSTEP;               // MFMA steps per stage
+  static constexpr int FRAG = M16 ? 1 : InT<IN>::FRAG;   // 16-byte chunks per lane
+  using Acc = typename std::conditional<M16, f32x4, f32x16>::type;
 };
 
 __device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
@@ -90,11 +95,12 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_tile_kernel(GemmAr
   constexpr int EB = T::EB;
   constexpr int BKE = T::BKE;
   constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;  // wave tile
-  constexpr int FM = WTM / 32, FN = WTN / 32;
+  constexpr int BLK = T::BLK;
+  constexpr int FM = WTM / BLK, FN = WTN / BLK;
   constexpr int A_CH = BM * CHUNKS / THREADS;            // A chunks per thread
   constexpr int NB = BN * EB / 16;                       // 16-byte column groups of B
   constexpr int B_TASKS = (BKE / 4) * NB;                // 4-row blocks of B
-  static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be a multiple of 32");
+  static_assert(WTM % BLK == 0 && WTN % BLK == 0, "wave tile must be a multiple of the block");
   static_assert(BM * CHUNKS % THREADS == 0 && B_TASKS == THREADS, "staging layout");
   constexpr int STAGE = (BM + BN) * ROWB;
 
@@ -104,7 +110,7 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_tile_kernel(GemmAr
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
-  const int h = lane >> 5, l32 = lane & 31;
+  const int lb = lane % BLK, hq = lane / BLK;  // row / column in the block, K piece
 
   int64_t ks, pm, pn;
   raster_tile(blockIdx.x, g.grid, g.tiles_m, g.tiles_n, g.group_m, &ks, &pm, &pn);
@@ -176,11 +182,11 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_tile_kernel(GemmAr
     }
   };
 
-  f32x16 acc[FM][FN];
+  typename T::Acc acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{};
+    for (int j = 0; j < FN; ++j) acc[i][j] = typename T::Acc{};
 
   if (nt > 0) {
     load_tile(0);
@@ -195,43 +201,51 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_tile_kernel(GemmAr
 #pragma unroll
     for (int kk = 0; kk < T::NKK; ++kk) {
       i32x4 af[FM][T::FRAG], bfr[FN][T::FRAG];
+      // chunk of K piece f of this lane in step kk
+      auto chunk = [&](int f) { return kk * (T::KSTEP / 16) + hq * T::FRAG + f; };
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
-        const int r = wm * WTM + i * 32 + l32;
+        const int r = wm * WTM + i * BLK + lb;
 #pragma unroll
-        for (int f = 0; f < T::FRAG; ++f) {
-          const int ch = kk * 2 * T::FRAG + h * T::FRAG + f;
-          af[i][f] = *reinterpret_cast<const i32x4*>(sa + r * ROWB + ((ch ^ swz(r)) << 4));
-        }
+        for (int f = 0; f < T::FRAG; ++f)
+          af[i][f] = *reinterpret_cast<const i32x4*>(sa + r * ROWB + ((chunk(f) ^ swz(r)) << 4));
       }
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
-        const int n = wn * WTN + j * 32 + l32;
+        const int n = wn * WTN + j * BLK + lb;
 #pragma unroll
-        for (int f = 0; f < T::FRAG; ++f) {
-          const int ch = kk * 2 * T::FRAG + h * T::FRAG + f;
-          bfr[j][f] = *reinterpret_cast<const i32x4*>(sb + n * ROWB + ((ch ^ swz(n)) << 4));
-        }
+        for (int f = 0; f < T::FRAG; ++f)
+          bfr[j][f] = *reinterpret_cast<const i32x4*>(sb + n * ROWB + ((chunk(f) ^ swz(n)) << 4));
       }
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < FN; ++j) acc[i][j] = mfma<IN>(af[i], bfr[j], acc[i][j]);
+        for (int j = 0; j < FN; ++j) {
+          if constexpr (T::M16) {
+            acc[i][j] = mfma16_v<IN>(af[i][0], bfr[j][0], acc[i][j]);
+          } else {
+            const i32x8 av = __builtin_shufflevector(af[i][0], af[i][1], 0, 1, 2, 3, 4, 5, 6, 7);
+            const i32x8 bv = __builtin_shufflevector(bfr[j][0], bfr[j][1], 0, 1, 2, 3, 4, 5, 6, 7);
+            acc[i][j] = mfma_v<IN>(av, bv, acc[i][j]);
+          }
+        }
     }
     if (t + 1 < nt) store_tile(cur ^ 1);
     __syncthreads();
   }
 
-  // Write-back.  32x32 accumulator layout: lane l, register r holds
-  // row 8*(r/4) + 4*(l/32) + r%4, column l%32 of the block.
+  // Write-back.  Accumulator layouts: 16x16 blocks, lane l, register r holds
+  // row 4*(l/16) + r, column l%16; 32x32 blocks, row 8*(r/4) + 4*(l/32) + r%4,
+  // column l%32.
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
-      const int64_t col = n0 + wn * WTN + j * 32 + l32;
+      const int64_t col = n0 + wn * WTN + j * BLK + lb;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t row = m0 + wm * WTM + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+      for (int r = 0; r < T::NACC; ++r) {
+        const int64_t row = m0 + wm * WTM + i * BLK +
+                            (T::M16 ? 4 * hq + r : 8 * (r >> 2) + 4 * hq + (r & 3));
         if (row < g.M && col < g.N) {
           const float v = acc[i][j][r];
           if constexpr (SLICE) {

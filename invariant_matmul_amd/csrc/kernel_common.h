@@ -27,35 +27,32 @@ template <int IN>
 struct InT {
   static constexpr bool I8 = IN == GEMM_I8;  // int8 (Ozaki slices), int32 accumulators
   static constexpr int EB = (IN == GEMM_F8_E4M3 || IN == GEMM_F8_E5M2 || I8) ? 1 : 2;
-  static constexpr int KSTEP_B = (EB == 2 || I8) ? 32 : 64;  // bytes of K per MFMA (per row)
-  static constexpr int FRAG = KSTEP_B / 32;                  // 16-byte pieces per lane per operand
+  // The 32x32-block step (mfma_v): bytes of K per instruction per row, and
+  // 16-byte pieces per lane per operand.
+  static constexpr int KSTEP_B = (EB == 2 || I8) ? 32 : 64;
+  static constexpr int FRAG = KSTEP_B / 32;
 };
 
-// The one matrix-core step every kernel uses for an input dtype (the bits of
-// the product depend on this choice, [TDI] "Batch Invariance の由来", BLOCK_K
-// paragraph): a 32x32 output block, K = 16 (fp16/bf16), 64 (fp8) or 32
-// (int8, int32 accumulators carried in the fp32 registers' bits).  Lane l
-// supplies row (l % 32) of A and column (l % 32) of B; its data are the K
-// elements [h*half, (h+1)*half) of the step, h = l / 32, in increasing k.
-template <int IN>
-__device__ __forceinline__ f32x16 mfma(const i32x4* a, const i32x4* b, f32x16 c) {
-  if constexpr (IN == GEMM_F16) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a[0]),
-                                                  __builtin_bit_cast(f16x8, b[0]), c, 0, 0, 0);
-  } else if constexpr (IN == GEMM_BF16) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[0]),
-                                                   __builtin_bit_cast(bf16x8, b[0]), c, 0, 0, 0);
-  } else {
-    // cbsz / blgp select the operand formats: 0 = fp8 e4m3, 1 = bf8 e5m2.
-    constexpr int fmt = IN == GEMM_F8_E4M3 ? 0 : 1;
-    const i32x8 av = __builtin_shufflevector(a[0], a[1], 0, 1, 2, 3, 4, 5, 6, 7);
-    const i32x8 bv = __builtin_shufflevector(b[0], b[1], 0, 1, 2, 3, 4, 5, 6, 7);
-    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, c, fmt, fmt, 0, 0, 0, 0);
-  }
-}
+// The matrix-core steps.  The bits of a product depend on the instruction
+// that accumulates it ([TDI] "Batch Invariance の由来", BLOCK_K paragraph),
+// so every GEMM kernel uses one step per input dtype:
+//   fp16 / bf16: mfma16_v, a 16x16 output block, K = 32.  Lane l supplies
+//     row (l % 16) of A and column (l % 16) of B, with the K elements
+//     [8 (l / 16), 8 (l / 16) + 8) of the step in increasing k; it holds
+//     rows 4 (l / 16) .. 4 (l / 16) + 3 of column (l % 16) of the block.
+//     (Measured on MI355X: the same bits as the 32x32x16 instruction, and
+//     about 15 % less energy per flop on random data, which is what sets the
+//     clock of a large product.)
+//   fp8: mfma_v, a 32x32 block, K = 64; int8 (Ozaki slices): mfma_v, a 32x32
+//     block, K = 32, int32 accumulators carried in the fp32 registers' bits.
+//     Lane l supplies row (l % 32) of A and column (l % 32) of B, with the K
+//     elements [h*half, (h+1)*half) of the step, h = l / 32, in increasing k.
+// The Ozaki slice products accumulate exact chains, where the instruction
+// cannot change a bit; there 16-bit slices use mfma_v (32x32x16), whose
+// smaller fragments leave room for the fp64 accumulators.
 
-// The same step on whole-operand registers: 4 dwords (16-bit inputs) or 8
-// dwords (fp8) per lane, allocated as one register tuple.
+// The 32x32 step on whole-operand registers: 4 dwords (16-bit inputs and
+// int8) or 8 dwords (fp8) per lane, allocated as one register tuple.
 template <int IN>
 struct FragOf {
   using type = typename std::conditional<InT<IN>::FRAG == 1, i32x4, i32x8>::type;
@@ -74,9 +71,22 @@ __device__ __forceinline__ f32x16 mfma_v(const typename FragOf<IN>::type& a,
     return __builtin_bit_cast(
         f32x16, __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, __builtin_bit_cast(i32x16, c), 0, 0, 0));
   } else {
+    // cbsz / blgp select the operand formats: 0 = fp8 e4m3, 1 = bf8 e5m2.
     constexpr int fmt = IN == GEMM_F8_E4M3 ? 0 : 1;
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, fmt, fmt, 0, 0, 0, 0);
   }
+}
+
+// The 16x16x32 step of 16-bit inputs: 4 dwords per lane and operand.
+template <int IN>
+__device__ __forceinline__ f32x4 mfma16_v(const i32x4& a, const i32x4& b, f32x4 c) {
+  static_assert(IN == GEMM_F16 || IN == GEMM_BF16, "16-bit inputs only");
+  if constexpr (IN == GEMM_F16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
 // fp32 -> bf16, round to nearest, ties to even (quiet NaN stays NaN).
