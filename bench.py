@@ -40,6 +40,9 @@ MALL_BYTES = 256 * 2 ** 20
 KERNEL_SOURCES = [os.path.join(ROOT, "invariant_matmul_amd", "csrc", f)
                   for f in ("gemm_dma.hip", "kernel_common.h", "imm_internal.h", "api.cpp")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_square_f16_8192.json")
+CLOCK_FILE = os.path.join(ROOT, "profiles", "clock_square_f16_8192.json")
+CLOCK_COUNTERS = ("GRBM_GUI_ACTIVE", "GRBM_COUNT", "SQ_BUSY_CYCLES", "SQ_VALU_MFMA_BUSY_CYCLES",
+                  "SQ_INSTS_VALU_MFMA_MOPS_F16", "SQ_INSTS_MFMA")
 
 
 def kernel_source_hash() -> str:
@@ -88,6 +91,73 @@ def write_traffic(fetch_csv, write_csv):
            "bytes_per_launch": (gf * ff + gw * wf) * 1024}
     os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
     with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out))
+
+
+def write_clock(counter_csv, agent_csv):
+    """Turn one rocprofv3 --pmc run of `bench.py --clock-pass` (the CLOCK_COUNTERS)
+    into the engine cycles, clock and matrix-core occupancy of the headline
+    kernel, of hipBLASLt's kernel for the same product and of a plain copy.
+
+    GRBM_GUI_ACTIVE is the per-dispatch count of busy engine cycles, summed over
+    the XCDs: count / XCDs is the cycles one launch takes, and that over the
+    dispatch's duration is the clock the part held.  SQ_VALU_MFMA_BUSY_CYCLES,
+    summed over SIMDs, over those cycles times the SIMD count is the fraction of
+    cycles the matrix units were busy; that is the kernel's fraction of the
+    matrix peak at whatever clock it ran.  The fp16 MFMA op counter (512 flop
+    per op) checks the flop count against 2*M*N*K."""
+    import csv
+
+    with open(agent_csv) as f:
+        gpu = next(r for r in csv.DictReader(f) if r["Agent_Type"] == "GPU")
+    xcc, simds = int(gpu["Num_Xcc"]), int(gpu["Simd_Count"])
+    fmax_ghz = int(gpu["Max_Engine_Clk_Fcompute"]) / 1000.0
+    disp = {}
+    with open(counter_csv) as f:
+        for r in csv.DictReader(f):
+            d = disp.setdefault(r["Dispatch_Id"], {
+                "name": r["Kernel_Name"],
+                "ns": int(r["End_Timestamp"]) - int(r["Start_Timestamp"])})
+            d[r["Counter_Name"]] = float(r["Counter_Value"])
+
+    def kind(name):
+        if "gemm_dma_kernel" in name:
+            return "headline"
+        if name.startswith("Cijk"):
+            return "hipblaslt"
+        if "copyBuffer" in name:
+            return "copy"
+        return None
+
+    groups = {}
+    for d in disp.values():
+        k = kind(d["name"])
+        if k is None or "GRBM_GUI_ACTIVE" not in d or d["ns"] <= 0:
+            continue
+        cyc = d["GRBM_GUI_ACTIVE"] / xcc
+        groups.setdefault(k, []).append({
+            "us": d["ns"] / 1e3, "cycles": cyc, "ghz": cyc / d["ns"],
+            "mfma_busy": d.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / (cyc * simds),
+            "mfma_tflop": d.get("SQ_INSTS_VALU_MFMA_MOPS_F16", 0.0) * 512 / 1e12,
+            "mfma_insts": d.get("SQ_INSTS_MFMA", 0.0), "name": d["name"][:120]})
+    if "headline" not in groups:
+        raise SystemExit(f"{counter_csv}: no headline-kernel dispatches with the clock counters")
+    out = {"kernel": "gemm_dma_kernel<f16, f32 out, 256x256 tile>, M=N=K=8192",
+           "kernel_source_hash": kernel_source_hash(), "counters": list(CLOCK_COUNTERS),
+           "num_xcc": xcc, "simds": simds, "max_engine_clock_ghz": fmax_ghz}
+    for k, g in groups.items():
+        mean = {f: statistics.mean(x[f] for x in g)
+                for f in ("us", "cycles", "ghz", "mfma_busy", "mfma_tflop", "mfma_insts")}
+        out[k] = {"dispatches": len(g), "kernel_name": g[0]["name"],
+                  "mean_us": mean["us"], "mean_cycles": mean["cycles"],
+                  "min_cycles": min(x["cycles"] for x in g), "max_cycles": max(x["cycles"] for x in g),
+                  "mean_clock_ghz": mean["ghz"],
+                  "min_clock_ghz": min(x["ghz"] for x in g), "max_clock_ghz": max(x["ghz"] for x in g),
+                  "mfma_busy_frac": mean["mfma_busy"], "mfma_tflop_per_launch": mean["mfma_tflop"],
+                  "mfma_insts_per_launch": mean["mfma_insts"]}
+    with open(CLOCK_FILE, "w") as f:
         json.dump(out, f, indent=1)
         f.write("\n")
     print(json.dumps(out))
@@ -297,9 +367,19 @@ def main():
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="host only: write the headline kernel's HBM traffic from two "
                          "counter runs of --profile-pass, then exit")
+    ap.add_argument("--clock-pass", action="store_true",
+                    help="back-to-back launches of the headline kernel, of torch.matmul on "
+                         "the same fp16 product and of a plain copy, for the clock counters; "
+                         "prints nothing else")
+    ap.add_argument("--write-clock", nargs=2, metavar=("COUNTER_CSV", "AGENT_CSV"),
+                    help="host only: write the headline kernel's engine clock and matrix-core "
+                         "occupancy from a counter run of --clock-pass, then exit")
     args = ap.parse_args()
     if args.write_traffic:
         write_traffic(*args.write_traffic)
+        return
+    if args.write_clock:
+        write_clock(*args.write_clock)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (this build has no multi-GPU path); "
@@ -334,6 +414,26 @@ def main():
         print("profile pass done", flush=True)
         return
 
+    if args.clock_pass:
+        w = wl.WORKLOADS["square_f16_8192"]
+        A, B = w.make()
+        Ad, Bd = A.cuda(), B.cuda()
+        plan = imm.gemm_plan(w.M, w.N, w.K, w.dtype)
+        C = torch.empty((w.M, w.N), dtype=torch.float32, device="cuda")
+        ref = torch.empty((w.M, w.N), dtype=torch.float16, device="cuda")
+        src = torch.empty(2 ** 30 // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)   # plain copy: 1 GiB read + 1 GiB written
+        for _ in range(10):
+            imm.gemm_run(plan, Ad, Bd, C)
+        for _ in range(10):
+            torch.matmul(Ad, Bd, out=ref)
+        torch.cuda.synchronize()
+        print("clock pass done", flush=True)
+        return
+
     log("headline: square fp16 8192^3, gemm_run")
     w, plan, per, total, host = bench_square("square_f16_8192", args.steps, args.warmup,
                                              torch, imm, wl)
@@ -347,12 +447,25 @@ def main():
             t = json.load(f)
         if t.get("kernel_source_hash") == kernel_source_hash():
             traffic = t.get("bytes_per_launch")
+    clock = None
+    if os.path.exists(CLOCK_FILE):
+        with open(CLOCK_FILE) as f:
+            c = json.load(f)
+        if c.get("kernel_source_hash") == kernel_source_hash():
+            # the launch's cycle count is stable across runs; the clock is not
+            h = c["headline"]
+            ghz = h["mean_cycles"] / (kavg * 1e6)
+            peak_at = PEAK_TFLOPS["f16"] * ghz / c["max_engine_clock_ghz"]
+            clock = {"cycles_per_launch": h["mean_cycles"], "clock_ghz_timed": ghz,
+                     "peak_at_clock_tflops": peak_at, "frac_at_clock": achieved / peak_at,
+                     "mfma_busy_frac_counters": h["mfma_busy_frac"],
+                     "source": os.path.relpath(CLOCK_FILE, ROOT)}
     roofline = {"bound": "mfma", "achieved": achieved, "peak": PEAK_TFLOPS["f16"],
                 "unit": "TFLOP/s", "frac": achieved / PEAK_TFLOPS["f16"], "traffic": traffic,
                 "kernel": "gemm_dma_kernel<f16, f32 out, 256x256 tile>",
                 "algorithmic_flop_per_launch": w.flops, "avg_launch_ms": kavg}
 
-    extra = {"headline_kernel": summary(per),
+    extra = {"headline_kernel": summary(per), "headline_clock": clock,
              "plan": {k: plan.info[k] for k in ("run_block_m", "run_block_n", "block_k", "run_waves",
                                                   "group_m", "split_k", "mfma_k")}}
     if not args.no_extra:
