@@ -13,7 +13,8 @@ cache), the huge-K product 256 x 256 x 131072 at split_k in {1, 8, 32, 128},
 the fp64 product by the Ozaki scheme (bf16 and e4m3 slices, n = 4096 .. 16384:
 split, slice-pair product and whole call, in fp64-equivalent TFLOP/s and as
 matrix-core throughput of the slice products), and torch.matmul (hipBLASLt /
-the fp64 path) on the same shapes as run-only comparators.
+the fp64 path) on the same shapes and a 1 GiB device copy (an achievable HBM
+rate) as run-only comparators.
 
 "roofline" reports the dominant kernel (the DMA-fed 256x256 GEMM kernel) against
 the MI355X dense fp16 matrix peak: achieved = 2*M*N*K flop per launch divided
@@ -43,6 +44,9 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_square_f16_8192.json")
 CLOCK_FILE = os.path.join(ROOT, "profiles", "clock_square_f16_8192.json")
 CLOCK_COUNTERS = ("GRBM_GUI_ACTIVE", "GRBM_COUNT", "SQ_BUSY_CYCLES", "SQ_VALU_MFMA_BUSY_CYCLES",
                   "SQ_INSTS_VALU_MFMA_MOPS_F16", "SQ_INSTS_MFMA")
+# a second run of the clock pass: LDS and L2 behaviour
+LDS_COUNTERS = ("GRBM_GUI_ACTIVE", "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "SQ_INSTS_LDS",
+                "TCC_HIT_sum", "TCC_MISS_sum")
 
 
 def kernel_source_hash() -> str:
@@ -96,7 +100,7 @@ def write_traffic(fetch_csv, write_csv):
     print(json.dumps(out))
 
 
-def write_clock(counter_csv, agent_csv):
+def write_clock(counter_csv, agent_csv, lds_csv=None):
     """Turn one rocprofv3 --pmc run of `bench.py --clock-pass` (the CLOCK_COUNTERS)
     into the engine cycles, clock and matrix-core occupancy of the headline
     kernel, of hipBLASLt's kernel for the same product and of a plain copy.
@@ -107,20 +111,27 @@ def write_clock(counter_csv, agent_csv):
     summed over SIMDs, over those cycles times the SIMD count is the fraction of
     cycles the matrix units were busy; that is the kernel's fraction of the
     matrix peak at whatever clock it ran.  The fp16 MFMA op counter (512 flop
-    per op) checks the flop count against 2*M*N*K."""
+    per op) checks the flop count against 2*M*N*K.  The optional second run
+    (LDS_COUNTERS) adds, per CU and cycle, the LDS bank-conflict and LDS-active
+    cycles, and the L2 hit rate."""
     import csv
 
     with open(agent_csv) as f:
         gpu = next(r for r in csv.DictReader(f) if r["Agent_Type"] == "GPU")
     xcc, simds = int(gpu["Num_Xcc"]), int(gpu["Simd_Count"])
     fmax_ghz = int(gpu["Max_Engine_Clk_Fcompute"]) / 1000.0
-    disp = {}
-    with open(counter_csv) as f:
-        for r in csv.DictReader(f):
-            d = disp.setdefault(r["Dispatch_Id"], {
-                "name": r["Kernel_Name"],
-                "ns": int(r["End_Timestamp"]) - int(r["Start_Timestamp"])})
-            d[r["Counter_Name"]] = float(r["Counter_Value"])
+    cus = int(gpu["Cu_Count"])
+
+    def dispatches(path):
+        disp = {}
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                d = disp.setdefault(r["Dispatch_Id"], {
+                    "name": r["Kernel_Name"],
+                    "ns": int(r["End_Timestamp"]) - int(r["Start_Timestamp"])})
+                d[r["Counter_Name"]] = float(r["Counter_Value"])
+        return disp
+    disp = dispatches(counter_csv)
 
     def kind(name):
         if "gemm_dma_kernel" in name:
@@ -157,6 +168,27 @@ def write_clock(counter_csv, agent_csv):
                   "min_clock_ghz": min(x["ghz"] for x in g), "max_clock_ghz": max(x["ghz"] for x in g),
                   "mfma_busy_frac": mean["mfma_busy"], "mfma_tflop_per_launch": mean["mfma_tflop"],
                   "mfma_insts_per_launch": mean["mfma_insts"]}
+    if lds_csv:
+        out["counters"] += [c for c in LDS_COUNTERS if c not in out["counters"]]
+        lds = {}
+        for d in dispatches(lds_csv).values():
+            k = kind(d["name"])
+            if k is None or "GRBM_GUI_ACTIVE" not in d or "SQ_LDS_IDX_ACTIVE" not in d:
+                continue
+            cyc = d["GRBM_GUI_ACTIVE"] / xcc
+            hit, miss = d.get("TCC_HIT_sum", 0.0), d.get("TCC_MISS_sum", 0.0)
+            lds.setdefault(k, []).append({
+                "conflict": d["SQ_LDS_BANK_CONFLICT"] / (cyc * cus),
+                "active": d["SQ_LDS_IDX_ACTIVE"] / (cyc * cus),
+                "insts": d.get("SQ_INSTS_LDS", 0.0),
+                "l2hit": hit / (hit + miss) if hit + miss > 0 else 0.0})
+        for k, g in lds.items():
+            if k in out:
+                out[k].update({
+                    "lds_bank_conflict_per_cu_cycle": statistics.mean(x["conflict"] for x in g),
+                    "lds_active_per_cu_cycle": statistics.mean(x["active"] for x in g),
+                    "lds_insts_per_launch": statistics.mean(x["insts"] for x in g),
+                    "l2_hit_rate": statistics.mean(x["l2hit"] for x in g)})
     with open(CLOCK_FILE, "w") as f:
         json.dump(out, f, indent=1)
         f.write("\n")
@@ -256,6 +288,18 @@ def bench_splitk(name, split, torch, imm, wl, n=30, warmup=5, M=None):
             "pct_hbm_peak": 100.0 * algo / (med * 1e-3) / 1e9 / PEAK_HBM_GBS,
             "TFLOPs": 2.0 * Mrows * w.N * w.K / (med * 1e-3) / 1e12,
             "workspace_traffic_bytes": 2 * plan.info["workspace_bytes"]}
+
+
+def bench_hbm_probes(torch, nbytes=2 ** 30):
+    """An achievable HBM rate on this part, from the runtime's device copy of
+    1 GiB (read + write bytes over time; a comparator only)."""
+    x = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    y = torch.empty_like(x)
+    tc, _ = time_launches(lambda i: y.copy_(x), 20, 5, torch)
+    out = {"bytes": nbytes, "copy_GBps": 2 * nbytes / (statistics.median(tc) * 1e-3) / 1e9}
+    del x, y
+    torch.cuda.empty_cache()
+    return out
 
 
 def bench_m_sweep(torch, imm, wl, N=6144, K=4096, ms=(1, 16, 64, 256, 1024, 4096, 8192)):
@@ -371,14 +415,17 @@ def main():
                     help="back-to-back launches of the headline kernel, of torch.matmul on "
                          "the same fp16 product and of a plain copy, for the clock counters; "
                          "prints nothing else")
-    ap.add_argument("--write-clock", nargs=2, metavar=("COUNTER_CSV", "AGENT_CSV"),
-                    help="host only: write the headline kernel's engine clock and matrix-core "
-                         "occupancy from a counter run of --clock-pass, then exit")
+    ap.add_argument("--write-clock", nargs="+", metavar="CSV",
+                    help="host only: COUNTER_CSV AGENT_CSV [LDS_CSV]: write the headline kernel's "
+                         "engine clock and matrix-core occupancy from a counter run of "
+                         "--clock-pass (and LDS / L2 behaviour from a second one), then exit")
     args = ap.parse_args()
     if args.write_traffic:
         write_traffic(*args.write_traffic)
         return
     if args.write_clock:
+        if len(args.write_clock) not in (2, 3):
+            ap.error("--write-clock takes COUNTER_CSV AGENT_CSV [LDS_CSV]")
         write_clock(*args.write_clock)
         return
     if args.gpus != 1:
@@ -499,6 +546,11 @@ def main():
         log("decode bf16 N=4096 K=14336, split-K path")
         extra["decode_bf16"] = [bench_splitk("decode_bf16_m128", 0, torch, imm, wl, M=m)
                                 for m in (1, 8, 32, 128)]
+        log("HBM probe (1 GiB device copy)")
+        probes = bench_hbm_probes(torch)
+        extra["hbm_probes"] = probes
+        for d in extra["decode_bf16"]:
+            d["pct_of_copy_probe"] = 100.0 * d["GBps"] / probes["copy_GBps"]
         torch.cuda.empty_cache()
         log("M sweep on the fused-QKV projection shape N=6144 K=4096, gemm_run")
         extra["qkv_m_sweep_f16"] = bench_m_sweep(torch, imm, wl)
