@@ -60,7 +60,7 @@ def kernel_source_hash() -> str:
 COPY_BYTES = 256 * 2 ** 20  # the plain copy of the profile pass: this many bytes read and written
 
 
-def write_traffic(fetch_csv, write_csv):
+def write_traffic(fetch_csv, write_csv, out_path=TRAFFIC_FILE):
     """Turn two rocprofv3 --pmc runs of `bench.py --profile-pass` (FETCH_SIZE, then
     WRITE_SIZE, KiB per dispatch) into the per-launch HBM traffic of the headline
     kernel.  Each counter is scaled by what it reads for the plain copy of known
@@ -93,14 +93,14 @@ def write_traffic(fetch_csv, write_csv):
            "fetch_scale": ff, "write_scale": wf,
            "read_bytes_per_launch": gf * ff * 1024, "write_bytes_per_launch": gw * wf * 1024,
            "bytes_per_launch": (gf * ff + gw * wf) * 1024}
-    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
-    with open(TRAFFIC_FILE, "w") as f:
+    os.makedirs(os.path.dirname(out_path), exist_ok=True)
+    with open(out_path, "w") as f:
         json.dump(out, f, indent=1)
         f.write("\n")
     print(json.dumps(out))
 
 
-def write_clock(counter_csv, agent_csv, lds_csv=None):
+def write_clock(counter_csv, agent_csv, lds_csv=None, out_path=CLOCK_FILE):
     """Turn one rocprofv3 --pmc run of `bench.py --clock-pass` (the CLOCK_COUNTERS)
     into the engine cycles, clock and matrix-core occupancy of the headline
     kernel, of hipBLASLt's kernel for the same product and of a plain copy.
@@ -189,7 +189,7 @@ def write_clock(counter_csv, agent_csv, lds_csv=None):
                     "lds_active_per_cu_cycle": statistics.mean(x["active"] for x in g),
                     "lds_insts_per_launch": statistics.mean(x["insts"] for x in g),
                     "l2_hit_rate": statistics.mean(x["l2hit"] for x in g)})
-    with open(CLOCK_FILE, "w") as f:
+    with open(out_path, "w") as f:
         json.dump(out, f, indent=1)
         f.write("\n")
     print(json.dumps(out))

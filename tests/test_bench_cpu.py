@@ -1,0 +1,134 @@
+"""Host logic of bench.py, on the CPU: the --gpus contract and the two counter
+summaries (HBM traffic, clock and matrix-unit occupancy) on synthetic
+rocprofv3 CSV files of known content."""
+import csv
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+
+COUNTER_FIELDS = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value",
+                  "Start_Timestamp", "End_Timestamp"]
+HEADLINE = "void imm::(anonymous namespace)::gemm_dma_kernel<0, 4, 0, 256, 2, 2, false>(imm::GemmArgs)"
+BLAS = "Cijk_Ailk_Bljk_HHS_BH_MT256x256x64_MI16x16x1"
+COPY = "__amd_rocclr_copyBuffer"
+
+
+def write_counters(path, dispatches):
+    """dispatches: list of (id, kernel, start_ns, end_ns, {counter: value})."""
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=COUNTER_FIELDS)
+        w.writeheader()
+        for did, name, t0, t1, counters in dispatches:
+            for c, v in counters.items():
+                w.writerow({"Dispatch_Id": did, "Kernel_Name": name, "Counter_Name": c,
+                            "Counter_Value": v, "Start_Timestamp": t0, "End_Timestamp": t1})
+
+
+def write_agent(path, xcc=8, simds=1024, cus=256, mhz=2400):
+    fields = ["Agent_Type", "Num_Xcc", "Simd_Count", "Cu_Count", "Max_Engine_Clk_Fcompute"]
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=fields)
+        w.writeheader()
+        w.writerow({"Agent_Type": "CPU", "Num_Xcc": 0, "Simd_Count": 0, "Cu_Count": 0,
+                    "Max_Engine_Clk_Fcompute": 0})
+        w.writerow({"Agent_Type": "GPU", "Num_Xcc": xcc, "Simd_Count": simds, "Cu_Count": cus,
+                    "Max_Engine_Clk_Fcompute": mhz})
+
+
+def test_more_than_one_gpu_exits_with_a_message():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""
+
+
+def test_traffic_scales_each_counter_by_the_copy(tmp_path):
+    copy_kib = bench.COPY_BYTES / 1024
+    fetch, write = tmp_path / "fetch.csv", tmp_path / "write.csv"
+    # FETCH_SIZE reads half a copy's bytes, WRITE_SIZE all of them
+    write_counters(fetch, [(1, COPY, 0, 10, {"FETCH_SIZE": copy_kib / 2}),
+                           (2, HEADLINE, 20, 30, {"FETCH_SIZE": 1000.0}),
+                           (3, HEADLINE, 40, 50, {"FETCH_SIZE": 3000.0})])
+    write_counters(write, [(1, COPY, 0, 10, {"WRITE_SIZE": copy_kib}),
+                           (2, HEADLINE, 20, 30, {"WRITE_SIZE": 500.0})])
+    out = tmp_path / "traffic.json"
+    bench.write_traffic(str(fetch), str(write), out_path=str(out))
+    t = json.loads(out.read_text())
+    assert t["fetch_scale"] == pytest.approx(2.0)
+    assert t["write_scale"] == pytest.approx(1.0)
+    assert t["launches"] == 2
+    assert t["read_bytes_per_launch"] == pytest.approx(2000.0 * 2 * 1024)
+    assert t["write_bytes_per_launch"] == pytest.approx(500.0 * 1024)
+    assert t["bytes_per_launch"] == pytest.approx((4000.0 + 500.0) * 1024)
+    assert t["kernel_source_hash"] == bench.kernel_source_hash()
+
+
+def test_traffic_without_the_copy_is_an_error(tmp_path):
+    fetch = tmp_path / "fetch.csv"
+    write_counters(fetch, [(2, HEADLINE, 20, 30, {"FETCH_SIZE": 1000.0})])
+    with pytest.raises(SystemExit):
+        bench.write_traffic(str(fetch), str(fetch), out_path=str(tmp_path / "t.json"))
+
+
+def test_clock_cycles_occupancy_lds_and_l2(tmp_path):
+    agent, counters, lds = tmp_path / "agent.csv", tmp_path / "c.csv", tmp_path / "lds.csv"
+    write_agent(agent)
+    cyc = 1.5e6                      # per XCD
+    ns = 1.0e6                       # 1 ms: 1.5 GHz
+    busy = 0.75 * cyc * 1024         # matrix units busy 75 % of the SIMD-cycles
+    head = {"GRBM_GUI_ACTIVE": 8 * cyc, "SQ_VALU_MFMA_BUSY_CYCLES": busy,
+            "SQ_INSTS_VALU_MFMA_MOPS_F16": 2.0 ** 40 / 512, "SQ_INSTS_MFMA": 2.0 ** 26}
+    write_counters(counters, [
+        (1, COPY, 0, 400_000, {"GRBM_GUI_ACTIVE": 8 * 0.96e6}),                 # 2.4 GHz
+        (2, HEADLINE, 1_000_000, 1_000_000 + int(ns), head),
+        (3, HEADLINE, 3_000_000, 3_000_000 + int(2 * ns), dict(head)),          # same cycles, half clock
+        (4, BLAS, 6_000_000, 6_000_000 + int(ns), {"GRBM_GUI_ACTIVE": 8 * 1.6e6,
+                                                   "SQ_VALU_MFMA_BUSY_CYCLES": 0.5 * 1.6e6 * 1024}),
+        (5, "some_other_kernel", 0, 10, {"GRBM_GUI_ACTIVE": 5.0})])
+    write_counters(lds, [(7, HEADLINE, 0, int(ns), {"GRBM_GUI_ACTIVE": 8 * cyc,
+                                                     "SQ_LDS_BANK_CONFLICT": 0.0,
+                                                     "SQ_LDS_IDX_ACTIVE": 0.25 * cyc * 256,
+                                                     "SQ_INSTS_LDS": 123.0,
+                                                     "TCC_HIT_sum": 78.0, "TCC_MISS_sum": 22.0})])
+    out = tmp_path / "clock.json"
+    bench.write_clock(str(counters), str(agent), str(lds), out_path=str(out))
+    c = json.loads(out.read_text())
+    h = c["headline"]
+    assert h["dispatches"] == 2
+    assert h["mean_cycles"] == pytest.approx(cyc)
+    assert h["min_clock_ghz"] == pytest.approx(0.75)
+    assert h["max_clock_ghz"] == pytest.approx(1.5)
+    assert h["mfma_busy_frac"] == pytest.approx(0.75)
+    assert h["mfma_tflop_per_launch"] == pytest.approx(2.0 ** 40 / 1e12)
+    assert h["lds_active_per_cu_cycle"] == pytest.approx(0.25)
+    assert h["lds_bank_conflict_per_cu_cycle"] == 0.0
+    assert h["l2_hit_rate"] == pytest.approx(0.78)
+    assert c["copy"]["mean_clock_ghz"] == pytest.approx(2.4)
+    assert c["hipblaslt"]["mfma_busy_frac"] == pytest.approx(0.5)
+    assert "some_other_kernel" not in json.dumps(c)
+    assert c["max_engine_clock_ghz"] == pytest.approx(2.4)
+    assert c["kernel_source_hash"] == bench.kernel_source_hash()
+
+
+def test_clock_without_the_headline_kernel_is_an_error(tmp_path):
+    agent, counters = tmp_path / "agent.csv", tmp_path / "c.csv"
+    write_agent(agent)
+    write_counters(counters, [(1, COPY, 0, 400_000, {"GRBM_GUI_ACTIVE": 8 * 0.96e6})])
+    with pytest.raises(SystemExit):
+        bench.write_clock(str(counters), str(agent), out_path=str(tmp_path / "x.json"))
+
+
+def test_committed_counter_files_match_the_kernel_sources():
+    """The traffic and clock summaries in profiles/ were taken with the kernel
+    sources as they are (bench.py reports them only then)."""
+    for path in (bench.TRAFFIC_FILE, bench.CLOCK_FILE):
+        with open(path) as f:
+            assert json.load(f)["kernel_source_hash"] == bench.kernel_source_hash(), path
