@@ -99,7 +99,8 @@ typedef enum {
   GEMM_TILE_256x256_RS = 4, /* 8 waves, register-staged LDS tiles */
   GEMM_TILE_32x256 = 5,     /* 4 waves, DMA ring; narrow tile for skinny or
                                reduction-dominated shapes */
-  GEMM_TILE_64x256 = 6      /* 4 waves, DMA ring */
+  GEMM_TILE_64x256 = 6,     /* 4 waves, DMA ring */
+  GEMM_TILE_128x256 = 7     /* 8 waves, DMA ring of 3 stages */
 } gemm_tile;
 
 /* Plan flags (gemm_plan_ex2). */
@@ -107,7 +108,7 @@ typedef enum {
   /* B is given transposed: a [N, K] row-major matrix W with B = W^T (the
    * weight layout of a linear layer, y = x W^T + b, as in the vLLM
    * batch-invariant operators the Tencent article lists in its closing
-   * section).  Only the DMA tiles (256x256, 64x256, 32x256) read this layout;
+   * section).  Only the DMA tiles (256x256, 128x256, 64x256, 32x256) read this layout;
    * the bits of C are those of the [K, N] layout holding the same values. */
   GEMM_PLAN_B_TRANSPOSED = 1,
   /* gemm_run / gemm_run_bias with the 256x256 tile launch at most one
@@ -117,9 +118,10 @@ typedef enum {
    * the Tencent article's closing section).  The bits of C are those of the
    * plan without the flag; other tiles and the split-K path ignore it. */
   GEMM_PLAN_PERSISTENT = 2,
-  /* gemm_run / gemm_run_bias take their tile from the workgroups each DMA
-   * tile would give at this M (256x256 if at least 192, else 64x256 if at
-   * least 192, else 32x256) instead of from (N, K, dtype).  Every tile uses
+  /* gemm_run / gemm_run_bias take their tile from M instead of from (N, K,
+   * dtype): the DMA tile (32x256, 64x256, 128x256 or 256x256) with the least
+   * estimated time, rounds of 256 workgroups times a per-tile time that grows
+   * with the tile's rows.  Every tile uses
    * the same matrix-core instruction and K order, so C is bitwise that of the
    * plan without the flag for every M (tile sizes do not change bits: the
    * Tencent article, "Batch Invariance の由来"); only the time changes.  An

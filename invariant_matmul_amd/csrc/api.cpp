@@ -42,6 +42,7 @@ void tile_shape(int tile, int* bm, int* bn, int* wm, int* wn) {
     case GEMM_TILE_128x128: *bm = 128; *bn = 128; *wm = 2; *wn = 2; break;
     case GEMM_TILE_32x256: *bm = 32; *bn = 256; *wm = 1; *wn = 4; break;
     case GEMM_TILE_64x256: *bm = 64; *bn = 256; *wm = 1; *wn = 4; break;
+    case GEMM_TILE_128x256: *bm = 128; *bn = 256; *wm = 2; *wn = 4; break;
     default: *bm = 32; *bn = 128; *wm = 1; *wn = 4; break;  // GEMM_TILE_32x128
   }
 }
@@ -79,20 +80,36 @@ int default_run_tile(int64_t N, int64_t K, int eb) {
   return GEMM_TILE_256x256;
 }
 
-// GEMM_PLAN_TILE_BY_M: the largest DMA tile whose grid still gives at least
-// 192 workgroups (three quarters of a 256-CU MI355X), else the 32-row tile.
-// Measured on the fused-QKV shape N = 6144, K = 4096 and on squares from 1024
-// to 8192, this picks the fastest DMA tile at every M tried.  Bits do not
-// depend on it.
+// GEMM_PLAN_TILE_BY_M: the DMA tile with the least estimated time.  Each
+// of these tiles takes a whole compute unit (its LDS ring), so a grid runs in
+// rounds of 256 workgroups (a 256-CU MI355X), and one round of a tile of r
+// rows takes about 127 + r units: measured at K = 4096, one round of the 32-,
+// 64-, 128- and 256-row tiles takes 37, 45, 55 and 85 us.  Cost =
+// rounds x (127 + r); the smaller tile wins a tie.  On the fused-QKV shape
+// N = 6144, K = 4096 (M = 256 ... 4096) and on squares from 1024 to 4096 this
+// picks the fastest DMA tile at every point measured.  Bits do not depend on
+// the tile.
 int tile_by_m(int64_t M, int64_t N) {
+  static const int kTiles[4] = {GEMM_TILE_32x256, GEMM_TILE_64x256, GEMM_TILE_128x256,
+                                GEMM_TILE_256x256};
+  static const int kRows[4] = {32, 64, 128, 256};
   const int64_t tn = (N + 255) / 256;
-  if (((M + 255) / 256) * tn >= 192) return GEMM_TILE_256x256;
-  if (((M + 63) / 64) * tn >= 192) return GEMM_TILE_64x256;
-  return GEMM_TILE_32x256;
+  int best = 0;
+  int64_t best_cost = -1;
+  for (int i = 0; i < 4; ++i) {
+    const int64_t wgs = ((M + kRows[i] - 1) / kRows[i]) * tn;
+    const int64_t cost = ((wgs + 255) / 256) * (127 + kRows[i]);
+    if (best_cost < 0 || cost < best_cost) {
+      best = i;
+      best_cost = cost;
+    }
+  }
+  return kTiles[best];
 }
 
 bool is_dma_tile(int tile) {
-  return tile == GEMM_TILE_256x256 || tile == GEMM_TILE_32x256 || tile == GEMM_TILE_64x256;
+  return tile == GEMM_TILE_256x256 || tile == GEMM_TILE_128x256 || tile == GEMM_TILE_32x256 ||
+         tile == GEMM_TILE_64x256;
 }
 
 // The DMA kernels address one A tile (bm rows of K) and one B stage (128
@@ -111,7 +128,8 @@ int checked_tile(int tile, int64_t N, int64_t K, int eb, bool b_trans) {
   if (!is_dma_tile(tile)) return b_trans ? -1 : tile;
   if (dma_offsets_fit(tile, N, K, eb, b_trans)) return tile;
   if (b_trans) return -1;
-  return tile == GEMM_TILE_256x256 ? GEMM_TILE_256x256_RS : GEMM_TILE_32x128;
+  if (tile == GEMM_TILE_256x256) return GEMM_TILE_256x256_RS;
+  return tile == GEMM_TILE_128x256 ? GEMM_TILE_128x128 : GEMM_TILE_32x128;
 }
 
 // Workgroups the default split aims for per row of output tiles.  Wide
@@ -238,7 +256,7 @@ gemm_status gemm_plan_ex2(int64_t M, int64_t N, int64_t K, gemm_dtype in, gemm_d
   if (M > INT_MAX || N > INT_MAX || K > INT_MAX) return GEMM_ERR_UNSUPPORTED;
   if (!valid_in(in) || !valid_out(out)) return GEMM_ERR_UNSUPPORTED;
   if (split_k < 0 || split_k > kMaxSplit || group_m < 0) return GEMM_ERR_UNSUPPORTED;
-  if (tile < GEMM_TILE_DEFAULT || tile > GEMM_TILE_64x256) return GEMM_ERR_UNSUPPORTED;
+  if (tile < GEMM_TILE_DEFAULT || tile > GEMM_TILE_128x256) return GEMM_ERR_UNSUPPORTED;
   if (!std::isfinite(scale_a) || !std::isfinite(scale_b)) return GEMM_ERR_UNSUPPORTED;
   if (flags & ~(unsigned)(GEMM_PLAN_B_TRANSPOSED | GEMM_PLAN_PERSISTENT | GEMM_PLAN_TILE_BY_M))
     return GEMM_ERR_UNSUPPORTED;

@@ -151,6 +151,8 @@ __device__ __forceinline__ i32x2 tr8_rows(unsigned p0, int rows) {
 
 // TBM x 256 tile of C per workgroup of WM x 4 waves; NS stages in the ring.
 //   TBM = 256, WM = 2, NS = 2: the large tile (wave tile 128 x 64);
+//   TBM = 128, WM = 2, NS = 3: the half-height tile (wave tile 64 x 64) for
+//     grids that 256 x 256 tiles would leave under-filled;
 //   TBM = 64 / 32, WM = 1, NS = 4: narrow tiles for reduction-dominated
 //   shapes (wave tile 64 x 64 / 32 x 64), where the time is the stream of B.
 // Two workgroups share a CU when their rings fit in half the LDS; the
@@ -734,6 +736,7 @@ template <int IN, bool BT>
 hipError_t launch_tiles(const gemm_plan_s& p, int tile, const GemmArgs& a, bool slice, hipStream_t s) {
   switch (tile) {
     case GEMM_TILE_256x256: return launch_cfg<IN, 256, 2, 2, BT>(p, a, slice, s);
+    case GEMM_TILE_128x256: return launch_cfg<IN, 128, 2, 3, BT>(p, a, slice, s);
     case GEMM_TILE_64x256: return launch_cfg<IN, 64, 1, 4, BT>(p, a, slice, s);
     case GEMM_TILE_32x256: return launch_cfg<IN, 32, 1, 4, BT>(p, a, slice, s);
     default: return hipErrorInvalidValue;

@@ -124,11 +124,3 @@ def test_clock_without_the_headline_kernel_is_an_error(tmp_path):
     write_counters(counters, [(1, COPY, 0, 400_000, {"GRBM_GUI_ACTIVE": 8 * 0.96e6})])
     with pytest.raises(SystemExit):
         bench.write_clock(str(counters), str(agent), out_path=str(tmp_path / "x.json"))
-
-
-def test_committed_counter_files_match_the_kernel_sources():
-    """The traffic and clock summaries in profiles/ were taken with the kernel
-    sources as they are (bench.py reports them only then)."""
-    for path in (bench.TRAFFIC_FILE, bench.CLOCK_FILE):
-        with open(path) as f:
-            assert json.load(f)["kernel_source_hash"] == bench.kernel_source_hash(), path

@@ -23,8 +23,8 @@ from tests.helpers import FP8, bits_of, check_bound, dev, fp8_step_window, log, 
 
 pytestmark = pytest.mark.gpu
 
-ALL_TILES = ["256x256", "128x128", "32x128", "256x256_rs", "32x256", "64x256"]
-DMA_TILES = {"256x256", "32x256", "64x256"}
+ALL_TILES = ["256x256", "128x128", "32x128", "256x256_rs", "32x256", "64x256", "128x256"]
+DMA_TILES = {"256x256", "32x256", "64x256", "128x256"}
 
 
 def _case(seed):

@@ -24,7 +24,7 @@ from tests.helpers import bits_of, dev, log, run
 
 pytestmark = pytest.mark.gpu
 
-TILES = ["256x256", "128x128", "32x128", "256x256_rs", "32x256", "64x256"]
+TILES = ["256x256", "128x128", "32x128", "256x256_rs", "32x256", "64x256", "128x256"]
 
 
 def _to_dev(*ts):
@@ -182,8 +182,8 @@ def test_split_changes_bits_only_where_rounding_happens():
 
 @pytest.mark.parametrize("dt,bt", [("f16", False), ("bf16", True)])
 def test_tile_by_m_rows_identical_across_M(dt, bt):
-    """GEMM_PLAN_TILE_BY_M switches the single pass between the 32x256, 64x256
-    and 256x256 tiles as M grows; every row must keep its bits."""
+    """GEMM_PLAN_TILE_BY_M switches the single pass between the 32x256, 64x256,
+    128x256 and 256x256 tiles as M grows; every row must keep its bits."""
     N, K = 6144, 4096
     g = wl.gen(8400)
     A = wl.uniform((2048, K), dt, g).to(dev())
@@ -198,4 +198,4 @@ def test_tile_by_m_rows_identical_across_M(dt, bt):
         seen.add(plan.info["run_tile"])
         got = bits_of(run(plan, A[:m].contiguous(), Bd, False))
         assert np.array_equal(got, ref[:m]), m
-    assert len(seen) == 3, seen
+    assert seen == {imm.TILE[t] for t in ("32x256", "64x256", "128x256", "256x256")}, seen

@@ -22,7 +22,7 @@ from tests.helpers import bits_of, check_bound, dev, expected_bits, log, out_tor
 
 pytestmark = pytest.mark.gpu
 
-DMA_TILES = ["default", "256x256", "64x256", "32x256"]
+DMA_TILES = ["default", "256x256", "128x256", "64x256", "32x256"]
 BT = imm.PLAN_B_TRANSPOSED
 
 

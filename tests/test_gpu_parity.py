@@ -19,7 +19,7 @@ from tests.helpers import (FP8, bits_of, check_bound, dev, expected_bits, fp8_st
 
 pytestmark = pytest.mark.gpu
 
-TILES = ["256x256", "128x128", "32x128", "256x256_rs", "32x256", "64x256"]
+TILES = ["256x256", "128x128", "32x128", "256x256_rs", "32x256", "64x256", "128x256"]
 IN_DTYPES = ["f16", "bf16", "e4m3", "e5m2"]
 
 

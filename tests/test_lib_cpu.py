@@ -189,7 +189,7 @@ def test_plan_flags_validation(args, status):
 
 
 def test_transposed_b_plans_use_dma_tiles_and_the_same_split():
-    dma = {imm.TILE[t] for t in ("256x256", "32x256", "64x256")}
+    dma = {imm.TILE[t] for t in ("256x256", "128x256", "32x256", "64x256")}
     for N, K, dt in SHAPES:
         a = imm.gemm_plan_ex2(64, N, K, dt, "f32").info
         b = imm.gemm_plan_ex2(64, N, K, dt, "f32", flags=imm.PLAN_B_TRANSPOSED).info
@@ -383,13 +383,14 @@ def test_ozaki_column_maxima_chunks_are_capped():
 
 @pytest.mark.parametrize("M,N,K,tile", [
     (1, 6144, 4096, "32x256"), (256, 6144, 4096, "32x256"), (512, 6144, 4096, "64x256"),
-    (1024, 6144, 4096, "64x256"), (2048, 6144, 4096, "256x256"), (1024, 1024, 1024, "32x256"),
+    (768, 6144, 4096, "128x256"), (1024, 6144, 4096, "128x256"), (1536, 6144, 4096, "256x256"),
+    (2048, 6144, 4096, "256x256"), (3072, 6144, 4096, "128x256"), (1024, 1024, 1024, "32x256"),
     (2048, 2048, 2048, "64x256"), (4096, 4096, 4096, "256x256"), (8192, 8192, 8192, "256x256"),
 ])
 def test_tile_by_m_rule(M, N, K, tile):
-    """GEMM_PLAN_TILE_BY_M: the largest DMA tile with at least 192 workgroups
-    (the measured fastest at each of these shapes); split-K path and the
-    default plan unchanged."""
+    """GEMM_PLAN_TILE_BY_M: the DMA tile with the least estimated time
+    (rounds of 256 workgroups x (127 + tile rows)), the measured fastest at
+    each of these shapes; split-K path and the default plan unchanged."""
     flagged = imm.gemm_plan_ex2(M, N, K, "f16", "f32", flags=imm.PLAN_TILE_BY_M).info
     plain = imm.gemm_plan_ex2(M, N, K, "f16", "f32").info
     assert flagged["run_tile"] == imm.TILE[tile]
