@@ -389,9 +389,12 @@ gemm_status gemm_run_bias(gemm_plan_t p, const void* A, const void* B, const flo
   if (e != hipSuccess) return hip_fail(e);
   GemmArgs a = make_args(p, A, B, C, false);
   a.bias = bias;
-  // The persistent kernel evaluates the raster in 32-bit arithmetic.
+  // The persistent kernel evaluates the raster in 32-bit arithmetic and
+  // needs whole K stages (its transfers carry no K check); otherwise the
+  // plan runs one tile per workgroup, with the same bits.
   const bool raster32 = a.grid < INT_MAX && a.group_m * a.tiles_n < INT_MAX;
-  if (p->persistent && p->run_tile == GEMM_TILE_256x256 && p->K > 0 && raster32) {
+  if (p->persistent && p->run_tile == GEMM_TILE_256x256 && p->K > 0 && p->K % p->bk == 0 &&
+      raster32) {
     // One workgroup per compute unit (a multiple of 8, the XCD count, so
     // that every virtual workgroup stays on the XCD the raster assigns it);
     // the device query only places work, it never changes a bit.

@@ -370,16 +370,25 @@ __global__ __launch_bounds__(256 * WM, (waves_per_simd<TBM, WM, NS>())) void gem
   // else B rows.
   auto dma_one = [&](const StageSrc& q, int t, int x) {
     if (x < DA) {
-      bool ok = a_kel[x] < q.rem;
-      if constexpr (PER_TILE) ok = ok && ((q.amask >> x) & 1u);
+      // MODE_PERSIST runs only where K is a multiple of the stage (every stage
+      // is whole) and past the last tile the masks are clear: the masks
+      // alone decide.
+      bool ok;
+      if constexpr (PER_TILE)
+        ok = (q.amask >> x) & 1u;
+      else
+        ok = a_kel[x] < q.rem;
       const unsigned off = ok ? a_off[x] : OOB;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           __builtin_amdgcn_make_buffer_rsrc((void*)q.pa, 0, NREC, RSRC_FLAGS),
           IMM_LDS(lds + a_slot(t) + (w * DA + x) * 1024), 16, off, 0, 0, 0);
     } else {
       const int i = x - DA;
-      bool ok = b_k[i] < q.rem;
-      if constexpr (PER_TILE) ok = ok && ((q.bmask >> i) & 1u);
+      bool ok;
+      if constexpr (PER_TILE)
+        ok = (q.bmask >> i) & 1u;
+      else
+        ok = b_k[i] < q.rem;
       const unsigned off = ok ? b_off[i] : OOB;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           __builtin_amdgcn_make_buffer_rsrc((void*)q.pb, 0, NREC, RSRC_FLAGS),
