@@ -6,7 +6,8 @@ Prints ONE JSON line.  The headline workload is the square fp16 product
 M = N = K = 8192 with fp32 output through gemm_run (one step = one product
 over one batch of seeded synthetic input already resident in HBM); `value`
 is its throughput in TFLOP/s.  The same run also measures, as secondary
-results under "extra": the fp8 e5m2 8192^3 product (bf16 out), the decode
+results under "extra": the headline product with its inputs rotated over two
+copies (no help from the last-level cache), the fp8 e5m2 8192^3 product (bf16 out), the decode
 products N=4096 K=14336 at M in {1, 8, 32, 128} through the split-K path
 (GB/s, inputs rotated through enough copies to defeat the 256 MB last-level
 cache), the huge-K product 256 x 256 x 131072 at split_k in {1, 8, 32, 128},
@@ -523,7 +524,18 @@ def main():
             extra["torch_matmul_f16_8192_TFLOPs"] = w.flops / (statistics.median(tper) * 1e-3) / 1e12
         except Exception as e:  # comparator only
             extra["torch_matmul_error"] = str(e)
-        del Ad, Bd
+        # The same product with A and B rotated over two copies (537 MB, twice
+        # the 256 MB last-level cache), so that no launch finds its operands
+        # left in that cache by the one before.
+        log("headline with rotated inputs")
+        Cr = torch.empty((w.M, w.N), dtype=torch.float32, device="cuda")
+        As, Bs = [Ad, Ad.clone()], [Bd, Bd.clone()]
+        rper, _ = time_launches(lambda i: imm.gemm_run(plan, As[i % 2], Bs[i % 2], Cr), 20, 4, torch)
+        extra["headline_rotated_inputs"] = {
+            **summary(rper), "copies": 2,
+            "TFLOPs": w.flops / (statistics.median(rper) * 1e-3) / 1e12,
+            "pct_mfma_peak": 100.0 * w.flops / (statistics.median(rper) * 1e-3) / 1e12 / PEAK_TFLOPS["f16"]}
+        del Ad, Bd, As, Bs, Cr
         torch.cuda.empty_cache()
         log("fp8 e5m2 8192^3")
         w8, plan8, per8, _, _ = bench_square("square_e5m2_8192", 30, 5, torch, imm, wl)
