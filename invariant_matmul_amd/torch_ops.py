@@ -4,12 +4,14 @@ The Tencent deterministic-inference article closes with vLLM's
 batch-invariant mode, which replaces ``mm``, ``addmm``, ``matmul`` and
 ``linear`` with a GEMM whose configuration never depends on the batch size.
 This module gives the same four operators on this library, and a context
-manager that routes torch's own entry points through them:
+manager that installs the library as torch's CUDA kernels of ``aten::mm`` and
+``aten::addmm`` (through ``torch.library``, the mechanism of that mode), so
+every CUDA product that reaches them takes the library's path:
 
     from invariant_matmul_amd import torch_ops
     y = torch_ops.linear(x, weight, bias)          # x [..., K], weight [N, K]
     with torch_ops.batch_invariant_mode():
-        y = model(x)                               # nn.Linear, torch.mm, @ ...
+        y = model(x)                               # nn.Linear, torch.mm, x.mm, @ ...
 
 The split of K is planned from (N, K, dtype) alone (the library's rule) and
 the single pass takes its output tile from M (GEMM_PLAN_TILE_BY_M), which
@@ -26,15 +28,21 @@ slices, default slice count and Fast Mode threshold: the Insight Edge cuTile
 blog's FP64 emulation, here with one exponent per row, so it is batch-
 invariant too); a bias is then added with one fp64 addition.  Any N and K.
 
-The direct functions raise for anything else.  The context manager only
-reroutes what the library computes (2-D weights; fp16 / bf16 with N and K
-multiples of 8, or fp64; alpha = beta = 1) and leaves other calls (fp32
-tensors, CPU tensors, batched weights) to torch's own implementation.
+The direct functions raise for anything else.  Under the context manager the
+library computes what it supports (2-D weights; fp16 / bf16 with N and K
+multiples of 8, or fp64; alpha = beta = 1; a bias of N values); other CUDA
+calls of aten::mm / aten::addmm (fp32 tensors, a full-matrix bias, other
+alpha and beta) run on torch's own batched GEMM (aten::bmm, batch of one),
+since the registration replaces torch's mm kernel while it is active.  CPU
+tensors and batched products (aten::bmm) are not affected.  Autograd's
+backward products go through aten::mm too, so they take the same path.
 """
 from __future__ import annotations
 
 import contextlib
 import functools
+import threading
+import warnings
 
 import torch
 
@@ -159,47 +167,60 @@ def matmul(a: torch.Tensor, b: torch.Tensor) -> torch.Tensor:
     return _product(a.reshape(-1, a.shape[-1]), b, None).reshape(*lead, b.shape[1])
 
 
+def _torch_mm(a: torch.Tensor, b: torch.Tensor) -> torch.Tensor:
+    """a @ b on torch's batched GEMM (a batch of one); both operands contiguous."""
+    return torch.bmm(a.unsqueeze(0).contiguous(), b.unsqueeze(0).contiguous()).squeeze(0)
+
+
+def _row_bias(bias: torch.Tensor, N: int) -> bool:
+    """True if bias holds N values broadcast over the rows."""
+    return bias.numel() == N and (bias.dim() == 1 or (bias.dim() == 2 and bias.shape[0] == 1))
+
+
+def _mode_mm(a, b):
+    if a.dim() == 2 and supported(a, b):
+        return _product(a, b, None)
+    return _torch_mm(a, b)
+
+
+def _mode_addmm(bias, a, b, *, beta=1, alpha=1):
+    if (beta == 1 and alpha == 1 and a.dim() == 2 and supported(a, b)
+            and _row_bias(bias, b.shape[1])):
+        return _product(a, b, bias)
+    r = _torch_mm(a, b)
+    if alpha != 1:
+        r = r * alpha
+    if beta == 0:
+        return r
+    return r + (bias if beta == 1 else bias * beta)
+
+
+_mode_lock = threading.Lock()
+_mode_depth = 0
+_mode_lib = None
+
+
 @contextlib.contextmanager
 def batch_invariant_mode():
-    """Route torch.nn.functional.linear, torch.mm, torch.addmm, torch.matmul and
-    the ``@`` operator through this module while the context is active."""
-    import torch.nn.functional as F
-
-    saved = {"linear": F.linear, "mm": torch.mm, "addmm": torch.addmm,
-             "matmul": torch.matmul, "tmatmul": torch.Tensor.__matmul__}
-
-    def _linear(x, weight, bias=None):
-        if weight.dim() == 2 and supported(x, weight.t()) and (
-                bias is None or bias.numel() == weight.shape[0]):
-            return linear(x, weight, bias)
-        return saved["linear"](x, weight, bias)
-
-    def _mm(a, b, **kw):
-        if not kw and a.dim() == 2 and supported(a, b):
-            return mm(a, b)
-        return saved["mm"](a, b, **kw)
-
-    def _addmm(bias, a, b, *, beta=1, alpha=1, **kw):
-        if (not kw and beta == 1 and alpha == 1 and a.dim() == 2 and supported(a, b)
-                and bias.numel() == b.shape[1]):
-            return addmm(bias, a, b)
-        return saved["addmm"](bias, a, b, beta=beta, alpha=alpha, **kw)
-
-    def _matmul(a, b, **kw):
-        if not kw and isinstance(a, torch.Tensor) and isinstance(b, torch.Tensor) and supported(a, b):
-            return matmul(a, b)
-        return saved["matmul"](a, b, **kw)
-
-    def _tmatmul(a, b):
-        if isinstance(b, torch.Tensor) and supported(a, b):
-            return matmul(a, b)
-        return saved["tmatmul"](a, b)
-
-    F.linear, torch.mm, torch.addmm, torch.matmul = _linear, _mm, _addmm, _matmul
-    torch.Tensor.__matmul__ = _tmatmul
+    """Install this module's products as the CUDA kernels of aten::mm and
+    aten::addmm while the context is active (nested contexts share one
+    registration; the last exit removes it and torch's kernels return)."""
+    global _mode_depth, _mode_lib
+    with _mode_lock:
+        if _mode_depth == 0:
+            lib = torch.library.Library("aten", "IMPL")
+            with warnings.catch_warnings():
+                # replacing a registered kernel is what this mode is for
+                warnings.simplefilter("ignore")
+                lib.impl("mm", _mode_mm, "CUDA")
+                lib.impl("addmm", _mode_addmm, "CUDA")
+            _mode_lib = lib
+        _mode_depth += 1
     try:
         yield
     finally:
-        F.linear, torch.mm, torch.addmm = saved["linear"], saved["mm"], saved["addmm"]
-        torch.matmul, torch.Tensor.__matmul__ = saved["matmul"], saved["tmatmul"]
-
+        with _mode_lock:
+            _mode_depth -= 1
+            if _mode_depth == 0:
+                _mode_lib._destroy()
+                _mode_lib = None

@@ -115,3 +115,63 @@ def test_fp64_products_go_through_the_ozaki_scheme():
     with torch_ops.batch_invariant_mode():
         part = (ad[:7] @ bd).cpu().numpy()
     assert np.array_equal(part, got[:7])
+
+
+def test_mode_routes_every_entry_point_through_the_library():
+    """Under the mode, aten::mm and aten::addmm are the library's: torch.mm,
+    the Tensor.mm and Tensor.matmul methods, @, F.linear on 2-D and 3-D input
+    and nn.Linear give the direct functions' bits."""
+    M, N, K = 48, 384, 256
+    g = wl.gen(8600)
+    x = wl.uniform((M, K), "f16", g).to(dev())
+    W = wl.normal((N, K), "f16", g, std=K ** -0.5).to(dev())
+    bias = wl.normal((N,), "f16", g).to(dev())
+    want_mm = bits_of(torch_ops.mm(x, W.t().contiguous()))
+    want_lin = bits_of(torch_ops.linear(x, W, bias))
+    lin = torch.nn.Linear(K, N).to(dev(), torch.float16)
+    with torch.no_grad():
+        lin.weight.copy_(W)
+        lin.bias.copy_(bias)
+    Wt = W.t().contiguous()
+    with torch.no_grad(), torch_ops.batch_invariant_mode():
+        for got in (torch.mm(x, Wt), x.mm(Wt), x.matmul(Wt), x @ Wt, torch.matmul(x, Wt)):
+            assert np.array_equal(bits_of(got), want_mm)
+        for got in (torch.nn.functional.linear(x, W, bias), lin(x),
+                    torch.nn.functional.linear(x.reshape(4, 12, K), W, bias).reshape(M, N)):
+            assert np.array_equal(bits_of(got), want_lin)
+
+
+def test_mode_falls_back_to_torch_for_other_products():
+    """fp32 CUDA products and addmm with alpha / beta or a full-matrix bias run
+    on torch's batched GEMM under the mode: the values torch gives outside it."""
+    g = torch.Generator().manual_seed(8700)
+    a = torch.randn((40, 96), generator=g).to(dev())
+    b = torch.randn((96, 72), generator=g).to(dev())
+    full = torch.randn((40, 72), generator=g).to(dev())
+    ah, bh = a.half(), b.half()
+    ref = (a @ b, torch.addmm(full, a, b), torch.addmm(full.half(), ah, bh, beta=0.5, alpha=2.0))
+    with torch_ops.batch_invariant_mode():
+        got = (a @ b, torch.addmm(full, a, b), torch.addmm(full.half(), ah, bh, beta=0.5, alpha=2.0))
+    for r, x in zip(ref, got):
+        assert x.dtype == r.dtype and x.shape == r.shape
+        assert torch.allclose(x.float(), r.float(), rtol=2e-2, atol=2e-2)
+
+
+def test_backward_under_the_mode_is_batch_invariant():
+    """Autograd's backward products are aten::mm calls too: under the mode the
+    input gradient of each row depends only on that row."""
+    torch.manual_seed(0)
+    layer = torch.nn.Linear(512, 256).to(dev(), torch.float16)
+    g = torch.Generator().manual_seed(8800)
+    x = torch.randn((64, 512), generator=g).to(dev(), torch.float16)
+    gy = torch.randn((64, 256), generator=g).to(dev(), torch.float16)
+
+    def input_grad(rows):
+        xi = x[:rows].clone().requires_grad_(True)
+        with torch_ops.batch_invariant_mode():
+            layer(xi).backward(gy[:rows])
+        return bits_of(xi.grad)
+
+    full = input_grad(64)
+    for m in (1, 5, 33):
+        assert np.array_equal(input_grad(m), full[:m]), m

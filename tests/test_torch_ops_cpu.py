@@ -5,13 +5,26 @@ import torch.nn.functional as F
 from invariant_matmul_amd import torch_ops
 
 
-def test_mode_restores_torch_entry_points():
-    before = (F.linear, torch.mm, torch.addmm, torch.matmul, torch.Tensor.__matmul__)
+def _cuda_kernels(op):
+    """The dispatcher's CUDA-key registrations of an aten operator."""
+    return [ln for ln in torch._C._dispatch_dump(op).splitlines() if ln.startswith("CUDA")]
+
+
+def test_mode_registers_and_removes_the_cuda_kernels():
+    before = {op: _cuda_kernels(op) for op in ("aten::mm", "aten::addmm", "aten::bmm")}
+    assert all(len(v) == 1 for v in before.values())
     with torch_ops.batch_invariant_mode():
-        inside = (F.linear, torch.mm, torch.addmm, torch.matmul, torch.Tensor.__matmul__)
-        assert all(a is not b for a, b in zip(before, inside))
-    after = (F.linear, torch.mm, torch.addmm, torch.matmul, torch.Tensor.__matmul__)
-    assert all(a is b for a, b in zip(before, after))
+        with torch_ops.batch_invariant_mode():      # nested: one registration
+            inner = {op: _cuda_kernels(op) for op in before}
+        outer = {op: _cuda_kernels(op) for op in before}
+        for op in ("aten::mm", "aten::addmm"):
+            # this module's kernel in front, torch's own one inactive behind it
+            assert len(inner[op]) == 2 and "(inactive)" in inner[op][1], inner[op]
+            assert "torch_ops.py" in inner[op][0], inner[op]
+            assert outer[op] == inner[op]
+        assert inner["aten::bmm"] == before["aten::bmm"]   # the fallback stays torch's
+    after = {op: _cuda_kernels(op) for op in before}
+    assert after == before
 
 
 def test_mode_leaves_cpu_and_fp32_products_to_torch():
