@@ -40,7 +40,7 @@ PEAK_TFLOPS = {"f16": 2516.6, "bf16": 2516.6, "e4m3": 5033.2, "e5m2": 5033.2, "i
 PEAK_HBM_GBS = 8000.0
 MALL_BYTES = 256 * 2 ** 20
 KERNEL_SOURCES = [os.path.join(ROOT, "invariant_matmul_amd", "csrc", f)
-                  for f in ("gemm_dma.hip", "kernel_common.h", "imm_internal.h", "api.cpp")]
+                  for f in ("gemm_dma.hip", "kernel_common.h", "imm_internal.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_square_f16_8192.json")
 CLOCK_FILE = os.path.join(ROOT, "profiles", "clock_square_f16_8192.json")
 CLOCK_COUNTERS = ("GRBM_GUI_ACTIVE", "GRBM_COUNT", "SQ_BUSY_CYCLES", "SQ_VALU_MFMA_BUSY_CYCLES",
@@ -51,10 +51,16 @@ LDS_COUNTERS = ("GRBM_GUI_ACTIVE", "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", 
 
 
 def kernel_source_hash() -> str:
+    """Hash of what decides the headline kernel's launches: the device sources
+    it is built from and the plan the library makes for the headline product
+    (tile, waves, raster, split, instruction shape)."""
+    import invariant_matmul_amd as imm
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
         with open(p, "rb") as f:
             h.update(f.read())
+    info = imm.gemm_plan(8192, 8192, 8192, "f16").info
+    h.update(json.dumps(info, sort_keys=True).encode())
     return h.hexdigest()[:16]
 
 
@@ -282,13 +288,25 @@ def bench_splitk(name, split, torch, imm, wl, n=30, warmup=5, M=None):
         n, warmup, torch)
     algo = bytes_in + Mrows * w.N * 4
     med = statistics.median(per)
-    return {"M": Mrows, "N": w.N, "K": w.K, "split_k": plan.info["split_k"],
-            "tile": f"{plan.info['block_m']}x{plan.info['block_n']}",
-            "copies_rotated": copies, **summary(per),
-            "algorithmic_bytes": algo, "GBps": algo / (med * 1e-3) / 1e9,
-            "pct_hbm_peak": 100.0 * algo / (med * 1e-3) / 1e9 / PEAK_HBM_GBS,
-            "TFLOPs": 2.0 * Mrows * w.N * w.K / (med * 1e-3) / 1e12,
-            "workspace_traffic_bytes": 2 * plan.info["workspace_bytes"]}
+    out = {"M": Mrows, "N": w.N, "K": w.K, "split_k": plan.info["split_k"],
+           "tile": f"{plan.info['block_m']}x{plan.info['block_n']}",
+           "copies_rotated": copies, **summary(per),
+           "algorithmic_bytes": algo, "GBps": algo / (med * 1e-3) / 1e9,
+           "pct_hbm_peak": 100.0 * algo / (med * 1e-3) / 1e9 / PEAK_HBM_GBS,
+           "TFLOPs": 2.0 * Mrows * w.N * w.K / (med * 1e-3) / 1e12,
+           "workspace_traffic_bytes": 2 * plan.info["workspace_bytes"]}
+    if split == 0:
+        # GEMM_PLAN_TILE_BY_M: the split-path tile from M (same split, same bits)
+        pm = imm.gemm_plan_ex2(Mrows, w.N, w.K, w.dtype, w.out, flags=imm.PLAN_TILE_BY_M)
+        if pm.info["tile"] != plan.info["tile"]:
+            pmm, _ = time_launches(
+                lambda i: imm.gemm_splitk_run(pm, As[i % copies], Bs[i % copies], C, ws),
+                n, warmup, torch)
+            mm_ = statistics.median(pmm)
+            out.update({"tile_by_m": f"{pm.info['block_m']}x{pm.info['block_n']}",
+                        "tile_by_m_median_us": mm_ * 1e3,
+                        "tile_by_m_GBps": algo / (mm_ * 1e-3) / 1e9})
+    return out
 
 
 def bench_hbm_probes(torch, nbytes=2 ** 30):

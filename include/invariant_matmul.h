@@ -121,11 +121,14 @@ typedef enum {
   /* gemm_run / gemm_run_bias take their tile from M instead of from (N, K,
    * dtype): the DMA tile (32x256, 64x256, 128x256 or 256x256) with the least
    * estimated time, rounds of 256 workgroups times a per-tile time that grows
-   * with the tile's rows.  Every tile uses
-   * the same matrix-core instruction and K order, so C is bitwise that of the
-   * plan without the flag for every M (tile sizes do not change bits: the
-   * Tencent article, "Batch Invariance の由来"); only the time changes.  An
-   * explicit tile or the split-K path ignore it. */
+   * with the tile's rows.  gemm_splitk_run of a wide reduction-dominated shape
+   * (K >= 2N, N > 512) takes from M the tile with the fewest row tiles (32-row,
+   * 64x256, 128x256 or 256x256); the split of K stays the one (N, K, dtype)
+   * gives.  Every tile uses the same matrix-core instruction and K order, so
+   * C is bitwise that of the plan without the flag for every M (tile sizes do
+   * not change bits: the Tencent article, "Batch Invariance の由来"); only the
+   * time changes.  An explicit tile, and the split-K path of other shapes,
+   * ignore it. */
   GEMM_PLAN_TILE_BY_M = 4
 } gemm_plan_flags;
 

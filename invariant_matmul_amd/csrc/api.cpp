@@ -107,6 +107,23 @@ int tile_by_m(int64_t M, int64_t N) {
   return kTiles[best];
 }
 
+// GEMM_PLAN_TILE_BY_M on the split-K path of wide reduction-dominated shapes
+// (K >= 2N, N > 512: the decode-like default, a 32-row tile): the tile with
+// the fewest row tiles, the fewer rows on a tie.  There the time is B's
+// stream, which every row tile reads again; the split (the default's, from
+// N and K alone) gives every tile enough workgroups.  Measured on the decode
+// shape N = 4096, K = 14336: M = 128 takes 38 us on 128 x 256 against 63 us on
+// 32 x 128, M = 256 takes 54 us on 256 x 256 against 111 us; M <= 32 stays
+// on the 32-row tile.  Bits do not depend on the tile.
+int split_tile_by_m(int64_t M, int narrow) {
+  static const int kRows[4] = {32, 64, 128, 256};
+  const int tiles[4] = {narrow, GEMM_TILE_64x256, GEMM_TILE_128x256, GEMM_TILE_256x256};
+  int best = 0;
+  for (int i = 1; i < 4; ++i)
+    if ((M + kRows[i] - 1) / kRows[i] < (M + kRows[best] - 1) / kRows[best]) best = i;
+  return tiles[best];
+}
+
 bool is_dma_tile(int tile) {
   return tile == GEMM_TILE_256x256 || tile == GEMM_TILE_128x256 || tile == GEMM_TILE_32x256 ||
          tile == GEMM_TILE_64x256;
@@ -280,6 +297,9 @@ gemm_status gemm_plan_ex2(int64_t M, int64_t N, int64_t K, gemm_dtype in, gemm_d
   // Transposed B runs on the DMA tiles only; its decode-like default is the
   // 32-row DMA tile.
   if (bt && tile == GEMM_TILE_DEFAULT && split_tile == GEMM_TILE_32x128) split_tile = GEMM_TILE_32x256;
+  if (tile == GEMM_TILE_DEFAULT && (flags & GEMM_PLAN_TILE_BY_M) && reduction_dominated(N, K) &&
+      N > 512)
+    split_tile = split_tile_by_m(M, split_tile);
   p->tile = checked_tile(split_tile, N, K, eb, bt);
   int run_tile = tile;
   if (tile == GEMM_TILE_DEFAULT)
@@ -343,8 +363,8 @@ gemm_status gemm_plan_info(gemm_plan_t p, gemm_plan_info_t* info) {
   info->block_m = p->bm;
   info->block_n = p->bn;
   info->block_k = p->bk;
-  info->mfma_m = 32;
-  info->mfma_n = 32;
+  info->mfma_m = mfma_mn(p->in);
+  info->mfma_n = mfma_mn(p->in);
   info->mfma_k = mfma_k(p->in);
   info->waves = p->waves_m * p->waves_n;
   info->group_m = p->group_m;

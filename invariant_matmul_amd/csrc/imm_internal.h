@@ -28,7 +28,10 @@ constexpr int kTileKBytes = 128;
 
 inline int elem_bytes(int dt) { return (dt == GEMM_F8_E4M3 || dt == GEMM_F8_E5M2) ? 1 : 2; }
 inline int block_k_elems(int dt) { return kTileKBytes / elem_bytes(dt); }
-inline int mfma_k(int dt) { return elem_bytes(dt) == 1 ? 64 : 16; }
+// Shape of the matrix-core step the GEMM kernels use for an input dtype:
+// 16 x 16 x 32 for fp16 / bf16, 32 x 32 x 64 for fp8.
+inline int mfma_mn(int dt) { return elem_bytes(dt) == 1 ? 32 : 16; }
+inline int mfma_k(int dt) { return elem_bytes(dt) == 1 ? 64 : 32; }
 
 }  // namespace imm
 

@@ -199,3 +199,28 @@ def test_tile_by_m_rows_identical_across_M(dt, bt):
         got = bits_of(run(plan, A[:m].contiguous(), Bd, False))
         assert np.array_equal(got, ref[:m]), m
     assert seen == {imm.TILE[t] for t in ("32x256", "64x256", "128x256", "256x256")}, seen
+
+
+@pytest.mark.parametrize("bt", [False, True])
+def test_tile_by_m_split_path_bits_equal_the_plain_plan(bt):
+    """GEMM_PLAN_TILE_BY_M on the split-K path of the decode shape walks the
+    32-row, 64x256, 128x256 and 256x256 tiles as M grows; the split stays the
+    plain plan's, so every row keeps the bits of the plain plan at full M."""
+    w = wl.WORKLOADS["decode_bf16_m128"]
+    N, K = w.N, w.K
+    g = wl.gen(8450)
+    A = wl.normal((256, K), "bf16", g, std=K ** -0.5).to(dev())
+    B = wl.normal((K, N), "bf16", g).to(torch.bfloat16)
+    Bd = (B.float().t().contiguous().to(torch.bfloat16) if bt else B).to(dev())
+    fl = imm.PLAN_B_TRANSPOSED if bt else 0
+    plain = imm.gemm_plan_ex2(256, N, K, "bf16", "f32", flags=fl)
+    ref = bits_of(run(plain, A, Bd, True))
+    seen = set()
+    for m in (1, 40, 64, 128, 256):
+        plan = imm.gemm_plan_ex2(m, N, K, "bf16", "f32", flags=fl | imm.PLAN_TILE_BY_M)
+        assert plan.info["split_k"] == plain.info["split_k"]
+        seen.add(plan.info["tile"])
+        got = bits_of(run(plan, A[:m].contiguous(), Bd, True))
+        log(f"split path tile_by_m M={m} tile {plan.info['tile']} bt={bt}")
+        assert np.array_equal(got, ref[:m]), m
+    assert len(seen) == 4, seen

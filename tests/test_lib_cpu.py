@@ -90,9 +90,10 @@ def test_split_covers_K_in_block_multiples(N, K, dt):
 def test_default_plans_of_the_workloads():
     sq = imm.gemm_plan(8192, 8192, 8192, "f16").info
     assert (sq["block_m"], sq["block_n"], sq["split_k"]) == (256, 256, 1)
-    assert sq["mfma_k"] == 16
+    assert (sq["mfma_m"], sq["mfma_n"], sq["mfma_k"]) == (16, 16, 32)
     fp8 = imm.gemm_plan(8192, 8192, 8192, "e5m2").info
-    assert fp8["mfma_k"] == 64 and fp8["out_dtype"] == imm.DTYPE["bf16"]
+    assert (fp8["mfma_m"], fp8["mfma_n"], fp8["mfma_k"]) == (32, 32, 64)
+    assert fp8["out_dtype"] == imm.DTYPE["bf16"]
     dec = imm.gemm_plan(1, 4096, 14336, "bf16").info
     assert dec["split_k"] > 1 and dec["block_m"] == 32
     # without a split the single pass keeps the large tile (the plan cannot
@@ -396,3 +397,29 @@ def test_tile_by_m_rule(M, N, K, tile):
     assert flagged["run_tile"] == imm.TILE[tile]
     for k in ("tile", "split_k", "k_per_split", "block_m", "block_n"):
         assert flagged[k] == plain[k]
+
+
+@pytest.mark.parametrize("M,tile", [(1, "32x128"), (8, "32x128"), (32, "32x128"), (64, "64x256"),
+                                    (128, "128x256"), (256, "256x256"), (512, "256x256")])
+def test_tile_by_m_on_the_split_path_of_decode_shapes(M, tile):
+    """GEMM_PLAN_TILE_BY_M: the split-K path of a wide reduction-dominated shape
+    takes the tile with the fewest row tiles; the split itself (which decides
+    the bits) is the plain plan's."""
+    N, K = 4096, 14336
+    flagged = imm.gemm_plan_ex2(M, N, K, "bf16", "f32", flags=imm.PLAN_TILE_BY_M).info
+    plain = imm.gemm_plan_ex2(M, N, K, "bf16", "f32").info
+    assert flagged["tile"] == imm.TILE[tile]
+    assert plain["tile"] == imm.TILE["32x128"]
+    assert (flagged["split_k"], flagged["k_per_split"]) == (plain["split_k"], plain["k_per_split"])
+    bt = imm.gemm_plan_ex2(M, N, K, "bf16", "f32",
+                           flags=imm.PLAN_TILE_BY_M | imm.PLAN_B_TRANSPOSED).info
+    assert bt["tile"] == imm.TILE["32x256" if tile == "32x128" else tile]
+    assert (bt["split_k"], bt["k_per_split"]) == (plain["split_k"], plain["k_per_split"])
+
+
+def test_tile_by_m_leaves_the_split_path_of_narrow_shapes():
+    """N <= 512 (the huge-K case) keeps its split-path tile under the flag."""
+    for M in (1, 256, 1024):
+        flagged = imm.gemm_plan_ex2(M, 256, 131072, "f16", "f32", flags=imm.PLAN_TILE_BY_M).info
+        plain = imm.gemm_plan_ex2(M, 256, 131072, "f16", "f32").info
+        assert flagged["tile"] == plain["tile"] == imm.TILE["64x256"]
