@@ -137,7 +137,9 @@ typedef struct gemm_plan_s* gemm_plan_t;
 /* A plan holds one tile for each entry point: tile / block_m / block_n /
  * waves / tiles_m / tiles_n describe gemm_splitk_run's partial kernel, the
  * run_* fields gemm_run's single pass.  Both are chosen from (N, K, dtype,
- * options) alone, and the bits of C depend on neither. */
+ * options) alone (with GEMM_PLAN_TILE_BY_M, also from M), and the bits of C
+ * depend on neither: only split_k and k_per_split, which never depend on M,
+ * decide them. */
 typedef struct {
   int64_t M, N, K;
   int32_t in_dtype, out_dtype;  /* gemm_dtype values */
