@@ -298,8 +298,12 @@ gemm_status gemm_plan_ex2(int64_t M, int64_t N, int64_t K, gemm_dtype in, gemm_d
   // 32-row DMA tile.
   if (bt && tile == GEMM_TILE_DEFAULT && split_tile == GEMM_TILE_32x128) split_tile = GEMM_TILE_32x256;
   if (tile == GEMM_TILE_DEFAULT && (flags & GEMM_PLAN_TILE_BY_M) && reduction_dominated(N, K) &&
-      N > 512)
-    split_tile = split_tile_by_m(M, split_tile);
+      N > 512) {
+    // the flag never makes a plan fail: a tile whose offsets would not fit
+    // (transposed B with a very long K) leaves the default in place
+    const int by_m = split_tile_by_m(M, split_tile);
+    if (checked_tile(by_m, N, K, eb, bt) >= 0) split_tile = by_m;
+  }
   p->tile = checked_tile(split_tile, N, K, eb, bt);
   int run_tile = tile;
   if (tile == GEMM_TILE_DEFAULT)

@@ -204,7 +204,9 @@ _mode_lib = None
 def batch_invariant_mode():
     """Install this module's products as the CUDA kernels of aten::mm and
     aten::addmm while the context is active (nested contexts share one
-    registration; the last exit removes it and torch's kernels return)."""
+    registration; the last exit removes it and torch's kernels return).  The
+    registration is process-wide: products issued by other threads while it
+    is active take the same path."""
     global _mode_depth, _mode_lib
     with _mode_lock:
         if _mode_depth == 0:

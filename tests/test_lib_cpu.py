@@ -423,3 +423,20 @@ def test_tile_by_m_leaves_the_split_path_of_narrow_shapes():
         flagged = imm.gemm_plan_ex2(M, 256, 131072, "f16", "f32", flags=imm.PLAN_TILE_BY_M).info
         plain = imm.gemm_plan_ex2(M, 256, 131072, "f16", "f32").info
         assert flagged["tile"] == plain["tile"] == imm.TILE["64x256"]
+
+
+def test_tile_by_m_never_makes_a_split_plan_fail():
+    """Near and past the K where the DMA tiles' 32-bit offsets overflow: where
+    the plain plan exists, the flagged one exists too, with the same split."""
+    N = 1024
+    for K in (2 ** 21, 2 ** 22 - 64, 2 ** 22 + 64, 2 ** 23):
+        for fl in (0, imm.PLAN_B_TRANSPOSED):
+            for M in (1, 300):
+                try:
+                    plain = imm.gemm_plan_ex2(M, N, K, "bf16", "f32", flags=fl).info
+                except imm.GemmError:
+                    continue
+                flagged = imm.gemm_plan_ex2(M, N, K, "bf16", "f32",
+                                            flags=fl | imm.PLAN_TILE_BY_M).info
+                assert (flagged["split_k"], flagged["k_per_split"]) == (
+                    plain["split_k"], plain["k_per_split"]), (K, fl, M)
