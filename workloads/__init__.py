@@ -61,8 +61,9 @@ def normal(shape, dtype, g, std=1.0) -> torch.Tensor:
 
 
 def integers(shape, dtype, g, lo=-4, hi=4) -> torch.Tensor:
-    """i.i.d. uniform integers in [lo, hi] (inclusive), stored exactly in ``dtype``."""
-    x = torch.randint(lo, hi + 1, shape, generator=g, dtype=torch.int32)
+    """i.i.d. uniform integers in [lo, hi] (inclusive), stored exactly in ``dtype``,
+    on the generator's device (a CUDA generator draws very large inputs in place)."""
+    x = torch.randint(lo, hi + 1, shape, generator=g, dtype=torch.int32, device=g.device)
     return x.to(DTYPES[dtype] if isinstance(dtype, str) else dtype)
 
 
