@@ -11,17 +11,12 @@
 
 namespace imm {
 
-// Static description of one tile configuration.  Every configuration of an
-// input dtype uses the same matrix-core instruction (32x32 output block; K of
-// 16 for 16-bit inputs, 64 for fp8) and walks K in ascending order in steps of
-// that instruction, so configurations differ only in how output elements are
+// Every tile configuration of an input dtype uses the same matrix-core
+// instruction (a 16x16 output block with K of 32 for 16-bit inputs, a 32x32
+// block with K of 64 for fp8) and walks K in ascending order in steps of that
+// instruction, so configurations differ only in how output elements are
 // spread over workgroups and waves -- which [TDI] "Batch Invariance の由来"
 // (BLOCK_M / BLOCK_N, num_warps paragraphs) shows has no effect on bits.
-struct TileCfg {
-  int tile;     // gemm_tile
-  int bm, bn;   // output tile
-  int waves_m, waves_n;
-};
 
 // Bytes of K staged per main-loop step: 64 fp16/bf16 elements or 128 fp8.
 constexpr int kTileKBytes = 128;
