@@ -260,8 +260,11 @@ void gemm_plan_destroy(gemm_plan_t plan);
  * Domain: finite inputs whose nonzero row / column maxima lie in
  * [2^-300, 2^300].  There every slice value, scaled term and partial sum is
  * a normal fp64 number, so the kernel may apply 2^(c0(row) + c0(column)) once
- * at the end instead of to every term without changing a bit.  Outside it
- * the result is unspecified (no error is reported).
+ * at the end instead of to every term without changing a bit.  A row of A or
+ * a column of B outside it (holding a NaN or an infinity, a magnitude above
+ * 2^300, or a nonzero maximum below 2^-300) gets the exponent -2^30 in the
+ * workspace and zero slices, and its whole row / column of C is NaN; every
+ * other entry of C is unaffected (no error is reported).
  *
  * Workspace (device memory, caller-owned, 16-byte aligned, at least
  * ozaki_workspace_size bytes), with the offsets that ozaki_plan_info reports:

@@ -573,10 +573,13 @@ __global__ __launch_bounds__(256 * WM, (waves_per_simd<TBM, WM, NS>())) void gem
           if constexpr (MODE == MODE_OZAKI) {
             // C = 2^(ea[row] + eb[col]) * sum: the same bits as scaling every
             // pair's term by its full exponent while no value leaves fp64's
-            // normal range
-            if (row < g.M && col < g.n_out)
+            // normal range; NaN where the row or the column is outside it
+            if (row < g.M && col < g.n_out) {
+              const int er = g.ea[row], ec = g.eb[col];
               static_cast<double*>(g.C)[row * g.ldc + col] =
-                  ldexp(acc64[i][j][r], g.ea[row] + g.eb[col]);
+                  (er == kOzBadExp || ec == kOzBadExp) ? __builtin_nan("")
+                                                       : ldexp(acc64[i][j][r], er + ec);
+            }
           } else if (row < g.M && col < g.N) {
             const float v = acc[i][j][r];
             if constexpr (MODE == MODE_SLICE) {

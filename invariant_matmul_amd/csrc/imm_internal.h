@@ -163,6 +163,11 @@ hipError_t launch_gemm_persist(const gemm_plan_s& p, const PersistArgs& a, hipSt
 // The Ozaki slice-pair product on the DMA kernel (gemm_dma.hip); type2 is
 // GEMM_BF16, GEMM_F8_E4M3 or GEMM_I8.  Output tile oz_tile_m(type2) x 256.
 constexpr int kOzTileN = 256;
+// Exponent of a row of A or a column of B outside the Ozaki domain (a NaN or
+// an infinity, a magnitude above 2^300, or a nonzero maximum below 2^-300):
+// its slices are zero and its row / column of C is NaN.
+constexpr int kOzBadExp = -(1 << 30);
+constexpr double kOzMaxMag = 0x1p300, kOzMinMax = 0x1p-300;
 inline int oz_tile_m(int type2) { return type2 == GEMM_F8_E4M3 ? 64 : 128; }
 hipError_t launch_ozaki_gemm(int type2, const OzGemmArgs& a, hipStream_t s);
 // The Ozaki split (ozaki.hip): exponents of the rows of x [R, C] ...

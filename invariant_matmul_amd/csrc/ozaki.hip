@@ -35,20 +35,35 @@ __device__ __forceinline__ int ceil_log2_exact(double m) {
   return f == 0.5 ? e - 1 : e;
 }
 
-// Maximum of |x| over each row of x [R, C]: one workgroup per row.
+// |x| for the maxima, with a NaN, an infinity or a magnitude above the
+// domain's bound turned into +inf (fmax would drop a NaN; +inf survives it).
+__device__ __forceinline__ double dom_abs(double x) {
+  const double a = fabs(x);
+  return a <= kOzMaxMag ? a : __builtin_inf();
+}
+
+// The exponent c0 of a vector from the maximum of dom_abs over it, or
+// kOzBadExp outside the domain.
+__device__ __forceinline__ int exp_of_max(double m) {
+  if (m > kOzMaxMag || (m != 0.0 && m < kOzMinMax)) return kOzBadExp;
+  return ceil_log2_exact(m);
+}
+
+// Exponent of each row of x [R, C] from the maximum of dom_abs over it: one
+// workgroup per row.
 __global__ __launch_bounds__(256) void oz_row_exp_kernel(const double* x, int64_t C, int32_t* e) {
   const double* row = x + (int64_t)blockIdx.x * C;
   double m = 0.0;
-  for (int64_t k = threadIdx.x; k < C; k += 256) m = fmax(m, fabs(row[k]));
+  for (int64_t k = threadIdx.x; k < C; k += 256) m = fmax(m, dom_abs(row[k]));
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) m = fmax(m, __shfl_xor(m, off));
   __shared__ double red[4];
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
   __syncthreads();
-  if (threadIdx.x == 0) e[blockIdx.x] = ceil_log2_exact(fmax(fmax(red[0], red[1]), fmax(red[2], red[3])));
+  if (threadIdx.x == 0) e[blockIdx.x] = exp_of_max(fmax(fmax(red[0], red[1]), fmax(red[2], red[3])));
 }
 
-// Maximum of |x| over rows [y*rc, (y+1)*rc) of each column of x [R, C].
+// Maximum of dom_abs over rows [y*rc, (y+1)*rc) of each column of x [R, C].
 __global__ __launch_bounds__(256) void oz_col_max_kernel(const double* x, int64_t R, int64_t C,
                                                          int64_t rc, double* part) {
   const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -56,7 +71,7 @@ __global__ __launch_bounds__(256) void oz_col_max_kernel(const double* x, int64_
   const int64_t r0 = (int64_t)blockIdx.y * rc;
   const int64_t r1 = R < r0 + rc ? R : r0 + rc;
   double m = 0.0;
-  for (int64_t r = r0; r < r1; ++r) m = fmax(m, fabs(x[r * C + c]));
+  for (int64_t r = r0; r < r1; ++r) m = fmax(m, dom_abs(x[r * C + c]));
   part[(int64_t)blockIdx.y * C + c] = m;
 }
 
@@ -67,7 +82,7 @@ __global__ __launch_bounds__(256) void oz_col_exp_kernel(const double* part, int
   if (c >= C) return;
   double m = 0.0;
   for (int64_t y = 0; y < chunks; ++y) m = fmax(m, part[y * C + c]);
-  e[c] = ceil_log2_exact(m);
+  e[c] = exp_of_max(m);
 }
 
 // Exact Type2 encodings of a float that holds a slice value.
@@ -101,6 +116,10 @@ __global__ __launch_bounds__(256) void oz_split_kernel(const double* x, int64_t 
     const int64_t c = c0 + u;
     xr[u] = (r < R && c < C) ? x[r * C + c] : 0.0;
     ex[u] = PER_ROW ? (r < R ? e[r] : 0) : (c < C ? e[c] : 0);
+    if (ex[u] == kOzBadExp) {  // outside the domain: zero slices (C is NaN there)
+      ex[u] = 0;
+      xr[u] = 0.0;
+    }
   }
   const int64_t plane = Ro * Co;
   for (int p = 0; p < s; ++p) {

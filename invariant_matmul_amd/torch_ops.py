@@ -27,6 +27,9 @@ fp64 CUDA tensors go through the library's Ozaki-scheme product (int8
 slices, default slice count and Fast Mode threshold: the Insight Edge cuTile
 blog's FP64 emulation, here with one exponent per row, so it is batch-
 invariant too); a bias is then added with one fp64 addition.  Any N and K.
+Its domain: a row of the first operand or a column of the second that holds
+a NaN or an infinity, a magnitude above 2^300, or only nonzero magnitudes
+below 2^-300 gives NaN in its whole row or column of the result.
 
 The direct functions raise for anything else.  Under the context manager the
 library computes what it supports (2-D weights; fp16 / bf16 with N and K

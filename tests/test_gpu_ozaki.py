@@ -229,3 +229,40 @@ def test_long_K_wider_column_chunks():
     C, _ = _run(plan, A.to(dev()), B.to(dev()))
     want = OZ.gemm(A.numpy(), B.numpy(), "i8")
     assert np.array_equal(_bits64(C), _bits64(want))
+
+
+@pytest.mark.parametrize("t2", ["bf16", "e4m3", "i8"])
+def test_rows_and_columns_outside_the_domain_give_nan(t2):
+    """A row of A or a column of B holding a NaN, an infinity, a magnitude
+    above 2^300 or a nonzero maximum below 2^-300 is outside the domain: its
+    exponent is the marker -2^30, its slices are zero, and its whole row or
+    column of C is NaN.  Every other entry keeps the oracle's bits (rows and
+    columns are split independently)."""
+    M, N, K = 70, 90, 200
+    A, B = _inputs(M, N, K, "uniform", 7700)
+    A, B = A.clone(), B.clone()
+    A[3, 5] = float("nan")
+    A[5, 0] = float("inf")
+    A[7, 10] = 2.0 ** 301
+    A[9, :] = A[9, :] * 2.0 ** -330           # nonzero maximum below 2^-300
+    B[7, 2] = float("-inf")
+    B[150, 4] = float("nan")
+    B[0, 60] = -(2.0 ** 302)
+    bad_rows, bad_cols = [3, 5, 7, 9], [2, 4, 60]
+    plan = imm.ozaki_plan(M, N, K, t2)
+    i = plan.info
+    C, ws = _run(plan, A.to(dev()), B.to(dev()))
+    got = C.cpu().numpy()
+    assert np.isnan(got[bad_rows, :]).all() and np.isnan(got[:, bad_cols]).all()
+    ea = ws[i["a_exp_offset"]:i["a_exp_offset"] + 4 * M].cpu().numpy().view(np.int32)
+    eb = ws[i["b_exp_offset"]:i["b_exp_offset"] + 4 * N].cpu().numpy().view(np.int32)
+    assert (ea[bad_rows] == -(1 << 30)).all() and (eb[bad_cols] == -(1 << 30)).all()
+    # the rest: the oracle on the same data with the bad vectors cleared
+    Ac, Bc = A.clone(), B.clone()
+    Ac[bad_rows, :] = 0.0
+    Bc[:, bad_cols] = 0.0
+    want = OZ.gemm(Ac.numpy(), Bc.numpy(), t2)
+    good_r = [r for r in range(M) if r not in bad_rows]
+    good_c = [c for c in range(N) if c not in bad_cols]
+    assert np.array_equal(_bits64(got[np.ix_(good_r, good_c)]), _bits64(want[np.ix_(good_r, good_c)]))
+    assert not np.isnan(got[np.ix_(good_r, good_c)]).any()
