@@ -224,3 +224,26 @@ def test_tile_by_m_split_path_bits_equal_the_plain_plan(bt):
         log(f"split path tile_by_m M={m} tile {plan.info['tile']} bt={bt}")
         assert np.array_equal(got, ref[:m]), m
     assert len(seen) == 4, seen
+
+
+@pytest.mark.parametrize("split", [False, True])
+@pytest.mark.parametrize("tile", ["256x256", "128x256", "32x256", "32x128"])
+def test_nan_and_inf_rows_stay_in_their_rows(tile, split):
+    """A request whose row of A holds a NaN or an infinity must not touch the
+    other rows of the batch: their bits equal a run without it, and the NaN
+    row of C is NaN throughout."""
+    M, N, K = 300, 512, 1024
+    g = wl.gen(8470)
+    A = wl.uniform((M, K), "f16", g)
+    B = wl.uniform((K, N), "f16", g).to(dev())
+    bad = A.clone()
+    bad[3, 17] = float("nan")
+    bad[200, 900] = float("inf")
+    plan = imm.gemm_plan_ex(M, N, K, "f16", "f32", tile=tile)
+    clean = bits_of(run(plan, A.to(dev()), B, split))
+    C = run(plan, bad.to(dev()), B, split)
+    got = bits_of(C)
+    rows = [r for r in range(M) if r not in (3, 200)]
+    assert np.array_equal(got[rows], clean[rows])
+    assert torch.isnan(C[3]).all()
+    assert not torch.isfinite(C[200]).any()
