@@ -247,3 +247,46 @@ def test_nan_and_inf_rows_stay_in_their_rows(tile, split):
     assert np.array_equal(got[rows], clean[rows])
     assert torch.isnan(C[3]).all()
     assert not torch.isfinite(C[200]).any()
+
+
+def test_host_threads_on_their_own_streams():
+    """Plans are immutable and the library keeps no state between calls: four
+    host threads, each on its own stream with its own buffers, running the
+    single pass and the split-K path at the same time, all get the bits of the
+    single-threaded run."""
+    import threading
+    M, N, K = 512, 1024, 2048
+    g = wl.gen(8480)
+    A = wl.uniform((M, K), "bf16", g).to(dev())
+    B = wl.uniform((K, N), "bf16", g).to(dev())
+    plan = imm.gemm_plan_ex(M, N, K, "bf16", "f32", split_k=4)
+    ref_run = bits_of(run(plan, A, B, False))
+    ref_split = bits_of(run(plan, A, B, True))
+    errors = []
+
+    def worker(t):
+        try:
+            s = torch.cuda.Stream()
+            C = torch.empty((M, N), dtype=torch.float32, device=dev())
+            ws = torch.empty(imm.gemm_workspace_size(plan) // 4, dtype=torch.float32, device=dev())
+            for i in range(12):
+                split = (i + t) % 2 == 1
+                with torch.cuda.stream(s):
+                    if split:
+                        imm.gemm_splitk_run(plan, A, B, C, ws, s)
+                    else:
+                        imm.gemm_run(plan, A, B, C, s)
+                s.synchronize()
+                got = wl.bits(C.cpu())
+                if not np.array_equal(got, ref_split if split else ref_run):
+                    errors.append((t, i, split))
+        except Exception as e:  # reported below
+            errors.append((t, repr(e)))
+
+    torch.cuda.synchronize()
+    threads = [threading.Thread(target=worker, args=(t,)) for t in range(4)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    assert not errors, errors
