@@ -202,6 +202,60 @@ def write_clock(counter_csv, agent_csv, lds_csv=None, out_path=CLOCK_FILE):
     print(json.dumps(out))
 
 
+def _smi_power_clocks():
+    """Socket power (W) and the XCDs' engine clocks (MHz) from amd-smi."""
+    import re
+    import subprocess
+    r = subprocess.run(["amd-smi", "metric", "-p", "-c", "--json"], capture_output=True,
+                       text=True, timeout=60)
+    if r.returncode != 0:
+        return {"error": r.stderr.strip()[:200]}
+    j = json.loads(r.stdout)
+    gpu = j["gpu_data"][0] if isinstance(j, dict) else j[0]
+    power = gpu["power"]["socket_power"]["value"]
+    clocks = [v["clk"]["value"] for k, v in gpu["clock"].items()
+              if re.fullmatch(r"gfx_\d+", k) and isinstance(v, dict)]
+    return {"socket_power_w": power, "gfx_clocks_mhz": clocks}
+
+
+def power_sample(torch, imm, wl, seconds=6.0):
+    """The headline product in a loop (random inputs, then all-zero ones),
+    with amd-smi read half-way through each: the board's power and clocks
+    under the same instructions and data movement with different operand
+    switching activity."""
+    import threading
+    out = {"idle": _smi_power_clocks()}
+    w = wl.WORKLOADS["square_f16_8192"]
+    A, B = w.make()
+    Ad, Bd = A.cuda(), B.cuda()
+    plan = imm.gemm_plan(w.M, w.N, w.K, w.dtype)
+    C = torch.empty((w.M, w.N), dtype=torch.float32, device="cuda")
+    for kind in ("random", "zeros"):
+        if kind == "zeros":
+            Ad.zero_()
+            Bd.zero_()
+        stop = time.time() + seconds
+        launches = [0]
+
+        def loop():
+            while time.time() < stop:
+                for _ in range(20):
+                    imm.gemm_run(plan, Ad, Bd, C)
+                torch.cuda.synchronize()
+                launches[0] += 20
+
+        th = threading.Thread(target=loop)
+        t0 = time.time()
+        th.start()
+        time.sleep(seconds / 2)
+        sample = _smi_power_clocks()
+        th.join()
+        dt = time.time() - t0
+        out[kind] = {**sample, "launches": launches[0],
+                     "TFLOPs": launches[0] * w.flops / dt / 1e12}
+    return out
+
+
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
@@ -434,6 +488,10 @@ def main():
                     help="back-to-back launches of the headline kernel, of torch.matmul on "
                          "the same fp16 product and of a plain copy, for the clock counters; "
                          "prints nothing else")
+    ap.add_argument("--power-sample", action="store_true",
+                    help="run the headline product in a loop on random, then all-zero inputs "
+                         "and read the board's power and engine clocks with amd-smi during "
+                         "each; prints one JSON line")
     ap.add_argument("--write-clock", nargs="+", metavar="CSV",
                     help="host only: COUNTER_CSV AGENT_CSV [LDS_CSV]: write the headline kernel's "
                          "engine clock and matrix-core occupancy from a counter run of "
@@ -478,6 +536,10 @@ def main():
             imm.gemm_run(plan, Ad, Bd, C)
         torch.cuda.synchronize()
         print("profile pass done", flush=True)
+        return
+
+    if args.power_sample:
+        print(json.dumps(power_sample(torch, imm, wl)), flush=True)
         return
 
     if args.clock_pass:
