@@ -51,9 +51,8 @@ void tile_shape(int tile, int* bm, int* bn, int* wm, int* wn) {
 // output has few tiles and split-K is the tool ([TDI] "Split-K": tiny M x N,
 // huge K; the parameter table restricts SPLIT_K to such shapes).  Wide ones
 // (decode-like, N > 512) get the narrow 32 x 128 tile, whose time is the
-// stream of B; narrow ones (N <= 512) get the 64 x 256 DMA tile, which reads
-// each slice of B once per 64 rows instead of once per 32.  The rest get the
-// large tile.
+// stream of B; narrow ones (N <= 512) get the 128 x 256 DMA tile, which reads
+// each slice of B once per 128 rows.  The rest get the large tile.
 bool reduction_dominated(int64_t N, int64_t K) { return K >= 2 * N; }
 
 // Small B (at most 4 MB, the L2 of one XCD): the product is too small to
@@ -65,7 +64,7 @@ bool small_b(int64_t N, int64_t K, int eb) { return N * K * eb <= ((int64_t)4 <<
 // Tile of the split-K path.
 int default_tile(int64_t N, int64_t K, int eb) {
   if (!reduction_dominated(N, K)) return small_b(N, K, eb) ? GEMM_TILE_32x256 : GEMM_TILE_256x256;
-  return N <= 512 ? GEMM_TILE_64x256 : GEMM_TILE_32x128;
+  return N <= 512 ? GEMM_TILE_128x256 : GEMM_TILE_32x128;
 }
 
 // Tile of the single pass.  Without a split, a 32-row tile only pays off
@@ -151,11 +150,15 @@ int checked_tile(int tile, int64_t N, int64_t K, int eb, bool b_trans) {
 
 // Workgroups the default split aims for per row of output tiles.  Wide
 // shapes: two per compute unit of a 256-CU MI355X (512).  Narrow shapes
-// (N <= 512): 64, because there the row tiles multiply it -- at M = 256 the
-// 64 x 256 tile gives 4 x 64 = 256 workgroups, one per CU, and more slices
-// only add workspace traffic (measured: 64 slices beat 32 and 128 at
-// 256 x 256 x 131072).  Constants, not device queries, so a plan (and
-// therefore the bits) never depends on the machine it was made on.
+// (N <= 512): 64, because there the row tiles multiply it and more slices
+// add workspace traffic; 128 where every slice still keeps at least
+// kLongSliceSteps main-loop steps.  Measured on the 128 x 256 tile (fp16,
+// N = 128 / 256 / 512): at K = 131072 the larger split takes 24-28 us at
+// M <= 32 against 30-35 and is level or ahead at M = 256; at K = 32768 (4- and
+// 8-step slices) it lost 10-35 % at M >= 256.  Constants, not device
+// queries, so a plan (and therefore the bits) never depends on the machine
+// it was made on.
+constexpr int64_t kLongSliceSteps = 16;
 int64_t target_workgroups(int64_t N) { return N <= 512 ? 64 : 512; }
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -163,7 +166,8 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Default split: only for reduction-dominated shapes; the largest power of two
 // that brings one tile-row of the grid to about target_workgroups(N) while
-// every slice keeps at least 4 main-loop steps.
+// every slice keeps at least 4 main-loop steps; for narrow shapes, one more
+// doubling if every slice still keeps kLongSliceSteps steps.
 int default_split(int64_t N, int64_t K, int bn, int bk) {
   if (!reduction_dominated(N, K)) return 1;
   const int64_t tiles_n = ceil_div(N, bn);
@@ -171,6 +175,9 @@ int default_split(int64_t N, int64_t K, int bn, int bk) {
   const int64_t target = target_workgroups(N);
   int s = 1;
   while (s * 2 <= kMaxSplit && tiles_n * s * 2 <= target && steps / (s * 2) >= 4) s *= 2;
+  if (N <= 512 && s * 2 <= kMaxSplit && tiles_n * s * 2 <= 2 * target &&
+      steps / (s * 2) >= kLongSliceSteps)
+    s *= 2;
   return s;
 }
 

@@ -264,10 +264,10 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_tile_kernel(GemmAr
 // reduction kernel that sums the workspace over split_k).  Four consecutive
 // elements per thread, grid-stride.  The slices are loaded in groups of RG
 // before they are added (in order), so a thread waits for one memory latency
-// per group instead of one per slice.
+// per group instead of one per slice: one group for the decode splits.
 template <int OUT>
-__global__ __launch_bounds__(256) void splitk_reduce_kernel(ReduceArgs r) {
-  constexpr int RG = 8;
+__global__ __launch_bounds__(64) void splitk_reduce_kernel(ReduceArgs r) {
+  constexpr int RG = 16;
   const int64_t n4 = r.MN / 4;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   const f32x4* ws = reinterpret_cast<const f32x4*>(r.ws);
@@ -341,16 +341,19 @@ hipError_t launch_gemm(const gemm_plan_s& p, int tile, const GemmArgs& a, bool s
 }
 
 hipError_t launch_reduce(const gemm_plan_s& p, const ReduceArgs& a, hipStream_t s) {
+  // One-wave workgroups: a small output (decode) spreads over more compute
+  // units, so each issues fewer of the slice loads.
+  constexpr int kThreads = 64;
   const int64_t n4 = a.MN / 4;
-  int64_t blocks = (n4 + 255) / 256;
-  if (blocks > 4096) blocks = 4096;
+  int64_t blocks = (n4 + kThreads - 1) / kThreads;
+  if (blocks > 16384) blocks = 16384;
   if (blocks < 1) blocks = 1;
   if (p.out == GEMM_F32)
-    hipLaunchKernelGGL(splitk_reduce_kernel<GEMM_F32>, dim3((unsigned)blocks), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(splitk_reduce_kernel<GEMM_F32>, dim3((unsigned)blocks), dim3(kThreads), 0, s, a);
   else if (p.out == GEMM_F16)
-    hipLaunchKernelGGL(splitk_reduce_kernel<GEMM_F16>, dim3((unsigned)blocks), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(splitk_reduce_kernel<GEMM_F16>, dim3((unsigned)blocks), dim3(kThreads), 0, s, a);
   else
-    hipLaunchKernelGGL(splitk_reduce_kernel<GEMM_BF16>, dim3((unsigned)blocks), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(splitk_reduce_kernel<GEMM_BF16>, dim3((unsigned)blocks), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 

@@ -100,7 +100,10 @@ def test_default_plans_of_the_workloads():
     # know that M is small)
     assert (dec["run_block_m"], dec["run_block_n"]) == (256, 256)
     hk = imm.gemm_plan(256, 256, 131072, "f16").info
-    assert (hk["block_m"], hk["block_n"], hk["split_k"]) == (64, 256, 64)
+    assert (hk["block_m"], hk["block_n"], hk["split_k"]) == (128, 256, 128)
+    # fp8 slices of 2048 elements are 16 steps: no extra doubling
+    hk8 = imm.gemm_plan(256, 256, 131072, "e5m2").info
+    assert (hk8["block_m"], hk8["split_k"]) == (128, 64)
     small = imm.gemm_plan(1024, 1024, 1024, "f16").info
     assert (small["run_block_m"], small["run_block_n"]) == (32, 256)
 
@@ -422,7 +425,7 @@ def test_tile_by_m_leaves_the_split_path_of_narrow_shapes():
     for M in (1, 256, 1024):
         flagged = imm.gemm_plan_ex2(M, 256, 131072, "f16", "f32", flags=imm.PLAN_TILE_BY_M).info
         plain = imm.gemm_plan_ex2(M, 256, 131072, "f16", "f32").info
-        assert flagged["tile"] == plain["tile"] == imm.TILE["64x256"]
+        assert flagged["tile"] == plain["tile"] == imm.TILE["128x256"]
 
 
 def test_tile_by_m_never_makes_a_split_plan_fail():
