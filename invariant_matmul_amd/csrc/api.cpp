@@ -61,10 +61,15 @@ bool reduction_dominated(int64_t N, int64_t K) { return K >= 2 * N; }
 // 14.5 us with 32 x 256 against 29.4 us with 256 x 256.
 bool small_b(int64_t N, int64_t K, int eb) { return N * K * eb <= ((int64_t)4 << 20); }
 
-// Tile of the split-K path.
+bool dma_offsets_fit(int tile, int64_t N, int64_t K, int eb, bool b_trans);
+
+// Tile of the split-K path.  Past the K where a 128-row tile's 32-bit A
+// offsets overflow, narrow shapes keep a DMA tile of 64 rows (the split,
+// and so the bits, depend only on the tile's 256 columns).
 int default_tile(int64_t N, int64_t K, int eb) {
   if (!reduction_dominated(N, K)) return small_b(N, K, eb) ? GEMM_TILE_32x256 : GEMM_TILE_256x256;
-  return N <= 512 ? GEMM_TILE_128x256 : GEMM_TILE_32x128;
+  if (N > 512) return GEMM_TILE_32x128;
+  return dma_offsets_fit(GEMM_TILE_128x256, N, K, eb, false) ? GEMM_TILE_128x256 : GEMM_TILE_64x256;
 }
 
 // Tile of the single pass.  Without a split, a 32-row tile only pays off

@@ -428,6 +428,18 @@ def test_tile_by_m_leaves_the_split_path_of_narrow_shapes():
         assert flagged["tile"] == plain["tile"] == imm.TILE["128x256"]
 
 
+def test_narrow_default_steps_down_to_64_rows_past_the_offset_limit():
+    """N <= 512: the 128x256 split-path tile while its 32-bit A offsets fit
+    (K < 2^23 for 16-bit inputs), then the 64x256 DMA tile; the split is the
+    one any tile gets at that K."""
+    for K, tile in ((2 ** 23 - 64, "128x256"), (2 ** 23 + 64, "64x256")):
+        d = imm.gemm_plan(300, 40, K, "bf16").info
+        assert d["tile"] == imm.TILE[tile], K
+        for other in ("128x256", "32x128"):
+            e = imm.gemm_plan_ex(300, 40, K, "bf16", "f32", tile=other).info
+            assert (e["split_k"], e["k_per_split"]) == (d["split_k"], d["k_per_split"])
+
+
 def test_tile_by_m_never_makes_a_split_plan_fail():
     """Near and past the K where the DMA tiles' 32-bit offsets overflow: where
     the plain plan exists, the flagged one exists too, with the same split."""
