@@ -43,6 +43,7 @@ KERNEL_SOURCES = [os.path.join(ROOT, "invariant_matmul_amd", "csrc", f)
                   for f in ("gemm_dma.hip", "kernel_common.h", "imm_internal.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_square_f16_8192.json")
 CLOCK_FILE = os.path.join(ROOT, "profiles", "clock_square_f16_8192.json")
+STREAM_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_splitk_decode_hugek.json")
 CLOCK_COUNTERS = ("GRBM_GUI_ACTIVE", "GRBM_COUNT", "SQ_BUSY_CYCLES", "SQ_VALU_MFMA_BUSY_CYCLES",
                   "SQ_INSTS_VALU_MFMA_MOPS_F16", "SQ_INSTS_MFMA")
 # a second run of the clock pass: LDS and L2 behaviour
@@ -100,6 +101,109 @@ def write_traffic(fetch_csv, write_csv, out_path=TRAFFIC_FILE):
            "fetch_scale": ff, "write_scale": wf,
            "read_bytes_per_launch": gf * ff * 1024, "write_bytes_per_launch": gw * wf * 1024,
            "bytes_per_launch": (gf * ff + gw * wf) * 1024}
+    os.makedirs(os.path.dirname(out_path), exist_ok=True)
+    with open(out_path, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out))
+
+
+# The memory-bound cases of the stream pass, in launch order: (workload, rows, launches).
+STREAM_CASES = (("decode_bf16_m1", 1, 6), ("decode_bf16_m8", 8, 6), ("decode_bf16_m32", 32, 6),
+                ("hugek_f16", 256, 6))
+
+
+def stream_pass(torch, imm, wl):
+    """A plain copy of COPY_BYTES, then each STREAM_CASES product through the
+    default split-K plan, inputs rotated so that no launch finds its A or B in
+    the last-level cache."""
+    src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    del src, dst
+    for name, rows, launches in STREAM_CASES:
+        w = wl.WORKLOADS[name]
+        A, B = w.make()
+        Ad, Bd = A[:rows].contiguous().cuda(), B.cuda()
+        bytes_in = Ad.numel() * Ad.element_size() + Bd.numel() * Bd.element_size()
+        copies = max(1, -(-2 * MALL_BYTES // bytes_in)) + 1
+        As = [Ad] + [Ad.clone() for _ in range(copies - 1)]
+        Bs = [Bd] + [Bd.clone() for _ in range(copies - 1)]
+        plan = imm.gemm_plan(rows, w.N, w.K, w.dtype)
+        C = torch.empty((rows, w.N), dtype=torch.float32, device="cuda")
+        ws = torch.empty(max(1, imm.gemm_workspace_size(plan) // 4), dtype=torch.float32,
+                         device="cuda")
+        torch.cuda.synchronize()
+        for i in range(launches):
+            imm.gemm_splitk_run(plan, As[i % copies], Bs[i % copies], C, ws)
+        torch.cuda.synchronize()
+        del As, Bs, C, ws
+        torch.cuda.empty_cache()
+
+
+def write_stream_traffic(fetch_csv, write_csv, out_path=STREAM_TRAFFIC_FILE):
+    """Turn two rocprofv3 --pmc runs of `bench.py --stream-pass` (FETCH_SIZE,
+    then WRITE_SIZE) into bytes per launch of each split-K kernel of each
+    STREAM_CASES product, scaled by the copy as in write_traffic, next to the
+    kernel's algorithmic bytes: the partial reads A and B once and writes the
+    S slices of M x N fp32; the reduction reads those slices and writes C."""
+    import csv
+
+    import invariant_matmul_amd as imm
+    import workloads as wl
+
+    def rows_of(path, counter):
+        out = []
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] == counter:
+                    out.append((int(r["Dispatch_Id"]), r["Kernel_Name"], float(r["Counter_Value"])))
+        out.sort()
+        # the first three copies are the calibration copy (the input rotation's
+        # clones come later and have other sizes)
+        copy = [v for _, n, v in out if "copyBuffer" in n][:3]
+        ours = [(n, v) for _, n, v in out if "gemm_" in n or "splitk_reduce" in n]
+        if not copy:
+            raise SystemExit(f"{path}: no copy dispatches with {counter}")
+        return statistics.mean(copy), ours
+
+    cf, fetch = rows_of(fetch_csv, "FETCH_SIZE")
+    cw, write = rows_of(write_csv, "WRITE_SIZE")
+    ff, wf = COPY_BYTES / 1024 / cf, COPY_BYTES / 1024 / cw
+    want = sum(2 * n for _, _, n in STREAM_CASES)
+    if len(fetch) != want or len(write) != want:
+        raise SystemExit(f"expected {want} split-K dispatches, got {len(fetch)} / {len(write)}")
+    cases, at = [], 0
+    for name, rows, launches in STREAM_CASES:
+        w = wl.WORKLOADS[name]
+        info = imm.gemm_plan(rows, w.N, w.K, w.dtype).info
+        eb = 1 if w.dtype in ("e4m3", "e5m2") else 2
+        slices = info["split_k"] * rows * w.N * 4
+        algo = {"partial": (rows * w.K + w.K * w.N) * eb + slices,
+                "reduce": slices + rows * w.N * 4}
+        got = {}
+        for i in range(2 * launches):
+            (kn, fv), (kn2, wv) = fetch[at + i], write[at + i]
+            kind = "reduce" if "splitk_reduce" in kn else "partial"
+            if kn != kn2:
+                raise SystemExit(f"dispatch order differs between the runs: {kn} / {kn2}")
+            got.setdefault(kind, {"kernel": kn, "read": [], "write": []})
+            got[kind]["read"].append(fv * ff * 1024)
+            got[kind]["write"].append(wv * wf * 1024)
+        at += 2 * launches
+        entry = {"workload": name, "M": rows, "N": w.N, "K": w.K, "split_k": info["split_k"],
+                 "tile": f"{info['block_m']}x{info['block_n']}"}
+        for kind, g in got.items():
+            rd, wr = statistics.mean(g["read"]), statistics.mean(g["write"])
+            entry[kind] = {"kernel": g["kernel"], "launches": len(g["read"]),
+                           "read_bytes_per_launch": rd, "write_bytes_per_launch": wr,
+                           "algorithmic_bytes": algo[kind],
+                           "measured_over_algorithmic": (rd + wr) / algo[kind]}
+        cases.append(entry)
+    out = {"fetch_scale": ff, "write_scale": wf, "copy_fetch_kib": cf, "copy_write_kib": cw,
+           "cases": cases}
     os.makedirs(os.path.dirname(out_path), exist_ok=True)
     with open(out_path, "w") as f:
         json.dump(out, f, indent=1)
@@ -484,6 +588,12 @@ def main():
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="host only: write the headline kernel's HBM traffic from two "
                          "counter runs of --profile-pass, then exit")
+    ap.add_argument("--stream-pass", action="store_true",
+                    help="a plain copy of known size, then the decode and huge-K split-K products "
+                         "on cold inputs, for HBM-traffic counter runs; prints nothing else")
+    ap.add_argument("--write-stream-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="host only: write the split-K kernels' HBM traffic from two counter "
+                         "runs of --stream-pass, then exit")
     ap.add_argument("--clock-pass", action="store_true",
                     help="back-to-back launches of the headline kernel, of torch.matmul on "
                          "the same fp16 product and of a plain copy, for the clock counters; "
@@ -499,6 +609,9 @@ def main():
     args = ap.parse_args()
     if args.write_traffic:
         write_traffic(*args.write_traffic)
+        return
+    if args.write_stream_traffic:
+        write_stream_traffic(*args.write_stream_traffic)
         return
     if args.write_clock:
         if len(args.write_clock) not in (2, 3):
@@ -540,6 +653,11 @@ def main():
 
     if args.power_sample:
         print(json.dumps(power_sample(torch, imm, wl)), flush=True)
+        return
+
+    if args.stream_pass:
+        stream_pass(torch, imm, wl)
+        print("stream pass done", flush=True)
         return
 
     if args.clock_pass:

@@ -124,3 +124,61 @@ def test_clock_without_the_headline_kernel_is_an_error(tmp_path):
     write_counters(counters, [(1, COPY, 0, 400_000, {"GRBM_GUI_ACTIVE": 8 * 0.96e6})])
     with pytest.raises(SystemExit):
         bench.write_clock(str(counters), str(agent), out_path=str(tmp_path / "x.json"))
+
+
+PARTIAL = "void imm::(anonymous namespace)::gemm_tile_kernel<1, 4, 32, 128, 1, 4, true>(imm::GemmArgs)"
+REDUCE = "void imm::(anonymous namespace)::splitk_reduce_kernel<4>(imm::ReduceArgs)"
+HK_PARTIAL = "void imm::(anonymous namespace)::gemm_dma_kernel<0, 4, 1, 128, 2, 3, false, imm::GemmArgs>(imm::GemmArgs)"
+
+
+def _stream_dispatches(counter, copy_value, per_case):
+    """Calibration copies, a clone of another size, then each case's launches
+    (partial, reduction) with the values per_case(case_index, kind)."""
+    d, did = [], 1
+    for _ in range(3):
+        d.append((did, COPY, 0, 10, {counter: copy_value}))
+        did += 1
+    for ci, (_, _, launches) in enumerate(bench.STREAM_CASES):
+        d.append((did, COPY, 0, 10, {counter: 12345.0}))  # input rotation clone
+        did += 1
+        for _ in range(launches):
+            part = HK_PARTIAL if ci == len(bench.STREAM_CASES) - 1 else PARTIAL
+            d.append((did, part, 0, 10, {counter: per_case(ci, "partial")}))
+            d.append((did + 1, REDUCE, 0, 10, {counter: per_case(ci, "reduce")}))
+            did += 2
+    return d
+
+
+def test_stream_traffic_per_case_and_kernel(tmp_path):
+    copy_kib = bench.COPY_BYTES / 1024
+    fetch, write = tmp_path / "fetch.csv", tmp_path / "write.csv"
+    write_counters(fetch, _stream_dispatches("FETCH_SIZE", copy_kib / 2,
+                                             lambda c, k: 1000.0 * (c + 1) + (5 if k == "reduce" else 0)))
+    write_counters(write, _stream_dispatches("WRITE_SIZE", copy_kib,
+                                             lambda c, k: 10.0 * (c + 1)))
+    out = tmp_path / "s.json"
+    bench.write_stream_traffic(str(fetch), str(write), out_path=str(out))
+    t = json.loads(out.read_text())
+    assert t["fetch_scale"] == pytest.approx(2.0) and t["write_scale"] == pytest.approx(1.0)
+    assert [c["workload"] for c in t["cases"]] == [c[0] for c in bench.STREAM_CASES]
+    for ci, c in enumerate(t["cases"]):
+        p, r = c["partial"], c["reduce"]
+        assert p["launches"] == r["launches"] == bench.STREAM_CASES[ci][2]
+        assert p["read_bytes_per_launch"] == pytest.approx(2 * 1000.0 * (ci + 1) * 1024)
+        assert r["read_bytes_per_launch"] == pytest.approx(2 * (1000.0 * (ci + 1) + 5) * 1024)
+        assert p["write_bytes_per_launch"] == pytest.approx(10.0 * (ci + 1) * 1024)
+        # algorithmic bytes: A and B once plus the slices; the slices plus C
+        M, N, K, S = c["M"], c["N"], c["K"], c["split_k"]
+        assert p["algorithmic_bytes"] == (M * K + K * N) * 2 + S * M * N * 4
+        assert r["algorithmic_bytes"] == S * M * N * 4 + M * N * 4
+    assert t["cases"][-1]["partial"]["kernel"] == HK_PARTIAL
+
+
+def test_stream_traffic_rejects_a_missing_launch(tmp_path):
+    copy_kib = bench.COPY_BYTES / 1024
+    fetch, write = tmp_path / "fetch.csv", tmp_path / "write.csv"
+    d = _stream_dispatches("FETCH_SIZE", copy_kib, lambda c, k: 1.0)
+    write_counters(fetch, d[:-1])
+    write_counters(write, _stream_dispatches("WRITE_SIZE", copy_kib, lambda c, k: 1.0))
+    with pytest.raises(SystemExit):
+        bench.write_stream_traffic(str(fetch), str(write), out_path=str(tmp_path / "x.json"))
