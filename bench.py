@@ -426,6 +426,34 @@ def bench_square(name, steps, warmup, torch, imm, wl):
     return w, plan, per, total, (A, B, Ad, Bd)
 
 
+def fp8_comparator(w, plan, host, torch, imm, rounds=3):
+    """The fp8 product next to torch._scaled_mm (hipBLASLt) on the same inputs
+    and per-tensor scales of 1, bf16 out, in alternating rounds of 20 launches
+    (the part's clock follows its recent power draw); best round medians."""
+    _, _, Ad, Bd = host
+    Bcm = Bd.t().contiguous().t()  # the column-major B that _scaled_mm takes
+    one = torch.tensor(1.0, device="cuda")
+    C = torch.empty((w.M, w.N), dtype=torch.bfloat16, device="cuda")
+    last = [None]
+    runs = {"ours": lambda i: imm.gemm_run(plan, Ad, Bd, C),
+            "hipblaslt": lambda i: last.__setitem__(0, torch._scaled_mm(
+                Ad, Bcm, scale_a=one, scale_b=one, out_dtype=torch.bfloat16))}
+    best = {k: [] for k in runs}
+    for r in range(rounds):
+        for k in (("ours", "hipblaslt") if r % 2 == 0 else ("hipblaslt", "ours")):
+            per, _ = time_launches(runs[k], 20, 5, torch)
+            best[k].append(statistics.median(per))
+    out = {}
+    for k, v in best.items():
+        ms = min(v)
+        out[k] = {"best_round_median_ms": ms, "round_medians_ms": v,
+                  "TFLOPs": w.flops / (ms * 1e-3) / 1e12}
+    torch.cuda.synchronize()
+    C2 = last[0].float()
+    out["max_abs_diff_over_max_abs"] = float((C.float() - C2).abs().max() / C2.abs().max())
+    return out
+
+
 def bench_splitk(name, split, torch, imm, wl, n=30, warmup=5, M=None):
     """Split-K path with inputs rotated through enough copies to defeat the MALL."""
     w = wl.WORKLOADS[name]
@@ -736,12 +764,17 @@ def main():
         del Ad, Bd, As, Bs, Cr
         torch.cuda.empty_cache()
         log("fp8 e5m2 8192^3")
-        w8, plan8, per8, _, _ = bench_square("square_e5m2_8192", 30, 5, torch, imm, wl)
+        w8, plan8, per8, _, h8 = bench_square("square_e5m2_8192", 30, 5, torch, imm, wl)
         med8 = statistics.median(per8)
         extra["square_e5m2_8192"] = {**summary(per8),
                                      "TFLOPs": w8.flops / (med8 * 1e-3) / 1e12,
                                      "pct_mfma_peak": 100 * w8.flops / (med8 * 1e-3) / 1e12 /
                                      PEAK_TFLOPS["e5m2"]}
+        try:
+            extra["square_e5m2_8192"]["vs_hipblaslt"] = fp8_comparator(w8, plan8, h8, torch, imm)
+        except Exception as e:  # comparator only
+            extra["square_e5m2_8192"]["hipblaslt_error"] = str(e)
+        del h8
         torch.cuda.empty_cache()
         for n in ("square_f16_4096", "square_f16_1024"):
             # the default plan and GEMM_PLAN_TILE_BY_M in alternating rounds, so
