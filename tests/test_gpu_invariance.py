@@ -75,6 +75,23 @@ def test_random_rows_identical_across_M(dt, split):
         assert np.array_equal(C, full[:m]), (dt, split, m)
 
 
+def test_narrow_long_k_rows_identical_across_M():
+    """The default plan of a narrow reduction-dominated shape with long slices
+    (N = 128, K = 131072: the 128x256 tile and 128 slices of 1024): rows of C
+    keep their bits at every M, on the default tile and on an explicit one."""
+    N, K = 128, 131072
+    A, B = _rand(300, N, K, "bf16", 8050)
+    Ad, Bd = _to_dev(A, B)
+    p = imm.gemm_plan(300, N, K, "bf16")
+    assert (p.info["block_m"], p.info["split_k"]) == (128, 128)
+    full = bits_of(run(p, Ad, Bd, True))
+    for m in (1, 33, 129, 299):
+        for tile in ("default", "32x128"):
+            pm = imm.gemm_plan_ex(m, N, K, "bf16", "f32", tile=tile)
+            C = bits_of(run(pm, Ad[:m].contiguous(), Bd, True))
+            assert np.array_equal(C, full[:m]), (m, tile)
+
+
 def test_row_depends_only_on_its_own_row():
     # Permute rows and replace every other row with fresh data: the surviving
     # rows must come out with the same bits wherever they land.
