@@ -266,3 +266,26 @@ def test_rows_and_columns_outside_the_domain_give_nan(t2):
     good_c = [c for c in range(N) if c not in bad_cols]
     assert np.array_equal(_bits64(got[np.ix_(good_r, good_c)]), _bits64(want[np.ix_(good_r, good_c)]))
     assert not np.isnan(got[np.ix_(good_r, good_c)]).any()
+
+
+@pytest.mark.parametrize("t2", ["bf16", "e4m3", "i8"])
+def test_pair_outer_chunk_inner_order(t2):
+    """The kernel adds the exact chunk products to the fp64 sum pair by pair,
+    chunks inside each pair (the page's fused kernel, "行列積の計算": the K loop
+    inside the slice-pair loops).  On the hand-traced case of the oracle's
+    nesting pin that order gives exactly 2^-70; chunks outside the pairs would
+    give 0.  Rows 1.. and the other columns are zero-padded copies."""
+    from tests.test_oracle_ozaki import nesting_case
+    K, kc = 256, 128
+    x, y = nesting_case(K, kc)
+    A = np.zeros((5, K))
+    A[0] = x[0]
+    A[3] = -x[0]
+    B = np.zeros((K, 20))
+    B[:, 0] = y[:, 0]
+    B[:, 17] = y[:, 0]
+    plan = imm.ozaki_plan(5, 20, K, t2, chunk=kc)
+    C, _ = _run(plan, torch.from_numpy(A).to(dev()), torch.from_numpy(B).to(dev()))
+    want = OZ.gemm(A, B, t2, kc=kc)
+    assert want[0, 0] == 2.0 ** -70 and want[3, 17] == -(2.0 ** -70)
+    assert np.array_equal(_bits64(C), _bits64(want))

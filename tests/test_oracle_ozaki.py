@@ -266,6 +266,39 @@ def pin_chunking_only_moves_roundings(oz=OZ):
     assert np.all(np.abs(c1 - c2) <= 64 * 2.0 ** -53 * ab)
 
 
+def nesting_case(K, kc):
+    """One row x and one column y whose exact chunk products are known by hand
+    (row and column maxima 1, so c0 = 0 on both sides):
+      chunk 0: x_0 y_0 = 1 at slice pair (0, 0); x_1 y_1 = 2^-35 2^-35 = 2^-70,
+               whose only nonzero slices are at a depth p with p delta = 35 or
+               more, so it is a term of a deeper pair than (0, 0);
+      chunk 1 (k = kc): x_kc y_kc = -1 at slice pair (0, 0).
+    Every other term is zero."""
+    x = np.zeros((1, K))
+    y = np.zeros((K, 1))
+    x[0, 0], y[0, 0] = 1.0, 1.0
+    x[0, 1], y[1, 0] = 2.0 ** -35, 2.0 ** -35
+    x[0, kc], y[kc, 0] = -1.0, 1.0
+    return x, y
+
+
+def pin_pair_outer_chunk_inner_order(oz=OZ):
+    """The page's fused kernel ("行列積の計算") runs the K loop inside the loop
+    over slice pairs and adds each pair's product to the fp64 result; with K
+    cut into exact chunks, the chunk loop sits inside the pair loop.  Written
+    out in that order for nesting_case, the fp64 additions are
+        pair (0, 0): 0 + 1 = 1, then 1 + (-1) = 0;
+        the pairs in between add +0;
+        the deeper pair holding x_1 y_1: 0 + 2^-70 = 2^-70,
+    which is also the exact product.  Chunk-outer order would add 2^-70 to 1
+    (lost: 1 + 2^-70 rounds to 1) before the -1 of chunk 1, and give 0."""
+    for t2 in ("bf16", "e4m3", "i8"):
+        for K, kc in ((32, 16), (256, 128)):
+            x, y = nesting_case(K, kc)
+            C = oz.gemm(x, y, t2, kc=kc)
+            assert C.shape == (1, 1) and C[0, 0] == 2.0 ** -70, (t2, K, kc, C[0, 0])
+
+
 def pin_zero_rows(oz=OZ):
     A = np.zeros((3, 32))
     A[1] = np.arange(32) - 7.5
@@ -278,7 +311,7 @@ PINS = [pin_pair_counts, pin_gamma_formula, pin_slices_are_type2_on_grid,
         pin_split_reconstructs, pin_split_residual_bound, pin_integer_inputs_exact,
         pin_identity, pin_powers_of_two_and_sign, pin_rows_independent,
         pin_random_vs_exact, pin_vs_numpy, pin_elems_match_full, pin_chunking_only_moves_roundings,
-        pin_zero_rows]
+        pin_pair_outer_chunk_inner_order, pin_zero_rows]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -311,6 +344,12 @@ MUTANTS = [
      "rho = max(gamma_of(max(1, kc), TYPE3_BITS[type2]), xi)"),
     ("first_slice_dropped", "for p in range(P.s):\n        cp =",
      "for p in range(P.s):\n        if p == 0: r = r - ((r + np.ldexp(0.75, P.rho + c0.reshape(shape))) - np.ldexp(0.75, P.rho + c0.reshape(shape)))\n        cp ="),
+    # the chunk loop outside the pair loop: the same terms, other fp64 roundings
+    ("chunk_outer_pair_inner",
+     "    for p, q in P.pairs:\n        scale = (ca - p * P.delta)[:, None] + (cb - q * P.delta)[None, :]\n"
+     "        for k0 in range(0, K, P.kc):\n",
+     "    for k0 in range(0, K, P.kc):\n      for p, q in P.pairs:\n"
+     "        scale = (ca - p * P.delta)[:, None] + (cb - q * P.delta)[None, :]\n        if True:\n"),
 ]
 
 
