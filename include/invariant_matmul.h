@@ -20,15 +20,39 @@
  * A and of B only: they do not depend on M, on other rows, on concurrently
  * running work, on the stream or on how often the call has run.
  *
- * Calls, their passages:
+ * Calls, their passages (each call's own comment below repeats its passage):
+ *   gemm_plan, gemm_plan_ex, gemm_plan_ex2
+ *                     the problem statement C = A x B with A [M,K], B [K,N],
+ *                     C [M,N] and a configuration fixed from (N, K, dtypes)
+ *                     alone (article, section "Batch Invariance の由来"; section
+ *                     "演算子チューニング" shows the M-driven tile and split
+ *                     choices this planner does not make).
+ *   gemm_plan_info    the configuration a plan fixed: BLOCK_M / BLOCK_N /
+ *                     BLOCK_K, SPLIT_K, GROUP_M and the waves (the tuning
+ *                     parameters of section "演算子チューニング").
+ *   gemm_workspace_size
+ *                     bytes of the [split_k, M, N] fp32 partial-sum workspace
+ *                     (section "Split-K").
+ *   gemm_plan_tile_of the workgroup -> output tile order (section "GROUP_M -
+ *                     Swizzle L2 Cache").
  *   gemm_run          one workgroup per output tile running the K loop
- *                     (article, section "Tiling - 分塊行列乗算": accumulator
- *                     init, load/compute/accumulate per K step, one write-back);
+ *                     (section "Tiling - 分塊行列乗算": accumulator init,
+ *                     load/compute/accumulate per K step, one write-back);
  *                     tiles visited in GROUP_M order (section "GROUP_M -
  *                     Swizzle L2 Cache").
+ *   gemm_run_bias, gemm_splitk_run_bias
+ *                     the same plus the bias of a linear layer (the vLLM
+ *                     batch-invariant linear operator listed in the article's
+ *                     closing section).
  *   gemm_splitk_run   split-K through a [split_k, M, N] fp32 workspace and a
  *                     separate reduction kernel on the same stream, no atomics
  *                     (section "Split-K", the workspace variant).
+ *   ozaki_*           the fp64 product by the Ozaki scheme (Insight Edge blog
+ *                     on cuTile Python, section "倍精度行列積エミュレーション").
+ *   gemm_plan_destroy, ozaki_plan_destroy, gemm_status_string,
+ *   gemm_last_hip_error
+ *                     library housekeeping (freeing a host plan, naming a
+ *                     status, the last HIP error); no passage defines them.
  *
  * Conventions for every call:
  *   - All matrices and the workspace are DEVICE memory owned by the caller; the
@@ -36,15 +60,25 @@
  *     the caller (free it with gemm_plan_destroy).  Plans are immutable and
  *     may be used from several host threads / streams at once (each concurrent
  *     split-K call needs its own workspace).
- *   - `stream` is a hipStream_t passed as void* (NULL means the null stream).
- *     Run calls only enqueue work on it: they never synchronise the host.
+ *   - `stream` is a hipStream_t passed as void* (NULL means the null stream),
+ *     so that a caller needs no HIP header to include this one; a hipStream_t
+ *     converts to void* implicitly in C and C++.  Run calls only enqueue work
+ *     on it: they never synchronise the host.
  *   - Inputs are read-only.  C is fully overwritten (there is no beta).  The
  *     workspace holds no meaningful data after the call.
- *   - Every argument is validated before any HIP call; on error nothing is
- *     enqueued and C is untouched.  A status other than GEMM_OK is returned:
+ *   - Every argument is validated before anything is enqueued (the checks
+ *     that need no runtime come first, so they also run without a GPU); on
+ *     error nothing is enqueued and C is untouched.  A status other than
+ *     GEMM_OK is returned:
  *       GEMM_ERR_INVALID_VALUE  negative size, NULL pointer for a non-empty
  *                               operand, pointer not 16-byte aligned, NULL
- *                               plan or output handle;
+ *                               plan or output handle; on a machine with a
+ *                               GPU also an operand that does not lie
+ *                               wholly inside one device allocation of the
+ *                               current device (host memory, another
+ *                               device's memory, or a buffer shorter than
+ *                               the operand), checked with the runtime's
+ *                               pointer queries before anything is enqueued;
  *       GEMM_ERR_UNSUPPORTED    unsupported dtype pair, N or K not a multiple of
  *                               16 bytes' worth of elements (8 for 16-bit
  *                               inputs, 16 for fp8), bad option value;
@@ -162,44 +196,58 @@ typedef struct {
   int64_t run_tiles_m, run_tiles_n;
 } gemm_plan_info_t;
 
-/* Plan C[M,N] = A[M,K] x B[K,N] with default options: fp32 output for fp16 /
- * bf16 inputs and bf16 output for fp8 inputs, split and tile chosen from
- * (N, K, dtype), GROUP_M = 8, scales 1.0.  M only sizes the grid and the
- * workspace.  On success *out receives a new plan. */
+/* Plan C[M,N] = A[M,K] x B[K,N] (Tencent article, "Batch Invariance の由来":
+ * the problem statement, and the conclusion that the K step and the split of
+ * K must not follow the batch size) with default options: fp32 output for
+ * fp16 / bf16 inputs and bf16 output for fp8 inputs, split and tile chosen
+ * from (N, K, dtype), GROUP_M = 8, scales 1.0.  M only sizes the grid and the
+ * workspace.  On success *out receives a new plan (host memory; free it with
+ * gemm_plan_destroy). */
 gemm_status gemm_plan(int64_t M, int64_t N, int64_t K, gemm_dtype in, gemm_plan_t* out);
 
-/* As gemm_plan with explicit options.  out_dtype: GEMM_F32, GEMM_BF16 or
- * GEMM_F16.
+/* As gemm_plan with explicit options (same passage).  out_dtype: GEMM_F32,
+ * GEMM_BF16 or GEMM_F16.
  * split_k: 0 = default, else 1..4096 (the slice length is rounded up to a
  * multiple of block_k; the split actually used is reported by
- * gemm_plan_info).  group_m: 0 = default (8), else >= 1.  tile: a gemm_tile
- * value.  scale_a, scale_b: per-tensor scales multiplied into the result
- * (their fp32 product is applied to the fp32 sum before the output
- * conversion); must be finite. */
+ * gemm_plan_info).  group_m: 0 = default (8), else >= 1.  scale_a, scale_b:
+ * per-tensor scales multiplied into the result (their fp32 product is applied
+ * to the fp32 sum before the output conversion); must be finite. */
 gemm_status gemm_plan_ex(int64_t M, int64_t N, int64_t K, gemm_dtype in, gemm_dtype out,
-                         int split_k, int group_m, int tile, float scale_a, float scale_b,
+                         int split_k, int group_m, float scale_a, float scale_b,
                          gemm_plan_t* plan);
 
-/* As gemm_plan_ex with plan flags (a bitwise OR of gemm_plan_flags; unknown
- * bits give GEMM_ERR_UNSUPPORTED).  With GEMM_PLAN_B_TRANSPOSED, B is read as
- * [N, K] row-major; an explicit register-staged tile, or a K so large that the
- * DMA tiles' 32-bit offsets overflow, gives GEMM_ERR_UNSUPPORTED. */
+/* As gemm_plan_ex with an explicit output tile and plan flags (same passage;
+ * the tile is the article's BLOCK_M / BLOCK_N, which it shows changes no bit).
+ * tile: a gemm_tile value (GEMM_TILE_DEFAULT: chosen from (N, K, dtype)).
+ * flags: a bitwise OR of gemm_plan_flags; unknown bits give
+ * GEMM_ERR_UNSUPPORTED.  With GEMM_PLAN_B_TRANSPOSED, B is read as [N, K]
+ * row-major; an explicit register-staged tile, or a K so large that the DMA
+ * tiles' 32-bit offsets overflow, gives GEMM_ERR_UNSUPPORTED. */
 gemm_status gemm_plan_ex2(int64_t M, int64_t N, int64_t K, gemm_dtype in, gemm_dtype out,
                           int split_k, int group_m, int tile, float scale_a, float scale_b,
                           unsigned flags, gemm_plan_t* plan);
 
+/* The configuration a plan fixed (Tencent article, "演算子チューニング": the
+ * tile sizes, the K step, SPLIT_K and GROUP_M of its parameter table), into
+ * *info.  Pure host call.  GEMM_ERR_INVALID_VALUE for a NULL argument. */
 gemm_status gemm_plan_info(gemm_plan_t plan, gemm_plan_info_t* info);
 
-/* Bytes of workspace gemm_splitk_run needs: split_k * M * N * sizeof(float). */
+/* Bytes of workspace gemm_splitk_run needs: split_k * M * N * sizeof(float),
+ * the [split_k, M, N] fp32 partial sums (Tencent article, "Split-K").  0 for
+ * a NULL plan. */
 size_t gemm_workspace_size(gemm_plan_t plan);
 
 /* Tile raster: the (k_slice, pid_m, pid_n) that workgroup `workgroup` of the
- * split-K partial kernel computes (k_slice is 0 for gemm_run's grid).  Pure
- * host function, exposed so the raster can be checked to be a bijection. */
+ * split-K partial kernel computes (k_slice is 0 for gemm_run's grid), after
+ * the XCD remap and the GROUP_M order (Tencent article, "GROUP_M - Swizzle L2
+ * Cache").  Pure host function, exposed so the raster can be checked to be a
+ * bijection.  GEMM_ERR_INVALID_VALUE for a workgroup outside the grid. */
 gemm_status gemm_plan_tile_of(gemm_plan_t plan, int64_t workgroup, int64_t* k_slice,
                               int64_t* pid_m, int64_t* pid_n);
 
-/* C = A x B in one pass: one workgroup per output tile, full K in order. */
+/* C = A x B in one pass: one workgroup per output tile, full K in order
+ * (Tencent article, "Tiling - 分塊行列乗算").  A, B, C: device memory,
+ * row-major, 16-byte aligned; enqueued on `stream`. */
 gemm_status gemm_run(gemm_plan_t plan, const void* A, const void* B, void* C, void* stream);
 
 /* As gemm_run plus a bias: C[i, j] = convert(scale * sum_ij + bias[j]), one
@@ -209,10 +257,12 @@ gemm_status gemm_run(gemm_plan_t plan, const void* A, const void* B, void* C, vo
 gemm_status gemm_run_bias(gemm_plan_t plan, const void* A, const void* B, const float* bias,
                           void* C, void* stream);
 
-/* C = A x B through the split-K workspace: the partial kernel writes slice s
- * of K to workspace[s, :, :] (fp32, no atomics), then a reduction kernel sums
- * the slices in ascending s and writes C.  With split_k == 1 the result is
- * bitwise identical to gemm_run. */
+/* C = A x B through the split-K workspace (Tencent article, "Split-K", the
+ * workspace variant): the partial kernel writes slice s of K to
+ * workspace[s, :, :] (fp32, no atomics), then a reduction kernel sums the
+ * slices in ascending s and writes C.  With split_k == 1 the result is
+ * bitwise identical to gemm_run.  workspace: device memory of at least
+ * gemm_workspace_size(plan) bytes, 16-byte aligned, owned by the caller. */
 gemm_status gemm_splitk_run(gemm_plan_t plan, const void* A, const void* B, void* C,
                             void* workspace, size_t workspace_bytes, void* stream);
 
@@ -222,7 +272,9 @@ gemm_status gemm_splitk_run_bias(gemm_plan_t plan, const void* A, const void* B,
                                  const float* bias, void* C, void* workspace,
                                  size_t workspace_bytes, void* stream);
 
+/* Frees a host plan (NULL is ignored).  Housekeeping: no passage. */
 void gemm_plan_destroy(gemm_plan_t plan);
+
 
 /* ---------------------------------------------------------------------------
  * fp64 matrix product by the Ozaki scheme: C = A x B with A [M,K], B [K,N]
@@ -324,6 +376,7 @@ gemm_status ozaki_run(ozaki_plan_t plan, const double* A, const double* B, doubl
 
 void ozaki_plan_destroy(ozaki_plan_t plan);
 
+/* Name of a status ("GEMM_OK", ...); a static string.  Housekeeping. */
 const char* gemm_status_string(gemm_status status);
 
 /* HIP error code (hipError_t as int) of the most recent GEMM_ERR_HIP return on

@@ -22,7 +22,8 @@ import os
 __all__ = [
     "GemmError", "Plan", "PlanInfo", "gemm_plan", "gemm_plan_ex", "gemm_plan_ex2",
     "gemm_plan_info", "gemm_workspace_size", "gemm_plan_tile_of", "gemm_run", "gemm_splitk_run",
-    "gemm_plan_destroy", "gemm_status_string", "gemm_last_hip_error", "mm", "lib", "LIB_PATH",
+    "gemm_plan_destroy", "gemm_status_string", "gemm_last_hip_error", "mm", "out_torch_dtype",
+    "lib", "LIB_PATH",
     "DTYPE", "TILE", "STATUS", "EXPORTED_SYMBOLS", "PLAN_B_TRANSPOSED", "PLAN_PERSISTENT",
     "PLAN_TILE_BY_M",
     "OzakiPlan", "ozaki_plan", "ozaki_plan_info", "ozaki_workspace_size", "ozaki_split",
@@ -110,7 +111,7 @@ def lib() -> ctypes.CDLL:
         i64, i32, vp, f32 = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_float
         pp = ctypes.POINTER(ctypes.c_void_p)
         L.gemm_plan.argtypes = [i64, i64, i64, i32, pp]
-        L.gemm_plan_ex.argtypes = [i64, i64, i64, i32, i32, i32, i32, i32, f32, f32, pp]
+        L.gemm_plan_ex.argtypes = [i64, i64, i64, i32, i32, i32, i32, f32, f32, pp]
         L.gemm_plan_ex2.argtypes = [i64, i64, i64, i32, i32, i32, i32, i32, f32, f32,
                                     ctypes.c_uint, pp]
         L.gemm_plan_info.argtypes = [vp, ctypes.POINTER(PlanInfo)]
@@ -192,10 +193,18 @@ def gemm_plan(M: int, N: int, K: int, dtype) -> Plan:
 def gemm_plan_ex(M: int, N: int, K: int, dtype, out_dtype="f32", split_k: int = 0,
                  group_m: int = 0, tile="default", scale_a: float = 1.0,
                  scale_b: float = 1.0) -> Plan:
+    """Plan with explicit options.  An explicit tile is a gemm_plan_ex2 option
+    (the C call gemm_plan_ex has none), so a tile other than "default" plans
+    through gemm_plan_ex2 with no flags."""
     h = ctypes.c_void_p()
     t = TILE[tile] if isinstance(tile, str) else int(tile)
-    _check(lib().gemm_plan_ex(M, N, K, _dtype_code(dtype), _dtype_code(out_dtype), split_k,
-                              group_m, t, scale_a, scale_b, ctypes.byref(h)), "gemm_plan_ex")
+    if t == TILE["default"]:
+        _check(lib().gemm_plan_ex(M, N, K, _dtype_code(dtype), _dtype_code(out_dtype), split_k,
+                                  group_m, scale_a, scale_b, ctypes.byref(h)), "gemm_plan_ex")
+    else:
+        _check(lib().gemm_plan_ex2(M, N, K, _dtype_code(dtype), _dtype_code(out_dtype), split_k,
+                                   group_m, t, scale_a, scale_b, 0, ctypes.byref(h)),
+               "gemm_plan_ex2")
     return Plan(h.value)
 
 
@@ -245,6 +254,17 @@ def _stream(stream, *tensors):
     return 0
 
 
+def _check_device(t, name):
+    """A tensor operand must live on the current CUDA (HIP) device: the kernels
+    run there and would take a memory fault on a host or foreign address."""
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a CUDA (HIP) tensor, got one on {t.device}")
+    import torch
+    cur = torch.cuda.current_device()
+    if t.device.index != cur:
+        raise ValueError(f"{name} is on {t.device}, but the current device is cuda:{cur}")
+
+
 def _check_tensor(t, name, dtype_code, numel):
     if t is None or isinstance(t, int):
         return
@@ -254,6 +274,7 @@ def _check_tensor(t, name, dtype_code, numel):
         raise ValueError(f"{name} has dtype {t.dtype}, plan expects code {dtype_code}")
     if t.numel() != numel:
         raise ValueError(f"{name} has {t.numel()} elements, plan expects {numel}")
+    _check_device(t, name)
 
 
 def _check_operands(plan: Plan, A, B, C, bias=None):
@@ -275,6 +296,7 @@ def gemm_splitk_run(plan: Plan, A, B, C, workspace, stream=None, workspace_bytes
                     bias=None) -> None:
     """C = A @ B (+ bias) through the split-K workspace and the reduction kernel."""
     _check_operands(plan, A, B, C, bias)
+    _check_ws_device(workspace)
     if workspace_bytes is None:
         workspace_bytes = 0 if workspace is None or isinstance(workspace, int) else (
             workspace.numel() * workspace.element_size())
@@ -297,6 +319,16 @@ def gemm_last_hip_error() -> int:
     return int(lib().gemm_last_hip_error())
 
 
+def out_torch_dtype(code: int):
+    """The torch dtype of an output dtype code (GEMM_F32, GEMM_BF16, GEMM_F16)."""
+    import torch
+    table = {DTYPE["f32"]: torch.float32, DTYPE["bf16"]: torch.bfloat16,
+             DTYPE["f16"]: torch.float16}
+    if code not in table:
+        raise ValueError(f"output dtype code {code} is not one of f32, bf16, f16")
+    return table[code]
+
+
 def mm(A, B, out_dtype=None, split_k=None, plan: Plan | None = None, stream=None):
     """C = A @ B through the library, allocating C (and a workspace) with torch.
 
@@ -304,6 +336,8 @@ def mm(A, B, out_dtype=None, split_k=None, plan: Plan | None = None, stream=None
     path.  The plan is made from (N, K, dtype) options only, never from M.
     """
     import torch
+    _check_device(A, "A")
+    _check_device(B, "B")
     M, K = A.shape
     N = B.shape[1]
     if plan is None:
@@ -311,8 +345,7 @@ def mm(A, B, out_dtype=None, split_k=None, plan: Plan | None = None, stream=None
             "bf16" if A.dtype in (torch.float8_e4m3fn, torch.float8_e5m2) else "f32")
         plan = gemm_plan_ex(M, N, K, A.dtype, od, split_k=split_k or 0)
     info = gemm_plan_info(plan)
-    out_t = torch.float32 if info["out_dtype"] == DTYPE["f32"] else torch.bfloat16
-    C = torch.empty((M, N), dtype=out_t, device=A.device)
+    C = torch.empty((M, N), dtype=out_torch_dtype(info["out_dtype"]), device=A.device)
     if split_k is None:
         gemm_run(plan, A, B, C, stream)
     else:
@@ -361,6 +394,11 @@ def ozaki_workspace_size(plan: OzakiPlan) -> int:
     return int(lib().ozaki_workspace_size(plan.handle))
 
 
+def _check_ws_device(workspace):
+    if workspace is not None and not isinstance(workspace, int):
+        _check_device(workspace, "workspace")
+
+
 def _ws_bytes(workspace, workspace_bytes):
     if workspace_bytes is not None:
         return int(workspace_bytes)
@@ -375,6 +413,7 @@ def _check_f64(t, name, numel):
     import torch
     if t.dtype != torch.float64 or not t.is_contiguous() or t.numel() != numel:
         raise ValueError(f"{name} must be a contiguous float64 tensor of {numel} elements")
+    _check_device(t, name)
 
 
 def ozaki_split(plan: OzakiPlan, operand: int, x, workspace, stream=None,
@@ -382,6 +421,7 @@ def ozaki_split(plan: OzakiPlan, operand: int, x, workspace, stream=None,
     """Slices and exponents of A (operand 0, [M, K]) or B (1, [K, N]) into the workspace."""
     i = ozaki_plan_info(plan)
     _check_f64(x, "x", i["M"] * i["K"] if operand == 0 else i["K"] * i["N"])
+    _check_ws_device(workspace)
     _check(lib().ozaki_split(plan.handle, int(operand), _addr(x), _addr(workspace),
                              _ws_bytes(workspace, workspace_bytes), _stream(stream, x, workspace)),
            "ozaki_split")
@@ -391,6 +431,7 @@ def ozaki_multiply(plan: OzakiPlan, workspace, C, stream=None, workspace_bytes=N
     """The slice-pair product from a workspace filled by ozaki_split of A and B."""
     i = ozaki_plan_info(plan)
     _check_f64(C, "C", i["M"] * i["N"])
+    _check_ws_device(workspace)
     _check(lib().ozaki_multiply(plan.handle, _addr(workspace), _ws_bytes(workspace, workspace_bytes),
                                 _addr(C), _stream(stream, C, workspace)), "ozaki_multiply")
 
@@ -401,6 +442,7 @@ def ozaki_run(plan: OzakiPlan, A, B, C, workspace, stream=None, workspace_bytes=
     _check_f64(A, "A", i["M"] * i["K"])
     _check_f64(B, "B", i["K"] * i["N"])
     _check_f64(C, "C", i["M"] * i["N"])
+    _check_ws_device(workspace)
     _check(lib().ozaki_run(plan.handle, _addr(A), _addr(B), _addr(C), _addr(workspace),
                            _ws_bytes(workspace, workspace_bytes), _stream(stream, A, B, C)),
            "ozaki_run")
@@ -409,6 +451,8 @@ def ozaki_run(plan: OzakiPlan, A, B, C, workspace, stream=None, workspace_bytes=
 def ozaki_mm(A, B, type2="bf16", slices: int = 0, d: int = 0, chunk: int = 0, stream=None):
     """C = A @ B for fp64 CUDA tensors, allocating C and the workspace with torch."""
     import torch
+    _check_device(A, "A")
+    _check_device(B, "B")
     M, K = A.shape
     N = B.shape[1]
     plan = ozaki_plan(M, N, K, type2, slices, d, chunk)

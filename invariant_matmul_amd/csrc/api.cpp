@@ -18,9 +18,10 @@
 #include <climits>
 #include <cmath>
 #include <cstring>
+#include <initializer_list>
 #include <new>
 
-#include "imm_internal.h"
+#include "host_internal.h"
 
 using namespace imm;
 
@@ -205,6 +206,60 @@ hipError_t device_ready() {
   return n > 0 ? hipSuccess : hipErrorNoDevice;
 }
 
+// One operand of a call: its first byte and the bytes the kernels touch.
+struct Span {
+  const void* p;
+  size_t bytes;
+};
+
+// True if the span lies in device memory that kernels on device `dev` may
+// access: inside one allocation made on that device, or in managed memory.
+// A pointer the runtime does not know (pageable host memory), host memory,
+// another device's memory or a span running past the end of its allocation
+// is rejected: a kernel touching it would take a memory fault.
+bool on_device(const Span& s, int dev) {
+  hipPointerAttribute_t at;
+  if (hipPointerGetAttributes(&at, s.p) != hipSuccess) {
+    (void)hipGetLastError();  // clear the lookup's error: it is not a failed call
+    return false;
+  }
+  if (at.type == hipMemoryTypeManaged || at.isManaged) return true;
+  if (at.type != hipMemoryTypeDevice || at.device != dev) return false;
+  hipDeviceptr_t base = nullptr;
+  size_t size = 0;
+  if (hipMemGetAddressRange(&base, &size, const_cast<void*>(s.p)) != hipSuccess) {
+    (void)hipGetLastError();
+    return false;
+  }
+  const uintptr_t b = reinterpret_cast<uintptr_t>(base), q = reinterpret_cast<uintptr_t>(s.p);
+  return q >= b && q - b <= size && s.bytes <= size - (q - b);
+}
+
+// After device_ready(): every span with a non-null pointer must lie in device
+// memory of the current device (GEMM_ERR_INVALID_VALUE otherwise, nothing
+// enqueued).
+gemm_status check_device_spans(std::initializer_list<Span> spans) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e);
+  for (const Span& sp : spans)
+    if (sp.p && !on_device(sp, dev)) return GEMM_ERR_INVALID_VALUE;
+  return GEMM_OK;
+}
+
+// The spans of a GEMM call's operands (A and B only when K > 0).
+gemm_status check_gemm_spans(const gemm_plan_s* p, const void* A, const void* B, const void* C,
+                             const float* bias, const void* ws, size_t ws_bytes) {
+  const size_t eb = (size_t)elem_bytes(p->in);
+  const size_t ob = p->out == GEMM_F32 ? 4 : 2;
+  const size_t M = (size_t)p->M, N = (size_t)p->N, K = (size_t)p->K;
+  return check_device_spans({{K > 0 ? A : nullptr, M * K * eb},
+                             {K > 0 ? B : nullptr, K * N * eb},
+                             {C, M * N * ob},
+                             {bias, N * sizeof(float)},
+                             {ws, ws_bytes}});
+}
+
 gemm_status check_operands(const gemm_plan_s* p, const void* A, const void* B, const void* C) {
   if (!p) return GEMM_ERR_INVALID_VALUE;
   if (p->M == 0 || p->N == 0) return GEMM_OK;
@@ -257,6 +312,48 @@ int oz_exact_bits(int64_t k, int m3) {
 
 }  // namespace
 
+namespace imm {
+
+gemm_status record_hip_error(hipError_t e) { return hip_fail(e); }
+
+gemm_status check_run_args(const gemm_plan_s* p, const void* A, const void* B, const void* C,
+                           const float* bias) {
+  gemm_status st = check_operands(p, A, B, C);
+  if (st != GEMM_OK) return st;
+  if (bias && !aligned4(bias)) return GEMM_ERR_INVALID_VALUE;
+  return GEMM_OK;
+}
+
+gemm_status splitk_run(const gemm_plan_s* p, const void* A, const void* B, const float* bias,
+                       void* C, void* workspace, size_t workspace_bytes, bool check_ws,
+                       hipStream_t s) {
+  gemm_status st = check_run_args(p, A, B, C, bias);
+  if (st != GEMM_OK || p->M == 0 || p->N == 0) return st;
+  if (!workspace || workspace_bytes < gemm_workspace_size(const_cast<gemm_plan_s*>(p)))
+    return GEMM_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return GEMM_ERR_INVALID_VALUE;
+  hipError_t e = device_ready();
+  if (e != hipSuccess) return hip_fail(e);
+  const size_t ws_need = gemm_workspace_size(const_cast<gemm_plan_s*>(p));
+  st = check_gemm_spans(p, A, B, C, bias, check_ws ? workspace : nullptr, ws_need);
+  if (st != GEMM_OK) return st;
+  e = launch_gemm(*p, p->tile, make_args(p, A, B, workspace, true), true, s);
+  if (e != hipSuccess) return hip_fail(e);
+  ReduceArgs r;
+  r.ws = static_cast<const float*>(workspace);
+  r.C = C;
+  r.bias = bias;
+  r.MN = p->M * p->N;
+  r.N = p->N;
+  r.split_k = p->split_k;
+  r.scale = p->scale;
+  e = launch_reduce(*p, r, s);
+  if (e != hipSuccess) return hip_fail(e);
+  return GEMM_OK;
+}
+
+}  // namespace imm
+
 struct ozaki_plan_s {
   int64_t M, N, K;
   int type2, eb;
@@ -271,9 +368,10 @@ struct ozaki_plan_s {
 extern "C" {
 
 gemm_status gemm_plan_ex(int64_t M, int64_t N, int64_t K, gemm_dtype in, gemm_dtype out,
-                         int split_k, int group_m, int tile, float scale_a, float scale_b,
+                         int split_k, int group_m, float scale_a, float scale_b,
                          gemm_plan_t* plan) {
-  return gemm_plan_ex2(M, N, K, in, out, split_k, group_m, tile, scale_a, scale_b, 0, plan);
+  return gemm_plan_ex2(M, N, K, in, out, split_k, group_m, GEMM_TILE_DEFAULT, scale_a, scale_b, 0,
+                       plan);
 }
 
 gemm_status gemm_plan_ex2(int64_t M, int64_t N, int64_t K, gemm_dtype in, gemm_dtype out,
@@ -364,7 +462,7 @@ gemm_status gemm_plan_ex2(int64_t M, int64_t N, int64_t K, gemm_dtype in, gemm_d
 
 gemm_status gemm_plan(int64_t M, int64_t N, int64_t K, gemm_dtype in, gemm_plan_t* out) {
   const gemm_dtype od = (in == GEMM_F8_E4M3 || in == GEMM_F8_E5M2) ? GEMM_BF16 : GEMM_F32;
-  return gemm_plan_ex(M, N, K, in, od, 0, 0, GEMM_TILE_DEFAULT, 1.0f, 1.0f, out);
+  return gemm_plan_ex(M, N, K, in, od, 0, 0, 1.0f, 1.0f, out);
 }
 
 gemm_status gemm_plan_info(gemm_plan_t p, gemm_plan_info_t* info) {
@@ -423,6 +521,8 @@ gemm_status gemm_run_bias(gemm_plan_t p, const void* A, const void* B, const flo
   if (bias && !aligned4(bias)) return GEMM_ERR_INVALID_VALUE;
   hipError_t e = device_ready();
   if (e != hipSuccess) return hip_fail(e);
+  st = check_gemm_spans(p, A, B, C, bias, nullptr, 0);
+  if (st != GEMM_OK) return st;
   GemmArgs a = make_args(p, A, B, C, false);
   a.bias = bias;
   // The persistent kernel evaluates the raster in 32-bit arithmetic and
@@ -461,27 +561,8 @@ gemm_status gemm_splitk_run(gemm_plan_t p, const void* A, const void* B, void* C
 
 gemm_status gemm_splitk_run_bias(gemm_plan_t p, const void* A, const void* B, const float* bias,
                                  void* C, void* workspace, size_t workspace_bytes, void* stream) {
-  gemm_status st = check_operands(p, A, B, C);
-  if (st != GEMM_OK || p->M == 0 || p->N == 0) return st;
-  if (bias && !aligned4(bias)) return GEMM_ERR_INVALID_VALUE;
-  if (!workspace || workspace_bytes < gemm_workspace_size(p)) return GEMM_ERR_WORKSPACE;
-  if (!aligned16(workspace)) return GEMM_ERR_INVALID_VALUE;
-  hipError_t e = device_ready();
-  if (e != hipSuccess) return hip_fail(e);
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  e = launch_gemm(*p, p->tile, make_args(p, A, B, workspace, true), true, s);
-  if (e != hipSuccess) return hip_fail(e);
-  ReduceArgs r;
-  r.ws = static_cast<const float*>(workspace);
-  r.C = C;
-  r.bias = bias;
-  r.MN = p->M * p->N;
-  r.N = p->N;
-  r.split_k = p->split_k;
-  r.scale = p->scale;
-  e = launch_reduce(*p, r, s);
-  if (e != hipSuccess) return hip_fail(e);
-  return GEMM_OK;
+  return imm::splitk_run(p, A, B, bias, C, workspace, workspace_bytes, true,
+                         static_cast<hipStream_t>(stream));
 }
 
 void gemm_plan_destroy(gemm_plan_t p) { delete p; }
@@ -627,6 +708,8 @@ gemm_status ozaki_split(ozaki_plan_t p, int operand, const double* x, void* ws, 
   if (st != GEMM_OK) return st;
   hipError_t e = device_ready();
   if (e != hipSuccess) return hip_fail(e);
+  st = check_device_spans({{n > 0 ? x : nullptr, (size_t)n * 8}, {ws, p->ws_bytes}});
+  if (st != GEMM_OK) return st;
   return oz_split(p, operand, x, ws, static_cast<hipStream_t>(stream));
 }
 
@@ -638,6 +721,8 @@ gemm_status ozaki_multiply(ozaki_plan_t p, const void* ws, size_t bytes, double*
   if (st != GEMM_OK) return st;
   hipError_t e = device_ready();
   if (e != hipSuccess) return hip_fail(e);
+  st = check_device_spans({{ws, p->ws_bytes}, {C, (size_t)p->M * p->N * 8}});
+  if (st != GEMM_OK) return st;
   const char* w = static_cast<const char*>(ws);
   OzGemmArgs a;
   a.A = w + p->off_sa;
@@ -678,6 +763,11 @@ gemm_status ozaki_run(ozaki_plan_t p, const double* A, const double* B, double* 
   if (st != GEMM_OK) return st;
   hipError_t e = device_ready();
   if (e != hipSuccess) return hip_fail(e);
+  st = check_device_spans({{p->K > 0 ? A : nullptr, (size_t)p->M * p->K * 8},
+                           {p->K > 0 ? B : nullptr, (size_t)p->K * p->N * 8},
+                           {C, (size_t)p->M * p->N * 8},
+                           {ws, p->ws_bytes}});
+  if (st != GEMM_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if ((st = oz_split(p, 0, A, ws, s)) != GEMM_OK) return st;
   if ((st = oz_split(p, 1, B, ws, s)) != GEMM_OK) return st;

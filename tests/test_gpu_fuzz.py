@@ -6,7 +6,8 @@ than a stage, K down to one 16-byte chunk), runs every tile the library has
 - all of them give the same bits (the tile and the B layout only move work in
   space, the Tencent deterministic-inference article, "Batch Invariance の由来");
 - the result is within the oracle's bound on every element (for fp8 inputs
-  with the matrix step's measured window added, see tests/helpers.py).
+  with K below FP8_PLAIN_BOUND_MIN_K, with the matrix step's measured window
+  added, see tests/helpers.py).
 The shapes and options come from a fixed seed, so a failure names a case
 that reruns identically.
 """
@@ -19,7 +20,7 @@ import torch
 import invariant_matmul_amd as imm
 import oracle
 import workloads as wl
-from tests.helpers import FP8, bits_of, check_bound, dev, fp8_step_window, log, out_torch_dtype, values_of
+from tests.helpers import bits_of, dev, fp8_check_bound, log, out_torch_dtype, values_of
 
 pytestmark = pytest.mark.gpu
 
@@ -75,9 +76,5 @@ def test_random_case(seed):
                 got = bits_of(C)
                 if ref is None:
                     ref = got
-                    win = None
-                    if dt in FP8:
-                        win = fp8_step_window(oracle.decode(dt, wl.bits(A)),
-                                              oracle.decode(dt, wl.bits(B)))
-                    check_bound(values_of(C), C64, Cabs, K, out, window=win)
+                    fp8_check_bound(values_of(C), C64, Cabs, K, out, dt, wl.bits(A), wl.bits(B))
                 assert np.array_equal(got, ref), (tile, flags, use_split)

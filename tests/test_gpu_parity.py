@@ -14,8 +14,8 @@ import torch
 import invariant_matmul_amd as imm
 import oracle
 import workloads as wl
-from tests.helpers import (FP8, bits_of, check_bound, dev, expected_bits, fp8_step_window, log,
-                           run, values_of)
+from tests.helpers import (FP8, FP8_PLAIN_BOUND_MIN_K, bits_of, check_bound, dev, expected_bits,
+                           fp8_check_bound, log, run, values_of)
 
 pytestmark = pytest.mark.gpu
 
@@ -106,17 +106,17 @@ def test_random_inputs_within_bound_ragged(dt):
     g = wl.gen(7300 + IN_DTYPES.index(dt))
     A = wl.uniform((M, K), dt, g) if dt in ("f16", "bf16") else wl.normal((M, K), dt, g)
     B = wl.uniform((K, N), dt, g) if dt in ("f16", "bf16") else wl.normal((K, N), dt, g)
-    C64, Ca = oracle.gemm(wl.bits(A), wl.bits(B), dt)
-    win = None
-    if dt in FP8:
-        win = fp8_step_window(oracle.decode(dt, wl.bits(A)), oracle.decode(dt, wl.bits(B)))
+    a_bits, b_bits = wl.bits(A), wl.bits(B)
+    C64, Ca = oracle.gemm(a_bits, b_bits, dt)
     Ad, Bd = _to_dev(A, B)
     for out in ("f32", "bf16"):
         for tile in TILES:
             for split in (1, 5):
                 p = imm.gemm_plan_ex(M, N, K, dt, out, split_k=split, tile=tile)
-                r1 = check_bound(values_of(run(p, Ad, Bd, False)), C64, Ca, K, out, window=win)
-                r2 = check_bound(values_of(run(p, Ad, Bd, True)), C64, Ca, K, out, window=win)
+                r1 = fp8_check_bound(values_of(run(p, Ad, Bd, False)), C64, Ca, K, out, dt,
+                                     a_bits, b_bits)
+                r2 = fp8_check_bound(values_of(run(p, Ad, Bd, True)), C64, Ca, K, out, dt,
+                                     a_bits, b_bits)
                 log(f"random {dt}->{out} tile {tile} split {split}: max err/bound {r1:.3g} {r2:.3g}")
 
 
@@ -187,23 +187,22 @@ def _check_sampled(w, plan, split, n=2048):
     ii, jj = _sample_positions(w.M, w.N, n, w.seed)
     got = C[torch.from_numpy(ii).to(dev()), torch.from_numpy(jj).to(dev())]
     got = got.cpu().to(torch.float64).numpy()
-    c64, ca = oracle.gemm_elems(wl.bits(A), wl.bits(B), w.dtype, ii, jj)
-    fp8 = w.dtype in FP8
-    if fp8:
-        Av, Bv = oracle.decode(w.dtype, wl.bits(A)), oracle.decode(w.dtype, wl.bits(B))
-    win = (lambda i, j: fp8_step_window(Av, Bv, i, j)) if fp8 else (lambda i, j: None)
-    r = check_bound(got, c64, ca, w.K, w.out, window=win(ii, jj))
-    # a full row and a full column as well
+    a_bits, b_bits = wl.bits(A), wl.bits(B)
+    c64, ca = oracle.gemm_elems(a_bits, b_bits, w.dtype, ii, jj)
+    # fp8 at these sizes (K >= FP8_PLAIN_BOUND_MIN_K) gets the plain bound
+    chk = lambda got_, c_, ca_, i_, j_: fp8_check_bound(got_, c_, ca_, w.K, w.out, w.dtype,
+                                                        a_bits, b_bits, i_, j_)
+    r = chk(got, c64, ca, ii, jj)
+    # a full row and a full column as well (element by element: the row form
+    # of the oracle decodes all of B)
     row = w.M // 2
-    cr, car = oracle.gemm(wl.bits(A), wl.bits(B), w.dtype, rows=[row])
     jr = np.arange(w.N)
-    r = max(r, check_bound(C[row].cpu().to(torch.float64).numpy(), cr[0], car[0], w.K, w.out,
-                           window=win(np.full(w.N, row), jr)))
+    cr, car = oracle.gemm_elems(a_bits, b_bits, w.dtype, np.full(w.N, row), jr)
+    r = max(r, chk(C[row].cpu().to(torch.float64).numpy(), cr, car, np.full(w.N, row), jr))
     col = w.N // 3
     ic = np.arange(w.M)
-    cc, cac = oracle.gemm_elems(wl.bits(A), wl.bits(B), w.dtype, ic, np.full(w.M, col))
-    r = max(r, check_bound(C[:, col].cpu().to(torch.float64).numpy(), cc, cac, w.K, w.out,
-                           window=win(ic, np.full(w.M, col))))
+    cc, cac = oracle.gemm_elems(a_bits, b_bits, w.dtype, ic, np.full(w.M, col))
+    r = max(r, chk(C[:, col].cpu().to(torch.float64).numpy(), cc, cac, ic, np.full(w.M, col)))
     log(f"{w.name}: max err/bound {r:.3g}")
     return C
 
@@ -212,6 +211,7 @@ def _check_sampled(w, plan, split, n=2048):
                                   "square_e5m2_4096", "square_e5m2_8192", "square_e5m2_16384"])
 def test_full_size_square(name):
     w = wl.WORKLOADS[name]
+    assert w.dtype not in FP8 or w.K >= FP8_PLAIN_BOUND_MIN_K  # fp8 sizes: plain bound
     plan = imm.gemm_plan(w.M, w.N, w.K, w.dtype)
     assert imm.DTYPE[w.out] == plan.info["out_dtype"]
     _check_sampled(w, plan, split=False)

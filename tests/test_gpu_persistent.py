@@ -1,5 +1,6 @@
 """The persistent single pass (GEMM_PLAN_PERSISTENT) against the one-tile-per-
-workgroup single pass, bit for bit.
+workgroup single pass, bit for bit, and against the CPU oracle: bit-exact on
+integer inputs, within the error bound on random ones.
 
 The Tencent deterministic-inference article's closing section lists a
 persistent matmul as the batch-invariant GEMM.  Here it is the same kernel
@@ -14,6 +15,7 @@ import pytest
 import torch
 
 import invariant_matmul_amd as imm
+import oracle
 import workloads as wl
 from tests.helpers import bits_of, dev, log, out_torch_dtype
 
@@ -81,3 +83,55 @@ def test_persistent_rows_independent_of_M():
     for m in (1, 255, 257, 1024, 2999):
         part, _ = _run(m, N, K, "f16", "f32", A[:m].contiguous(), B, imm.PLAN_PERSISTENT)
         assert np.array_equal(part, full[:m]), m
+
+
+# ------------------------------------------------------ against the oracle
+
+ORACLE_CASES = [c for c in CASES if c[0] * c[1] <= 8192 * 8192]
+
+
+@pytest.mark.parametrize("M,N,K,dt,out,bt", ORACLE_CASES,
+                         ids=[f"{c[0]}x{c[1]}x{c[2]}-{c[3]}-{c[4]}" + ("-bt" if c[5] else "")
+                              for c in ORACLE_CASES])
+def test_persistent_integers_bit_exact_vs_oracle(M, N, K, dt, out, bt):
+    """Integer inputs in [-4, 4]: every order is exact, so the persistent pass
+    must equal the exact product rounded once (full rows and columns from the
+    oracle's int64 twin and fp64 loop, 2048 random elements)."""
+    from tests.test_gpu_fullsize_exact import _check_exact
+    g = wl.gen(8400 + M % 89)
+    A, B = wl.integers((M, K), dt, g), wl.integers((K, N), dt, g)
+    Bx = B.float().t().contiguous().to(B.dtype) if bt else B
+    fl = (imm.PLAN_B_TRANSPOSED if bt else 0) | imm.PLAN_PERSISTENT
+    plan = imm.gemm_plan_ex2(M, N, K, dt, out, flags=fl)
+    if plan.info["run_tile"] != imm.TILE["256x256"]:
+        pytest.skip("the plan's single pass uses another tile")
+    C = torch.empty((M, N), dtype=out_torch_dtype(imm.DTYPE[out]), device=dev())
+    imm.gemm_run(plan, A.to(dev()), Bx.to(dev()), C)
+    log(f"persistent {M}x{N}x{K} {dt}->{out} bt={bt}: integers")
+    _check_exact(C, A, B, dt, out, 8400 + M)
+
+
+@pytest.mark.parametrize("M,N,K,dt,out,bt", ORACLE_CASES,
+                         ids=[f"{c[0]}x{c[1]}x{c[2]}-{c[3]}-{c[4]}" + ("-bt" if c[5] else "")
+                              for c in ORACLE_CASES])
+def test_persistent_random_within_bound_vs_oracle(M, N, K, dt, out, bt):
+    """Random inputs (uniform[-1, 1) for 16-bit inputs, N(0, 1) for fp8): 4096
+    sampled elements and one full row within the oracle's error bound."""
+    from tests.helpers import fp8_check_bound
+    A, B = _inputs(M, N, K, dt, 8500 + M % 83)
+    Bx = B.float().t().contiguous().to(B.dtype) if bt else B
+    fl = (imm.PLAN_B_TRANSPOSED if bt else 0) | imm.PLAN_PERSISTENT
+    plan = imm.gemm_plan_ex2(M, N, K, dt, out, flags=fl)
+    if plan.info["run_tile"] != imm.TILE["256x256"]:
+        pytest.skip("the plan's single pass uses another tile")
+    C = torch.empty((M, N), dtype=out_torch_dtype(imm.DTYPE[out]), device=dev())
+    imm.gemm_run(plan, A.to(dev()), Bx.to(dev()), C)
+    torch.cuda.synchronize()
+    Ch = C.cpu().to(torch.float64).numpy()
+    rng = np.random.default_rng(8500 + M)
+    ii = np.concatenate([rng.integers(0, M, 4096), np.full(N, M // 2)])
+    jj = np.concatenate([rng.integers(0, N, 4096), np.arange(N)])
+    a_bits, b_bits = wl.bits(A), wl.bits(B)
+    c64, ca = oracle.gemm_elems(a_bits, b_bits, dt, ii, jj)
+    r = fp8_check_bound(Ch[ii, jj], c64, ca, K, out, dt, a_bits, b_bits, ii, jj)
+    log(f"persistent {M}x{N}x{K} {dt}->{out} bt={bt}: max err/bound {r:.3g}")

@@ -140,8 +140,19 @@ def test_raster_groups_rows_within_an_xcd():
 
 
 def _plan_status(*args):
+    # (M, N, K, in, out, split_k, group_m, tile, scale_a, scale_b) through
+    # gemm_plan_ex2 without flags; with the default tile also through
+    # gemm_plan_ex, which must agree
+    L = imm.lib()
     h = ctypes.c_void_p()
-    return imm.lib().gemm_plan_ex(*args, ctypes.byref(h))
+    st = L.gemm_plan_ex2(*args, 0, ctypes.byref(h))
+    L.gemm_plan_destroy(h)
+    if args[7] == 0:
+        h1 = ctypes.c_void_p()
+        st1 = L.gemm_plan_ex(*args[:7], *args[8:], ctypes.byref(h1))
+        L.gemm_plan_destroy(h1)
+        assert st1 == st, (args, st1, st)
+    return st
 
 
 @pytest.mark.parametrize("args,status", [
@@ -271,6 +282,50 @@ def test_binding_checks_tensor_shapes_and_dtypes():
         imm.gemm_run(p, A, B, C.to(torch.bfloat16))
     with pytest.raises(ValueError):
         imm.gemm_run(p, A.t(), B, C)
+
+
+def test_binding_rejects_host_tensors_before_any_hip_call():
+    # Host tensors of the right shape and dtype: the kernels would read and
+    # write host addresses, so the binding refuses them before calling the
+    # library (on a machine with or without a GPU).
+    import torch
+    p = imm.gemm_plan(4, 8, 16, "f16")
+    A = torch.zeros((4, 16), dtype=torch.float16)
+    B = torch.zeros((16, 8), dtype=torch.float16)
+    C = torch.zeros((4, 8), dtype=torch.float32)
+    for call in (lambda: imm.gemm_run(p, A, B, C),
+                 lambda: imm.gemm_run(p, FAKE, FAKE, C),
+                 lambda: imm.gemm_splitk_run(p, A, B, C, torch.zeros(4 * 8 * 4)),
+                 lambda: imm.gemm_splitk_run(p, FAKE, FAKE, FAKE, torch.zeros(1024)),
+                 lambda: imm.mm(A, B),
+                 lambda: imm.mm(A, B, out_dtype="f16", split_k=0)):
+        with pytest.raises(ValueError, match="CUDA"):
+            call()
+    q = imm.ozaki_plan(4, 8, 16, "bf16")
+    A64, B64, C64 = torch.zeros((4, 16), dtype=torch.float64), torch.zeros(
+        (16, 8), dtype=torch.float64), torch.zeros((4, 8), dtype=torch.float64)
+    ws = torch.zeros(imm.ozaki_workspace_size(q), dtype=torch.uint8)
+    for call in (lambda: imm.ozaki_run(q, A64, B64, C64, FAKE),
+                 lambda: imm.ozaki_run(q, FAKE, FAKE, FAKE, ws),
+                 lambda: imm.ozaki_split(q, 0, A64, FAKE),
+                 lambda: imm.ozaki_multiply(q, FAKE, C64),
+                 lambda: imm.ozaki_mm(A64, B64)):
+        with pytest.raises(ValueError, match="CUDA"):
+            call()
+
+
+def test_output_dtype_of_each_plan():
+    # mm() allocates C in the plan's output dtype: fp32, bf16 or fp16
+    import torch
+    assert imm.out_torch_dtype(imm.DTYPE["f32"]) is torch.float32
+    assert imm.out_torch_dtype(imm.DTYPE["bf16"]) is torch.bfloat16
+    assert imm.out_torch_dtype(imm.DTYPE["f16"]) is torch.float16
+    for od in ("f32", "bf16", "f16"):
+        info = imm.gemm_plan_ex(4, 8, 16, "f16", od).info
+        assert imm.out_torch_dtype(info["out_dtype"]) is {
+            "f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[od]
+    with pytest.raises(ValueError):
+        imm.out_torch_dtype(imm.DTYPE["e5m2"])
 
 
 # ---- Ozaki-scheme fp64 product: host logic ----------------------------------
@@ -455,3 +510,4 @@ def test_tile_by_m_never_makes_a_split_plan_fail():
                                             flags=fl | imm.PLAN_TILE_BY_M).info
                 assert (flagged["split_k"], flagged["k_per_split"]) == (
                     plain["split_k"], plain["k_per_split"]), (K, fl, M)
+
