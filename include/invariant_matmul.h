@@ -275,6 +275,24 @@ gemm_status gemm_splitk_run_bias(gemm_plan_t plan, const void* A, const void* B,
 /* Frees a host plan (NULL is ignored).  Housekeeping: no passage. */
 void gemm_plan_destroy(gemm_plan_t plan);
 
+/* The largest split-K workspace gemm_splitk_run_noalloc serves: 64 MiB (for
+ * example the decode product 128 x 4096 x 14336 bf16 at its default 16 slices
+ * needs 32 MiB; 256 x 4096 x 14336 needs 64 MiB exactly). */
+#define GEMM_NOALLOC_WORKSPACE_BYTES ((size_t)64 << 20)
+
+/* For callers that cannot allocate device memory -- code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc: as
+ * gemm_splitk_run, with the [split_k, M, N] fp32 workspace taken from an array
+ * inside the library instead of from the caller.  The library holds one such
+ * array of GEMM_NOALLOC_WORKSPACE_BYTES on every GPU it runs on, from the
+ * first call on that GPU until the process ends; the call itself allocates
+ * nothing.  C is bitwise what gemm_splitk_run gives for the same plan.
+ * Errors: as gemm_splitk_run; GEMM_ERR_WORKSPACE if gemm_workspace_size(plan)
+ * exceeds GEMM_NOALLOC_WORKSPACE_BYTES (nothing is enqueued).  All calls on
+ * one GPU share its array: calls that overlap on one GPU (other streams or
+ * host threads) race and must be serialised by the caller. */
+gemm_status gemm_splitk_run_noalloc(gemm_plan_t plan, const void* A, const void* B, void* C,
+                                    void* stream);
 
 /* ---------------------------------------------------------------------------
  * fp64 matrix product by the Ozaki scheme: C = A x B with A [M,K], B [K,N]

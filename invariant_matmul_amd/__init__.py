@@ -22,6 +22,7 @@ import os
 __all__ = [
     "GemmError", "Plan", "PlanInfo", "gemm_plan", "gemm_plan_ex", "gemm_plan_ex2",
     "gemm_plan_info", "gemm_workspace_size", "gemm_plan_tile_of", "gemm_run", "gemm_splitk_run",
+    "gemm_splitk_run_noalloc", "NOALLOC_WORKSPACE_BYTES",
     "gemm_plan_destroy", "gemm_status_string", "gemm_last_hip_error", "mm", "out_torch_dtype",
     "lib", "LIB_PATH",
     "DTYPE", "TILE", "STATUS", "EXPORTED_SYMBOLS", "PLAN_B_TRANSPOSED", "PLAN_PERSISTENT",
@@ -40,10 +41,12 @@ TILE = {"default": 0, "256x256": 1, "128x128": 2, "32x128": 3, "256x256_rs": 4, 
 PLAN_B_TRANSPOSED = 1
 PLAN_PERSISTENT = 2
 PLAN_TILE_BY_M = 4
+# GEMM_NOALLOC_WORKSPACE_BYTES: the largest workspace gemm_splitk_run_noalloc serves
+NOALLOC_WORKSPACE_BYTES = 64 << 20
 EXPORTED_SYMBOLS = (
     "gemm_plan", "gemm_plan_ex", "gemm_plan_ex2", "gemm_plan_info", "gemm_workspace_size",
     "gemm_plan_tile_of", "gemm_run", "gemm_run_bias", "gemm_splitk_run", "gemm_splitk_run_bias",
-    "gemm_plan_destroy", "gemm_status_string", "gemm_last_hip_error",
+    "gemm_plan_destroy", "gemm_status_string", "gemm_last_hip_error", "gemm_splitk_run_noalloc",
     "ozaki_plan", "ozaki_plan_info", "ozaki_workspace_size", "ozaki_split", "ozaki_multiply",
     "ozaki_run", "ozaki_plan_destroy",
 )
@@ -123,6 +126,7 @@ def lib() -> ctypes.CDLL:
         L.gemm_run_bias.argtypes = [vp, vp, vp, vp, vp, vp]
         L.gemm_splitk_run.argtypes = [vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
         L.gemm_splitk_run_bias.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+        L.gemm_splitk_run_noalloc.argtypes = [vp, vp, vp, vp, vp]
         L.gemm_plan_destroy.argtypes = [vp]
         L.gemm_plan_destroy.restype = None
         L.gemm_status_string.argtypes = [i32]
@@ -140,7 +144,7 @@ def lib() -> ctypes.CDLL:
         L.ozaki_plan_destroy.restype = None
         for f in ("gemm_plan", "gemm_plan_ex", "gemm_plan_ex2", "gemm_plan_info",
                   "gemm_plan_tile_of", "gemm_run", "gemm_run_bias", "gemm_splitk_run",
-                  "gemm_splitk_run_bias", "gemm_last_hip_error", "ozaki_plan", "ozaki_plan_info",
+                  "gemm_splitk_run_bias", "gemm_splitk_run_noalloc", "gemm_last_hip_error", "ozaki_plan", "ozaki_plan_info",
                   "ozaki_split", "ozaki_multiply", "ozaki_run"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
@@ -303,6 +307,20 @@ def gemm_splitk_run(plan: Plan, A, B, C, workspace, stream=None, workspace_bytes
     _check(lib().gemm_splitk_run_bias(plan.handle, _addr(A), _addr(B), _addr(bias), _addr(C),
                                       _addr(workspace), int(workspace_bytes),
                                       _stream(stream, A, B, C)), "gemm_splitk_run")
+
+
+def gemm_splitk_run_noalloc(plan: Plan, A, B, C, stream=None) -> None:
+    """C = A @ B through the split-K path with the workspace taken from the
+    library's own device array (no allocation by the call); the plan's
+    workspace must fit in NOALLOC_WORKSPACE_BYTES.  Calls that overlap on one
+    GPU share that array and race."""
+    _check_operands(plan, A, B, C)
+    need = gemm_workspace_size(plan)
+    if need > NOALLOC_WORKSPACE_BYTES:
+        raise GemmError(3, f"gemm_splitk_run_noalloc: the plan needs a workspace of {need} "
+                           f"bytes, more than the library's {NOALLOC_WORKSPACE_BYTES}")
+    _check(lib().gemm_splitk_run_noalloc(plan.handle, _addr(A), _addr(B), _addr(C),
+                                         _stream(stream, A, B, C)), "gemm_splitk_run_noalloc")
 
 
 def gemm_plan_destroy(plan: Plan) -> None:

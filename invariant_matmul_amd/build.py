@@ -18,7 +18,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libinvariant_matmul.so")
 BUILD_DIR = os.path.join(HERE, "_build")
 
-SOURCES = ["api.cpp", "gemm_kernels.hip", "gemm_dma.hip", "ozaki.hip"]
+SOURCES = ["api.cpp", "gemm_kernels.hip", "gemm_dma.hip", "ozaki.hip", "noalloc.hip"]
 ARCH = "gfx950"
 
 # Packed fp32 VALU instructions are kept out of all device code.

@@ -511,3 +511,22 @@ def test_tile_by_m_never_makes_a_split_plan_fail():
                 assert (flagged["split_k"], flagged["k_per_split"]) == (
                     plain["split_k"], plain["k_per_split"]), (K, fl, M)
 
+
+def test_noalloc_entry_point_host_checks():
+    # gemm_splitk_run_noalloc: argument checks, then the workspace limit, both
+    # before any HIP call; a valid call without a GPU returns GEMM_ERR_HIP.
+    L = imm.lib()
+    small = imm.gemm_plan(8, 4096, 14336, "bf16")          # 16 slices: 2 MiB
+    assert imm.gemm_workspace_size(small) <= imm.NOALLOC_WORKSPACE_BYTES
+    big = imm.gemm_plan(512, 4096, 14336, "bf16")          # 128 MiB
+    assert imm.gemm_workspace_size(big) > imm.NOALLOC_WORKSPACE_BYTES
+    assert L.gemm_splitk_run_noalloc(None, FAKE, FAKE, FAKE, None) == 1
+    assert L.gemm_splitk_run_noalloc(small.handle, 0, FAKE, FAKE, None) == 1
+    assert L.gemm_splitk_run_noalloc(small.handle, FAKE, FAKE, FAKE + 4, None) == 1
+    assert L.gemm_splitk_run_noalloc(big.handle, FAKE, FAKE, FAKE, None) == 3
+    assert L.gemm_splitk_run_noalloc(imm.gemm_plan(0, 64, 64, "f16").handle, 0, 0, 0, None) == 0
+    if not _have_gpu():
+        assert L.gemm_splitk_run_noalloc(small.handle, FAKE, FAKE, FAKE, None) == 4
+    with pytest.raises(imm.GemmError) as e:
+        imm.gemm_splitk_run_noalloc(big, FAKE, FAKE, FAKE)
+    assert e.value.status == 3 and str(imm.NOALLOC_WORKSPACE_BYTES) in str(e.value)
