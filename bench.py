@@ -390,29 +390,68 @@ def summary(per):
             "p90_ms": s[min(len(s) - 1, int(0.9 * len(s)))], "n": len(s)}
 
 
-def cpu_baseline(w, A, B, target_s=15.0):
-    """Time the oracle on the first rows of the product (about target_s seconds)."""
+def oracle_sample(w, A, B, threads, target_s, gpu_ms=None, rows=None):
+    """Time the CPU oracle on the first rows of one workload's product.
+
+    One probe call on `threads` rows gives the time per row; then one call on
+    about target_s seconds' worth of rows (all of them if that fits) is timed.
+    decode_B_s is the oracle's decoder run alone on B (the oracle decodes B
+    once per call, on one thread, before its row loop); accumulate_s is the
+    rest of the call.  full_product_s_est extrapolates to all M rows."""
     import oracle
     import workloads as wl
     a_bits, b_bits = wl.bits(A), wl.bits(B)
-    threads = oracle.max_threads()
+    M, N, K = a_bits.shape[0], b_bits.shape[1], a_bits.shape[1]
 
-    def timed(rows):
+    def call(r):
         t = time.perf_counter()
-        oracle.gemm(a_bits, b_bits, w.dtype, rows=list(range(rows)))
+        oracle.gemm(a_bits, b_bits, w.dtype, rows=list(range(r)), nthreads=threads)
         return time.perf_counter() - t
 
-    r1, r2 = threads, 4 * threads
-    t1, t2 = timed(r1), timed(r2)
-    per_row = max((t2 - t1) / (r2 - r1), 1e-6)
-    fixed = max(t1 - r1 * per_row, 0.0)  # decoding B, once per call
-    rows = int(min(w.M, max(r2, (target_s - fixed) / per_row)))
-    rows -= rows % threads if rows > threads else 0
-    dt = timed(rows)
-    flops = 2.0 * rows * w.N * w.K
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"rows 0..{rows - 1} of the {w.M}x{w.N}x{w.K} {w.dtype} product, one "
-                      f"call including the decode of B, {dt:.1f} s wall"}
+    t = time.perf_counter()
+    oracle.decode(w.dtype, b_bits)
+    dec = time.perf_counter() - t
+    if rows is None:
+        r1 = min(M, threads)
+        if dec >= target_s / 2:
+            rows = r1  # decoding B alone takes most of the budget: one row per thread
+        else:
+            per_row = max((call(r1) - dec) / r1, 1e-9)
+            rows = int(min(M, max(r1, (target_s - dec) / per_row)))
+            if threads < rows < M:
+                rows -= rows % threads
+    total = call(rows)
+    acc = max(total - dec, 0.0)
+    out = {"workload": w.name, "shape": f"{M}x{N}x{K} {w.dtype}", "rows": rows, "of_rows": M,
+           "threads": threads, "total_s": total, "decode_B_s": dec, "accumulate_s": acc,
+           "GFLOPs": 2.0 * rows * N * K / total / 1e9,
+           "full_product_s_est": dec + acc * M / rows}
+    if gpu_ms:
+        out["gpu_ms"] = gpu_ms
+        out["gpu_speedup_est"] = out["full_product_s_est"] / (gpu_ms * 1e-3)
+    return out
+
+
+def cpu_baseline(samples):
+    """The oracle (test infrastructure: fp64 triple loop, OpenMP over rows) on
+    the host cores, one bounded sample per workload.  samples: list of
+    (workload, A, B, gpu_ms, target_s).  The headline value is the oracle's
+    rate on the square fp16 8192^3 sample; per_config holds every workload,
+    plus the 256^3 exact product on one core."""
+    import oracle
+    threads = oracle.max_threads()
+    per = []
+    for w, A, B, gpu_ms, target in samples:
+        per.append(oracle_sample(w, A, B, threads, target, gpu_ms))
+        if w.name == "exact256":
+            per.append(oracle_sample(w, A, B, 1, target, gpu_ms, rows=w.M))
+    head = next(x for x in per if x["workload"] == "square_f16_8192")
+    return {"value": head["GFLOPs"] / 1e3, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"rows 0..{head['rows'] - 1} of the 8192x8192x8192 f16 product, one call "
+                      f"({head['total_s']:.1f} s wall, of which {head['decode_B_s']:.1f} s decoding "
+                      f"B); per_config samples every workload the same way, full where it fits "
+                      f"in its budget, and the 256^3 product also on one core",
+            "per_config": per}
 
 
 def bench_square(name, steps, warmup, torch, imm, wl):
@@ -495,13 +534,60 @@ def bench_splitk(name, split, torch, imm, wl, n=30, warmup=5, M=None):
     return out
 
 
+def _probe_lib():
+    """The streaming-read probe library (built next to the GEMM library)."""
+    import ctypes
+
+    from invariant_matmul_amd import build as _b
+    if not os.path.exists(_b.PROBE_LIB):
+        raise RuntimeError(f"{_b.PROBE_LIB} is not built")
+    L = ctypes.CDLL(_b.PROBE_LIB)
+    L.imm_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int,
+                                 ctypes.c_int, ctypes.c_void_p]
+    L.imm_probe_read.restype = ctypes.c_int
+    return L
+
+
+def bench_read_probe(torch, nbytes, copies, n=20, warmup=5):
+    """Streaming read of nbytes (rotated over `copies` buffers so that with
+    copies * nbytes well above the 256 MB last-level cache every read comes
+    from HBM), best median over grid sizes and load kinds."""
+    L = _probe_lib()
+    bufs = [torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+            for _ in range(copies)]
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    best = None
+
+    def launch(i, wgs, nt):
+        rc = L.imm_probe_read(bufs[i % copies].data_ptr(), nbytes, sink.data_ptr(), wgs, nt, stream)
+        if rc != 0:
+            raise RuntimeError(f"imm_probe_read failed: {rc}")
+
+    for wgs in (1024, 2048, 4096, 8192):
+        for nt in (0, 1):
+            per, _ = time_launches(lambda i: launch(i, wgs, nt), n, warmup, torch)
+            med = statistics.median(per)
+            if best is None or med < best["median_ms"]:
+                best = {"median_ms": med, "workgroups": wgs, "nontemporal": bool(nt)}
+    del bufs
+    torch.cuda.empty_cache()
+    best.update({"bytes": nbytes, "copies_rotated": copies,
+                 "GBps": nbytes / (best["median_ms"] * 1e-3) / 1e9})
+    best["pct_hbm_peak"] = 100.0 * best["GBps"] / PEAK_HBM_GBS
+    return best
+
+
 def bench_hbm_probes(torch, nbytes=2 ** 30):
-    """An achievable HBM rate on this part, from the runtime's device copy of
-    1 GiB (read + write bytes over time; a comparator only)."""
+    """Achievable HBM rates on this part: a 1 GiB streaming read, a read of the
+    decode product's B (14336 x 4096 bf16) rotated over 5 copies, and the
+    runtime's 1 GiB device copy (read + write bytes over time)."""
+    out = {"read_1GiB": bench_read_probe(torch, nbytes, 1),
+           "read_decode_B": bench_read_probe(torch, 14336 * 4096 * 2, 5)}
     x = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
     y = torch.empty_like(x)
     tc, _ = time_launches(lambda i: y.copy_(x), 20, 5, torch)
-    out = {"bytes": nbytes, "copy_GBps": 2 * nbytes / (statistics.median(tc) * 1e-3) / 1e9}
+    out["copy_1GiB_GBps"] = 2 * nbytes / (statistics.median(tc) * 1e-3) / 1e9
     del x, y
     torch.cuda.empty_cache()
     return out
@@ -736,18 +822,25 @@ def main():
                      "source": os.path.relpath(CLOCK_FILE, ROOT)}
     roofline = {"bound": "mfma", "achieved": achieved, "peak": PEAK_TFLOPS["f16"],
                 "unit": "TFLOP/s", "frac": achieved / PEAK_TFLOPS["f16"], "traffic": traffic,
+                "frac_at_clock": clock["frac_at_clock"] if clock else None,
+                "clock_ghz_timed": clock["clock_ghz_timed"] if clock else None,
                 "kernel": "gemm_dma_kernel<f16, f32 out, 256x256 tile>",
                 "algorithmic_flop_per_launch": w.flops, "avg_launch_ms": kavg}
 
     extra = {"headline_kernel": summary(per), "headline_clock": clock,
              "plan": {k: plan.info[k] for k in ("run_block_m", "run_block_n", "block_k", "run_waves",
                                                   "group_m", "split_k", "mfma_k")}}
+    secondary = {}
+    # (workload, host A, host B, GPU median ms, seconds of oracle time) for the CPU baseline
+    samples = []
+    A, B = host[0], host[1]
     if not args.no_extra:
-        A, B, Ad, Bd = host
+        Ad, Bd = host[2], host[3]
         try:
             ref = torch.empty((w.M, w.N), dtype=torch.float16, device="cuda")
             tper, _ = time_launches(lambda i: torch.matmul(Ad, Bd, out=ref), 20, 5, torch)
             extra["torch_matmul_f16_8192_TFLOPs"] = w.flops / (statistics.median(tper) * 1e-3) / 1e12
+            del ref
         except Exception as e:  # comparator only
             extra["torch_matmul_error"] = str(e)
         # The same product with A and B rotated over two copies (537 MB, twice
@@ -761,21 +854,42 @@ def main():
             **summary(rper), "copies": 2,
             "TFLOPs": w.flops / (statistics.median(rper) * 1e-3) / 1e12,
             "pct_mfma_peak": 100.0 * w.flops / (statistics.median(rper) * 1e-3) / 1e12 / PEAK_TFLOPS["f16"]}
-        del Ad, Bd, As, Bs, Cr
+        secondary["fp16_8192_rotated_inputs_TFLOPs"] = round(extra["headline_rotated_inputs"]["TFLOPs"], 1)
+        del Ad, Bd, As, Bs, Cr, host
         torch.cuda.empty_cache()
-        log("fp8 e5m2 8192^3")
-        w8, plan8, per8, _, h8 = bench_square("square_e5m2_8192", 30, 5, torch, imm, wl)
-        med8 = statistics.median(per8)
-        extra["square_e5m2_8192"] = {**summary(per8),
-                                     "TFLOPs": w8.flops / (med8 * 1e-3) / 1e12,
-                                     "pct_mfma_peak": 100 * w8.flops / (med8 * 1e-3) / 1e12 /
-                                     PEAK_TFLOPS["e5m2"]}
-        try:
-            extra["square_e5m2_8192"]["vs_hipblaslt"] = fp8_comparator(w8, plan8, h8, torch, imm)
-        except Exception as e:  # comparator only
-            extra["square_e5m2_8192"]["hipblaslt_error"] = str(e)
-        del h8
-        torch.cuda.empty_cache()
+        samples.append((w, A, B, statistics.median(per), 6.0))
+
+        log("exact 256^3 fp16 (integers)")
+        we = wl.WORKLOADS["exact256"]
+        Ae, Be = we.make()
+        pe = imm.gemm_plan(we.M, we.N, we.K, we.dtype)
+        Ce = torch.empty((we.M, we.N), dtype=torch.float32, device="cuda")
+        Aed, Bed = Ae.cuda(), Be.cuda()
+        pere, _ = time_launches(lambda i: imm.gemm_run(pe, Aed, Bed, Ce), 30, 5, torch)
+        samples.append((we, Ae, Be, statistics.median(pere), 1.0))
+        del Aed, Bed, Ce
+
+        secondary["fp8_e5m2_bf16_out"] = {}
+        for n8, steps8 in ((4096, 30), (8192, 30), (16384, 10)):
+            log(f"fp8 e5m2 {n8}^3")
+            w8, plan8, per8, _, h8 = bench_square(f"square_e5m2_{n8}", steps8, 5, torch, imm, wl)
+            med8 = statistics.median(per8)
+            e8 = {**summary(per8), "TFLOPs": w8.flops / (med8 * 1e-3) / 1e12,
+                  "pct_mfma_peak": 100 * w8.flops / (med8 * 1e-3) / 1e12 / PEAK_TFLOPS["e5m2"]}
+            sec8 = {"TFLOPs": round(e8["TFLOPs"], 1), "pct_peak": round(e8["pct_mfma_peak"], 2),
+                    "median_us": round(med8 * 1e3, 1)}
+            if n8 == 8192:
+                try:
+                    e8["vs_hipblaslt"] = fp8_comparator(w8, plan8, h8, torch, imm)
+                    sec8["hipblaslt_TFLOPs"] = round(e8["vs_hipblaslt"]["hipblaslt"]["TFLOPs"], 1)
+                    sec8["ours_alternating_TFLOPs"] = round(e8["vs_hipblaslt"]["ours"]["TFLOPs"], 1)
+                except Exception as e:  # comparator only
+                    e8["hipblaslt_error"] = str(e)
+            extra[f"square_e5m2_{n8}"] = e8
+            secondary["fp8_e5m2_bf16_out"][str(n8)] = sec8
+            samples.append((w8, h8[0], h8[1], med8, {4096: 2.0, 8192: 2.0, 16384: 2.0}[n8]))
+            del h8
+            torch.cuda.empty_cache()
         for n in ("square_f16_4096", "square_f16_1024"):
             # the default plan and GEMM_PLAN_TILE_BY_M in alternating rounds, so
             # that the part's clock (which follows its recent power draw) treats
@@ -797,37 +911,63 @@ def main():
                         "tile_by_m": f"{mp.info['run_block_m']}x{mp.info['run_block_n']}",
                         "tile_by_m_TFLOPs": wn.flops / (min(rounds["tile_by_m"]) * 1e-3) / 1e12,
                         "round_medians_ms": {k: [round(x, 4) for x in v] for k, v in rounds.items()}}
+            secondary[f"fp16_{wn.M}_TFLOPs"] = round(extra[n]["TFLOPs"], 1)
+            samples.append((wn, hn[0], hn[1], medn, {4096: 2.0, 1024: 1.0}[wn.M]))
             del hn, Cn
             torch.cuda.empty_cache()
-        log("decode bf16 N=4096 K=14336, split-K path")
-        extra["decode_bf16"] = [bench_splitk("decode_bf16_m128", 0, torch, imm, wl, M=m)
-                                for m in (1, 8, 32, 128)]
-        log("HBM probe (1 GiB device copy)")
+        log("HBM probes (streaming reads, 1 GiB device copy)")
         probes = bench_hbm_probes(torch)
         extra["hbm_probes"] = probes
+        secondary["hbm_read_probe_GBps"] = {"1GiB": round(probes["read_1GiB"]["GBps"]),
+                                            "decode_B_rotated": round(probes["read_decode_B"]["GBps"])}
+        log("decode bf16 N=4096 K=14336, split-K path")
+        wd = wl.WORKLOADS["decode_bf16_m128"]
+        Adec, Bdec = wd.make()
+        extra["decode_bf16"] = [bench_splitk("decode_bf16_m128", 0, torch, imm, wl, M=m)
+                                for m in (1, 8, 32, 128)]
+        secondary["decode_bf16_N4096_K14336"] = []
         for d in extra["decode_bf16"]:
-            d["pct_of_copy_probe"] = 100.0 * d["GBps"] / probes["copy_GBps"]
+            d["pct_of_read_probe"] = 100.0 * d["GBps"] / probes["read_decode_B"]["GBps"]
+            d["pct_of_copy_probe"] = 100.0 * d["GBps"] / probes["copy_1GiB_GBps"]
+            secondary["decode_bf16_N4096_K14336"].append(
+                {"M": d["M"], "split": d["split_k"], "us": round(d["median_ms"] * 1e3, 2),
+                 "GBps": round(d["GBps"]), "pct_hbm_peak": round(d["pct_hbm_peak"], 1),
+                 "pct_read_probe": round(d["pct_of_read_probe"], 1)})
+            wm = wl.WORKLOADS[f"decode_bf16_m{d['M']}"]
+            samples.append((wm, Adec[:d["M"]].contiguous(), Bdec, d["median_ms"], 2.0))
         torch.cuda.empty_cache()
         log("M sweep on the fused-QKV projection shape N=6144 K=4096, gemm_run")
         extra["qkv_m_sweep_f16"] = bench_m_sweep(torch, imm, wl)
+        secondary["qkv_f16_N6144_K4096_us"] = [
+            {"M": x["M"], "default": round(x["median_us"], 1),
+             "tile_by_m": round(x["tile_by_m_median_us"], 1),
+             "torch": round(x["torch_matmul_median_us"], 1)} for x in extra["qkv_m_sweep_f16"]]
         torch.cuda.empty_cache()
         log("huge-K fp16 256x256x131072, split-K path")
         # split 0 = the plan's default for this shape
         extra["hugek_f16"] = [bench_splitk("hugek_f16", s, torch, imm, wl) for s in (1, 8, 32, 128, 0)]
+        secondary["hugek_f16_256x256x131072"] = [
+            {"split": x["split_k"], "default": i == 4, "us": round(x["median_ms"] * 1e3, 1),
+             "GBps": round(x["GBps"]), "pct_hbm_peak": round(x["pct_hbm_peak"], 1)}
+            for i, x in enumerate(extra["hugek_f16"])]
+        wh = wl.WORKLOADS["hugek_f16"]
+        Ah, Bh = wh.make()
+        samples.append((wh, Ah, Bh, extra["hugek_f16"][-1]["median_ms"], 2.0))
         torch.cuda.empty_cache()
         log("fp64 by the Ozaki scheme (bf16, e4m3 and int8 slices)")
         extra["ozaki_f64"] = [bench_ozaki(f"ozaki_{t2}_{n}", torch, imm, wl)
                               for t2 in ("bf16", "e4m3", "i8") for n in (4096, 8192, 16384)]
+        secondary["ozaki_f64_TFLOPs"] = {f"{x['type2']}_{x['n']}": round(x["fp64_TFLOPs"], 1)
+                                         for x in extra["ozaki_f64"]}
         log("Ozaki Fast Mode d sweep at 8192")
         extra["ozaki_d_sweep"] = bench_ozaki_d_sweep(torch, imm, wl)
-        A, B = host[0], host[1]
     else:
-        A, B = host[0], host[1]
+        samples.append((w, A, B, statistics.median(per), 6.0))
 
     cpu = None
     if not args.no_cpu:
         log("cpu baseline (oracle)")
-        cpu = cpu_baseline(w, A, B)
+        cpu = cpu_baseline(samples)
 
     line = {
         "metric": "GEMM TFLOPS & % MFMA peak (8192^3 fp16, fp8); GB/s at M<=32; batch-invariance",
@@ -837,7 +977,8 @@ def main():
         "data": "synthetic (seeded uniform[-1,1) fp16, resident in HBM)",
         "config": {"workload": "square fp16 GEMM M=N=K=8192, fp32 accumulate, fp32 output, "
                                "gemm_run (no split-K)",
-                   "M": w.M, "N": w.N, "K": w.K, "pct_mfma_peak": 100 * value / PEAK_TFLOPS["f16"]},
+                   "M": w.M, "N": w.N, "K": w.K, "pct_mfma_peak": 100 * value / PEAK_TFLOPS["f16"],
+                   "secondary": secondary},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "extra": extra,

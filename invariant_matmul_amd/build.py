@@ -19,6 +19,9 @@ LIB = os.path.join(HERE, "libinvariant_matmul.so")
 BUILD_DIR = os.path.join(HERE, "_build")
 
 SOURCES = ["api.cpp", "gemm_kernels.hip", "gemm_dma.hip", "ozaki.hip", "noalloc.hip"]
+# The benchmark's HBM read probe: a library of its own, never linked into the GEMM library.
+PROBE_SOURCES = ["hbm_probe.hip"]
+PROBE_LIB = os.path.join(HERE, "libimm_hbm_probe.so")
 ARCH = "gfx950"
 
 # Packed fp32 VALU instructions are kept out of all device code.
@@ -47,12 +50,8 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source and link the shared library; returns its path."""
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = LIB + ".tmp%d" % os.getpid()
+def _link(objs, out: str, verbose: bool) -> None:
+    tmp = out + ".tmp%d" % os.getpid()
     cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -60,7 +59,18 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
     _check_loads(tmp)
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source and link the shared library (and the benchmark's
+    probe library); returns the GEMM library's path."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    srcs = SOURCES + PROBE_SOURCES
+    with concurrent.futures.ThreadPoolExecutor(max_workers=len(srcs)) as ex:
+        objs = dict(zip(srcs, ex.map(lambda s: _compile(s, verbose), srcs)))
+    _link([objs[s] for s in SOURCES], LIB, verbose)
+    _link([objs[s] for s in PROBE_SOURCES], PROBE_LIB, verbose)
     return LIB
 
 

@@ -182,3 +182,22 @@ def test_stream_traffic_rejects_a_missing_launch(tmp_path):
     write_counters(write, _stream_dispatches("WRITE_SIZE", copy_kib, lambda c, k: 1.0))
     with pytest.raises(SystemExit):
         bench.write_stream_traffic(str(fetch), str(write), out_path=str(tmp_path / "x.json"))
+
+
+def test_cpu_baseline_samples_every_workload():
+    import workloads as wl
+    small = wl.Workload("square_f16_8192", 96, 64, 128, "f16", "f32", 2002, "uniform", "run")
+    exact = wl.WORKLOADS["exact256"]
+    samples = [(small, *small.make(), 0.5, 0.2), (exact, *exact.make(), 0.01, 0.2)]
+    cpu = bench.cpu_baseline(samples)
+    assert cpu["kind"] == "oracle" and cpu["unit"] == "TFLOP/s" and cpu["cores"] >= 1
+    names = [x["workload"] for x in cpu["per_config"]]
+    assert names == ["square_f16_8192", "exact256", "exact256"]
+    one_core = cpu["per_config"][2]
+    assert one_core["threads"] == 1 and one_core["rows"] == 256 == one_core["of_rows"]
+    for x in cpu["per_config"]:
+        assert x["total_s"] > 0 and x["decode_B_s"] >= 0 and x["accumulate_s"] >= 0
+        assert 1 <= x["rows"] <= x["of_rows"]
+        assert x["full_product_s_est"] >= x["total_s"] - x["decode_B_s"] - 1e-9
+        assert x["gpu_speedup_est"] > 0
+    assert cpu["value"] == cpu["per_config"][0]["GFLOPs"] / 1e3
