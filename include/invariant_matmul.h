@@ -134,7 +134,11 @@ typedef enum {
   GEMM_TILE_32x256 = 5,     /* 4 waves, DMA ring; narrow tile for skinny or
                                reduction-dominated shapes */
   GEMM_TILE_64x256 = 6,     /* 4 waves, DMA ring */
-  GEMM_TILE_128x256 = 7     /* 8 waves, DMA ring of 3 stages */
+  GEMM_TILE_128x256 = 7,    /* 8 waves, DMA ring of 3 stages */
+  GEMM_TILE_32x64 = 8,      /* 2 waves, DMA ring of 10 stages; fp16 / bf16 only:
+                               narrow tile for small M (4x the workgroups of
+                               32x256) */
+  GEMM_TILE_64x64 = 9       /* 2 waves, DMA ring of 8 stages; fp16 / bf16 only */
 } gemm_tile;
 
 /* Plan flags (gemm_plan_ex2). */

@@ -44,6 +44,8 @@ void tile_shape(int tile, int* bm, int* bn, int* wm, int* wn) {
     case GEMM_TILE_32x256: *bm = 32; *bn = 256; *wm = 1; *wn = 4; break;
     case GEMM_TILE_64x256: *bm = 64; *bn = 256; *wm = 1; *wn = 4; break;
     case GEMM_TILE_128x256: *bm = 128; *bn = 256; *wm = 2; *wn = 4; break;
+    case GEMM_TILE_32x64: *bm = 32; *bn = 64; *wm = 2; *wn = 1; break;
+    case GEMM_TILE_64x64: *bm = 64; *bn = 64; *wm = 2; *wn = 1; break;
     default: *bm = 32; *bn = 128; *wm = 1; *wn = 4; break;  // GEMM_TILE_32x128
   }
 }
@@ -63,6 +65,10 @@ bool reduction_dominated(int64_t N, int64_t K) { return K >= 2 * N; }
 bool small_b(int64_t N, int64_t K, int eb) { return N * K * eb <= ((int64_t)4 << 20); }
 
 bool dma_offsets_fit(int tile, int64_t N, int64_t K, int eb, bool b_trans);
+
+// The 64-column DMA tiles take 16-bit inputs only (an fp8 matrix step covers
+// 32 rows, more than their waves' row blocks).
+bool is_narrow_tile(int tile) { return tile == GEMM_TILE_32x64 || tile == GEMM_TILE_64x64; }
 
 // Tile of the split-K path.  Past the K where a 128-row tile's 32-bit A
 // offsets overflow, narrow shapes keep a DMA tile of 64 rows (the split,
@@ -87,29 +93,36 @@ int default_run_tile(int64_t N, int64_t K, int eb) {
 
 // GEMM_PLAN_TILE_BY_M: the DMA tile with the least estimated time.  Each
 // of these tiles takes a whole compute unit (its LDS ring), so a grid runs in
-// rounds of 256 workgroups (a 256-CU MI355X), and one round of a tile of r
-// rows takes about 127 + r units: measured at K = 4096, one round of the 32-,
-// 64-, 128- and 256-row tiles takes 37, 45, 55 and 85 us.  Cost =
-// rounds x (127 + r); the smaller tile wins a tie.  On the fused-QKV shape
-// N = 6144, K = 4096 (M = 256 ... 4096) and on squares from 1024 to 4096 this
-// picks the fastest DMA tile at every point measured.  Bits do not depend on
-// the tile.
-int tile_by_m(int64_t M, int64_t N) {
-  static const int kTiles[4] = {GEMM_TILE_32x256, GEMM_TILE_64x256, GEMM_TILE_128x256,
-                                GEMM_TILE_256x256};
-  static const int kRows[4] = {32, 64, 128, 256};
-  const int64_t tn = (N + 255) / 256;
-  int best = 0;
+// rounds of 256 workgroups (a 256-CU MI355X), and one round of a tile takes
+// about the same time whatever the shape: it is a workgroup's walk through
+// K.  Units per round, fitted on a sweep at K = 4096 (M = 1 ... 2048; N = 1024,
+// 4096, 6144, 14336; both B layouts), where one round took about 27, 29, 32,
+// 40, 47 and 71 us: 32 x 64: 134, 64 x 64: 144, 32 x 256: 159, 64 x 256: 191,
+// 128 x 256: 255, 256 x 256: 383.  Cost = rounds x units; the smaller tile wins
+// a tie.  On that sweep this picks the fastest tile, or one within 3 % of it,
+// at every point.  The 64-column tiles take 16-bit inputs only.  Bits do not
+// depend on the tile.
+int tile_by_m(int64_t M, int64_t N, int eb) {
+  struct Cand {
+    int tile, rows, cols, units;
+  };
+  static const Cand kCands[6] = {{GEMM_TILE_32x64, 32, 64, 134},   {GEMM_TILE_64x64, 64, 64, 144},
+                                 {GEMM_TILE_32x256, 32, 256, 159}, {GEMM_TILE_64x256, 64, 256, 191},
+                                 {GEMM_TILE_128x256, 128, 256, 255},
+                                 {GEMM_TILE_256x256, 256, 256, 383}};
+  int best = -1;
   int64_t best_cost = -1;
-  for (int i = 0; i < 4; ++i) {
-    const int64_t wgs = ((M + kRows[i] - 1) / kRows[i]) * tn;
-    const int64_t cost = ((wgs + 255) / 256) * (127 + kRows[i]);
+  for (int i = 0; i < 6; ++i) {
+    if (is_narrow_tile(kCands[i].tile) && eb != 2) continue;
+    const int64_t wgs = ((M + kCands[i].rows - 1) / kCands[i].rows) *
+                        ((N + kCands[i].cols - 1) / kCands[i].cols);
+    const int64_t cost = ((wgs + 255) / 256) * kCands[i].units;
     if (best_cost < 0 || cost < best_cost) {
       best = i;
       best_cost = cost;
     }
   }
-  return kTiles[best];
+  return kCands[best].tile;
 }
 
 // GEMM_PLAN_TILE_BY_M on the split-K path of wide reduction-dominated shapes
@@ -131,8 +144,9 @@ int split_tile_by_m(int64_t M, int narrow) {
 
 bool is_dma_tile(int tile) {
   return tile == GEMM_TILE_256x256 || tile == GEMM_TILE_128x256 || tile == GEMM_TILE_32x256 ||
-         tile == GEMM_TILE_64x256;
+         tile == GEMM_TILE_64x256 || tile == GEMM_TILE_32x64 || tile == GEMM_TILE_64x64;
 }
+
 
 // The DMA kernels address one A tile (bm rows of K) and one B stage (128
 // bytes of K: 128 / eb rows of N elements, or with B transposed bn rows of
@@ -151,7 +165,8 @@ int checked_tile(int tile, int64_t N, int64_t K, int eb, bool b_trans) {
   if (dma_offsets_fit(tile, N, K, eb, b_trans)) return tile;
   if (b_trans) return -1;
   if (tile == GEMM_TILE_256x256) return GEMM_TILE_256x256_RS;
-  return tile == GEMM_TILE_128x256 ? GEMM_TILE_128x128 : GEMM_TILE_32x128;
+  return (tile == GEMM_TILE_128x256 || tile == GEMM_TILE_64x64) ? GEMM_TILE_128x128
+                                                                 : GEMM_TILE_32x128;
 }
 
 // Workgroups the default split aims for per row of output tiles.  Wide
@@ -383,7 +398,8 @@ gemm_status gemm_plan_ex2(int64_t M, int64_t N, int64_t K, gemm_dtype in, gemm_d
   if (M > INT_MAX || N > INT_MAX || K > INT_MAX) return GEMM_ERR_UNSUPPORTED;
   if (!valid_in(in) || !valid_out(out)) return GEMM_ERR_UNSUPPORTED;
   if (split_k < 0 || split_k > kMaxSplit || group_m < 0) return GEMM_ERR_UNSUPPORTED;
-  if (tile < GEMM_TILE_DEFAULT || tile > GEMM_TILE_128x256) return GEMM_ERR_UNSUPPORTED;
+  if (tile < GEMM_TILE_DEFAULT || tile > GEMM_TILE_64x64) return GEMM_ERR_UNSUPPORTED;
+  if (is_narrow_tile(tile) && elem_bytes(in) != 2) return GEMM_ERR_UNSUPPORTED;
   if (!std::isfinite(scale_a) || !std::isfinite(scale_b)) return GEMM_ERR_UNSUPPORTED;
   if (flags & ~(unsigned)(GEMM_PLAN_B_TRANSPOSED | GEMM_PLAN_PERSISTENT | GEMM_PLAN_TILE_BY_M))
     return GEMM_ERR_UNSUPPORTED;
@@ -417,7 +433,7 @@ gemm_status gemm_plan_ex2(int64_t M, int64_t N, int64_t K, gemm_dtype in, gemm_d
   p->tile = checked_tile(split_tile, N, K, eb, bt);
   int run_tile = tile;
   if (tile == GEMM_TILE_DEFAULT)
-    run_tile = (flags & GEMM_PLAN_TILE_BY_M) ? tile_by_m(M, N) : default_run_tile(N, K, eb);
+    run_tile = (flags & GEMM_PLAN_TILE_BY_M) ? tile_by_m(M, N, eb) : default_run_tile(N, K, eb);
   p->run_tile = checked_tile(run_tile, N, K, eb, bt);
   if (p->tile < 0 || p->run_tile < 0) {
     delete p;

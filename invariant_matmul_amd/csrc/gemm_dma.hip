@@ -51,7 +51,7 @@ namespace imm {
 namespace {
 using namespace dev;
 
-constexpr int TBN = 256;  // tile columns (every configuration)
+constexpr int WIDE_TBN = 256;  // tile columns of the wide tiles, the persistent and Ozaki modes
 
 // What a workgroup does with its tile.
 //   MODE_STORE: the product, scaled, converted, stored to C.
@@ -149,15 +149,20 @@ __device__ __forceinline__ i32x2 tr8_rows(unsigned p0, int rows) {
   }
 }
 
-// TBM x 256 tile of C per workgroup of WM x 4 waves; NS stages in the ring.
-//   TBM = 256, WM = 2, NS = 2: the large tile (wave tile 128 x 64);
-//   TBM = 128, WM = 2, NS = 3: the half-height tile (wave tile 64 x 64) for
+// TBM x TBN tile of C per workgroup of WM x (TBN / 64) waves; NS stages in
+// the ring.
+//   256 x 256, WM = 2, NS = 2: the large tile (wave tile 128 x 64);
+//   128 x 256, WM = 2, NS = 3: the half-height tile (wave tile 64 x 64) for
 //     grids that 256 x 256 tiles would leave under-filled;
-//   TBM = 64 / 32, WM = 1, NS = 4: narrow tiles for reduction-dominated
-//   shapes (wave tile 64 x 64 / 32 x 64), where the time is the stream of B.
+//   64 x 256 / 32 x 256, WM = 1, NS = 4: short tiles for reduction-dominated
+//     shapes (wave tile 64 x 64 / 32 x 64), where the time is the stream of B;
+//   64 x 64 / 32 x 64, WM = 2, NS = 8 / 10: narrow tiles (16-bit inputs) for
+//     small M, where N / 256 column tiles would leave most compute units
+//     idle: four times the workgroups, each with a deep ring (about 120 KB in
+//     flight) to keep its share of B streaming.
 // Two workgroups share a CU when their rings fit in half the LDS; the
 // register budget then has to allow two waves per SIMD.
-template <int TBM, int WM, int NS>
+template <int TBM, int TBN, int WM, int NS>
 constexpr int waves_per_simd() {
   return NS * (TBM + TBN) * SKB <= 80 * 1024 || WM == 2 ? 2 : 1;
 }
@@ -167,11 +172,12 @@ constexpr int waves_per_simd() {
 // staged and read exactly like A (128-byte rows, ds_read_b128); the matrix
 // core sees the same values in the same K order, so the bits are those of
 // the [K, N] layout.
-template <int IN, int OUT, int MODE, int TBM, int WM, int NS, bool BT, class ARGS>
-__global__ __launch_bounds__(256 * WM, (waves_per_simd<TBM, WM, NS>())) void gemm_dma_kernel(ARGS g) {
+template <int IN, int OUT, int MODE, int TBM, int TBN, int WM, int NS, bool BT, class ARGS>
+__global__ __launch_bounds__(WM * TBN, (waves_per_simd<TBM, TBN, WM, NS>())) void gemm_dma_kernel(ARGS g) {
   using T = InT<IN>;
   constexpr int EB = T::EB;
-  constexpr int WN = 4;
+  static_assert(TBN % 64 == 0, "tile width");
+  constexpr int WN = TBN / 64;
   constexpr int WAVES = WM * WN;
   constexpr int WTM = TBM / WM;              // wave tile rows
   constexpr int WTN = TBN / WN;              // wave tile columns (64)
@@ -248,8 +254,26 @@ __global__ __launch_bounds__(256 * WM, (waves_per_simd<TBM, WM, NS>())) void gem
 
   // A row r keeps its 16-byte slot c at c ^ aswz(r).
   auto aswz = [](int r) { return (r >> 1) & 7; };
-  // 16-bit B row k keeps its 16-byte slot c at c ^ bswz16(k).
-  auto bswz16 = [](int k) { return ((k & 3) << 2) ^ (((k >> 3) & 1) << 1); };
+  // B row k (the [K, N] layout) keeps its 16-byte slot c at c ^ bswz(k): a
+  // bijection of the row's BSLOTS slots, chosen so that the K rows one
+  // transposing read gathers lie on different banks.  A lane's transposing
+  // reads of one stage reach rows k + (row offset) through the instruction's
+  // immediate offset, with the slot computed once for row k, so bswz may only
+  // use bits of k that those offsets never change: 16-bit inputs add 4 r and
+  // 32 ks to k = 8 grp + t (t < 4), leaving bits 0, 1, 3 and 4; fp8 adds
+  // 8 r and 64 ks to k = 32 h + t (t < 8), leaving bits 0 - 2 and 5; int8
+  // adds 8, 32 and 64 multiples to k = 16 h + t, leaving bits 0 - 2 and 4.
+  auto bswz = [](int k) {
+    if constexpr (EB == 2) {
+      if constexpr (BSLOTS >= 16) return ((k & 3) << 2) ^ (((k >> 3) & 1) << 1);
+      else return ((k & 3) << 1) ^ ((k >> 3) & 1);
+    } else {
+      if constexpr (BSLOTS >= 16) return (k & 7) << 1;
+      else if constexpr (BSLOTS == 8) return k & 7;
+      else return (k & 3) ^ ((k >> 2) & 1);
+    }
+  };
+  static_assert(BSLOTS >= 4, "B row of at least four 16-byte slots");
 
   // ---- DMA geometry of this lane (the same for every stage).  Offsets of
   // rows past M / columns past N are replaced by an out-of-range offset once;
@@ -279,7 +303,7 @@ __global__ __launch_bounds__(256 * WM, (waves_per_simd<TBM, WM, NS>())) void gem
     } else {
       const int k = BROWS_PER_DMA * idx + lane / BSLOTS;
       const int s = lane % BSLOTS;
-      const int cb = EB == 2 ? (s ^ bswz16(k)) : (s ^ ((k & 7) << 1));
+      const int cb = s ^ bswz(k);
       b_off[i] = (PER_TILE || n0 + cb * (16 / EB) < g.N) ? (unsigned)(k * g.N * EB + cb * 16) : OOB;
       b_k[i] = k;  // K row of the chunk
     }
@@ -303,7 +327,7 @@ __global__ __launch_bounds__(256 * WM, (waves_per_simd<TBM, WM, NS>())) void gem
       } else {
         const int k = BROWS_PER_DMA * (w * DB + i) + lane / BSLOTS;
         const int sl = lane % BSLOTS;
-        col = (EB == 2 ? (sl ^ bswz16(k)) : (sl ^ ((k & 7) << 1))) * (16 / EB);
+        col = (sl ^ bswz(k)) * (16 / EB);
       }
       *bm |= (unsigned)(tn0 + col < g.N) << i;
     }
@@ -415,7 +439,7 @@ __global__ __launch_bounds__(256 * WM, (waves_per_simd<TBM, WM, NS>())) void gem
     for (int j = 0; j < FN; ++j) {
       const int n = M16 ? wn * WTN + j * 16 + 4 * q : wn * WTN + j * 32 + 16 * (grp & 1) + 4 * q;
       const int k = (M16 ? 8 * grp : 8 * (grp >> 1)) + t_;
-      b_rd[j] = k * BROW + (((n >> 3) ^ bswz16(k)) << 4) + (q & 1) * 8;
+      b_rd[j] = k * BROW + (((n >> 3) ^ bswz(k)) << 4) + (q & 1) * 8;
     }
   } else {
     const int t_ = gi >> 1, q = gi & 1;
@@ -423,7 +447,7 @@ __global__ __launch_bounds__(256 * WM, (waves_per_simd<TBM, WM, NS>())) void gem
     for (int j = 0; j < FN; ++j) {
       const int n = wn * WTN + j * 32 + 16 * (grp & 1) + 8 * q;
       const int k = (I8 ? 16 : 32) * (grp >> 1) + t_;  // this lane half's K rows
-      b_rd[j] = k * BROW + (((n >> 4) ^ (t_ << 1)) << 4) + q * 8;
+      b_rd[j] = k * BROW + (((n >> 4) ^ bswz(k)) << 4) + q * 8;
     }
   }
 
@@ -705,21 +729,21 @@ __global__ __launch_bounds__(256 * WM, (waves_per_simd<TBM, WM, NS>())) void gem
   if constexpr (!PER_TILE) store_tile(m0, n0);
 }
 
-template <int IN, int TBM, int WM, int NS, bool BT>
+template <int IN, int TBM, int TBN, int WM, int NS, bool BT>
 hipError_t launch_cfg(const gemm_plan_s& p, const GemmArgs& a, bool slice, hipStream_t s) {
-  const dim3 grid((unsigned)a.grid), block(256 * WM);
+  const dim3 grid((unsigned)a.grid), block(WM * TBN);
   if (slice)
-    hipLaunchKernelGGL((gemm_dma_kernel<IN, GEMM_F32, MODE_SLICE, TBM, WM, NS, BT, GemmArgs>), grid,
-                       block, 0, s, a);
+    hipLaunchKernelGGL((gemm_dma_kernel<IN, GEMM_F32, MODE_SLICE, TBM, TBN, WM, NS, BT, GemmArgs>),
+                       grid, block, 0, s, a);
   else if (p.out == GEMM_F32)
-    hipLaunchKernelGGL((gemm_dma_kernel<IN, GEMM_F32, MODE_STORE, TBM, WM, NS, BT, GemmArgs>), grid,
-                       block, 0, s, a);
+    hipLaunchKernelGGL((gemm_dma_kernel<IN, GEMM_F32, MODE_STORE, TBM, TBN, WM, NS, BT, GemmArgs>),
+                       grid, block, 0, s, a);
   else if (p.out == GEMM_F16)
-    hipLaunchKernelGGL((gemm_dma_kernel<IN, GEMM_F16, MODE_STORE, TBM, WM, NS, BT, GemmArgs>), grid,
-                       block, 0, s, a);
+    hipLaunchKernelGGL((gemm_dma_kernel<IN, GEMM_F16, MODE_STORE, TBM, TBN, WM, NS, BT, GemmArgs>),
+                       grid, block, 0, s, a);
   else
-    hipLaunchKernelGGL((gemm_dma_kernel<IN, GEMM_BF16, MODE_STORE, TBM, WM, NS, BT, GemmArgs>), grid,
-                       block, 0, s, a);
+    hipLaunchKernelGGL((gemm_dma_kernel<IN, GEMM_BF16, MODE_STORE, TBM, TBN, WM, NS, BT, GemmArgs>),
+                       grid, block, 0, s, a);
   return hipGetLastError();
 }
 
@@ -728,14 +752,14 @@ template <int IN, bool BT>
 hipError_t launch_persist_in(const gemm_plan_s& p, const PersistArgs& a, hipStream_t s) {
   const dim3 grid((unsigned)a.wgs), block(512);
   if (p.out == GEMM_F32)
-    hipLaunchKernelGGL((gemm_dma_kernel<IN, GEMM_F32, MODE_PERSIST, 256, 2, 2, BT, PersistArgs>),
-                       grid, block, 0, s, a);
+    hipLaunchKernelGGL((gemm_dma_kernel<IN, GEMM_F32, MODE_PERSIST, 256, WIDE_TBN, 2, 2, BT,
+                                        PersistArgs>), grid, block, 0, s, a);
   else if (p.out == GEMM_F16)
-    hipLaunchKernelGGL((gemm_dma_kernel<IN, GEMM_F16, MODE_PERSIST, 256, 2, 2, BT, PersistArgs>),
-                       grid, block, 0, s, a);
+    hipLaunchKernelGGL((gemm_dma_kernel<IN, GEMM_F16, MODE_PERSIST, 256, WIDE_TBN, 2, 2, BT,
+                                        PersistArgs>), grid, block, 0, s, a);
   else
-    hipLaunchKernelGGL((gemm_dma_kernel<IN, GEMM_BF16, MODE_PERSIST, 256, 2, 2, BT, PersistArgs>),
-                       grid, block, 0, s, a);
+    hipLaunchKernelGGL((gemm_dma_kernel<IN, GEMM_BF16, MODE_PERSIST, 256, WIDE_TBN, 2, 2, BT,
+                                        PersistArgs>), grid, block, 0, s, a);
   return hipGetLastError();
 }
 
@@ -747,12 +771,20 @@ hipError_t launch_persist_bt(const gemm_plan_s& p, const PersistArgs& a, hipStre
 template <int IN, bool BT>
 hipError_t launch_tiles(const gemm_plan_s& p, int tile, const GemmArgs& a, bool slice, hipStream_t s) {
   switch (tile) {
-    case GEMM_TILE_256x256: return launch_cfg<IN, 256, 2, 2, BT>(p, a, slice, s);
-    case GEMM_TILE_128x256: return launch_cfg<IN, 128, 2, 3, BT>(p, a, slice, s);
-    case GEMM_TILE_64x256: return launch_cfg<IN, 64, 1, 4, BT>(p, a, slice, s);
-    case GEMM_TILE_32x256: return launch_cfg<IN, 32, 1, 4, BT>(p, a, slice, s);
-    default: return hipErrorInvalidValue;
+    case GEMM_TILE_256x256: return launch_cfg<IN, 256, 256, 2, 2, BT>(p, a, slice, s);
+    case GEMM_TILE_128x256: return launch_cfg<IN, 128, 256, 2, 3, BT>(p, a, slice, s);
+    case GEMM_TILE_64x256: return launch_cfg<IN, 64, 256, 1, 4, BT>(p, a, slice, s);
+    case GEMM_TILE_32x256: return launch_cfg<IN, 32, 256, 1, 4, BT>(p, a, slice, s);
+    default: break;
   }
+  if constexpr (InT<IN>::EB == 2) {  // the narrow tiles take 16-bit inputs only
+    switch (tile) {
+      case GEMM_TILE_64x64: return launch_cfg<IN, 64, 64, 2, 8, BT>(p, a, slice, s);
+      case GEMM_TILE_32x64: return launch_cfg<IN, 32, 64, 2, 10, BT>(p, a, slice, s);
+      default: break;
+    }
+  }
+  return hipErrorInvalidValue;
 }
 
 template <int IN>
@@ -764,7 +796,7 @@ hipError_t launch_in(const gemm_plan_s& p, int tile, const GemmArgs& a, bool sli
 }  // namespace
 
 hipError_t launch_ozaki_gemm(int type2, const OzGemmArgs& a, hipStream_t s) {
-  static_assert(kOzTileN == TBN, "Ozaki tile");
+  static_assert(kOzTileN == WIDE_TBN, "Ozaki tile");
   // The fp64 sums (two registers per element) must sit in architectural
   // VGPRs, at most 256 per wave.  bf16: a 128 x 256 tile of 8 waves (two per
   // SIMD) of 64 x 64, 253 VGPRs, 3-stage ring (144 KB).  fp8 fragments are
@@ -774,13 +806,13 @@ hipError_t launch_ozaki_gemm(int type2, const OzGemmArgs& a, hipStream_t s) {
   // measured 7-10 % faster than 2 and 3 stages.
   const dim3 grid((unsigned)a.grid);
   if (type2 == GEMM_BF16)
-    hipLaunchKernelGGL((gemm_dma_kernel<GEMM_BF16, GEMM_F32, MODE_OZAKI, 128, 2, 3, false,
+    hipLaunchKernelGGL((gemm_dma_kernel<GEMM_BF16, GEMM_F32, MODE_OZAKI, 128, WIDE_TBN, 2, 3, false,
                                         OzGemmArgs>), grid, dim3(512), 0, s, a);
   else if (type2 == GEMM_F8_E4M3)
-    hipLaunchKernelGGL((gemm_dma_kernel<GEMM_F8_E4M3, GEMM_F32, MODE_OZAKI, 64, 1, 4, false,
+    hipLaunchKernelGGL((gemm_dma_kernel<GEMM_F8_E4M3, GEMM_F32, MODE_OZAKI, 64, WIDE_TBN, 1, 4, false,
                                         OzGemmArgs>), grid, dim3(256), 0, s, a);
   else if (type2 == GEMM_I8)
-    hipLaunchKernelGGL((gemm_dma_kernel<GEMM_I8, GEMM_F32, MODE_OZAKI, 128, 2, 3, false,
+    hipLaunchKernelGGL((gemm_dma_kernel<GEMM_I8, GEMM_F32, MODE_OZAKI, 128, WIDE_TBN, 2, 3, false,
                                         OzGemmArgs>), grid, dim3(512), 0, s, a);
   else
     return hipErrorInvalidValue;

@@ -172,5 +172,14 @@ def fp8_check_bound(C, C64, Cabs, K, out, dt, a_bits=None, b_bits=None, ii=None,
     return check_bound(C, C64, Cabs, K, out, bias=bias, window=win)
 
 
+NARROW_TILES = ("32x64", "64x64")   # DMA tiles of 64 columns: fp16 / bf16 inputs only
+
+
+def tiles_for(dt: str, tiles):
+    """The tiles of `tiles` that take input dtype dt (the narrow tiles take
+    16-bit inputs only)."""
+    return [t for t in tiles if dt in ("f16", "bf16") or t not in NARROW_TILES]
+
+
 def dtype_name(code: int) -> str:
     return {v: k for k, v in imm.DTYPE.items()}[code]

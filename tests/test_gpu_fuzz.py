@@ -20,12 +20,13 @@ import torch
 import invariant_matmul_amd as imm
 import oracle
 import workloads as wl
-from tests.helpers import bits_of, dev, fp8_check_bound, log, out_torch_dtype, values_of
+from tests.helpers import bits_of, dev, fp8_check_bound, log, out_torch_dtype, tiles_for, values_of
 
 pytestmark = pytest.mark.gpu
 
-ALL_TILES = ["256x256", "128x128", "32x128", "256x256_rs", "32x256", "64x256", "128x256"]
-DMA_TILES = {"256x256", "32x256", "64x256", "128x256"}
+ALL_TILES = ["256x256", "128x128", "32x128", "256x256_rs", "32x256", "64x256", "128x256", "32x64",
+             "64x64"]
+DMA_TILES = {"256x256", "32x256", "64x256", "128x256", "32x64", "64x64"}
 
 
 def _case(seed):
@@ -63,7 +64,7 @@ def test_random_case(seed):
     C64, Cabs = oracle.gemm(wl.bits(A), wl.bits(B), dt)
     Ad, Bd, Wd = A.to(dev()), B.to(dev()), B.t().contiguous().to(dev())
     ref = None
-    for tile in ALL_TILES:
+    for tile in tiles_for(dt, ALL_TILES):
         layouts = [(0, Bd), (imm.PLAN_B_TRANSPOSED, Wd)] if tile in DMA_TILES else [(0, Bd)]
         for flags, Bx in layouts:
             plan = imm.gemm_plan_ex2(M, N, K, dt, out, split_k=split, tile=tile, flags=flags)

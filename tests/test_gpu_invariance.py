@@ -20,11 +20,12 @@ import torch
 
 import invariant_matmul_amd as imm
 import workloads as wl
-from tests.helpers import bits_of, dev, log, run
+from tests.helpers import bits_of, dev, log, run, tiles_for
 
 pytestmark = pytest.mark.gpu
 
-TILES = ["256x256", "128x128", "32x128", "256x256_rs", "32x256", "64x256", "128x256"]
+TILES = ["256x256", "128x128", "32x128", "256x256_rs", "32x256", "64x256", "128x256", "32x64",
+         "64x64"]
 
 
 def _to_dev(*ts):
@@ -135,7 +136,7 @@ def test_group_m_and_tile_shape_do_not_change_bits():
         Ad, Bd = _to_dev(A, B)
         for split in (False, True):
             ref = None
-            for tile in TILES:
+            for tile in tiles_for(dt, TILES):
                 for gm in (1, 3, 8):
                     p = imm.gemm_plan_ex(M, N, K, dt, "f32", split_k=3, group_m=gm, tile=tile)
                     C = bits_of(run(p, Ad, Bd, split))
@@ -199,8 +200,9 @@ def test_split_changes_bits_only_where_rounding_happens():
 
 @pytest.mark.parametrize("dt,bt", [("f16", False), ("bf16", True)])
 def test_tile_by_m_rows_identical_across_M(dt, bt):
-    """GEMM_PLAN_TILE_BY_M switches the single pass between the 32x256, 64x256,
-    128x256 and 256x256 tiles as M grows; every row must keep its bits."""
+    """GEMM_PLAN_TILE_BY_M switches the single pass between the 32x64, 64x64,
+    32x256, 64x256, 128x256 and 256x256 tiles as M grows; every row must keep
+    its bits."""
     N, K = 6144, 4096
     g = wl.gen(8400)
     A = wl.uniform((2048, K), dt, g).to(dev())
@@ -215,7 +217,8 @@ def test_tile_by_m_rows_identical_across_M(dt, bt):
         seen.add(plan.info["run_tile"])
         got = bits_of(run(plan, A[:m].contiguous(), Bd, False))
         assert np.array_equal(got, ref[:m]), m
-    assert seen == {imm.TILE[t] for t in ("32x256", "64x256", "128x256", "256x256")}, seen
+    assert seen == {imm.TILE[t] for t in ("32x64", "64x64", "32x256", "64x256", "128x256",
+                                          "256x256")}, seen
 
 
 @pytest.mark.parametrize("bt", [False, True])

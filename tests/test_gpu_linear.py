@@ -18,11 +18,12 @@ import torch
 import invariant_matmul_amd as imm
 import oracle
 import workloads as wl
-from tests.helpers import bits_of, check_bound, dev, expected_bits, log, out_torch_dtype, values_of
+from tests.helpers import (bits_of, check_bound, dev, expected_bits, log, out_torch_dtype,
+                           tiles_for, values_of)
 
 pytestmark = pytest.mark.gpu
 
-DMA_TILES = ["default", "256x256", "128x256", "64x256", "32x256"]
+DMA_TILES = ["default", "256x256", "128x256", "64x256", "32x256", "32x64", "64x64"]
 BT = imm.PLAN_B_TRANSPOSED
 
 
@@ -47,7 +48,7 @@ def test_transposed_b_gives_the_same_bits(dt, M, N, K):
     else:
         A, B = wl.uniform((M, K), dt, g), wl.uniform((K, N), dt, g)
     Ad, Bd, Wd = A.to(dev()), B.to(dev()), B.t().contiguous().to(dev())
-    for tile in DMA_TILES:
+    for tile in tiles_for(dt, DMA_TILES):
         for split in (0, 3):
             p = imm.gemm_plan_ex2(M, N, K, dt, "f32", split_k=split, tile=tile)
             pt = imm.gemm_plan_ex2(M, N, K, dt, "f32", split_k=split, tile=tile, flags=BT)

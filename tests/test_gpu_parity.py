@@ -15,11 +15,12 @@ import invariant_matmul_amd as imm
 import oracle
 import workloads as wl
 from tests.helpers import (FP8, FP8_PLAIN_BOUND_MIN_K, bits_of, check_bound, dev, expected_bits,
-                           fp8_check_bound, log, run, values_of)
+                           fp8_check_bound, log, run, tiles_for, values_of)
 
 pytestmark = pytest.mark.gpu
 
-TILES = ["256x256", "128x128", "32x128", "256x256_rs", "32x256", "64x256", "128x256"]
+TILES = ["256x256", "128x128", "32x128", "256x256_rs", "32x256", "64x256", "128x256", "32x64",
+         "64x64"]
 IN_DTYPES = ["f16", "bf16", "e4m3", "e5m2"]
 
 
@@ -58,7 +59,7 @@ def test_integer_inputs_bit_exact_ragged(dt, out):
     C64, _ = oracle.gemm(wl.bits(A), wl.bits(B), dt)
     want = expected_bits(C64, out)
     Ad, Bd = _to_dev(A, B)
-    for tile in TILES:
+    for tile in tiles_for(dt, TILES):
         for split in (1, 3):
             log(f"int {dt}->{out}: tile {tile} split {split}")
             p = imm.gemm_plan_ex(M, N, K, dt, out, split_k=split, tile=tile)
@@ -110,7 +111,7 @@ def test_random_inputs_within_bound_ragged(dt):
     C64, Ca = oracle.gemm(a_bits, b_bits, dt)
     Ad, Bd = _to_dev(A, B)
     for out in ("f32", "bf16"):
-        for tile in TILES:
+        for tile in tiles_for(dt, TILES):
             for split in (1, 5):
                 p = imm.gemm_plan_ex(M, N, K, dt, out, split_k=split, tile=tile)
                 r1 = fp8_check_bound(values_of(run(p, Ad, Bd, False)), C64, Ca, K, out, dt,

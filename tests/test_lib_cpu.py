@@ -169,7 +169,7 @@ def _plan_status(*args):
     ((8, 8, 8, 0, 4, -1, 0, 0, 1.0, 1.0), 2),     # split_k < 0
     ((8, 8, 8, 0, 4, 4097, 0, 0, 1.0, 1.0), 2),   # split_k too large
     ((8, 8, 8, 0, 4, 0, -1, 0, 1.0, 1.0), 2),     # group_m < 0
-    ((8, 8, 8, 0, 4, 0, 0, 9, 1.0, 1.0), 2),      # unknown tile
+    ((8, 8, 8, 0, 4, 0, 0, 10, 1.0, 1.0), 2),     # unknown tile
     ((8, 8, 8, 0, 4, 0, 0, 0, float("inf"), 1.0), 2),
     ((8, 8, 8, 0, 4, 0, 0, 0, 1.0, float("nan")), 2),
     ((2 ** 31, 8, 8, 0, 4, 0, 0, 0, 1.0, 1.0), 2),
@@ -440,21 +440,33 @@ def test_ozaki_column_maxima_chunks_are_capped():
         assert chunks * N * 8 <= scratch <= -(-(16384 * N * 8) // 256) * 256
 
 
-@pytest.mark.parametrize("M,N,K,tile", [
-    (1, 6144, 4096, "32x256"), (256, 6144, 4096, "32x256"), (512, 6144, 4096, "64x256"),
-    (768, 6144, 4096, "128x256"), (1024, 6144, 4096, "128x256"), (1536, 6144, 4096, "256x256"),
-    (2048, 6144, 4096, "256x256"), (3072, 6144, 4096, "128x256"), (1024, 1024, 1024, "32x256"),
-    (2048, 2048, 2048, "64x256"), (4096, 4096, 4096, "256x256"), (8192, 8192, 8192, "256x256"),
+@pytest.mark.parametrize("M,N,K,tile,tile8", [
+    (1, 6144, 4096, "32x64", "32x256"), (64, 6144, 4096, "32x64", "32x256"),
+    (96, 6144, 4096, "64x64", "32x256"), (128, 6144, 4096, "64x64", "32x256"),
+    (192, 6144, 4096, "32x256", "32x256"), (256, 6144, 4096, "32x256", "32x256"),
+    (512, 6144, 4096, "64x256", "64x256"), (768, 6144, 4096, "128x256", "128x256"),
+    (1024, 6144, 4096, "128x256", "128x256"), (1536, 6144, 4096, "256x256", "256x256"),
+    (2048, 6144, 4096, "256x256", "256x256"), (3072, 6144, 4096, "128x256", "128x256"),
+    (512, 1024, 4096, "32x64", "32x256"), (1024, 1024, 4096, "64x64", "32x256"),
+    (2048, 1024, 4096, "32x256", "32x256"), (48, 14336, 4096, "64x64", "32x256"),
+    (2048, 2048, 2048, "64x256", "64x256"), (4096, 4096, 4096, "256x256", "256x256"),
+    (8192, 8192, 8192, "256x256", "256x256"),
 ])
-def test_tile_by_m_rule(M, N, K, tile):
-    """GEMM_PLAN_TILE_BY_M: the DMA tile with the least estimated time
-    (rounds of 256 workgroups x (127 + tile rows)), the measured fastest at
-    each of these shapes; split-K path and the default plan unchanged."""
-    flagged = imm.gemm_plan_ex2(M, N, K, "f16", "f32", flags=imm.PLAN_TILE_BY_M).info
-    plain = imm.gemm_plan_ex2(M, N, K, "f16", "f32").info
-    assert flagged["run_tile"] == imm.TILE[tile]
-    for k in ("tile", "split_k", "k_per_split", "block_m", "block_n"):
-        assert flagged[k] == plain[k]
+def test_tile_by_m_rule(M, N, K, tile, tile8):
+    """GEMM_PLAN_TILE_BY_M: the DMA tile with the least estimated time (rounds
+    of 256 workgroups x the tile's units per round), the measured fastest at
+    each of these shapes (fp8 inputs skip the 64-column tiles); split-K path
+    and the default plan unchanged."""
+    for dt, want in (("f16", tile), ("bf16", tile), ("e5m2", tile8)):
+        flagged = imm.gemm_plan_ex2(M, N, K, dt, "f32", flags=imm.PLAN_TILE_BY_M).info
+        plain = imm.gemm_plan_ex2(M, N, K, dt, "f32").info
+        assert flagged["run_tile"] == imm.TILE[want], dt
+        # the split (which decides bits) never moves; the split-path tile moves
+        # only for wide reduction-dominated shapes (K >= 2N, N > 512)
+        same = ("split_k", "k_per_split") if K >= 2 * N and N > 512 else (
+            "tile", "split_k", "k_per_split", "block_m", "block_n")
+        for k in same:
+            assert flagged[k] == plain[k], (dt, k)
 
 
 @pytest.mark.parametrize("M,tile", [(1, "32x128"), (8, "32x128"), (32, "32x128"), (64, "64x256"),
@@ -530,3 +542,16 @@ def test_noalloc_entry_point_host_checks():
     with pytest.raises(imm.GemmError) as e:
         imm.gemm_splitk_run_noalloc(big, FAKE, FAKE, FAKE)
     assert e.value.status == 3 and str(imm.NOALLOC_WORKSPACE_BYTES) in str(e.value)
+
+
+def test_narrow_tiles_take_16_bit_inputs_only():
+    for tile in ("32x64", "64x64"):
+        for dt in ("f16", "bf16"):
+            for fl in (0, imm.PLAN_B_TRANSPOSED):
+                i = imm.gemm_plan_ex2(100, 6144, 4096, dt, "f32", tile=tile, flags=fl).info
+                assert i["run_tile"] == i["tile"] == imm.TILE[tile]
+                assert (i["run_block_m"], i["run_block_n"]) == tuple(map(int, tile.split("x")))
+                assert i["run_tiles_n"] == 6144 // 64
+        for dt in ("e4m3", "e5m2"):
+            assert _plan2_status(100, 6144, 4096, imm.DTYPE[dt], 4, 0, 0, imm.TILE[tile],
+                                 1.0, 1.0, 0) == 2
