@@ -306,6 +306,68 @@ def write_clock(counter_csv, agent_csv, lds_csv=None, out_path=CLOCK_FILE):
     print(json.dumps(out))
 
 
+TRACE_SUMMARY_FILE = os.path.join(ROOT, "profiles", "gemm_dma_square_f16_8192_kernel_trace.md")
+HEADLINE_KERNEL = "gemm_dma_kernel<0, 4, 0, 256, 256, 2, 2, false, imm::GemmArgs>"
+
+
+def write_trace_summary(trace_csv, bench_json, out_path=TRACE_SUMMARY_FILE):
+    """Summarise a rocprofv3 --kernel-trace run of the default bench command:
+    the headline kernel's dispatches (all, and the timed ones: the last
+    `steps` of its 1024-workgroup launches before the next kernel), and every
+    kernel by launch shape, next to the same run's event-timed numbers."""
+    import csv
+    with open(bench_json) as f:
+        line = json.loads(f.read().strip().splitlines()[-1])
+    rows = []
+    with open(trace_csv) as f:
+        for r in csv.DictReader(f):
+            wg = int(r["Workgroup_Size_X"]) * int(r["Workgroup_Size_Y"]) * int(r["Workgroup_Size_Z"])
+            grid = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])
+            rows.append((int(r["Start_Timestamp"]), r["Kernel_Name"], grid // max(wg, 1), wg,
+                         (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3))
+    rows.sort()
+    head = [x for x in rows if HEADLINE_KERNEL in x[1] and x[2] == 1024]
+    if not head:
+        raise SystemExit(f"{trace_csv}: no headline dispatches")
+    # the headline leg runs warm-up + steps launches back to back first
+    first = [x[4] for x in head[: line["warmup"] + line["steps"]]]
+    timed = first[line["warmup"]:]
+    groups = {}
+    for _, name, wgs, wg, us in rows:
+        groups.setdefault((name, wgs, wg), []).append(us)
+
+    def short(n):
+        n = n.replace("void imm::(anonymous namespace)::", "").replace("imm::", "")
+        n = n.split("(")[0] if n.startswith("gemm_") or n.startswith("splitk") else n
+        return n if len(n) <= 72 else n[:69] + "..."
+
+    out = ["# Kernel trace of the default bench run (square fp16 8192^3 headline)", "",
+           "Commands (repository root, MI355X):", "",
+           "    rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/prof_bench -o bench "
+           "-- python3 bench.py --steps 20 --warmup 5 > gpurun_out/bench_prof.json",
+           "    python3 bench.py --write-trace-summary gpurun_out/prof_bench/bench_kernel_trace.csv "
+           "gpurun_out/bench_prof.json", "",
+           f"The same run printed value = {line['value']:.1f} TFLOP/s and roofline.avg_launch_ms = "
+           f"{line['roofline']['avg_launch_ms'] * 1e3:.1f} us (HIP events on the launch stream).", "",
+           f"Headline kernel `{HEADLINE_KERNEL}` at M=N=K=8192 (1024 workgroups x 512 threads): "
+           f"{len(head)} dispatches in the whole run, average {statistics.mean(x[4] for x in head):.1f} us. "
+           f"Its first {len(first)} ({line['warmup']} warm-up + {line['steps']} timed) back to back: "
+           f"the timed {len(timed)} average {statistics.mean(timed):.1f} us, median "
+           f"{statistics.median(timed):.1f} us, min {min(timed):.1f} us, max {max(timed):.1f} us.", "",
+           "## Per kernel and launch shape", "",
+           "| kernel | workgroups | threads/WG | calls | avg us | median us | min us |",
+           "|---|---:|---:|---:|---:|---:|---:|"]
+    order = sorted(groups.items(), key=lambda kv: -sum(kv[1]))
+    for (name, wgs, wg), v in order[:60]:
+        out.append(f"| `{short(name)}` | {wgs} | {wg} | {len(v)} | {statistics.mean(v):.2f} | "
+                   f"{statistics.median(v):.2f} | {min(v):.2f} |")
+    if len(order) > 60:
+        out.append(f"| ({len(order) - 60} more kernel shapes, each a smaller share of the time) | | | | | | |")
+    with open(out_path, "w") as f:
+        f.write("\n".join(out) + "\n")
+    print(out_path)
+
+
 def _smi_power_clocks():
     """Socket power (W) and the XCDs' engine clocks (MHz) from amd-smi."""
     import re
@@ -712,6 +774,9 @@ def main():
                     help="back-to-back launches of the headline kernel, of torch.matmul on "
                          "the same fp16 product and of a plain copy, for the clock counters; "
                          "prints nothing else")
+    ap.add_argument("--write-trace-summary", nargs=2, metavar=("TRACE_CSV", "BENCH_JSON"),
+                    help="host only: write the kernel-trace summary of a rocprofv3 --kernel-trace run "
+                         "of the default bench command, then exit")
     ap.add_argument("--power-sample", action="store_true",
                     help="run the headline product in a loop on random, then all-zero inputs "
                          "and read the board's power and engine clocks with amd-smi during "
@@ -726,6 +791,9 @@ def main():
         return
     if args.write_stream_traffic:
         write_stream_traffic(*args.write_stream_traffic)
+        return
+    if args.write_trace_summary:
+        write_trace_summary(*args.write_trace_summary)
         return
     if args.write_clock:
         if len(args.write_clock) not in (2, 3):

@@ -5,10 +5,10 @@
 //
 // One workgroup of 8 waves (two per SIMD) owns a 256 x 256 tile of C (or of
 // one K slice of it); each wave owns a 128 x 64 block held in 128 fp32
-// accumulators per lane, as 8 x 4 blocks of 16 x 16 (16-bit inputs, the
-// 16x16x32 matrix-core step) or 4 x 2 blocks of 32 x 32 (fp8).  K is walked in ascending stages ([TDI] "Tiling -
-// 分塊行列乗算": load, compute, accumulate per K step, one write-back at the
-// end).  Two waves per SIMD, because a single wave serialises its own LDS and
+// accumulators per lane, as 8 x 4 blocks of 16 x 16 (the 16x16x32 matrix-core
+// step for 16-bit inputs, 16x16x128 for fp8).  K is walked in ascending
+// stages ([TDI] "Tiling - 分塊行列乗算": load, compute, accumulate per K step,
+// one write-back at the end).  Two waves per SIMD, because a single wave serialises its own LDS and
 // DMA instructions with its MFMAs while a second wave's memory instructions
 // overlap the first wave's MFMAs (both measured).
 //
@@ -181,13 +181,15 @@ __global__ __launch_bounds__(WM * TBN, (waves_per_simd<TBM, TBN, WM, NS>())) voi
   constexpr int WAVES = WM * WN;
   constexpr int WTM = TBM / WM;              // wave tile rows
   constexpr int WTN = TBN / WN;              // wave tile columns (64)
-  // 16-bit inputs: the 16x16x32 step; fp8, int8 and the exact Ozaki chains
-  // (whose bits no instruction changes): the 32x32 step
+  // 16-bit inputs: the 16x16x32 step; fp8: the 16x16x128 step; int8 and the
+  // exact Ozaki chains (whose bits no instruction changes): the 32x32 step
   constexpr bool M16 = EB == 2 && MODE != MODE_OZAKI;
-  constexpr int BLK = M16 ? 16 : 32;         // MFMA output block edge
+  constexpr bool F8S = EB == 1 && !T::I8 && MODE != MODE_OZAKI;
+  constexpr bool B16 = M16 || F8S;           // 16 x 16 output blocks
+  constexpr int BLK = B16 ? 16 : 32;         // MFMA output block edge
   constexpr int NACC = BLK * BLK / 64;       // accumulators per lane per block
-  using AccT = typename std::conditional<M16, f32x4, f32x16>::type;
-  constexpr int KSTEP = M16 ? 64 : T::KSTEP_B;  // bytes of K per MFMA step
+  using AccT = typename std::conditional<B16, f32x4, f32x16>::type;
+  constexpr int KSTEP = F8S ? 128 : (M16 ? 64 : T::KSTEP_B);  // bytes of K per MFMA step
   constexpr int FM = WTM / BLK;              // MFMA row blocks per wave
   constexpr int FN = WTN / BLK;              // MFMA column blocks per wave
   constexpr int NM = FM * FN;                // MFMAs per k-step per wave
@@ -212,7 +214,9 @@ __global__ __launch_bounds__(WM * TBN, (waves_per_simd<TBM, TBN, WM, NS>())) voi
   constexpr int NREAD = NRA + NRB;
   constexpr int LDS_BYTES = NS * STAGE;
   static_assert(LDS_BYTES <= 160 * 1024, "LDS ring too large");
-  static_assert(KS % 2 == 0, "k-steps per stage");
+  // fp8 (one 128-byte k-step per stage): single-buffered fragments; the
+  // other paths alternate two fragment sets over an even number of k-steps
+  static_assert(F8S ? KS == 1 : KS % 2 == 0, "k-steps per stage");
 
   __shared__ __attribute__((aligned(1024))) char lds[LDS_BYTES];
   // LDS offsets of the A and B blocks of stage t.
@@ -442,11 +446,14 @@ __global__ __launch_bounds__(WM * TBN, (waves_per_simd<TBM, TBN, WM, NS>())) voi
       b_rd[j] = k * BROW + (((n >> 3) ^ bswz(k)) << 4) + (q & 1) * 8;
     }
   } else {
+    // each group of 16 lanes reads 8 K rows x 16 columns per transposing read:
+    // 16x16 blocks (fp8), the column block and K rows 32 grp ..; 32x32 blocks,
+    // column half grp & 1 and K rows 32 (grp >> 1) .. (16 for int8)
     const int t_ = gi >> 1, q = gi & 1;
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
-      const int n = wn * WTN + j * 32 + 16 * (grp & 1) + 8 * q;
-      const int k = (I8 ? 16 : 32) * (grp >> 1) + t_;  // this lane half's K rows
+      const int n = F8S ? wn * WTN + j * 16 + 8 * q : wn * WTN + j * 32 + 16 * (grp & 1) + 8 * q;
+      const int k = F8S ? 32 * grp + t_ : (I8 ? 16 : 32) * (grp >> 1) + t_;
       b_rd[j] = k * BROW + (((n >> 4) ^ bswz(k)) << 4) + q * 8;
     }
   }
@@ -486,7 +493,7 @@ __global__ __launch_bounds__(WM * TBN, (waves_per_simd<TBM, TBN, WM, NS>())) voi
           F.b[j] = *reinterpret_cast<const i32x4*>(sbb + b_rd[j] + ((c ^ asw) << 4));
         } else {
           const int j = (x - NRA) >> 1, f = (x - NRA) & 1;
-          const int c = ks * 4 + 2 * hq + f;
+          const int c = ks * (KSTEP / 16) + 2 * hq + f;
           const i32x4 v = *reinterpret_cast<const i32x4*>(sbb + b_rd[j] + ((c ^ asw) << 4));
 #pragma unroll
           for (int e = 0; e < 4; ++e) F.b[j][4 * f + e] = v[e];
@@ -507,13 +514,13 @@ __global__ __launch_bounds__(WM * TBN, (waves_per_simd<TBM, TBN, WM, NS>())) voi
     } else {
       if (x < NRA) {
         const int i = x >> 1, f = x & 1;
-        const int c = ks * 4 + 2 * hq + f;
+        const int c = ks * (KSTEP / 16) + 2 * hq + f;
         const i32x4 v = *reinterpret_cast<const i32x4*>(sb + a_rd[i] + ((c ^ asw) << 4));
 #pragma unroll
         for (int e = 0; e < 4; ++e) F.a[i][4 * f + e] = v[e];
       } else {
         const int j = (x - NRA) >> 2, r = (x - NRA) & 3;
-        const i32x2 v = tr8_rows<BROW>(lds_addr + bs + b_rd[j], ks * 64 + 8 * r);
+        const i32x2 v = tr8_rows<BROW>(lds_addr + bs + b_rd[j], ks * KSTEP + 8 * r);
         F.b[j][2 * r] = v[0];
         F.b[j][2 * r + 1] = v[1];
       }
@@ -538,6 +545,8 @@ __global__ __launch_bounds__(WM * TBN, (waves_per_simd<TBM, TBN, WM, NS>())) voi
   auto mfma_x = [&](const Frag<IN, FM, FN>& F, int x) {
     if constexpr (M16)
       acc[x / FN][x % FN] = mfma16_v<IN>(F.a[x / FN], F.b[x % FN], acc[x / FN][x % FN]);
+    else if constexpr (F8S)
+      acc[x / FN][x % FN] = mfma16_f8<IN>(F.a[x / FN], F.b[x % FN], acc[x / FN][x % FN]);
     else
       acc[x / FN][x % FN] = mfma_v<IN>(F.a[x / FN], F.b[x % FN], acc[x / FN][x % FN]);
   };
@@ -593,7 +602,7 @@ __global__ __launch_bounds__(WM * TBN, (waves_per_simd<TBM, TBN, WM, NS>())) voi
         const int64_t col = tn0 + lcol + j * BLK;
 #pragma unroll
         for (int r = 0; r < NACC; ++r) {
-          const int64_t row = tm0 + lrow + i * BLK + (M16 ? r : 8 * (r >> 2) + (r & 3));
+          const int64_t row = tm0 + lrow + i * BLK + (B16 ? r : 8 * (r >> 2) + (r & 3));
           if constexpr (MODE == MODE_OZAKI) {
             // C = 2^(ea[row] + eb[col]) * sum: the same bits as scaling every
             // pair's term by its full exponent while no value leaves fp64's
@@ -683,24 +692,95 @@ __global__ __launch_bounds__(WM * TBN, (waves_per_simd<TBM, TBN, WM, NS>())) voi
     if (refill) __builtin_amdgcn_s_setprio(0);
   };
 
-  // k-steps alternate between F0 and F1; KS is even, so every stage starts on F0
+  // fp8: one k-step per stage on single-buffered fragments (F0).  Two
+  // fragment sets of the 16x16x128 step do not fit beside the accumulators at
+  // two waves per SIMD, so the reads of stage t+1 go into the registers the
+  // MFMAs of stage t free, ordered so that each is read long before its first
+  // use.  Phase 1 runs the blocks (i, j) with j < FN/2, phase 2 those with
+  // j >= FN/2, both i-major.  Between the phases sits the stage change: all of
+  // this wave's reads of stage t landed long before (full LDS wait), its DMA
+  // of stage t+1 has landed, and one barrier certifies both for every wave.
+  // Then the B blocks j < FN/2 of stage t+1 are read (first used a whole
+  // phase later), phase 2 runs with the refill of stage t's slot (stage t+NS)
+  // spread over its MFMAs and A block i of stage t+1 read after its last MFMA
+  // (i, FN-1) (first used (FM-1) FN/2 MFMAs later), and the B blocks
+  // j >= FN/2 are read last (first used in phase 2 of stage t+1).  At the
+  // start of stage t+1 a wave waits for all but those last B reads.
+  constexpr int F8_LATE = F8S ? (FN / 2) * (NRB / FN) : 0;  // reads left in flight at a stage start
+  auto kstep_f8 = [&](int t) {
+    if constexpr (F8S) {
+      constexpr int H = FN / 2;
+      constexpr int RA = NRA / FM, RB = NRB / FN;  // fragment reads per A block, per B block
+      static_assert(RA * FM == NRA && RB * FN == NRB && H * 2 == FN, "fragment reads");
+      static_assert(F8_LATE <= 15, "lgkmcnt field");
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < H; ++j) {
+          mfma_x(F0, i * FN + j);
+          fence();
+        }
+      lds_wait();
+      stage_change();
+      StageSrc q;
+      if constexpr (PER_TILE)
+        q = next_src();
+      else
+        q = stage_src(t + NS);
+      const int as = a_slot(t + 1), bs = b_slot(t + 1);
+#pragma unroll
+      for (int y = 0; y < H * RB; ++y) read_one(F0, as, bs, 0, NRA + y);
+      fence();
+      __builtin_amdgcn_s_setprio(3);
+      constexpr int NM2 = FM * H;  // MFMAs of phase 2, over which the refill is spread
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+#pragma unroll
+        for (int j = H; j < FN; ++j) {
+          mfma_x(F0, i * FN + j);
+          const int c = i * H + (j - H);
+#pragma unroll
+          for (int y = c * DPW / NM2; y < (c + 1) * DPW / NM2; ++y) dma_one(q, t + NS, y);
+          fence();
+        }
+#pragma unroll
+        for (int y = 0; y < RA; ++y) read_one(F0, as, bs, 0, i * RA + y);
+        fence();
+      }
+#pragma unroll
+      for (int y = H * RB; y < NRB; ++y) read_one(F0, as, bs, 0, NRA + y);
+      fence();
+      __builtin_amdgcn_s_setprio(0);
+    }
+  };
+
+  // k-steps alternate between F0 and F1; KS is even, so every stage starts on
+  // F0 (fp8: one k-step per stage, on F0 alone)
   OzCursor cur;      // Ozaki mode: the pair and stage being computed
   int chunk_left = 0;
   if constexpr (MODE == MODE_OZAKI) chunk_left = g.chunk_stages;
   int cur_tile = 0, cur_kt = 0;  // MODE_PERSIST: the tile and stage being computed
   int64_t cur_m0 = m0, cur_n0 = n0;
   for (int t = 0; t < nt; ++t) {
+    if constexpr (F8S) {
+      // all fragment reads of stage t but the last B blocks have landed
+      fence();
+      __builtin_amdgcn_s_waitcnt(lgkmcnt_imm(F8_LATE));
+      fence();
+      kstep_f8(t);
+    } else {
 #pragma unroll
-    for (int ks = 0; ks + 1 < KS; ++ks) {
-      lds_wait();  // fragments of k-step ks have landed
-      if (ks % 2 == 0)
-        kstep(false, F0, t, F1, t, ks + 1);
-      else
-        kstep(false, F1, t, F0, t, ks + 1);
+      for (int ks = 0; ks + 1 < KS; ++ks) {
+        lds_wait();  // fragments of k-step ks have landed
+        if (ks % 2 == 0)
+          kstep(false, F0, t, F1, t, ks + 1);
+        else
+          kstep(false, F1, t, F0, t, ks + 1);
+      }
+      lds_wait();  // last k-step's fragments landed: this wave has read all of stage t
+      stage_change();
+      kstep(true, F1, t, F0, t + 1, 0);
     }
-    lds_wait();  // last k-step's fragments landed: this wave has read all of stage t
-    stage_change();
-    kstep(true, F1, t, F0, t + 1, 0);
     if constexpr (MODE == MODE_OZAKI) {
       const int level = cur.p + cur.q;
       const bool pair_end = cur.step(ntp, g.slices, g.d);

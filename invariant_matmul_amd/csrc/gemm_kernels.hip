@@ -14,9 +14,9 @@
 // written to a double-buffered LDS tile, and fed to the matrix cores from
 // LDS.  The accumulators never leave registers until the single write-back.
 //
-// Bits.  Each output element is one accumulation chain: its MFMA block
-// (16x16 for fp16/bf16, 32x32 for fp8) is updated once per instruction-K step
-// (32 elements for fp16/bf16, 64 for fp8) in ascending k, starting from +0.  The instruction is fixed per input
+// Bits.  Each output element is one accumulation chain: its 16x16 MFMA block
+// is updated once per instruction-K step (32 elements for fp16/bf16, 128 for
+// fp8) in ascending k, starting from +0.  The instruction is fixed per input
 // dtype and the chain does not depend on BM, BN, the wave layout or the tile
 // order ([TDI] "Batch Invariance の由来": BLOCK_M/BLOCK_N and GROUP_M change
 // no bits, the K step does).  Rows past M load as zero and are never stored,
@@ -45,13 +45,14 @@ template <int IN>
 struct TileT {
   static constexpr int EB = InT<IN>::EB;
   static constexpr bool M16 = EB == 2;                   // 16x16x32 step (16-bit inputs)
-  static constexpr int BLK = M16 ? 16 : 32;              // MFMA output block edge
+  static constexpr bool F8 = EB == 1;                    // 16x16x128 step (fp8 inputs)
+  static constexpr int BLK = 16;                         // MFMA output block edge
   static constexpr int NACC = BLK * BLK / 64;            // accumulators per lane per block
-  static constexpr int KSTEP = M16 ? 64 : InT<IN>::KSTEP_B;  // bytes of K per MFMA step
+  static constexpr int KSTEP = M16 ? 64 : 128;           // bytes of K per MFMA step
   static constexpr int BKE = ROWB / EB;                  // K elements per stage
   static constexpr int NKK = ROWB / KSTEP;               // MFMA steps per stage
-  static constexpr int FRAG = M16 ? 1 : InT<IN>::FRAG;   // 16-byte chunks per lane
-  using Acc = typename std::conditional<M16, f32x4, f32x16>::type;
+  static constexpr int FRAG = M16 ? 1 : 2;               // 16-byte chunks per lane
+  using Acc = f32x4;
 };
 
 __device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
@@ -226,7 +227,7 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_tile_kernel(GemmAr
           } else {
             const i32x8 av = __builtin_shufflevector(af[i][0], af[i][1], 0, 1, 2, 3, 4, 5, 6, 7);
             const i32x8 bv = __builtin_shufflevector(bfr[j][0], bfr[j][1], 0, 1, 2, 3, 4, 5, 6, 7);
-            acc[i][j] = mfma_v<IN>(av, bv, acc[i][j]);
+            acc[i][j] = mfma16_f8<IN>(av, bv, acc[i][j]);
           }
         }
     }
@@ -234,9 +235,8 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_tile_kernel(GemmAr
     __syncthreads();
   }
 
-  // Write-back.  Accumulator layouts: 16x16 blocks, lane l, register r holds
-  // row 4*(l/16) + r, column l%16; 32x32 blocks, row 8*(r/4) + 4*(l/32) + r%4,
-  // column l%32.
+  // Write-back.  Accumulator layout of a 16x16 block: lane l, register r holds
+  // row 4*(l/16) + r, column l%16.
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
 #pragma unroll
@@ -244,8 +244,7 @@ __global__ __launch_bounds__(WAVES_M* WAVES_N * 64) void gemm_tile_kernel(GemmAr
       const int64_t col = n0 + wn * WTN + j * BLK + lb;
 #pragma unroll
       for (int r = 0; r < T::NACC; ++r) {
-        const int64_t row = m0 + wm * WTM + i * BLK +
-                            (T::M16 ? 4 * hq + r : 8 * (r >> 2) + 4 * hq + (r & 3));
+        const int64_t row = m0 + wm * WTM + i * BLK + 4 * hq + r;
         if (row < g.M && col < g.N) {
           const float v = acc[i][j][r];
           if constexpr (SLICE) {

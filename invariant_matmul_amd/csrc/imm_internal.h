@@ -12,8 +12,8 @@
 namespace imm {
 
 // Every tile configuration of an input dtype uses the same matrix-core
-// instruction (a 16x16 output block with K of 32 for 16-bit inputs, a 32x32
-// block with K of 64 for fp8) and walks K in ascending order in steps of that
+// instruction (a 16x16 output block with K of 32 for 16-bit inputs, with K of
+// 128 for fp8) and walks K in ascending order in steps of that
 // instruction, so configurations differ only in how output elements are
 // spread over workgroups and waves -- which [TDI] "Batch Invariance の由来"
 // (BLOCK_M / BLOCK_N, num_warps paragraphs) shows has no effect on bits.
@@ -24,9 +24,9 @@ constexpr int kTileKBytes = 128;
 inline int elem_bytes(int dt) { return (dt == GEMM_F8_E4M3 || dt == GEMM_F8_E5M2) ? 1 : 2; }
 inline int block_k_elems(int dt) { return kTileKBytes / elem_bytes(dt); }
 // Shape of the matrix-core step the GEMM kernels use for an input dtype:
-// 16 x 16 x 32 for fp16 / bf16, 32 x 32 x 64 for fp8.
-inline int mfma_mn(int dt) { return elem_bytes(dt) == 1 ? 32 : 16; }
-inline int mfma_k(int dt) { return elem_bytes(dt) == 1 ? 64 : 32; }
+// 16 x 16 x 32 for fp16 / bf16, 16 x 16 x 128 for fp8.
+inline int mfma_mn(int) { return 16; }
+inline int mfma_k(int dt) { return elem_bytes(dt) == 1 ? 128 : 32; }
 
 }  // namespace imm
 

@@ -3,14 +3,15 @@
 The pages state fp32 accumulation (the Tencent deterministic-inference
 article, "Batch Invariance の由来", and the north-star bound K 2^-24 |A||B|);
 what a matrix instruction does inside one step is hardware-defined.  Measured
-on gfx950 through the library (one 32 x 32 output block, products placed in
+on gfx950 through the library (one 16 x 16 output block, products placed in
 known K positions):
-- fp8 (e4m3, e5m2; the 64-deep step): the products of a step are added in a
-  window that ends 13 binades below the largest product of that step; parts
-  below it are truncated toward zero.  The fp32 accumulator carried from the
-  previous step is not part of the window.
-- fp16 / bf16 (16-deep step): 1 + 2^-23 survives, i.e. no window inside fp32
-  precision.
+- fp8 (e4m3, e5m2; the 16x16x128 step): the products of each aligned group
+  of 8 consecutive K positions are added in a window that ends 13 binades
+  below the largest product of that group; parts below it are truncated
+  toward zero.  Products of other groups, of the same step or not, and the
+  fp32 accumulator are not part of that window.
+- fp16 / bf16 (the 16x16x32 step): 1 + 2^-23 survives, i.e. no window inside
+  fp32 precision.
 If the hardware or the toolchain ever changes this, these tests say so before
 the bounds in tests/helpers.py silently become wrong.
 """
@@ -18,7 +19,7 @@ import pytest
 import torch
 
 import invariant_matmul_amd as imm
-from tests.helpers import dev
+from tests.helpers import FP8_GROUP, FP8_WINDOW, dev
 
 pytestmark = pytest.mark.gpu
 
@@ -26,7 +27,7 @@ TORCH = {"e4m3": torch.float8_e4m3fn, "e5m2": torch.float8_e5m2, "f16": torch.fl
          "bf16": torch.bfloat16}
 
 
-def _dot(dt, a_vals, b_vals, K=64):
+def _dot(dt, a_vals, b_vals, K=128):
     """The library's value of sum_k a_k b_k for one output element (row 0, col 0)."""
     A = torch.zeros((32, K), dtype=torch.float64)
     B = torch.zeros((K, 32), dtype=torch.float64)
@@ -44,10 +45,11 @@ def _dot(dt, a_vals, b_vals, K=64):
 
 
 @pytest.mark.parametrize("dt", ["e4m3", "e5m2"])
-def test_fp8_step_window(dt):
+def test_fp8_group_window_depth_and_rounding(dt):
+    assert FP8_WINDOW == 13
     t = 2.0 ** -13
     cases = [
-        # (a at K=1, b at K=1): result with 1 * 1 at K=0 in the same step
+        # (a at K=1, b at K=1): result with 1 * 1 at K=0, in the same group
         ((2.0 ** -6, 2.0 ** -7), 1.0 + t),                   # 13 binades below: kept
         ((2.0 ** -7, 2.0 ** -7), 1.0),                       # 14 below: dropped
         ((1.5 * 2.0 ** -7, 2.0 ** -7), 1.0),                 # between 14 and 13 below: dropped
@@ -58,14 +60,36 @@ def test_fp8_step_window(dt):
     for (x, y), want in cases:
         got = _dot(dt, {0: 1.0, 1: x}, {0: 1.0, 1: y})
         assert got == want, (dt, x, y, got, want)
-    # the window moves with the largest product of the step
+    # the window moves with the group's largest product
     big = 2.0 ** -4
     assert _dot(dt, {0: big, 1: 2.0 ** -8}, {0: 1.0, 1: 2.0 ** -9}) == big + 2.0 ** -17
     assert _dot(dt, {0: big, 1: 2.0 ** -9}, {0: 1.0, 1: 2.0 ** -9}) == big
-    # a step with no large product keeps a small one exactly
+    # a group with no large product keeps a small one exactly
     assert _dot(dt, {1: 2.0 ** -9}, {1: 2.0 ** -9}) == 2.0 ** -18
-    # the accumulator of the previous step is not in the window (K = 128: two steps)
-    got = _dot(dt, {0: 1.0, 64: 2.0 ** -9}, {0: 1.0, 64: 2.0 ** -9}, K=128)
+
+
+@pytest.mark.parametrize("dt", ["e4m3", "e5m2"])
+def test_fp8_window_covers_one_aligned_group_of_8(dt):
+    """1 at position b, 2^-16 at position p: dropped exactly when p and b lie in
+    the same aligned group of FP8_GROUP positions, in the first step or a
+    later one."""
+    assert FP8_GROUP == 8
+    small = 2.0 ** -8
+    for b in (0, 5, 13, 77, 130):
+        K = 256
+        for p in sorted({b ^ 1, (b // 8) * 8, (b // 8) * 8 + 7, (b // 8) * 8 + 8,
+                         max(0, (b // 8) * 8 - 1), b + 31, b + 64}):
+            if p == b or not 0 <= p < K:
+                continue
+            got = _dot(dt, {b: 1.0, p: small}, {b: 1.0, p: small}, K)
+            want = 1.0 if p // 8 == b // 8 else 1.0 + 2.0 ** -16
+            assert got == want, (dt, b, p, got)
+    # two small products in one group and a larger one: the group's maximum
+    # sets the window
+    got = _dot(dt, {0: 1.0, 1: 2.0 ** -8, 2: 2.0 ** -4}, {0: 1.0, 1: 2.0 ** -8, 2: 2.0 ** -4})
+    assert got == 1.0 + 2.0 ** -8
+    # the accumulator of the previous step is not in the window (K = 256: two steps)
+    got = _dot(dt, {0: 1.0, 128: 2.0 ** -9}, {0: 1.0, 128: 2.0 ** -9}, K=256)
     assert got == 1.0 + 2.0 ** -18
 
 
@@ -74,4 +98,4 @@ def test_16bit_step_keeps_fp32_precision(dt):
     for e in (12, 20, 23):
         x = 2.0 ** -(e // 2)
         y = 2.0 ** -(e - e // 2)
-        assert _dot(dt, {0: 1.0, 1: x}, {0: 1.0, 1: y}) == 1.0 + 2.0 ** -e, (dt, e)
+        assert _dot(dt, {0: 1.0, 1: x}, {0: 1.0, 1: y}, K=64) == 1.0 + 2.0 ** -e, (dt, e)

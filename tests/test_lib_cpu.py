@@ -92,7 +92,7 @@ def test_default_plans_of_the_workloads():
     assert (sq["block_m"], sq["block_n"], sq["split_k"]) == (256, 256, 1)
     assert (sq["mfma_m"], sq["mfma_n"], sq["mfma_k"]) == (16, 16, 32)
     fp8 = imm.gemm_plan(8192, 8192, 8192, "e5m2").info
-    assert (fp8["mfma_m"], fp8["mfma_n"], fp8["mfma_k"]) == (32, 32, 64)
+    assert (fp8["mfma_m"], fp8["mfma_n"], fp8["mfma_k"]) == (16, 16, 128)
     assert fp8["out_dtype"] == imm.DTYPE["bf16"]
     dec = imm.gemm_plan(1, 4096, 14336, "bf16").info
     assert dec["split_k"] > 1 and dec["block_m"] == 32
