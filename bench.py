@@ -307,7 +307,7 @@ def write_clock(counter_csv, agent_csv, lds_csv=None, out_path=CLOCK_FILE):
 
 
 TRACE_SUMMARY_FILE = os.path.join(ROOT, "profiles", "gemm_dma_square_f16_8192_kernel_trace.md")
-HEADLINE_KERNEL = "gemm_dma_kernel<0, 4, 0, 256, 256, 2, 2, false, imm::GemmArgs>"
+HEADLINE_KERNEL = "gemm_dma_kernel<0, 4, 0, 256, 256, 2, 4, 2, false, imm::GemmArgs>"
 
 
 def write_trace_summary(trace_csv, bench_json, out_path=TRACE_SUMMARY_FILE):

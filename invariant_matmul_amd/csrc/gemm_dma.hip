@@ -37,8 +37,13 @@
 // Synchronisation.  Each wave waits (vmcnt) for its own DMA of the next stage,
 // then one s_barrier makes every wave's data visible and certifies that every
 // wave has finished reading the stage about to be refilled.  The barrier sits
-// half-way through the stage's last MFMA step, so the fragment reads of the
-// next stage overlap the remaining MFMAs.
+// at the start of the stage's last MFMA k-step (fp8: half-way through its one
+// k-step), so the refill and the fragment reads of the next stage overlap the
+// remaining MFMAs.  The fp8 tiles and the 16-bit 256 x 256 tile issue their
+// LDS reads in the order the next MFMAs use them, spread between MFMAs, and
+// wait for exactly the reads each MFMA row needs, with one MFMA issued before
+// the barrier (F8Sched, M16Sched); the other tiles spread the reads of a
+// k-step evenly and wait for all of them at its start.
 //
 // Bits: the per-element chain is the same as in every other kernel of the
 // library (same instruction per input dtype, MFMA K steps in ascending k from
@@ -91,6 +96,138 @@ struct OzCursor {
       if (d - p <= 0) p = s;  // no pair left with p + q < d
     }
     return true;
+  }
+};
+
+// Issue plan of the fp8 stage (one 16x16x128 k-step per stage, fragments
+// single-buffered), for a wave tile of FM x FN blocks with RA LDS reads per A
+// block, RB per B block and DPW DMA instructions per stage.  H = FN / 2.
+//   Phase 1: the MFMAs (i, j < H), i-major.  After MFMA p (p < SP) the late
+//     B reads [late_lo(p), late_hi(p)) of this stage: the pieces of blocks
+//     j >= H, whose registers phase 2 of the previous stage freed.
+//   Then MFMA (0, H), the LDS wait and the barrier (the stage change).
+//   Phase 2: the MFMAs (i, j >= H), i-major.  Slot s follows its MFMA s and
+//     carries DMA instructions [dma_lo(s), dma_hi(s)) of stage t + NS, the
+//     early B reads [early_lo(s), early_hi(s)) of stage t + 1 (blocks j < H,
+//     free since phase 1), and, at the end of a row (s % H == H - 1), the RA
+//     reads of A block s / H of stage t + 1.
+// LDS reads complete in issue order, so each use waits until at most the
+// reads issued after the last one it needs are still in flight (capped at 15,
+// the counter field, which only waits longer).
+template <int FM, int FN, int RA, int RB, int DPW>
+struct F8Sched {
+  static constexpr int H = FN / 2;
+  static constexpr int NP = FM * H;             // MFMAs per phase
+  static constexpr int NB = H * RB;             // reads of half the B blocks
+  static constexpr int SP = NP < 16 ? NP : 16;  // slots the spread-out work covers
+  // item k of n spread over the SP slots goes to slot floor(k SP / n): slot s
+  // holds items [lo(s, n), lo(s + 1, n))
+  static constexpr int lo(int s, int n) { return s < SP ? (s * n + SP - 1) / SP : n; }
+  static constexpr int late_lo(int p) { return lo(p, NB); }
+  static constexpr int late_hi(int p) { return lo(p + 1, NB); }
+  static constexpr int early_lo(int s) { return lo(s, NB); }
+  static constexpr int early_hi(int s) { return lo(s + 1, NB); }
+  static constexpr int dma_lo(int s) { return lo(s, DPW); }
+  static constexpr int dma_hi(int s) { return lo(s + 1, DPW); }
+  static constexpr bool a_at(int s) { return s % H == H - 1; }
+  // LDS reads phase 2 issues in slots 0 .. s
+  static constexpr int reads_thru(int s) {
+    int n = 0;
+    for (int u = 0; u <= s; ++u) n += early_hi(u) - early_lo(u) + (a_at(u) ? RA : 0);
+    return n;
+  }
+  static constexpr int NR2 = reads_thru(NP - 1);
+  // phase-2 issue index of the last read of A block i, of the last early read
+  static constexpr int a_last(int i) { return reads_thru(i * H + H - 1) - 1; }
+  static constexpr int early_last() {
+    constexpr int sl = (NB - 1) * SP / NB;  // the slot of the last early read
+    return (sl > 0 ? reads_thru(sl - 1) : 0) + early_hi(sl) - early_lo(sl) - 1;
+  }
+  static constexpr int cap(int n) { return n > 15 ? 15 : n; }
+  // stage start: the early B reads and A block 0
+  static constexpr int need0() { return early_last() > a_last(0) ? early_last() : a_last(0); }
+  static constexpr int wait_start() { return cap(NR2 - 1 - need0()); }
+  // before row i of phase 1: A block i (-1: already covered)
+  static constexpr int wait_row(int i) {
+    return a_last(i) <= need0() ? -1 : cap(NR2 - 1 - a_last(i) + late_lo(i * H));
+  }
+  // before MFMA (0, H): the late reads of block H (the first RB)
+  static constexpr int wait_mid() { return cap(NB - RB); }
+  // Replays the plan over one stage with in-order completion and checks that
+  // every read has landed before the MFMA that first uses it.
+  static constexpr bool verified() {
+    // issue times: phase-2 reads of the previous stage 0 .. NR2 - 1, then the
+    // late reads of this stage NR2 .. NR2 + NB - 1; `done` reads have landed
+    int issued = NR2, done = 0;
+    auto wait = [&](int n) {
+      if (issued - done > n) done = issued - n;
+    };
+    wait(wait_start());
+    if (early_last() >= done) return false;
+    for (int p = 0; p < NP; ++p) {
+      const int i = p / H;
+      if (p % H == 0 && i > 0) {
+        if (wait_row(i) >= 0) wait(wait_row(i));
+        if (a_last(i) >= done) return false;
+      }
+      if (p == 0 && a_last(0) >= done) return false;
+      issued += late_hi(p) - late_lo(p);
+    }
+    wait(wait_mid());
+    return NR2 + RB - 1 < done;
+  }
+};
+
+// Issue plan of the 16-bit stage: two 16x16x32 k-steps per stage on
+// double-buffered fragments, FM x FN blocks per wave, RA LDS reads per A block
+// and RB per B block, DPW DMA instructions per stage.  The reads of one
+// k-step go out B blocks first, then A blocks 0 .. FM-1: the first row of
+// MFMAs needs every B block and A block 0, row i only A block i more.
+//   k-step 0: the MFMAs on F0, i-major; after MFMA p the reads
+//     [lo0(p), lo0(p + 1)) of k-step 1 into F1, spread over the first SW0
+//     MFMAs so that the last of them lands before the stage change.
+//   Then MFMA 0 of k-step 1, the LDS wait and the barrier.
+//   k-step 1: MFMAs 1 .. NM-1 on F1; slot s after MFMA s carries the DMA
+//     instructions [dlo(s), dlo(s + 1)) of stage t + NS and the reads
+//     [lo1(s), lo1(s + 1)) of k-step 0 of stage t + 1 into F0.
+// As in F8Sched, each use waits for exactly the reads it needs.
+template <int FM, int FN, int RA, int RB, int DPW>
+struct M16Sched {
+  static constexpr int NM = FM * FN;           // MFMAs per k-step
+  static constexpr int NBR = FN * RB;          // B reads per k-step (issued first)
+  static constexpr int NR = NBR + FM * RA;     // reads per k-step
+  static constexpr int SW0 = NM > 4 ? NM - NM / 4 : NM;
+  static constexpr int SW1 = NM - 1 > 3 ? (NM - 1) - (NM - 1) / 4 : NM - 1;
+  static constexpr int spread(int s, int n, int w) { return s < w ? (s * n + w - 1) / w : n; }
+  static constexpr int lo0(int p) { return spread(p, NR, SW0); }
+  static constexpr int lo1(int s) { return spread(s, NR, SW1); }
+  static constexpr int dlo(int s) { return spread(s, DPW, SW1); }
+  static constexpr int cap(int n) { return n > 15 ? 15 : n; }
+  static constexpr int a_last(int i) { return NBR + (i + 1) * RA - 1; }  // in a k-step's read order
+  // start of either k-step: its B reads and A block 0 (nothing issued since)
+  static constexpr int wait_start() { return cap(NR - 1 - a_last(0)); }
+  // before row i of k-step 0: A block i of F0, with the F1 reads issued so far
+  static constexpr int wait_row(int i) { return cap(NR - 1 - a_last(i) + lo0(i * FN)); }
+  static constexpr bool verified() {
+    if (SW1 < 1 || lo0(SW0) != NR || lo1(SW1) != NR || dlo(SW1) != DPW) return false;
+    // k-step 0: F0's reads 0 .. NR-1 issued, then F1's NR .. 2NR-1 interleaved
+    int issued = NR, done = 0;
+    auto wait = [&](int n) {
+      if (issued - done > n) done = issued - n;
+    };
+    wait(wait_start());
+    if (a_last(0) >= done) return false;
+    for (int p = 0; p < NM; ++p) {
+      const int i = p / FN;
+      if (p % FN == 0 && i > 0) {
+        wait(wait_row(i));
+        if (a_last(i) >= done) return false;
+      }
+      issued += lo0(p + 1) - lo0(p);
+    }
+    // k-step 1 start: F1's B reads and A block 0
+    wait(wait_start());
+    return NR + a_last(0) < done;
   }
 };
 
@@ -149,22 +286,23 @@ __device__ __forceinline__ i32x2 tr8_rows(unsigned p0, int rows) {
   }
 }
 
-// TBM x TBN tile of C per workgroup of WM x (TBN / 64) waves; NS stages in
-// the ring.
-//   256 x 256, WM = 2, NS = 2: the large tile (wave tile 128 x 64);
-//   128 x 256, WM = 2, NS = 3: the half-height tile (wave tile 64 x 64) for
-//     grids that 256 x 256 tiles would leave under-filled;
-//   64 x 256 / 32 x 256, WM = 1, NS = 4: short tiles for reduction-dominated
-//     shapes (wave tile 64 x 64 / 32 x 64), where the time is the stream of B;
-//   64 x 64 / 32 x 64, WM = 2, NS = 8 / 10: narrow tiles (16-bit inputs) for
+// TBM x TBN tile of C per workgroup of WM x WN waves; NS stages in the ring.
+//   256 x 256, WM = 2, WN = 4, NS = 2: the large tile (wave tile 128 x 64);
+//   128 x 256, WM = 2, WN = 4, NS = 3: the half-height tile (wave tile
+//     64 x 64) for grids that 256 x 256 tiles would leave under-filled;
+//   64 x 256 / 32 x 256, WM = 1, WN = 4, NS = 4: short tiles for
+//     reduction-dominated shapes (wave tile 64 x 64 / 32 x 64), where the time
+//     is the stream of B;
+//   64 x 64 / 32 x 64, WM = 2, WN = 1, NS = 8 / 10: narrow tiles (16-bit inputs) for
 //     small M, where N / 256 column tiles would leave most compute units
 //     idle: four times the workgroups, each with a deep ring (about 120 KB in
 //     flight) to keep its share of B streaming.
 // Two workgroups share a CU when their rings fit in half the LDS; the
-// register budget then has to allow two waves per SIMD.
-template <int TBM, int TBN, int WM, int NS>
+// register budget then has to allow two waves per SIMD.  A four-wave
+// workgroup alone on its CU has one wave per SIMD and the whole register file.
+template <int TBM, int TBN, int WM, int WN, int NS>
 constexpr int waves_per_simd() {
-  return NS * (TBM + TBN) * SKB <= 80 * 1024 || WM == 2 ? 2 : 1;
+  return WM * WN == 4 && NS * (TBM + TBN) * SKB > 80 * 1024 ? 1 : 2;
 }
 
 // BT: B is given transposed, as [N, K] row-major (the weight layout of a
@@ -172,15 +310,13 @@ constexpr int waves_per_simd() {
 // staged and read exactly like A (128-byte rows, ds_read_b128); the matrix
 // core sees the same values in the same K order, so the bits are those of
 // the [K, N] layout.
-template <int IN, int OUT, int MODE, int TBM, int TBN, int WM, int NS, bool BT, class ARGS>
-__global__ __launch_bounds__(WM * TBN, (waves_per_simd<TBM, TBN, WM, NS>())) void gemm_dma_kernel(ARGS g) {
+template <int IN, int OUT, int MODE, int TBM, int TBN, int WM, int WN, int NS, bool BT, class ARGS>
+__global__ __launch_bounds__(WM * WN * 64, (waves_per_simd<TBM, TBN, WM, WN, NS>())) void gemm_dma_kernel(ARGS g) {
   using T = InT<IN>;
   constexpr int EB = T::EB;
-  static_assert(TBN % 64 == 0, "tile width");
-  constexpr int WN = TBN / 64;
   constexpr int WAVES = WM * WN;
   constexpr int WTM = TBM / WM;              // wave tile rows
-  constexpr int WTN = TBN / WN;              // wave tile columns (64)
+  constexpr int WTN = TBN / WN;              // wave tile columns
   // 16-bit inputs: the 16x16x32 step; fp8: the 16x16x128 step; int8 and the
   // exact Ozaki chains (whose bits no instruction changes): the 32x32 step
   constexpr bool M16 = EB == 2 && MODE != MODE_OZAKI;
@@ -217,6 +353,9 @@ __global__ __launch_bounds__(WM * TBN, (waves_per_simd<TBM, TBN, WM, NS>())) voi
   // fp8 (one 128-byte k-step per stage): single-buffered fragments; the
   // other paths alternate two fragment sets over an even number of k-steps
   static_assert(F8S ? KS == 1 : KS % 2 == 0, "k-steps per stage");
+  // wave tiles are 64 columns wide (a 128-wide fp8 wave tile, one wave per
+  // SIMD on the 256 x 256 tile, compiles too but measured 6-13 % slower)
+  static_assert(WN * WTN == TBN && WTN == 64, "wave tile width");
 
   __shared__ __attribute__((aligned(1024))) char lds[LDS_BYTES];
   // LDS offsets of the A and B blocks of stage t.
@@ -536,6 +675,12 @@ __global__ __launch_bounds__(WM * TBN, (waves_per_simd<TBM, TBN, WM, NS>())) voi
     __builtin_amdgcn_s_waitcnt(lgkmcnt_imm(0));
     fence();
   };
+  // wait until at most N LDS reads are in flight (N a compile-time constant)
+  auto lgkm_wait = [&](auto N) {
+    fence();
+    __builtin_amdgcn_s_waitcnt(lgkmcnt_imm(decltype(N)::value));
+    fence();
+  };
 
   AccT acc[FM][FN];
 #pragma unroll
@@ -634,6 +779,84 @@ __global__ __launch_bounds__(WM * TBN, (waves_per_simd<TBM, TBN, WM, NS>())) voi
   constexpr int WAIT_FIRST = (NS - 1) * DPW;
   constexpr int WAIT_NEXT = (NS - 2) * DPW;
   Frag<IN, FM, FN> F0, F1;
+
+  // fp8: fragment reads with compile-time block indices, so that the block
+  // offsets are immediates and every wait is placed by the schedule
+  // (F8Sched).  A (and B given transposed) rows: two 16-byte halves per lane
+  // at f8_row[f] + (block row) * SKB; B in the [K, N] layout: four
+  // transposing reads of 8 K rows per block.
+  constexpr int RA8 = F8S ? NRA / FM : 1, RB8 = F8S ? NRB / FN : 1;
+  unsigned f8_arow[2], f8_brow[2];
+#pragma unroll
+  for (int f = 0; f < 2; ++f) {
+    const unsigned sl = (unsigned)((((2 * hq + f) ^ asw) << 4));
+    f8_arow[f] = lds_addr + (unsigned)((wm * WTM + lb) * SKB) + sl;
+    f8_brow[f] = lds_addr + (unsigned)((wn * WTN + lb) * SKB) + sl;
+  }
+  auto f8_read_a = [&](auto I, int as) {  // both halves of A block I
+    constexpr int i = decltype(I)::value;
+    static_for<0, 2>([&](auto Fh) {
+      constexpr int f = decltype(Fh)::value;
+      const i32x4 v = ds_read_b128_at<i * BLK * SKB>(f8_arow[f] + as);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) F0.a[i][4 * f + e] = v[e];
+    });
+  };
+  auto f8_read_b = [&](auto X, int bs) {  // B read X: block X / RB8, piece X % RB8
+    constexpr int x = decltype(X)::value;
+    constexpr int j = x / RB8, r = x % RB8;
+    if constexpr (BT) {
+      const i32x4 v = ds_read_b128_at<j * BLK * SKB>(f8_brow[r] + bs);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) F0.b[j][4 * r + e] = v[e];
+    } else {
+      const i32x2 v = ds_read_tr8_b64<8 * r * BROW>(lds_addr + b_rd[j] + bs);
+      F0.b[j][2 * r] = v[0];
+      F0.b[j][2 * r + 1] = v[1];
+    }
+  };
+  // before stage 0: the B blocks j < FN / 2 and every A block, all landed
+  auto f8_prologue_reads = [&]() {
+    if constexpr (F8S) {
+      static_for<0, (FN / 2) * RB8>([&](auto X) { f8_read_b(X, b_slot(0)); });
+      static_for<0, FM>([&](auto I) { f8_read_a(I, a_slot(0)); });
+      lds_wait();
+    }
+  };
+
+  // 16-bit inputs: the same immediate-offset reads for the 16x16x32 steps
+  // (M16Sched).  Read X of a k-step: X < NRB the B reads (transposing reads of
+  // 4 K rows, two per block, or one 16-byte read per block given
+  // transposed), then one 16-byte read per A block at m16_arow[ks] +
+  // (block row) * SKB.
+  // Used on the 256 x 256 tile: there it measured 1.7 % faster than the
+  // evenly spread k-steps below (8192^3 fp16); on the 128 x 256 tile it
+  // measured about 1 % slower, so the smaller tiles keep those.
+  constexpr bool M16S = M16 && FM == 8;
+  constexpr int RA16 = M16 ? NRA / FM : 1, RB16 = M16 ? NRB / FN : 1;
+  unsigned m16_arow[2], m16_brow[2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    const unsigned sl = (unsigned)(((((KSTEP / 16) * ks + hq) ^ asw) << 4));
+    m16_arow[ks] = lds_addr + (unsigned)((wm * WTM + lb) * SKB) + sl;
+    m16_brow[ks] = lds_addr + (unsigned)((wn * WTN + lb) * SKB) + sl;
+  }
+  auto m16_read = [&](auto KS_, auto X, Frag<IN, FM, FN>& F, int as, int bs) {
+    constexpr int ks = decltype(KS_)::value, x = decltype(X)::value;
+    if constexpr (x < NRB) {
+      constexpr int j = x / RB16, r = x % RB16;
+      if constexpr (BT) {
+        F.b[j] = ds_read_b128_at<j * BLK * SKB>(m16_brow[ks] + bs);
+      } else {
+        const i32x2 v = ds_read_tr16_b64<(ks * (KSTEP / 2) + 4 * r) * BROW>(lds_addr + b_rd[j] + bs);
+        F.b[j][2 * r] = v[0];
+        F.b[j][2 * r + 1] = v[1];
+      }
+    } else {
+      constexpr int i = x - NRB;
+      F.a[i] = ds_read_b128_at<i * BLK * SKB>(m16_arow[ks] + as);
+    }
+  };
   if (nt > 0) {
     for (int p = 0; p < NS; ++p) {
       const StageSrc q = (MODE == MODE_OZAKI || PER_TILE) ? next_src() : stage_src(p);
@@ -643,8 +866,18 @@ __global__ __launch_bounds__(WM * TBN, (waves_per_simd<TBM, TBN, WM, NS>())) voi
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(WAIT_FIRST));
     __builtin_amdgcn_s_barrier();
     fence();
+    if constexpr (F8S) {
+      f8_prologue_reads();
+    } else if constexpr (M16S) {
+      // k-step 0 of stage 0 into F0, all landed
+      static_for<0, NREAD>([&](auto X) {
+        m16_read(std::integral_constant<int, 0>{}, X, F0, a_slot(0), b_slot(0));
+      });
+      lds_wait();
+    } else {
 #pragma unroll
-    for (int x = 0; x < NREAD; ++x) read_one(F0, a_slot(0), b_slot(0), 0, x);
+      for (int x = 0; x < NREAD; ++x) read_one(F0, a_slot(0), b_slot(0), 0, x);
+    }
   }
 
   // The stage change sits at the start of the last k-step of stage t: once a
@@ -693,33 +926,38 @@ __global__ __launch_bounds__(WM * TBN, (waves_per_simd<TBM, TBN, WM, NS>())) voi
   };
 
   // fp8: one k-step per stage on single-buffered fragments (F0).  Two
-  // fragment sets of the 16x16x128 step do not fit beside the accumulators at
-  // two waves per SIMD, so the reads of stage t+1 go into the registers the
-  // MFMAs of stage t free, ordered so that each is read long before its first
-  // use.  Phase 1 runs the blocks (i, j) with j < FN/2, phase 2 those with
-  // j >= FN/2, both i-major.  Between the phases sits the stage change: all of
-  // this wave's reads of stage t landed long before (full LDS wait), its DMA
-  // of stage t+1 has landed, and one barrier certifies both for every wave.
-  // Then the B blocks j < FN/2 of stage t+1 are read (first used a whole
-  // phase later), phase 2 runs with the refill of stage t's slot (stage t+NS)
-  // spread over its MFMAs and A block i of stage t+1 read after its last MFMA
-  // (i, FN-1) (first used (FM-1) FN/2 MFMAs later), and the B blocks
-  // j >= FN/2 are read last (first used in phase 2 of stage t+1).  At the
-  // start of stage t+1 a wave waits for all but those last B reads.
-  constexpr int F8_LATE = F8S ? (FN / 2) * (NRB / FN) : 0;  // reads left in flight at a stage start
-  auto kstep_f8 = [&](int t) {
+  // fragment sets of the 16x16x128 step do not fit beside the accumulators, so
+  // the reads of stage t+1 go into the registers the MFMAs of stage t free, in
+  // the order F8Sched lays out: phase 1 runs the blocks (i, j < FN/2) while
+  // the B blocks j >= FN/2 of stage t are read; MFMA (0, FN/2) runs across
+  // the stage change (all of this wave's reads of stage t landed, its DMA of
+  // stage t+1 landed, one barrier for every wave); phase 2 runs the blocks
+  // (i, j >= FN/2) with the refill of stage t's slot (stage t+NS) and the
+  // reads of B blocks j < FN/2 and of every A block of stage t+1 in between.
+  // Every memory instruction sits between two MFMAs, and each wait is for
+  // exactly the reads the next MFMA needs, so one wave per SIMD can keep its
+  // matrix unit fed.
+  auto f8_stage = [&](int t) {
     if constexpr (F8S) {
-      constexpr int H = FN / 2;
-      constexpr int RA = NRA / FM, RB = NRB / FN;  // fragment reads per A block, per B block
-      static_assert(RA * FM == NRA && RB * FN == NRB && H * 2 == FN, "fragment reads");
-      static_assert(F8_LATE <= 15, "lgkmcnt field");
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < H; ++j) {
-          mfma_x(F0, i * FN + j);
-          fence();
-        }
+      using S = F8Sched<FM, FN, RA8, RB8, DPW>;
+      static_assert(RA8 * FM == NRA && RB8 * FN == NRB && S::H * 2 == FN, "fragment reads");
+      static_assert(S::verified(), "fp8 read schedule");
+      constexpr int H = S::H;
+      lgkm_wait(std::integral_constant<int, S::wait_start()>{});
+      const int bs = b_slot(t);
+      static_for<0, S::NP>([&](auto P) {
+        constexpr int p = decltype(P)::value;
+        constexpr int i = p / H, j = p % H;
+        if constexpr (j == 0 && i > 0 && S::wait_row(i) >= 0)
+          lgkm_wait(std::integral_constant<int, S::wait_row(i)>{});
+        mfma_x(F0, i * FN + j);
+        static_for<S::late_lo(p), S::late_hi(p)>([&](auto L) {
+          f8_read_b(std::integral_constant<int, H * RB8 + decltype(L)::value>{}, bs);
+        });
+        fence();
+      });
+      lgkm_wait(std::integral_constant<int, S::wait_mid()>{});
+      mfma_x(F0, H);
       lds_wait();
       stage_change();
       StageSrc q;
@@ -727,29 +965,67 @@ __global__ __launch_bounds__(WM * TBN, (waves_per_simd<TBM, TBN, WM, NS>())) voi
         q = next_src();
       else
         q = stage_src(t + NS);
-      const int as = a_slot(t + 1), bs = b_slot(t + 1);
-#pragma unroll
-      for (int y = 0; y < H * RB; ++y) read_one(F0, as, bs, 0, NRA + y);
-      fence();
+      const int as1 = a_slot(t + 1), bs1 = b_slot(t + 1);
       __builtin_amdgcn_s_setprio(3);
-      constexpr int NM2 = FM * H;  // MFMAs of phase 2, over which the refill is spread
-#pragma unroll
-      for (int i = 0; i < FM; ++i) {
-#pragma unroll
-        for (int j = H; j < FN; ++j) {
-          mfma_x(F0, i * FN + j);
-          const int c = i * H + (j - H);
-#pragma unroll
-          for (int y = c * DPW / NM2; y < (c + 1) * DPW / NM2; ++y) dma_one(q, t + NS, y);
+      static_for<0, S::NP>([&](auto Sl) {
+        constexpr int s = decltype(Sl)::value;
+        static_for<S::dma_lo(s), S::dma_hi(s)>([&](auto Y) { dma_one(q, t + NS, decltype(Y)::value); });
+        static_for<S::early_lo(s), S::early_hi(s)>([&](auto E) { f8_read_b(E, bs1); });
+        if constexpr (S::a_at(s)) f8_read_a(std::integral_constant<int, s / H>{}, as1);
+        fence();
+        if constexpr (s + 1 < S::NP) {
+          constexpr int c = s + 1;
+          mfma_x(F0, (c / H) * FN + H + c % H);
           fence();
         }
-#pragma unroll
-        for (int y = 0; y < RA; ++y) read_one(F0, as, bs, 0, i * RA + y);
+      });
+      __builtin_amdgcn_s_setprio(0);
+    }
+  };
+
+  // 16-bit inputs: the two k-steps of a stage in the order M16Sched lays out:
+  // k-step 0 on F0 while k-step 1 of the stage is read into F1 (B blocks
+  // first, front-loaded); MFMA 0 of k-step 1 runs across the stage change;
+  // the rest of k-step 1 carries the refill of stage t's slot (stage t+NS)
+  // and the reads of k-step 0 of stage t+1 into F0.
+  auto m16_stage = [&](int t) {
+    if constexpr (M16S) {
+      using S = M16Sched<FM, FN, RA16, RB16, DPW>;
+      static_assert(KS == 2 && RA16 * FM == NRA && RB16 * FN == NRB, "16-bit k-steps");
+      static_assert(S::verified(), "16-bit read schedule");
+      const int as = a_slot(t), bs = b_slot(t);
+      lgkm_wait(std::integral_constant<int, S::wait_start()>{});
+      static_for<0, S::NM>([&](auto P) {
+        constexpr int p = decltype(P)::value;
+        constexpr int i = p / FN;
+        if constexpr (p % FN == 0 && i > 0) lgkm_wait(std::integral_constant<int, S::wait_row(i)>{});
+        mfma_x(F0, p);
+        static_for<S::lo0(p), S::lo0(p + 1)>([&](auto X) {
+          m16_read(std::integral_constant<int, 1>{}, X, F1, as, bs);
+        });
         fence();
-      }
-#pragma unroll
-      for (int y = H * RB; y < NRB; ++y) read_one(F0, as, bs, 0, NRA + y);
-      fence();
+      });
+      lgkm_wait(std::integral_constant<int, S::wait_start()>{});
+      mfma_x(F1, 0);
+      lds_wait();
+      stage_change();
+      StageSrc q;
+      if constexpr (PER_TILE)
+        q = next_src();
+      else
+        q = stage_src(t + NS);
+      const int as1 = a_slot(t + 1), bs1 = b_slot(t + 1);
+      __builtin_amdgcn_s_setprio(3);
+      static_for<0, S::NM - 1>([&](auto Sl) {
+        constexpr int s = decltype(Sl)::value;
+        static_for<S::dlo(s), S::dlo(s + 1)>([&](auto Y) { dma_one(q, t + NS, decltype(Y)::value); });
+        static_for<S::lo1(s), S::lo1(s + 1)>([&](auto X) {
+          m16_read(std::integral_constant<int, 0>{}, X, F0, as1, bs1);
+        });
+        fence();
+        mfma_x(F1, s + 1);
+        fence();
+      });
       __builtin_amdgcn_s_setprio(0);
     }
   };
@@ -763,11 +1039,9 @@ __global__ __launch_bounds__(WM * TBN, (waves_per_simd<TBM, TBN, WM, NS>())) voi
   int64_t cur_m0 = m0, cur_n0 = n0;
   for (int t = 0; t < nt; ++t) {
     if constexpr (F8S) {
-      // all fragment reads of stage t but the last B blocks have landed
-      fence();
-      __builtin_amdgcn_s_waitcnt(lgkmcnt_imm(F8_LATE));
-      fence();
-      kstep_f8(t);
+      f8_stage(t);
+    } else if constexpr (M16S) {
+      m16_stage(t);
     } else {
 #pragma unroll
       for (int ks = 0; ks + 1 < KS; ++ks) {
@@ -809,20 +1083,20 @@ __global__ __launch_bounds__(WM * TBN, (waves_per_simd<TBM, TBN, WM, NS>())) voi
   if constexpr (!PER_TILE) store_tile(m0, n0);
 }
 
-template <int IN, int TBM, int TBN, int WM, int NS, bool BT>
+template <int IN, int TBM, int TBN, int WM, int WN, int NS, bool BT>
 hipError_t launch_cfg(const gemm_plan_s& p, const GemmArgs& a, bool slice, hipStream_t s) {
-  const dim3 grid((unsigned)a.grid), block(WM * TBN);
+  const dim3 grid((unsigned)a.grid), block(WM * WN * 64);
   if (slice)
-    hipLaunchKernelGGL((gemm_dma_kernel<IN, GEMM_F32, MODE_SLICE, TBM, TBN, WM, NS, BT, GemmArgs>),
+    hipLaunchKernelGGL((gemm_dma_kernel<IN, GEMM_F32, MODE_SLICE, TBM, TBN, WM, WN, NS, BT, GemmArgs>),
                        grid, block, 0, s, a);
   else if (p.out == GEMM_F32)
-    hipLaunchKernelGGL((gemm_dma_kernel<IN, GEMM_F32, MODE_STORE, TBM, TBN, WM, NS, BT, GemmArgs>),
+    hipLaunchKernelGGL((gemm_dma_kernel<IN, GEMM_F32, MODE_STORE, TBM, TBN, WM, WN, NS, BT, GemmArgs>),
                        grid, block, 0, s, a);
   else if (p.out == GEMM_F16)
-    hipLaunchKernelGGL((gemm_dma_kernel<IN, GEMM_F16, MODE_STORE, TBM, TBN, WM, NS, BT, GemmArgs>),
+    hipLaunchKernelGGL((gemm_dma_kernel<IN, GEMM_F16, MODE_STORE, TBM, TBN, WM, WN, NS, BT, GemmArgs>),
                        grid, block, 0, s, a);
   else
-    hipLaunchKernelGGL((gemm_dma_kernel<IN, GEMM_BF16, MODE_STORE, TBM, TBN, WM, NS, BT, GemmArgs>),
+    hipLaunchKernelGGL((gemm_dma_kernel<IN, GEMM_BF16, MODE_STORE, TBM, TBN, WM, WN, NS, BT, GemmArgs>),
                        grid, block, 0, s, a);
   return hipGetLastError();
 }
@@ -832,13 +1106,13 @@ template <int IN, bool BT>
 hipError_t launch_persist_in(const gemm_plan_s& p, const PersistArgs& a, hipStream_t s) {
   const dim3 grid((unsigned)a.wgs), block(512);
   if (p.out == GEMM_F32)
-    hipLaunchKernelGGL((gemm_dma_kernel<IN, GEMM_F32, MODE_PERSIST, 256, WIDE_TBN, 2, 2, BT,
+    hipLaunchKernelGGL((gemm_dma_kernel<IN, GEMM_F32, MODE_PERSIST, 256, WIDE_TBN, 2, 4, 2, BT,
                                         PersistArgs>), grid, block, 0, s, a);
   else if (p.out == GEMM_F16)
-    hipLaunchKernelGGL((gemm_dma_kernel<IN, GEMM_F16, MODE_PERSIST, 256, WIDE_TBN, 2, 2, BT,
+    hipLaunchKernelGGL((gemm_dma_kernel<IN, GEMM_F16, MODE_PERSIST, 256, WIDE_TBN, 2, 4, 2, BT,
                                         PersistArgs>), grid, block, 0, s, a);
   else
-    hipLaunchKernelGGL((gemm_dma_kernel<IN, GEMM_BF16, MODE_PERSIST, 256, WIDE_TBN, 2, 2, BT,
+    hipLaunchKernelGGL((gemm_dma_kernel<IN, GEMM_BF16, MODE_PERSIST, 256, WIDE_TBN, 2, 4, 2, BT,
                                         PersistArgs>), grid, block, 0, s, a);
   return hipGetLastError();
 }
@@ -851,16 +1125,16 @@ hipError_t launch_persist_bt(const gemm_plan_s& p, const PersistArgs& a, hipStre
 template <int IN, bool BT>
 hipError_t launch_tiles(const gemm_plan_s& p, int tile, const GemmArgs& a, bool slice, hipStream_t s) {
   switch (tile) {
-    case GEMM_TILE_256x256: return launch_cfg<IN, 256, 256, 2, 2, BT>(p, a, slice, s);
-    case GEMM_TILE_128x256: return launch_cfg<IN, 128, 256, 2, 3, BT>(p, a, slice, s);
-    case GEMM_TILE_64x256: return launch_cfg<IN, 64, 256, 1, 4, BT>(p, a, slice, s);
-    case GEMM_TILE_32x256: return launch_cfg<IN, 32, 256, 1, 4, BT>(p, a, slice, s);
+    case GEMM_TILE_256x256: return launch_cfg<IN, 256, 256, 2, 4, 2, BT>(p, a, slice, s);
+    case GEMM_TILE_128x256: return launch_cfg<IN, 128, 256, 2, 4, 3, BT>(p, a, slice, s);
+    case GEMM_TILE_64x256: return launch_cfg<IN, 64, 256, 1, 4, 4, BT>(p, a, slice, s);
+    case GEMM_TILE_32x256: return launch_cfg<IN, 32, 256, 1, 4, 4, BT>(p, a, slice, s);
     default: break;
   }
   if constexpr (InT<IN>::EB == 2) {  // the narrow tiles take 16-bit inputs only
     switch (tile) {
-      case GEMM_TILE_64x64: return launch_cfg<IN, 64, 64, 2, 8, BT>(p, a, slice, s);
-      case GEMM_TILE_32x64: return launch_cfg<IN, 32, 64, 2, 10, BT>(p, a, slice, s);
+      case GEMM_TILE_64x64: return launch_cfg<IN, 64, 64, 2, 1, 8, BT>(p, a, slice, s);
+      case GEMM_TILE_32x64: return launch_cfg<IN, 32, 64, 2, 1, 10, BT>(p, a, slice, s);
       default: break;
     }
   }
@@ -886,13 +1160,13 @@ hipError_t launch_ozaki_gemm(int type2, const OzGemmArgs& a, hipStream_t s) {
   // measured 7-10 % faster than 2 and 3 stages.
   const dim3 grid((unsigned)a.grid);
   if (type2 == GEMM_BF16)
-    hipLaunchKernelGGL((gemm_dma_kernel<GEMM_BF16, GEMM_F32, MODE_OZAKI, 128, WIDE_TBN, 2, 3, false,
+    hipLaunchKernelGGL((gemm_dma_kernel<GEMM_BF16, GEMM_F32, MODE_OZAKI, 128, WIDE_TBN, 2, 4, 3, false,
                                         OzGemmArgs>), grid, dim3(512), 0, s, a);
   else if (type2 == GEMM_F8_E4M3)
-    hipLaunchKernelGGL((gemm_dma_kernel<GEMM_F8_E4M3, GEMM_F32, MODE_OZAKI, 64, WIDE_TBN, 1, 4, false,
+    hipLaunchKernelGGL((gemm_dma_kernel<GEMM_F8_E4M3, GEMM_F32, MODE_OZAKI, 64, WIDE_TBN, 1, 4, 4, false,
                                         OzGemmArgs>), grid, dim3(256), 0, s, a);
   else if (type2 == GEMM_I8)
-    hipLaunchKernelGGL((gemm_dma_kernel<GEMM_I8, GEMM_F32, MODE_OZAKI, 128, WIDE_TBN, 2, 3, false,
+    hipLaunchKernelGGL((gemm_dma_kernel<GEMM_I8, GEMM_F32, MODE_OZAKI, 128, WIDE_TBN, 2, 4, 3, false,
                                         OzGemmArgs>), grid, dim3(512), 0, s, a);
   else
     return hipErrorInvalidValue;

@@ -5,6 +5,7 @@
 #pragma once
 
 #include <type_traits>
+#include <utility>
 
 #include "imm_internal.h"
 
@@ -153,6 +154,26 @@ __device__ __forceinline__ i32x2 ds_read_tr8_b64(unsigned addr) {
   i32x2 v;
   asm volatile("ds_read_b64_tr_b8 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "n"(OFF));
   return v;
+}
+// A plain 16-byte LDS read issued the same way, for schedules that place every
+// LDS wait themselves.
+template <int OFF>
+__device__ __forceinline__ i32x4 ds_read_b128_at(unsigned addr) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds_read offset field");
+  i32x4 v;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "n"(OFF));
+  return v;
+}
+
+// Calls f(std::integral_constant<int, I>) for I = LO .. HI-1 in order, so that
+// the body can use I in constant expressions (immediate offsets, wait counts).
+template <int LO, class F, int... I>
+__device__ __forceinline__ void static_for_impl(F& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, LO + I>{}), ...);
+}
+template <int LO, int HI, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (HI > LO) static_for_impl<LO>(f, std::make_integer_sequence<int, HI - LO>{});
 }
 
 // s_waitcnt immediate that waits until at most `n` vector-memory operations

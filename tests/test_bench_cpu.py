@@ -15,7 +15,7 @@ import bench  # noqa: E402
 
 COUNTER_FIELDS = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value",
                   "Start_Timestamp", "End_Timestamp"]
-HEADLINE = "void imm::(anonymous namespace)::gemm_dma_kernel<0, 4, 0, 256, 2, 2, false>(imm::GemmArgs)"
+HEADLINE = "void imm::(anonymous namespace)::gemm_dma_kernel<0, 4, 0, 256, 256, 2, 4, 2, false, imm::GemmArgs>(imm::GemmArgs)"
 BLAS = "Cijk_Ailk_Bljk_HHS_BH_MT256x256x64_MI16x16x1"
 COPY = "__amd_rocclr_copyBuffer"
 
@@ -128,7 +128,7 @@ def test_clock_without_the_headline_kernel_is_an_error(tmp_path):
 
 PARTIAL = "void imm::(anonymous namespace)::gemm_tile_kernel<1, 4, 32, 128, 1, 4, true>(imm::GemmArgs)"
 REDUCE = "void imm::(anonymous namespace)::splitk_reduce_kernel<4>(imm::ReduceArgs)"
-HK_PARTIAL = "void imm::(anonymous namespace)::gemm_dma_kernel<0, 4, 1, 128, 2, 3, false, imm::GemmArgs>(imm::GemmArgs)"
+HK_PARTIAL = "void imm::(anonymous namespace)::gemm_dma_kernel<0, 4, 1, 128, 256, 2, 4, 3, false, imm::GemmArgs>(imm::GemmArgs)"
 
 
 def _stream_dispatches(counter, copy_value, per_case):
