@@ -26,7 +26,7 @@ __all__ = [
     "gemm_plan_destroy", "gemm_status_string", "gemm_last_hip_error", "mm", "out_torch_dtype",
     "lib", "LIB_PATH",
     "DTYPE", "TILE", "STATUS", "EXPORTED_SYMBOLS", "PLAN_B_TRANSPOSED", "PLAN_PERSISTENT",
-    "PLAN_TILE_BY_M",
+    "PLAN_TILE_BY_M", "PLAN_FP8_FP32_ACCUM",
     "OzakiPlan", "ozaki_plan", "ozaki_plan_info", "ozaki_workspace_size", "ozaki_split",
     "ozaki_multiply", "ozaki_run", "ozaki_mm",
 ]
@@ -41,6 +41,7 @@ TILE = {"default": 0, "256x256": 1, "128x128": 2, "32x128": 3, "256x256_rs": 4, 
 PLAN_B_TRANSPOSED = 1
 PLAN_PERSISTENT = 2
 PLAN_TILE_BY_M = 4
+PLAN_FP8_FP32_ACCUM = 8  # fp8 widened to fp16: the fp32 bound for every K (DMA tiles only)
 # GEMM_NOALLOC_WORKSPACE_BYTES: the largest workspace gemm_splitk_run_noalloc serves
 NOALLOC_WORKSPACE_BYTES = 64 << 20
 EXPORTED_SYMBOLS = (

@@ -50,6 +50,23 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
+# Device assembly of the DMA kernels, written beside the objects: the tests
+# check in it that no instruction touches a register an inline-assembly LDS
+# read (whose completion the compiler does not track) will still write.
+DMA_ASM = os.path.join(BUILD_DIR, "gemm_dma.gfx950.s")
+
+
+def _device_asm(src: str, out: str, verbose: bool) -> str:
+    cmd = [_hipcc(), *HIP_FLAGS, "-x", "hip", "-S", "--offload-device-only",
+           os.path.join(CSRC, src), "-o", out]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc -S failed for {src}:\n{r.stdout}\n{r.stderr}")
+    return out
+
+
 def _link(objs, out: str, verbose: bool) -> None:
     tmp = out + ".tmp%d" % os.getpid()
     cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
@@ -67,8 +84,10 @@ def build(verbose: bool = False) -> str:
     probe library); returns the GEMM library's path."""
     os.makedirs(BUILD_DIR, exist_ok=True)
     srcs = SOURCES + PROBE_SOURCES
-    with concurrent.futures.ThreadPoolExecutor(max_workers=len(srcs)) as ex:
+    with concurrent.futures.ThreadPoolExecutor(max_workers=len(srcs) + 1) as ex:
+        asm = ex.submit(_device_asm, "gemm_dma.hip", DMA_ASM, verbose)
         objs = dict(zip(srcs, ex.map(lambda s: _compile(s, verbose), srcs)))
+        asm.result()
     _link([objs[s] for s in SOURCES], LIB, verbose)
     _link([objs[s] for s in PROBE_SOURCES], PROBE_LIB, verbose)
     return LIB

@@ -159,11 +159,12 @@ bool dma_offsets_fit(int tile, int64_t N, int64_t K, int eb, bool b_trans) {
 }
 
 // A DMA tile whose offsets would overflow falls back to a register-staged
-// tile of the same bits (none exists for transposed B: -1).
-int checked_tile(int tile, int64_t N, int64_t K, int eb, bool b_trans) {
-  if (!is_dma_tile(tile)) return b_trans ? -1 : tile;
+// tile of the same bits; plans that only the DMA tiles run (transposed B,
+// widened fp8) get -1 instead.
+int checked_tile(int tile, int64_t N, int64_t K, int eb, bool b_trans, bool dma_only) {
+  if (!is_dma_tile(tile)) return dma_only ? -1 : tile;
   if (dma_offsets_fit(tile, N, K, eb, b_trans)) return tile;
-  if (b_trans) return -1;
+  if (dma_only) return -1;
   if (tile == GEMM_TILE_256x256) return GEMM_TILE_256x256_RS;
   return (tile == GEMM_TILE_128x256 || tile == GEMM_TILE_64x64) ? GEMM_TILE_128x128
                                                                  : GEMM_TILE_32x128;
@@ -401,9 +402,13 @@ gemm_status gemm_plan_ex2(int64_t M, int64_t N, int64_t K, gemm_dtype in, gemm_d
   if (tile < GEMM_TILE_DEFAULT || tile > GEMM_TILE_64x64) return GEMM_ERR_UNSUPPORTED;
   if (is_narrow_tile(tile) && elem_bytes(in) != 2) return GEMM_ERR_UNSUPPORTED;
   if (!std::isfinite(scale_a) || !std::isfinite(scale_b)) return GEMM_ERR_UNSUPPORTED;
-  if (flags & ~(unsigned)(GEMM_PLAN_B_TRANSPOSED | GEMM_PLAN_PERSISTENT | GEMM_PLAN_TILE_BY_M))
+  if (flags & ~(unsigned)(GEMM_PLAN_B_TRANSPOSED | GEMM_PLAN_PERSISTENT | GEMM_PLAN_TILE_BY_M |
+                          GEMM_PLAN_FP8_FP32_ACCUM))
     return GEMM_ERR_UNSUPPORTED;
   const bool bt = (flags & GEMM_PLAN_B_TRANSPOSED) != 0;
+  const bool f8w = (flags & GEMM_PLAN_FP8_FP32_ACCUM) != 0;
+  if (f8w && in != GEMM_F8_E4M3 && in != GEMM_F8_E5M2) return GEMM_ERR_UNSUPPORTED;
+  const bool dma_only = bt || f8w;
   // 16-byte vector access of every row of A and B needs K and N to be
   // multiples of 16 bytes' worth of elements.
   const int eb = elem_bytes(in);
@@ -418,23 +423,25 @@ gemm_status gemm_plan_ex2(int64_t M, int64_t N, int64_t K, gemm_dtype in, gemm_d
   p->in = in;
   p->out = out;
   p->b_trans = bt;
+  p->f8_fp32 = f8w;
   p->persistent = (flags & GEMM_PLAN_PERSISTENT) != 0;
   int split_tile = tile == GEMM_TILE_DEFAULT ? default_tile(N, K, eb) : tile;
-  // Transposed B runs on the DMA tiles only; its decode-like default is the
-  // 32-row DMA tile.
-  if (bt && tile == GEMM_TILE_DEFAULT && split_tile == GEMM_TILE_32x128) split_tile = GEMM_TILE_32x256;
+  // Transposed B and widened fp8 run on the DMA tiles only; their decode-like
+  // default is the 32-row DMA tile.
+  if (dma_only && tile == GEMM_TILE_DEFAULT && split_tile == GEMM_TILE_32x128)
+    split_tile = GEMM_TILE_32x256;
   if (tile == GEMM_TILE_DEFAULT && (flags & GEMM_PLAN_TILE_BY_M) && reduction_dominated(N, K) &&
       N > 512) {
     // the flag never makes a plan fail: a tile whose offsets would not fit
     // (transposed B with a very long K) leaves the default in place
     const int by_m = split_tile_by_m(M, split_tile);
-    if (checked_tile(by_m, N, K, eb, bt) >= 0) split_tile = by_m;
+    if (checked_tile(by_m, N, K, eb, bt, dma_only) >= 0) split_tile = by_m;
   }
-  p->tile = checked_tile(split_tile, N, K, eb, bt);
+  p->tile = checked_tile(split_tile, N, K, eb, bt, dma_only);
   int run_tile = tile;
   if (tile == GEMM_TILE_DEFAULT)
     run_tile = (flags & GEMM_PLAN_TILE_BY_M) ? tile_by_m(M, N, eb) : default_run_tile(N, K, eb);
-  p->run_tile = checked_tile(run_tile, N, K, eb, bt);
+  p->run_tile = checked_tile(run_tile, N, K, eb, bt, dma_only);
   if (p->tile < 0 || p->run_tile < 0) {
     delete p;
     return GEMM_ERR_UNSUPPORTED;
@@ -495,7 +502,7 @@ gemm_status gemm_plan_info(gemm_plan_t p, gemm_plan_info_t* info) {
   info->block_k = p->bk;
   info->mfma_m = mfma_mn(p->in);
   info->mfma_n = mfma_mn(p->in);
-  info->mfma_k = mfma_k(p->in);
+  info->mfma_k = p->f8_fp32 ? 32 : mfma_k(p->in);
   info->waves = p->waves_m * p->waves_n;
   info->group_m = p->group_m;
   info->split_k = p->split_k;

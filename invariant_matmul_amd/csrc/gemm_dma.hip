@@ -320,12 +320,16 @@ __global__ __launch_bounds__(WM * WN * 64, (waves_per_simd<TBM, TBN, WM, WN, NS>
   // 16-bit inputs: the 16x16x32 step; fp8: the 16x16x128 step; int8 and the
   // exact Ozaki chains (whose bits no instruction changes): the 32x32 step
   constexpr bool M16 = EB == 2 && MODE != MODE_OZAKI;
-  constexpr bool F8S = EB == 1 && !T::I8 && MODE != MODE_OZAKI;
-  constexpr bool B16 = M16 || F8S;           // 16 x 16 output blocks
+  // fp8 data widened to fp16 in registers (GEMM_PLAN_FP8_FP32_ACCUM): the
+  // 16x16x32 fp16 step over the fp8 LDS layout, 8 bytes of K per lane
+  constexpr bool W16 = T::W16;
+  static_assert(!W16 || MODE != MODE_OZAKI, "widened fp8 in an Ozaki pass");
+  constexpr bool F8S = EB == 1 && !T::I8 && !W16 && MODE != MODE_OZAKI;
+  constexpr bool B16 = M16 || F8S || W16;    // 16 x 16 output blocks
   constexpr int BLK = B16 ? 16 : 32;         // MFMA output block edge
   constexpr int NACC = BLK * BLK / 64;       // accumulators per lane per block
   using AccT = typename std::conditional<B16, f32x4, f32x16>::type;
-  constexpr int KSTEP = F8S ? 128 : (M16 ? 64 : T::KSTEP_B);  // bytes of K per MFMA step
+  constexpr int KSTEP = F8S ? 128 : (M16 ? 64 : (W16 ? 32 : T::KSTEP_B));  // bytes of K per MFMA step
   constexpr int FM = WTM / BLK;              // MFMA row blocks per wave
   constexpr int FN = WTN / BLK;              // MFMA column blocks per wave
   constexpr int NM = FM * FN;                // MFMAs per k-step per wave
@@ -345,8 +349,8 @@ __global__ __launch_bounds__(WM * WN * 64, (waves_per_simd<TBM, TBN, WM, WN, NS>
   static_assert(DA * WAVES * 1024 == A_STAGE && DB * WAVES * 1024 == B_STAGE, "DMA split");
   static_assert(FM * BLK * WM == TBM, "tile rows");
   constexpr bool I8 = T::I8;                 // int8: 16-bit-like A reads, 8-bit B reads
-  constexpr int NRA = T::FRAG == 1 ? FM : 2 * FM;  // fragment reads per k-step: A ...
-  constexpr int NRB = BT ? (T::FRAG == 1 ? FN : 2 * FN) : (EB == 2 || I8 ? 2 * FN : 4 * FN);  // ... B
+  constexpr int NRA = (T::FRAG == 1 || W16) ? FM : 2 * FM;  // fragment reads per k-step: A ...
+  constexpr int NRB = W16 ? FN : BT ? (T::FRAG == 1 ? FN : 2 * FN) : (EB == 2 || I8 ? 2 * FN : 4 * FN);  // ... B
   constexpr int NREAD = NRA + NRB;
   constexpr int LDS_BYTES = NS * STAGE;
   static_assert(LDS_BYTES <= 160 * 1024, "LDS ring too large");
@@ -588,11 +592,12 @@ __global__ __launch_bounds__(WM * WN * 64, (waves_per_simd<TBM, TBN, WM, WN, NS>
     // each group of 16 lanes reads 8 K rows x 16 columns per transposing read:
     // 16x16 blocks (fp8), the column block and K rows 32 grp ..; 32x32 blocks,
     // column half grp & 1 and K rows 32 (grp >> 1) .. (16 for int8)
+    // (widened fp8: the column block and K rows 8 grp .., one read per k-step)
     const int t_ = gi >> 1, q = gi & 1;
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
-      const int n = F8S ? wn * WTN + j * 16 + 8 * q : wn * WTN + j * 32 + 16 * (grp & 1) + 8 * q;
-      const int k = F8S ? 32 * grp + t_ : (I8 ? 16 : 32) * (grp >> 1) + t_;
+      const int n = (F8S || W16) ? wn * WTN + j * 16 + 8 * q : wn * WTN + j * 32 + 16 * (grp & 1) + 8 * q;
+      const int k = F8S ? 32 * grp + t_ : W16 ? 8 * grp + t_ : (I8 ? 16 : 32) * (grp >> 1) + t_;
       b_rd[j] = k * BROW + (((n >> 4) ^ bswz(k)) << 4) + q * 8;
     }
   }
@@ -610,6 +615,21 @@ __global__ __launch_bounds__(WM * WN * 64, (waves_per_simd<TBM, TBN, WM, WN, NS>
   //   16-bit, 2j + half for fp8).
   auto read_one = [&](Frag<IN, FM, FN>& F, int as, int bs, int ks, int x) {
     const char* sb = lds + as;
+    if constexpr (W16) {
+      // widened fp8: 8 bytes of K (32 ks + 8 hq ..) per lane and block, A and
+      // B^T rows by plain 8-byte reads, B by one 8-row transposing read
+      const int c = 2 * ks + (hq >> 1), h = (hq & 1) * 8;
+      if (x < NRA) {
+        F.a[x] = *reinterpret_cast<const i32x2*>(sb + a_rd[x] + ((c ^ asw) << 4) + h);
+      } else if constexpr (BT) {
+        const int j = x - NRA;
+        F.b[j] = *reinterpret_cast<const i32x2*>(lds + bs + b_rd[j] + ((c ^ asw) << 4) + h);
+      } else {
+        const int j = x - NRA;
+        F.b[j] = tr8_rows_k32<BROW>(lds_addr + bs + b_rd[j], 32 * ks);
+      }
+      return;
+    }
     if constexpr (I8 && !BT) {
       // int8: A as for 16-bit inputs (one 16-byte slot per k-step half), B by
       // two 8-bit transposing reads of 8 K rows each.
@@ -687,8 +707,16 @@ __global__ __launch_bounds__(WM * WN * 64, (waves_per_simd<TBM, TBN, WM, WN, NS>
   for (int i = 0; i < FM; ++i)
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = AccT{};
+  // widened fp8: the fp16 operands of the current A row block and of every B
+  // block, widened at first use (after the k-step's LDS wait)
+  i32x4 w16_a, w16_b[FN];
   auto mfma_x = [&](const Frag<IN, FM, FN>& F, int x) {
-    if constexpr (M16)
+    if constexpr (W16) {
+      const int i = x / FN, j = x % FN;
+      if (j == 0) w16_a = widen_f8<T::F8>(F.a[i]);
+      if (i == 0) w16_b[j] = widen_f8<T::F8>(F.b[j]);
+      acc[i][j] = mfma16_v<GEMM_F16>(w16_a, w16_b[j], acc[i][j]);
+    } else if constexpr (M16)
       acc[x / FN][x % FN] = mfma16_v<IN>(F.a[x / FN], F.b[x % FN], acc[x / FN][x % FN]);
     else if constexpr (F8S)
       acc[x / FN][x % FN] = mfma16_f8<IN>(F.a[x / FN], F.b[x % FN], acc[x / FN][x % FN]);
@@ -1078,8 +1106,30 @@ __global__ __launch_bounds__(WM * WN * 64, (waves_per_simd<TBM, TBN, WM, WN, NS>
     }
   }
   // No LDS transfer or read may still be in flight when the workgroup ends.
+  // The last stage issued the fragment reads of a stage that does not exist;
+  // their results are never used, but the hardware still writes their
+  // registers when the data arrives.  The fences keep the epilogue below the
+  // waits, and keep_live holds the registers of those reads until here, so that no register copy or epilogue value (on any path the
+  // compiler lays out, the loop peeled or not) is given a register a read
+  // will still write.
+  fence();
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   __builtin_amdgcn_s_waitcnt(lgkmcnt_imm(0));
+  fence();
+  // (Those reads all go to F0: every path reads the next stage's first
+  // k-step into F0, and F1's reads land within their own stage.  The
+  // persistent mode stores its tiles inside the loop, where F0 is live, and
+  // has no epilogue here.)
+  if constexpr (!PER_TILE) {
+    if (nt > 0) {
+      constexpr int FD = sizeof(F0.a[0]) / 4;  // dwords per fragment
+#pragma unroll
+      for (int i = 0; i < FM; ++i) keep_live<FD>(F0.a[i]);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) keep_live<FD>(F0.b[j]);
+    }
+  }
+  fence();
   if constexpr (!PER_TILE) store_tile(m0, n0);
 }
 
@@ -1177,8 +1227,10 @@ hipError_t launch_gemm_persist(const gemm_plan_s& p, const PersistArgs& a, hipSt
   switch (p.in) {
     case GEMM_F16: return launch_persist_bt<GEMM_F16>(p, a, s);
     case GEMM_BF16: return launch_persist_bt<GEMM_BF16>(p, a, s);
-    case GEMM_F8_E4M3: return launch_persist_bt<GEMM_F8_E4M3>(p, a, s);
-    case GEMM_F8_E5M2: return launch_persist_bt<GEMM_F8_E5M2>(p, a, s);
+    case GEMM_F8_E4M3:
+      return p.f8_fp32 ? launch_persist_bt<kInE4M3W>(p, a, s) : launch_persist_bt<GEMM_F8_E4M3>(p, a, s);
+    case GEMM_F8_E5M2:
+      return p.f8_fp32 ? launch_persist_bt<kInE5M2W>(p, a, s) : launch_persist_bt<GEMM_F8_E5M2>(p, a, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -1188,8 +1240,12 @@ hipError_t launch_gemm_dma(const gemm_plan_s& p, int tile, const GemmArgs& a, bo
   switch (p.in) {
     case GEMM_F16: return launch_in<GEMM_F16>(p, tile, a, slice_mode, s);
     case GEMM_BF16: return launch_in<GEMM_BF16>(p, tile, a, slice_mode, s);
-    case GEMM_F8_E4M3: return launch_in<GEMM_F8_E4M3>(p, tile, a, slice_mode, s);
-    case GEMM_F8_E5M2: return launch_in<GEMM_F8_E5M2>(p, tile, a, slice_mode, s);
+    case GEMM_F8_E4M3:
+      return p.f8_fp32 ? launch_in<kInE4M3W>(p, tile, a, slice_mode, s)
+                       : launch_in<GEMM_F8_E4M3>(p, tile, a, slice_mode, s);
+    case GEMM_F8_E5M2:
+      return p.f8_fp32 ? launch_in<kInE5M2W>(p, tile, a, slice_mode, s)
+                       : launch_in<GEMM_F8_E5M2>(p, tile, a, slice_mode, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -330,6 +330,7 @@ hipError_t launch_gemm(const gemm_plan_s& p, int tile, const GemmArgs& a, bool s
   if (tile == GEMM_TILE_256x256 || tile == GEMM_TILE_128x256 || tile == GEMM_TILE_32x256 ||
       tile == GEMM_TILE_64x256 || tile == GEMM_TILE_32x64 || tile == GEMM_TILE_64x64)
     return launch_gemm_dma(p, tile, a, slice_mode, s);
+  if (p.f8_fp32) return hipErrorInvalidValue;  // the planner keeps such plans on DMA tiles
   switch (p.in) {
     case GEMM_F16: return launch_in<GEMM_F16>(p, tile, a, slice_mode, s);
     case GEMM_BF16: return launch_in<GEMM_BF16>(p, tile, a, slice_mode, s);

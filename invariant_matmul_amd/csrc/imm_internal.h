@@ -28,6 +28,12 @@ inline int block_k_elems(int dt) { return kTileKBytes / elem_bytes(dt); }
 inline int mfma_mn(int) { return 16; }
 inline int mfma_k(int dt) { return elem_bytes(dt) == 1 ? 128 : 32; }
 
+// Kernel input codes of fp8 data under GEMM_PLAN_FP8_FP32_ACCUM: fp8 bytes in
+// memory and LDS, widened to fp16 in registers for the 16x16x32 fp16 step.
+constexpr int kInWiden = 0x10;
+constexpr int kInE4M3W = kInWiden | GEMM_F8_E4M3;
+constexpr int kInE5M2W = kInWiden | GEMM_F8_E5M2;
+
 }  // namespace imm
 
 struct gemm_plan_s {
@@ -45,6 +51,7 @@ struct gemm_plan_s {
   int run_waves_m, run_waves_n;
   int64_t run_tiles_m, run_tiles_n;
   bool b_trans;         // B is given as [N, K] row-major (DMA tiles only)
+  bool f8_fp32;         // fp8 through the fp16 step (DMA tiles only)
   bool persistent;      // gemm_run: at most one workgroup per compute unit
   int group_m;
   int split_k;          // slices actually used (after rounding)

@@ -27,7 +27,10 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 template <int IN>
 struct InT {
   static constexpr bool I8 = IN == GEMM_I8;  // int8 (Ozaki slices), int32 accumulators
-  static constexpr int EB = (IN == GEMM_F8_E4M3 || IN == GEMM_F8_E5M2 || I8) ? 1 : 2;
+  // fp8 data widened to fp16 for the 16x16x32 step (kInE4M3W, kInE5M2W)
+  static constexpr bool W16 = (IN & kInWiden) != 0;
+  static constexpr int F8 = IN & ~kInWiden;   // the fp8 format of the data
+  static constexpr int EB = (F8 == GEMM_F8_E4M3 || F8 == GEMM_F8_E5M2 || I8) ? 1 : 2;
   // The 32x32-block step (mfma_v): bytes of K per instruction per row, and
   // 16-byte pieces per lane per operand.
   static constexpr int KSTEP_B = (EB == 2 || I8) ? 32 : 64;
@@ -58,7 +61,8 @@ struct InT {
 // int8) or 8 dwords (fp8) per lane, allocated as one register tuple.
 template <int IN>
 struct FragOf {
-  using type = typename std::conditional<InT<IN>::FRAG == 1, i32x4, i32x8>::type;
+  using type = typename std::conditional<
+      InT<IN>::W16, i32x2, typename std::conditional<InT<IN>::FRAG == 1, i32x4, i32x8>::type>::type;
 };
 
 template <int IN>
@@ -105,6 +109,32 @@ __device__ __forceinline__ f32x4 mfma16_v(const i32x4& a, const i32x4& b, f32x4 
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+// Eight fp8 values (K-consecutive, one per byte) widened to the eight fp16
+// values of a 16x16x32 operand, in the same order.  Every e4m3 and e5m2 value
+// (NaN and, for e5m2, infinity included) is an fp16 value, and the unit scale
+// makes the conversion exact.
+template <int F8>
+__device__ __forceinline__ i32x4 widen_f8(const i32x2& v) {
+  static_assert(F8 == GEMM_F8_E4M3 || F8 == GEMM_F8_E5M2, "fp8 formats");
+  typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+  i32x4 r;
+#pragma unroll
+  for (int d = 0; d < 2; ++d) {
+    const unsigned u = (unsigned)v[d];
+    f16x2 lo, hi;
+    if constexpr (F8 == GEMM_F8_E4M3) {
+      lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(u, 1.0f, false);
+      hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(u, 1.0f, true);
+    } else {
+      lo = __builtin_amdgcn_cvt_scalef32_pk_f16_bf8(u, 1.0f, false);
+      hi = __builtin_amdgcn_cvt_scalef32_pk_f16_bf8(u, 1.0f, true);
+    }
+    r[2 * d] = __builtin_bit_cast(int, lo);
+    r[2 * d + 1] = __builtin_bit_cast(int, hi);
+  }
+  return r;
+}
+
 // fp32 -> bf16, round to nearest, ties to even (quiet NaN stays NaN).
 __device__ __forceinline__ unsigned short f32_to_bf16(float f) {
   unsigned u = __builtin_bit_cast(unsigned, f);
@@ -136,33 +166,47 @@ __device__ __forceinline__ void store_final(void* C, int64_t idx, float sum, flo
   store_out<OUT>(C, idx, v);
 }
 
-// Transposing LDS reads (gfx950).  Issued as inline assembly: the compiler
-// otherwise waits for every outstanding buffer->LDS transfer before each such
-// read (it cannot tell which LDS bytes the transfer writes), which would drain
-// the prefetch pipeline every stage.  The caller must wait for lgkmcnt before
-// using the result.  In each group of 16 lanes, lanes 4t..4t+3 (16-bit) or
-// 2t..2t+1 (8-bit) supply row t from their own addresses and lane j receives
-// column j of those rows.
+// Transposing LDS reads (gfx950), and plain 16-byte LDS reads, at an LDS
+// byte address plus a compile-time offset (the instruction's offset field).
+// Issued as inline assembly: the compiler's own transposing-read builtin makes
+// it wait for every outstanding buffer->LDS transfer before each read (it
+// cannot tell which LDS bytes a transfer writes), which would drain the
+// prefetch pipeline every stage.  The caller must wait for lgkmcnt before
+// using a result, and must keep every result live until such a wait (the
+// compiler takes an assembly output as written at issue, so a result it
+// proves unused could share its registers with live values that the arriving
+// data then overwrites).  In each group of 16 lanes of a transposing read,
+// lanes 4t..4t+3 (16-bit) or 2t..2t+1 (8-bit) supply row t from their own
+// addresses and lane j receives column j of those rows.
 template <int OFF>
 __device__ __forceinline__ i32x2 ds_read_tr16_b64(unsigned addr) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds_read offset field");
   i32x2 v;
   asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "n"(OFF));
   return v;
 }
 template <int OFF>
 __device__ __forceinline__ i32x2 ds_read_tr8_b64(unsigned addr) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds_read offset field");
   i32x2 v;
   asm volatile("ds_read_b64_tr_b8 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "n"(OFF));
   return v;
 }
-// A plain 16-byte LDS read issued the same way, for schedules that place every
-// LDS wait themselves.
 template <int OFF>
 __device__ __forceinline__ i32x4 ds_read_b128_at(unsigned addr) {
   static_assert(OFF >= 0 && OFF < 65536, "ds_read offset field");
   i32x4 v;
   asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "n"(OFF));
   return v;
+}
+// Keeps the N dwords of v live (in their registers) up to this point.
+template <int N, class V>
+__device__ __forceinline__ void keep_live(const V& v) {
+#pragma unroll
+  for (int e = 0; e < N; ++e) {
+    const int x = v[e];
+    asm volatile("" : : "v"(x));
+  }
 }
 
 // Calls f(std::integral_constant<int, I>) for I = LO .. HI-1 in order, so that

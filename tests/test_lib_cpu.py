@@ -193,7 +193,15 @@ def _plan2_status(*args):
     ((8, 8, 8, 0, 4, 0, 0, 0, 1.0, 1.0, 3), 0),
     ((8, 8, 8, 0, 4, 0, 0, 0, 1.0, 1.0, 4), 0),            # tile from M (single pass)
     ((8, 8, 8, 0, 4, 0, 0, 0, 1.0, 1.0, 7), 0),
-    ((8, 8, 8, 0, 4, 0, 0, 0, 1.0, 1.0, 8), 2),            # unknown flag bit
+    ((8, 8, 8, 0, 4, 0, 0, 0, 1.0, 1.0, 16), 2),           # unknown flag bit
+    ((8, 8, 8, 0, 4, 0, 0, 0, 1.0, 1.0, 8), 2),            # fp16 step for fp8: fp16 input
+    ((16, 16, 16, 1, 4, 0, 0, 0, 1.0, 1.0, 8), 2),         # ... bf16 input
+    ((16, 16, 16, 2, 1, 0, 0, 0, 1.0, 1.0, 8), 0),         # ... e4m3
+    ((16, 16, 16, 3, 4, 0, 0, 0, 1.0, 1.0, 15), 0),        # ... e5m2 with every flag
+    ((16, 16, 16, 2, 1, 0, 0, 3, 1.0, 1.0, 8), 2),         # ... needs a DMA tile
+    ((16, 16, 16, 2, 1, 0, 0, 5, 1.0, 1.0, 8), 0),
+    ((16, 16, 2 ** 26, 2, 1, 0, 0, 0, 1.0, 1.0, 8), 2),    # ... DMA offsets would overflow
+    ((16, 16, 2 ** 26, 2, 1, 0, 0, 0, 1.0, 1.0, 0), 0),    # register-staged fallback
     ((8, 8, 8, 0, 4, 0, 0, 3, 1.0, 1.0, 1), 2),            # transposed B needs a DMA tile
     ((8, 8, 8, 0, 4, 0, 0, 5, 1.0, 1.0, 1), 0),
     ((8, 8, 2 ** 24, 0, 4, 0, 0, 0, 1.0, 1.0, 1), 2),      # DMA offsets would overflow
@@ -211,6 +219,22 @@ def test_transposed_b_plans_use_dma_tiles_and_the_same_split():
         assert b["tile"] in dma and b["run_tile"] in dma, (N, K, dt)
         # the split (which decides the bits) does not depend on the layout
         assert (a["split_k"], a["k_per_split"]) == (b["split_k"], b["k_per_split"]), (N, K, dt)
+
+
+def test_fp8_fp16_step_plans_use_dma_tiles_the_same_split_and_report_the_step():
+    dma = {imm.TILE[t] for t in ("256x256", "128x256", "32x256", "64x256")}
+    for M, N, K in ((1, 4096, 14336), (64, 4096, 14336), (8192, 8192, 8192), (256, 256, 131072),
+                    (1024, 1024, 1024), (300, 272, 384), (1, 16, 16)):
+        for dt in ("e4m3", "e5m2"):
+            a = imm.gemm_plan_ex2(M, N, K, dt, "bf16").info
+            for fl in (0, imm.PLAN_B_TRANSPOSED, imm.PLAN_TILE_BY_M):
+                b = imm.gemm_plan_ex2(M, N, K, dt, "bf16", flags=fl | imm.PLAN_FP8_FP32_ACCUM).info
+                assert b["tile"] in dma and b["run_tile"] in dma, (M, N, K, dt, fl)
+                # the split of K does not depend on the step
+                assert (a["split_k"], a["k_per_split"]) == (b["split_k"], b["k_per_split"])
+                assert (b["mfma_m"], b["mfma_n"], b["mfma_k"]) == (16, 16, 32)
+                assert b["block_k"] == a["block_k"] == 128 and b["in_dtype"] == imm.DTYPE[dt]
+            assert a["mfma_k"] == 128
 
 
 def test_null_plan_handles():
