@@ -17,6 +17,11 @@ matrix-core throughput of the slice products), and torch.matmul (hipBLASLt /
 the fp64 path) on the same shapes and a 1 GiB device copy (an achievable HBM
 rate) as run-only comparators.
 
+Every timed series is preceded by SETTLE_MS of untimed launches of the same
+call, then its warm-up launches: the engine clock rises over the first ~50
+ms of load after an idle spell (launches in that window ran up to 10 %
+longer on MI355X), and the figures are for sustained load.
+
 "roofline" reports the dominant kernel (the DMA-fed 256x256 GEMM kernel) against
 the MI355X dense fp16 matrix peak: achieved = 2*M*N*K flop per launch divided
 by the kernel's average duration, timed with HIP events on the launch
@@ -329,8 +334,9 @@ def write_trace_summary(trace_csv, bench_json, out_path=TRACE_SUMMARY_FILE):
     head = [x for x in rows if HEADLINE_KERNEL in x[1] and x[2] == 1024]
     if not head:
         raise SystemExit(f"{trace_csv}: no headline dispatches")
-    # the headline leg runs warm-up + steps launches back to back first
-    first = [x[4] for x in head[: line["warmup"] + line["steps"]]]
+    # the headline leg runs its settle launches, then warm-up + steps back to back, first
+    ns = line.get("extra", {}).get("settle", {}).get("headline_launches", 0)
+    first = [x[4] for x in head[ns: ns + line["warmup"] + line["steps"]]]
     timed = first[line["warmup"]:]
     groups = {}
     for _, name, wgs, wg, us in rows:
@@ -351,7 +357,8 @@ def write_trace_summary(trace_csv, bench_json, out_path=TRACE_SUMMARY_FILE):
            f"{line['roofline']['avg_launch_ms'] * 1e3:.1f} us (HIP events on the launch stream).", "",
            f"Headline kernel `{HEADLINE_KERNEL}` at M=N=K=8192 (1024 workgroups x 512 threads): "
            f"{len(head)} dispatches in the whole run, average {statistics.mean(x[4] for x in head):.1f} us. "
-           f"Its first {len(first)} ({line['warmup']} warm-up + {line['steps']} timed) back to back: "
+           f"After its {ns} untimed settle launches, the next {len(first)} ({line['warmup']} warm-up + "
+           f"{line['steps']} timed) back to back: "
            f"the timed {len(timed)} average {statistics.mean(timed):.1f} us, median "
            f"{statistics.median(timed):.1f} us, min {min(timed):.1f} us, max {max(timed):.1f} us.", "",
            "## Per kernel and launch shape", "",
@@ -426,8 +433,32 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def time_launches(fn, n, warmup, torch):
-    """Per-call durations (ms) from HIP events recorded on the current stream."""
+SETTLE_MS = 150.0
+# untimed settle launches before each timed series, in order (the headline's first)
+SETTLE_LAUNCHES = []
+
+
+def settle(fn, torch, ms=SETTLE_MS):
+    """Launch fn back to back, untimed, until about `ms` of GPU time has
+    passed; returns the number of launches."""
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    n = 0
+    while True:
+        for _ in range(4):
+            fn(0)
+        n += 4
+        e.record()
+        e.synchronize()
+        if s.elapsed_time(e) >= ms:
+            return n
+
+
+def time_launches(fn, n, warmup, torch, settle_ms=SETTLE_MS):
+    """Per-call durations (ms) from HIP events recorded on the current stream,
+    after the settle launches and `warmup` untimed calls."""
+    SETTLE_LAUNCHES.append(settle(fn, torch, settle_ms) if settle_ms > 0 else 0)
     for _ in range(warmup):
         fn(0)
     torch.cuda.synchronize()
@@ -896,6 +927,7 @@ def main():
                 "algorithmic_flop_per_launch": w.flops, "avg_launch_ms": kavg}
 
     extra = {"headline_kernel": summary(per), "headline_clock": clock,
+             "settle": {"ms": SETTLE_MS, "headline_launches": SETTLE_LAUNCHES[0]},
              "plan": {k: plan.info[k] for k in ("run_block_m", "run_block_n", "block_k", "run_waves",
                                                   "group_m", "split_k", "mfma_k")}}
     secondary = {}
@@ -911,6 +943,20 @@ def main():
             del ref
         except Exception as e:  # comparator only
             extra["torch_matmul_error"] = str(e)
+        # The headline series again after 2 s of idle, with its warm-up but no
+        # settle launches: what the first launches after an idle spell get.
+        log("headline after an idle spell")
+        Ci = torch.empty((w.M, w.N), dtype=torch.float32, device="cuda")
+        torch.cuda.synchronize()
+        time.sleep(2.0)
+        iper, itot = time_launches(lambda i: imm.gemm_run(plan, Ad, Bd, Ci), args.steps, args.warmup,
+                                   torch, settle_ms=0)
+        del Ci
+        extra["headline_after_idle"] = {**summary(iper), "idle_s": 2.0, "settle_ms": 0,
+                                        "ms_per_step": itot / args.steps,
+                                        "TFLOPs": w.flops / (itot / args.steps * 1e-3) / 1e12}
+        secondary["fp16_8192_after_2s_idle_no_settle_TFLOPs"] = round(
+            extra["headline_after_idle"]["TFLOPs"], 1)
         # The same product with A and B rotated over two copies (537 MB, twice
         # the 256 MB last-level cache), so that no launch finds its operands
         # left in that cache by the one before.

@@ -768,6 +768,55 @@ __global__ __launch_bounds__(WM * WN * 64, (waves_per_simd<TBM, TBN, WM, WN, NS>
     // out of the loop (where they would sit in registers or scratch).
     int lrow = wm * WTM + 4 * hq, lcol = wn * WTN + lb;
     if constexpr (PER_TILE) asm volatile("" : "+v"(lrow), "+v"(lcol));
+    if constexpr (MODE != MODE_OZAKI) {
+      // A tile wholly inside C whose byte offsets from its first element fit
+      // in 31 bits: every element is a uniform row address plus one 32-bit
+      // offset per lane (plus a constant), with no bounds checks.  The
+      // values, and the order of operations that makes them, are those of
+      // the general path below.  (Transposing 4 x 4 pieces within quads of
+      // lanes, for one 8- or 16-byte store per four elements, measured
+      // slower: the exchanges cost more than the stores they save.)
+      constexpr int OB = (MODE == MODE_SLICE || OUT == GEMM_F32) ? 4 : 2;
+      if (tm0 + TBM <= g.M && tn0 + TBN <= g.N && g.N * (TBM * OB) < (int64_t(1) << 31)) {
+        const int64_t row0 = MODE == MODE_SLICE ? ksl * g.M + tm0 : tm0;
+        char* const base = static_cast<char*>(g.C) + (row0 * g.N + tn0) * OB;
+        const unsigned loff = (unsigned)(lrow * (int)g.N + lcol) * OB;
+        auto body = [&](auto plain) {
+#pragma clang fp contract(off)
+          float bv[FN];
+          if constexpr (!decltype(plain)::value) {
+#pragma unroll
+            for (int j = 0; j < FN; ++j) bv[j] = g.bias ? g.bias[tn0 + lcol + j * BLK] : 0.0f;
+          }
+#pragma unroll
+          for (int i = 0; i < FM; ++i) {
+#pragma unroll
+            for (int r = 0; r < NACC; ++r) {
+              const int rr = i * BLK + (B16 ? r : 8 * (r >> 2) + (r & 3));
+              char* const rb = base + (int64_t)rr * g.N * OB;
+#pragma unroll
+              for (int j = 0; j < FN; ++j) {
+                float v = acc[i][j][r];
+                if constexpr (!decltype(plain)::value) {
+                  v = g.scale == 1.0f ? v : v * g.scale;
+                  if (g.bias) v = v + bv[j];
+                }
+                char* const p = rb + j * BLK * OB + loff;
+                if constexpr (MODE == MODE_SLICE)
+                  *reinterpret_cast<float*>(p) = v;
+                else
+                  store_at<OUT>(p, v);
+              }
+            }
+          }
+        };
+        if (MODE == MODE_SLICE || (g.scale == 1.0f && !g.bias))
+          body(std::true_type{});
+        else if constexpr (MODE != MODE_SLICE)
+          body(std::false_type{});
+        return;
+      }
+    }
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
 #pragma unroll
@@ -1096,6 +1145,9 @@ __global__ __launch_bounds__(WM * WN * 64, (waves_per_simd<TBM, TBN, WM, WN, NS>
       // start the next one from +0.
       if (++cur_kt == ntp) {
         cur_kt = 0;
+        // the next stage's first fragment reads land before the epilogue,
+        // which may copy their registers (the compiler takes them as written)
+        lds_wait();
         store_tile(cur_m0, cur_n0);
 #pragma unroll
         for (int i = 0; i < FM; ++i)

@@ -135,12 +135,13 @@ __device__ __forceinline__ i32x4 widen_f8(const i32x2& v) {
   return r;
 }
 
-// fp32 -> bf16, round to nearest, ties to even (quiet NaN stays NaN).
+// fp32 -> bf16, round to nearest, ties to even; a NaN keeps its sign and
+// the top of its payload, with the quiet bit set (upper half-word | 0x0040).
+// gfx950's v_cvt_pk_bf16_f32 does exactly this (measured on MI355X against
+// the integer form u + 0x7fff + ((u >> 16) & 1) on every upper half-word with
+// eight lower halves each, ties and NaN payloads included: no difference).
 __device__ __forceinline__ unsigned short f32_to_bf16(float f) {
-  unsigned u = __builtin_bit_cast(unsigned, f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (unsigned short)((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (unsigned short)(u >> 16);
+  return __builtin_bit_cast(unsigned short, static_cast<__bf16>(f));
 }
 
 template <int OUT>
@@ -155,13 +156,28 @@ __device__ __forceinline__ void store_out(void* C, int64_t idx, float v) {
   }
 }
 
+// One output element at a byte address.
+template <int OUT>
+__device__ __forceinline__ void store_at(char* p, float v) {
+  if constexpr (OUT == GEMM_F32) {
+    *reinterpret_cast<float*>(p) = v;
+  } else if constexpr (OUT == GEMM_F16) {
+    *reinterpret_cast<_Float16*>(p) = static_cast<_Float16>(v);
+  } else {
+    *reinterpret_cast<unsigned short*>(p) = f32_to_bf16(v);
+  }
+}
+
 // The epilogue of one output element: the fp32 sum times the fp32 product
 // of the scales, plus the fp32 bias of its column when there is one (one
-// fp32 add), converted to the output format.
+// fp32 add), converted to the output format.  The multiply and the add
+// round separately (never fused); a scale of 1 leaves the sum as it is
+// (also a NaN's payload bits).
 template <int OUT>
 __device__ __forceinline__ void store_final(void* C, int64_t idx, float sum, float scale,
                                             const float* bias, int64_t col) {
-  float v = sum * scale;
+#pragma clang fp contract(off)
+  float v = scale == 1.0f ? sum : sum * scale;
   if (bias) v = v + bias[col];
   store_out<OUT>(C, idx, v);
 }

@@ -98,3 +98,4 @@ def file_hazards(text: str, name_pattern: str = r"gemm_dma_kernel") -> dict:
         if h:
             out[m.group(1)] = h
     return out, n
+

@@ -201,3 +201,34 @@ def test_cpu_baseline_samples_every_workload():
         assert x["full_product_s_est"] >= x["total_s"] - x["decode_B_s"] - 1e-9
         assert x["gpu_speedup_est"] > 0
     assert cpu["value"] == cpu["per_config"][0]["GFLOPs"] / 1e3
+
+
+def test_trace_summary_skips_the_settle_launches(tmp_path):
+    # 12 settle launches (1100 us), 2 warm-up (1000 us), 3 timed (800, 900, 1000 us),
+    # then more headline launches of a later leg (700 us) and another kernel
+    fields = ["Kernel_Name", "Start_Timestamp", "End_Timestamp", "Workgroup_Size_X",
+              "Workgroup_Size_Y", "Workgroup_Size_Z", "Grid_Size_X", "Grid_Size_Y", "Grid_Size_Z"]
+    durs = [1100] * 12 + [1000, 1000] + [800, 900, 1000] + [700] * 4
+    rows, t = [], 0
+    for d in durs:
+        rows.append((HEADLINE, t, t + d * 1000, 512, 1024 * 512))
+        t += d * 1000 + 5000
+    rows.append((COPY, t, t + 50000, 256, 256 * 100))
+    trace = tmp_path / "trace.csv"
+    with open(trace, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=fields)
+        w.writeheader()
+        for name, t0, t1, wg, grid in rows:
+            w.writerow({"Kernel_Name": name, "Start_Timestamp": t0, "End_Timestamp": t1,
+                        "Workgroup_Size_X": wg, "Workgroup_Size_Y": 1, "Workgroup_Size_Z": 1,
+                        "Grid_Size_X": grid, "Grid_Size_Y": 1, "Grid_Size_Z": 1})
+    line = {"value": 1.0, "warmup": 2, "steps": 3, "roofline": {"avg_launch_ms": 0.9},
+            "extra": {"settle": {"ms": 150.0, "headline_launches": 12}}}
+    bj = tmp_path / "bench.json"
+    bj.write_text(json.dumps(line) + "\n")
+    out = tmp_path / "summary.md"
+    bench.write_trace_summary(str(trace), str(bj), out_path=str(out))
+    text = out.read_text()
+    assert "After its 12 untimed settle launches, the next 5 (2 warm-up + 3 timed)" in text
+    assert "the timed 3 average 900.0 us, median 900.0 us, min 800.0 us, max 1000.0 us" in text
+    assert f"{len(durs)} dispatches in the whole run" in text
