@@ -58,10 +58,16 @@ void tile_shape(int tile, int* bm, int* bn, int* wm, int* wn) {
 // each slice of B once per 128 rows.  The rest get the large tile.
 bool reduction_dominated(int64_t N, int64_t K) { return K >= 2 * N; }
 
-// Small B (at most 4 MB, the L2 of one XCD): the product is too small to
-// fill the machine with 256 x 256 tiles (1024^3 has 16 of them), while
-// re-reading B from L2 for every 32 rows of A is cheap.  Measured at 1024^3:
-// 14.5 us with 32 x 256 against 29.4 us with 256 x 256.
+// Small B (at most 4 MB, the L2 of one XCD): 256 x 256 tiles leave most of
+// the machine idle unless M is large (1024^3 has 16 of them), so these
+// shapes take the 128 x 256 tile, the one whose worst case over M is least.
+// Measured on N = K = 1024 fp16 (us, 32 x 256 / 128 x 256 / 256 x 256):
+// M = 1: 15.8 / 16.8 / 24.2; M = 1024: 16.0 / 17.5 / 25.1; M = 4096: 28.4 /
+// 20.1 / 27.3; M = 16384: 103.8 / 44.2 / 38.7.  On N = K = 2048 e5m2: M =
+// 1024: 15.0 / 18.4 / 25.8; M = 4096: 44.4 / 23.4 / 28.8; M = 16384: 163.2 /
+// 77.6 / 67.3.  The 32-row tile wins by up to 25 % at small M and loses up to
+// 2.7x at large M, where every 32 rows of A re-read B from L2.  Bits do not
+// depend on the tile, and these shapes are never split.
 bool small_b(int64_t N, int64_t K, int eb) { return N * K * eb <= ((int64_t)4 << 20); }
 
 bool dma_offsets_fit(int tile, int64_t N, int64_t K, int eb, bool b_trans);
@@ -74,7 +80,7 @@ bool is_narrow_tile(int tile) { return tile == GEMM_TILE_32x64 || tile == GEMM_T
 // offsets overflow, narrow shapes keep a DMA tile of 64 rows (the split,
 // and so the bits, depend only on the tile's 256 columns).
 int default_tile(int64_t N, int64_t K, int eb) {
-  if (!reduction_dominated(N, K)) return small_b(N, K, eb) ? GEMM_TILE_32x256 : GEMM_TILE_256x256;
+  if (!reduction_dominated(N, K)) return small_b(N, K, eb) ? GEMM_TILE_128x256 : GEMM_TILE_256x256;
   if (N > 512) return GEMM_TILE_32x128;
   return dma_offsets_fit(GEMM_TILE_128x256, N, K, eb, false) ? GEMM_TILE_128x256 : GEMM_TILE_64x256;
 }
@@ -86,7 +92,7 @@ int default_tile(int64_t N, int64_t K, int eb) {
 // the large tile except for small B (as above) and narrow N (N <= 512, where
 // 256 columns already cover all of N).
 int default_run_tile(int64_t N, int64_t K, int eb) {
-  if (small_b(N, K, eb)) return GEMM_TILE_32x256;
+  if (small_b(N, K, eb)) return GEMM_TILE_128x256;
   if (reduction_dominated(N, K) && N <= 512) return GEMM_TILE_64x256;
   return GEMM_TILE_256x256;
 }

@@ -104,8 +104,16 @@ def test_default_plans_of_the_workloads():
     # fp8 slices of 2048 elements are 16 steps: no extra doubling
     hk8 = imm.gemm_plan(256, 256, 131072, "e5m2").info
     assert (hk8["block_m"], hk8["split_k"]) == (128, 64)
-    small = imm.gemm_plan(1024, 1024, 1024, "f16").info
-    assert (small["run_block_m"], small["run_block_n"]) == (32, 256)
+    # small B: the 128 x 256 tile, for the single pass and the (unsplit) split path
+    for dt in ("f16", "e5m2", "bf16"):
+        small = imm.gemm_plan(1024, 1024, 1024, dt).info
+        assert (small["run_block_m"], small["run_block_n"]) == (128, 256)
+        assert (small["block_m"], small["block_n"], small["split_k"]) == (128, 256, 1)
+    # a reduction-dominated small B keeps its split path (and bits); the single pass
+    # takes the 128 x 256 tile too
+    rd = imm.gemm_plan(16, 1024, 2048, "f16").info
+    assert (rd["block_m"], rd["block_n"]) == (32, 128) and rd["split_k"] > 1
+    assert (rd["run_block_m"], rd["run_block_n"]) == (128, 256)
 
 
 @pytest.mark.parametrize("M,N,K,dt,split,gm", [
