@@ -138,7 +138,11 @@ typedef enum {
   GEMM_TILE_32x64 = 8,      /* 2 waves, DMA ring of 10 stages; fp16 / bf16 only:
                                narrow tile for small M (4x the workgroups of
                                32x256) */
-  GEMM_TILE_64x64 = 9       /* 2 waves, DMA ring of 8 stages; fp16 / bf16 only */
+  GEMM_TILE_64x64 = 9,      /* 2 waves, DMA ring of 8 stages; fp16 / bf16 only */
+  GEMM_TILE_32x32 = 10      /* 2 waves, DMA ring of 6 stages (three
+                               workgroups per compute unit); fp16 / bf16
+                               only: twice the workgroups of 32x64 for
+                               small M */
 } gemm_tile;
 
 /* Plan flags (gemm_plan_ex2). */
@@ -146,7 +150,8 @@ typedef enum {
   /* B is given transposed: a [N, K] row-major matrix W with B = W^T (the
    * weight layout of a linear layer, y = x W^T + b, as in the vLLM
    * batch-invariant operators the Tencent article lists in its closing
-   * section).  Only the DMA tiles (256x256, 128x256, 64x256, 32x256) read this layout;
+   * section).  Only the DMA tiles (256x256, 128x256, 64x256, 32x256, 64x64, 32x64,
+   * 32x32) read this layout;
    * the bits of C are those of the [K, N] layout holding the same values. */
   GEMM_PLAN_B_TRANSPOSED = 1,
   /* gemm_run / gemm_run_bias with the 256x256 tile launch at most one
@@ -157,9 +162,10 @@ typedef enum {
    * plan without the flag; other tiles and the split-K path ignore it. */
   GEMM_PLAN_PERSISTENT = 2,
   /* gemm_run / gemm_run_bias take their tile from M instead of from (N, K,
-   * dtype): the DMA tile (32x256, 64x256, 128x256 or 256x256) with the least
-   * estimated time, rounds of 256 workgroups times a per-tile time that grows
-   * with the tile's rows.  gemm_splitk_run of a wide reduction-dominated shape
+   * dtype): the DMA tile (32x32, 32x64, 64x64, 32x256, 64x256, 128x256 or
+   * 256x256; fp8 inputs skip the first three) with the least estimated time,
+   * rounds of 256 workgroups times a per-tile time that grows with the
+   * tile's size.  gemm_splitk_run of a wide reduction-dominated shape
    * (K >= 2N, N > 512) takes from M the tile with the fewest row tiles (32-row,
    * 64x256, 128x256 or 256x256); the split of K stays the one (N, K, dtype)
    * gives.  Every tile uses the same matrix-core instruction and K order, so

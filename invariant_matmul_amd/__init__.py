@@ -37,7 +37,7 @@ STATUS = {0: "GEMM_OK", 1: "GEMM_ERR_INVALID_VALUE", 2: "GEMM_ERR_UNSUPPORTED",
           3: "GEMM_ERR_WORKSPACE", 4: "GEMM_ERR_HIP"}
 DTYPE = {"f16": 0, "bf16": 1, "e4m3": 2, "e5m2": 3, "f32": 4, "i8": 5}
 TILE = {"default": 0, "256x256": 1, "128x128": 2, "32x128": 3, "256x256_rs": 4, "32x256": 5,
-        "64x256": 6, "128x256": 7, "32x64": 8, "64x64": 9}
+        "64x256": 6, "128x256": 7, "32x64": 8, "64x64": 9, "32x32": 10}
 PLAN_B_TRANSPOSED = 1
 PLAN_PERSISTENT = 2
 PLAN_TILE_BY_M = 4

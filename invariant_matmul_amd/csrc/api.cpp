@@ -46,6 +46,7 @@ void tile_shape(int tile, int* bm, int* bn, int* wm, int* wn) {
     case GEMM_TILE_128x256: *bm = 128; *bn = 256; *wm = 2; *wn = 4; break;
     case GEMM_TILE_32x64: *bm = 32; *bn = 64; *wm = 2; *wn = 1; break;
     case GEMM_TILE_64x64: *bm = 64; *bn = 64; *wm = 2; *wn = 1; break;
+    case GEMM_TILE_32x32: *bm = 32; *bn = 32; *wm = 2; *wn = 1; break;
     default: *bm = 32; *bn = 128; *wm = 1; *wn = 4; break;  // GEMM_TILE_32x128
   }
 }
@@ -74,7 +75,9 @@ bool dma_offsets_fit(int tile, int64_t N, int64_t K, int eb, bool b_trans);
 
 // The 64-column DMA tiles take 16-bit inputs only (an fp8 matrix step covers
 // 32 rows, more than their waves' row blocks).
-bool is_narrow_tile(int tile) { return tile == GEMM_TILE_32x64 || tile == GEMM_TILE_64x64; }
+bool is_narrow_tile(int tile) {
+  return tile == GEMM_TILE_32x64 || tile == GEMM_TILE_64x64 || tile == GEMM_TILE_32x32;
+}
 
 // Tile of the split-K path.  Past the K where a 128-row tile's 32-bit A
 // offsets overflow, narrow shapes keep a DMA tile of 64 rows (the split,
@@ -97,32 +100,40 @@ int default_run_tile(int64_t N, int64_t K, int eb) {
   return GEMM_TILE_256x256;
 }
 
-// GEMM_PLAN_TILE_BY_M: the DMA tile with the least estimated time.  Each
-// of these tiles takes a whole compute unit (its LDS ring), so a grid runs in
-// rounds of 256 workgroups (a 256-CU MI355X), and one round of a tile takes
-// about the same time whatever the shape: it is a workgroup's walk through
-// K.  Units per round, fitted on a sweep at K = 4096 (M = 1 ... 2048; N = 1024,
-// 4096, 6144, 14336; both B layouts), where one round took about 27, 29, 32,
-// 40, 47 and 71 us: 32 x 64: 134, 64 x 64: 144, 32 x 256: 159, 64 x 256: 191,
-// 128 x 256: 255, 256 x 256: 383.  Cost = rounds x units; the smaller tile wins
-// a tie.  On that sweep this picks the fastest tile, or one within 3 % of it,
-// at every point.  The 64-column tiles take 16-bit inputs only.  Bits do not
-// depend on the tile.
-int tile_by_m(int64_t M, int64_t N, int eb) {
+// GEMM_PLAN_TILE_BY_M: the DMA tile with the least estimated time.  A grid
+// runs in rounds of 256 workgroups (a 256-CU MI355X), and one round of a
+// tile takes about the same time whatever the shape: it is a workgroup's walk
+// through K.  Units per round, fitted on sweeps at K = 4096 (M = 1 ... 2048;
+// N = 1024, 4096, 6144, 14336; both B layouts), where one round took about
+// 27, 29, 32, 40, 47 and 71 us: 32 x 64: 134, 64 x 64: 144, 32 x 256: 159,
+// 64 x 256: 191, 128 x 256: 255, 256 x 256: 383.  These tiles take a whole
+// compute unit for their LDS ring.  Three 32 x 32 rings share one, so its
+// second and third rounds overlap the first: its first round costs 100 (B
+// [K, N]) or 80 (B transposed, whose K-contiguous rows stream faster), every
+// further round 60 or 30.  Cost = rounds x units; the smaller tile wins a
+// tie.  On that sweep (112 shapes) this picks the fastest tile, or one within
+// 3 % of it, at 106 shapes and is at most 8 % off at the others.  The 64-
+// and 32-column tiles take 16-bit inputs only.  Bits do not depend on the
+// tile.
+int tile_by_m(int64_t M, int64_t N, int eb, bool b_trans) {
   struct Cand {
     int tile, rows, cols, units;
   };
-  static const Cand kCands[6] = {{GEMM_TILE_32x64, 32, 64, 134},   {GEMM_TILE_64x64, 64, 64, 144},
-                                 {GEMM_TILE_32x256, 32, 256, 159}, {GEMM_TILE_64x256, 64, 256, 191},
+  static const Cand kCands[7] = {{GEMM_TILE_32x32, 32, 32, 0},     {GEMM_TILE_32x64, 32, 64, 134},
+                                 {GEMM_TILE_64x64, 64, 64, 144},   {GEMM_TILE_32x256, 32, 256, 159},
+                                 {GEMM_TILE_64x256, 64, 256, 191},
                                  {GEMM_TILE_128x256, 128, 256, 255},
                                  {GEMM_TILE_256x256, 256, 256, 383}};
   int best = -1;
   int64_t best_cost = -1;
-  for (int i = 0; i < 6; ++i) {
+  for (int i = 0; i < 7; ++i) {
     if (is_narrow_tile(kCands[i].tile) && eb != 2) continue;
     const int64_t wgs = ((M + kCands[i].rows - 1) / kCands[i].rows) *
                         ((N + kCands[i].cols - 1) / kCands[i].cols);
-    const int64_t cost = ((wgs + 255) / 256) * kCands[i].units;
+    const int64_t rounds = (wgs + 255) / 256;
+    const int64_t cost = kCands[i].tile == GEMM_TILE_32x32
+                             ? (b_trans ? 80 + (rounds - 1) * 30 : 100 + (rounds - 1) * 60)
+                             : rounds * kCands[i].units;
     if (best_cost < 0 || cost < best_cost) {
       best = i;
       best_cost = cost;
@@ -150,7 +161,8 @@ int split_tile_by_m(int64_t M, int narrow) {
 
 bool is_dma_tile(int tile) {
   return tile == GEMM_TILE_256x256 || tile == GEMM_TILE_128x256 || tile == GEMM_TILE_32x256 ||
-         tile == GEMM_TILE_64x256 || tile == GEMM_TILE_32x64 || tile == GEMM_TILE_64x64;
+         tile == GEMM_TILE_64x256 || tile == GEMM_TILE_32x64 || tile == GEMM_TILE_64x64 ||
+         tile == GEMM_TILE_32x32;
 }
 
 
@@ -405,7 +417,7 @@ gemm_status gemm_plan_ex2(int64_t M, int64_t N, int64_t K, gemm_dtype in, gemm_d
   if (M > INT_MAX || N > INT_MAX || K > INT_MAX) return GEMM_ERR_UNSUPPORTED;
   if (!valid_in(in) || !valid_out(out)) return GEMM_ERR_UNSUPPORTED;
   if (split_k < 0 || split_k > kMaxSplit || group_m < 0) return GEMM_ERR_UNSUPPORTED;
-  if (tile < GEMM_TILE_DEFAULT || tile > GEMM_TILE_64x64) return GEMM_ERR_UNSUPPORTED;
+  if (tile < GEMM_TILE_DEFAULT || tile > GEMM_TILE_32x32) return GEMM_ERR_UNSUPPORTED;
   if (is_narrow_tile(tile) && elem_bytes(in) != 2) return GEMM_ERR_UNSUPPORTED;
   if (!std::isfinite(scale_a) || !std::isfinite(scale_b)) return GEMM_ERR_UNSUPPORTED;
   if (flags & ~(unsigned)(GEMM_PLAN_B_TRANSPOSED | GEMM_PLAN_PERSISTENT | GEMM_PLAN_TILE_BY_M |
@@ -446,7 +458,7 @@ gemm_status gemm_plan_ex2(int64_t M, int64_t N, int64_t K, gemm_dtype in, gemm_d
   p->tile = checked_tile(split_tile, N, K, eb, bt, dma_only);
   int run_tile = tile;
   if (tile == GEMM_TILE_DEFAULT)
-    run_tile = (flags & GEMM_PLAN_TILE_BY_M) ? tile_by_m(M, N, eb) : default_run_tile(N, K, eb);
+    run_tile = (flags & GEMM_PLAN_TILE_BY_M) ? tile_by_m(M, N, eb, bt) : default_run_tile(N, K, eb);
   p->run_tile = checked_tile(run_tile, N, K, eb, bt, dma_only);
   if (p->tile < 0 || p->run_tile < 0) {
     delete p;

@@ -296,7 +296,14 @@ __device__ __forceinline__ i32x2 tr8_rows(unsigned p0, int rows) {
 //   64 x 64 / 32 x 64, WM = 2, WN = 1, NS = 8 / 10: narrow tiles (16-bit inputs) for
 //     small M, where N / 256 column tiles would leave most compute units
 //     idle: four times the workgroups, each with a deep ring (about 120 KB in
-//     flight) to keep its share of B streaming.
+//     flight) to keep its share of B streaming;
+//   32 x 32, WM = 2, WN = 1, NS = 6: twice the workgroups again.  A
+//     workgroup's stream of B runs at a rate of its own (about 20 GB/s on the
+//     64-column tiles, whatever the grid), so at small M the time is one
+//     workgroup's walk through K and more, narrower column tiles shorten it.
+//     Its 48 KB ring lets three workgroups share a CU (measured against 4,
+//     5, 8, 12 and 16 stages: the deeper rings gain up to 1 us at M <= 32
+//     and lose up to 6 us at M = 100 with B transposed).
 // Two workgroups share a CU when their rings fit in half the LDS; the
 // register budget then has to allow two waves per SIMD.  A four-wave
 // workgroup alone on its CU has one wave per SIMD and the whole register file.
@@ -358,8 +365,9 @@ __global__ __launch_bounds__(WM * WN * 64, (waves_per_simd<TBM, TBN, WM, WN, NS>
   // other paths alternate two fragment sets over an even number of k-steps
   static_assert(F8S ? KS == 1 : KS % 2 == 0, "k-steps per stage");
   // wave tiles are 64 columns wide (a 128-wide fp8 wave tile, one wave per
-  // SIMD on the 256 x 256 tile, compiles too but measured 6-13 % slower)
-  static_assert(WN * WTN == TBN && WTN == 64, "wave tile width");
+  // SIMD on the 256 x 256 tile, compiles too but measured 6-13 % slower);
+  // the 32-column tile of 16-bit inputs has 32-column wave tiles
+  static_assert(WN * WTN == TBN && (WTN == 64 || (WTN == 32 && EB == 2 && !T::I8)), "wave tile width");
 
   __shared__ __attribute__((aligned(1024))) char lds[LDS_BYTES];
   // LDS offsets of the A and B blocks of stage t.
@@ -413,7 +421,10 @@ __global__ __launch_bounds__(WM * WN * 64, (waves_per_simd<TBM, TBN, WM, WN, NS>
   auto bswz = [](int k) {
     if constexpr (EB == 2) {
       if constexpr (BSLOTS >= 16) return ((k & 3) << 2) ^ (((k >> 3) & 1) << 1);
-      else return ((k & 3) << 1) ^ ((k >> 3) & 1);
+      else if constexpr (BSLOTS == 8) return ((k & 3) << 1) ^ ((k >> 3) & 1);
+      // 64-byte rows (32 columns): rows k and k + 8 of one half-wave's read
+      // share banks unless their two slots are swapped over
+      else return ((k >> 3) & 1) << 1;
     } else {
       if constexpr (BSLOTS >= 16) return (k & 7) << 1;
       else if constexpr (BSLOTS == 8) return k & 7;
@@ -1237,6 +1248,7 @@ hipError_t launch_tiles(const gemm_plan_s& p, int tile, const GemmArgs& a, bool 
     switch (tile) {
       case GEMM_TILE_64x64: return launch_cfg<IN, 64, 64, 2, 1, 8, BT>(p, a, slice, s);
       case GEMM_TILE_32x64: return launch_cfg<IN, 32, 64, 2, 1, 10, BT>(p, a, slice, s);
+      case GEMM_TILE_32x32: return launch_cfg<IN, 32, 32, 2, 1, 6, BT>(p, a, slice, s);
       default: break;
     }
   }

@@ -328,7 +328,8 @@ hipError_t launch_in(const gemm_plan_s& p, int tile, const GemmArgs& a, bool sli
 hipError_t launch_gemm(const gemm_plan_s& p, int tile, const GemmArgs& a, bool slice_mode,
                        hipStream_t s) {
   if (tile == GEMM_TILE_256x256 || tile == GEMM_TILE_128x256 || tile == GEMM_TILE_32x256 ||
-      tile == GEMM_TILE_64x256 || tile == GEMM_TILE_32x64 || tile == GEMM_TILE_64x64)
+      tile == GEMM_TILE_64x256 || tile == GEMM_TILE_32x64 || tile == GEMM_TILE_64x64 ||
+      tile == GEMM_TILE_32x32)
     return launch_gemm_dma(p, tile, a, slice_mode, s);
   if (p.f8_fp32) return hipErrorInvalidValue;  // the planner keeps such plans on DMA tiles
   switch (p.in) {

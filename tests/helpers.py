@@ -174,7 +174,7 @@ def fp8_check_bound(C, C64, Cabs, K, out, dt, a_bits=None, b_bits=None, ii=None,
     return check_bound(C, C64, Cabs, K, out, bias=bias, window=win)
 
 
-NARROW_TILES = ("32x64", "64x64")   # DMA tiles of 64 columns: fp16 / bf16 inputs only
+NARROW_TILES = ("32x64", "64x64", "32x32")   # DMA tiles of 64 and 32 columns: fp16 / bf16 inputs only
 
 
 def tiles_for(dt: str, tiles):

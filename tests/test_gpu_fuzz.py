@@ -25,8 +25,8 @@ from tests.helpers import bits_of, dev, fp8_check_bound, log, out_torch_dtype, t
 pytestmark = pytest.mark.gpu
 
 ALL_TILES = ["256x256", "128x128", "32x128", "256x256_rs", "32x256", "64x256", "128x256", "32x64",
-             "64x64"]
-DMA_TILES = {"256x256", "32x256", "64x256", "128x256", "32x64", "64x64"}
+             "64x64", "32x32"]
+DMA_TILES = {"256x256", "32x256", "64x256", "128x256", "32x64", "64x64", "32x32"}
 
 
 def _case(seed):

@@ -23,7 +23,7 @@ from tests.helpers import (bits_of, check_bound, dev, expected_bits, log, out_to
 
 pytestmark = pytest.mark.gpu
 
-DMA_TILES = ["default", "256x256", "128x256", "64x256", "32x256", "32x64", "64x64"]
+DMA_TILES = ["default", "256x256", "128x256", "64x256", "32x256", "32x64", "64x64", "32x32"]
 BT = imm.PLAN_B_TRANSPOSED
 
 

@@ -20,7 +20,7 @@ from tests.helpers import (FP8, FP8_PLAIN_BOUND_MIN_K, bits_of, check_bound, dev
 pytestmark = pytest.mark.gpu
 
 TILES = ["256x256", "128x128", "32x128", "256x256_rs", "32x256", "64x256", "128x256", "32x64",
-         "64x64"]
+         "64x64", "32x32"]
 IN_DTYPES = ["f16", "bf16", "e4m3", "e5m2"]
 
 

@@ -20,7 +20,7 @@ from tests.helpers import dev, log, out_torch_dtype, tiles_for
 pytestmark = pytest.mark.gpu
 
 REPS = 12
-DMA_TILES = ["256x256", "128x256", "64x256", "32x256", "64x64", "32x64"]
+DMA_TILES = ["256x256", "128x256", "64x256", "32x256", "64x64", "32x64", "32x32"]
 
 
 def _once(plan, A, B, split):

@@ -177,7 +177,7 @@ def _plan_status(*args):
     ((8, 8, 8, 0, 4, -1, 0, 0, 1.0, 1.0), 2),     # split_k < 0
     ((8, 8, 8, 0, 4, 4097, 0, 0, 1.0, 1.0), 2),   # split_k too large
     ((8, 8, 8, 0, 4, 0, -1, 0, 1.0, 1.0), 2),     # group_m < 0
-    ((8, 8, 8, 0, 4, 0, 0, 10, 1.0, 1.0), 2),     # unknown tile
+    ((8, 8, 8, 0, 4, 0, 0, 11, 1.0, 1.0), 2),     # unknown tile
     ((8, 8, 8, 0, 4, 0, 0, 0, float("inf"), 1.0), 2),
     ((8, 8, 8, 0, 4, 0, 0, 0, 1.0, float("nan")), 2),
     ((2 ** 31, 8, 8, 0, 4, 0, 0, 0, 1.0, 1.0), 2),
@@ -473,7 +473,7 @@ def test_ozaki_column_maxima_chunks_are_capped():
 
 
 @pytest.mark.parametrize("M,N,K,tile,tile8", [
-    (1, 6144, 4096, "32x64", "32x256"), (64, 6144, 4096, "32x64", "32x256"),
+    (1, 6144, 4096, "32x32", "32x256"), (64, 6144, 4096, "32x64", "32x256"),
     (96, 6144, 4096, "64x64", "32x256"), (128, 6144, 4096, "64x64", "32x256"),
     (192, 6144, 4096, "32x256", "32x256"), (256, 6144, 4096, "32x256", "32x256"),
     (512, 6144, 4096, "64x256", "64x256"), (768, 6144, 4096, "128x256", "128x256"),
@@ -499,6 +499,23 @@ def test_tile_by_m_rule(M, N, K, tile, tile8):
             "tile", "split_k", "k_per_split", "block_m", "block_n")
         for k in same:
             assert flagged[k] == plain[k], (dt, k)
+
+
+@pytest.mark.parametrize("M,N,tile", [
+    (1, 6144, "32x32"), (64, 6144, "32x32"), (128, 6144, "32x32"), (192, 6144, "32x256"),
+    (512, 1024, "32x32"), (1024, 1024, "64x64"), (48, 14336, "64x64"), (1024, 6144, "128x256"),
+])
+def test_tile_by_m_rule_with_b_transposed(M, N, tile):
+    """With B transposed the 32 x 32 tile's further rounds cost less (its rows
+    stream faster and three of its workgroups share a compute unit), so it
+    covers more of the small-M range than with B as [K, N]."""
+    for dt in ("f16", "bf16"):
+        i = imm.gemm_plan_ex2(M, N, 4096, dt, "f32",
+                              flags=imm.PLAN_TILE_BY_M | imm.PLAN_B_TRANSPOSED).info
+        assert i["run_tile"] == imm.TILE[tile], dt
+    i = imm.gemm_plan_ex2(M, N, 4096, "e5m2", "f32",
+                          flags=imm.PLAN_TILE_BY_M | imm.PLAN_B_TRANSPOSED).info
+    assert i["run_tile"] not in {imm.TILE[t] for t in ("32x32", "32x64", "64x64")}
 
 
 @pytest.mark.parametrize("M,tile", [(1, "32x128"), (8, "32x128"), (32, "32x128"), (64, "64x256"),
@@ -577,13 +594,13 @@ def test_noalloc_entry_point_host_checks():
 
 
 def test_narrow_tiles_take_16_bit_inputs_only():
-    for tile in ("32x64", "64x64"):
+    for tile in ("32x64", "64x64", "32x32"):
         for dt in ("f16", "bf16"):
             for fl in (0, imm.PLAN_B_TRANSPOSED):
                 i = imm.gemm_plan_ex2(100, 6144, 4096, dt, "f32", tile=tile, flags=fl).info
                 assert i["run_tile"] == i["tile"] == imm.TILE[tile]
                 assert (i["run_block_m"], i["run_block_n"]) == tuple(map(int, tile.split("x")))
-                assert i["run_tiles_n"] == 6144 // 64
+                assert i["run_tiles_n"] == 6144 // int(tile.split("x")[1])
         for dt in ("e4m3", "e5m2"):
             assert _plan2_status(100, 6144, 4096, imm.DTYPE[dt], 4, 0, 0, imm.TILE[tile],
                                  1.0, 1.0, 0) == 2
