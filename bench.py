@@ -455,9 +455,16 @@ def settle(fn, torch, ms=SETTLE_MS):
             return n
 
 
-def time_launches(fn, n, warmup, torch, settle_ms=SETTLE_MS):
+def time_launches(fn, n, warmup, torch, settle_ms=SETTLE_MS, queue_ahead=False):
     """Per-call durations (ms) from HIP events recorded on the current stream,
-    after the settle launches and `warmup` untimed calls."""
+    after the settle launches and `warmup` untimed calls.
+
+    queue_ahead: for calls of a few tens of us, whose host side (argument
+    checks, launches, two event records) takes about as long as the GPU side.
+    The timed calls are then enqueued behind a spin kernel of a few ms, so the
+    GPU never waits for the host between them; otherwise a call's start event
+    can fire while the host is still preparing the launch, and some calls
+    measure 1.5-2x their kernel time."""
     SETTLE_LAUNCHES.append(settle(fn, torch, settle_ms) if settle_ms > 0 else 0)
     for _ in range(warmup):
         fn(0)
@@ -466,6 +473,9 @@ def time_launches(fn, n, warmup, torch, settle_ms=SETTLE_MS):
           for _ in range(n)]
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
+    if queue_ahead:
+        # about 0.1 ms of engine cycles per timed call, at least 2 ms
+        torch.cuda._sleep(int(2.4e5 * max(20, n)))
     t0.record()
     for i in range(n):
         ev[i][0].record()
@@ -547,14 +557,15 @@ def cpu_baseline(samples):
             "per_config": per}
 
 
-def bench_square(name, steps, warmup, torch, imm, wl):
+def bench_square(name, steps, warmup, torch, imm, wl, queue_ahead=False):
     w = wl.WORKLOADS[name]
     A, B = w.make()
     Ad, Bd = A.cuda(), B.cuda()
     plan = imm.gemm_plan(w.M, w.N, w.K, w.dtype)
     out_t = torch.float32 if w.out == "f32" else torch.bfloat16
     C = torch.empty((w.M, w.N), dtype=out_t, device="cuda")
-    per, total = time_launches(lambda i: imm.gemm_run(plan, Ad, Bd, C), steps, warmup, torch)
+    per, total = time_launches(lambda i: imm.gemm_run(plan, Ad, Bd, C), steps, warmup, torch,
+                               queue_ahead=queue_ahead)
     return w, plan, per, total, (A, B, Ad, Bd)
 
 
@@ -603,7 +614,7 @@ def bench_splitk(name, split, torch, imm, wl, n=30, warmup=5, M=None):
                      device="cuda")
     per, _ = time_launches(
         lambda i: imm.gemm_splitk_run(plan, As[i % copies], Bs[i % copies], C, ws),
-        n, warmup, torch)
+        n, warmup, torch, queue_ahead=True)
     algo = bytes_in + Mrows * w.N * 4
     med = statistics.median(per)
     out = {"M": Mrows, "N": w.N, "K": w.K, "split_k": plan.info["split_k"],
@@ -619,7 +630,7 @@ def bench_splitk(name, split, torch, imm, wl, n=30, warmup=5, M=None):
         if pm.info["tile"] != plan.info["tile"]:
             pmm, _ = time_launches(
                 lambda i: imm.gemm_splitk_run(pm, As[i % copies], Bs[i % copies], C, ws),
-                n, warmup, torch)
+                n, warmup, torch, queue_ahead=True)
             mm_ = statistics.median(pmm)
             out.update({"tile_by_m": f"{pm.info['block_m']}x{pm.info['block_n']}",
                         "tile_by_m_median_us": mm_ * 1e3,
@@ -693,17 +704,28 @@ def bench_m_sweep(torch, imm, wl, N=6144, K=4096, ms=(1, 16, 64, 256, 1024, 4096
     g = wl.gen(6000)
     A = wl.uniform((max(ms), K), "f16", g).cuda()
     B = wl.uniform((K, N), "f16", g).cuda()
+    W = B.t().contiguous()
     out = []
     for m in ms:
         a = A[:m].contiguous()
         plan = imm.gemm_plan(m, N, K, "f16")
         C = torch.empty((m, N), dtype=torch.float32, device="cuda")
-        per, _ = time_launches(lambda i: imm.gemm_run(plan, a, B, C), 20, 5, torch)
+        per, _ = time_launches(lambda i: imm.gemm_run(plan, a, B, C), 20, 5, torch, queue_ahead=True)
         # the same bits with the tile taken from M (GEMM_PLAN_TILE_BY_M)
         mplan = imm.gemm_plan_ex2(m, N, K, "f16", "f32", flags=imm.PLAN_TILE_BY_M)
-        mper, _ = time_launches(lambda i: imm.gemm_run(mplan, a, B, C), 20, 5, torch)
+        mper, _ = time_launches(lambda i: imm.gemm_run(mplan, a, B, C), 20, 5, torch,
+                                queue_ahead=True)
         ref = torch.empty((m, N), dtype=torch.float16, device="cuda")
-        tper, _ = time_launches(lambda i: torch.matmul(a, B, out=ref), 20, 5, torch)
+        tper, _ = time_launches(lambda i: torch.matmul(a, B, out=ref), 20, 5, torch,
+                                queue_ahead=True)
+        # the weight layout of a linear layer: W [N, K] read in place
+        # (GEMM_PLAN_B_TRANSPOSED), tile from M, next to F.linear on the same W
+        wplan = imm.gemm_plan_ex2(m, N, K, "f16", "f32",
+                                  flags=imm.PLAN_TILE_BY_M | imm.PLAN_B_TRANSPOSED)
+        wper, _ = time_launches(lambda i: imm.gemm_run(wplan, a, W, C), 20, 5, torch,
+                                queue_ahead=True)
+        lper, _ = time_launches(lambda i: torch.nn.functional.linear(a, W), 20, 5, torch,
+                                queue_ahead=True)
         med, mmed, tmed = statistics.median(per), statistics.median(mper), statistics.median(tper)
         out.append({"M": m, "N": N, "K": K,
                     "tile": f"{plan.info['run_block_m']}x{plan.info['run_block_n']}",
@@ -711,7 +733,10 @@ def bench_m_sweep(torch, imm, wl, N=6144, K=4096, ms=(1, 16, 64, 256, 1024, 4096
                     "tile_by_m": f"{mplan.info['run_block_m']}x{mplan.info['run_block_n']}",
                     "tile_by_m_median_us": mmed * 1e3,
                     "torch_matmul_median_us": tmed * 1e3,
-                    "torch_matmul_TFLOPs": 2.0 * m * N * K / (tmed * 1e-3) / 1e12})
+                    "torch_matmul_TFLOPs": 2.0 * m * N * K / (tmed * 1e-3) / 1e12,
+                    "weight_nk_tile_by_m": f"{wplan.info['run_block_m']}x{wplan.info['run_block_n']}",
+                    "weight_nk_tile_by_m_median_us": statistics.median(wper) * 1e3,
+                    "torch_linear_median_us": statistics.median(lper) * 1e3})
     return out
 
 
@@ -986,7 +1011,8 @@ def main():
         secondary["fp8_e5m2_bf16_out"] = {}
         for n8, steps8 in ((4096, 30), (8192, 30), (16384, 10)):
             log(f"fp8 e5m2 {n8}^3")
-            w8, plan8, per8, _, h8 = bench_square(f"square_e5m2_{n8}", steps8, 5, torch, imm, wl)
+            w8, plan8, per8, _, h8 = bench_square(f"square_e5m2_{n8}", steps8, 5, torch, imm, wl,
+                                                  queue_ahead=n8 == 4096)
             med8 = statistics.median(per8)
             e8 = {**summary(per8), "TFLOPs": w8.flops / (med8 * 1e-3) / 1e12,
                   "pct_mfma_peak": 100 * w8.flops / (med8 * 1e-3) / 1e12 / PEAK_TFLOPS["e5m2"]}
@@ -1008,14 +1034,15 @@ def main():
             # the default plan and GEMM_PLAN_TILE_BY_M in alternating rounds, so
             # that the part's clock (which follows its recent power draw) treats
             # both alike; each reports its best round's median
-            wn, _, pn, _, hn = bench_square(n, 30, 10, torch, imm, wl)
+            wn, _, pn, _, hn = bench_square(n, 30, 10, torch, imm, wl, queue_ahead=True)
             pd = imm.gemm_plan(wn.M, wn.N, wn.K, wn.dtype)
             mp = imm.gemm_plan_ex2(wn.M, wn.N, wn.K, wn.dtype, wn.out, flags=imm.PLAN_TILE_BY_M)
             Cn = torch.empty((wn.M, wn.N), dtype=torch.float32, device="cuda")
             rounds = {"default": [statistics.median(pn)], "tile_by_m": []}
             for r in range(3):
                 for key, pl in (("tile_by_m", mp), ("default", pd)):
-                    pr, _ = time_launches(lambda i: imm.gemm_run(pl, hn[2], hn[3], Cn), 30, 5, torch)
+                    pr, _ = time_launches(lambda i: imm.gemm_run(pl, hn[2], hn[3], Cn), 30, 5, torch,
+                                          queue_ahead=True)
                     rounds[key].append(statistics.median(pr))
                     if key == "default":
                         pn = pr if statistics.median(pr) < statistics.median(pn) else pn
@@ -1055,7 +1082,9 @@ def main():
         secondary["qkv_f16_N6144_K4096_us"] = [
             {"M": x["M"], "default": round(x["median_us"], 1),
              "tile_by_m": round(x["tile_by_m_median_us"], 1),
-             "torch": round(x["torch_matmul_median_us"], 1)} for x in extra["qkv_m_sweep_f16"]]
+             "torch": round(x["torch_matmul_median_us"], 1),
+             "w_nk_tile_by_m": round(x["weight_nk_tile_by_m_median_us"], 1),
+             "torch_linear": round(x["torch_linear_median_us"], 1)} for x in extra["qkv_m_sweep_f16"]]
         torch.cuda.empty_cache()
         log("huge-K fp16 256x256x131072, split-K path")
         # split 0 = the plan's default for this shape
