@@ -135,13 +135,16 @@ typedef enum {
                                reduction-dominated shapes */
   GEMM_TILE_64x256 = 6,     /* 4 waves, DMA ring */
   GEMM_TILE_128x256 = 7,    /* 8 waves, DMA ring of 3 stages */
-  GEMM_TILE_32x64 = 8,      /* 2 waves, DMA ring of 10 stages; fp16 / bf16 only:
-                               narrow tile for small M (4x the workgroups of
-                               32x256) */
-  GEMM_TILE_64x64 = 9,      /* 2 waves, DMA ring of 8 stages; fp16 / bf16 only */
-  GEMM_TILE_32x32 = 10      /* 2 waves, DMA ring of 6 stages (three
-                               workgroups per compute unit); fp16 / bf16
-                               only: twice the workgroups of 32x64 for
+  GEMM_TILE_32x64 = 8,      /* 2 waves, DMA ring of 3 stages of 256 bytes of
+                               K (two workgroups per compute unit); fp16 /
+                               bf16 only: narrow tile for small M (4x the
+                               workgroups of 32x256) */
+  GEMM_TILE_64x64 = 9,      /* 2 waves, DMA ring of 2 stages of 256 bytes of
+                               K (two workgroups per compute unit); fp16 /
+                               bf16 only */
+  GEMM_TILE_32x32 = 10      /* 2 waves, DMA ring of 3 stages of 256 bytes of
+                               K (three workgroups per compute unit); fp16 /
+                               bf16 only: twice the workgroups of 32x64 for
                                small M */
 } gemm_tile;
 

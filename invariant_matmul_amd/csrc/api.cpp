@@ -102,38 +102,41 @@ int default_run_tile(int64_t N, int64_t K, int eb) {
 
 // GEMM_PLAN_TILE_BY_M: the DMA tile with the least estimated time.  A grid
 // runs in rounds of 256 workgroups (a 256-CU MI355X), and one round of a
-// tile takes about the same time whatever the shape: it is a workgroup's walk
-// through K.  Units per round, fitted on sweeps at K = 4096 (M = 1 ... 2048;
-// N = 1024, 4096, 6144, 14336; both B layouts), where one round took about
-// 27, 29, 32, 40, 47 and 71 us: 32 x 64: 134, 64 x 64: 144, 32 x 256: 159,
-// 64 x 256: 191, 128 x 256: 255, 256 x 256: 383.  These tiles take a whole
-// compute unit for their LDS ring.  Three 32 x 32 rings share one, so its
-// second and third rounds overlap the first: its first round costs 100 (B
-// [K, N]) or 80 (B transposed, whose K-contiguous rows stream faster), every
-// further round 60 or 30.  Cost = rounds x units; the smaller tile wins a
-// tie.  On that sweep (112 shapes) this picks the fastest tile, or one within
-// 3 % of it, at 106 shapes and is at most 8 % off at the others.  The 64-
-// and 32-column tiles take 16-bit inputs only.  Bits do not depend on the
-// tile.
+// tile takes about the same time whatever the shape: it is a workgroup's
+// walk through K.  The narrow tiles' rings let c workgroups share a compute
+// unit (c = 3 for 32x32, 2 for 32x64 and 64x64, 1 for the others), so their
+// rounds come in waves of c, and a round that shares its compute units with
+// the wave's first costs much less than a new wave.  Estimated time (in
+// units of 0.2 us) = waves x wave cost + (rounds - waves) x shared-round
+// cost, per tile and B layout, fitted on a sweep at K = 4096 (M = 1 ...
+// 2048; N = 1024, 4096, 6144, 14336; both B layouts; 112 shapes, identical
+// bits from every tile): there it picks the fastest tile, or one within
+// 3 % of it, at 105 shapes, and one at most 11 % slower at the others.  The
+// smaller tile wins a tie.  The 64- and 32-column tiles take 16-bit inputs
+// only.  Bits do not depend on the tile.
 int tile_by_m(int64_t M, int64_t N, int eb, bool b_trans) {
   struct Cand {
-    int tile, rows, cols, units;
+    int tile, rows, cols, per_cu;
+    int wave[2], shared[2];  // [K, N] B, transposed B
   };
-  static const Cand kCands[7] = {{GEMM_TILE_32x32, 32, 32, 0},     {GEMM_TILE_32x64, 32, 64, 134},
-                                 {GEMM_TILE_64x64, 64, 64, 144},   {GEMM_TILE_32x256, 32, 256, 159},
-                                 {GEMM_TILE_64x256, 64, 256, 191},
-                                 {GEMM_TILE_128x256, 128, 256, 255},
-                                 {GEMM_TILE_256x256, 256, 256, 383}};
+  static const Cand kCands[7] = {
+      {GEMM_TILE_32x32, 32, 32, 3, {106, 81}, {14, 12}},
+      {GEMM_TILE_32x64, 32, 64, 2, {112, 99}, {16, 19}},
+      {GEMM_TILE_64x64, 64, 64, 2, {172, 156}, {14, 9}},
+      {GEMM_TILE_32x256, 32, 256, 1, {219, 208}, {0, 0}},
+      {GEMM_TILE_64x256, 64, 256, 1, {279, 256}, {0, 0}},
+      {GEMM_TILE_128x256, 128, 256, 1, {274, 269}, {0, 0}},
+      {GEMM_TILE_256x256, 256, 256, 1, {443, 429}, {0, 0}}};
+  const int l = b_trans ? 1 : 0;
   int best = -1;
   int64_t best_cost = -1;
   for (int i = 0; i < 7; ++i) {
-    if (is_narrow_tile(kCands[i].tile) && eb != 2) continue;
-    const int64_t wgs = ((M + kCands[i].rows - 1) / kCands[i].rows) *
-                        ((N + kCands[i].cols - 1) / kCands[i].cols);
+    const Cand& c = kCands[i];
+    if (is_narrow_tile(c.tile) && eb != 2) continue;
+    const int64_t wgs = ((M + c.rows - 1) / c.rows) * ((N + c.cols - 1) / c.cols);
     const int64_t rounds = (wgs + 255) / 256;
-    const int64_t cost = kCands[i].tile == GEMM_TILE_32x32
-                             ? (b_trans ? 80 + (rounds - 1) * 30 : 100 + (rounds - 1) * 60)
-                             : rounds * kCands[i].units;
+    const int64_t waves = (rounds + c.per_cu - 1) / c.per_cu;
+    const int64_t cost = waves * c.wave[l] + (rounds - waves) * c.shared[l];
     if (best_cost < 0 || cost < best_cost) {
       best = i;
       best_cost = cost;
@@ -167,13 +170,14 @@ bool is_dma_tile(int tile) {
 
 
 // The DMA kernels address one A tile (bm rows of K) and one B stage (128
-// bytes of K: 128 / eb rows of N elements, or with B transposed bn rows of
-// K) with 32-bit offsets.
+// bytes of K, 256 on the 32x32 tile: that many / eb rows of N elements, or
+// with B transposed bn rows of K) with 32-bit offsets.
 bool dma_offsets_fit(int tile, int64_t N, int64_t K, int eb, bool b_trans) {
   int bm, bn, wm, wn;
   tile_shape(tile, &bm, &bn, &wm, &wn);
   const int64_t lim = ((int64_t)1 << 31) - 256;
-  return bm * K * eb < lim && (b_trans ? bn * K * eb < lim : 128 * N < lim);
+  const int64_t stage = is_narrow_tile(tile) ? 256 : 128;
+  return bm * K * eb < lim && (b_trans ? bn * K * eb < lim : stage * N < lim);
 }
 
 // A DMA tile whose offsets would overflow falls back to a register-staged

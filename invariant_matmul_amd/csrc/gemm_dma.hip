@@ -231,7 +231,15 @@ struct M16Sched {
   }
 };
 
-constexpr int SKB = 128;  // bytes of K per row per stage
+// Bytes of K per row per stage: 128 (whole cache lines of A rows), and 256
+// on the narrow tiles (64 and 32 columns, 16-bit inputs), whose small-M time
+// is one workgroup's walk through K: there each stage costs a fixed latency
+// (LDS waits, the barrier, the DMA wait) whatever it holds, so fewer, larger
+// stages shorten the walk.
+template <int TBN>
+constexpr int stage_kbytes() {
+  return TBN <= 64 ? 256 : 128;
+}
 constexpr unsigned OOB = 0x80000000u;
 constexpr int NREC = 0x7fffffff;
 constexpr int RSRC_FLAGS = 0x00020000;
@@ -255,7 +263,11 @@ __device__ __forceinline__ i32x2 tr16_rows(unsigned p0, int rows) {
     case 32: return ds_read_tr16_b64<32 * BROW>(p0);
     case 36: return ds_read_tr16_b64<36 * BROW>(p0);
     case 48: return ds_read_tr16_b64<48 * BROW>(p0);
-    default: return ds_read_tr16_b64<52 * BROW>(p0);
+    case 52: return ds_read_tr16_b64<52 * BROW>(p0);
+    case 64: return ds_read_tr16_b64<64 * BROW>(p0);
+    case 68: return ds_read_tr16_b64<68 * BROW>(p0);
+    case 96: return ds_read_tr16_b64<96 * BROW>(p0);
+    default: return ds_read_tr16_b64<100 * BROW>(p0);
   }
 }
 // int8 steps are 32 K rows: two reads of 8 rows per half-step
@@ -293,23 +305,23 @@ __device__ __forceinline__ i32x2 tr8_rows(unsigned p0, int rows) {
 //   64 x 256 / 32 x 256, WM = 1, WN = 4, NS = 4: short tiles for
 //     reduction-dominated shapes (wave tile 64 x 64 / 32 x 64), where the time
 //     is the stream of B;
-//   64 x 64 / 32 x 64, WM = 2, WN = 1, NS = 8 / 10: narrow tiles (16-bit inputs) for
-//     small M, where N / 256 column tiles would leave most compute units
-//     idle: four times the workgroups, each with a deep ring (about 120 KB in
-//     flight) to keep its share of B streaming;
-//   32 x 32, WM = 2, WN = 1, NS = 6: twice the workgroups again.  A
-//     workgroup's stream of B runs at a rate of its own (about 20 GB/s on the
-//     64-column tiles, whatever the grid), so at small M the time is one
-//     workgroup's walk through K and more, narrower column tiles shorten it.
-//     Its 48 KB ring lets three workgroups share a CU (measured against 4,
-//     5, 8, 12 and 16 stages: the deeper rings gain up to 1 us at M <= 32
-//     and lose up to 6 us at M = 100 with B transposed).
+//   64 x 64 / 32 x 64 / 32 x 32, WM = 2, WN = 1, NS = 2 / 3 / 3, with 256-byte
+//     K stages: narrow tiles (16-bit inputs) for small M, where N / 256
+//     column tiles would leave most compute units idle.  A workgroup's
+//     stream of B runs at a rate of its own (about 20 GB/s on the 64-column
+//     tiles with 128-byte stages, whatever the grid), so at small M the time
+//     is one workgroup's walk through K, which fewer, larger stages and more,
+//     narrower column tiles shorten.  Their rings (64, 72 and 48 KB) let two,
+//     two and three workgroups share a compute unit, which gains more at
+//     mid M than deeper rings gain at M = 1 (measured against 128-byte
+//     stages with 6-10 stage rings: the 64 x 64 tile at M = 1 / 256 on the
+//     fused-QKV shape 39.9 / 76.2 us before, 30.1 / 35.7 after).
 // Two workgroups share a CU when their rings fit in half the LDS; the
 // register budget then has to allow two waves per SIMD.  A four-wave
 // workgroup alone on its CU has one wave per SIMD and the whole register file.
 template <int TBM, int TBN, int WM, int WN, int NS>
 constexpr int waves_per_simd() {
-  return WM * WN == 4 && NS * (TBM + TBN) * SKB > 80 * 1024 ? 1 : 2;
+  return WM * WN == 4 && NS * (TBM + TBN) * stage_kbytes<TBN>() > 80 * 1024 ? 1 : 2;
 }
 
 // BT: B is given transposed, as [N, K] row-major (the weight layout of a
@@ -340,6 +352,8 @@ __global__ __launch_bounds__(WM * WN * 64, (waves_per_simd<TBM, TBN, WM, WN, NS>
   constexpr int FM = WTM / BLK;              // MFMA row blocks per wave
   constexpr int FN = WTN / BLK;              // MFMA column blocks per wave
   constexpr int NM = FM * FN;                // MFMAs per k-step per wave
+  constexpr int SKB = stage_kbytes<TBN>();   // bytes of K per row per stage
+  static_assert(SKB == 128 || (EB == 2 && !T::I8 && !W16 && MODE != MODE_OZAKI), "256-byte stages");
   constexpr int A_STAGE = TBM * SKB;         // bytes of A per stage
   constexpr int B_STAGE = TBN * SKB;         // bytes of B per stage (32 KB)
   constexpr int STAGE = A_STAGE + B_STAGE;
@@ -407,8 +421,13 @@ __global__ __launch_bounds__(WM * WN * 64, (waves_per_simd<TBM, TBN, WM, WN, NS>
   const char* A = static_cast<const char*>(g.A);
   const char* B = static_cast<const char*>(g.B);
 
-  // A row r keeps its 16-byte slot c at c ^ aswz(r).
-  auto aswz = [](int r) { return (r >> 1) & 7; };
+  // A row r keeps its 16-byte slot c at c ^ aswz(r): 128-byte rows put rows
+  // r and r + 2 on the same banks, 256-byte rows every row, so the 16 rows a
+  // quarter-wave reads take 8 or 16 different slots.
+  auto aswz = [](int r) {
+    if constexpr (SKB == 256) return r & 15;
+    else return (r >> 1) & 7;
+  };
   // B row k (the [K, N] layout) keeps its 16-byte slot c at c ^ bswz(k): a
   // bijection of the row's BSLOTS slots, chosen so that the K rows one
   // transposing read gathers lie on different banks.  A lane's transposing
@@ -1246,9 +1265,9 @@ hipError_t launch_tiles(const gemm_plan_s& p, int tile, const GemmArgs& a, bool 
   }
   if constexpr (InT<IN>::EB == 2) {  // the narrow tiles take 16-bit inputs only
     switch (tile) {
-      case GEMM_TILE_64x64: return launch_cfg<IN, 64, 64, 2, 1, 8, BT>(p, a, slice, s);
-      case GEMM_TILE_32x64: return launch_cfg<IN, 32, 64, 2, 1, 10, BT>(p, a, slice, s);
-      case GEMM_TILE_32x32: return launch_cfg<IN, 32, 32, 2, 1, 6, BT>(p, a, slice, s);
+      case GEMM_TILE_64x64: return launch_cfg<IN, 64, 64, 2, 1, 2, BT>(p, a, slice, s);
+      case GEMM_TILE_32x64: return launch_cfg<IN, 32, 64, 2, 1, 3, BT>(p, a, slice, s);
+      case GEMM_TILE_32x32: return launch_cfg<IN, 32, 32, 2, 1, 3, BT>(p, a, slice, s);
       default: break;
     }
   }

@@ -474,14 +474,14 @@ def test_ozaki_column_maxima_chunks_are_capped():
 
 @pytest.mark.parametrize("M,N,K,tile,tile8", [
     (1, 6144, 4096, "32x32", "32x256"), (64, 6144, 4096, "32x64", "32x256"),
-    (96, 6144, 4096, "64x64", "32x256"), (128, 6144, 4096, "64x64", "32x256"),
-    (192, 6144, 4096, "32x256", "32x256"), (256, 6144, 4096, "32x256", "32x256"),
-    (512, 6144, 4096, "64x256", "64x256"), (768, 6144, 4096, "128x256", "128x256"),
+    (96, 6144, 4096, "32x64", "32x256"), (128, 6144, 4096, "32x64", "32x256"),
+    (192, 6144, 4096, "64x64", "32x256"), (256, 6144, 4096, "64x64", "32x256"),
+    (512, 6144, 4096, "128x256", "128x256"), (768, 6144, 4096, "128x256", "128x256"),
     (1024, 6144, 4096, "128x256", "128x256"), (1536, 6144, 4096, "256x256", "256x256"),
     (2048, 6144, 4096, "256x256", "256x256"), (3072, 6144, 4096, "128x256", "128x256"),
-    (512, 1024, 4096, "32x64", "32x256"), (1024, 1024, 4096, "64x64", "32x256"),
-    (2048, 1024, 4096, "32x256", "32x256"), (48, 14336, 4096, "64x64", "32x256"),
-    (2048, 2048, 2048, "64x256", "64x256"), (4096, 4096, 4096, "256x256", "256x256"),
+    (512, 1024, 4096, "32x64", "32x256"), (1024, 1024, 4096, "32x64", "32x256"),
+    (2048, 1024, 4096, "64x64", "32x256"), (48, 14336, 4096, "32x64", "32x256"),
+    (2048, 2048, 2048, "128x256", "128x256"), (4096, 4096, 4096, "256x256", "256x256"),
     (8192, 8192, 8192, "256x256", "256x256"),
 ])
 def test_tile_by_m_rule(M, N, K, tile, tile8):
@@ -502,13 +502,14 @@ def test_tile_by_m_rule(M, N, K, tile, tile8):
 
 
 @pytest.mark.parametrize("M,N,tile", [
-    (1, 6144, "32x32"), (64, 6144, "32x32"), (128, 6144, "32x32"), (192, 6144, "32x256"),
-    (512, 1024, "32x32"), (1024, 1024, "64x64"), (48, 14336, "64x64"), (1024, 6144, "128x256"),
+    (1, 6144, "32x32"), (64, 6144, "32x32"), (128, 6144, "32x32"), (192, 6144, "64x64"),
+    (512, 6144, "64x256"), (512, 1024, "32x32"), (1024, 1024, "32x64"), (48, 14336, "32x64"),
+    (1024, 6144, "128x256"),
 ])
 def test_tile_by_m_rule_with_b_transposed(M, N, tile):
-    """With B transposed the 32 x 32 tile's further rounds cost less (its rows
-    stream faster and three of its workgroups share a compute unit), so it
-    covers more of the small-M range than with B as [K, N]."""
+    """With B transposed the narrow tiles' rows stream faster (K-contiguous),
+    so the 32 x 32 tile covers more of the small-M range than with B as
+    [K, N]."""
     for dt in ("f16", "bf16"):
         i = imm.gemm_plan_ex2(M, N, 4096, dt, "f32",
                               flags=imm.PLAN_TILE_BY_M | imm.PLAN_B_TRANSPOSED).info

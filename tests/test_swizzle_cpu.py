@@ -44,8 +44,9 @@ def test_swizzle_ignores_the_read_offsets(eb, tbn):
     # (t < 8) for fp8; the reads add the offsets below
     bslots = tbn * eb // 16
     if eb == 2:
+        # the narrow tiles' 256-byte stages have four k-steps
         bases = [8 * g + t for g in range(4) for t in range(4)]
-        offsets = [4 * r + 32 * ks for r in range(2) for ks in range(2)]
+        offsets = [4 * r + 32 * ks for r in range(2) for ks in range(4 if tbn <= 64 else 2)]
     else:
         bases = [32 * g + t for g in range(4) for t in range(8)]
         offsets = [8 * r for r in range(4)]
@@ -85,12 +86,13 @@ def _distinct_banks(addrs, lanes):
 
 @pytest.mark.parametrize("eb,tbn", CASES)
 def test_transposing_reads_hit_distinct_banks(eb, tbn):
-    offsets = [4 * r + 32 * ks for r in range(2) for ks in range(2)] if eb == 2 else \
+    kbytes = 256 if tbn <= 64 else 128  # K bytes per stage
+    offsets = [4 * r + 32 * ks for r in range(2) for ks in range(kbytes // 64)] if eb == 2 else \
         [8 * r for r in range(4)]
     for j in range(tbn // 16):
         for off in offsets:
             addrs = _read_addrs(eb, tbn, j, off)
-            assert max(addrs) + 8 <= (128 // eb) * tbn * eb  # inside the stage's B block
+            assert max(addrs) + 8 <= (kbytes // eb) * tbn * eb  # inside the stage's B block
             assert _distinct_banks(addrs, 16), (j, off)
             if tbn == 32:
                 assert _distinct_banks(addrs, 32), (j, off)
@@ -109,3 +111,24 @@ def test_the_32_column_swizzle_separates_rows_k_and_k_plus_8():
         return out
     assert not _distinct_banks(addrs(False), 32)
     assert _distinct_banks(addrs(True), 32)
+
+
+def aswz(row_bytes: int, r: int) -> int:
+    return r & 15 if row_bytes == 256 else (r >> 1) & 7
+
+
+@pytest.mark.parametrize("row_bytes", [128, 256])
+def test_a_rows_quarter_waves_hit_distinct_banks(row_bytes):
+    """A (and B given transposed): the 16 lanes of a quarter-wave read 16
+    bytes of rows base + 0 .. 15 at one slot c; the row swizzle puts them on
+    64 distinct banks, for every slot c and block row base."""
+    slots = row_bytes // 16
+    for base in range(0, 64, 16):
+        for c in range(slots):
+            assert sorted(c2 ^ aswz(row_bytes, base) for c2 in range(slots)) == list(range(slots))
+            banks = []
+            for lb in range(16):
+                r = base + lb
+                a = r * row_bytes + ((c ^ aswz(row_bytes, lb)) << 4)
+                banks += [(a // 4 + d) % 64 for d in range(4)]
+            assert len(set(banks)) == 64, (row_bytes, base, c)
