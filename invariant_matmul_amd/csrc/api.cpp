@@ -61,14 +61,18 @@ bool reduction_dominated(int64_t N, int64_t K) { return K >= 2 * N; }
 
 // Small B (at most 4 MB, the L2 of one XCD): 256 x 256 tiles leave most of
 // the machine idle unless M is large (1024^3 has 16 of them), so these
-// shapes take the 128 x 256 tile, the one whose worst case over M is least.
-// Measured on N = K = 1024 fp16 (us, 32 x 256 / 128 x 256 / 256 x 256):
-// M = 1: 15.8 / 16.8 / 24.2; M = 1024: 16.0 / 17.5 / 25.1; M = 4096: 28.4 /
-// 20.1 / 27.3; M = 16384: 103.8 / 44.2 / 38.7.  On N = K = 2048 e5m2: M =
-// 1024: 15.0 / 18.4 / 25.8; M = 4096: 44.4 / 23.4 / 28.8; M = 16384: 163.2 /
-// 77.6 / 67.3.  The 32-row tile wins by up to 25 % at small M and loses up to
-// 2.7x at large M, where every 32 rows of A re-read B from L2.  Bits do not
-// depend on the tile, and these shapes are never split.
+// shapes take the tile whose worst case over M is least: 64 x 64 for 16-bit
+// inputs, 128 x 256 for fp8 (which the narrow tiles do not take).  Measured
+// (us; fp16, fp32 out; 32 x 32 / 32 x 64 / 64 x 64 / 32 x 256 / 128 x 256 /
+// 256 x 256) on N = K = 1024: M = 1: 8.2 / 9.9 / 11.4 / 14.8 / 16.5 / 23.9;
+// M = 1024: 15.4 / 11.4 / 11.7 / 15.7 / 17.7 / 25.4; M = 4096: 37.9 / 34.0 /
+// 23.1 / 28.2 / 19.7 / 27.9; M = 16384: 131.6 / 119.5 / 77.0 / 99.7 / 48.7 /
+// 40.0.  Worst case against the fastest tile at each M, over N = K = 1024,
+// N = 2048 K = 1024 and N = 1024 K = 2048, both B layouts: 64 x 64 2.07x
+// (large M), 128 x 256 2.31x (small M), the others 2.9x and more.  On
+// N = K = 2048 e5m2 (us, 32 x 256 / 128 x 256 / 256 x 256): M = 1024: 15.0 /
+// 18.4 / 25.8; M = 4096: 44.4 / 23.4 / 28.8; M = 16384: 163.2 / 77.6 / 67.3.
+// Bits do not depend on the tile, and these shapes are never split.
 bool small_b(int64_t N, int64_t K, int eb) { return N * K * eb <= ((int64_t)4 << 20); }
 
 bool dma_offsets_fit(int tile, int64_t N, int64_t K, int eb, bool b_trans);
@@ -79,11 +83,13 @@ bool is_narrow_tile(int tile) {
   return tile == GEMM_TILE_32x64 || tile == GEMM_TILE_64x64 || tile == GEMM_TILE_32x32;
 }
 
+int small_b_tile(int eb) { return eb == 2 ? GEMM_TILE_64x64 : GEMM_TILE_128x256; }
+
 // Tile of the split-K path.  Past the K where a 128-row tile's 32-bit A
 // offsets overflow, narrow shapes keep a DMA tile of 64 rows (the split,
 // and so the bits, depend only on the tile's 256 columns).
 int default_tile(int64_t N, int64_t K, int eb) {
-  if (!reduction_dominated(N, K)) return small_b(N, K, eb) ? GEMM_TILE_128x256 : GEMM_TILE_256x256;
+  if (!reduction_dominated(N, K)) return small_b(N, K, eb) ? small_b_tile(eb) : GEMM_TILE_256x256;
   if (N > 512) return GEMM_TILE_32x128;
   return dma_offsets_fit(GEMM_TILE_128x256, N, K, eb, false) ? GEMM_TILE_128x256 : GEMM_TILE_64x256;
 }
@@ -95,7 +101,7 @@ int default_tile(int64_t N, int64_t K, int eb) {
 // the large tile except for small B (as above) and narrow N (N <= 512, where
 // 256 columns already cover all of N).
 int default_run_tile(int64_t N, int64_t K, int eb) {
-  if (small_b(N, K, eb)) return GEMM_TILE_128x256;
+  if (small_b(N, K, eb)) return small_b_tile(eb);
   if (reduction_dominated(N, K) && N <= 512) return GEMM_TILE_64x256;
   return GEMM_TILE_256x256;
 }

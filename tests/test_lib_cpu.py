@@ -104,16 +104,19 @@ def test_default_plans_of_the_workloads():
     # fp8 slices of 2048 elements are 16 steps: no extra doubling
     hk8 = imm.gemm_plan(256, 256, 131072, "e5m2").info
     assert (hk8["block_m"], hk8["split_k"]) == (128, 64)
-    # small B: the 128 x 256 tile, for the single pass and the (unsplit) split path
-    for dt in ("f16", "e5m2", "bf16"):
+    # small B: the 64 x 64 tile for 16-bit inputs, 128 x 256 for fp8, for the
+    # single pass and the (unsplit) split path
+    for dt, tile in (("f16", (64, 64)), ("e5m2", (128, 256)), ("bf16", (64, 64))):
         small = imm.gemm_plan(1024, 1024, 1024, dt).info
-        assert (small["run_block_m"], small["run_block_n"]) == (128, 256)
-        assert (small["block_m"], small["block_n"], small["split_k"]) == (128, 256, 1)
+        assert (small["run_block_m"], small["run_block_n"]) == tile
+        assert (small["block_m"], small["block_n"], small["split_k"]) == (*tile, 1)
+        bt = imm.gemm_plan_ex2(1024, 1024, 1024, dt, "f32", flags=imm.PLAN_B_TRANSPOSED).info
+        assert (bt["run_block_m"], bt["run_block_n"]) == tile
     # a reduction-dominated small B keeps its split path (and bits); the single pass
-    # takes the 128 x 256 tile too
+    # takes the small-B tile too
     rd = imm.gemm_plan(16, 1024, 2048, "f16").info
     assert (rd["block_m"], rd["block_n"]) == (32, 128) and rd["split_k"] > 1
-    assert (rd["run_block_m"], rd["run_block_n"]) == (128, 256)
+    assert (rd["run_block_m"], rd["run_block_n"]) == (64, 64)
 
 
 @pytest.mark.parametrize("M,N,K,dt,split,gm", [
@@ -220,7 +223,7 @@ def test_plan_flags_validation(args, status):
 
 
 def test_transposed_b_plans_use_dma_tiles_and_the_same_split():
-    dma = {imm.TILE[t] for t in ("256x256", "128x256", "32x256", "64x256")}
+    dma = {imm.TILE[t] for t in ("256x256", "128x256", "32x256", "64x256", "64x64", "32x64", "32x32")}
     for N, K, dt in SHAPES:
         a = imm.gemm_plan_ex2(64, N, K, dt, "f32").info
         b = imm.gemm_plan_ex2(64, N, K, dt, "f32", flags=imm.PLAN_B_TRANSPOSED).info
