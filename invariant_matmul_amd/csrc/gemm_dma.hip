@@ -23,14 +23,16 @@
 // 3-slot A ring beside a 2-slot B ring and L2 prefetching of later stages).
 //
 // LDS layouts.  A is stored K-contiguous (128 bytes per row in 16-byte
-// slots, slot c of row r at c ^ ((r >> 1) & 7)), read with ds_read_b128.
+// slots, slot c of row r at c ^ ((r >> 1) & 7); the narrow tiles' 256-byte
+// rows at c ^ (r & 15)), read with ds_read_b128.
 // B is stored as it lies in memory, N-contiguous (512 bytes per K row for
 // 16-bit, 256 for fp8), and read with the gfx950 transposing LDS reads
 // (ds_read_b64_tr_b16 / _b8), which hand each lane the K-contiguous column
 // piece the matrix core needs.  16-byte slot c of B row k lives at
 // c ^ ((k & 3) << 2) ^ (((k >> 3) & 1) << 1) (16-bit) or c ^ ((k & 7) << 1)
-// (fp8) so that the rows and columns the 32 lanes of one half-wave read fall
-// on different banks.  The swizzles are applied
+// (fp8), and narrower rows by swizzles of their own (bswz below), so that
+// the rows and columns each quarter-wave reads fall on different banks.  The
+// swizzles are applied
 // on the global side: each DMA lane fetches the chunk that belongs in its
 // fixed LDS slot.
 //
