@@ -77,8 +77,10 @@ bool small_b(int64_t N, int64_t K, int eb) { return N * K * eb <= ((int64_t)4 <<
 
 bool dma_offsets_fit(int tile, int64_t N, int64_t K, int eb, bool b_trans);
 
-// The 64-column DMA tiles take 16-bit inputs only (an fp8 matrix step covers
-// 32 rows, more than their waves' row blocks).
+// The narrow DMA tiles (64 and 32 columns) take 16-bit inputs only: their
+// 256-byte K stages hold two fp8 k-steps where the fp8 schedule runs one per
+// stage, and a 32-column fp8 row would be 32 bytes, below the four 16-byte
+// slots the B swizzle needs.
 bool is_narrow_tile(int tile) {
   return tile == GEMM_TILE_32x64 || tile == GEMM_TILE_64x64 || tile == GEMM_TILE_32x32;
 }
