@@ -375,6 +375,104 @@ def write_trace_summary(trace_csv, bench_json, out_path=TRACE_SUMMARY_FILE):
     print(out_path)
 
 
+QKV_TRACE_FILE = os.path.join(ROOT, "profiles", "qkv_m_sweep_kernel_trace.md")
+QKV_PASS_CALLS = 50
+
+
+def qkv_pass(torch, imm, wl, N=6144, K=4096, ms=(1, 16, 64, 256, 1024)):
+    """The fused-QKV M sweep's calls for a kernel trace: for each M, our plan
+    with the tile from M (B as [K, N], then W [N, K]) and torch.matmul /
+    F.linear on the same operands, each QKV_PASS_CALLS calls back to back
+    after warm-up.  A one-element fill separates the cases in the trace.
+    Prints the list of cases (one JSON line)."""
+    g = wl.gen(6000)
+    A = wl.uniform((max(ms), K), "f16", g).cuda()
+    B = wl.uniform((K, N), "f16", g).cuda()
+    W = B.t().contiguous()
+    sep = torch.empty(1, device="cuda")  # filled only as a separator (no kernel here)
+    cases = []
+    for m in ms:
+        a = A[:m].contiguous()
+        C = torch.empty((m, N), dtype=torch.float32, device="cuda")
+        pk = imm.gemm_plan_ex2(m, N, K, "f16", "f32", flags=imm.PLAN_TILE_BY_M)
+        pw = imm.gemm_plan_ex2(m, N, K, "f16", "f32",
+                               flags=imm.PLAN_TILE_BY_M | imm.PLAN_B_TRANSPOSED)
+        ref = torch.empty((m, N), dtype=torch.float16, device="cuda")
+        runs = [("ours, B [K, N]", f"{pk.info['run_block_m']}x{pk.info['run_block_n']}",
+                 lambda: imm.gemm_run(pk, a, B, C)),
+                ("torch.matmul, B [K, N]", "hipBLASLt", lambda: torch.matmul(a, B, out=ref)),
+                ("ours, W [N, K]", f"{pw.info['run_block_m']}x{pw.info['run_block_n']}",
+                 lambda: imm.gemm_run(pw, a, W, C)),
+                ("F.linear, W [N, K]", "hipBLASLt", lambda: torch.nn.functional.linear(a, W))]
+        for name, tile, fn in runs:
+            for _ in range(20):
+                fn()
+            torch.cuda.synchronize()
+            sep.fill_(1.0)
+            torch.cuda.synchronize()
+            for _ in range(QKV_PASS_CALLS):
+                fn()
+            torch.cuda.synchronize()
+            sep.fill_(1.0)
+            torch.cuda.synchronize()
+            cases.append({"M": m, "N": N, "K": K, "what": name, "tile": tile})
+    print(json.dumps({"calls": QKV_PASS_CALLS, "cases": cases}))
+
+
+def write_qkv_trace_summary(trace_csv, pass_json, out_path=QKV_TRACE_FILE):
+    """Summarise a rocprofv3 --kernel-trace run of `bench.py --qkv-pass`:
+    kernel time per call of every case (the kernels between the separating
+    fills that enclose its timed calls, divided by the calls)."""
+    import csv
+    with open(pass_json) as f:
+        meta = json.loads(f.read().strip().splitlines()[-1])
+    rows = []
+    with open(trace_csv) as f:
+        for r in csv.DictReader(f):
+            rows.append((int(r["Start_Timestamp"]), r["Kernel_Name"],
+                         (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3))
+    rows.sort()
+    is_sep = ["FillFunctor" in n for _, n, us in rows]
+    # segments between consecutive separators; the timed calls of case i are
+    # segment 2i + 1 (warm-up, sep, timed calls, sep; nothing else fills)
+    segs, cur = [], []
+    for (t, n, us), sp in zip(rows, is_sep):
+        if sp:
+            segs.append(cur)
+            cur = []
+        else:
+            cur.append((n, us))
+    segs.append(cur)
+    calls = meta["calls"]
+    out = ["# Kernel trace of the fused-QKV M sweep (N = 6144, K = 4096, fp16)", "",
+           "Commands (repository root, MI355X):", "",
+           "    rocprofv3 --kernel-trace --output-format csv -d gpurun_out/prof_qkv -o qkv "
+           "-- python3 bench.py --qkv-pass > gpurun_out/qkv_pass.json",
+           "    python3 bench.py --write-qkv-trace-summary gpurun_out/prof_qkv/qkv_kernel_trace.csv "
+           "gpurun_out/qkv_pass.json", "",
+           f"Each case: {calls} calls back to back after 20 warm-up calls, one B (held by the "
+           "last-level cache between calls), our fp32 out against torch's fp16 out. Kernel time "
+           "per call is the trace's kernel durations between the separating fills divided by "
+           "the calls; it leaves out launch gaps, which the bench's event timings include.", "",
+           "| M | call | tile | kernels per call | kernel us per call | main kernel |",
+           "|---:|---|---|---:|---:|---|"]
+    if len(segs) != 2 * len(meta["cases"]) + 1:
+        raise SystemExit(f"{trace_csv}: {len(segs) - 1} separators, expected {2 * len(meta['cases'])}")
+    for i, c in enumerate(meta["cases"]):
+        seg = segs[2 * i + 1]
+        if len(seg) < calls:
+            raise SystemExit(f"{trace_csv}: {len(seg)} kernels for case {i} ({c}), expected >= {calls}")
+        tot = sum(us for _, us in seg)
+        main = max(set(n for n, _ in seg), key=lambda n: sum(us for m_, us in seg if m_ == n))
+        main = main.replace("void imm::(anonymous namespace)::", "").split("(")[0]
+        main = main if len(main) <= 60 else main[:57] + "..."
+        out.append(f"| {c['M']} | {c['what']} | {c['tile']} | {len(seg) / calls:.2f} | "
+                   f"{tot / calls:.2f} | `{main}` |")
+    with open(out_path, "w") as f:
+        f.write("\n".join(out) + "\n")
+    print(out_path)
+
+
 def _smi_power_clocks():
     """Socket power (W) and the XCDs' engine clocks (MHz) from amd-smi."""
     import re
@@ -833,6 +931,11 @@ def main():
     ap.add_argument("--write-trace-summary", nargs=2, metavar=("TRACE_CSV", "BENCH_JSON"),
                     help="host only: write the kernel-trace summary of a rocprofv3 --kernel-trace run "
                          "of the default bench command, then exit")
+    ap.add_argument("--qkv-pass", action="store_true",
+                    help="the fused-QKV M sweep's calls, back to back with separators, for a "
+                         "kernel trace; prints the list of cases")
+    ap.add_argument("--write-qkv-trace-summary", nargs=2, metavar=("TRACE_CSV", "PASS_JSON"),
+                    help="host only: write the kernel-trace summary of a --qkv-pass run, then exit")
     ap.add_argument("--power-sample", action="store_true",
                     help="run the headline product in a loop on random, then all-zero inputs "
                          "and read the board's power and engine clocks with amd-smi during "
@@ -850,6 +953,9 @@ def main():
         return
     if args.write_trace_summary:
         write_trace_summary(*args.write_trace_summary)
+        return
+    if args.write_qkv_trace_summary:
+        write_qkv_trace_summary(*args.write_qkv_trace_summary)
         return
     if args.write_clock:
         if len(args.write_clock) not in (2, 3):
@@ -871,6 +977,10 @@ def main():
         sys.exit(1)
     torch.cuda.set_device(0)
     imm.lib()
+
+    if args.qkv_pass:
+        qkv_pass(torch, imm, wl)
+        return
 
     if args.profile_pass:
         w = wl.WORKLOADS["square_f16_8192"]
