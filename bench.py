@@ -571,7 +571,7 @@ def time_launches(fn, n, warmup, torch, settle_ms=SETTLE_MS, queue_ahead=False):
           for _ in range(n)]
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
-    if queue_ahead:
+    if queue_ahead and hasattr(torch.cuda, "_sleep"):
         # about 0.1 ms of engine cycles per timed call, at least 2 ms
         torch.cuda._sleep(int(2.4e5 * max(20, n)))
     t0.record()
