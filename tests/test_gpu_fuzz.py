@@ -53,7 +53,7 @@ def _run(plan, A, B, split):
     return C
 
 
-@pytest.mark.parametrize("seed", range(24))
+@pytest.mark.parametrize("seed", range(64))
 def test_random_case(seed):
     dt, M, N, K, out, split = _case(seed)
     g = wl.gen(9000 + seed)
